@@ -1,0 +1,217 @@
+"""CPU oracle for the HEAL hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU baseline leg may
+import this package.  The GPU library and its Python binding never import it.
+
+The arithmetic lives in heal_oracle.c (plain C, binary64 / naive binary32);
+this module only marshals numpy arrays through ctypes.  See heal_oracle.c
+for the passage of the HEAL paper each function follows and what pins it.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+_c_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+def lib():
+    """Load the oracle library, building it first only if it is missing."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        sigs = {
+            "oracle_f32_to_f16": [_p, _c_i64, _p],
+            "oracle_f16_to_f64": [_p, _c_i64, _p],
+            "oracle_split_f16": [_p, _c_i64, _p, _p],
+            "oracle_gemm_f64": [_p, _c_i64, _p, _c_i64, ctypes.c_int, _p, _c_i64, _c_i64, _c_i64, _c_i64],
+            "oracle_gemm_f32_naive": [_p, _c_i64, _p, _c_i64, ctypes.c_int, _p, _c_i64, _c_i64, _c_i64, _c_i64],
+            "oracle_gemm_comp_model": [_p, _c_i64, _p, _c_i64, ctypes.c_int, _p, _c_i64, _c_i64, _c_i64, _c_i64],
+            "oracle_gemm_f64_rows": [_p, _c_i64, _p, _c_i64, ctypes.c_int, _p, _c_i64, _p, _c_i64, _c_i64, _c_i64],
+            "oracle_gemm_f32_naive_rows": [_p, _c_i64, _p, _c_i64, ctypes.c_int, _p, _c_i64, _p, _c_i64, _c_i64, _c_i64],
+            "oracle_quant_i16": [_p, _c_i64, _c_i64, _c_i64, _p, _c_i64, _p],
+            "oracle_dequant_f32": [_p, _c_i64, _c_i64, _c_i64, _p, _p, _c_i64],
+            "oracle_dequant_f16x2": [_p, _c_i64, _c_i64, _c_i64, _p, _p, _c_i64],
+            "oracle_attn_decode_f64": [_p] * 6 + [_p] + [_c_i64] * 5,
+            "oracle_attn_decode_weight_norm": [_p] * 6 + [_p] + [_c_i64] * 5,
+            "oracle_attn_decode_f32_naive": [_p] * 6 + [_p] + [_c_i64] * 5,
+        }
+        for name, argtypes in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = argtypes
+            fn.restype = None
+        L.oracle_abi_version.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# --- binary16 -----------------------------------------------------------------
+
+def f32_to_f16_bits(x):
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().oracle_f32_to_f16(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def f16_bits_to_f64(h):
+    h = _c(h, np.uint16)
+    out = np.empty(h.shape, np.float64)
+    lib().oracle_f16_to_f64(_ptr(h), h.size, _ptr(out))
+    return out
+
+
+# --- split ----------------------------------------------------------------------
+
+def split_f16(x):
+    """x (float32, any shape) -> (hi, lo) binary16 bit patterns, x ~= hi + lo/2^10."""
+    x = _c(x, np.float32)
+    hi = np.empty(x.shape, np.uint16)
+    lo = np.empty(x.shape, np.uint16)
+    lib().oracle_split_f16(_ptr(x), x.size, _ptr(hi), _ptr(lo))
+    return hi, lo
+
+
+# --- GEMM -----------------------------------------------------------------------
+
+def _gemm_args(A, W, w_layout):
+    A = _c(A, np.float32)
+    W = _c(W, np.float32)
+    M, K = A.shape
+    if w_layout == "nk":
+        N, K2 = W.shape
+        w_kn = 0
+    elif w_layout == "kn":
+        K2, N = W.shape
+        w_kn = 1
+    else:
+        raise ValueError(w_layout)
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    return A, W, M, N, K, w_kn
+
+
+def gemm_f64(A, W, w_layout="nk"):
+    """C64 = A . B in binary64, B = W^T for W [N,K] ('nk') or B = W for W [K,N] ('kn')."""
+    A, W, M, N, K, w_kn = _gemm_args(A, W, w_layout)
+    C = np.empty((M, N), np.float64)
+    lib().oracle_gemm_f64(_ptr(A), K, _ptr(W), W.shape[1], w_kn, _ptr(C), N, M, N, K)
+    return C
+
+
+def gemm_f32_naive(A, W, w_layout="nk"):
+    A, W, M, N, K, w_kn = _gemm_args(A, W, w_layout)
+    C = np.empty((M, N), np.float32)
+    lib().oracle_gemm_f32_naive(_ptr(A), K, _ptr(W), W.shape[1], w_kn, _ptr(C), N, M, N, K)
+    return C
+
+
+def gemm_comp_model(A, W, w_layout="nk"):
+    A, W, M, N, K, w_kn = _gemm_args(A, W, w_layout)
+    C = np.empty((M, N), np.float64)
+    lib().oracle_gemm_comp_model(_ptr(A), K, _ptr(W), W.shape[1], w_kn, _ptr(C), N, M, N, K)
+    return C
+
+
+def gemm_f64_rows(A, W, rows, w_layout="nk"):
+    """Rows `rows` of the binary64 product (for shapes too large to do whole)."""
+    A, W, M, N, K, w_kn = _gemm_args(A, W, w_layout)
+    rows = _c(rows, np.int64)
+    C = np.empty((rows.size, N), np.float64)
+    lib().oracle_gemm_f64_rows(_ptr(A), K, _ptr(W), W.shape[1], w_kn, _ptr(rows), rows.size,
+                               _ptr(C), N, N, K)
+    return C
+
+
+def gemm_f32_naive_rows(A, W, rows, w_layout="nk"):
+    A, W, M, N, K, w_kn = _gemm_args(A, W, w_layout)
+    rows = _c(rows, np.int64)
+    C = np.empty((rows.size, N), np.float32)
+    lib().oracle_gemm_f32_naive_rows(_ptr(A), K, _ptr(W), W.shape[1], w_kn, _ptr(rows), rows.size,
+                                     _ptr(C), N, N, K)
+    return C
+
+
+# --- INT16 quant / dequant ----------------------------------------------------
+
+def quant_i16(X):
+    """X float32 [..., D] -> (codes int16 [..., D], scales float32 [...]), one scale per row."""
+    X = _c(X, np.float32)
+    D = X.shape[-1]
+    rows = X.size // D if D else 0
+    codes = np.empty(X.shape, np.int16)
+    scales = np.empty(X.shape[:-1], np.float32)
+    lib().oracle_quant_i16(_ptr(X), rows, D, D, _ptr(codes), D, _ptr(scales))
+    return codes, scales
+
+
+def dequant_f32(codes, scales):
+    codes = _c(codes, np.int16)
+    scales = _c(scales, np.float32)
+    D = codes.shape[-1]
+    rows = codes.size // D if D else 0
+    out = np.empty(codes.shape, np.float32)
+    lib().oracle_dequant_f32(_ptr(codes), rows, D, D, _ptr(scales), _ptr(out), D)
+    return out
+
+
+def dequant_f16x2(codes):
+    codes = _c(codes, np.int16)
+    D = codes.shape[-1]
+    rows = codes.size // D if D else 0
+    hi = np.empty(codes.shape, np.uint16)
+    lo = np.empty(codes.shape, np.uint16)
+    lib().oracle_dequant_f16x2(_ptr(codes), rows, D, D, _ptr(hi), _ptr(lo), D)
+    return hi, lo
+
+
+# --- decode attention -----------------------------------------------------------
+
+def _attn_args(q, qs, k, ks, v, vs):
+    q = _c(q, np.int16); qs = _c(qs, np.float32)
+    k = _c(k, np.int16); ks = _c(ks, np.float32)
+    v = _c(v, np.int16); vs = _c(vs, np.float32)
+    B, Hq, D = q.shape
+    B2, T, Hkv, D2 = k.shape
+    if B2 != B or D2 != D or v.shape != k.shape or Hq % Hkv:
+        raise ValueError("attention shapes")
+    return q, qs, k, ks, v, vs, B, T, Hq, Hkv, D
+
+
+def attn_decode_f64(q, qs, k, ks, v, vs):
+    """q [B,Hq,D] int16 + qs [B,Hq]; k, v [B,T,Hkv,D] int16 + [B,T,Hkv] -> o [B,Hq,D] float64."""
+    q, qs, k, ks, v, vs, B, T, Hq, Hkv, D = _attn_args(q, qs, k, ks, v, vs)
+    out = np.empty((B, Hq, D), np.float64)
+    lib().oracle_attn_decode_f64(_ptr(q), _ptr(qs), _ptr(k), _ptr(ks), _ptr(v), _ptr(vs),
+                                 _ptr(out), B, T, Hq, Hkv, D)
+    return out
+
+
+def attn_decode_weight_norm(q, qs, k, ks, v, vs):
+    q, qs, k, ks, v, vs, B, T, Hq, Hkv, D = _attn_args(q, qs, k, ks, v, vs)
+    out = np.empty((B, Hq, D), np.float64)
+    lib().oracle_attn_decode_weight_norm(_ptr(q), _ptr(qs), _ptr(k), _ptr(ks), _ptr(v), _ptr(vs),
+                                         _ptr(out), B, T, Hq, Hkv, D)
+    return out
+
+
+def attn_decode_f32_naive(q, qs, k, ks, v, vs):
+    q, qs, k, ks, v, vs, B, T, Hq, Hkv, D = _attn_args(q, qs, k, ks, v, vs)
+    out = np.empty((B, Hq, D), np.float32)
+    lib().oracle_attn_decode_f32_naive(_ptr(q), _ptr(qs), _ptr(k), _ptr(ks), _ptr(v), _ptr(vs),
+                                       _ptr(out), B, T, Hq, Hkv, D)
+    return out
