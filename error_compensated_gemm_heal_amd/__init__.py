@@ -1,0 +1,249 @@
+"""Python binding of libheal: the HEAL hot path on MI355X (gfx950).
+
+Thin ctypes wrappers with the same names as the C ABI in include/heal.h.
+They only marshal arguments: every step of the computation runs in the HIP
+kernels of libheal.so.  PyTorch supplies device memory (tensors, workspaces)
+and the stream (the current torch stream).  There is no CPU fallback: if the
+library is missing the binding raises.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "HealError", "lib", "heal_status_str", "heal_version", "heal_split_f32", "heal_gemm_f32c",
+    "heal_gemm_f32c_workspace", "heal_pack_w", "heal_pack_w_bytes", "heal_qkv_quant_i16",
+    "heal_kv_dequant_i16", "heal_attn_decode_i16", "heal_attn_decode_workspace", "PackedWeight",
+    "HEAL_W_NK", "HEAL_W_KN", "HEAL_W_PACKED", "HEAL_FLAG_F16_RANGE", "HEAL_DQ_F32", "HEAL_DQ_F16X2",
+    "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libheal.so")
+
+HEAL_OK = 0
+HEAL_W_NK, HEAL_W_KN, HEAL_W_PACKED = 0, 1, 2
+HEAL_FLAG_F16_RANGE = 1
+HEAL_DQ_F32, HEAL_DQ_F16X2 = 0, 1
+
+# (name, argtypes, restype) of every exported entry point
+_I64, _P, _SZ, _U32, _INT = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_int
+SIGNATURES = {
+    "heal_status_str": ([_INT], ctypes.c_char_p),
+    "heal_version": ([], _INT),
+    "heal_split_f32": ([_P, _I64, _P, _P, _P, _P], _INT),
+    "heal_gemm_f32c": ([_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _U32, _P, _SZ, _P, _P], _INT),
+    "heal_gemm_f32c_workspace": ([_I64, _I64, _I64, _U32], _SZ),
+    "heal_pack_w": ([_P, _I64, _I64, _I64, _U32, _P, _SZ, _P, _P], _INT),
+    "heal_pack_w_bytes": ([_I64, _I64], _SZ),
+    "heal_qkv_quant_i16": ([_P, _I64, _I64, _I64, _P, _I64, _P, _P], _INT),
+    "heal_kv_dequant_i16": ([_P, _I64, _I64, _I64, _P, _INT, _P, _P, _I64, _P], _INT),
+    "heal_attn_decode_i16": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _SZ, _P], _INT),
+    "heal_attn_decode_workspace": ([_I64, _I64, _I64, _I64, _I64], _SZ),
+}
+
+_LIB = None
+
+
+class HealError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {heal_status_str(status)}")
+        self.status = status
+
+
+def lib():
+    """The loaded libheal.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with error_compensated_gemm_heal_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (argtypes, restype) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = argtypes
+            fn.restype = restype
+        _LIB = L
+    return _LIB
+
+
+def heal_status_str(status: int) -> str:
+    return lib().heal_status_str(int(status)).decode()
+
+
+def heal_version() -> int:
+    return lib().heal_version()
+
+
+def _check(fn: str, status: int):
+    if status != HEAL_OK:
+        raise HealError(fn, status)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _rowmajor_ld(t: torch.Tensor, name: str) -> int:
+    """Leading dimension of a 2-D row-major view (unit stride along rows)."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along its rows")
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0))
+
+
+def _workspace(nbytes: int, device):
+    if nbytes == 0:
+        return None
+    # 256-byte alignment: torch's caching allocator returns blocks aligned far beyond that
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# ---- operand split ------------------------------------------------------------
+
+def heal_split_f32(X: torch.Tensor, hi=None, lo=None, dev_status=None):
+    """x -> (hi, lo) fp16 with x ~= hi + lo / 2^10 (elementwise, contiguous)."""
+    _dev(X, "X", torch.float32)
+    X = X.contiguous()
+    hi = torch.empty(X.shape, dtype=torch.float16, device=X.device) if hi is None else hi
+    lo = torch.empty(X.shape, dtype=torch.float16, device=X.device) if lo is None else lo
+    _check("heal_split_f32", lib().heal_split_f32(_ptr(X), X.numel(), _ptr(hi), _ptr(lo),
+                                                  _ptr(dev_status), _stream()))
+    return hi, lo
+
+
+# ---- compensated GEMM ------------------------------------------------------------
+
+class PackedWeight:
+    """A weight split once into the GEMM's packed dual-FP16 form (opaque buffer)."""
+
+    def __init__(self, buf: torch.Tensor, N: int, K: int):
+        self.buf, self.N, self.K = buf, N, K
+
+
+def heal_pack_w_bytes(N: int, K: int) -> int:
+    return lib().heal_pack_w_bytes(N, K)
+
+
+def heal_pack_w(W: torch.Tensor, w_layout: str = "nk", dev_status=None) -> PackedWeight:
+    _dev(W, "W", torch.float32)
+    flags = HEAL_W_KN if w_layout == "kn" else HEAL_W_NK
+    if w_layout == "kn":
+        K, N = W.shape
+    else:
+        N, K = W.shape
+    ldw = _rowmajor_ld(W, "W")
+    nbytes = heal_pack_w_bytes(N, K)
+    buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=W.device)
+    _check("heal_pack_w", lib().heal_pack_w(_ptr(W), ldw, N, K, flags, _ptr(buf), nbytes,
+                                            _ptr(dev_status), _stream()))
+    return PackedWeight(buf, N, K)
+
+
+def heal_gemm_f32c_workspace(M: int, N: int, K: int, flags: int) -> int:
+    return lib().heal_gemm_f32c_workspace(M, N, K, flags)
+
+
+def heal_gemm_f32c(A: torch.Tensor, W, w_layout: str = "nk", C=None, workspace=None, dev_status=None):
+    """C = A . B with B = W^T ('nk', W [N,K]) or B = W ('kn', W [K,N]), or W a PackedWeight."""
+    _dev(A, "A", torch.float32)
+    M, K = A.shape
+    lda = _rowmajor_ld(A, "A")
+    if isinstance(W, PackedWeight):
+        if W.K != K:
+            raise ValueError("packed weight has a different K")
+        N, flags, wptr, ldw = W.N, HEAL_W_PACKED, _ptr(W.buf), 0
+    else:
+        _dev(W, "W", torch.float32)
+        if w_layout == "kn":
+            K2, N = W.shape
+            flags = HEAL_W_KN
+        else:
+            N, K2 = W.shape
+            flags = HEAL_W_NK
+        if K2 != K:
+            raise ValueError("inner dimensions differ")
+        wptr, ldw = _ptr(W), _rowmajor_ld(W, "W")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    ldc = _rowmajor_ld(C, "C") if M > 0 and N > 0 else N
+    nbytes = heal_gemm_f32c_workspace(M, N, K, flags)
+    if workspace is None:
+        workspace = _workspace(nbytes, A.device)
+    elif workspace.numel() < nbytes:
+        raise ValueError("workspace too small")
+    _check("heal_gemm_f32c", lib().heal_gemm_f32c(_ptr(A), lda, wptr, ldw, _ptr(C), ldc, M, N, K, flags,
+                                                  _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                                  _ptr(dev_status), _stream()))
+    return C
+
+
+# ---- INT16 quant / dequant -------------------------------------------------------------
+
+def heal_qkv_quant_i16(X: torch.Tensor, codes=None, scales=None):
+    """X [..., D] fp32 -> (codes int16 [..., D], scales fp32 [...]), one scale per row of D."""
+    _dev(X, "X", torch.float32)
+    X = X.contiguous()
+    D = X.shape[-1]
+    rows = X.numel() // D if D else 0
+    codes = torch.empty(X.shape, dtype=torch.int16, device=X.device) if codes is None else codes
+    scales = torch.empty(X.shape[:-1], dtype=torch.float32, device=X.device) if scales is None else scales
+    _check("heal_qkv_quant_i16", lib().heal_qkv_quant_i16(_ptr(X), rows, D, D, _ptr(codes), D, _ptr(scales),
+                                                          _stream()))
+    return codes, scales
+
+
+def heal_kv_dequant_i16(codes: torch.Tensor, scales=None, fmt: str = "f32"):
+    """codes [..., D] int16 (+ scales [...]) -> fp32 values, or (hi, lo) fp16 planes for fmt='f16x2'."""
+    _dev(codes, "codes", torch.int16)
+    codes = codes.contiguous()
+    D = codes.shape[-1]
+    rows = codes.numel() // D if D else 0
+    if fmt == "f32":
+        out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
+        _check("heal_kv_dequant_i16", lib().heal_kv_dequant_i16(_ptr(codes), rows, D, D, _ptr(scales), HEAL_DQ_F32,
+                                                                _ptr(out), None, D, _stream()))
+        return out
+    hi = torch.empty(codes.shape, dtype=torch.float16, device=codes.device)
+    lo = torch.empty(codes.shape, dtype=torch.float16, device=codes.device)
+    _check("heal_kv_dequant_i16", lib().heal_kv_dequant_i16(_ptr(codes), rows, D, D, _ptr(scales), HEAL_DQ_F16X2,
+                                                            _ptr(hi), _ptr(lo), D, _stream()))
+    return hi, lo
+
+
+# ---- decode attention over INT16 Q/K/V -----------------------------------------------------
+
+def heal_attn_decode_workspace(B, T, Hq, Hkv, D) -> int:
+    return lib().heal_attn_decode_workspace(B, T, Hq, Hkv, D)
+
+
+def heal_attn_decode_i16(q, q_scale, k, k_scale, v, v_scale, out=None, workspace=None):
+    """q [B,Hq,D] int16 + [B,Hq]; k, v [B,T,Hkv,D] int16 + [B,T,Hkv] -> out [B,Hq,D] fp32."""
+    for name, t, dt in (("q", q, torch.int16), ("k", k, torch.int16), ("v", v, torch.int16),
+                        ("q_scale", q_scale, torch.float32), ("k_scale", k_scale, torch.float32),
+                        ("v_scale", v_scale, torch.float32)):
+        _dev(t, name, dt)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, Hq, D = q.shape
+    _, T, Hkv, _ = k.shape
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device) if out is None else out
+    nbytes = heal_attn_decode_workspace(B, T, Hq, Hkv, D)
+    if workspace is None:
+        workspace = _workspace(nbytes, q.device)
+    _check("heal_attn_decode_i16", lib().heal_attn_decode_i16(
+        _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(v), _ptr(v_scale), _ptr(out), B, T, Hq, Hkv, D,
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream()))
+    return out

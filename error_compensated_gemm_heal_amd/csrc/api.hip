@@ -1,0 +1,198 @@
+// C ABI of libheal: argument validation (host only, before any HIP call),
+// workspace layout and kernel selection.  Entry points and their contracts
+// are documented in include/heal.h.
+#include <cstdint>
+
+#include "heal_internal.h"
+
+using namespace heal;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+heal_status hip_status(hipError_t e) { return e == hipSuccess ? HEAL_OK : HEAL_ERR_HIP; }
+
+// Path choice for heal_gemm_f32c.  The decode kernel streams an fp32 [N,K]
+// weight directly; every other case packs the operands for the prefill kernel.
+bool use_decode(int64_t M, uint32_t flags) {
+    return M <= 64 && !(flags & HEAL_W_PACKED) && (flags & HEAL_W_KN) == 0;
+}
+
+__global__ void zero_rows_kernel(float* C, int64_t ldc, int64_t M, int64_t N) {
+    const int64_t total = M * N;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t m = i / N;
+        C[m * ldc + (i - m * N)] = 0.0f;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* heal_status_str(heal_status s) {
+    switch (s) {
+        case HEAL_OK: return "HEAL_OK";
+        case HEAL_ERR_NULL: return "HEAL_ERR_NULL: a required pointer is NULL";
+        case HEAL_ERR_SHAPE: return "HEAL_ERR_SHAPE: a dimension is negative or out of range";
+        case HEAL_ERR_STRIDE: return "HEAL_ERR_STRIDE: a leading dimension is smaller than its row";
+        case HEAL_ERR_ALIGN: return "HEAL_ERR_ALIGN: a pointer or leading dimension is misaligned";
+        case HEAL_ERR_UNSUPPORTED: return "HEAL_ERR_UNSUPPORTED: unsupported flags or sizes";
+        case HEAL_ERR_WORKSPACE: return "HEAL_ERR_WORKSPACE: workspace missing or too small";
+        case HEAL_ERR_HIP: return "HEAL_ERR_HIP: a HIP kernel launch failed";
+    }
+    return "HEAL: unknown status";
+}
+
+int heal_version(void) { return (1 << 16) | 0; }
+
+heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo,
+                           uint32_t* dev_status, void* stream) {
+    if (n < 0) return HEAL_ERR_SHAPE;
+    if (n == 0) return HEAL_OK;
+    if (!X || !hi || !lo) return HEAL_ERR_NULL;
+    if (misaligned(X, 16) || misaligned(hi, 8) || misaligned(lo, 8) || misaligned(dev_status, 4))
+        return HEAL_ERR_ALIGN;
+    return hip_status(launch_split(X, n, hi, lo, dev_status, static_cast<hipStream_t>(stream)));
+}
+
+size_t heal_pack_w_bytes(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0 || N >= kMaxDim || K >= kMaxDim) return 0;
+    return (size_t)pack_bytes(N, K);
+}
+
+heal_status heal_pack_w(const float* W, int64_t ldw, int64_t N, int64_t K, uint32_t flags,
+                        void* packed, size_t packed_bytes, uint32_t* dev_status, void* stream) {
+    if (N < 0 || K < 0 || N >= kMaxDim || K >= kMaxDim) return HEAL_ERR_SHAPE;
+    if (flags & ~(uint32_t)HEAL_W_KN) return HEAL_ERR_UNSUPPORTED;
+    if (N == 0 || K == 0) return HEAL_OK;
+    if (!W || !packed) return HEAL_ERR_NULL;
+    const bool kn = flags & HEAL_W_KN;
+    if (ldw < (kn ? N : K)) return HEAL_ERR_STRIDE;
+    if (misaligned(W, 4) || misaligned(packed, 256) || misaligned(dev_status, 4)) return HEAL_ERR_ALIGN;
+    if (packed_bytes < (size_t)pack_bytes(N, K)) return HEAL_ERR_WORKSPACE;
+    return hip_status(launch_pack(W, ldw, N, K, kn ? 1 : 0, packed, dev_status,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags) {
+    if (M <= 0 || N <= 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return 0;
+    if (use_decode(M, flags)) {
+        const DecodePlan p = decode_plan(M, N, K);
+        return (size_t)(round256(p.a_bytes) + round256(p.p_bytes));
+    }
+    int64_t b = round256(pack_bytes(M, K));
+    if (!(flags & HEAL_W_PACKED)) b += round256(pack_bytes(N, K));
+    return (size_t)b;
+}
+
+heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t ldw, float* C,
+                           int64_t ldc, int64_t M, int64_t N, int64_t K, uint32_t flags,
+                           void* workspace, size_t workspace_bytes, uint32_t* dev_status,
+                           void* stream) {
+    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return HEAL_ERR_SHAPE;
+    if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_PACKED)) return HEAL_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return HEAL_OK;
+    if (!C) return HEAL_ERR_NULL;
+    if (ldc < N) return HEAL_ERR_STRIDE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0) {
+        const int64_t blocks = std::min<int64_t>((M * N + 255) / 256, 4096);
+        hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, C, ldc, M, N);
+        return hip_status(hipGetLastError());
+    }
+    if (!A || !W) return HEAL_ERR_NULL;
+    if (lda < K) return HEAL_ERR_STRIDE;
+    const bool packed = flags & HEAL_W_PACKED;
+    const bool kn = flags & HEAL_W_KN;
+    if (!packed && ldw < (kn ? N : K)) return HEAL_ERR_STRIDE;
+    if (misaligned(A, 4) || misaligned(W, packed ? 256 : 4) || misaligned(C, 4) || misaligned(dev_status, 4))
+        return HEAL_ERR_ALIGN;
+    const size_t need = heal_gemm_f32c_workspace(M, N, K, flags);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return HEAL_ERR_WORKSPACE;
+        if (misaligned(workspace, 256)) return HEAL_ERR_ALIGN;
+    }
+
+    if (use_decode(M, flags)) {
+        const DecodePlan p = decode_plan(M, N, K);
+        unsigned char* ws = static_cast<unsigned char*>(workspace);
+        return hip_status(launch_gemm_decode(A, lda, static_cast<const float*>(W), ldw, C, ldc, M, N,
+                                             K, ws + round256(p.a_bytes), p, dev_status, s));
+    }
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    void* apk = ws;
+    const void* bpk = W;
+    hipError_t e = launch_pack(A, lda, M, K, 0, apk, dev_status, s);
+    if (e != hipSuccess) return HEAL_ERR_HIP;
+    if (!packed) {
+        void* wpk = ws + round256(pack_bytes(M, K));
+        e = launch_pack(static_cast<const float*>(W), ldw, N, K, kn ? 1 : 0, wpk, dev_status, s);
+        if (e != hipSuccess) return HEAL_ERR_HIP;
+        bpk = wpk;
+    }
+    return hip_status(launch_gemm_prefill(apk, bpk, C, ldc, M, N, K, s));
+}
+
+heal_status heal_qkv_quant_i16(const float* X, int64_t rows, int64_t D, int64_t ldx, int16_t* codes,
+                               int64_t ldq, float* scales, void* stream) {
+    if (rows < 0 || D < 0) return HEAL_ERR_SHAPE;
+    if (rows == 0) return HEAL_OK;
+    if (D < 4 || D > 4096 || (D & 3)) return HEAL_ERR_SHAPE;
+    if (!X || !codes || !scales) return HEAL_ERR_NULL;
+    if (ldx < D || ldq < D) return HEAL_ERR_STRIDE;
+    if (misaligned(X, 16) || (ldx & 3) || misaligned(codes, 8) || (ldq & 3) || misaligned(scales, 4))
+        return HEAL_ERR_ALIGN;
+    return hip_status(launch_quant(X, rows, D, ldx, codes, ldq, scales, static_cast<hipStream_t>(stream)));
+}
+
+heal_status heal_kv_dequant_i16(const int16_t* codes, int64_t rows, int64_t D, int64_t ldq,
+                                const float* scales, int fmt, void* out, void* out_lo, int64_t ldo,
+                                void* stream) {
+    if (rows < 0 || D < 0) return HEAL_ERR_SHAPE;
+    if (fmt != HEAL_DQ_F32 && fmt != HEAL_DQ_F16X2) return HEAL_ERR_UNSUPPORTED;
+    if (rows == 0) return HEAL_OK;
+    if (D < 4 || D > 4096 || (D & 3)) return HEAL_ERR_SHAPE;
+    if (!codes || !out) return HEAL_ERR_NULL;
+    if (fmt == HEAL_DQ_F32 && !scales) return HEAL_ERR_NULL;
+    if (fmt == HEAL_DQ_F16X2 && !out_lo) return HEAL_ERR_NULL;
+    if (ldq < D || ldo < D) return HEAL_ERR_STRIDE;
+    if (misaligned(codes, 8) || (ldq & 3) || (ldo & 3) || misaligned(scales, 4)) return HEAL_ERR_ALIGN;
+    if (fmt == HEAL_DQ_F32 ? misaligned(out, 16) : (misaligned(out, 8) || misaligned(out_lo, 8)))
+        return HEAL_ERR_ALIGN;
+    return hip_status(launch_dequant(codes, rows, D, ldq, scales, fmt, out, out_lo, ldo,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t heal_attn_decode_workspace(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D) {
+    if (B <= 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return 0;
+    return (size_t)attn_workspace_bytes(B, T, Hq, Hkv, D);
+}
+
+heal_status heal_attn_decode_i16(const int16_t* q, const float* q_scale, const int16_t* k,
+                                 const float* k_scale, const int16_t* v, const float* v_scale,
+                                 float* out, int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || T < 0 || Hq < 0 || Hkv < 0 || D < 0 || B >= kMaxDim || T >= kMaxDim) return HEAL_ERR_SHAPE;
+    if (B == 0 || Hq == 0) return HEAL_OK;
+    if (Hkv == 0 || Hq % Hkv) return HEAL_ERR_SHAPE;
+    if (T == 0) return HEAL_ERR_SHAPE;
+    if (D != 128 || Hq / Hkv > 8) return HEAL_ERR_UNSUPPORTED;
+    if (!q || !q_scale || !k || !k_scale || !v || !v_scale || !out) return HEAL_ERR_NULL;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
+        misaligned(q_scale, 4) || misaligned(k_scale, 4) || misaligned(v_scale, 4))
+        return HEAL_ERR_ALIGN;
+    const size_t need = heal_attn_decode_workspace(B, T, Hq, Hkv, D);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return HEAL_ERR_WORKSPACE;
+        if (misaligned(workspace, 256)) return HEAL_ERR_ALIGN;
+    }
+    return hip_status(launch_attn_decode(q, q_scale, k, k_scale, v, v_scale, out, B, T, Hq, Hkv, D,
+                                         workspace, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Internal declarations shared by the HIP translation units of libheal.
+// Device helpers for the dual-FP16 representation and the kernel launchers
+// that the C ABI layer (api.hip) calls after validating arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "heal.h"
+
+namespace heal {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// fp32 -> fp16 with round-to-nearest-even and fp16 subnormals kept (the
+// hardware conversion under the default rounding and denormal modes), and the
+// dual-FP16 residual lo = fp16((x - hi) * 2^10); x - hi is exact in fp32.
+__device__ __forceinline__ void split_one(float x, _Float16& hi, _Float16& lo) {
+    hi = (_Float16)x;
+    float r = x - (float)hi;
+    lo = (_Float16)(r * 1024.0f);
+}
+
+__device__ __forceinline__ uint16_t f16_bits(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
+
+// An operand magnitude at or above 65520 rounds to an infinite fp16 high part.
+__device__ __forceinline__ bool f16_out_of_range(float x) { return __builtin_fabsf(x) >= 65520.0f; }
+__device__ __forceinline__ bool f16_out_of_range4(const float4& v) {
+    return fmaxf(fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
+                 fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w))) >= 65520.0f;
+}
+
+// ---- packed dual-FP16 operand layout used by the prefill GEMM --------------
+// Row r of a packed operand holds, for each 32-wide block kb of the reduction
+// dimension, 32 fp16 hi parts followed by 32 fp16 lo parts (128 bytes).  Rows
+// are padded to a multiple of kPackRows and k to a multiple of kPackK, with
+// zeros, so the GEMM main loop needs no bounds checks.
+constexpr int kPackK = 32;
+constexpr int kPackRows = 256;
+
+__host__ __device__ inline int64_t pack_kp(int64_t K) { return (K + kPackK - 1) / kPackK * kPackK; }
+__host__ __device__ inline int64_t pack_rows(int64_t R) { return (R + kPackRows - 1) / kPackRows * kPackRows; }
+// bytes of one packed operand of R rows and reduction length K
+__host__ __device__ inline int64_t pack_bytes(int64_t R, int64_t K) { return pack_rows(R) * pack_kp(K) * 4; }
+
+// ---- launchers (return the launch status; never synchronize) -------------
+hipError_t launch_split(const float* X, int64_t n, uint16_t* hi, uint16_t* lo, uint32_t* status,
+                        hipStream_t s);
+// Pack fp32 rows into the layout above.  kn == 0: src is [rows, K] with ld;
+// kn == 1: src is [K, rows] with ld (the packed operand is its transpose).
+hipError_t launch_pack(const float* src, int64_t ld, int64_t rows, int64_t K, int kn, void* packed,
+                       uint32_t* status, hipStream_t s);
+
+hipError_t launch_quant(const float* X, int64_t rows, int64_t D, int64_t ldx, int16_t* codes,
+                        int64_t ldq, float* scales, hipStream_t s);
+hipError_t launch_dequant(const int16_t* codes, int64_t rows, int64_t D, int64_t ldq,
+                          const float* scales, int fmt, void* out, void* out_lo, int64_t ldo,
+                          hipStream_t s);
+
+// C[M,N] from packed A (rows M) and packed B (rows N).
+hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, float* C, int64_t ldc, int64_t M,
+                               int64_t N, int64_t K, hipStream_t s);
+
+// Decode path (M <= 64): fp32 W [N,K] streamed and split in registers.
+struct DecodePlan {
+    int splits;        // number of K chunks (fixed by N and K only)
+    int64_t kchunk;    // reduction length of one chunk (multiple of 256)
+    int64_t a_bytes;   // workspace bytes of the split activation planes
+    int64_t p_bytes;   // workspace bytes of the split-K partials
+};
+DecodePlan decode_plan(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_decode(const float* A, int64_t lda, const float* W, int64_t ldw, float* C,
+                              int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace,
+                              const DecodePlan& plan, uint32_t* status, hipStream_t s);
+
+int64_t attn_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D);
+hipError_t launch_attn_decode(const int16_t* q, const float* qs, const int16_t* k, const float* ks,
+                              const int16_t* v, const float* vs, float* out, int64_t B, int64_t T,
+                              int64_t Hq, int64_t Hkv, int64_t D, void* workspace, hipStream_t s);
+
+}  // namespace heal

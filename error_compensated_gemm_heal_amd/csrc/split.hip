@@ -1,0 +1,154 @@
+// Operand split into the dual-FP16 pair x ~= hi + lo / 2^10.
+//
+// HEAL paper, section 3, "Mitigating GEMM Truncation via FP16 Promotion and
+// Algebraic Compensation": the FP32 input is decomposed into an FP16 value
+// plus an FP16 residual shifted by 2^10, so that 16-bit matrix units can
+// evaluate the product.  Two kernels:
+//  * split_kernel: plain elementwise planes (hi[], lo[]), bit-exact.
+//  * pack kernels: the same split written straight into the padded,
+//    hi/lo-interleaved layout the prefill GEMM streams (one 128-byte line per
+//    row and 32-wide k block), so the GEMM needs no bounds checks.
+// Both are HBM-bound: 4 bytes read and 4 bytes written per element.
+#include "heal_internal.h"
+
+namespace heal {
+
+__global__ __launch_bounds__(256) void split_kernel(const float4* __restrict__ X, int64_t n,
+                                                    uint2* __restrict__ hi, uint2* __restrict__ lo,
+                                                    uint32_t* __restrict__ status) {
+    const int64_t n4 = n >> 2;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    bool bad = false;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        float4 x = X[i];
+        _Float16 h0, h1, h2, h3, l0, l1, l2, l3;
+        split_one(x.x, h0, l0);
+        split_one(x.y, h1, l1);
+        split_one(x.z, h2, l2);
+        split_one(x.w, h3, l3);
+        bad |= f16_out_of_range4(x);
+        hi[i] = make_uint2(f16_bits(h0) | ((uint32_t)f16_bits(h1) << 16),
+                           f16_bits(h2) | ((uint32_t)f16_bits(h3) << 16));
+        lo[i] = make_uint2(f16_bits(l0) | ((uint32_t)f16_bits(l1) << 16),
+                           f16_bits(l2) | ((uint32_t)f16_bits(l3) << 16));
+    }
+    // ragged tail (n % 4 elements), one thread each
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < (n & 3)) {
+        const float* Xs = reinterpret_cast<const float*>(X);
+        int64_t j = (n4 << 2) + t;
+        _Float16 h, l;
+        split_one(Xs[j], h, l);
+        bad |= f16_out_of_range(Xs[j]);
+        reinterpret_cast<uint16_t*>(hi)[j] = f16_bits(h);
+        reinterpret_cast<uint16_t*>(lo)[j] = f16_bits(l);
+    }
+    if (bad && status) atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
+}
+
+hipError_t launch_split(const float* X, int64_t n, uint16_t* hi, uint16_t* lo, uint32_t* status,
+                        hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    int64_t n4 = n >> 2;
+    int64_t blocks = (std::max<int64_t>(n4, 4) + 255) / 256;
+    if (blocks > 256 * 32) blocks = 256 * 32;
+    hipLaunchKernelGGL(split_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<const float4*>(X), n, reinterpret_cast<uint2*>(hi),
+                       reinterpret_cast<uint2*>(lo), status);
+    return hipGetLastError();
+}
+
+// Packed layout writer, source rows contiguous in k ([rows, K], ld).
+// One thread per (row, 4 consecutive k); the grid covers the padded extent
+// so the zero padding is written too.
+template <bool VEC>
+__global__ __launch_bounds__(256) void pack_rowmajor_kernel(const float* __restrict__ src, int64_t ld,
+                                                            int64_t rows, int64_t K, int64_t Kp,
+                                                            int64_t rows_p, uint16_t* __restrict__ out,
+                                                            uint32_t* __restrict__ status) {
+    const int64_t kq = Kp >> 2;  // 4-wide groups per padded row
+    const int64_t total = rows_p * kq;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    bool bad = false;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t r = i / kq;
+        const int64_t k = (i - r * kq) << 2;
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+        if (r < rows) {
+            const float* p = src + r * ld + k;
+            if (VEC && k + 4 <= K) {
+                float4 v = *reinterpret_cast<const float4*>(p);
+                x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+            } else {
+                for (int j = 0; j < 4; ++j)
+                    if (k + j < K) x[j] = p[j];
+            }
+        }
+        uint16_t h[4], l[4];
+        for (int j = 0; j < 4; ++j) {
+            _Float16 hh, ll;
+            split_one(x[j], hh, ll);
+            bad |= f16_out_of_range(x[j]);
+            h[j] = f16_bits(hh);
+            l[j] = f16_bits(ll);
+        }
+        uint16_t* o = out + r * (Kp * 2) + (k / kPackK) * (2 * kPackK) + (k % kPackK);
+        *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+        *reinterpret_cast<uint2*>(o + kPackK) =
+            make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+    }
+    if (bad && status) atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
+}
+
+// Packed layout writer for a source stored [K, rows] (ld >= rows): the packed
+// operand is the transpose.  Threads run along the source row (the packed
+// row index) so reads are coalesced; each thread packs 4 consecutive k.
+__global__ __launch_bounds__(256) void pack_colmajor_kernel(const float* __restrict__ src, int64_t ld,
+                                                            int64_t rows, int64_t K, int64_t Kp,
+                                                            int64_t rows_p, uint16_t* __restrict__ out,
+                                                            uint32_t* __restrict__ status) {
+    const int64_t kq = Kp >> 2;
+    const int64_t total = rows_p * kq;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    bool bad = false;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t kg = i / rows_p;
+        const int64_t r = i - kg * rows_p;
+        const int64_t k = kg << 2;
+        uint16_t h[4], l[4];
+        for (int j = 0; j < 4; ++j) {
+            float x = (r < rows && k + j < K) ? src[(k + j) * ld + r] : 0.f;
+            _Float16 hh, ll;
+            split_one(x, hh, ll);
+            bad |= f16_out_of_range(x);
+            h[j] = f16_bits(hh);
+            l[j] = f16_bits(ll);
+        }
+        uint16_t* o = out + r * (Kp * 2) + (k / kPackK) * (2 * kPackK) + (k % kPackK);
+        *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+        *reinterpret_cast<uint2*>(o + kPackK) =
+            make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+    }
+    if (bad && status) atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
+}
+
+hipError_t launch_pack(const float* src, int64_t ld, int64_t rows, int64_t K, int kn, void* packed,
+                       uint32_t* status, hipStream_t s) {
+    const int64_t Kp = pack_kp(K), rows_p = pack_rows(rows);
+    const int64_t total = rows_p * (Kp >> 2);
+    if (total == 0) return hipSuccess;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 256 * 64) blocks = 256 * 64;
+    if (kn)
+        hipLaunchKernelGGL(pack_colmajor_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, ld, rows,
+                           K, Kp, rows_p, static_cast<uint16_t*>(packed), status);
+    else if ((reinterpret_cast<uintptr_t>(src) & 15) == 0 && (ld & 3) == 0)
+        hipLaunchKernelGGL(pack_rowmajor_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, src, ld, rows,
+                           K, Kp, rows_p, static_cast<uint16_t*>(packed), status);
+    else
+        hipLaunchKernelGGL(pack_rowmajor_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, src, ld, rows,
+                           K, Kp, rows_p, static_cast<uint16_t*>(packed), status);
+    return hipGetLastError();
+}
+
+}  // namespace heal

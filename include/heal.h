@@ -1,0 +1,216 @@
+/*
+ * heal.h -- C ABI of the HEAL hot path on AMD Instinct MI355X (gfx950).
+ *
+ * HEAL ("Hybrid Error ALleviation") comes from the paper "Demystifying
+ * Numerical Instability in LLM Inference: Achieving Reproducible Inference
+ * for Mission-Critical Tasks with HEAL" (arXiv 2606.21023).  Citations
+ * below name its sections and paragraph titles:
+ *   [INT16]  section 3, "Mitigating QKV Truncation Error via INT16 Quantization"
+ *   [GEMM]   section 3, "Mitigating GEMM Truncation via FP16 Promotion and
+ *            Algebraic Compensation"
+ *
+ * The library gives FP32-grade linear-layer products without an FP32
+ * pipeline, and FP32-grade attention operands without doubling the KV cache
+ * (section 1, "Key Insight"; section 3 opening).
+ *
+ * Conventions shared by every call
+ *  - Pointers named as device pointers are device memory owned by the caller.
+ *    The library never allocates, frees or synchronizes.  Scratch memory is
+ *    the caller's `workspace`, sized by the matching *_workspace call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Each call enqueues its kernels on that stream and returns at once.
+ *  - Matrices are row-major.  Leading dimensions (ld*) count elements.
+ *  - Arguments are validated on the host before any HIP call.  A failed check
+ *    returns its code and touches no device state.  A dimension of 0 is
+ *    valid and makes the call a no-op, except where a call says otherwise.
+ *  - Conditions that depend on the data never fail a call.  They set bits in
+ *    an optional device status word (HEAL_FLAG_*) with an atomic OR.
+ *  - NaN and Inf inputs are outside the numerical contract.  They never
+ *    crash a call, and their results follow IEEE-754.
+ *  - Calls are thread-safe.  Concurrent calls must use distinct output and
+ *    workspace buffers, or the calls race.
+ */
+#ifndef HEAL_H
+#define HEAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum heal_status {
+    HEAL_OK = 0,
+    HEAL_ERR_NULL = 1,        /* a required pointer is NULL                              */
+    HEAL_ERR_SHAPE = 2,       /* a dimension is negative or outside the supported range  */
+    HEAL_ERR_STRIDE = 3,      /* a leading dimension is smaller than its row length      */
+    HEAL_ERR_ALIGN = 4,       /* a pointer or leading dimension breaks required alignment */
+    HEAL_ERR_UNSUPPORTED = 5, /* unknown flag bits or an unsupported combination         */
+    HEAL_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the *_workspace size     */
+    HEAL_ERR_HIP = 7          /* the HIP runtime rejected a kernel launch                */
+} heal_status;
+
+/* Flags of heal_gemm_f32c / heal_pack_w. */
+enum {
+    HEAL_W_NK = 0u,     /* W is fp32 [N, K] (a linear layer's weight, B = W^T)          */
+    HEAL_W_KN = 1u,     /* W is fp32 [K, N] (B = W)                                     */
+    HEAL_W_PACKED = 2u  /* W is a buffer written by heal_pack_w (ldw and layout ignored) */
+};
+
+/* Bits of the optional device status word. */
+enum {
+    HEAL_FLAG_F16_RANGE = 1u  /* an operand had |x| >= 65520: its fp16 high part is inf */
+};
+
+/* Formats of heal_kv_dequant_i16. */
+enum {
+    HEAL_DQ_F32 = 0,   /* out: fp32 values fl(q * s)                                  */
+    HEAL_DQ_F16X2 = 1  /* out: fp16 hi plane, out_lo: fp16 lo plane, q = hi + lo/2^10 */
+};
+
+/* Text for a status code (static storage, never NULL). */
+const char* heal_status_str(heal_status s);
+
+/* Library version, (major << 16) | minor. */
+int heal_version(void);
+
+/* ------------------------------------------------------------------------
+ * heal_split_f32 -- operand split into a dual-FP16 pair.   [GEMM], [INT16]
+ *
+ * For each of the n fp32 values x:
+ *   hi = fp16(x)                      round to nearest even, subnormals kept
+ *   lo = fp16((x - hi) * 2^10)        the residual is exact in fp32
+ * so that x ~= hi + lo / 2^10, with |x - (hi + lo/2^10)| <= 2^-22|x| + 2^-35
+ * for |x| < 65504.
+ *   X      device, n fp32 values, 16-byte aligned
+ *   hi, lo device, n fp16 bit patterns each, 8-byte aligned
+ *   dev_status  device, nullable.  HEAL_FLAG_F16_RANGE is set when some
+ *          |x| >= 65520 (hi is then inf, lo is -inf/+inf/NaN per IEEE).
+ * Errors: NULL X/hi/lo (when n > 0), n < 0, misalignment.
+ * ------------------------------------------------------------------------ */
+heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo,
+                           uint32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------
+ * heal_gemm_f32c -- FP32-accurate GEMM by algebraic error compensation on
+ * 16-bit matrix cores.   [GEMM]
+ *
+ *   C[M,N] = A[M,K] . B[K,N]      B = W^T (HEAL_W_NK) or B = W (HEAL_W_KN)
+ *
+ * Both fp32 operands are split as in heal_split_f32.  The product expands to
+ *   C = A_hi.B_hi + 2^-10 (A_hi.B_lo + A_lo.B_hi)
+ * with the three 16-bit products on fp16 MFMA and fp32 accumulation in two
+ * accumulators, combined once in fp32.  The output stays fp32, so no
+ * downcast happens at the kernel boundary.  The lo.lo term (2^-20) is
+ * dropped.  Accuracy: normwise error max_ij |C - C_exact| / (|a_i| |b_j|)
+ * within 2x that of a naive FP32 GEMM and below 1e-5.  The summation order
+ * depends on (M, N, K) but not on the data.  For M <= 64 it also does not
+ * depend on M, so decode-sized results do not change with batch size.
+ *
+ *   A      device fp32, lda >= K, 4-byte aligned (rows that are 16-byte
+ *          aligned, lda % 4 == 0, take 16-byte vector loads)
+ *   W      device fp32: [N, K] with ldw >= K (NK) or [K, N] with ldw >= N
+ *          (KN), 4-byte aligned (16-byte aligned rows vectorize as for A).
+ *          With HEAL_W_PACKED it is a heal_pack_w buffer for the same
+ *          (N, K), 256-byte aligned.
+ *   C      device fp32 [M, N], ldc >= N.  C must not overlap A or W.
+ *   flags  one of HEAL_W_NK / HEAL_W_KN, optionally | HEAL_W_PACKED
+ *   workspace  device, >= heal_gemm_f32c_workspace(M, N, K, flags) bytes,
+ *          256-byte aligned (NULL allowed when that size is 0)
+ *   dev_status  device, nullable; HEAL_FLAG_F16_RANGE as in heal_split_f32.
+ * Limits: M, N, K < 2^31.  K == 0 writes zeros.
+ * ------------------------------------------------------------------------ */
+heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t ldw,
+                           float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                           uint32_t flags, void* workspace, size_t workspace_bytes,
+                           uint32_t* dev_status, void* stream);
+
+/* Workspace bytes heal_gemm_f32c needs for this shape and flags. */
+size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags);
+
+/* ------------------------------------------------------------------------
+ * heal_pack_w -- split a weight once into the GEMM's packed dual-FP16 form.
+ *  [GEMM]  Weights are fixed across calls, so their split can be done once
+ *  and reused (HEAL_W_PACKED).  The packed form is internal and opaque: each
+ *  output row n holds, for every 32-wide block of k, the 32 fp16 hi parts
+ *  then the 32 fp16 lo parts.  Rows are padded to a multiple of 256 and k to
+ *  a multiple of 32 with zeros.
+ *   W      as in heal_gemm_f32c (flags HEAL_W_NK or HEAL_W_KN), 4-byte aligned
+ *   packed device, >= heal_pack_w_bytes(N, K) bytes, 256-byte aligned
+ * ------------------------------------------------------------------------ */
+heal_status heal_pack_w(const float* W, int64_t ldw, int64_t N, int64_t K, uint32_t flags,
+                        void* packed, size_t packed_bytes, uint32_t* dev_status, void* stream);
+
+size_t heal_pack_w_bytes(int64_t N, int64_t K);
+
+/* ------------------------------------------------------------------------
+ * heal_qkv_quant_i16 -- INT16 symmetric absmax quantization.   [INT16]
+ *
+ * Q_INT16(X) = Round((2^15 - 1) X / max|X|), applied per row of D values
+ * (one row = one token of one head).  Per row:
+ *   M = max_d |x_d|
+ *   M == 0 :  s = 0, every code 0
+ *   else   :  s = fl(M / 32767),  q_d = rne( fl( fl(32767 * x_d) / M ) )
+ * using correctly rounded fp32 multiply and divide, then rounding half to
+ * even.  Codes lie in [-32767, 32767].  Domain: finite x with
+ * |x| <= 1.0e34 (above FLT_MAX / 32767 the product 32767 * x overflows; such
+ * rows are outside the contract like NaN and Inf).  The results are bit-exact: the same
+ * on every run and equal to the scalar CPU definition above.
+ *   X      device fp32 [rows, D] with ldx >= D.  16-byte aligned, ldx % 4 == 0.
+ *   codes  device int16 [rows, D] with ldq >= D.  8-byte aligned, ldq % 4 == 0.
+ *   scales device fp32 [rows], 4-byte aligned
+ * Limits: D % 4 == 0, 4 <= D <= 4096 (when rows > 0).
+ * ------------------------------------------------------------------------ */
+heal_status heal_qkv_quant_i16(const float* X, int64_t rows, int64_t D, int64_t ldx,
+                               int16_t* codes, int64_t ldq, float* scales, void* stream);
+
+/* ------------------------------------------------------------------------
+ * heal_kv_dequant_i16 -- INT16 dequantization.   [INT16]
+ *   fmt HEAL_DQ_F32:   out fp32 [rows, D], x^ = fl(q * s)  (out_lo unused)
+ *   fmt HEAL_DQ_F16X2: out / out_lo fp16 [rows, D] planes with
+ *          hi = fp16(q), lo = fp16((q - hi) * 2^10).  Both are exact for
+ *          every int16 code, so q = hi + lo / 2^10 holds exactly (the
+ *          pages' dual-FP16 unpack).  The scale is applied by the consumer.
+ *   codes  device int16 [rows, D], ldq >= D, 8-byte aligned, ldq % 4 == 0
+ *   scales device fp32 [rows] (may be NULL for HEAL_DQ_F16X2)
+ *   out    device, ldo >= D, 16-byte aligned (F32) / 8-byte (F16X2), ldo % 4 == 0
+ * Limits: D % 4 == 0, 4 <= D <= 4096 (when rows > 0).  Bit-exact.
+ * ------------------------------------------------------------------------ */
+heal_status heal_kv_dequant_i16(const int16_t* codes, int64_t rows, int64_t D, int64_t ldq,
+                                const float* scales, int fmt, void* out, void* out_lo,
+                                int64_t ldo, void* stream);
+
+/* ------------------------------------------------------------------------
+ * heal_attn_decode_i16 -- one decode step of grouped-query attention over
+ * INT16 Q/K/V, with the INT16 -> dual-FP16 unpack fused into the operand
+ * load.   [INT16]
+ *
+ *   o[b,h,:] = softmax_t( q~[b,h] . k~[b,t,g] / sqrt(D) ) . v~[b,t,g,:]
+ *   x~ = code * scale,  g = h / (Hq / Hkv)
+ *
+ * q.k uses the exact split of each code into fp16 hi + lo/2^10 and all four
+ * 16-bit products.  The scales are applied in fp32.  Softmax is fp32 with a
+ * running maximum.  For P.V, the scale of token t is folded into its fp32
+ * weight, which is split into fp16 hi/lo against V's exact hi/lo parts.
+ *   q  [B, Hq, D] int16, q_scale [B, Hq] fp32
+ *   k, v  [B, T, Hkv, D] int16 (the KV cache), k_scale, v_scale [B, T, Hkv]
+ *   out   [B, Hq, D] fp32
+ *   workspace  device, >= heal_attn_decode_workspace(B, T, Hq, Hkv, D)
+ *   bytes, 256-byte aligned.  All tensors dense, 16-byte aligned.
+ * Limits: D == 128, Hq % Hkv == 0, Hq / Hkv <= 8, T >= 1 when B*Hq > 0.
+ * ------------------------------------------------------------------------ */
+heal_status heal_attn_decode_i16(const int16_t* q, const float* q_scale,
+                                 const int16_t* k, const float* k_scale,
+                                 const int16_t* v, const float* v_scale,
+                                 float* out, int64_t B, int64_t T, int64_t Hq, int64_t Hkv,
+                                 int64_t D, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+size_t heal_attn_decode_workspace(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HEAL_H */

@@ -1,0 +1,147 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+* libheal.so loads and exports every entry point declared in include/heal.h;
+* the binding declares a signature for each of them;
+* argument validation returns the documented HEAL_ERR_* code before any HIP
+  call (pointers below are never dereferenced: every case fails validation or
+  is a documented no-op);
+* workspace-size queries are pure host arithmetic.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import error_compensated_gemm_heal_amd as heal
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "heal.h")
+
+OK, NULL, SHAPE, STRIDE, ALIGN, UNSUP, WS = 0, 1, 2, 3, 4, 5, 6
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced
+FAKE_ODD = ctypes.c_void_p(0x10004)    # 4-byte aligned only
+NULLP = None
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(heal_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported_and_bound():
+    L = heal.lib()
+    syms = declared_symbols()
+    assert len(syms) >= 11
+    for s in syms:
+        assert hasattr(L, s), s
+        assert s in heal.SIGNATURES, s
+
+
+def test_status_strings_and_version():
+    for code in range(8):
+        assert heal.heal_status_str(code).startswith("HEAL")
+    assert heal.heal_version() >> 16 == 1
+
+
+def test_split_validation():
+    L = heal.lib()
+    assert L.heal_split_f32(FAKE, -1, FAKE, FAKE, None, None) == SHAPE
+    assert L.heal_split_f32(NULLP, 0, NULLP, NULLP, None, None) == OK
+    assert L.heal_split_f32(NULLP, 8, FAKE, FAKE, None, None) == NULL
+    assert L.heal_split_f32(FAKE_ODD, 8, FAKE, FAKE, None, None) == ALIGN
+    assert L.heal_split_f32(FAKE, 8, ctypes.c_void_p(0x10002), FAKE, None, None) == ALIGN
+
+
+def _gemm(A=FAKE, lda=4096, W=FAKE, ldw=4096, C=FAKE, ldc=4096, M=8, N=4096, K=4096, flags=0, ws=FAKE,
+          wsb=1 << 30, st=None):
+    return heal.lib().heal_gemm_f32c(A, lda, W, ldw, C, ldc, M, N, K, flags, ws, wsb, st, None)
+
+
+def test_gemm_validation():
+    assert _gemm(M=-1) == SHAPE
+    assert _gemm(K=1 << 31) == SHAPE
+    assert _gemm(flags=8) == UNSUP
+    assert _gemm(M=0, A=None, W=None, C=None) == OK
+    assert _gemm(N=0, A=None, W=None, C=None) == OK
+    assert _gemm(C=None) == NULL
+    assert _gemm(ldc=4095) == STRIDE
+    assert _gemm(A=None) == NULL
+    assert _gemm(W=None) == NULL
+    assert _gemm(lda=4095) == STRIDE
+    assert _gemm(ldw=4095) == STRIDE
+    assert _gemm(flags=heal.HEAL_W_KN, N=8192, ldc=8192) == STRIDE   # KN needs ldw >= N
+    assert _gemm(A=ctypes.c_void_p(0x10002)) == ALIGN
+    assert _gemm(W=ctypes.c_void_p(0x10001)) == ALIGN
+    assert _gemm(flags=heal.HEAL_W_PACKED, W=ctypes.c_void_p(0x10010)) == ALIGN
+    assert heal.heal_gemm_f32c_workspace(8, 4096, 4096, 0) > 0     # split-K partials
+    assert _gemm(ws=None) == WS
+    assert _gemm(wsb=16) == WS
+    assert _gemm(ws=ctypes.c_void_p(0x10010)) == ALIGN
+    assert _gemm(st=ctypes.c_void_p(0x10002)) == ALIGN
+
+
+def test_gemm_workspace_sizes():
+    ws = heal.heal_gemm_f32c_workspace
+    assert ws(0, 64, 64, 0) == 0 and ws(8, 64, -1, 0) == 0
+    # decode path (M <= 64, fp32 NK weight): split-K partials only, fixed by (N, K)
+    for M in (1, 8, 32, 64):
+        b = ws(M, 4096, 4096, 0)
+        assert b % 256 == 0
+    assert ws(64, 4096, 4096, 0) >= 64 * 4096 * 4
+    # prefill path: packed A (rows padded to 256, k to 32, 4 bytes per element) + packed W
+    assert ws(2048, 4096, 14336, 0) == 2048 * 14336 * 4 + 4096 * 14336 * 4
+    assert ws(2048, 4096, 14336, heal.HEAL_W_PACKED) == 2048 * 14336 * 4
+    assert ws(65, 100, 33, 0) == 256 * 64 * 4 + 256 * 64 * 4
+    assert heal.heal_pack_w_bytes(100, 33) == 256 * 64 * 4
+
+
+def test_pack_validation():
+    L = heal.lib()
+    assert L.heal_pack_w(FAKE, 64, -1, 64, 0, FAKE, 1 << 30, None, None) == SHAPE
+    assert L.heal_pack_w(FAKE, 64, 64, 64, 4, FAKE, 1 << 30, None, None) == UNSUP
+    assert L.heal_pack_w(FAKE, 64, 0, 64, 0, None, 0, None, None) == OK
+    assert L.heal_pack_w(None, 64, 64, 64, 0, FAKE, 1 << 30, None, None) == NULL
+    assert L.heal_pack_w(FAKE, 32, 64, 64, 0, FAKE, 1 << 30, None, None) == STRIDE
+    assert L.heal_pack_w(FAKE, 64, 64, 64, 0, ctypes.c_void_p(0x10080), 1 << 30, None, None) == ALIGN
+    assert L.heal_pack_w(ctypes.c_void_p(0x10002), 64, 64, 64, 0, FAKE, 1 << 30, None, None) == ALIGN
+    assert L.heal_pack_w(FAKE, 64, 64, 64, 0, FAKE, 100, None, None) == WS
+
+
+def test_quant_dequant_validation():
+    L = heal.lib()
+    q = L.heal_qkv_quant_i16
+    assert q(FAKE, -1, 128, 128, FAKE, 128, FAKE, None) == SHAPE
+    assert q(None, 0, 128, 128, None, 128, None, None) == OK
+    for D in (0, 2, 6, 4100):
+        assert q(FAKE, 4, D, 4104, FAKE, 4104, FAKE, None) == SHAPE
+    assert q(None, 4, 128, 128, FAKE, 128, FAKE, None) == NULL
+    assert q(FAKE, 4, 128, 124, FAKE, 128, FAKE, None) == STRIDE
+    assert q(FAKE, 4, 128, 128, FAKE, 124, FAKE, None) == STRIDE
+    assert q(FAKE_ODD, 4, 128, 128, FAKE, 128, FAKE, None) == ALIGN
+    assert q(FAKE, 4, 128, 130, FAKE, 128, FAKE, None) == ALIGN
+    assert q(FAKE, 4, 128, 128, ctypes.c_void_p(0x10002), 128, FAKE, None) == ALIGN
+    d = L.heal_kv_dequant_i16
+    assert d(FAKE, 4, 128, 128, FAKE, 7, FAKE, None, 128, None) == UNSUP
+    assert d(FAKE, 4, 128, 128, None, heal.HEAL_DQ_F32, FAKE, None, 128, None) == NULL
+    assert d(FAKE, 4, 128, 128, None, heal.HEAL_DQ_F16X2, FAKE, None, 128, None) == NULL
+    assert d(FAKE, 4, 128, 128, FAKE, heal.HEAL_DQ_F32, FAKE_ODD, None, 128, None) == ALIGN
+    assert d(FAKE, 4, 128, 120, FAKE, heal.HEAL_DQ_F32, FAKE, None, 128, None) == STRIDE
+
+
+def _attn(B=2, T=16, Hq=8, Hkv=2, D=128, ws=FAKE, wsb=1 << 30, q=FAKE):
+    return heal.lib().heal_attn_decode_i16(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, T, Hq, Hkv, D, ws, wsb, None)
+
+
+def test_attention_validation():
+    assert _attn(B=-1) == SHAPE
+    assert _attn(B=0, q=None) == OK
+    assert _attn(Hkv=3) == SHAPE
+    assert _attn(T=0) == SHAPE
+    assert _attn(D=64) == UNSUP
+    assert _attn(Hq=18, Hkv=1) == UNSUP
+    assert _attn(q=None) == NULL
+    assert _attn(q=ctypes.c_void_p(0x10008)) == ALIGN
+    assert _attn(ws=None) == WS
+    assert _attn(wsb=8) == WS
+    assert heal.heal_attn_decode_workspace(16, 8192, 32, 8, 128) > 0

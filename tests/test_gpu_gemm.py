@@ -1,0 +1,145 @@
+"""GPU parity of the compensated GEMM against the CPU oracle.
+
+Tolerance (normwise, see tests/metrics.py): at most 2x the error of a naive
+FP32 GEMM against the binary64 reference, and at most 1e-5.  Exact cases
+(binary16-representable operands with exact partial sums) must match the
+binary64 reference bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import error_compensated_gemm_heal_amd as heal
+import heal_workloads as WL
+import oracle
+from metrics import gemm_normwise_error, gemm_tolerance
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _run(A, W, w_layout="nk", packed=False, C=None):
+    Ad = torch.from_numpy(A).to(DEV)
+    Wd = torch.from_numpy(W).to(DEV)
+    if packed:
+        Wd = heal.heal_pack_w(Wd, w_layout)
+    out = heal.heal_gemm_f32c(Ad, Wd, w_layout=w_layout, C=C)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check(A, W, w_layout="nk", packed=False, rows=None, label=""):
+    print(f"gemm {label} M={A.shape[0]} K={A.shape[1]} W={W.shape} {w_layout} packed={packed}", flush=True)
+    C = _run(A, W, w_layout, packed).cpu().numpy()
+    K = A.shape[1]
+    if rows is None:
+        C64 = oracle.gemm_f64(A, W, w_layout)
+        C32 = oracle.gemm_f32_naive(A, W, w_layout)
+        Cg = C
+    else:
+        C64 = oracle.gemm_f64_rows(A, W, rows, w_layout)
+        C32 = oracle.gemm_f32_naive_rows(A, W, rows, w_layout)
+        Cg = C[rows]
+    e_gpu = gemm_normwise_error(Cg, C64, A, W, w_layout, rows)
+    e_naive = gemm_normwise_error(C32, C64, A, W, w_layout, rows)
+    bar = gemm_tolerance(e_naive, K)
+    print(f"   e_gpu={e_gpu:.3e} e_naive={e_naive:.3e} ratio={e_gpu / max(e_naive, 1e-300):.3f}", flush=True)
+    assert np.all(np.isfinite(Cg))
+    assert e_gpu <= bar, (e_gpu, e_naive)
+    return C
+
+
+def test_gemm_smoke_case():
+    A, W = WL.smoke_gemm()
+    _check(A, W, label="smoke 16x256x256")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 7), (2, 33, 1), (17, 40, 31), (64, 100, 300), (65, 129, 33),
+                                   (300, 200, 100), (257, 300, 1000), (513, 257, 129)])
+@pytest.mark.parametrize("layout", ["nk", "kn"])
+def test_gemm_ragged_shapes(M, N, K, layout):
+    g = WL.rng(M * 7 + N * 3 + K)
+    A = WL.normal(g, (M, K))
+    W = WL.normal(g, (N, K) if layout == "nk" else (K, N), std=0.02)
+    _check(A, W, layout, label="ragged")
+
+
+@pytest.mark.parametrize("M", [1, 8, 64, 200])
+def test_gemm_packed_weight(M):
+    A, W = WL.decode_gemm(M, 1024, 384, seed=77 + M)
+    _check(A, W, "nk", packed=True, label="packed")
+
+
+def test_gemm_strided_operands():
+    g = WL.rng(5)
+    A_big = WL.normal(g, (40, 520))
+    W_big = WL.normal(g, (72, 516), std=0.02)
+    A, W = A_big[:, :500], W_big[:, :500]          # lda = 520, ldw = 516
+    Ad = torch.from_numpy(A_big).to(DEV)[:, :500]
+    Wd = torch.from_numpy(W_big).to(DEV)[:, :500]
+    Cbig = torch.full((40, 80), float("nan"), device=DEV)
+    heal.heal_gemm_f32c(Ad, Wd, C=Cbig[:, :72])
+    torch.cuda.synchronize()
+    C = Cbig.cpu().numpy()
+    assert np.all(np.isnan(C[:, 72:]))            # nothing written outside the view
+    e = gemm_normwise_error(C[:, :72], oracle.gemm_f64(A, W), A, W)
+    e32 = gemm_normwise_error(oracle.gemm_f32_naive(A, W), oracle.gemm_f64(A, W), A, W)
+    assert e <= gemm_tolerance(e32, 500)
+
+
+@pytest.mark.parametrize("M,K", [(16, 256), (100, 256), (64, 40)])
+def test_gemm_exact_on_binary16_operands(M, K):
+    g = WL.rng(M + K)
+    A = (g.integers(-8, 9, size=(M, K)) / 8.0).astype(np.float32)
+    W = (g.integers(-8, 9, size=(96, K)) / 8.0).astype(np.float32)
+    C = _run(A, W).cpu().numpy()
+    assert np.array_equal(C.astype(np.float64), oracle.gemm_f64(A, W))
+
+
+def test_gemm_k_zero_and_empty():
+    A = torch.zeros((5, 0), device=DEV)
+    W = torch.zeros((7, 0), device=DEV)
+    C = torch.full((5, 7), 3.0, device=DEV)
+    heal.heal_gemm_f32c(A, W, C=C)
+    assert torch.all(C == 0).item()
+    out = heal.heal_gemm_f32c(torch.zeros((0, 8), device=DEV), torch.zeros((4, 8), device=DEV))
+    assert out.shape == (0, 4)
+
+
+def test_gemm_range_flag():
+    A = np.ones((4, 64), np.float32)
+    A[2, 5] = 70000.0
+    W = np.ones((8, 64), np.float32)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    heal.heal_gemm_f32c(torch.from_numpy(A).to(DEV), torch.from_numpy(W).to(DEV), dev_status=st)
+    assert st.item() == heal.HEAL_FLAG_F16_RANGE
+
+
+@pytest.mark.parametrize("K,N", WL.LLAMA3_8B_DECODE_KN)
+def test_gemm_decode_shapes_and_batch_invariance(K, N):
+    """Decode-shaped Llama-3-8B-like layers, M = 1, 8, 32, 64: tolerance on every M,
+    and row i of the product identical for every M (fixed K chunking)."""
+    A, W = WL.decode_gemm(64, K, N, seed=2000 + K + N)
+    Wd = torch.from_numpy(W).to(DEV)
+    Ad = torch.from_numpy(A).to(DEV)
+    outs = {}
+    for M in WL.DECODE_M:
+        outs[M] = heal.heal_gemm_f32c(Ad[:M], Wd).cpu().numpy()
+    for M in WL.DECODE_M:
+        assert np.array_equal(outs[M], outs[64][:M]), M
+    rows = np.array([0, 1, 7, 31, 63])
+    C64 = oracle.gemm_f64_rows(A, W, rows)
+    C32 = oracle.gemm_f32_naive_rows(A, W, rows)
+    e_gpu = gemm_normwise_error(outs[64][rows], C64, A, W, rows=rows)
+    e_naive = gemm_normwise_error(C32, C64, A, W, rows=rows)
+    print(f"decode K={K} N={N}: e_gpu={e_gpu:.3e} e_naive={e_naive:.3e}", flush=True)
+    assert e_gpu <= gemm_tolerance(e_naive, K)
+
+
+@pytest.mark.parametrize("K,N", WL.PREFILL_KN)
+def test_gemm_prefill_full_size_sampled_rows(K, N):
+    """Prefill shape M = 2048 with massive-activation channels, packed weight as
+    the benchmark times it; 24 sampled rows against the oracle."""
+    A, W = WL.prefill_gemm(WL.PREFILL_M, K, N, seed=3000 + K)
+    rows = np.sort(WL.rng(K).choice(WL.PREFILL_M, size=24, replace=False))
+    _check(A, W, "nk", packed=True, rows=rows, label="prefill")
