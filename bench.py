@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark of the HEAL hot path on one MI355X.
+
+One step is one pass over every step of the path, each on its synthetic
+workload (inputs resident in HBM before timing starts):
+
+  split    activation split of the two prefill GEMMs (fp32 -> packed fp16 hi/lo)
+  prefill  compensated GEMM, M=2048 tokens, (K,N) = (4096,14336) and (14336,4096),
+           weights split once beforehand (as deployed: weights are fixed)
+  decode   16 compensated GEMMs of a Llama-3-8B-like layer: M = 1, 8, 32, 64
+           x (K,N) in {(4096,4096), (4096,1024), (4096,14336), (14336,4096)},
+           fp32 weights streamed from HBM (M-outer order, so consecutive calls
+           touch different weights and the 256 MB MALL cannot serve repeats)
+  quant    INT16 quant of a Qwen3-8B-like layer's Q/K/V: 32 x 2048 tokens,
+           32 + 8 + 8 heads of 128 (one [65536, 48, 128] launch)
+  dequant  INT16 -> fp32 dequant of the same codes
+  attn     decode attention over the INT16 KV cache: batch 16, context 8192,
+           32 query / 8 KV heads, D = 128
+
+Output: one JSON line.  `value` is the metric's first half, FP32-accurate GEMM
+TFLOP/s on the prefill workload (useful flops 2MNK over the time of split +
+GEMM); `quant_GBps` is its second half.  `roofline` is the prefill GEMM kernel
+against the 16-bit MFMA peak (3 fp16 products per useful multiply-add).
+`cpu_baseline` is the CPU oracle timed on host cores on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP32-accurate GEMM TFLOP/s (% of 16-bit MFMA peak); INT16 QKV quant GB/s"
+PEAK_MFMA16_TFLOPS = 2516.6      # MI355X dense fp16/bf16 matrix peak
+PEAK_HBM_GBPS = 8000.0           # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_prefill_kernel_traffic.json")
+PREFILL_SRC = os.path.join(ROOT, "error_compensated_gemm_heal_amd", "csrc", "gemm_prefill.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def build_workload(rows_sel):
+    import torch
+    import error_compensated_gemm_heal_amd as heal
+    import heal_workloads as WL
+
+    dev = "cuda:0"
+    W = {}
+    t0 = time.time()
+
+    if "split" in rows_sel or "prefill" in rows_sel:
+        pre = []
+        for i, (K, N) in enumerate(WL.PREFILL_KN):
+            A, Wt = WL.prefill_gemm(WL.PREFILL_M, K, N, seed=3000 + i)
+            Ad = torch.from_numpy(A).to(dev)
+            Wp = heal.heal_pack_w(torch.from_numpy(Wt).to(dev))      # one-time weight split
+            Ap = heal.heal_pack_w(Ad)                                  # output buffer of the split row
+            C = torch.empty((WL.PREFILL_M, N), dtype=torch.float32, device=dev)
+            pre.append(dict(M=WL.PREFILL_M, K=K, N=N, A=Ad, Ap=Ap, Wp=Wp, C=C))
+            del A, Wt
+        W["prefill"] = pre
+        log(f"[bench] prefill inputs ready ({time.time() - t0:.1f}s)")
+
+    if "decode" in rows_sel:
+        weights = {}
+        acts = {}
+        for i, (K, N) in enumerate(WL.LLAMA3_8B_DECODE_KN):
+            A, Wt = WL.decode_gemm(64, K, N, seed=2000 + i)
+            weights[(K, N)] = torch.from_numpy(Wt).to(dev)
+            acts[(K, N)] = torch.from_numpy(A).to(dev)
+        calls = []
+        for M in WL.DECODE_M:
+            for (K, N) in WL.LLAMA3_8B_DECODE_KN:
+                Wd = weights[(K, N)]
+                ws_bytes = heal.heal_gemm_f32c_workspace(M, N, K, 0)
+                ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+                C = torch.empty((M, N), dtype=torch.float32, device=dev)
+                calls.append(dict(M=M, K=K, N=N, A=acts[(K, N)][:M], W=Wd, C=C, ws=ws))
+        W["decode"] = calls
+        log(f"[bench] decode inputs ready ({time.time() - t0:.1f}s)")
+
+    if "quant" in rows_sel or "dequant" in rows_sel:
+        tokens = 32 * 2048
+        Q, K_, V = WL.qkv(tokens, 32, 8, 128, seed=4000)
+        X = torch.empty((tokens, 48, 128), dtype=torch.float32, device=dev)
+        X[:, :32] = torch.from_numpy(Q).to(dev)
+        X[:, 32:40] = torch.from_numpy(K_).to(dev)
+        X[:, 40:] = torch.from_numpy(V).to(dev)
+        del Q, K_, V
+        codes = torch.empty(X.shape, dtype=torch.int16, device=dev)
+        scales = torch.empty(X.shape[:-1], dtype=torch.float32, device=dev)
+        deq = torch.empty(X.shape, dtype=torch.float32, device=dev)
+        heal.heal_qkv_quant_i16(X, codes, scales)
+        W["quant"] = dict(X=X, codes=codes, scales=scales, deq=deq, n=X.numel(), rows=X.numel() // 128)
+        log(f"[bench] quant inputs ready ({time.time() - t0:.1f}s)")
+
+    if "attn" in rows_sel:
+        B, T, Hq, Hkv, D = 16, 8192, 32, 8, 128
+        qf, kf, vf = WL.attention_fp32(B, T, Hq, Hkv, D, seed=5000)
+        q, qs = heal.heal_qkv_quant_i16(torch.from_numpy(qf).to(dev))
+        k, ks = heal.heal_qkv_quant_i16(torch.from_numpy(kf).to(dev))
+        v, vs = heal.heal_qkv_quant_i16(torch.from_numpy(vf).to(dev))
+        del qf, kf, vf
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        ws = torch.empty(heal.heal_attn_decode_workspace(B, T, Hq, Hkv, D), dtype=torch.uint8, device=dev)
+        W["attn"] = dict(args=(q, qs, k, ks, v, vs), out=out, ws=ws, B=B, T=T, Hq=Hq, Hkv=Hkv, D=D)
+        log(f"[bench] attention inputs ready ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+    return W
+
+
+def make_rows(W):
+    """(name, launch function, work, unit) for each row present in W."""
+    import error_compensated_gemm_heal_amd as heal
+    rows = []
+    if "prefill" in W:
+        pre = W["prefill"]
+
+        def run_split():
+            for p in pre:
+                heal.heal_pack_w(p["A"], out=p["Ap"])
+
+        def run_prefill():
+            for p in pre:
+                heal.heal_gemm_f32c(p["Ap"], p["Wp"], C=p["C"])
+
+        split_bytes = sum(p["M"] * p["K"] * 8 for p in pre)          # 4 B in + 2 x 2 B out per element
+        useful = sum(2.0 * p["M"] * p["N"] * p["K"] for p in pre)
+        rows.append(("split", run_split, split_bytes, "B"))
+        rows.append(("prefill", run_prefill, useful, "flop"))
+    if "decode" in W:
+        calls = W["decode"]
+
+        def run_decode():
+            for c in calls:
+                heal.heal_gemm_f32c(c["A"], c["W"], C=c["C"], workspace=c["ws"])
+
+        dbytes = sum(4 * (c["K"] * c["N"] + c["M"] * c["K"] + c["M"] * c["N"]) for c in calls)
+        rows.append(("decode", run_decode, dbytes, "B"))
+    if "quant" in W:
+        q = W["quant"]
+        qbytes = q["n"] * (4 + 2) + q["rows"] * 4
+        rows.append(("quant", lambda: heal.heal_qkv_quant_i16(q["X"], q["codes"], q["scales"]), qbytes, "B"))
+        rows.append(("dequant", lambda: heal.heal_kv_dequant_i16(q["codes"], q["scales"], "f32", out=q["deq"]),
+                     qbytes, "B"))
+    if "attn" in W:
+        a = W["attn"]
+        B, T, Hq, Hkv, D = a["B"], a["T"], a["Hq"], a["Hkv"], a["D"]
+        abytes = 2 * B * T * Hkv * D * 2 + 2 * B * T * Hkv * 4 + B * Hq * D * 2 + B * Hq * 4 + B * Hq * D * 4
+        rows.append(("attn", lambda: heal.heal_attn_decode_i16(*a["args"], out=a["out"], workspace=a["ws"]),
+                     abytes, "B"))
+    return rows
+
+
+def cpu_baseline(seconds):
+    """The oracle's FP64 GEMM, as it stands, on a row sample of the prefill shape."""
+    import numpy as np
+    import heal_workloads as WL
+    import oracle
+    K, N = WL.PREFILL_KN[0]
+    A, Wt = WL.prefill_gemm(WL.PREFILL_M, K, N, seed=3000)
+    nth = oracle.num_threads()
+    probe = np.arange(nth, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.gemm_f64_rows(A, Wt, probe)
+    dt = time.perf_counter() - t0
+    # dt covers nth rows: scale the sample to about `seconds` of CPU work (whole multiples of nth)
+    nrows = int(max(nth, min(WL.PREFILL_M, round(seconds / max(dt, 1e-6)) * nth)))
+    rows = np.arange(nrows, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.gemm_f64_rows(A, Wt, rows)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * nrows * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nth, "kind": "oracle",
+            "sample": f"FP64-accumulated GEMM (the oracle) on {nrows} of the 2048 rows of the "
+                      f"M=2048, K={K}, N={N} prefill shape; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--rows", default="split,prefill,decode,quant,dequant,attn",
+                    help="comma-separated subset of rows to run (profiling)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
+                    help="only run a device copy of this many MiB (counter calibration) and exit")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}, WORLD_SIZE {world}): the HEAL hot "
+              "path here is a single-GPU library; how it would shard is described in DESIGN.md.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import error_compensated_gemm_heal_amd as heal
+    heal.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 3}))
+        return
+
+    sel = set(args.rows.split(","))
+    W = build_workload(sel)
+    rows = [r for r in make_rows(W) if r[0] in sel]
+
+    def step(events=None):
+        for i, (name, fn, _, _) in enumerate(rows):
+            if events is not None:
+                events[i][0].record()
+            fn()
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in rows]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / max(args.steps, 1) * 1e3
+
+    per_row = {}
+    for i, (name, _, work, unit) in enumerate(rows):
+        ms = sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)) / max(args.steps, 1)
+        rate = work / (ms * 1e-3)
+        if unit == "flop":
+            per_row[name] = {"ms": ms, "TFLOPs": rate / 1e12}
+        else:
+            per_row[name] = {"ms": ms, "GBps": rate / 1e9, "hbm_frac": rate / 1e9 / PEAK_HBM_GBPS}
+
+    res = {"metric": METRIC, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "fp32 in/out; fp16 hi/lo MFMA products, fp32 accumulate; int16 codes",
+           "data": "synthetic (seeded; model-shaped, see heal_workloads.py)"}
+    cfg = {"workload": "HEAL hot path step: split + prefill GEMM (M=2048; K,N = 4096,14336 and 14336,4096), "
+                       "16 decode GEMMs (M=1,8,32,64 x Llama-3-8B q/o, k/v, gate/up, down), INT16 quant + dequant "
+                       "(32x2048 tokens, 32+8+8 heads x 128), INT16 decode attention (B=16, T=8192, 32/8 heads)",
+           "rows": sorted(sel)}
+    res["config"] = cfg
+    if "prefill" in per_row:
+        pre = W["prefill"]
+        useful = sum(2.0 * p["M"] * p["N"] * p["K"] for p in pre)
+        t_gemm = per_row["prefill"]["ms"] * 1e-3
+        t_split = per_row["split"]["ms"] * 1e-3 if "split" in per_row else 0.0
+        res["value"] = useful / (t_gemm + t_split) / 1e12
+        launches = len(pre)
+        mfma_flops_per_launch = 3.0 * useful / launches
+        avg_launch = t_gemm / launches
+        achieved = mfma_flops_per_launch / avg_launch / 1e12
+        traffic = None
+        if os.path.exists(TRAFFIC_FILE):
+            tr = json.load(open(TRAFFIC_FILE))
+            if tr.get("source_sha") == source_sha(PREFILL_SRC):
+                traffic = tr.get("bytes_per_launch")
+        res["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": achieved / PEAK_MFMA16_TFLOPS, "traffic": traffic,
+                           "kernel": "gemm_prefill_kernel", "per_launch_mfma_flop": mfma_flops_per_launch,
+                           "avg_launch_ms": avg_launch * 1e3}
+        res["prefill_gemm_only_TFLOPs"] = useful / t_gemm / 1e12
+    else:
+        res["value"] = None
+    if "quant" in per_row:
+        res["quant_GBps"] = per_row["quant"]["GBps"]
+    res["rows"] = per_row
+
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

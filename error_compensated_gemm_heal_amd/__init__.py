@@ -14,15 +14,16 @@ import torch
 __all__ = [
     "HealError", "lib", "heal_status_str", "heal_version", "heal_split_f32", "heal_gemm_f32c",
     "heal_gemm_f32c_workspace", "heal_pack_w", "heal_pack_w_bytes", "heal_qkv_quant_i16",
-    "heal_kv_dequant_i16", "heal_attn_decode_i16", "heal_attn_decode_workspace", "PackedWeight",
-    "HEAL_W_NK", "HEAL_W_KN", "HEAL_W_PACKED", "HEAL_FLAG_F16_RANGE", "HEAL_DQ_F32", "HEAL_DQ_F16X2",
+    "heal_kv_dequant_i16", "heal_attn_decode_i16", "heal_attn_decode_workspace", "PackedOperand",
+    "PackedWeight", "HEAL_W_NK", "HEAL_W_KN", "HEAL_W_PACKED", "HEAL_A_PACKED", "HEAL_FLAG_F16_RANGE",
+    "HEAL_DQ_F32", "HEAL_DQ_F16X2",
     "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libheal.so")
 
 HEAL_OK = 0
-HEAL_W_NK, HEAL_W_KN, HEAL_W_PACKED = 0, 1, 2
+HEAL_W_NK, HEAL_W_KN, HEAL_W_PACKED, HEAL_A_PACKED = 0, 1, 2, 4
 HEAL_FLAG_F16_RANGE = 1
 HEAL_DQ_F32, HEAL_DQ_F16X2 = 0, 1
 
@@ -126,18 +127,26 @@ def heal_split_f32(X: torch.Tensor, hi=None, lo=None, dev_status=None):
 
 # ---- compensated GEMM ------------------------------------------------------------
 
-class PackedWeight:
-    """A weight split once into the GEMM's packed dual-FP16 form (opaque buffer)."""
+class PackedOperand:
+    """An operand of `rows` x K split once into the GEMM's packed dual-FP16 form
+    (opaque buffer): a weight (rows = N) or an activation (rows = M)."""
 
-    def __init__(self, buf: torch.Tensor, N: int, K: int):
-        self.buf, self.N, self.K = buf, N, K
+    def __init__(self, buf: torch.Tensor, rows: int, K: int):
+        self.buf, self.rows, self.K = buf, rows, K
+
+    @property
+    def N(self):
+        return self.rows
+
+
+PackedWeight = PackedOperand
 
 
 def heal_pack_w_bytes(N: int, K: int) -> int:
     return lib().heal_pack_w_bytes(N, K)
 
 
-def heal_pack_w(W: torch.Tensor, w_layout: str = "nk", dev_status=None) -> PackedWeight:
+def heal_pack_w(W: torch.Tensor, w_layout: str = "nk", dev_status=None, out=None) -> PackedOperand:
     _dev(W, "W", torch.float32)
     flags = HEAL_W_KN if w_layout == "kn" else HEAL_W_NK
     if w_layout == "kn":
@@ -146,25 +155,35 @@ def heal_pack_w(W: torch.Tensor, w_layout: str = "nk", dev_status=None) -> Packe
         N, K = W.shape
     ldw = _rowmajor_ld(W, "W")
     nbytes = heal_pack_w_bytes(N, K)
-    buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=W.device)
+    if out is None:
+        buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=W.device)
+    else:
+        buf = out.buf
+        if buf.numel() < nbytes:
+            raise ValueError("packed buffer too small")
     _check("heal_pack_w", lib().heal_pack_w(_ptr(W), ldw, N, K, flags, _ptr(buf), nbytes,
                                             _ptr(dev_status), _stream()))
-    return PackedWeight(buf, N, K)
+    return PackedOperand(buf, N, K)
 
 
 def heal_gemm_f32c_workspace(M: int, N: int, K: int, flags: int) -> int:
     return lib().heal_gemm_f32c_workspace(M, N, K, flags)
 
 
-def heal_gemm_f32c(A: torch.Tensor, W, w_layout: str = "nk", C=None, workspace=None, dev_status=None):
-    """C = A . B with B = W^T ('nk', W [N,K]) or B = W ('kn', W [K,N]), or W a PackedWeight."""
-    _dev(A, "A", torch.float32)
-    M, K = A.shape
-    lda = _rowmajor_ld(A, "A")
-    if isinstance(W, PackedWeight):
+def heal_gemm_f32c(A, W, w_layout: str = "nk", C=None, workspace=None, dev_status=None):
+    """C = A . B with B = W^T ('nk', W [N,K]) or B = W ('kn', W [K,N]).
+    A and/or W may be PackedOperand buffers from heal_pack_w."""
+    aflags = 0
+    if isinstance(A, PackedOperand):
+        M, K, lda, aptr, adev, aflags = A.rows, A.K, 0, _ptr(A.buf), A.buf.device, HEAL_A_PACKED
+    else:
+        _dev(A, "A", torch.float32)
+        M, K = A.shape
+        lda, aptr, adev = _rowmajor_ld(A, "A"), _ptr(A), A.device
+    if isinstance(W, PackedOperand):
         if W.K != K:
             raise ValueError("packed weight has a different K")
-        N, flags, wptr, ldw = W.N, HEAL_W_PACKED, _ptr(W.buf), 0
+        N, flags, wptr, ldw = W.rows, HEAL_W_PACKED, _ptr(W.buf), 0
     else:
         _dev(W, "W", torch.float32)
         if w_layout == "kn":
@@ -176,15 +195,16 @@ def heal_gemm_f32c(A: torch.Tensor, W, w_layout: str = "nk", C=None, workspace=N
         if K2 != K:
             raise ValueError("inner dimensions differ")
         wptr, ldw = _ptr(W), _rowmajor_ld(W, "W")
+    flags |= aflags
     if C is None:
-        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+        C = torch.empty((M, N), dtype=torch.float32, device=adev)
     ldc = _rowmajor_ld(C, "C") if M > 0 and N > 0 else N
     nbytes = heal_gemm_f32c_workspace(M, N, K, flags)
     if workspace is None:
-        workspace = _workspace(nbytes, A.device)
+        workspace = _workspace(nbytes, adev)
     elif workspace.numel() < nbytes:
         raise ValueError("workspace too small")
-    _check("heal_gemm_f32c", lib().heal_gemm_f32c(_ptr(A), lda, wptr, ldw, _ptr(C), ldc, M, N, K, flags,
+    _check("heal_gemm_f32c", lib().heal_gemm_f32c(aptr, lda, wptr, ldw, _ptr(C), ldc, M, N, K, flags,
                                                   _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                                   _ptr(dev_status), _stream()))
     return C
@@ -205,14 +225,14 @@ def heal_qkv_quant_i16(X: torch.Tensor, codes=None, scales=None):
     return codes, scales
 
 
-def heal_kv_dequant_i16(codes: torch.Tensor, scales=None, fmt: str = "f32"):
+def heal_kv_dequant_i16(codes: torch.Tensor, scales=None, fmt: str = "f32", out=None):
     """codes [..., D] int16 (+ scales [...]) -> fp32 values, or (hi, lo) fp16 planes for fmt='f16x2'."""
     _dev(codes, "codes", torch.int16)
     codes = codes.contiguous()
     D = codes.shape[-1]
     rows = codes.numel() // D if D else 0
     if fmt == "f32":
-        out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
+        out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device) if out is None else out
         _check("heal_kv_dequant_i16", lib().heal_kv_dequant_i16(_ptr(codes), rows, D, D, _ptr(scales), HEAL_DQ_F32,
                                                                 _ptr(out), None, D, _stream()))
         return out

@@ -18,7 +18,7 @@ heal_status hip_status(hipError_t e) { return e == hipSuccess ? HEAL_OK : HEAL_E
 // Path choice for heal_gemm_f32c.  The decode kernel streams an fp32 [N,K]
 // weight directly; every other case packs the operands for the prefill kernel.
 bool use_decode(int64_t M, uint32_t flags) {
-    return M <= 64 && !(flags & HEAL_W_PACKED) && (flags & HEAL_W_KN) == 0;
+    return M <= 64 && !(flags & (HEAL_W_PACKED | HEAL_A_PACKED)) && (flags & HEAL_W_KN) == 0;
 }
 
 __global__ void zero_rows_kernel(float* C, int64_t ldc, int64_t M, int64_t N) {
@@ -85,7 +85,7 @@ size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags)
         const DecodePlan p = decode_plan(M, N, K);
         return (size_t)(round256(p.a_bytes) + round256(p.p_bytes));
     }
-    int64_t b = round256(pack_bytes(M, K));
+    int64_t b = (flags & HEAL_A_PACKED) ? 0 : round256(pack_bytes(M, K));
     if (!(flags & HEAL_W_PACKED)) b += round256(pack_bytes(N, K));
     return (size_t)b;
 }
@@ -95,7 +95,7 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
                            void* workspace, size_t workspace_bytes, uint32_t* dev_status,
                            void* stream) {
     if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return HEAL_ERR_SHAPE;
-    if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_PACKED)) return HEAL_ERR_UNSUPPORTED;
+    if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_PACKED | HEAL_A_PACKED)) return HEAL_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return HEAL_OK;
     if (!C) return HEAL_ERR_NULL;
     if (ldc < N) return HEAL_ERR_STRIDE;
@@ -106,11 +106,13 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
         return hip_status(hipGetLastError());
     }
     if (!A || !W) return HEAL_ERR_NULL;
-    if (lda < K) return HEAL_ERR_STRIDE;
     const bool packed = flags & HEAL_W_PACKED;
+    const bool a_packed = flags & HEAL_A_PACKED;
     const bool kn = flags & HEAL_W_KN;
+    if (!a_packed && lda < K) return HEAL_ERR_STRIDE;
     if (!packed && ldw < (kn ? N : K)) return HEAL_ERR_STRIDE;
-    if (misaligned(A, 4) || misaligned(W, packed ? 256 : 4) || misaligned(C, 4) || misaligned(dev_status, 4))
+    if (misaligned(A, a_packed ? 256 : 4) || misaligned(W, packed ? 256 : 4) || misaligned(C, 4) ||
+        misaligned(dev_status, 4))
         return HEAL_ERR_ALIGN;
     const size_t need = heal_gemm_f32c_workspace(M, N, K, flags);
     if (need > 0) {
@@ -125,12 +127,17 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
                                              K, ws + round256(p.a_bytes), p, dev_status, s));
     }
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    void* apk = ws;
+    const void* apk = A;
     const void* bpk = W;
-    hipError_t e = launch_pack(A, lda, M, K, 0, apk, dev_status, s);
-    if (e != hipSuccess) return HEAL_ERR_HIP;
+    if (!a_packed) {
+        hipError_t e = launch_pack(A, lda, M, K, 0, ws, dev_status, s);
+        if (e != hipSuccess) return HEAL_ERR_HIP;
+        apk = ws;
+        ws += round256(pack_bytes(M, K));
+    }
     if (!packed) {
-        void* wpk = ws + round256(pack_bytes(M, K));
+        void* wpk = ws;
+        hipError_t e;
         e = launch_pack(static_cast<const float*>(W), ldw, N, K, kn ? 1 : 0, wpk, dev_status, s);
         if (e != hipSuccess) return HEAL_ERR_HIP;
         bpk = wpk;

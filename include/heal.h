@@ -55,7 +55,8 @@ typedef enum heal_status {
 enum {
     HEAL_W_NK = 0u,     /* W is fp32 [N, K] (a linear layer's weight, B = W^T)          */
     HEAL_W_KN = 1u,     /* W is fp32 [K, N] (B = W)                                     */
-    HEAL_W_PACKED = 2u  /* W is a buffer written by heal_pack_w (ldw and layout ignored) */
+    HEAL_W_PACKED = 2u, /* W is a buffer written by heal_pack_w (ldw and layout ignored) */
+    HEAL_A_PACKED = 4u  /* A is a buffer written by heal_pack_w for A's M rows (lda ignored) */
 };
 
 /* Bits of the optional device status word. */
@@ -115,7 +116,9 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  *          With HEAL_W_PACKED it is a heal_pack_w buffer for the same
  *          (N, K), 256-byte aligned.
  *   C      device fp32 [M, N], ldc >= N.  C must not overlap A or W.
- *   flags  one of HEAL_W_NK / HEAL_W_KN, optionally | HEAL_W_PACKED
+ *   flags  one of HEAL_W_NK / HEAL_W_KN, optionally | HEAL_W_PACKED and/or
+ *          | HEAL_A_PACKED (A then is heal_pack_w(A, lda, M, K, HEAL_W_NK)'s
+ *          buffer: an activation split once can feed several GEMMs)
  *   workspace  device, >= heal_gemm_f32c_workspace(M, N, K, flags) bytes,
  *          256-byte aligned (NULL allowed when that size is 0)
  *   dev_status  device, nullable; HEAL_FLAG_F16_RANGE as in heal_split_f32.
@@ -130,12 +133,13 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
 size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags);
 
 /* ------------------------------------------------------------------------
- * heal_pack_w -- split a weight once into the GEMM's packed dual-FP16 form.
+ * heal_pack_w -- split an operand once into the GEMM's packed dual-FP16 form.
  *  [GEMM]  Weights are fixed across calls, so their split can be done once
- *  and reused (HEAL_W_PACKED).  The packed form is internal and opaque: each
- *  output row n holds, for every 32-wide block of k, the 32 fp16 hi parts
- *  then the 32 fp16 lo parts.  Rows are padded to a multiple of 256 and k to
- *  a multiple of 32 with zeros.
+ *  and reused (HEAL_W_PACKED); an activation read by several GEMMs can be
+ *  split once as well (HEAL_A_PACKED, with N := M rows of A and HEAL_W_NK).
+ *  The packed form is internal and opaque: each row holds, for every 32-wide
+ *  block of k, the 32 fp16 hi parts then the 32 fp16 lo parts.  Rows are
+ *  padded to a multiple of 256 and k to a multiple of 32 with zeros.
  *   W      as in heal_gemm_f32c (flags HEAL_W_NK or HEAL_W_KN), 4-byte aligned
  *   packed device, >= heal_pack_w_bytes(N, K) bytes, 256-byte aligned
  * ------------------------------------------------------------------------ */

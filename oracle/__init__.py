@@ -47,8 +47,14 @@ def lib():
             fn.argtypes = argtypes
             fn.restype = None
         L.oracle_abi_version.restype = ctypes.c_int
+        L.oracle_num_threads.restype = ctypes.c_int
         _LIB = L
     return _LIB
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return lib().oracle_num_threads()
 
 
 def _ptr(a: np.ndarray):

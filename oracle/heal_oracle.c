@@ -19,6 +19,7 @@
  * Parity status of each function (what pins it) is stated at the function.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stddef.h>
 #include <string.h>
@@ -458,3 +459,6 @@ ORACLE_API void oracle_attn_decode_f32_naive(const int16_t* q, const float* qs,
 }
 
 ORACLE_API int oracle_abi_version(void) { return 1; }
+
+/* Threads the OpenMP loops above run on (for reporting CPU timings). */
+ORACLE_API int oracle_num_threads(void) { return omp_get_max_threads(); }

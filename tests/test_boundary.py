@@ -74,6 +74,8 @@ def test_gemm_validation():
     assert _gemm(A=ctypes.c_void_p(0x10002)) == ALIGN
     assert _gemm(W=ctypes.c_void_p(0x10001)) == ALIGN
     assert _gemm(flags=heal.HEAL_W_PACKED, W=ctypes.c_void_p(0x10010)) == ALIGN
+    assert _gemm(flags=heal.HEAL_A_PACKED, A=ctypes.c_void_p(0x10010)) == ALIGN
+    assert _gemm(flags=16) == UNSUP
     assert heal.heal_gemm_f32c_workspace(8, 4096, 4096, 0) > 0     # split-K partials
     assert _gemm(ws=None) == WS
     assert _gemm(wsb=16) == WS
@@ -92,6 +94,8 @@ def test_gemm_workspace_sizes():
     # prefill path: packed A (rows padded to 256, k to 32, 4 bytes per element) + packed W
     assert ws(2048, 4096, 14336, 0) == 2048 * 14336 * 4 + 4096 * 14336 * 4
     assert ws(2048, 4096, 14336, heal.HEAL_W_PACKED) == 2048 * 14336 * 4
+    assert ws(2048, 4096, 14336, heal.HEAL_W_PACKED | heal.HEAL_A_PACKED) == 0
+    assert ws(8, 4096, 4096, heal.HEAL_A_PACKED) == 4096 * 4096 * 4   # packed A -> prefill path
     assert ws(65, 100, 33, 0) == 256 * 64 * 4 + 256 * 64 * 4
     assert heal.heal_pack_w_bytes(100, 33) == 256 * 64 * 4
 

@@ -70,6 +70,27 @@ def test_gemm_packed_weight(M):
     _check(A, W, "nk", packed=True, label="packed")
 
 
+@pytest.mark.parametrize("M", [5, 300])
+def test_gemm_packed_activation_reused(M):
+    """One activation split once (HEAL_A_PACKED) feeding two GEMMs equals the unpacked calls."""
+    g = WL.rng(900 + M)
+    A = WL.normal(g, (M, 700))
+    W1 = WL.normal(g, (130, 700), std=0.02)
+    W2 = WL.normal(g, (64, 700), std=0.02)
+    Ad = torch.from_numpy(A).to(DEV)
+    Ap = heal.heal_pack_w(Ad)
+    for W in (W1, W2):
+        Wd = torch.from_numpy(W).to(DEV)
+        Wp = heal.heal_pack_w(Wd)
+        c1 = heal.heal_gemm_f32c(Ap, Wp).cpu().numpy()
+        c2 = heal.heal_gemm_f32c(Ap, Wd).cpu().numpy()
+        c3 = heal.heal_gemm_f32c(Ad, Wp).cpu().numpy()
+        assert np.array_equal(c1, c2) and np.array_equal(c1, c3)
+        e = gemm_normwise_error(c1, oracle.gemm_f64(A, W), A, W)
+        e32 = gemm_normwise_error(oracle.gemm_f32_naive(A, W), oracle.gemm_f64(A, W), A, W)
+        assert e <= gemm_tolerance(e32, 700)
+
+
 def test_gemm_strided_operands():
     g = WL.rng(5)
     A_big = WL.normal(g, (40, 520))
