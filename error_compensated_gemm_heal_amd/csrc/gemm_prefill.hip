@@ -12,13 +12,28 @@
 //  * operands arrive packed by the split kernels: per row, each 32-wide k
 //    block is one 128-byte line [32 hi | 32 lo] fp16, zero-padded to whole
 //    tiles, so the main loop has no bounds checks;
-//  * block tile 256 (M) x 128 (N) x 32 (K), 4 waves in a 2 x 2 grid of
-//    128 x 64 wave tiles, each made of 4 x 2 tiles of v_mfma_f32_32x32x16_f16;
-//  * two fp32 accumulator sets per wave tile (hi.hi and the correction sum),
-//    256 registers, combined once in the epilogue: C = hh + c * 2^-10;
-//  * k tiles staged global -> registers -> LDS with two LDS buffers (one
-//    barrier per k tile); LDS rows padded to 80 bytes so the 16-byte fragment
-//    reads of 16 consecutive rows hit distinct banks;
+//  * the 2^-10 of the correction terms is folded into the activation
+//    fragments in registers (A_hi 2^-10 and A_lo 2^-10, exact power-of-two
+//    fp16 scaling), so all three products accumulate into one fp32
+//    accumulator per output and the epilogue is a plain store;
+//  * block tile 256 x 256 x 32, 4 waves in a 2 x 2 grid of 128 x 128 wave
+//    tiles, each 4 x 4 tiles of v_mfma_f32_32x32x16_f16 (256 accumulator
+//    registers per wave); a wave issues 96 MFMAs per k tile for 32 16-byte
+//    LDS reads;
+//  * k tiles move HBM -> LDS by buffer loads that write LDS directly (16
+//    bytes per lane, no register staging) into two 64 KB stages;
+//  * software pipeline with one barrier per k tile, placed mid-tile: the
+//    MFMAs of k16 step 0 run while step 1's fragments are read; then the
+//    barrier (tile t+1 landed, stage t free); then the MFMAs of step 1 run
+//    while tile t+1's step-0 fragments are read and tile t+2's loads are
+//    issued into the freed stage, so neither LDS latency nor the loads sit on
+//    the MFMA critical path at tile boundaries;
+//  * LDS rows are the packed 128-byte lines with their eight 16-byte chunks
+//    XOR-swizzled by (row / 2) % 8, so the fragment reads of 16 consecutive
+//    rows hit distinct banks with no padding;
+//  * when the grid would fill at most half the chip, the k range is split in
+//    two and both halves add into a zeroed C with fp32 atomics; two addends
+//    commute exactly, so the result does not depend on their order;
 //  * block -> tile order keeps the blocks that share a B tile on one XCD
 //    (blocks are dealt to the 8 XCDs round-robin), so B is read from HBM once
 //    and re-served from that XCD's L2.
@@ -28,120 +43,188 @@ namespace heal {
 
 namespace {
 
-constexpr int BM = 256, BN = 128, BK = 32;
-constexpr int WM = 128, WN = 64;            // wave tile
+constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int WM = 128, WN = 128;           // wave tile
 constexpr int TM = WM / 32, TN = WN / 32;   // 32x32 MFMA tiles per wave
-constexpr int ROWB = 80;                    // LDS bytes per row per plane (64 data + 16 pad)
-constexpr int A_PLANE = BM * ROWB;          // bytes
-constexpr int B_PLANE = BN * ROWB;
-constexpr int STAGE = 2 * A_PLANE + 2 * B_PLANE;   // 61440
-constexpr int A_CHUNKS = BM * 8 / 256;     // 16-byte global chunks per thread per k tile (A)
-constexpr int B_CHUNKS = BN * 8 / 256;     // (B)
+constexpr int ROWB = 128;                   // LDS bytes per row: 32 hi + 32 lo fp16 (swizzled)
+constexpr int A_REGION = BM * ROWB;         // 32 KB
+constexpr int B_REGION = BN * ROWB;         // 32 KB
+constexpr int STAGE = A_REGION + B_REGION;  // 64 KB
+constexpr int NSTAGE = 2;
+constexpr int A_DMA = BM / 8 / 4;           // 1 KB (8-row) DMA blocks per wave per tile (A)
+constexpr int B_DMA = BN / 8 / 4;           // (B)
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void mfma32(const half8& a, const half8& b, floatx16& c) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// x * 2^-10 on 8 fp16 values (exact for normal results)
+__device__ __forceinline__ half8 scale_m10(const half8& x) {
+    return x * (_Float16)0.0009765625f;
+}
+
+template <bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_prefill_kernel(const uint4* __restrict__ Apk, const uint4* __restrict__ Bpk,
+void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned char* __restrict__ Bpk,
                          float* __restrict__ C, int64_t ldc, int M, int N, int Kp,
                          int tiles_m, int tiles_n) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-    // ---- XCD-aware tile order -------------------------------------------
-    const int nblk = tiles_m * tiles_n;
+    // ---- XCD-aware tile order (tm fastest, then tn, then the k half) -------
+    const int nblk = tiles_m * tiles_n * (SPLIT ? 2 : 1);
     int bid = blockIdx.x;
     if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
     const int tm = bid % tiles_m;
-    const int tn = bid / tiles_m;
+    const int tn = (bid / tiles_m) % tiles_n;
+    const int half_k = SPLIT ? bid / (tiles_m * tiles_n) : 0;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave index as a scalar: DMA destinations and offsets must be wave-uniform
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
+    const uint32_t rowbytes = (uint32_t)Kp * 4u;   // Kp hi + Kp lo fp16
+    const int nkt_all = Kp / BK;
+    const int kt_begin = SPLIT ? half_k * (nkt_all / 2) : 0;
+    const int kt_end = SPLIT ? (half_k ? nkt_all : nkt_all / 2) : nkt_all;
+    const int nkt = kt_end - kt_begin;
 
-    // Packed row stride in 16-byte chunks: Kp fp16 hi + Kp fp16 lo = Kp*4 bytes.
-    const int64_t row_chunks = (int64_t)Kp / 4;
-    const int nkt = Kp / BK;
+    // ---- DMA: wave w fills the 1 KB blocks b = w + 4 i (8 rows each) ------
+    // Lane L writes LDS row L/8, slot L%8 of its block; the slot holds chunk
+    // (L%8) ^ sw(row) with sw(row) = (row / 2) % 8.  b has the parity of w, so
+    // sw depends on the lane and the wave only.
+    const int drow = lane >> 3;
+    const int dsw = ((wave & 1) << 2) | (drow >> 1);
+    const uint32_t dma_voff = (uint32_t)drow * rowbytes + (uint32_t)((lane & 7) ^ dsw) * 16u;
+    const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(Apk + (int64_t)tm * BM * rowbytes, BM * rowbytes);
+    const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(Bpk + (int64_t)tn * BN * rowbytes, BN * rowbytes);
 
-    // ---- global -> register staging (one k tile) ---------------------------
-    // chunk c = tid + 256 i of a tile: row c / 8 (= tid / 8 + 32 i), piece c % 8
-    // (0..3 hi, 4..7 lo, 16 bytes each).  Chunk i sits 32 i rows below chunk 0,
-    // so one base pointer per operand plus uniform offsets addresses them all.
-    const int r0 = tid >> 3, p0 = tid & 7;
-    const uint4* a_src = Apk + ((int64_t)tm * BM + r0) * row_chunks + p0;
-    const uint4* b_src = Bpk + ((int64_t)tn * BN + r0) * row_chunks + p0;
-    const int a_dst = (p0 >> 2) * A_PLANE + r0 * ROWB + (p0 & 3) * 16;
-    const int b_dst = 2 * A_PLANE + (p0 >> 2) * B_PLANE + r0 * ROWB + (p0 & 3) * 16;
-    const int64_t rows32 = 32 * row_chunks;
-    u32x4 ra[A_CHUNKS], rb[B_CHUNKS];
-#define HEAL_GLOAD(kt)                                                                         \
-    do {                                                                                       \
-        const u32x4* pa = reinterpret_cast<const u32x4*>(a_src + (kt) * 8);                    \
-        const u32x4* pb = reinterpret_cast<const u32x4*>(b_src + (kt) * 8);                    \
-        _Pragma("unroll") for (int i = 0; i < A_CHUNKS; ++i) ra[i] = pa[i * rows32];           \
-        _Pragma("unroll") for (int i = 0; i < B_CHUNKS; ++i) rb[i] = pb[i * rows32];           \
+#define HEAL_DMA_TILE(kt_, stage_)                                                                    \
+    do {                                                                                              \
+        unsigned char* st_ = smem + (stage_) * STAGE;                                                 \
+        const uint32_t koff_ = (uint32_t)(kt_) * 128u;                                                \
+        _Pragma("unroll") for (int i = 0; i < A_DMA; ++i) {                                           \
+            const int b_ = wave + 4 * i;                                                              \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_ptr)(st_ + b_ * 1024), 16, dma_voff, \
+                                                     (uint32_t)(8 * b_) * rowbytes + koff_, 0, 0);   \
+        }                                                                                             \
+        _Pragma("unroll") for (int i = 0; i < B_DMA; ++i) {                                           \
+            const int b_ = wave + 4 * i;                                                              \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, (lds_ptr)(st_ + A_REGION + b_ * 1024), 16, \
+                                                     dma_voff, (uint32_t)(8 * b_) * rowbytes + koff_, 0, 0); \
+        }                                                                                             \
     } while (0)
-#define HEAL_SWRITE(buf)                                                                       \
-    do {                                                                                       \
-        unsigned char* base_ = smem + (buf) * STAGE;                                           \
-        _Pragma("unroll") for (int i = 0; i < A_CHUNKS; ++i)                                   \
-            *reinterpret_cast<u32x4*>(base_ + a_dst + i * 32 * ROWB) = ra[i];                  \
-        _Pragma("unroll") for (int i = 0; i < B_CHUNKS; ++i)                                   \
-            *reinterpret_cast<u32x4*>(base_ + b_dst + i * 32 * ROWB) = rb[i];                  \
-    } while (0)
 
-    floatx16 acc_hh[TM][TN], acc_c[TM][TN];
+    // ---- fragment reads: lane reads row (l % 32) of a 32-row tile, chunk
+    //      2 ks + l / 32 (hi) or 4 + 2 ks + l / 32 (lo), at its swizzled slot
+    const int sw = (lane >> 1) & 7;
+    const int a_row = (wm * WM + (lane & 31)) * ROWB;
+    const int b_row = A_REGION + (wn * WN + (lane & 31)) * ROWB;
+    int slot_off[2][2];   // [ks][hi/lo]
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) slot_off[ks][p] = ((4 * p + 2 * ks + (lane >> 5)) ^ sw) * 16;
+
+    floatx16 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) { acc_hh[i][j][e] = 0.f; acc_c[i][j][e] = 0.f; }
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    // fragment read offsets: lane reads row (l % 32) of a 32-row tile, k half (l / 32)
-    const int frag_off = (lane & 31) * ROWB + (lane >> 5) * 16;
-    const int a_frag = wm * WM * ROWB + frag_off;
-    const int b_frag = 2 * A_PLANE + wn * WN * ROWB + frag_off;
+    // fragments of one k16 step: ah/al (A hi, A lo), bh/bl (B hi, B lo)
+#define HEAL_FRAGS(ah_, al_, bh_, bl_, ks_)                                                              \
+    do {                                                                                                 \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                                 \
+            ah_[i] = *reinterpret_cast<const half8*>(base + a_row + i * 32 * ROWB + slot_off[ks_][0]);   \
+            al_[i] = *reinterpret_cast<const half8*>(base + a_row + i * 32 * ROWB + slot_off[ks_][1]);   \
+        }                                                                                                \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                                 \
+            bh_[j] = *reinterpret_cast<const half8*>(base + b_row + j * 32 * ROWB + slot_off[ks_][0]);   \
+            bl_[j] = *reinterpret_cast<const half8*>(base + b_row + j * 32 * ROWB + slot_off[ks_][1]);   \
+        }                                                                                                \
+    } while (0)
+    // the three products of one k16 step; each product sweeps all 16 output
+    // tiles before the next, so an accumulator is re-read 16 MFMAs later
+#define HEAL_MFMAS(ah_, al_, bh_, bl_)                                                                   \
+    do {                                                                                                 \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                   \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32(ah_[i], bh_[j], acc[i][j]);            \
+        half8 as_[TM];                                                                                   \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i) as_[i] = scale_m10(ah_[i]);                       \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                   \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32(as_[i], bl_[j], acc[i][j]);            \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i) as_[i] = scale_m10(al_[i]);                       \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                   \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32(as_[i], bh_[j], acc[i][j]);            \
+    } while (0)
 
-    HEAL_GLOAD(0);
-    HEAL_SWRITE(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nkt) HEAL_GLOAD(kt + 1);
-        const unsigned char* base = smem + buf * STAGE;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {           // two k16 steps per k tile
-            half8 ah[TM], al[TM], bh[TN], bl[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                ah[i] = *reinterpret_cast<const half8*>(base + a_frag + i * 32 * ROWB + ks * 32);
-                al[i] = *reinterpret_cast<const half8*>(base + a_frag + A_PLANE + i * 32 * ROWB + ks * 32);
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                bh[j] = *reinterpret_cast<const half8*>(base + b_frag + j * 32 * ROWB + ks * 32);
-                bl[j] = *reinterpret_cast<const half8*>(base + b_frag + B_PLANE + j * 32 * ROWB + ks * 32);
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    mfma32(ah[i], bh[j], acc_hh[i][j]);
-                    mfma32(ah[i], bl[j], acc_c[i][j]);
-                }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) mfma32(al[i], bh[j], acc_c[i][j]);
-        }
-        if (kt + 1 < nkt) HEAL_SWRITE(buf ^ 1);
-        __syncthreads();
+    // Pipeline, one barrier per k tile placed mid-tile:
+    //   phase 1 of tile t: MFMAs of k16 step 0 while step 1's fragments load;
+    //   sync: this wave's reads of stage t done, tile t+1's DMA landed, barrier;
+    //   phase 2: MFMAs of step 1 while tile t+1's step-0 fragments load and
+    //   tile t+2's DMA refills the stage tile t used.
+    half8 ah0[TM], al0[TM], bh0[TN], bl0[TN], ah1[TM], al1[TM], bh1[TN], bl1[TN];
+    HEAL_DMA_TILE(kt_begin, 0);
+    if (nkt > 1) {
+        HEAL_DMA_TILE(kt_begin + 1, 1);
+        __builtin_amdgcn_s_waitcnt(0x4F70);          // vmcnt(16) (high bits [15:14]): tile 0 landed
+    } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0)
     }
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    {
+        const unsigned char* base = smem;
+        HEAL_FRAGS(ah0, al0, bh0, bl0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- epilogue: one fp32 combination, bounds-checked store ---------------
+    for (int t = 0; t < nkt; ++t) {
+        {   // phase 1
+            const unsigned char* base = smem + (t & 1) * STAGE;
+            HEAL_FRAGS(ah1, al1, bh1, bl1, 1);
+            HEAL_MFMAS(ah0, al0, bh0, bl0);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // three MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (t + 1 < nkt) {   // sync (uniform across the block)
+            __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        {   // phase 2 (branch-free so the loads interleave with the MFMAs): near
+            // the end the tile indices clamp to the last tile, whose re-fetch
+            // writes bytes identical to the ones already in LDS
+            HEAL_DMA_TILE(kt_begin + min(t + 2, nkt - 1), t & 1);
+            const unsigned char* base = smem + (min(t + 1, nkt - 1) & 1) * STAGE;
+            HEAL_FRAGS(ah0, al0, bh0, bl0, 0);
+            HEAL_MFMAS(ah1, al1, bh1, bl1);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // three MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one DMA load
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // no LDS write of this block may land after it ends
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+#undef HEAL_FRAGS
+#undef HEAL_MFMAS
+#undef HEAL_DMA_TILE
+
+    // ---- epilogue: bounds-checked store (or atomic add of one k half) -------
     const int row0 = tm * BM + wm * WM + (lane >> 5) * 4;
     const int col0 = tn * BN + wn * WN + (lane & 31);
 #pragma unroll
@@ -153,11 +236,24 @@ void gemm_prefill_kernel(const uint4* __restrict__ Apk, const uint4* __restrict_
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int row = row0 + i * 32 + (e >> 2) * 8 + (e & 3);
-                if (row < M) C[(int64_t)row * ldc + col] = acc_hh[i][j][e] + acc_c[i][j][e] * 0.0009765625f;
+                if (row < M) {
+                    float* dst = C + (int64_t)row * ldc + col;
+                    if (SPLIT)
+                        unsafeAtomicAdd(dst, acc[i][j][e]);
+                    else
+                        *dst = acc[i][j][e];
+                }
             }
         }
-#undef HEAL_GLOAD
-#undef HEAL_SWRITE
+}
+
+__global__ void zero_c_kernel(float* C, int64_t ldc, int64_t M, int64_t N) {
+    const int64_t total = M * N;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t m = i / N;
+        C[m * ldc + (i - m * N)] = 0.0f;
+    }
 }
 
 }  // namespace
@@ -167,18 +263,33 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, float* C, int64
     if (M == 0 || N == 0) return hipSuccess;
     const int64_t Kp = pack_kp(K);
     if (Kp == 0) return hipErrorInvalidValue;  // K == 0 is handled by the caller
+    // one operand block must be addressable by a 32-bit buffer offset
+    if ((int64_t)BM * Kp * 4 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
+    // split the k range in two when the tiles fill at most half of the 256 CUs
+    const bool split = (int64_t)tiles_m * tiles_n <= 128 && Kp / BK >= 8;
     static bool attr_set = false;  // idempotent; racing first calls set the same value
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_prefill_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_prefill_kernel<false>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * STAGE);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_prefill_kernel<true>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * STAGE);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(gemm_prefill_kernel, dim3(tiles_m * tiles_n), dim3(256), 2 * STAGE, s,
-                       static_cast<const uint4*>(Apk), static_cast<const uint4*>(Bpk), C, ldc, (int)M,
-                       (int)N, (int)Kp, tiles_m, tiles_n);
+    const unsigned char* a = static_cast<const unsigned char*>(Apk);
+    const unsigned char* b = static_cast<const unsigned char*>(Bpk);
+    if (split) {
+        const unsigned zb = (unsigned)std::min<int64_t>((M * N + 255) / 256, 4096);
+        hipLaunchKernelGGL(zero_c_kernel, dim3(zb), dim3(256), 0, s, C, ldc, M, N);
+        hipLaunchKernelGGL(gemm_prefill_kernel<true>, dim3(tiles_m * tiles_n * 2), dim3(256), NSTAGE * STAGE, s,
+                           a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n);
+    } else {
+        hipLaunchKernelGGL(gemm_prefill_kernel<false>, dim3(tiles_m * tiles_n), dim3(256), NSTAGE * STAGE, s,
+                           a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n);
+    }
     return hipGetLastError();
 }
 

@@ -16,6 +16,14 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Buffer resource for raw buffer loads over [base, base + bytes): the address
+// is base + voffset (per lane, 32-bit) + soffset (wave-uniform), so a loop of
+// loads needs one VGPR per lane and keeps every other offset in scalars.
+// Loads past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // fp32 -> fp16 with round-to-nearest-even and fp16 subnormals kept (the
 // hardware conversion under the default rounding and denormal modes), and the
 // dual-FP16 residual lo = fp16((x - hi) * 2^10); x - hi is exact in fp32.
