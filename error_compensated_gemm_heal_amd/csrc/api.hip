@@ -188,7 +188,8 @@ heal_status heal_attn_decode_i16(const int16_t* q, const float* q_scale, const i
     if (B == 0 || Hq == 0) return HEAL_OK;
     if (Hkv == 0 || Hq % Hkv) return HEAL_ERR_SHAPE;
     if (T == 0) return HEAL_ERR_SHAPE;
-    if (D != 128 || Hq / Hkv > 8) return HEAL_ERR_UNSUPPORTED;
+    if (D != 128 || Hq / Hkv > 8 || T > 262144) return HEAL_ERR_UNSUPPORTED;
+    if (T * Hkv * D * 2 >= ((int64_t)1 << 32)) return HEAL_ERR_UNSUPPORTED;   // 32-bit offsets per batch
     if (!q || !q_scale || !k || !k_scale || !v || !v_scale || !out) return HEAL_ERR_NULL;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
         misaligned(q_scale, 4) || misaligned(k_scale, 4) || misaligned(v_scale, 4))

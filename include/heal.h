@@ -193,16 +193,19 @@ heal_status heal_kv_dequant_i16(const int16_t* codes, int64_t rows, int64_t D, i
  *   o[b,h,:] = softmax_t( q~[b,h] . k~[b,t,g] / sqrt(D) ) . v~[b,t,g,:]
  *   x~ = code * scale,  g = h / (Hq / Hkv)
  *
- * q.k uses the exact split of each code into fp16 hi + lo/2^10 and all four
- * 16-bit products.  The scales are applied in fp32.  Softmax is fp32 with a
- * running maximum.  For P.V, the scale of token t is folded into its fp32
- * weight, which is split into fp16 hi/lo against V's exact hi/lo parts.
+ * q.k uses an exact split of each code into two fp16 parts (64 (q >> 6)
+ * and q & 63) and all four 16-bit products.  The scales are applied in fp32.
+ * Softmax is fp32 with a running maximum.  For P.V, the scale of token t is
+ * folded into its fp32 weight, which is split into fp16 hi/lo against V's
+ * exact parts.
  *   q  [B, Hq, D] int16, q_scale [B, Hq] fp32
  *   k, v  [B, T, Hkv, D] int16 (the KV cache), k_scale, v_scale [B, T, Hkv]
  *   out   [B, Hq, D] fp32
  *   workspace  device, >= heal_attn_decode_workspace(B, T, Hq, Hkv, D)
  *   bytes, 256-byte aligned.  All tensors dense, 16-byte aligned.
- * Limits: D == 128, Hq % Hkv == 0, Hq / Hkv <= 8, T >= 1 when B*Hq > 0.
+ * Limits: D == 128, Hq % Hkv == 0, Hq / Hkv <= 8, 1 <= T <= 262144 and
+ * T * Hkv * D * 2 < 2^32 (one batch's K or V block is addressed with 32-bit
+ * byte offsets) when B*Hq > 0; otherwise HEAL_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------ */
 heal_status heal_attn_decode_i16(const int16_t* q, const float* q_scale,
                                  const int16_t* k, const float* k_scale,

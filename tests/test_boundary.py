@@ -144,6 +144,8 @@ def test_attention_validation():
     assert _attn(T=0) == SHAPE
     assert _attn(D=64) == UNSUP
     assert _attn(Hq=18, Hkv=1) == UNSUP
+    assert _attn(T=262145) == UNSUP
+    assert _attn(T=131072, Hq=128, Hkv=128) == UNSUP   # K block of one batch past 4 GiB
     assert _attn(q=None) == NULL
     assert _attn(q=ctypes.c_void_p(0x10008)) == ALIGN
     assert _attn(ws=None) == WS
