@@ -15,26 +15,28 @@
 // an exponent bias and one packed subtract): 2.5 instructions per code.
 // Every 16-bit product is exact in fp32.
 //
-// One wave owns one (batch b, KV head g, range of TW tokens):
+// One block of 4 waves owns one (batch b, KV head g, range of 256 tokens);
+// each wave takes 64 of them:
+//  * all loads are issued first: K straight into MFMA operand registers
+//    (lane = token, 8 consecutive d), V by direct-to-LDS loads into a
+//    wave-private 16 KB tile whose 16-byte chunks are XOR-swizzled by row;
 //  * scores as S^T = K . q^T on v_mfma_f32_16x16x32_f16.  The 16 rows are
-//    tokens; K goes from HBM straight into operand registers (lane = token,
-//    8 consecutive d), then is unpacked.  The 16 columns pack
-//    [64 q_hi of the G heads | q_lo of the G heads].  K_hi and K_lo have one
-//    accumulator each, and k.q = 64 (S_hi[c] + S_hi[G+c]) + S_lo[c] + S_lo[G+c];
-//  * fp32 online softmax per head in base 2 (log2 e folded into the score
-//    scale s_q s_k / sqrt(D), hardware exp2), rescaling the running output
-//    only when a head's maximum rises by more than 2^8;
+//    tokens; the 16 columns pack [64 q_hi of the G heads | q_lo of the G
+//    heads].  K_hi and K_lo have one accumulator each, and
+//    k.q = 64 (S_hi[c] + S_hi[G+c]) + S_lo[c] + S_lo[G+c];
+//  * softmax in base 2 (log2 e folded into the score scale s_q s_k / sqrt(D),
+//    hardware exp2) against the maximum over the wave's 64 tokens, taken
+//    before any product with V, so nothing is ever rescaled inside a wave;
 //  * P.V: the token weight p_t s_v(t) 2^E (2^E a power of two per wave that
-//    keeps the weights in fp16 range) is split into fp16 hi/lo by round to
+//    keeps the weights in [0, 2)) is split into fp16 hi/lo by round to
 //    nearest.  The S^T register layout already is the MFMA A-operand layout
-//    (lane = head, lane group = 4 + 4 tokens), so no transpose of P is
-//    needed.  The rows pack [P_hi | P_lo].  V codes go through a
-//    wave-private LDS tile (the operand needs 8 tokens of one d per lane),
-//    with one accumulator for V_hi and one for V_lo;
-//  * the wave's token scales are loaded once and handed to the lanes that
-//    need them with lane shuffles;
-//  * each wave writes (m, l, o) for its range, and a second kernel merges
-//    the ranges of a head in range order.
+//    (lane = head, lane group = 4 + 4 tokens), so P needs no transpose.  The
+//    rows pack [P_hi | P_lo].  The V operand (8 tokens of one d per lane) is
+//    read from LDS with the transposing ds_read_b64_tr_b16; V_hi and V_lo
+//    have one accumulator each;
+//  * the 4 waves merge their (m, l, o) in LDS, each block writes one partial
+//    for its range, and a second kernel merges the ranges of a head in
+//    range order.
 #include "heal_internal.h"
 
 namespace heal {
@@ -42,14 +44,18 @@ namespace heal {
 namespace {
 
 constexpr int D = 128;
-constexpr int TW = 128;               // tokens per wave
-constexpr int VROW = D * 2 + 16;      // LDS bytes per V token row (padded)
-constexpr int VTILE = 32 * VROW;      // wave-private LDS bytes
+constexpr int TW = 64;                // tokens per wave
+constexpr int WPB = 4;                // waves per block
+constexpr int TB = TW * WPB;          // tokens per block
+constexpr int VTILE = TW * D * 2;     // wave-private LDS bytes: V codes of 64 tokens
 constexpr float kLog2eInvSqrtD = 0.12751743074602467f;   // log2(e) / sqrt(128)
 
 typedef short short2v __attribute__((ext_vector_type(2)));
 typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(3))) short4v* lds_s4_ptr;
 
 __device__ __forceinline__ void mfma16(const half8& a, const half8& b, floatx4& c) {
     c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -80,208 +86,235 @@ __device__ __forceinline__ void unpack8(const u32x4& raw, half8& hi, half8& lo) 
     lo = __builtin_bit_cast(half8, lw);
 }
 
+// Cross-lane steps without LDS instructions (VALU lane permutes and DPP), so
+// that nothing before the wait for the direct-to-LDS V loads is an LDS access.
+// v_permlane16_swap / v_permlane32_swap of x with itself hand each lane the
+// value of lane ^ 16 / lane ^ 32 in one of the two results.
 __device__ __forceinline__ float group_max(float x) {   // over lanes with equal lane % 16
-    x = fmaxf(x, __shfl_xor(x, 16, 64));
-    return fmaxf(x, __shfl_xor(x, 32, 64));
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t w = __builtin_bit_cast(uint32_t, x);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float group_sum(float x) {
-    x += __shfl_xor(x, 16, 64);
-    return x + __shfl_xor(x, 32, 64);
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t w = __builtin_bit_cast(uint32_t, x);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+// Lane c of each 16-lane row gets lane c + N (row_shl) or c - N (row_shr) of
+// the same row; lanes whose source is outside the row get 0.
+template <int N>
+__device__ __forceinline__ float row_from_right(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x100 + N, 0xF, 0xF, true));
+}
+template <int N>
+__device__ __forceinline__ float row_from_left(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, true));
+}
+
+// LDS placement of V: token row r of a wave tile holds its sixteen 16-byte
+// chunks (8 d each) in slots chunk ^ vswz(r).  The transposing reads of P.V
+// then touch 32 distinct 8-byte bank groups per 32 lanes.
+__device__ __forceinline__ int vswz(int r) { return 2 * (r & 7); }
 
 template <int G>
 __global__ __launch_bounds__(256) void attn_decode_kernel(
     const int16_t* __restrict__ q, const float* __restrict__ qs, const int16_t* __restrict__ k,
     const float* __restrict__ ks, const int16_t* __restrict__ v, const float* __restrict__ vs,
-    float* __restrict__ part, int B, int T, int Hkv, int units) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[4 * VTILE];
+    float* __restrict__ part, int T, int Hkv, int units) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[WPB * VTILE];
+    __shared__ float wm[WPB][8], wl[WPB][8], winv[WPB];
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-    const int64_t gw = (int64_t)blockIdx.x * 4 + wid;
-    if (gw >= (int64_t)B * Hkv * units) return;
-    const int u = (int)(gw % units);
-    const int gk = (int)((gw / units) % Hkv);
-    const int b = (int)(gw / ((int64_t)units * Hkv));
-    const int t_begin = u * TW, t_end = min(T, t_begin + TW);
+    const int ub = blockIdx.x % units;
+    const int gk = (blockIdx.x / units) % Hkv;
+    const int b = blockIdx.x / (units * Hkv);
+    const int t_begin = ub * TB + wid * TW;
+    // this wave's tokens (0 past the end); scalar, as the buffer resources are
+    const int nt = __builtin_amdgcn_readfirstlane(max(0, min(TW, T - t_begin)));
     unsigned char* vt = lds + wid * VTILE;
 
     const int c = lane & 15, grp = lane >> 4;
     const int Hq = G * Hkv;
-    const int64_t tok_stride = (int64_t)Hkv * D;               // int16 elements between tokens
-    // K and V of (b, gk) are read through buffer resources that start at the
-    // current tile and end at token T: a read past the cache returns zeros,
-    // so loads need no per-lane guards (tokens outside this wave's range are
-    // masked through their scores and weights instead).  The resources are
-    // scalar; lane offsets stay below 32 token rows.
+    const int64_t tok_stride = (int64_t)Hkv * D;                  // int16 elements between tokens
     const uint32_t row_bytes = (uint32_t)(tok_stride * 2);
-    const uint32_t region = (uint32_t)T * row_bytes;             // < 2^32, checked by the caller
-    const int16_t* kb = k + ((int64_t)b * T * Hkv + gk) * D;
-    const int16_t* vb = v + ((int64_t)b * T * Hkv + gk) * D;
-    const float* ksb = ks + (int64_t)b * T * Hkv + gk;
-    const float* vsb = vs + (int64_t)b * T * Hkv + gk;
+
+    // K and V of this wave's tokens through buffer resources that end at its
+    // last token (so no read reaches another wave's tokens or past the
+    // cache: those return zeros).  All offsets are per lane.
+    const int tfirst = __builtin_amdgcn_readfirstlane(min(t_begin, T - 1));
+    const int64_t tok0 = ((int64_t)b * T + tfirst) * Hkv + gk;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + tok0 * D, (uint32_t)nt * row_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + tok0 * D, (uint32_t)nt * row_bytes);
+
+    // ---- loads, in the order they are needed: q and the token scales, K,
+    //      then V.  They are unconditional, from clamped in-range indices
+    //      (unused values are dropped afterwards), so no branch splits them.
+    const int head = c < G ? c : (c < 2 * G ? c - G : 0);
+    const int16_t* qrow = q + ((int64_t)b * Hq + gk * G + head) * D;
+    u32x4 qraw[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qraw[s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * grp);
+    const float qscale_raw = qs[(int64_t)b * Hq + gk * G + head];
+    // token scales where the score and weight layouts need them: ksv[4 st + e]
+    // and vsv[4 st + e] belong to token 16 st + 4 grp + e (0 past the wave's
+    // tokens, by the resource bound)
+    float ksv[16], vsv[16];
+    {
+        const uint32_t srec = nt > 0 ? (uint32_t)(((nt - 1) * Hkv + 1) * 4) : 0u;
+        const __amdgpu_buffer_rsrc_t ksrs = make_rsrc(ks + tok0, srec);
+        const __amdgpu_buffer_rsrc_t vsrs = make_rsrc(vs + tok0, srec);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t off = (uint32_t)((16 * (i >> 2) + 4 * grp + (i & 3)) * Hkv * 4);
+            ksv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ksrs, off, 0, 0));
+            vsv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vsrs, off, 0, 0));
+        }
+    }
+
+    // K: lane (c, grp) of score block st gets token 16 st + c,
+    // d = 32 s + 8 grp + j (j < 8), in kr[4 st + s]
+    u32x4 kr[16];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            kr[4 * st + s] = __builtin_amdgcn_raw_buffer_load_b128(
+                krs, (uint32_t)(16 * st + c) * row_bytes + (uint32_t)(64 * s + 16 * grp), 0, 0);
+    // V into LDS: load i fills rows 4 i .. 4 i + 3; lane L writes row
+    // 4 i + L / 16, slot L % 16, which holds chunk slot ^ vswz(row)
+    {
+        const int r_in = lane >> 4;
+        const uint32_t v_even = (uint32_t)r_in * row_bytes + 16u * (uint32_t)((lane & 15) ^ vswz(r_in));
+        const uint32_t v_odd = (uint32_t)r_in * row_bytes + 16u * (uint32_t)((lane & 15) ^ vswz(4 + r_in));
+#pragma unroll
+        for (int i = 0; i < TW / 4; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr)(vt + 1024 * i), 16,
+                                                     ((i & 1) ? v_odd : v_even) + (uint32_t)(4 * i) * row_bytes,
+                                                     0, 0, 0);
+    }
 
     // ---- q as the packed B operand: column c < G -> 64 (q >> 6) of head c,
     //      G <= c < 2G -> q & 63 of head c - G, else 0.  d = 32 s + 8 grp + j.
+    // (selected by exact fp16 factors 64 / 1 / 0 rather than by branches)
     half8 qf[4];
     {
-        const int head = c < G ? c : c - G;
-        const bool use = c < 2 * G;
-        const int16_t* qrow = q + ((int64_t)b * Hq + gk * G + (use ? head : 0)) * D;
+        const _Float16 fh = c < G ? (_Float16)64.0f : (_Float16)0.0f;
+        const _Float16 fl = (c >= G && c < 2 * G) ? (_Float16)1.0f : (_Float16)0.0f;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            u32x4 raw = use ? *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * grp) : (u32x4)(0u);
             half8 hi, lo;
-            unpack8(raw, hi, lo);
-            qf[s] = c < G ? hi * (_Float16)64.0f : lo;
+            unpack8(qraw[s], hi, lo);
+            qf[s] = hi * fh + lo * fl;
         }
     }
-    const float qscale = c < G ? qs[(int64_t)b * Hq + gk * G + c] : 0.0f;
-
-    // ---- this wave's token scales: lane l holds tokens t_begin + l and + 64 + l
-    const float ks0 = (t_begin + lane < t_end) ? ksb[(int64_t)(t_begin + lane) * Hkv] : 0.0f;
-    const float ks1 = (t_begin + 64 + lane < t_end) ? ksb[(int64_t)(t_begin + 64 + lane) * Hkv] : 0.0f;
-    const float vs0 = (t_begin + lane < t_end) ? vsb[(int64_t)(t_begin + lane) * Hkv] : 0.0f;
-    const float vs1 = (t_begin + 64 + lane < t_end) ? vsb[(int64_t)(t_begin + 64 + lane) * Hkv] : 0.0f;
-
-    // ---- power of two keeping s_v(t) 2^E in [1, 2) for this wave's tokens ----
-    float vmax = fmaxf(vs0, vs1);
+    const float qscale = c < G ? qscale_raw : 0.0f;
+    // power of two keeping s_v(t) 2^E in [1, 2) for this wave's tokens (the
+    // four rows of lanes together hold all 64 of them)
+    float vmax = vsv[0];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off, 64));
+    for (int i = 1; i < 16; ++i) vmax = fmaxf(vmax, vsv[i]);
+    vmax = group_max(vmax);
     int vexp = 0;
     (void)frexpf(vmax, &vexp);                                  // vmax in [2^(vexp-1), 2^vexp)
     const float p2 = vmax > 0.0f ? ldexpf(1.0f, 1 - vexp) : 1.0f;
 
-    float m_run = -INFINITY, l_run = 0.0f;
+    // ---- scores for 4 x 16 tokens; sc[4 st + e] is token 16 st + 4 grp + e
+    float sc[16];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        floatx4 s_hi = {0.f, 0.f, 0.f, 0.f}, s_lo = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            half8 kh, kl;
+            unpack8(kr[4 * st + s], kh, kl);
+            mfma16(kh, qf[s], s_hi);
+            mfma16(kl, qf[s], s_lo);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float part_c = 64.0f * s_hi[e] + s_lo[e];
+            const float dot = part_c + row_from_right<G>(part_c);      // + the q & 63 column
+            const int tl = 16 * st + 4 * grp + e;
+            // masked by adding -inf (the product is finite), so the scale
+            // load is consumed unconditionally and stays with the others
+            const float mask = (c < G && tl < nt) ? 0.0f : -INFINITY;
+            sc[4 * st + e] = dot * (qscale * ksv[4 * st + e] * kLog2eInvSqrtD) + mask;
+        }
+    }
+    float m = sc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) m = fmaxf(m, sc[i]);
+    m = group_max(m);
+    const bool live = m > -INFINITY;                   // a head lane with at least one token
+    float p[16], psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        p[i] = live ? __builtin_amdgcn_exp2f(sc[i] - m) : 0.0f;
+        psum += p[i];
+    }
+    const float l = group_sum(psum);
+
+    // ---- P.V operand A for token blocks kb = 0, 1 (32 tokens each): row
+    //      c < G -> fp16 hi of head c's weight, G <= c < 2G -> fp16 lo of head
+    //      c - G's weight.  Slot i = token 32 kb + 16 (i / 4) + 4 grp + i % 4.
+    half8 pa[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float w = p[8 * kb + i] * vsv[8 * kb + i] * p2;
+            const float wo = row_from_left<G>(w);
+            _Float16 h, lo;
+            split_one(c < G ? w : wo, h, lo);
+            pa[kb][i] = c < G ? h : (c < 2 * G ? lo : (_Float16)0.0f);
+        }
+
+    // ---- V operand by transposing LDS reads.  In each 16-lane group, lane
+    //      4 j + x supplies the address of 4 d starting at 16 dt + 4 x of token
+    //      row 4 grp + j (+ 16 h + 32 kb); lane i then receives d = 16 dt + i of
+    //      those 4 tokens, which are slots 4 h .. 4 h + 3.
+    __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0): V is in LDS
+    __builtin_amdgcn_sched_barrier(0);
     floatx4 acc_h[8], acc_l[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) { acc_h[i][e] = 0.0f; acc_l[i][e] = 0.0f; }
-
-    for (int t0 = t_begin; t0 < t_end; t0 += 32) {
-        const int t0l = t0 - t_begin;                // 0, 32, 64 or 96: uniform
-        const float ksel = t0l < 64 ? ks0 : ks1;
-        const float vsel = t0l < 64 ? vs0 : vs1;
-        // ---- V tile -> wave-private LDS (issued first, consumed last) -------
-        const uint32_t tile_off = (uint32_t)t0 * row_bytes;
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kb + (int64_t)t0 * tok_stride, region - tile_off);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vb + (int64_t)t0 * tok_stride, region - tile_off);
-        u32x4 vraw[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {                 // 32 rows x 16 chunks of 16 bytes
-            const int chunk = lane + 64 * i;
-            vraw[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                vrs, (uint32_t)(chunk >> 4) * row_bytes + (uint32_t)(chunk & 15) * 16u, 0, 0);
-        }
-        // ---- scores S^T for 2 x 16 tokens ------------------------------------
-        float sc[8];
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            u32x4 kr[4];
-            const uint32_t koff = (uint32_t)(16 * st + c) * row_bytes + (uint32_t)grp * 16u;
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                kr[s] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff + 64u * s, 0, 0);
-            floatx4 s_hi = {0.f, 0.f, 0.f, 0.f}, s_lo = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                half8 kh, kl;
-                unpack8(kr[s], kh, kl);
-                mfma16(kh, qf[s], s_hi);
-                mfma16(kl, qf[s], s_lo);
-            }
-            // lane (c, grp), reg e: token t0 + 16 st + 4 grp + e, column c
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float part_c = 64.0f * s_hi[e] + s_lo[e];
-                const float dot = part_c + __shfl_down(part_c, G, 16);     // + the q & 63 column
-                const int tl = t0l + 16 * st + 4 * grp + e;               // token within the wave
-                const float kscale = __shfl(ksel, tl & 63, 64);
-                const bool valid = c < G && t0 + 16 * st + 4 * grp + e < t_end;
-                sc[4 * st + e] = valid ? dot * (qscale * kscale * kLog2eInvSqrtD) : -INFINITY;
-            }
-        }
-        float mt = sc[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sc[i]);
-        mt = group_max(mt);
-        // Lazy rescale: the reference maximum of a head moves only when the
-        // scores pass it by more than 8 (log2 units), so unscaled weights stay
-        // below 2^8 (fp16-safe after the scale fold) and the running output
-        // is rescaled on rare tiles only.
-        const bool bump = c < G && mt > m_run + 8.0f;   // always true on the first tile
-        if (__builtin_amdgcn_ballot_w64(bump)) {
-            const float m_new = bump ? mt : m_run;
-            const float alpha = c < G ? (m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new)) : 0.0f;
-            l_run *= alpha;
-            m_run = m_new;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {   // rows of the running output, by head
-                const int r = 4 * grp + e;
-                const int hr = r < G ? r : (r < 2 * G ? r - G : 0);
-                const float ar = __shfl(alpha, hr, 64);
-                const float f = r < 2 * G ? ar : 0.0f;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt) {
-                    acc_h[dt][e] *= f;
-                    acc_l[dt][e] *= f;
-                }
-            }
-        }
-        float p[8], psum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            p[i] = c < G ? __builtin_amdgcn_exp2f(sc[i] - m_run) : 0.0f;
-            psum += p[i];
-        }
-        l_run += group_sum(psum);
-
-        // ---- P.V operand A: row c < G -> fp16 hi of head c's weight, row
-        //      G <= c < 2G -> fp16 lo of head c - G's weight.  Slot i = token
-        //      t0 + 16 (i / 4) + 4 grp + i % 4, the same slots V uses below.
-        half8 pa;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int tl = t0l + 16 * (i >> 2) + 4 * grp + (i & 3);
-            const float vscale = __shfl(vsel, tl & 63, 64);
-            const float w = p[i] * vscale * p2;
-            const float wo = __shfl_up(w, G, 16);
-            _Float16 h, l;
-            split_one(c < G ? w : wo, h, l);
-            pa[i] = c < G ? h : (c < 2 * G ? l : (_Float16)0.0f);
-        }
-        // ---- V tile into LDS, then 8 d-tiles of 16 ---------------------------
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int chunk = lane + 64 * i;
-            *reinterpret_cast<u32x4*>(vt + (chunk >> 4) * VROW + (chunk & 15) * 16) = vraw[i];
-        }
-        __builtin_amdgcn_wave_barrier();
+    {
+        const int s16 = lane & 15;
+        const int rr = 4 * grp + (s16 >> 2);           // row within a 16-row half, mod 8 = vswz input
+        const int lane_off = rr * (D * 2) + 16 * ((s16 & 3) >> 1) + 8 * (s16 & 1);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-            const int d = 16 * dt + c;
-            u32x4 raw;
+            const int off = lane_off + 16 * ((2 * dt) ^ vswz(rr));
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int i0 = 2 * jj, i1 = 2 * jj + 1;
-                const int r0 = 16 * (i0 >> 2) + 4 * grp + (i0 & 3);
-                const int r1 = 16 * (i1 >> 2) + 4 * grp + (i1 & 3);
-                const uint16_t a0 = *reinterpret_cast<const uint16_t*>(vt + r0 * VROW + 2 * d);
-                const uint16_t a1 = *reinterpret_cast<const uint16_t*>(vt + r1 * VROW + 2 * d);
-                raw[jj] = (uint32_t)a0 | ((uint32_t)a1 << 16);
+            for (int kb = 0; kb < 2; ++kb) {
+                const short4v lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s4_ptr)(vt + off + (32 * kb) * (D * 2)));
+                const short4v hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s4_ptr)(vt + off + (32 * kb + 16) * (D * 2)));
+                u32x4 raw;
+                raw[0] = __builtin_bit_cast(uint32_t, (short2v){lo4[0], lo4[1]});
+                raw[1] = __builtin_bit_cast(uint32_t, (short2v){lo4[2], lo4[3]});
+                raw[2] = __builtin_bit_cast(uint32_t, (short2v){hi4[0], hi4[1]});
+                raw[3] = __builtin_bit_cast(uint32_t, (short2v){hi4[2], hi4[3]});
+                half8 vh, vl;
+                unpack8(raw, vh, vl);
+                mfma16(pa[kb], vh, acc_h[dt]);
+                mfma16(pa[kb], vl, acc_l[dt]);
             }
-            half8 vh, vl;
-            unpack8(raw, vh, vl);
-            mfma16(pa, vh, acc_h[dt]);
-            mfma16(pa, vl, acc_l[dt]);
         }
-        __builtin_amdgcn_wave_barrier();
     }
 
-    // ---- write this range's (m, l, o): row r = 64 acc_h + acc_l;
-    //      o[h][d] = row h + row (G + h) / 2^10, divided by the power of two
-    //      folded into the weights.  m is in base 2.
-    float* ob = reinterpret_cast<float*>(vt);        // [2G][D] staging, reuses the V tile
+    // ---- stage this wave's rows R = 64 acc_h + acc_l (2G rows of D) in its
+    //      own LDS tile (after its own reads), plus (m, l, 1 / 2^E)
+    float* ob = reinterpret_cast<float*>(vt);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -289,16 +322,34 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
             const int r = 4 * grp + e;
             if (r < 2 * G) ob[r * D + 16 * dt + c] = 64.0f * acc_h[dt][e] + acc_l[dt][e];
         }
-    __builtin_amdgcn_wave_barrier();
-    float* pout = part + gw * (int64_t)(2 * G + G * D);
     if (lane < G) {
-        pout[lane] = m_run;
-        pout[G + lane] = l_run;
+        wm[wid][lane] = m;
+        wl[wid][lane] = l;
     }
-    const float inv_p2 = 1.0f / p2;
-    for (int i = lane; i < G * D; i += 64) {
+    if (lane == 0) winv[wid] = 1.0f / p2;
+    __syncthreads();
+
+    // ---- merge the 4 waves: o[h][d] = (R[h][d] + R[G+h][d] / 2^10) / 2^E
+    float* pout = part + (int64_t)blockIdx.x * (2 * G + G * D);
+    for (int i = threadIdx.x; i < G * D; i += 256) {
         const int h = i / D, d = i - h * D;
-        pout[2 * G + i] = (ob[h * D + d] + ob[(G + h) * D + d] * 0.0009765625f) * inv_p2;
+        float M = wm[0][h];
+#pragma unroll
+        for (int w = 1; w < WPB; ++w) M = fmaxf(M, wm[w][h]);
+        float O = 0.0f, L = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WPB; ++w) {
+            const float mw = wm[w][h];
+            const float f = mw > -INFINITY ? __builtin_amdgcn_exp2f(mw - M) : 0.0f;
+            const float* R = reinterpret_cast<const float*>(lds + w * VTILE);
+            O += f * ((R[h * D + d] + R[(G + h) * D + d] * 0.0009765625f) * winv[w]);
+            L += f * wl[w][h];
+        }
+        pout[2 * G + i] = O;
+        if (d == 0) {
+            pout[h] = M;
+            pout[G + h] = L;
+        }
     }
 }
 
@@ -348,7 +399,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
 int64_t attn_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dd) {
     (void)Dd;
     const int64_t G = Hq / Hkv;
-    const int64_t units = (T + TW - 1) / TW;
+    const int64_t units = (T + TB - 1) / TB;
     return (B * Hkv * units * (2 * G + G * D) * 4 + 255) / 256 * 256;
 }
 
@@ -357,15 +408,14 @@ hipError_t launch_attn_decode(const int16_t* q, const float* qs, const int16_t* 
                               int64_t Hq, int64_t Hkv, int64_t Dd, void* workspace, hipStream_t s) {
     if (Dd != D) return hipErrorInvalidValue;
     const int G = (int)(Hq / Hkv);
-    const int units = (int)((T + TW - 1) / TW);
-    if (units > kMaxUnits) return hipErrorInvalidValue;   // T up to 262144 tokens
-    const int64_t waves = B * Hkv * units;
-    const unsigned blocks = (unsigned)((waves + 3) / 4);
+    const int units = (int)((T + TB - 1) / TB);
+    if (units > kMaxUnits) return hipErrorInvalidValue;   // T up to 524288 tokens
+    const unsigned blocks = (unsigned)(B * Hkv * units);
     float* part = static_cast<float*>(workspace);
 #define HEAL_ATT(G_)                                                                                \
     case G_:                                                                                        \
         hipLaunchKernelGGL((attn_decode_kernel<G_>), dim3(blocks), dim3(256), 0, s, q, qs, k, ks, v, \
-                           vs, part, (int)B, (int)T, (int)Hkv, units);                              \
+                           vs, part, (int)T, (int)Hkv, units);                              \
         break;
     switch (G) {
         HEAL_ATT(1) HEAL_ATT(2) HEAL_ATT(3) HEAL_ATT(4) HEAL_ATT(5) HEAL_ATT(6) HEAL_ATT(7) HEAL_ATT(8)
