@@ -54,6 +54,7 @@ typedef short short2v __attribute__((ext_vector_type(2)));
 typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef short short4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(3))) short4v* lds_s4_ptr;
 
@@ -71,6 +72,27 @@ __device__ __forceinline__ void unpack2(uint32_t w, half2v& hi, half2v& lo) {
     const ushort2v u = __builtin_bit_cast(ushort2v, t) + (ushort2v)(unsigned short)0x6600;
     hi = __builtin_bit_cast(half2v, u) - (half2v)(_Float16)1536.0f;
     lo = __builtin_bit_cast(half2v, (w & 0x003F003Fu) | 0x64006400u) - (half2v)(_Float16)1024.0f;
+}
+
+// Same high halves; the low halves are left biased, as the fp16 numbers
+// 1024 + (code & 63), in a single bit operation ((w & 0x003F003F) | 0x64006400).
+// A product chain over biased low halves is started from -1024 times the sum
+// of the other operand, which removes the bias: every product stays exact
+// ((1024 + ql) has 11 significant bits), and the extra rounding is that of a
+// partial sum at most 1087 / 64 times larger than the unbiased one, far below
+// the rounding of the high-half chain it is added to.
+__device__ __forceinline__ void unpack8_lobias(const u32x4& raw, half8& hi, half8& lob) {
+    u32x4 hw, lw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w = raw[i];
+        const short2v t = __builtin_bit_cast(short2v, w) >> (short2v)(short)6;
+        const ushort2v u = __builtin_bit_cast(ushort2v, t) + (ushort2v)(unsigned short)0x6600;
+        hw[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, u) - (half2v)(_Float16)1536.0f);
+        lw[i] = __builtin_amdgcn_bitop3_b32(w, 0x003F003Fu, 0x64006400u, 0xEA);   // (w & m) | b
+    }
+    hi = __builtin_bit_cast(half8, hw);
+    lob = __builtin_bit_cast(half8, lw);
 }
 
 __device__ __forceinline__ void unpack8(const u32x4& raw, half8& hi, half8& lo) {
@@ -224,15 +246,24 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     (void)frexpf(vmax, &vexp);                                  // vmax in [2^(vexp-1), 2^vexp)
     const float p2 = vmax > 0.0f ? ldexpf(1.0f, 1 - vexp) : 1.0f;
 
-    // ---- scores for 4 x 16 tokens; sc[4 st + e] is token 16 st + 4 grp + e
+    // ---- scores for 4 x 16 tokens; sc[4 st + e] is token 16 st + 4 grp + e.
+    //      The K low halves come biased by 1024; their chains start from
+    //      qbias[col] = -1024 * sum_d q_col[d] (an MFMA against a constant
+    //      -1024 row, exact: integer sums below 2^24).
+    floatx4 qbias = {0.f, 0.f, 0.f, 0.f};
+    {
+        const half8 m1024 = (half8)(_Float16)-1024.0f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) mfma16(m1024, qf[s], qbias);
+    }
     float sc[16];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-        floatx4 s_hi = {0.f, 0.f, 0.f, 0.f}, s_lo = {0.f, 0.f, 0.f, 0.f};
+        floatx4 s_hi = {0.f, 0.f, 0.f, 0.f}, s_lo = qbias;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             half8 kh, kl;
-            unpack8(kr[4 * st + s], kh, kl);
+            unpack8_lobias(kr[4 * st + s], kh, kl);
             mfma16(kh, qf[s], s_hi);
             mfma16(kl, qf[s], s_lo);
         }
@@ -281,11 +312,22 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     //      those 4 tokens, which are slots 4 h .. 4 h + 3.
     __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0): V is in LDS
     __builtin_amdgcn_sched_barrier(0);
+    // V low halves come biased by 1024: their chains start from
+    // pbias[row] = -1024 * sum_t P[row][t] (an MFMA against a constant
+    // -1024 column block), the same for every d.
+    floatx4 pbias = {0.f, 0.f, 0.f, 0.f};
+    {
+        const half8 m1024 = (half8)(_Float16)-1024.0f;
+        mfma16(pa[0], m1024, pbias);
+        mfma16(pa[1], m1024, pbias);
+    }
     floatx4 acc_h[8], acc_l[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+        acc_l[i] = pbias;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { acc_h[i][e] = 0.0f; acc_l[i][e] = 0.0f; }
+        for (int e = 0; e < 4; ++e) acc_h[i][e] = 0.0f;
+    }
     {
         const int s16 = lane & 15;
         const int rr = 4 * grp + (s16 >> 2);           // row within a 16-row half, mod 8 = vswz input
@@ -299,13 +341,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
                     (lds_s4_ptr)(vt + off + (32 * kb) * (D * 2)));
                 const short4v hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_s4_ptr)(vt + off + (32 * kb + 16) * (D * 2)));
-                u32x4 raw;
-                raw[0] = __builtin_bit_cast(uint32_t, (short2v){lo4[0], lo4[1]});
-                raw[1] = __builtin_bit_cast(uint32_t, (short2v){lo4[2], lo4[3]});
-                raw[2] = __builtin_bit_cast(uint32_t, (short2v){hi4[0], hi4[1]});
-                raw[3] = __builtin_bit_cast(uint32_t, (short2v){hi4[2], hi4[3]});
+                const u32x2 lo2 = __builtin_bit_cast(u32x2, lo4), hi2 = __builtin_bit_cast(u32x2, hi4);
+                const u32x4 raw = {lo2.x, lo2.y, hi2.x, hi2.y};
                 half8 vh, vl;
-                unpack8(raw, vh, vl);
+                unpack8_lobias(raw, vh, vl);
                 mfma16(pa[kb], vh, acc_h[dt]);
                 mfma16(pa[kb], vl, acc_l[dt]);
             }
