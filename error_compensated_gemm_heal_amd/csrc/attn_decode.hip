@@ -394,42 +394,42 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 
 // Merge the token ranges of one (b, h), in range order:
 //   out = sum_u w_u o_u / sum_u w_u l_u,   w_u = 2^(m_u - max_u m_u).
-// The per-range weights are computed once into LDS; every thread then sums its
-// d over the ranges with independent loads.
-constexpr int kMaxUnits = 2048;
+// One pass: each thread (one d) reads (m_u, l_u, o_u[d]) for 16 ranges at a
+// time with independent loads and folds them into a running (M, L, O).
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part,
                                                            float* __restrict__ out, int Hq, int Hkv,
                                                            int G, int units) {
-    __shared__ float wsh[kMaxUnits];
-    __shared__ float red[4];
     const int bh = blockIdx.x;
     const int b = bh / Hq, h = bh - b * Hq;
     const int gk = h / G, c = h - gk * G;
     const int d = threadIdx.x;
     const int64_t stride = 2 * G + G * D;
     const float* base = part + ((int64_t)b * Hkv + gk) * units * stride;
-    // maximum over ranges (two waves)
-    float mloc = -INFINITY;
-    for (int u = d; u < units; u += blockDim.x) mloc = fmaxf(mloc, base[u * stride + c]);
+    float M = -INFINITY, L = 0.0f, O = 0.0f;
+    for (int u0 = 0; u0 < units; u0 += 16) {
+        float mu[16], lu[16], ou[16];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
-    if ((d & 63) == 0) red[d >> 6] = mloc;
-    __syncthreads();
-    const float M = fmaxf(red[0], red[1]);
-    float lloc = 0.0f;
-    for (int u = d; u < units; u += blockDim.x) {
-        const float w = __builtin_amdgcn_exp2f(base[u * stride + c] - M);
-        wsh[u] = w;
-        lloc += w * base[u * stride + G + c];
+        for (int i = 0; i < 16; ++i) {
+            const int u = min(u0 + i, units - 1);
+            mu[i] = base[u * stride + c];
+            lu[i] = base[u * stride + G + c];
+            ou[i] = base[u * stride + 2 * G + c * D + d];
+        }
+        float mc = M;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (u0 + i < units) mc = fmaxf(mc, mu[i]);
+        const float r = M > -INFINITY ? __builtin_amdgcn_exp2f(M - mc) : 0.0f;
+        L *= r;
+        O *= r;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float w = (u0 + i < units && mu[i] > -INFINITY) ? __builtin_amdgcn_exp2f(mu[i] - mc) : 0.0f;
+            L += w * lu[i];
+            O += w * ou[i];
+        }
+        M = mc;
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) lloc += __shfl_xor(lloc, off, 64);
-    if ((d & 63) == 0) red[2 + (d >> 6)] = lloc;
-    __syncthreads();
-    const float L = red[2] + red[3];
-    float O = 0.0f;
-#pragma unroll 8
-    for (int u = 0; u < units; ++u) O += wsh[u] * base[u * stride + 2 * G + c * D + d];
     out[(int64_t)bh * D + d] = O / L;
 }
 
@@ -448,7 +448,6 @@ hipError_t launch_attn_decode(const int16_t* q, const float* qs, const int16_t* 
     if (Dd != D) return hipErrorInvalidValue;
     const int G = (int)(Hq / Hkv);
     const int units = (int)((T + TB - 1) / TB);
-    if (units > kMaxUnits) return hipErrorInvalidValue;   // T up to 524288 tokens
     const unsigned blocks = (unsigned)(B * Hkv * units);
     float* part = static_cast<float*>(workspace);
 #define HEAL_ATT(G_)                                                                                \
