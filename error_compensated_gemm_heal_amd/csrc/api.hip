@@ -17,9 +17,13 @@ heal_status hip_status(hipError_t e) { return e == hipSuccess ? HEAL_OK : HEAL_E
 
 // Path choice for heal_gemm_f32c.  The decode kernel streams an fp32 [N,K]
 // weight directly; every other case packs the operands for the prefill kernel.
-bool use_decode(int64_t M, uint32_t flags) {
-    return M <= 64 && !(flags & (HEAL_W_PACKED | HEAL_A_PACKED)) && (flags & HEAL_W_KN) == 0;
+// The decode kernel addresses its split activation (256 bytes per k) and
+// each 16-row slice of W with 32-bit byte offsets.
+bool use_decode(int64_t M, int64_t K, uint32_t flags) {
+    return M <= 64 && K < ((int64_t)1 << 23) && !(flags & (HEAL_W_PACKED | HEAL_A_PACKED)) &&
+           (flags & HEAL_W_KN) == 0;
 }
+constexpr int64_t kMaxDecodeLdw = (int64_t)1 << 26;
 
 __global__ void zero_rows_kernel(float* C, int64_t ldc, int64_t M, int64_t N) {
     const int64_t total = M * N;
@@ -81,7 +85,7 @@ heal_status heal_pack_w(const float* W, int64_t ldw, int64_t N, int64_t K, uint3
 
 size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags) {
     if (M <= 0 || N <= 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return 0;
-    if (use_decode(M, flags)) {
+    if (use_decode(M, K, flags)) {
         const DecodePlan p = decode_plan(M, N, K);
         return (size_t)(round256(p.a_bytes) + round256(p.p_bytes));
     }
@@ -120,11 +124,12 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
         if (misaligned(workspace, 256)) return HEAL_ERR_ALIGN;
     }
 
-    if (use_decode(M, flags)) {
+    if (use_decode(M, K, flags)) {
+        if (ldw >= kMaxDecodeLdw) return HEAL_ERR_UNSUPPORTED;
         const DecodePlan p = decode_plan(M, N, K);
         unsigned char* ws = static_cast<unsigned char*>(workspace);
         return hip_status(launch_gemm_decode(A, lda, static_cast<const float*>(W), ldw, C, ldc, M, N,
-                                             K, ws + round256(p.a_bytes), p, dev_status, s));
+                                             K, ws, p, dev_status, s));
     }
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     const void* apk = A;

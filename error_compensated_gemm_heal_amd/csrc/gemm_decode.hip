@@ -3,55 +3,96 @@
 // Same arithmetic as the prefill kernel (HEAL paper, section 3, "Mitigating
 // GEMM Truncation via FP16 Promotion and Algebraic Compensation"):
 //     C = A_hi.B_hi + 2^-10 (A_hi.B_lo + A_lo.B_hi),  fp32 accumulation,
-// but shaped for a skinny activation.  The weight dominates the traffic, so:
+// but shaped for a skinny activation, where the weight is the traffic:
 //  * W is read once from HBM as fp32 [N, K] (4 bytes per element, the same
 //    bytes as its two fp16 parts) and split into hi/lo in registers;
-//  * the activation block (<= 64 rows x 256 k) is split once per workgroup
-//    into LDS, stored in MFMA fragment order so every lane's read is one
-//    conflict-free 16-byte access;
+//  * the activation (<= 64 rows) is split once per call by a small kernel
+//    into hi/lo planes already in MFMA operand order (see asplit_kernel);
+//    each workgroup copies 128-wide k blocks of it into LDS with
+//    direct-to-LDS loads, double-buffered, so staging costs no VALU work
+//    and every operand read is one conflict-free 16-byte LDS access;
 //  * v_mfma_f32_16x16x32_f16 with the activation as the 16-row operand and W
-//    as the 16-column operand, so output columns are consecutive lanes;
+//    as the 16-column operand (16 W rows per wave), so output columns are
+//    consecutive lanes;
 //  * inside each 32-wide k step, lane group g (lanes 16g..16g+15) carries
 //    k = 4g..4g+3 and 16+4g..16+4g+3: any k order is valid as long as both
 //    operands use it, and this one makes each W load a 64-byte run per row;
-//  * W for the next 8 k steps is in flight while the current 8 are used;
+//  * W for the next 8 k steps is always in flight: every step issues exactly
+//    two W loads (the last steps re-read a clamped step), so the number of
+//    loads outstanding at each block boundary is a constant;
 //  * split-K: the k range is cut into chunks chosen from (N, K) only, and
 //    chunk partials are summed in chunk order by a second kernel.  The
 //    summation order of an output therefore does not depend on M: a
 //    decode-sized product does not change with the batch it is computed in.
+#include <type_traits>
+
 #include "heal_internal.h"
 
 namespace heal {
 
 namespace {
 
-constexpr int KA = 256;             // k block of activations staged in LDS
+constexpr int KA = 128;             // k block of activations per LDS buffer
 constexpr int STEPS = KA / 32;      // k32 steps per block
+constexpr int PF = 8;               // W prefetch distance in k32 steps
 constexpr int ROWS_PER_WAVE = 16;
 constexpr int DEC_ROWS = 4 * ROWS_PER_WAVE;   // W rows (outputs) per workgroup
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// s_waitcnt immediate that waits until at most n vector memory operations
+// are outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt not waited on).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 __device__ __forceinline__ void mfma16(const half8& a, const half8& b, floatx4& c) {
     c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Load this lane's 8 W values of one k32 step (k = k0 + 4g..+3 and k0 + 16 + 4g..+3).
-template <bool VEC>
-__device__ __forceinline__ void load_w(const float* __restrict__ wrow, bool row_ok, int64_t k0, int g,
-                                       int64_t K, float4& lo4, float4& hi4) {
-    const int64_t ka = k0 + 4 * g, kb = k0 + 16 + 4 * g;
-    if (VEC && row_ok && k0 + 32 <= K) {
-        lo4 = *reinterpret_cast<const float4*>(wrow + ka);
-        hi4 = *reinterpret_cast<const float4*>(wrow + kb);
-    } else {
-        float t[8];
+// Bytes of one activation block: hi and lo planes of STEPS x MT x 64 lanes x 16 B.
+template <int MT>
+constexpr int block_bytes() { return 2 * STEPS * MT * 64 * 16; }
+
+// ---- activation split into operand order --------------------------------
+// Block b (k in [128 b, 128 b + 128)), plane p (0 = hi, 1 = lo), step s,
+// tile t, lane l = 16 g + r holds, as 8 fp16, row 16 t + r at
+// k = 128 b + 32 s + {4g .. 4g+3, 16+4g .. 16+4g+3}.  Rows >= M and k >= K
+// are zero.  One thread per (b, s, t, l).
+template <int MT>
+__global__ __launch_bounds__(256) void asplit_kernel(const float* __restrict__ A, int64_t lda, int M,
+                                                     int K, int nblk, unsigned char* __restrict__ out,
+                                                     uint32_t* __restrict__ status) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = (int64_t)nblk * STEPS * MT * 64;
+    bool bad = false;
+    if (idx < total) {
+        const int l = (int)(idx & 63);
+        const int t = (int)((idx >> 6) % MT);
+        const int s = (int)((idx / (64 * MT)) % STEPS);
+        const int64_t b = idx / (64 * MT * STEPS);
+        const int m = 16 * t + (l & 15), g = l >> 4;
+        const int64_t k0 = b * KA + 32 * s;
+        float x[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            t[j] = (row_ok && ka + j < K) ? wrow[ka + j] : 0.f;
-            t[4 + j] = (row_ok && kb + j < K) ? wrow[kb + j] : 0.f;
+        for (int j = 0; j < 8; ++j) {
+            const int64_t k = k0 + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
+            x[j] = (m < M && k < K) ? A[(int64_t)m * lda + k] : 0.0f;
         }
-        lo4 = make_float4(t[0], t[1], t[2], t[3]);
-        hi4 = make_float4(t[4], t[5], t[6], t[7]);
+        half8 h, lo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            _Float16 hh, ll;
+            split_one(x[j], hh, ll);
+            bad |= f16_out_of_range(x[j]);
+            h[j] = hh;
+            lo[j] = ll;
+        }
+        unsigned char* blk = out + b * block_bytes<MT>();
+        const int64_t off = ((int64_t)(s * MT + t) * 64 + l) * 16;
+        *reinterpret_cast<half8*>(blk + off) = h;
+        *reinterpret_cast<half8*>(blk + block_bytes<MT>() / 2 + off) = lo;
     }
+    if (status && __builtin_amdgcn_ballot_w64(bad) && (threadIdx.x & 63) == 0)
+        atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
 }
 
 __device__ __forceinline__ void split8(const float4& a, const float4& b, half8& h, half8& l) {
@@ -65,26 +106,77 @@ __device__ __forceinline__ void split8(const float4& a, const float4& b, half8& 
     }
 }
 
+__device__ __forceinline__ float absmax8(float m, const float4& a, const float4& b) {
+    m = fmaxf(m, fmaxf(fmaxf(__builtin_fabsf(a.x), __builtin_fabsf(a.y)),
+                       fmaxf(__builtin_fabsf(a.z), __builtin_fabsf(a.w))));
+    return fmaxf(m, fmaxf(fmaxf(__builtin_fabsf(b.x), __builtin_fabsf(b.y)),
+                          fmaxf(__builtin_fabsf(b.z), __builtin_fabsf(b.w))));
+}
+
+// VEC: W rows 16-byte aligned and K % 32 == 0, so every step is two 16-byte
+// buffer loads per lane.  Otherwise lanes load element by element with
+// bounds checks, and block boundaries wait for every load.
 template <int MT, bool VEC>
-__global__ __launch_bounds__(256) void gemm_decode_kernel(const float* __restrict__ A, int64_t lda,
+__global__ __launch_bounds__(256) void gemm_decode_kernel(const unsigned char* __restrict__ Ablk,
                                                           const float* __restrict__ W, int64_t ldw,
                                                           float* __restrict__ out, int64_t ldo,
                                                           int64_t split_stride, int M, int N, int K,
-                                                          int kchunk, uint32_t* __restrict__ status) {
-    constexpr int MP = MT * 16;                  // padded activation rows
-    constexpr int PLANE = STEPS * 4 * MP * 16;   // bytes per hi or lo plane of one k block
-    __shared__ __attribute__((aligned(16))) unsigned char sa[2 * PLANE];
+                                                          int kchunk, int a_total_bytes,
+                                                          uint32_t* __restrict__ status) {
+    constexpr int BB = block_bytes<MT>();
+    constexpr int DMA_PER_WAVE = BB / 1024 / 4;    // 1 KB per wave-wide direct-to-LDS load
+    extern __shared__ __attribute__((aligned(16))) unsigned char sa[];   // 2 x BB
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4;
-    const int n = blockIdx.x * DEC_ROWS + wave * ROWS_PER_WAVE + (lane & 15);
+    const int n0 = blockIdx.x * DEC_ROWS + wave * ROWS_PER_WAVE;
+    const int n = n0 + (lane & 15);
     const bool row_ok = n < N;
-    const float* wrow = W + (int64_t)(row_ok ? n : 0) * ldw;
     const int split = blockIdx.y;
-    const int64_t k_begin = (int64_t)split * kchunk;
-    const int64_t k_end = std::min<int64_t>(k_begin + kchunk, K);
-    const int nsteps = (int)((k_end - k_begin + 31) / 32);
+    const int k_begin = split * kchunk;
+    const int k_end = min(k_begin + kchunk, K);
+    const int nsteps = (k_end - k_begin + 31) / 32;
     const int nblocks = (nsteps + STEPS - 1) / STEPS;
+    const int blk0 = k_begin / KA;
+
+    // activation blocks: wave w copies 1 KB pieces w, w + 4, ... of a block
+    const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(Ablk, (uint32_t)a_total_bytes);
+    auto dma_block = [&](int b, int buf) {
+#pragma unroll
+        for (int i = 0; i < DMA_PER_WAVE; ++i) {
+            const int piece = wave + 4 * i;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_ptr)(sa + buf * BB + piece * 1024), 16,
+                                                     (uint32_t)(lane * 16),
+                                                     (uint32_t)((blk0 + b) * BB + piece * 1024), 0, 0);
+        }
+    };
+
+    // W: lane reads row n, k = k_begin + 32 step + {4g.., 16+4g..}
+    // (scalars made explicit: the buffer resource must live in SGPRs)
+    const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(ROWS_PER_WAVE, N - n0)));
+    const int wrow0 = __builtin_amdgcn_readfirstlane(min(n0, N - 1));
+    const __amdgpu_buffer_rsrc_t wrsrc =
+        make_rsrc(W + (int64_t)wrow0 * ldw, (uint32_t)((int64_t)nrows * ldw * 4));
+    const uint32_t wlane = (uint32_t)((lane & 15) * ldw * 4 + (int64_t)(k_begin + 4 * g) * 4);
+    auto load_w = [&](int step, float4& a, float4& b) {
+        if (VEC) {
+            const uint32_t off = wlane + (uint32_t)(step * 128);
+            a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off, 0, 0));
+            b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off + 64, 0, 0));
+        } else {
+            const float* wrow = W + (int64_t)(row_ok ? n : 0) * ldw;
+            const int ka = k_begin + 32 * step + 4 * g, kb = ka + 16;
+            float t[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                t[j] = (row_ok && ka + j < k_end) ? wrow[ka + j] : 0.f;
+                t[4 + j] = (row_ok && kb + j < k_end) ? wrow[kb + j] : 0.f;
+            }
+            a = make_float4(t[0], t[1], t[2], t[3]);
+            b = make_float4(t[4], t[5], t[6], t[7]);
+        }
+    };
 
     floatx4 acc_hh[MT], acc_c[MT];
 #pragma unroll
@@ -92,76 +184,63 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(const float* __restric
 #pragma unroll
         for (int e = 0; e < 4; ++e) { acc_hh[t][e] = 0.f; acc_c[t][e] = 0.f; }
 
-    float4 wa[STEPS], wb[STEPS];
-    bool bad = false;
+    // prologue: activation block 0, then W for steps 0 .. PF-1
+    dma_block(0, 0);
+    float4 wa[PF], wb[PF];
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s)
-        if (s < nsteps) load_w<VEC>(wrow, row_ok, k_begin + 32 * s, g, K, wa[s], wb[s]);
+    for (int s = 0; s < PF; ++s) load_w(min(s, nsteps - 1), wa[s], wb[s]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (VEC) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PF));   // block 0 landed; W still in flight
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    float wmax = 0.0f;
 
-    for (int blk = 0; blk < nblocks; ++blk) {
-        const int64_t kb0 = k_begin + (int64_t)blk * KA;
-        // ---- stage the activation block: split into fragment-ordered LDS ----
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < MP * (KA / 4) / 256; ++i) {
-            const int f = tid + 256 * i;
-            const int m = f / (KA / 4);
-            const int kk = (f % (KA / 4)) * 4;      // k offset inside the block
-            const int64_t k = kb0 + kk;
-            float x[4] = {0.f, 0.f, 0.f, 0.f};
-            if (m < M) {
-                const float* ap = A + (int64_t)m * lda + k;
-                if (VEC && k + 4 <= k_end) {
-                    const float4 v = *reinterpret_cast<const float4*>(ap);
-                    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (k + j < k_end) x[j] = ap[j];
-                }
-            }
-            uint16_t h[4], l[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                _Float16 hh, ll;
-                split_one(x[j], hh, ll);
-                bad |= f16_out_of_range(x[j]);
-                h[j] = f16_bits(hh);
-                l[j] = f16_bits(ll);
-            }
-            const int kb = kk >> 5, kw = kk & 31;
-            const int half_sel = kw >> 4, grp = (kw & 15) >> 2;
-            const int off = ((kb * 4 + grp) * MP + m) * 16 + half_sel * 8;
-            *reinterpret_cast<uint2*>(sa + off) =
-                make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
-            *reinterpret_cast<uint2*>(sa + PLANE + off) =
-                make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
-        }
-        __syncthreads();
-
-        // ---- 8 k32 steps: consume W in registers, prefetch the next block ----
+    // one activation block of STEPS steps; J = position of its first step
+    // in the PF-deep W register ring
+    auto run_block = [&](int b, auto J_) {
+        constexpr int J = decltype(J_)::value;
+        const bool more = b + 1 < nblocks;
+        if (more) dma_block(b + 1, (b + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);     // the copy stays ahead of this block's W loads
+        const unsigned char* abuf = sa + (b & 1) * BB;
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) {
-            const int step = blk * STEPS + s;
+            const int step = b * STEPS + s;
+            float4& ra = wa[J + s];
+            float4& rb = wb[J + s];
+            half8 wh, wl;
+            split8(ra, rb, wh, wl);
+            wmax = absmax8(wmax, ra, rb);
+            load_w(min(step + PF, nsteps - 1), ra, rb);
             if (step < nsteps) {
-                half8 wh, wl;
-                split8(wa[s], wb[s], wh, wl);
-                bad |= f16_out_of_range4(wa[s]) || f16_out_of_range4(wb[s]);
-                const int nxt = step + STEPS;
-                if (nxt < nsteps) load_w<VEC>(wrow, row_ok, k_begin + 32 * (int64_t)nxt, g, K, wa[s], wb[s]);
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {
-                    const int off = ((s * 4 + g) * MP + t * 16 + (lane & 15)) * 16;
-                    const half8 ah = *reinterpret_cast<const half8*>(sa + off);
-                    const half8 al = *reinterpret_cast<const half8*>(sa + PLANE + off);
+                    const int off = ((s * MT + t) * 64 + lane) * 16;
+                    const half8 ah = *reinterpret_cast<const half8*>(abuf + off);
+                    const half8 al = *reinterpret_cast<const half8*>(abuf + BB / 2 + off);
                     mfma16(ah, wh, acc_hh[t]);
                     mfma16(ah, wl, acc_c[t]);
                     mfma16(al, wh, acc_c[t]);
                 }
             }
         }
+        if (more) {
+            // the next block's copy was issued before this block's 2 STEPS W loads
+            __builtin_amdgcn_sched_barrier(0);
+            if (VEC) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * STEPS));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    for (int b = 0; b < nblocks; b += 2) {
+        run_block(b, std::integral_constant<int, 0>{});
+        if (b + 1 < nblocks) run_block(b + 1, std::integral_constant<int, STEPS>{});
     }
-    if (bad && status) atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // drain the clamped tail loads
+    if (status && __builtin_amdgcn_ballot_w64(wmax >= 65520.0f) && lane == 0)
+        atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
 
     // ---- epilogue: lane holds column n, rows t*16 + 4g + e ------------------
     if (!row_ok) return;
@@ -189,18 +268,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
+int mtiles(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+
 }  // namespace
 
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
     DecodePlan p{};
     const int64_t nblk = (N + DEC_ROWS - 1) / DEC_ROWS;
-    const int64_t kblocks = std::max<int64_t>(1, (K + KA - 1) / KA);
-    int64_t want = std::max<int64_t>(1, (512 + nblk - 1) / std::max<int64_t>(nblk, 1));
+    const int64_t kblocks = std::max<int64_t>(1, (K + 255) / 256);
+    // about 512 workgroups (two per compute unit) in one round, without going over
+    int64_t want = std::max<int64_t>(1, 512 / std::max<int64_t>(nblk, 1));
     want = std::min(want, kblocks);
     const int64_t per = (K + want - 1) / want;
-    p.kchunk = std::max<int64_t>(KA, (per + KA - 1) / KA * KA);
+    p.kchunk = std::max<int64_t>(256, (per + 255) / 256 * 256);
     p.splits = (int)std::max<int64_t>(1, (K + p.kchunk - 1) / p.kchunk);
-    p.a_bytes = 0;
+    const int64_t ablocks = (K + KA - 1) / KA;
+    const int mt = mtiles(M);
+    p.a_bytes = ablocks * (mt == 1 ? block_bytes<1>() : mt == 2 ? block_bytes<2>() : block_bytes<4>());
     p.p_bytes = p.splits > 1 ? (p.splits * M * N * 4 + 255) / 256 * 256 : 0;
     return p;
 }
@@ -210,34 +294,42 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const float* W, int64
                               const DecodePlan& plan, uint32_t* status, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
     if (M > 64 || K == 0) return hipErrorInvalidValue;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    unsigned char* ablk = ws;
+    float* part = reinterpret_cast<float*>(ws + (plan.a_bytes + 255) / 256 * 256);
     const dim3 grid((unsigned)((N + DEC_ROWS - 1) / DEC_ROWS), (unsigned)plan.splits);
-    float* out = plan.splits > 1 ? static_cast<float*>(workspace) : C;
+    float* out = plan.splits > 1 ? part : C;
     const int64_t ldo = plan.splits > 1 ? N : ldc;
     const int64_t stride = plan.splits > 1 ? M * N : 0;
-    // 16-byte vector loads need 16-byte aligned rows of both operands
-    const bool vec = ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(W)) & 15) == 0 &&
-                     ((lda | ldw) & 3) == 0;
-#define HEAL_DEC(MT_)                                                                                    \
-    if (vec)                                                                                             \
-        hipLaunchKernelGGL((gemm_decode_kernel<MT_, true>), grid, dim3(256), 0, s, A, lda, W, ldw, out, \
-                           ldo, stride, (int)M, (int)N, (int)K, (int)plan.kchunk, status);               \
-    else                                                                                                 \
-        hipLaunchKernelGGL((gemm_decode_kernel<MT_, false>), grid, dim3(256), 0, s, A, lda, W, ldw, out, \
-                           ldo, stride, (int)M, (int)N, (int)K, (int)plan.kchunk, status)
-    if (M <= 16) {
-        HEAL_DEC(1);
-    } else if (M <= 32) {
-        HEAL_DEC(2);
-    } else {
-        HEAL_DEC(4);
-    }
+    const int nablk = (int)((K + KA - 1) / KA);
+    // 16-byte W loads need 16-byte aligned rows and whole k32 steps
+    const bool vec = (reinterpret_cast<uintptr_t>(W) & 15) == 0 && (ldw & 3) == 0 && (K & 31) == 0;
+#define HEAL_DEC(MT_)                                                                                     \
+    do {                                                                                                  \
+        const int64_t tot = (int64_t)nablk * STEPS * (MT_) * 64;                                          \
+        hipLaunchKernelGGL((asplit_kernel<MT_>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, A, \
+                           lda, (int)M, (int)K, nablk, ablk, status);                                     \
+        const int lds = 2 * block_bytes<MT_>();                                                           \
+        if (vec)                                                                                          \
+            hipLaunchKernelGGL((gemm_decode_kernel<MT_, true>), grid, dim3(256), lds, s, ablk, W, ldw, out, \
+                               ldo, stride, (int)M, (int)N, (int)K, (int)plan.kchunk, (int)plan.a_bytes, \
+                               status);                                                                   \
+        else                                                                                              \
+            hipLaunchKernelGGL((gemm_decode_kernel<MT_, false>), grid, dim3(256), lds, s, ablk, W, ldw,   \
+                               out, ldo, stride, (int)M, (int)N, (int)K, (int)plan.kchunk,                \
+                               (int)plan.a_bytes, status);                                                \
+    } while (0)
+    const int mt = mtiles(M);
+    if (mt == 1) HEAL_DEC(1);
+    else if (mt == 2) HEAL_DEC(2);
+    else HEAL_DEC(4);
 #undef HEAL_DEC
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
     const int64_t total = M * N;
     const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 256 * 16);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const float*>(workspace), plan.splits, M, N, C, ldc);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, part, plan.splits, M, N, C,
+                       ldc);
     return hipGetLastError();
 }
 

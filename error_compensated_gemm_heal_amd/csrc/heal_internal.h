@@ -74,6 +74,8 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, float* C, int64
                                int64_t N, int64_t K, hipStream_t s);
 
 // Decode path (M <= 64): fp32 W [N,K] streamed and split in registers.
+// Workspace: the split activation planes (a_bytes), then, 256-byte aligned,
+// the split-K partials (p_bytes).
 struct DecodePlan {
     int splits;        // number of K chunks (fixed by N and K only)
     int64_t kchunk;    // reduction length of one chunk (multiple of 256)

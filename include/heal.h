@@ -106,8 +106,9 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  * downcast happens at the kernel boundary.  The lo.lo term (2^-20) is
  * dropped.  Accuracy: normwise error max_ij |C - C_exact| / (|a_i| |b_j|)
  * within 2x that of a naive FP32 GEMM and below 1e-5.  The summation order
- * depends on (M, N, K) but not on the data.  For M <= 64 it also does not
- * depend on M, so decode-sized results do not change with batch size.
+ * depends on (M, N, K) but not on the data.  For M <= 64 (NK layout, K <
+ * 2^23, neither operand packed) it also does not depend on M, so
+ * decode-sized results do not change with batch size.
  *
  *   A      device fp32, lda >= K, 4-byte aligned (rows that are 16-byte
  *          aligned, lda % 4 == 0, take 16-byte vector loads)
@@ -122,7 +123,9 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  *   workspace  device, >= heal_gemm_f32c_workspace(M, N, K, flags) bytes,
  *          256-byte aligned (NULL allowed when that size is 0)
  *   dev_status  device, nullable; HEAL_FLAG_F16_RANGE as in heal_split_f32.
- * Limits: M, N, K < 2^31.  K == 0 writes zeros.
+ * Limits: M, N, K < 2^31.  K == 0 writes zeros.  In the M <= 64 case above,
+ * ldw < 2^26 (each 16-row slice of W is addressed with 32-bit byte offsets),
+ * else HEAL_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------ */
 heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t ldw,
                            float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
