@@ -34,9 +34,11 @@ namespace {
 
 constexpr int KA = 128;             // k block of activations per LDS buffer
 constexpr int STEPS = KA / 32;      // k32 steps per block
-constexpr int PF = 8;               // W prefetch distance in k32 steps
+constexpr int PF = 8;               // W prefetch distance in k32 steps (multiple of STEPS, <= 4 STEPS)
+constexpr int NW = 4;               // waves per workgroup
+constexpr int TARGET_WG = 512;      // workgroups aimed for (two per compute unit)
 constexpr int ROWS_PER_WAVE = 16;
-constexpr int DEC_ROWS = 4 * ROWS_PER_WAVE;   // W rows (outputs) per workgroup
+constexpr int DEC_ROWS = NW * ROWS_PER_WAVE;  // W rows (outputs) per workgroup
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -117,14 +119,14 @@ __device__ __forceinline__ float absmax8(float m, const float4& a, const float4&
 // buffer loads per lane.  Otherwise lanes load element by element with
 // bounds checks, and block boundaries wait for every load.
 template <int MT, bool VEC>
-__global__ __launch_bounds__(256) void gemm_decode_kernel(const unsigned char* __restrict__ Ablk,
+__global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const unsigned char* __restrict__ Ablk,
                                                           const float* __restrict__ W, int64_t ldw,
                                                           float* __restrict__ out, int64_t ldo,
                                                           int64_t split_stride, int M, int N, int K,
                                                           int kchunk, int a_total_bytes,
                                                           uint32_t* __restrict__ status) {
     constexpr int BB = block_bytes<MT>();
-    constexpr int DMA_PER_WAVE = BB / 1024 / 4;    // 1 KB per wave-wide direct-to-LDS load
+    constexpr int DMA_PER_WAVE = BB / 1024 / NW;   // 1 KB per wave-wide direct-to-LDS load
     extern __shared__ __attribute__((aligned(16))) unsigned char sa[];   // 2 x BB
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -140,12 +142,12 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(const unsigned char* _
     const int nblocks = (nsteps + STEPS - 1) / STEPS;
     const int blk0 = k_begin / KA;
 
-    // activation blocks: wave w copies 1 KB pieces w, w + 4, ... of a block
+    // activation blocks: wave w copies 1 KB pieces w, w + NW, ... of a block
     const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(Ablk, (uint32_t)a_total_bytes);
     auto dma_block = [&](int b, int buf) {
 #pragma unroll
         for (int i = 0; i < DMA_PER_WAVE; ++i) {
-            const int piece = wave + 4 * i;
+            const int piece = wave + NW * i;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_ptr)(sa + buf * BB + piece * 1024), 16,
                                                      (uint32_t)(lane * 16),
                                                      (uint32_t)((blk0 + b) * BB + piece * 1024), 0, 0);
@@ -234,9 +236,15 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(const unsigned char* _
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    for (int b = 0; b < nblocks; b += 2) {
+    static_assert(PF % STEPS == 0 && PF / STEPS <= 4, "W ring of whole blocks");
+    for (int b = 0; b < nblocks; b += PF / STEPS) {
         run_block(b, std::integral_constant<int, 0>{});
-        if (b + 1 < nblocks) run_block(b + 1, std::integral_constant<int, STEPS>{});
+        if constexpr (PF / STEPS > 1)
+            if (b + 1 < nblocks) run_block(b + 1, std::integral_constant<int, STEPS>{});
+        if constexpr (PF / STEPS > 2)
+            if (b + 2 < nblocks) run_block(b + 2, std::integral_constant<int, 2 * STEPS>{});
+        if constexpr (PF / STEPS > 3)
+            if (b + 3 < nblocks) run_block(b + 3, std::integral_constant<int, 3 * STEPS>{});
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // drain the clamped tail loads
     if (status && __builtin_amdgcn_ballot_w64(wmax >= 65520.0f) && lane == 0)
@@ -276,8 +284,8 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
     DecodePlan p{};
     const int64_t nblk = (N + DEC_ROWS - 1) / DEC_ROWS;
     const int64_t kblocks = std::max<int64_t>(1, (K + 255) / 256);
-    // about 512 workgroups (two per compute unit) in one round, without going over
-    int64_t want = std::max<int64_t>(1, 512 / std::max<int64_t>(nblk, 1));
+    // about TARGET_WG workgroups in one round, without going over
+    int64_t want = std::max<int64_t>(1, TARGET_WG / std::max<int64_t>(nblk, 1));
     want = std::min(want, kblocks);
     const int64_t per = (K + want - 1) / want;
     p.kchunk = std::max<int64_t>(256, (per + 255) / 256 * 256);
@@ -311,11 +319,11 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const float* W, int64
                            lda, (int)M, (int)K, nablk, ablk, status);                                     \
         const int lds = 2 * block_bytes<MT_>();                                                           \
         if (vec)                                                                                          \
-            hipLaunchKernelGGL((gemm_decode_kernel<MT_, true>), grid, dim3(256), lds, s, ablk, W, ldw, out, \
+            hipLaunchKernelGGL((gemm_decode_kernel<MT_, true>), grid, dim3(64 * NW), lds, s, ablk, W, ldw, out, \
                                ldo, stride, (int)M, (int)N, (int)K, (int)plan.kchunk, (int)plan.a_bytes, \
                                status);                                                                   \
         else                                                                                              \
-            hipLaunchKernelGGL((gemm_decode_kernel<MT_, false>), grid, dim3(256), lds, s, ablk, W, ldw,   \
+            hipLaunchKernelGGL((gemm_decode_kernel<MT_, false>), grid, dim3(64 * NW), lds, s, ablk, W, ldw, \
                                out, ldo, stride, (int)M, (int)N, (int)K, (int)plan.kchunk,                \
                                (int)plan.a_bytes, status);                                                \
     } while (0)
