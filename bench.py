@@ -227,8 +227,17 @@ def main():
     W = build_workload(sel)
     rows = [r for r in make_rows(W) if r[0] in sel]
 
+    # Before each row, an untimed read of a 512 MiB buffer (twice the
+    # 256 MB Infinity Cache) evicts whatever the previous row left there: the
+    # row's own inputs (so weights are not served from the cache) and the
+    # previous row's dirty lines (so their write-back to HBM does not land in
+    # this row's time).
+    flush = torch.ones(512 << 18, dtype=torch.float32, device="cuda:0")
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda:0")
+
     def step(events=None):
         for i, (name, fn, _, _) in enumerate(rows):
+            torch.amax(flush, dim=0, out=flush_out)
             if events is not None:
                 events[i][0].record()
             fn()
