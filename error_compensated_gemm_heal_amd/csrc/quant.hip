@@ -8,7 +8,8 @@
 // Both kernels are HBM-bound streaming maps (6 bytes per element plus 4 per
 // row).  A row of D floats is owned by a group of LPR lanes of one wave
 // (LPR = D/4 rounded up to a power of two, at most 64).  Each lane holds
-// NCH float4 chunks in registers, so a row is read from HBM once.  The row
+// NCH float4 chunks in registers, so a row is read from HBM once; a wave
+// issues the loads of several row groups before processing any of them.  The row
 // maximum is a butterfly over the group, which is exact and order-free.  The
 // per-element arithmetic follows the formula's own order with correctly
 // rounded fp32 operations: t = fl(32767 x), u = fl(t / M), q = rne(u).  That
@@ -19,52 +20,67 @@ namespace heal {
 
 namespace {
 
+// Each wave step covers U groups of RPW consecutive rows; all U x NCH
+// loads of a step are issued before any of them is used, so a wave keeps
+// U x 1 KB (or more) of reads in flight.
+template <int LPR, int NCH>
+struct RowTiling {
+    static constexpr int RPW = 64 / LPR;                 // rows per wave per group
+    static constexpr int U = NCH >= 4 ? 1 : 4 / NCH;     // row groups per step
+    static constexpr int ROWS = U * RPW;                 // rows per wave per step
+};
+
 template <int LPR, int NCH>
 __global__ __launch_bounds__(256) void quant_kernel(const float* __restrict__ X, int64_t rows, int D,
                                                     int64_t ldx, int16_t* __restrict__ codes,
                                                     int64_t ldq, float* __restrict__ scales) {
-    constexpr int RPW = 64 / LPR;  // rows per wave per step
+    using RT = RowTiling<LPR, NCH>;
     const int lane = threadIdx.x & 63;
-    const int sub = lane / LPR;     // which row of the wave's group
+    const int sub = lane / LPR;     // which row of a group
     const int gl = lane % LPR;      // lane within the row group
     const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
     const int d4 = D >> 2;
 
-    for (int64_t r0 = wave * RPW; r0 < rows; r0 += nwaves * RPW) {
-        const int64_t r = r0 + sub;
-        const bool live = r < rows;
-        float4 x[NCH];
-        float m = 0.0f;
+    for (int64_t r0 = wave * RT::ROWS; r0 < rows; r0 += nwaves * RT::ROWS) {
+        float4 x[RT::U][NCH];
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int j = gl + c * LPR;
-            if (live && j < d4) {
-                x[c] = *reinterpret_cast<const float4*>(X + r * ldx + 4 * j);
-            } else {
-                x[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int u = 0; u < RT::U; ++u) {
+            const int64_t r = r0 + u * RT::RPW + sub;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int j = gl + c * LPR;
+                x[u][c] = (r < rows && j < d4) ? *reinterpret_cast<const float4*>(X + r * ldx + 4 * j)
+                                               : make_float4(0.f, 0.f, 0.f, 0.f);
             }
-            m = fmaxf(m, fmaxf(fmaxf(__builtin_fabsf(x[c].x), __builtin_fabsf(x[c].y)),
-                               fmaxf(__builtin_fabsf(x[c].z), __builtin_fabsf(x[c].w))));
         }
 #pragma unroll
-        for (int off = LPR / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-        if (!live) continue;
-        if (gl == 0) scales[r] = (m == 0.0f) ? 0.0f : __fdiv_rn(m, 32767.0f);
+        for (int u = 0; u < RT::U; ++u) {
+            const int64_t r = r0 + u * RT::RPW + sub;
+            float m = 0.0f;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int j = gl + c * LPR;
-            if (j < d4) {
-                short4 q;
-                if (m == 0.0f) {
-                    q = make_short4(0, 0, 0, 0);
-                } else {
-                    q.x = (short)__builtin_rintf(__fdiv_rn(__fmul_rn(32767.0f, x[c].x), m));
-                    q.y = (short)__builtin_rintf(__fdiv_rn(__fmul_rn(32767.0f, x[c].y), m));
-                    q.z = (short)__builtin_rintf(__fdiv_rn(__fmul_rn(32767.0f, x[c].z), m));
-                    q.w = (short)__builtin_rintf(__fdiv_rn(__fmul_rn(32767.0f, x[c].w), m));
+            for (int c = 0; c < NCH; ++c)
+                m = fmaxf(m, fmaxf(fmaxf(__builtin_fabsf(x[u][c].x), __builtin_fabsf(x[u][c].y)),
+                                   fmaxf(__builtin_fabsf(x[u][c].z), __builtin_fabsf(x[u][c].w))));
+#pragma unroll
+            for (int off = LPR / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+            if (r >= rows) continue;
+            if (gl == 0) scales[r] = (m == 0.0f) ? 0.0f : __fdiv_rn(m, 32767.0f);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int j = gl + c * LPR;
+                if (j < d4) {
+                    short4 q;
+                    if (m == 0.0f) {
+                        q = make_short4(0, 0, 0, 0);
+                    } else {
+                        q.x = (short)__builtin_rintf(__fdiv_rn(__fmul_rn(32767.0f, x[u][c].x), m));
+                        q.y = (short)__builtin_rintf(__fdiv_rn(__fmul_rn(32767.0f, x[u][c].y), m));
+                        q.z = (short)__builtin_rintf(__fdiv_rn(__fmul_rn(32767.0f, x[u][c].z), m));
+                        q.w = (short)__builtin_rintf(__fdiv_rn(__fmul_rn(32767.0f, x[u][c].w), m));
+                    }
+                    *reinterpret_cast<short4*>(codes + r * ldq + 4 * j) = q;
                 }
-                *reinterpret_cast<short4*>(codes + r * ldq + 4 * j) = q;
             }
         }
     }
@@ -75,40 +91,56 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int16_t* __restrict_
                                                       int D, int64_t ldq, const float* __restrict__ scales,
                                                       void* __restrict__ out, void* __restrict__ out_lo,
                                                       int64_t ldo) {
-    constexpr int RPW = 64 / LPR;
+    using RT = RowTiling<LPR, NCH>;
     const int lane = threadIdx.x & 63;
     const int sub = lane / LPR;
     const int gl = lane % LPR;
     const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
     const int d4 = D >> 2;
-    for (int64_t r0 = wave * RPW; r0 < rows; r0 += nwaves * RPW) {
-        const int64_t r = r0 + sub;
-        if (r >= rows) continue;
-        const float s = FMT == HEAL_DQ_F32 ? scales[r] : 0.0f;
+    for (int64_t r0 = wave * RT::ROWS; r0 < rows; r0 += nwaves * RT::ROWS) {
+        short4 qv[RT::U][NCH];
+        float sv[RT::U];
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int j = gl + c * LPR;
-            if (j >= d4) continue;
-            const short4 q = *reinterpret_cast<const short4*>(codes + r * ldq + 4 * j);
-            if constexpr (FMT == HEAL_DQ_F32) {
-                float4 o = make_float4(__fmul_rn((float)q.x, s), __fmul_rn((float)q.y, s),
-                                       __fmul_rn((float)q.z, s), __fmul_rn((float)q.w, s));
-                *reinterpret_cast<float4*>(static_cast<float*>(out) + r * ldo + 4 * j) = o;
-            } else {
-                const float qv[4] = {(float)q.x, (float)q.y, (float)q.z, (float)q.w};
-                uint16_t h[4], l[4];
+        for (int u = 0; u < RT::U; ++u) {
+            const int64_t r = r0 + u * RT::RPW + sub;
+            sv[u] = (FMT == HEAL_DQ_F32 && r < rows) ? scales[r] : 0.0f;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    _Float16 hh, ll;
-                    split_one(qv[e], hh, ll);  // exact for every int16 code
-                    h[e] = f16_bits(hh);
-                    l[e] = f16_bits(ll);
+            for (int c = 0; c < NCH; ++c) {
+                const int j = gl + c * LPR;
+                qv[u][c] = (r < rows && j < d4) ? *reinterpret_cast<const short4*>(codes + r * ldq + 4 * j)
+                                                : make_short4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < RT::U; ++u) {
+            const int64_t r = r0 + u * RT::RPW + sub;
+            if (r >= rows) continue;
+            const float s = sv[u];
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int j = gl + c * LPR;
+                if (j >= d4) continue;
+                const short4 q = qv[u][c];
+                if constexpr (FMT == HEAL_DQ_F32) {
+                    float4 o = make_float4(__fmul_rn((float)q.x, s), __fmul_rn((float)q.y, s),
+                                           __fmul_rn((float)q.z, s), __fmul_rn((float)q.w, s));
+                    *reinterpret_cast<float4*>(static_cast<float*>(out) + r * ldo + 4 * j) = o;
+                } else {
+                    const float qf[4] = {(float)q.x, (float)q.y, (float)q.z, (float)q.w};
+                    uint16_t h[4], l[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        _Float16 hh, ll;
+                        split_one(qf[e], hh, ll);  // exact for every int16 code
+                        h[e] = f16_bits(hh);
+                        l[e] = f16_bits(ll);
+                    }
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + r * ldo + 4 * j) =
+                        make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out_lo) + r * ldo + 4 * j) =
+                        make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
                 }
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + r * ldo + 4 * j) =
-                    make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out_lo) + r * ldo + 4 * j) =
-                    make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
             }
         }
     }
@@ -124,9 +156,8 @@ void row_shape(int64_t D, int& lpr, int& nch) {
     while (nch < c) nch <<= 1;
 }
 
-unsigned grid_for(int64_t rows, int lpr) {
-    const int64_t rpw = 64 / lpr;
-    const int64_t waves = (rows + rpw - 1) / rpw;
+unsigned grid_for(int64_t rows, int rows_per_wave_step) {
+    const int64_t waves = (rows + rows_per_wave_step - 1) / rows_per_wave_step;
     int64_t blocks = (waves + 3) / 4;  // 4 waves per 256-thread block
     const int64_t cap = 256 * 40;      // enough resident waves to cover HBM latency
     return (unsigned)std::max<int64_t>(1, std::min(blocks, cap));
@@ -136,7 +167,7 @@ unsigned grid_for(int64_t rows, int lpr) {
 
 #define HEAL_QUANT_CASE(L, C)                                                                        \
     if (lpr == L && nch == C) {                                                                      \
-        hipLaunchKernelGGL((quant_kernel<L, C>), dim3(grid_for(rows, L)), dim3(256), 0, s, X, rows, \
+        hipLaunchKernelGGL((quant_kernel<L, C>), dim3(grid_for(rows, RowTiling<L, C>::ROWS)), dim3(256), 0, s, X, rows, \
                            (int)D, ldx, codes, ldq, scales);                                         \
         return hipGetLastError();                                                                    \
     }
@@ -156,10 +187,10 @@ hipError_t launch_quant(const float* X, int64_t rows, int64_t D, int64_t ldx, in
 #define HEAL_DQ_CASE(L, C)                                                                            \
     if (lpr == L && nch == C) {                                                                       \
         if (fmt == HEAL_DQ_F32)                                                                       \
-            hipLaunchKernelGGL((dequant_kernel<L, C, HEAL_DQ_F32>), dim3(grid_for(rows, L)), dim3(256), \
+            hipLaunchKernelGGL((dequant_kernel<L, C, HEAL_DQ_F32>), dim3(grid_for(rows, RowTiling<L, C>::ROWS)), dim3(256), \
                                0, s, codes, rows, (int)D, ldq, scales, out, out_lo, ldo);             \
         else                                                                                          \
-            hipLaunchKernelGGL((dequant_kernel<L, C, HEAL_DQ_F16X2>), dim3(grid_for(rows, L)),        \
+            hipLaunchKernelGGL((dequant_kernel<L, C, HEAL_DQ_F16X2>), dim3(grid_for(rows, RowTiling<L, C>::ROWS)), \
                                dim3(256), 0, s, codes, rows, (int)D, ldq, scales, out, out_lo, ldo);  \
         return hipGetLastError();                                                                     \
     }
