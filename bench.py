@@ -11,11 +11,16 @@ workload (inputs resident in HBM before timing starts):
            x (K,N) in {(4096,4096), (4096,1024), (4096,14336), (14336,4096)},
            fp32 weights streamed from HBM (M-outer order, so consecutive calls
            touch different weights and the 256 MB MALL cannot serve repeats)
+  decode_w16  the same 16 GEMMs with the weights held as binary16 (2 bytes each;
+           the paper's two-product form for 16-bit weights)
   quant    INT16 quant of a Qwen3-8B-like layer's Q/K/V: 32 x 2048 tokens,
            32 + 8 + 8 heads of 128 (one [65536, 48, 128] launch)
   dequant  INT16 -> fp32 dequant of the same codes
   attn     decode attention over the INT16 KV cache: batch 16, context 8192,
            32 query / 8 KV heads, D = 128
+
+Before each row an untimed read of a 512 MiB buffer evicts the Infinity
+Cache, so no row is served or slowed by what the previous one left there.
 
 Output: one JSON line.  `value` is the metric's first half, FP32-accurate GEMM
 TFLOP/s on the prefill workload (useful flops 2MNK over the time of split +
@@ -71,7 +76,7 @@ def build_workload(rows_sel):
         W["prefill"] = pre
         log(f"[bench] prefill inputs ready ({time.time() - t0:.1f}s)")
 
-    if "decode" in rows_sel:
+    if "decode" in rows_sel or "decode_w16" in rows_sel:
         weights = {}
         acts = {}
         for i, (K, N) in enumerate(WL.LLAMA3_8B_DECODE_KN):
@@ -87,6 +92,13 @@ def build_workload(rows_sel):
                 C = torch.empty((M, N), dtype=torch.float32, device=dev)
                 calls.append(dict(M=M, K=K, N=N, A=acts[(K, N)][:M], W=Wd, C=C, ws=ws))
         W["decode"] = calls
+        # the same layers with 16-bit weights (the paper's two-product form):
+        # the fp32 weights rounded to binary16, as an FP16 checkpoint holds them
+        calls16 = []
+        w16 = {kn: w.half() for kn, w in weights.items()}
+        for c in calls:
+            calls16.append(dict(c, W=w16[(c["K"], c["N"])]))
+        W["decode_w16"] = calls16
         log(f"[bench] decode inputs ready ({time.time() - t0:.1f}s)")
 
     if "quant" in rows_sel or "dequant" in rows_sel:
@@ -147,6 +159,15 @@ def make_rows(W):
 
         dbytes = sum(4 * (c["K"] * c["N"] + c["M"] * c["K"] + c["M"] * c["N"]) for c in calls)
         rows.append(("decode", run_decode, dbytes, "B"))
+    if "decode_w16" in W:
+        calls16 = W["decode_w16"]
+
+        def run_decode16():
+            for c in calls16:
+                heal.heal_gemm_f32c(c["A"], c["W"], C=c["C"], workspace=c["ws"])
+
+        d16bytes = sum(2 * c["K"] * c["N"] + 4 * (c["M"] * c["K"] + c["M"] * c["N"]) for c in calls16)
+        rows.append(("decode_w16", run_decode16, d16bytes, "B"))
     if "quant" in W:
         q = W["quant"]
         qbytes = q["n"] * (4 + 2) + q["rows"] * 4
@@ -191,7 +212,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--rows", default="split,prefill,decode,quant,dequant,attn",
+    ap.add_argument("--rows", default="split,prefill,decode,decode_w16,quant,dequant,attn",
                     help="comma-separated subset of rows to run (profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -272,7 +293,8 @@ def main():
            "dtype": "fp32 in/out; fp16 hi/lo MFMA products, fp32 accumulate; int16 codes",
            "data": "synthetic (seeded; model-shaped, see heal_workloads.py)"}
     cfg = {"workload": "HEAL hot path step: split + prefill GEMM (M=2048; K,N = 4096,14336 and 14336,4096), "
-                       "16 decode GEMMs (M=1,8,32,64 x Llama-3-8B q/o, k/v, gate/up, down), INT16 quant + dequant "
+                       "16 decode GEMMs (M=1,8,32,64 x Llama-3-8B q/o, k/v, gate/up, down; fp32 and fp16 weights), "
+                       "INT16 quant + dequant "
                        "(32x2048 tokens, 32+8+8 heads x 128), INT16 decode attention (B=16, T=8192, 32/8 heads)",
            "rows": sorted(sel)}
     res["config"] = cfg

@@ -15,7 +15,8 @@ __all__ = [
     "HealError", "lib", "heal_status_str", "heal_version", "heal_split_f32", "heal_gemm_f32c",
     "heal_gemm_f32c_workspace", "heal_pack_w", "heal_pack_w_bytes", "heal_qkv_quant_i16",
     "heal_kv_dequant_i16", "heal_attn_decode_i16", "heal_attn_decode_workspace", "PackedOperand",
-    "PackedWeight", "HEAL_W_NK", "HEAL_W_KN", "HEAL_W_PACKED", "HEAL_A_PACKED", "HEAL_FLAG_F16_RANGE",
+    "PackedWeight", "HEAL_W_NK", "HEAL_W_KN", "HEAL_W_PACKED", "HEAL_A_PACKED", "HEAL_W_F16",
+    "HEAL_FLAG_F16_RANGE",
     "HEAL_DQ_F32", "HEAL_DQ_F16X2",
     "LIB_PATH",
 ]
@@ -23,7 +24,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libheal.so")
 
 HEAL_OK = 0
-HEAL_W_NK, HEAL_W_KN, HEAL_W_PACKED, HEAL_A_PACKED = 0, 1, 2, 4
+HEAL_W_NK, HEAL_W_KN, HEAL_W_PACKED, HEAL_A_PACKED, HEAL_W_F16 = 0, 1, 2, 4, 8
 HEAL_FLAG_F16_RANGE = 1
 HEAL_DQ_F32, HEAL_DQ_F16X2 = 0, 1
 
@@ -146,9 +147,18 @@ def heal_pack_w_bytes(N: int, K: int) -> int:
     return lib().heal_pack_w_bytes(N, K)
 
 
+def _weight_dtype_flag(W: torch.Tensor) -> int:
+    """fp32 weights, or float16 ones (binary16 values: the two-product form)."""
+    if W.dtype == torch.float16:
+        return HEAL_W_F16
+    if W.dtype != torch.float32:
+        raise TypeError(f"W must be float32 or float16, got {W.dtype}")
+    return 0
+
+
 def heal_pack_w(W: torch.Tensor, w_layout: str = "nk", dev_status=None, out=None) -> PackedOperand:
-    _dev(W, "W", torch.float32)
-    flags = HEAL_W_KN if w_layout == "kn" else HEAL_W_NK
+    _dev(W, "W")
+    flags = (HEAL_W_KN if w_layout == "kn" else HEAL_W_NK) | _weight_dtype_flag(W)
     if w_layout == "kn":
         K, N = W.shape
     else:
@@ -185,13 +195,14 @@ def heal_gemm_f32c(A, W, w_layout: str = "nk", C=None, workspace=None, dev_statu
             raise ValueError("packed weight has a different K")
         N, flags, wptr, ldw = W.rows, HEAL_W_PACKED, _ptr(W.buf), 0
     else:
-        _dev(W, "W", torch.float32)
+        _dev(W, "W")
         if w_layout == "kn":
             K2, N = W.shape
             flags = HEAL_W_KN
         else:
             N, K2 = W.shape
             flags = HEAL_W_NK
+        flags |= _weight_dtype_flag(W)
         if K2 != K:
             raise ValueError("inner dimensions differ")
         wptr, ldw = _ptr(W), _rowmajor_ld(W, "W")

@@ -24,6 +24,7 @@ bool use_decode(int64_t M, int64_t K, uint32_t flags) {
            (flags & HEAL_W_KN) == 0;
 }
 constexpr int64_t kMaxDecodeLdw = (int64_t)1 << 26;
+constexpr int64_t kMaxDecodeLda = (int64_t)1 << 24;   // A (<= 64 rows) addressed with 32-bit byte offsets
 
 __global__ void zero_rows_kernel(float* C, int64_t ldc, int64_t M, int64_t N) {
     const int64_t total = M * N;
@@ -69,17 +70,18 @@ size_t heal_pack_w_bytes(int64_t N, int64_t K) {
     return (size_t)pack_bytes(N, K);
 }
 
-heal_status heal_pack_w(const float* W, int64_t ldw, int64_t N, int64_t K, uint32_t flags,
+heal_status heal_pack_w(const void* W, int64_t ldw, int64_t N, int64_t K, uint32_t flags,
                         void* packed, size_t packed_bytes, uint32_t* dev_status, void* stream) {
     if (N < 0 || K < 0 || N >= kMaxDim || K >= kMaxDim) return HEAL_ERR_SHAPE;
-    if (flags & ~(uint32_t)HEAL_W_KN) return HEAL_ERR_UNSUPPORTED;
+    if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_F16)) return HEAL_ERR_UNSUPPORTED;
     if (N == 0 || K == 0) return HEAL_OK;
     if (!W || !packed) return HEAL_ERR_NULL;
     const bool kn = flags & HEAL_W_KN;
+    const bool f16 = flags & HEAL_W_F16;
     if (ldw < (kn ? N : K)) return HEAL_ERR_STRIDE;
-    if (misaligned(W, 4) || misaligned(packed, 256) || misaligned(dev_status, 4)) return HEAL_ERR_ALIGN;
+    if (misaligned(W, f16 ? 2 : 4) || misaligned(packed, 256) || misaligned(dev_status, 4)) return HEAL_ERR_ALIGN;
     if (packed_bytes < (size_t)pack_bytes(N, K)) return HEAL_ERR_WORKSPACE;
-    return hip_status(launch_pack(W, ldw, N, K, kn ? 1 : 0, packed, dev_status,
+    return hip_status(launch_pack(W, f16, ldw, N, K, kn ? 1 : 0, packed, dev_status,
                                   static_cast<hipStream_t>(stream)));
 }
 
@@ -99,7 +101,8 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
                            void* workspace, size_t workspace_bytes, uint32_t* dev_status,
                            void* stream) {
     if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return HEAL_ERR_SHAPE;
-    if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_PACKED | HEAL_A_PACKED)) return HEAL_ERR_UNSUPPORTED;
+    if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_PACKED | HEAL_A_PACKED | HEAL_W_F16)) return HEAL_ERR_UNSUPPORTED;
+    if ((flags & HEAL_W_F16) && (flags & HEAL_W_PACKED)) return HEAL_ERR_UNSUPPORTED;   // packed: already split
     if (M == 0 || N == 0) return HEAL_OK;
     if (!C) return HEAL_ERR_NULL;
     if (ldc < N) return HEAL_ERR_STRIDE;
@@ -113,9 +116,10 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
     const bool packed = flags & HEAL_W_PACKED;
     const bool a_packed = flags & HEAL_A_PACKED;
     const bool kn = flags & HEAL_W_KN;
+    const bool wf16 = flags & HEAL_W_F16;
     if (!a_packed && lda < K) return HEAL_ERR_STRIDE;
     if (!packed && ldw < (kn ? N : K)) return HEAL_ERR_STRIDE;
-    if (misaligned(A, a_packed ? 256 : 4) || misaligned(W, packed ? 256 : 4) || misaligned(C, 4) ||
+    if (misaligned(A, a_packed ? 256 : 4) || misaligned(W, packed ? 256 : (wf16 ? 2 : 4)) || misaligned(C, 4) ||
         misaligned(dev_status, 4))
         return HEAL_ERR_ALIGN;
     const size_t need = heal_gemm_f32c_workspace(M, N, K, flags);
@@ -125,17 +129,16 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
     }
 
     if (use_decode(M, K, flags)) {
-        if (ldw >= kMaxDecodeLdw) return HEAL_ERR_UNSUPPORTED;
+        if (ldw >= kMaxDecodeLdw || lda >= kMaxDecodeLda) return HEAL_ERR_UNSUPPORTED;
         const DecodePlan p = decode_plan(M, N, K);
         unsigned char* ws = static_cast<unsigned char*>(workspace);
-        return hip_status(launch_gemm_decode(A, lda, static_cast<const float*>(W), ldw, C, ldc, M, N,
-                                             K, ws, p, dev_status, s));
+        return hip_status(launch_gemm_decode(A, lda, W, wf16, ldw, C, ldc, M, N, K, ws, p, dev_status, s));
     }
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     const void* apk = A;
     const void* bpk = W;
     if (!a_packed) {
-        hipError_t e = launch_pack(A, lda, M, K, 0, ws, dev_status, s);
+        hipError_t e = launch_pack(A, false, lda, M, K, 0, ws, dev_status, s);
         if (e != hipSuccess) return HEAL_ERR_HIP;
         apk = ws;
         ws += round256(pack_bytes(M, K));
@@ -143,7 +146,7 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
     if (!packed) {
         void* wpk = ws;
         hipError_t e;
-        e = launch_pack(static_cast<const float*>(W), ldw, N, K, kn ? 1 : 0, wpk, dev_status, s);
+        e = launch_pack(W, wf16, ldw, N, K, kn ? 1 : 0, wpk, dev_status, s);
         if (e != hipSuccess) return HEAL_ERR_HIP;
         bpk = wpk;
     }

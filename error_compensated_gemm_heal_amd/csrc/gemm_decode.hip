@@ -6,11 +6,15 @@
 // but shaped for a skinny activation, where the weight is the traffic:
 //  * W is read once from HBM as fp32 [N, K] (4 bytes per element, the same
 //    bytes as its two fp16 parts) and split into hi/lo in registers;
-//  * the activation (<= 64 rows) is split once per call by a small kernel
-//    into hi/lo planes already in MFMA operand order (see asplit_kernel);
-//    each workgroup copies 128-wide k blocks of it into LDS with
-//    direct-to-LDS loads, double-buffered, so staging costs no VALU work
-//    and every operand read is one conflict-free 16-byte LDS access;
+//  * the activation (<= 64 rows) is staged in 128-wide k blocks in a
+//    double-buffered LDS tile, in MFMA operand order, so every operand read
+//    is one conflict-free 16-byte LDS access.  Up to 16 rows, each
+//    workgroup loads the next block into registers while the current one
+//    is in use and splits it into hi/lo itself (no extra pass or launch);
+//    above 16 rows, where that split would be repeated by every workgroup,
+//    a small kernel splits the activation once per call into operand-ordered
+//    planes (asplit_kernel) and workgroups copy blocks of them into LDS with
+//    direct-to-LDS loads;
 //  * v_mfma_f32_16x16x32_f16 with the activation as the 16-row operand and W
 //    as the 16-column operand (16 W rows per wave), so output columns are
 //    consecutive lanes;
@@ -40,11 +44,12 @@ constexpr int TARGET_WG = 512;      // workgroups aimed for (two per compute uni
 constexpr int ROWS_PER_WAVE = 16;
 constexpr int DEC_ROWS = NW * ROWS_PER_WAVE;  // W rows (outputs) per workgroup
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // s_waitcnt immediate that waits until at most n vector memory operations
 // are outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt not waited on).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// s_waitcnt immediate that waits for all LDS operations (lgkmcnt 0) only.
+constexpr int lgkmcnt0_imm() { return 0xF | (0x3 << 14) | (0x7 << 4); }
 
 __device__ __forceinline__ void mfma16(const half8& a, const half8& b, floatx4& c) {
     c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -115,18 +120,28 @@ __device__ __forceinline__ float absmax8(float m, const float4& a, const float4&
                           fmaxf(__builtin_fabsf(b.z), __builtin_fabsf(b.w))));
 }
 
-// VEC: W rows 16-byte aligned and K % 32 == 0, so every step is two 16-byte
-// buffer loads per lane.  Otherwise lanes load element by element with
-// bounds checks, and block boundaries wait for every load.
-template <int MT, bool VEC>
-__global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const unsigned char* __restrict__ Ablk,
-                                                          const float* __restrict__ W, int64_t ldw,
-                                                          float* __restrict__ out, int64_t ldo,
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// VEC: W rows aligned to the load width and K % 32 == 0, so every step is two
+// buffer loads per lane (16 bytes each for fp32 W, 8 for fp16 W).  Otherwise
+// lanes load element by element with bounds checks, and block boundaries
+// wait for every load.
+// WF16: W holds binary16 values, exact in fp16: its residual is zero, so each
+// step keeps two products, A_hi.W and A_lo.W (2^-10 applied at the end).
+// AVEC: A rows 16-byte aligned, activation units load as one 16-byte load.
+// MT == 1 stages A itself (A, lda); MT > 1 copies the pre-split blocks (Ablk).
+template <int MT, bool VEC, bool WF16, bool AVEC>
+__global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const float* __restrict__ A, int64_t lda,
+                                                          const unsigned char* __restrict__ Ablk,
+                                                          int a_total_bytes, const void* __restrict__ W,
+                                                          int64_t ldw, float* __restrict__ out, int64_t ldo,
                                                           int64_t split_stride, int M, int N, int K,
-                                                          int kchunk, int a_total_bytes,
-                                                          uint32_t* __restrict__ status) {
+                                                          int kchunk, uint32_t* __restrict__ status) {
     constexpr int BB = block_bytes<MT>();
-    constexpr int DMA_PER_WAVE = BB / 1024 / NW;   // 1 KB per wave-wide direct-to-LDS load
+    constexpr bool INK = MT == 1;                   // split the activation in the kernel
+    constexpr int AU = 2 * MT;                      // 4-wide activation units per thread per block
+    constexpr int DMA_PER_WAVE = BB / 1024 / NW;    // 1 KB per wave-wide direct-to-LDS load
     extern __shared__ __attribute__((aligned(16))) unsigned char sa[];   // 2 x BB
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -140,15 +155,69 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const unsigned cha
     const int k_end = min(k_begin + kchunk, K);
     const int nsteps = (k_end - k_begin + 31) / 32;
     const int nblocks = (nsteps + STEPS - 1) / STEPS;
-    const int blk0 = k_begin / KA;
 
-    // activation blocks: wave w copies 1 KB pieces w, w + NW, ... of a block
-    const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(Ablk, (uint32_t)a_total_bytes);
-    auto dma_block = [&](int b, int buf) {
+    // ---- activation blocks.  Unit x = tid + 256 i (i < AU) of a block is 4
+    //      consecutive k of one row: r = x % 16, g = (x / 16) % 4, half =
+    //      (x / 64) % 2, step s = (x / 128) % 4, tile t = x / 512; it holds
+    //      row 16 t + r at k = 128 b + 32 s + 16 half + 4 g .. + 3, and its
+    //      hi and lo halves go to the 16-byte operand slot (s, t, lane 16 g + r),
+    //      bytes 8 half .. 8 half + 7, of the hi and lo planes.
+    float4 areg[AU];
+    // rows >= M fall outside the resource and read as zero; k past the
+    // chunk end is zeroed when the block is stored
+    const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(A, (uint32_t)((int64_t)M * lda * 4));
+    auto unit_k = [&](int b, int x) {
+        return k_begin + KA * b + 32 * ((x >> 7) & 3) + 16 * ((x >> 6) & 1) + 4 * ((x >> 4) & 3);
+    };
+    auto load_a = [&](int b) {
+#pragma unroll
+        for (int i = 0; i < AU; ++i) {
+            const int x = tid + 256 * i;
+            const int m = 16 * (x >> 9) + (x & 15);
+            const uint32_t off = (uint32_t)(((int64_t)m * lda + unit_k(b, x)) * 4);
+            if constexpr (AVEC) {
+                areg[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, off, 0, 0));
+            } else {
+                areg[i] = make_float4(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(arsrc, off, 0, 0)),
+                                      __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(arsrc, off + 4, 0, 0)),
+                                      __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(arsrc, off + 8, 0, 0)),
+                                      __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(arsrc, off + 12, 0, 0)));
+            }
+        }
+    };
+    float amax = 0.0f;
+    auto store_a = [&](int b) {
+        unsigned char* base = sa + (b & 1) * BB;
+#pragma unroll
+        for (int i = 0; i < AU; ++i) {
+            const int x = tid + 256 * i;
+            const int r = x & 15, gg = (x >> 4) & 3, half = (x >> 6) & 1, st = (x >> 7) & 3, t = x >> 9;
+            const int k = unit_k(b, x);
+            const float v[4] = {k < k_end ? areg[i].x : 0.0f, k + 1 < k_end ? areg[i].y : 0.0f,
+                                k + 2 < k_end ? areg[i].z : 0.0f, k + 3 < k_end ? areg[i].w : 0.0f};
+            half4 h, l;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                _Float16 hh, ll;
+                split_one(v[j], hh, ll);
+                h[j] = hh;
+                l[j] = ll;
+                amax = fmaxf(amax, __builtin_fabsf(v[j]));
+            }
+            const int off = ((st * MT + t) * 64 + 16 * gg + r) * 16 + 8 * half;
+            *reinterpret_cast<half4*>(base + off) = h;
+            *reinterpret_cast<half4*>(base + BB / 2 + off) = l;
+        }
+    };
+
+    // pre-split activation blocks: wave w copies 1 KB pieces w, w + NW, ...
+    const int blk0 = k_begin / KA;
+    const __amdgpu_buffer_rsrc_t pbrsrc = make_rsrc(Ablk, (uint32_t)a_total_bytes);
+    auto dma_block = [&](int b) {
 #pragma unroll
         for (int i = 0; i < DMA_PER_WAVE; ++i) {
             const int piece = wave + NW * i;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_ptr)(sa + buf * BB + piece * 1024), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(pbrsrc, (lds_ptr)(sa + (b & 1) * BB + piece * 1024), 16,
                                                      (uint32_t)(lane * 16),
                                                      (uint32_t)((blk0 + b) * BB + piece * 1024), 0, 0);
         }
@@ -156,27 +225,48 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const unsigned cha
 
     // W: lane reads row n, k = k_begin + 32 step + {4g.., 16+4g..}
     // (scalars made explicit: the buffer resource must live in SGPRs)
+    constexpr int ESZ = WF16 ? 2 : 4;          // bytes per W element
+    constexpr int PFW = PF;                    // W steps in flight
+    using WReg = std::conditional_t<WF16, u32x4, u32x8>;   // one step's 8 W values
     const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(ROWS_PER_WAVE, N - n0)));
     const int wrow0 = __builtin_amdgcn_readfirstlane(min(n0, N - 1));
+    const unsigned char* Wb = static_cast<const unsigned char*>(W);
     const __amdgpu_buffer_rsrc_t wrsrc =
-        make_rsrc(W + (int64_t)wrow0 * ldw, (uint32_t)((int64_t)nrows * ldw * 4));
-    const uint32_t wlane = (uint32_t)((lane & 15) * ldw * 4 + (int64_t)(k_begin + 4 * g) * 4);
-    auto load_w = [&](int step, float4& a, float4& b) {
+        make_rsrc(Wb + (int64_t)wrow0 * ldw * ESZ, (uint32_t)((int64_t)nrows * ldw * ESZ));
+    const uint32_t wlane = (uint32_t)((lane & 15) * ldw * ESZ + (int64_t)(k_begin + 4 * g) * ESZ);
+    auto load_w = [&](int step, WReg& w) {
         if (VEC) {
-            const uint32_t off = wlane + (uint32_t)(step * 128);
-            a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off, 0, 0));
-            b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off + 64, 0, 0));
-        } else {
-            const float* wrow = W + (int64_t)(row_ok ? n : 0) * ldw;
-            const int ka = k_begin + 32 * step + 4 * g, kb = ka + 16;
-            float t[8];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                t[j] = (row_ok && ka + j < k_end) ? wrow[ka + j] : 0.f;
-                t[4 + j] = (row_ok && kb + j < k_end) ? wrow[kb + j] : 0.f;
+            const uint32_t off = wlane + (uint32_t)(step * 32 * ESZ);
+            if constexpr (WF16) {
+                const auto a = __builtin_amdgcn_raw_buffer_load_b64(wrsrc, off, 0, 0);
+                const auto b = __builtin_amdgcn_raw_buffer_load_b64(wrsrc, off + 16 * ESZ, 0, 0);
+                w = WReg{a[0], a[1], b[0], b[1]};
+            } else {
+                const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off, 0, 0);
+                const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off + 16 * ESZ, 0, 0);
+                w = WReg{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
             }
-            a = make_float4(t[0], t[1], t[2], t[3]);
-            b = make_float4(t[4], t[5], t[6], t[7]);
+        } else {
+            const int ka = k_begin + 32 * step + 4 * g, kb = ka + 16;
+            if constexpr (WF16) {
+                const uint16_t* wrow = static_cast<const uint16_t*>(W) + (int64_t)(row_ok ? n : 0) * ldw;
+                uint32_t t[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    t[j] = (row_ok && ka + j < k_end) ? wrow[ka + j] : 0u;
+                    t[4 + j] = (row_ok && kb + j < k_end) ? wrow[kb + j] : 0u;
+                }
+                w = WReg{t[0] | (t[1] << 16), t[2] | (t[3] << 16), t[4] | (t[5] << 16), t[6] | (t[7] << 16)};
+            } else {
+                const float* wrow = static_cast<const float*>(W) + (int64_t)(row_ok ? n : 0) * ldw;
+                float t[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    t[j] = (row_ok && ka + j < k_end) ? wrow[ka + j] : 0.f;
+                    t[4 + j] = (row_ok && kb + j < k_end) ? wrow[kb + j] : 0.f;
+                }
+                w = __builtin_bit_cast(WReg, (floatx8){t[0], t[1], t[2], t[3], t[4], t[5], t[6], t[7]});
+            }
         }
     };
 
@@ -186,35 +276,54 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const unsigned cha
 #pragma unroll
         for (int e = 0; e < 4; ++e) { acc_hh[t][e] = 0.f; acc_c[t][e] = 0.f; }
 
-    // prologue: activation block 0, then W for steps 0 .. PF-1
-    dma_block(0, 0);
-    float4 wa[PF], wb[PF];
+    // prologue: W for steps 0 .. PFW-1 and activation block 0 in flight
+    // together; block 0 lands in LDS buffer 0 (split here, or copied, in
+    // which case the copy is issued first so its wait leaves W in flight)
+    WReg wr[PFW];
+    if constexpr (INK) {
 #pragma unroll
-    for (int s = 0; s < PF; ++s) load_w(min(s, nsteps - 1), wa[s], wb[s]);
-    __builtin_amdgcn_sched_barrier(0);
-    if (VEC) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PF));   // block 0 landed; W still in flight
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        for (int s = 0; s < PFW; ++s) load_w(min(s, nsteps - 1), wr[s]);
+        load_a(0);
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(0);
+        __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+    } else {
+        dma_block(0);
+#pragma unroll
+        for (int s = 0; s < PFW; ++s) load_w(min(s, nsteps - 1), wr[s]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (VEC) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PFW));   // block 0 landed; W still in flight
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     float wmax = 0.0f;
 
     // one activation block of STEPS steps; J = position of its first step
-    // in the PF-deep W register ring
+    // in the PFW-deep W register ring
     auto run_block = [&](int b, auto J_) {
         constexpr int J = decltype(J_)::value;
         const bool more = b + 1 < nblocks;
-        if (more) dma_block(b + 1, (b + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);     // the copy stays ahead of this block's W loads
+        if (more) {                            // next activation block, in flight during this one
+            if constexpr (INK) load_a(b + 1);
+            else dma_block(b + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         const unsigned char* abuf = sa + (b & 1) * BB;
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) {
             const int step = b * STEPS + s;
-            float4& ra = wa[J + s];
-            float4& rb = wb[J + s];
+            WReg& w = wr[J + s];
             half8 wh, wl;
-            split8(ra, rb, wh, wl);
-            wmax = absmax8(wmax, ra, rb);
-            load_w(min(step + PF, nsteps - 1), ra, rb);
+            if constexpr (WF16) {
+                wh = __builtin_bit_cast(half8, w);
+            } else {
+                const floatx8 wf = __builtin_bit_cast(floatx8, w);
+                const float4 ra = {wf[0], wf[1], wf[2], wf[3]}, rb = {wf[4], wf[5], wf[6], wf[7]};
+                split8(ra, rb, wh, wl);
+                wmax = absmax8(wmax, ra, rb);
+            }
+            load_w(min(step + PFW, nsteps - 1), w);
             if (step < nsteps) {
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {
@@ -222,32 +331,43 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const unsigned cha
                     const half8 ah = *reinterpret_cast<const half8*>(abuf + off);
                     const half8 al = *reinterpret_cast<const half8*>(abuf + BB / 2 + off);
                     mfma16(ah, wh, acc_hh[t]);
-                    mfma16(ah, wl, acc_c[t]);
+                    if constexpr (!WF16) mfma16(ah, wl, acc_c[t]);
                     mfma16(al, wh, acc_c[t]);
                 }
             }
         }
         if (more) {
-            // the next block's copy was issued before this block's 2 STEPS W loads
+            // the other buffer was last read in block b - 1, before the
+            // previous barrier; it now holds (or receives) block b + 1
             __builtin_amdgcn_sched_barrier(0);
-            if (VEC) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * STEPS));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            if constexpr (INK) {
+                store_a(b + 1);
+                __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+            } else {
+                // the copy was issued before this block's 2 STEPS W loads
+                if (VEC) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * STEPS));
+                else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            }
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    static_assert(PF % STEPS == 0 && PF / STEPS <= 4, "W ring of whole blocks");
-    for (int b = 0; b < nblocks; b += PF / STEPS) {
+    static_assert(PFW % STEPS == 0 && PFW / STEPS <= 4, "W ring of whole blocks");
+    // a do-while (every chunk has at least one block): the prologue's loads
+    // then stay in the entry block instead of being sunk into the loop
+    int b = 0;
+    do {
         run_block(b, std::integral_constant<int, 0>{});
-        if constexpr (PF / STEPS > 1)
+        if constexpr (PFW / STEPS > 1)
             if (b + 1 < nblocks) run_block(b + 1, std::integral_constant<int, STEPS>{});
-        if constexpr (PF / STEPS > 2)
+        if constexpr (PFW / STEPS > 2)
             if (b + 2 < nblocks) run_block(b + 2, std::integral_constant<int, 2 * STEPS>{});
-        if constexpr (PF / STEPS > 3)
+        if constexpr (PFW / STEPS > 3)
             if (b + 3 < nblocks) run_block(b + 3, std::integral_constant<int, 3 * STEPS>{});
-    }
+        b += PFW / STEPS;
+    } while (b < nblocks);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // drain the clamped tail loads
-    if (status && __builtin_amdgcn_ballot_w64(wmax >= 65520.0f) && lane == 0)
+    if (status && __builtin_amdgcn_ballot_w64(fmaxf(wmax, amax) >= 65520.0f) && lane == 0)
         atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
 
     // ---- epilogue: lane holds column n, rows t*16 + 4g + e ------------------
@@ -292,46 +412,61 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
     p.splits = (int)std::max<int64_t>(1, (K + p.kchunk - 1) / p.kchunk);
     const int64_t ablocks = (K + KA - 1) / KA;
     const int mt = mtiles(M);
-    p.a_bytes = ablocks * (mt == 1 ? block_bytes<1>() : mt == 2 ? block_bytes<2>() : block_bytes<4>());
+    p.a_bytes = mt == 1 ? 0 : ablocks * (mt == 2 ? block_bytes<2>() : block_bytes<4>());
     p.p_bytes = p.splits > 1 ? (p.splits * M * N * 4 + 255) / 256 * 256 : 0;
     return p;
 }
 
-hipError_t launch_gemm_decode(const float* A, int64_t lda, const float* W, int64_t ldw, float* C,
-                              int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace,
+hipError_t launch_gemm_decode(const float* A, int64_t lda, const void* W, bool wf16, int64_t ldw,
+                              float* C, int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace,
                               const DecodePlan& plan, uint32_t* status, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
     if (M > 64 || K == 0) return hipErrorInvalidValue;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     unsigned char* ablk = ws;
     float* part = reinterpret_cast<float*>(ws + (plan.a_bytes + 255) / 256 * 256);
+    const int nablk = (int)((K + KA - 1) / KA);
     const dim3 grid((unsigned)((N + DEC_ROWS - 1) / DEC_ROWS), (unsigned)plan.splits);
     float* out = plan.splits > 1 ? part : C;
     const int64_t ldo = plan.splits > 1 ? N : ldc;
     const int64_t stride = plan.splits > 1 ? M * N : 0;
-    const int nablk = (int)((K + KA - 1) / KA);
-    // 16-byte W loads need 16-byte aligned rows and whole k32 steps
-    const bool vec = (reinterpret_cast<uintptr_t>(W) & 15) == 0 && (ldw & 3) == 0 && (K & 31) == 0;
-#define HEAL_DEC(MT_)                                                                                     \
-    do {                                                                                                  \
-        const int64_t tot = (int64_t)nablk * STEPS * (MT_) * 64;                                          \
-        hipLaunchKernelGGL((asplit_kernel<MT_>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, A, \
-                           lda, (int)M, (int)K, nablk, ablk, status);                                     \
-        const int lds = 2 * block_bytes<MT_>();                                                           \
-        if (vec)                                                                                          \
-            hipLaunchKernelGGL((gemm_decode_kernel<MT_, true>), grid, dim3(64 * NW), lds, s, ablk, W, ldw, out, \
-                               ldo, stride, (int)M, (int)N, (int)K, (int)plan.kchunk, (int)plan.a_bytes, \
-                               status);                                                                   \
-        else                                                                                              \
-            hipLaunchKernelGGL((gemm_decode_kernel<MT_, false>), grid, dim3(64 * NW), lds, s, ablk, W, ldw, \
-                               out, ldo, stride, (int)M, (int)N, (int)K, (int)plan.kchunk,                \
-                               (int)plan.a_bytes, status);                                                \
+    // W loads of 8 elements per step need rows aligned to the load width
+    // (16 bytes fp32, 8 bytes fp16) and whole k32 steps
+    const uintptr_t walign = wf16 ? 7 : 15;
+    const bool vec = (reinterpret_cast<uintptr_t>(W) & walign) == 0 && (ldw & 3) == 0 && (K & 31) == 0;
+    // activation units load as float4 when rows are 16-byte aligned
+    const bool avec = (reinterpret_cast<uintptr_t>(A) & 15) == 0 && (lda & 3) == 0;
+#define HEAL_DEC_MAIN(MT_, VEC_, F16_, AV_)                                                             \
+    hipLaunchKernelGGL((gemm_decode_kernel<MT_, VEC_, F16_, AV_>), grid, dim3(64 * NW), 2 * block_bytes<MT_>(), \
+                       s, A, lda, ablk, (int)plan.a_bytes, W, ldw, out, ldo, stride, (int)M, (int)N, (int)K,  \
+                       (int)plan.kchunk, status)
+#define HEAL_DEC_AV(MT_, VEC_, F16_)                                                                    \
+    do {                                                                                                \
+        if (avec) HEAL_DEC_MAIN(MT_, VEC_, F16_, true);                                                 \
+        else HEAL_DEC_MAIN(MT_, VEC_, F16_, false);                                                     \
+    } while (0)
+#define HEAL_DEC(MT_)                                                                                   \
+    do {                                                                                                \
+        if ((MT_) > 1) {                                                                                \
+            const int64_t tot = (int64_t)nablk * STEPS * (MT_) * 64;                                    \
+            hipLaunchKernelGGL((asplit_kernel<MT_>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, \
+                               A, lda, (int)M, (int)K, nablk, ablk, status);                            \
+        }                                                                                               \
+        if (wf16) {                                                                                     \
+            if (vec) HEAL_DEC_AV(MT_, true, true);                                                      \
+            else HEAL_DEC_AV(MT_, false, true);                                                         \
+        } else {                                                                                        \
+            if (vec) HEAL_DEC_AV(MT_, true, false);                                                     \
+            else HEAL_DEC_AV(MT_, false, false);                                                        \
+        }                                                                                               \
     } while (0)
     const int mt = mtiles(M);
     if (mt == 1) HEAL_DEC(1);
     else if (mt == 2) HEAL_DEC(2);
     else HEAL_DEC(4);
 #undef HEAL_DEC
+#undef HEAL_DEC_AV
+#undef HEAL_DEC_MAIN
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
     const int64_t total = M * N;

@@ -13,6 +13,7 @@ namespace heal {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -58,9 +59,10 @@ __host__ __device__ inline int64_t pack_bytes(int64_t R, int64_t K) { return pac
 // ---- launchers (return the launch status; never synchronize) -------------
 hipError_t launch_split(const float* X, int64_t n, uint16_t* hi, uint16_t* lo, uint32_t* status,
                         hipStream_t s);
-// Pack fp32 rows into the layout above.  kn == 0: src is [rows, K] with ld;
-// kn == 1: src is [K, rows] with ld (the packed operand is its transpose).
-hipError_t launch_pack(const float* src, int64_t ld, int64_t rows, int64_t K, int kn, void* packed,
+// Pack rows into the layout above.  src holds fp32 values, or binary16
+// values when f16 (their residual is zero).  kn == 0: src is [rows, K] with
+// ld; kn == 1: src is [K, rows] with ld (the packed operand is its transpose).
+hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int64_t K, int kn, void* packed,
                        uint32_t* status, hipStream_t s);
 
 hipError_t launch_quant(const float* X, int64_t rows, int64_t D, int64_t ldx, int16_t* codes,
@@ -83,8 +85,9 @@ struct DecodePlan {
     int64_t p_bytes;   // workspace bytes of the split-K partials
 };
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K);
-hipError_t launch_gemm_decode(const float* A, int64_t lda, const float* W, int64_t ldw, float* C,
-                              int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace,
+// W is fp32, or binary16 values when wf16 (the two-product form).
+hipError_t launch_gemm_decode(const float* A, int64_t lda, const void* W, bool wf16, int64_t ldw,
+                              float* C, int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace,
                               const DecodePlan& plan, uint32_t* status, hipStream_t s);
 
 int64_t attn_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D);

@@ -58,11 +58,16 @@ hipError_t launch_split(const float* X, int64_t n, uint16_t* hi, uint16_t* lo, u
     return hipGetLastError();
 }
 
+// Source element T: float, or uint16_t holding binary16 values (whose split
+// is the value itself with a zero residual).
+__device__ __forceinline__ float src_value(float x) { return x; }
+__device__ __forceinline__ float src_value(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
 // Packed layout writer, source rows contiguous in k ([rows, K], ld).
 // One thread per (row, 4 consecutive k); the grid covers the padded extent
 // so the zero padding is written too.
-template <bool VEC>
-__global__ __launch_bounds__(256) void pack_rowmajor_kernel(const float* __restrict__ src, int64_t ld,
+template <typename T, bool VEC>
+__global__ __launch_bounds__(256) void pack_rowmajor_kernel(const T* __restrict__ src, int64_t ld,
                                                             int64_t rows, int64_t K, int64_t Kp,
                                                             int64_t rows_p, uint16_t* __restrict__ out,
                                                             uint32_t* __restrict__ status) {
@@ -75,13 +80,19 @@ __global__ __launch_bounds__(256) void pack_rowmajor_kernel(const float* __restr
         const int64_t k = (i - r * kq) << 2;
         float x[4] = {0.f, 0.f, 0.f, 0.f};
         if (r < rows) {
-            const float* p = src + r * ld + k;
+            const T* p = src + r * ld + k;
             if (VEC && k + 4 <= K) {
-                float4 v = *reinterpret_cast<const float4*>(p);
-                x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+                if constexpr (sizeof(T) == 4) {
+                    float4 v = *reinterpret_cast<const float4*>(p);
+                    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+                } else {
+                    const uint2 v = *reinterpret_cast<const uint2*>(p);
+                    x[0] = src_value((uint16_t)(v.x & 0xffff)); x[1] = src_value((uint16_t)(v.x >> 16));
+                    x[2] = src_value((uint16_t)(v.y & 0xffff)); x[3] = src_value((uint16_t)(v.y >> 16));
+                }
             } else {
                 for (int j = 0; j < 4; ++j)
-                    if (k + j < K) x[j] = p[j];
+                    if (k + j < K) x[j] = src_value(p[j]);
             }
         }
         uint16_t h[4], l[4];
@@ -103,7 +114,8 @@ __global__ __launch_bounds__(256) void pack_rowmajor_kernel(const float* __restr
 // Packed layout writer for a source stored [K, rows] (ld >= rows): the packed
 // operand is the transpose.  Threads run along the source row (the packed
 // row index) so reads are coalesced; each thread packs 4 consecutive k.
-__global__ __launch_bounds__(256) void pack_colmajor_kernel(const float* __restrict__ src, int64_t ld,
+template <typename T>
+__global__ __launch_bounds__(256) void pack_colmajor_kernel(const T* __restrict__ src, int64_t ld,
                                                             int64_t rows, int64_t K, int64_t Kp,
                                                             int64_t rows_p, uint16_t* __restrict__ out,
                                                             uint32_t* __restrict__ status) {
@@ -117,7 +129,7 @@ __global__ __launch_bounds__(256) void pack_colmajor_kernel(const float* __restr
         const int64_t k = kg << 2;
         uint16_t h[4], l[4];
         for (int j = 0; j < 4; ++j) {
-            float x = (r < rows && k + j < K) ? src[(k + j) * ld + r] : 0.f;
+            float x = (r < rows && k + j < K) ? src_value(src[(k + j) * ld + r]) : 0.f;
             _Float16 hh, ll;
             split_one(x, hh, ll);
             bad |= f16_out_of_range(x);
@@ -132,22 +144,39 @@ __global__ __launch_bounds__(256) void pack_colmajor_kernel(const float* __restr
     if (bad && status) atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
 }
 
-hipError_t launch_pack(const float* src, int64_t ld, int64_t rows, int64_t K, int kn, void* packed,
+hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int64_t K, int kn, void* packed,
                        uint32_t* status, hipStream_t s) {
     const int64_t Kp = pack_kp(K), rows_p = pack_rows(rows);
     const int64_t total = rows_p * (Kp >> 2);
     if (total == 0) return hipSuccess;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 256 * 64) blocks = 256 * 64;
-    if (kn)
-        hipLaunchKernelGGL(pack_colmajor_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, ld, rows,
-                           K, Kp, rows_p, static_cast<uint16_t*>(packed), status);
-    else if ((reinterpret_cast<uintptr_t>(src) & 15) == 0 && (ld & 3) == 0)
-        hipLaunchKernelGGL(pack_rowmajor_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, src, ld, rows,
-                           K, Kp, rows_p, static_cast<uint16_t*>(packed), status);
-    else
-        hipLaunchKernelGGL(pack_rowmajor_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, src, ld, rows,
-                           K, Kp, rows_p, static_cast<uint16_t*>(packed), status);
+    uint16_t* out = static_cast<uint16_t*>(packed);
+    const uintptr_t align = f16 ? 7 : 15;   // 4 elements per vector load
+    const bool vec = (reinterpret_cast<uintptr_t>(src) & align) == 0 && (ld & 3) == 0;
+    if (f16) {
+        const uint16_t* p = static_cast<const uint16_t*>(src);
+        if (kn)
+            hipLaunchKernelGGL(pack_colmajor_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, s, p, ld,
+                               rows, K, Kp, rows_p, out, status);
+        else if (vec)
+            hipLaunchKernelGGL((pack_rowmajor_kernel<uint16_t, true>), dim3((unsigned)blocks), dim3(256), 0, s, p,
+                               ld, rows, K, Kp, rows_p, out, status);
+        else
+            hipLaunchKernelGGL((pack_rowmajor_kernel<uint16_t, false>), dim3((unsigned)blocks), dim3(256), 0, s,
+                               p, ld, rows, K, Kp, rows_p, out, status);
+    } else {
+        const float* p = static_cast<const float*>(src);
+        if (kn)
+            hipLaunchKernelGGL(pack_colmajor_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, p, ld, rows,
+                               K, Kp, rows_p, out, status);
+        else if (vec)
+            hipLaunchKernelGGL((pack_rowmajor_kernel<float, true>), dim3((unsigned)blocks), dim3(256), 0, s, p, ld,
+                               rows, K, Kp, rows_p, out, status);
+        else
+            hipLaunchKernelGGL((pack_rowmajor_kernel<float, false>), dim3((unsigned)blocks), dim3(256), 0, s, p,
+                               ld, rows, K, Kp, rows_p, out, status);
+    }
     return hipGetLastError();
 }
 

@@ -56,7 +56,8 @@ enum {
     HEAL_W_NK = 0u,     /* W is fp32 [N, K] (a linear layer's weight, B = W^T)          */
     HEAL_W_KN = 1u,     /* W is fp32 [K, N] (B = W)                                     */
     HEAL_W_PACKED = 2u, /* W is a buffer written by heal_pack_w (ldw and layout ignored) */
-    HEAL_A_PACKED = 4u  /* A is a buffer written by heal_pack_w for A's M rows (lda ignored) */
+    HEAL_A_PACKED = 4u, /* A is a buffer written by heal_pack_w for A's M rows (lda ignored) */
+    HEAL_W_F16 = 8u     /* W holds binary16 values (2 bytes each), layout per HEAL_W_KN   */
 };
 
 /* Bits of the optional device status word. */
@@ -101,10 +102,15 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  *
  * Both fp32 operands are split as in heal_split_f32.  The product expands to
  *   C = A_hi.B_hi + 2^-10 (A_hi.B_lo + A_lo.B_hi)
- * with the three 16-bit products on fp16 MFMA and fp32 accumulation in two
- * accumulators, combined once in fp32.  The output stays fp32, so no
- * downcast happens at the kernel boundary.  The lo.lo term (2^-20) is
- * dropped.  Accuracy: normwise error max_ij |C - C_exact| / (|a_i| |b_j|)
+ * with the three 16-bit products on fp16 MFMA and fp32 accumulation (the
+ * 2^-10 applied exactly, as a power of two, to the correction terms).  The
+ * output stays fp32, so no downcast happens at the kernel boundary.  The
+ * lo.lo term (2^-20) is dropped.  With HEAL_W_F16 the weight is already
+ * 16-bit (exact in fp16, e.g. an FP16 checkpoint or a BF16 one converted
+ * exactly), B_lo is zero and two products remain,
+ *   C = A_hi.B + 2^-10 A_lo.B,
+ * the paper's own form (section 3, "Mitigating GEMM Truncation via FP16
+ * Promotion and Algebraic Compensation"), reading 2 bytes per weight.  Accuracy: normwise error max_ij |C - C_exact| / (|a_i| |b_j|)
  * within 2x that of a naive FP32 GEMM and below 1e-5.  The summation order
  * depends on (M, N, K) but not on the data.  For M <= 64 (NK layout, K <
  * 2^23, neither operand packed) it also does not depend on M, so
@@ -114,18 +120,20 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  *          aligned, lda % 4 == 0, take 16-byte vector loads)
  *   W      device fp32: [N, K] with ldw >= K (NK) or [K, N] with ldw >= N
  *          (KN), 4-byte aligned (16-byte aligned rows vectorize as for A).
- *          With HEAL_W_PACKED it is a heal_pack_w buffer for the same
- *          (N, K), 256-byte aligned.
+ *          With HEAL_W_F16 the same layouts hold binary16 values (uint16
+ *          bit patterns), 2-byte aligned.  With HEAL_W_PACKED it is a
+ *          heal_pack_w buffer for the same (N, K), 256-byte aligned.
  *   C      device fp32 [M, N], ldc >= N.  C must not overlap A or W.
- *   flags  one of HEAL_W_NK / HEAL_W_KN, optionally | HEAL_W_PACKED and/or
- *          | HEAL_A_PACKED (A then is heal_pack_w(A, lda, M, K, HEAL_W_NK)'s
- *          buffer: an activation split once can feed several GEMMs)
+ *   flags  one of HEAL_W_NK / HEAL_W_KN, optionally | HEAL_W_F16 or
+ *          | HEAL_W_PACKED (not both: UNSUPPORTED), and/or | HEAL_A_PACKED
+ *          (A then is heal_pack_w(A, lda, M, K, HEAL_W_NK)'s buffer: an
+ *          activation split once can feed several GEMMs)
  *   workspace  device, >= heal_gemm_f32c_workspace(M, N, K, flags) bytes,
  *          256-byte aligned (NULL allowed when that size is 0)
  *   dev_status  device, nullable; HEAL_FLAG_F16_RANGE as in heal_split_f32.
  * Limits: M, N, K < 2^31.  K == 0 writes zeros.  In the M <= 64 case above,
- * ldw < 2^26 (each 16-row slice of W is addressed with 32-bit byte offsets),
- * else HEAL_ERR_UNSUPPORTED.
+ * ldw < 2^26 and lda < 2^24 (each 16-row slice of W, and A, are addressed
+ * with 32-bit byte offsets), else HEAL_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------ */
 heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t ldw,
                            float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
@@ -143,10 +151,12 @@ size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags)
  *  The packed form is internal and opaque: each row holds, for every 32-wide
  *  block of k, the 32 fp16 hi parts then the 32 fp16 lo parts.  Rows are
  *  padded to a multiple of 256 and k to a multiple of 32 with zeros.
- *   W      as in heal_gemm_f32c (flags HEAL_W_NK or HEAL_W_KN), 4-byte aligned
+ *   W      as in heal_gemm_f32c (flags HEAL_W_NK or HEAL_W_KN, optionally
+ *          | HEAL_W_F16: binary16 input, its lo parts are zero), 4-byte
+ *          aligned (2-byte with HEAL_W_F16)
  *   packed device, >= heal_pack_w_bytes(N, K) bytes, 256-byte aligned
  * ------------------------------------------------------------------------ */
-heal_status heal_pack_w(const float* W, int64_t ldw, int64_t N, int64_t K, uint32_t flags,
+heal_status heal_pack_w(const void* W, int64_t ldw, int64_t N, int64_t K, uint32_t flags,
                         void* packed, size_t packed_bytes, uint32_t* dev_status, void* stream);
 
 size_t heal_pack_w_bytes(int64_t N, int64_t K);

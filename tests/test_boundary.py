@@ -61,7 +61,8 @@ def _gemm(A=FAKE, lda=4096, W=FAKE, ldw=4096, C=FAKE, ldc=4096, M=8, N=4096, K=4
 def test_gemm_validation():
     assert _gemm(M=-1) == SHAPE
     assert _gemm(K=1 << 31) == SHAPE
-    assert _gemm(flags=8) == UNSUP
+    assert _gemm(flags=heal.HEAL_W_F16 | heal.HEAL_W_PACKED) == UNSUP   # a packed weight is already split
+    assert _gemm(flags=32) == UNSUP
     assert _gemm(M=0, A=None, W=None, C=None) == OK
     assert _gemm(N=0, A=None, W=None, C=None) == OK
     assert _gemm(C=None) == NULL
@@ -73,6 +74,8 @@ def test_gemm_validation():
     assert _gemm(flags=heal.HEAL_W_KN, N=8192, ldc=8192) == STRIDE   # KN needs ldw >= N
     assert _gemm(A=ctypes.c_void_p(0x10002)) == ALIGN
     assert _gemm(W=ctypes.c_void_p(0x10001)) == ALIGN
+    assert _gemm(W=ctypes.c_void_p(0x10002)) == ALIGN                          # fp32 W: 4-byte aligned
+    assert _gemm(flags=heal.HEAL_W_F16, W=ctypes.c_void_p(0x10001)) == ALIGN   # fp16 W: 2-byte aligned
     assert _gemm(flags=heal.HEAL_W_PACKED, W=ctypes.c_void_p(0x10010)) == ALIGN
     assert _gemm(flags=heal.HEAL_A_PACKED, A=ctypes.c_void_p(0x10010)) == ALIGN
     assert _gemm(flags=16) == UNSUP
@@ -109,6 +112,8 @@ def test_pack_validation():
     assert L.heal_pack_w(FAKE, 32, 64, 64, 0, FAKE, 1 << 30, None, None) == STRIDE
     assert L.heal_pack_w(FAKE, 64, 64, 64, 0, ctypes.c_void_p(0x10080), 1 << 30, None, None) == ALIGN
     assert L.heal_pack_w(ctypes.c_void_p(0x10002), 64, 64, 64, 0, FAKE, 1 << 30, None, None) == ALIGN
+    assert L.heal_pack_w(ctypes.c_void_p(0x10001), 64, 64, 64, heal.HEAL_W_F16, FAKE, 1 << 30, None, None) == ALIGN
+    assert L.heal_pack_w(FAKE, 64, 64, 64, heal.HEAL_W_F16 | 16, FAKE, 1 << 30, None, None) == UNSUP
     assert L.heal_pack_w(FAKE, 64, 64, 64, 0, FAKE, 100, None, None) == WS
 
 

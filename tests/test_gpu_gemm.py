@@ -139,14 +139,17 @@ def test_gemm_range_flag():
 @pytest.mark.parametrize("K,N", WL.LLAMA3_8B_DECODE_KN)
 def test_gemm_decode_shapes_and_batch_invariance(K, N):
     """Decode-shaped Llama-3-8B-like layers, M = 1, 8, 32, 64: tolerance on every M,
-    and row i of the product identical for every M (fixed K chunking)."""
+    and row i of the product identical for every M (fixed K chunking; M = 16 and
+    17 straddle the switch from the in-kernel activation split to the pre-split
+    copy)."""
     A, W = WL.decode_gemm(64, K, N, seed=2000 + K + N)
     Wd = torch.from_numpy(W).to(DEV)
     Ad = torch.from_numpy(A).to(DEV)
     outs = {}
-    for M in WL.DECODE_M:
+    Ms = sorted(set(WL.DECODE_M) | {16, 17})
+    for M in Ms:
         outs[M] = heal.heal_gemm_f32c(Ad[:M], Wd).cpu().numpy()
-    for M in WL.DECODE_M:
+    for M in Ms:
         assert np.array_equal(outs[M], outs[64][:M]), M
     rows = np.array([0, 1, 7, 31, 63])
     C64 = oracle.gemm_f64_rows(A, W, rows)
@@ -164,3 +167,66 @@ def test_gemm_prefill_full_size_sampled_rows(K, N):
     A, W = WL.prefill_gemm(WL.PREFILL_M, K, N, seed=3000 + K)
     rows = np.sort(WL.rng(K).choice(WL.PREFILL_M, size=24, replace=False))
     _check(A, W, "nk", packed=True, rows=rows, label="prefill")
+
+
+# ---- 16-bit weights (HEAL_W_F16): the two-product form -------------------------------------
+
+def _f16_weight(W):
+    """Round a weight to binary16 (what an FP16 checkpoint holds); input data, not the method."""
+    return W.astype(np.float16)
+
+
+@pytest.mark.parametrize("K,N", [(4096, 1024), (14336, 4096)])
+def test_gemm_f16_weight_decode_equals_fp32_path(K, N):
+    """With fp16 weights the residual plane is zero, so the two-product path must give
+    bit for bit what the three-product path gives on the same values held in fp32
+    (the dropped product adds exact zeros), for every M; and it meets the tolerance."""
+    A, W = WL.decode_gemm(64, K, N, seed=5000 + K + N)
+    W16 = _f16_weight(W)
+    W32 = W16.astype(np.float32)            # the same values, exactly
+    Ad = torch.from_numpy(A).to(DEV)
+    W16d = torch.from_numpy(W16).to(DEV)
+    W32d = torch.from_numpy(W32).to(DEV)
+    outs = {}
+    for M in WL.DECODE_M:
+        c16 = heal.heal_gemm_f32c(Ad[:M], W16d).cpu().numpy()
+        c32 = heal.heal_gemm_f32c(Ad[:M], W32d).cpu().numpy()
+        assert np.array_equal(c16, c32), M
+        outs[M] = c16
+    for M in WL.DECODE_M:
+        assert np.array_equal(outs[M], outs[64][:M]), M
+    rows = np.array([0, 3, 40, 63])
+    C64 = oracle.gemm_f64_rows(A, W32, rows)
+    C32 = oracle.gemm_f32_naive_rows(A, W32, rows)
+    e_gpu = gemm_normwise_error(outs[64][rows], C64, A, W32, rows=rows)
+    e_naive = gemm_normwise_error(C32, C64, A, W32, rows=rows)
+    print(f"f16 weight K={K} N={N}: e_gpu={e_gpu:.3e} e_naive={e_naive:.3e}", flush=True)
+    assert e_gpu <= gemm_tolerance(e_naive, K)
+
+
+@pytest.mark.parametrize("layout", ["nk", "kn"])
+@pytest.mark.parametrize("M,N,K", [(3, 40, 31), (100, 130, 300), (64, 100, 33)])
+def test_gemm_f16_weight_ragged_and_packed(M, N, K, layout):
+    """Ragged shapes on both paths and layouts: the fp16 weight gives the same bits as
+    its fp32 copy, its packed form is byte-identical to the packed fp32 copy, and the
+    result meets the tolerance."""
+    print(f"gemm f16 weight M={M} N={N} K={K} {layout}", flush=True)
+    A, W = WL.decode_gemm(M, K, N, seed=5100 + M + N + K)
+    W16 = _f16_weight(W if layout == "nk" else np.ascontiguousarray(W.T))
+    W32 = W16.astype(np.float32)
+    Ad = torch.from_numpy(A).to(DEV)
+    W16d, W32d = torch.from_numpy(W16).to(DEV), torch.from_numpy(W32).to(DEV)
+    c16 = heal.heal_gemm_f32c(Ad, W16d, w_layout=layout).cpu().numpy()
+    c32 = heal.heal_gemm_f32c(Ad, W32d, w_layout=layout).cpu().numpy()
+    assert np.array_equal(c16, c32)
+    p16 = heal.heal_pack_w(W16d, layout)
+    p32 = heal.heal_pack_w(W32d, layout)
+    torch.cuda.synchronize()
+    assert torch.equal(p16.buf, p32.buf)
+    cp = heal.heal_gemm_f32c(Ad, p16).cpu().numpy()
+    C64 = oracle.gemm_f64(A, W32, layout)
+    C32 = oracle.gemm_f32_naive(A, W32, layout)
+    for C in (c16, cp):
+        e_gpu = gemm_normwise_error(C, C64, A, W32, layout)
+        e_naive = gemm_normwise_error(C32, C64, A, W32, layout)
+        assert e_gpu <= gemm_tolerance(e_naive, K), (e_gpu, e_naive)
