@@ -7,6 +7,8 @@ workload (inputs resident in HBM before timing starts):
   split    activation split of the two prefill GEMMs (fp32 -> packed fp16 hi/lo)
   prefill  compensated GEMM, M=2048 tokens, (K,N) = (4096,14336) and (14336,4096),
            weights split once beforehand (as deployed: weights are fixed)
+  prefill_w16  the same GEMMs with the weights held as binary16 and packed
+           once: the two-product form (2 of the 3 MFMA products)
   decode   16 compensated GEMMs of a Llama-3-8B-like layer: M = 1, 8, 32, 64
            x (K,N) in {(4096,4096), (4096,1024), (4096,14336), (14336,4096)},
            fp32 weights streamed from HBM (M-outer order, so consecutive calls
@@ -63,16 +65,19 @@ def build_workload(rows_sel):
     W = {}
     t0 = time.time()
 
-    if "split" in rows_sel or "prefill" in rows_sel:
+    if "split" in rows_sel or "prefill" in rows_sel or "prefill_w16" in rows_sel:
         pre = []
         for i, (K, N) in enumerate(WL.PREFILL_KN):
             A, Wt = WL.prefill_gemm(WL.PREFILL_M, K, N, seed=3000 + i)
             Ad = torch.from_numpy(A).to(dev)
-            Wp = heal.heal_pack_w(torch.from_numpy(Wt).to(dev))      # one-time weight split
+            Wd = torch.from_numpy(Wt).to(dev)
+            Wp = heal.heal_pack_w(Wd)                                  # one-time weight split
+            # the same weight as binary16 (an FP16 checkpoint), packed once
+            Wp16 = heal.heal_pack_w(Wd.half()) if "prefill_w16" in rows_sel else None
             Ap = heal.heal_pack_w(Ad)                                  # output buffer of the split row
             C = torch.empty((WL.PREFILL_M, N), dtype=torch.float32, device=dev)
-            pre.append(dict(M=WL.PREFILL_M, K=K, N=N, A=Ad, Ap=Ap, Wp=Wp, C=C))
-            del A, Wt
+            pre.append(dict(M=WL.PREFILL_M, K=K, N=N, A=Ad, Ap=Ap, Wp=Wp, Wp16=Wp16, C=C))
+            del A, Wt, Wd
         W["prefill"] = pre
         log(f"[bench] prefill inputs ready ({time.time() - t0:.1f}s)")
 
@@ -150,6 +155,12 @@ def make_rows(W):
         useful = sum(2.0 * p["M"] * p["N"] * p["K"] for p in pre)
         rows.append(("split", run_split, split_bytes, "B"))
         rows.append(("prefill", run_prefill, useful, "flop"))
+        if pre[0]["Wp16"] is not None:
+            def run_prefill16():
+                for p in pre:
+                    heal.heal_gemm_f32c(p["Ap"], p["Wp16"], C=p["C"])
+
+            rows.append(("prefill_w16", run_prefill16, useful, "flop"))
     if "decode" in W:
         calls = W["decode"]
 
@@ -212,7 +223,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--rows", default="split,prefill,decode,decode_w16,quant,dequant,attn",
+    ap.add_argument("--rows", default="split,prefill,prefill_w16,decode,decode_w16,quant,dequant,attn",
                     help="comma-separated subset of rows to run (profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -292,7 +303,8 @@ def main():
            "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "fp32 in/out; fp16 hi/lo MFMA products, fp32 accumulate; int16 codes",
            "data": "synthetic (seeded; model-shaped, see heal_workloads.py)"}
-    cfg = {"workload": "HEAL hot path step: split + prefill GEMM (M=2048; K,N = 4096,14336 and 14336,4096), "
+    cfg = {"workload": "HEAL hot path step: split + prefill GEMM (M=2048; K,N = 4096,14336 and 14336,4096; "
+                       "fp32 weights, and fp16 weights in the two-product form), "
                        "16 decode GEMMs (M=1,8,32,64 x Llama-3-8B q/o, k/v, gate/up, down; fp32 and fp16 weights), "
                        "INT16 quant + dequant "
                        "(32x2048 tokens, 32+8+8 heads x 128), INT16 decode attention (B=16, T=8192, 32/8 heads)",

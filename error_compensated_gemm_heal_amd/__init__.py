@@ -132,8 +132,10 @@ class PackedOperand:
     """An operand of `rows` x K split once into the GEMM's packed dual-FP16 form
     (opaque buffer): a weight (rows = N) or an activation (rows = M)."""
 
-    def __init__(self, buf: torch.Tensor, rows: int, K: int):
-        self.buf, self.rows, self.K = buf, rows, K
+    def __init__(self, buf: torch.Tensor, rows: int, K: int, f16: bool = False):
+        # f16: packed from binary16 weights (zero lo planes): GEMMs take the
+        # two-product form (HEAL_W_PACKED | HEAL_W_F16)
+        self.buf, self.rows, self.K, self.f16 = buf, rows, K, f16
 
     @property
     def N(self):
@@ -173,7 +175,7 @@ def heal_pack_w(W: torch.Tensor, w_layout: str = "nk", dev_status=None, out=None
             raise ValueError("packed buffer too small")
     _check("heal_pack_w", lib().heal_pack_w(_ptr(W), ldw, N, K, flags, _ptr(buf), nbytes,
                                             _ptr(dev_status), _stream()))
-    return PackedOperand(buf, N, K)
+    return PackedOperand(buf, N, K, f16=bool(flags & HEAL_W_F16))
 
 
 def heal_gemm_f32c_workspace(M: int, N: int, K: int, flags: int) -> int:
@@ -193,7 +195,7 @@ def heal_gemm_f32c(A, W, w_layout: str = "nk", C=None, workspace=None, dev_statu
     if isinstance(W, PackedOperand):
         if W.K != K:
             raise ValueError("packed weight has a different K")
-        N, flags, wptr, ldw = W.rows, HEAL_W_PACKED, _ptr(W.buf), 0
+        N, flags, wptr, ldw = W.rows, HEAL_W_PACKED | (HEAL_W_F16 if W.f16 else 0), _ptr(W.buf), 0
     else:
         _dev(W, "W")
         if w_layout == "kn":

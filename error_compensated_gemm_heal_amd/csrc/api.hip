@@ -102,7 +102,6 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
                            void* stream) {
     if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return HEAL_ERR_SHAPE;
     if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_PACKED | HEAL_A_PACKED | HEAL_W_F16)) return HEAL_ERR_UNSUPPORTED;
-    if ((flags & HEAL_W_F16) && (flags & HEAL_W_PACKED)) return HEAL_ERR_UNSUPPORTED;   // packed: already split
     if (M == 0 || N == 0) return HEAL_OK;
     if (!C) return HEAL_ERR_NULL;
     if (ldc < N) return HEAL_ERR_STRIDE;
@@ -150,7 +149,7 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
         if (e != hipSuccess) return HEAL_ERR_HIP;
         bpk = wpk;
     }
-    return hip_status(launch_gemm_prefill(apk, bpk, C, ldc, M, N, K, s));
+    return hip_status(launch_gemm_prefill(apk, bpk, wf16, C, ldc, M, N, K, s));
 }
 
 heal_status heal_qkv_quant_i16(const float* X, int64_t rows, int64_t D, int64_t ldx, int16_t* codes,

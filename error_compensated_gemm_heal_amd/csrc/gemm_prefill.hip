@@ -31,6 +31,9 @@
 //  * LDS rows are the packed 128-byte lines with their eight 16-byte chunks
 //    XOR-swizzled by (row / 2) % 8, so the fragment reads of 16 consecutive
 //    rows hit distinct banks with no padding;
+//  * with a 16-bit weight (binary16 values, packed with zero lo planes) the
+//    B_lo fragments are not read and the A_hi.B_lo product is skipped: the
+//    paper's own two-product form, 2/3 of the MFMAs;
 //  * when the grid would fill at most half the chip, the k range is split in
 //    two and both halves add into a zeroed C with fp32 atomics; two addends
 //    commute exactly, so the result does not depend on their order;
@@ -66,7 +69,8 @@ __device__ __forceinline__ half8 scale_m10(const half8& x) {
     return x * (_Float16)0.0009765625f;
 }
 
-template <bool SPLIT>
+// TWO: B is a 16-bit weight (zero lo planes): two products instead of three.
+template <bool SPLIT, bool TWO>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned char* __restrict__ Bpk,
                          float* __restrict__ C, int64_t ldc, int M, int N, int Kp,
@@ -146,7 +150,8 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
         }                                                                                                \
         _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                                 \
             bh_[j] = *reinterpret_cast<const half8*>(base + b_row + j * 32 * ROWB + slot_off[ks_][0]);   \
-            bl_[j] = *reinterpret_cast<const half8*>(base + b_row + j * 32 * ROWB + slot_off[ks_][1]);   \
+            if constexpr (!TWO)                                                                          \
+                bl_[j] = *reinterpret_cast<const half8*>(base + b_row + j * 32 * ROWB + slot_off[ks_][1]); \
         }                                                                                                \
     } while (0)
     // the three products of one k16 step; each product sweeps all 16 output
@@ -156,9 +161,11 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
         _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                   \
             _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32(ah_[i], bh_[j], acc[i][j]);            \
         half8 as_[TM];                                                                                   \
-        _Pragma("unroll") for (int i = 0; i < TM; ++i) as_[i] = scale_m10(ah_[i]);                       \
-        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                   \
-            _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32(as_[i], bl_[j], acc[i][j]);            \
+        if constexpr (!TWO) {                                                                            \
+            _Pragma("unroll") for (int i = 0; i < TM; ++i) as_[i] = scale_m10(ah_[i]);                   \
+            _Pragma("unroll") for (int i = 0; i < TM; ++i)                                               \
+                _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32(as_[i], bl_[j], acc[i][j]);        \
+        }                                                                                                \
         _Pragma("unroll") for (int i = 0; i < TM; ++i) as_[i] = scale_m10(al_[i]);                       \
         _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                   \
             _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32(as_[i], bh_[j], acc[i][j]);            \
@@ -192,8 +199,8 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
             HEAL_MFMAS(ah0, al0, bh0, bl0);
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // three MFMAs
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                __builtin_amdgcn_sched_group_barrier(0x008, TWO ? 2 : 3, 0);   // MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // one LDS read
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -211,9 +218,9 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
             HEAL_MFMAS(ah1, al1, bh1, bl1);
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // three MFMAs
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one DMA load
+                __builtin_amdgcn_sched_group_barrier(0x008, TWO ? 2 : 3, 0);   // MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // one LDS read
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);             // one DMA load
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -258,7 +265,7 @@ __global__ void zero_c_kernel(float* C, int64_t ldc, int64_t M, int64_t N) {
 
 }  // namespace
 
-hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, float* C, int64_t ldc, int64_t M,
+hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, bool b16, float* C, int64_t ldc, int64_t M,
                                int64_t N, int64_t K, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
     const int64_t Kp = pack_kp(K);
@@ -271,12 +278,14 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, float* C, int64
     const bool split = (int64_t)tiles_m * tiles_n <= 128 && Kp / BK >= 8;
     static bool attr_set = false;  // idempotent; racing first calls set the same value
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_prefill_kernel<false>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * STAGE);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_prefill_kernel<true>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * STAGE);
-        if (e != hipSuccess) return e;
+        const void* fns[4] = {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, false>),
+                              reinterpret_cast<const void*>(&gemm_prefill_kernel<true, false>),
+                              reinterpret_cast<const void*>(&gemm_prefill_kernel<false, true>),
+                              reinterpret_cast<const void*>(&gemm_prefill_kernel<true, true>)};
+        for (const void* f : fns) {
+            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * STAGE);
+            if (e != hipSuccess) return e;
+        }
         attr_set = true;
     }
     const unsigned char* a = static_cast<const unsigned char*>(Apk);
@@ -284,12 +293,19 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, float* C, int64
     if (split) {
         const unsigned zb = (unsigned)std::min<int64_t>((M * N + 255) / 256, 4096);
         hipLaunchKernelGGL(zero_c_kernel, dim3(zb), dim3(256), 0, s, C, ldc, M, N);
-        hipLaunchKernelGGL(gemm_prefill_kernel<true>, dim3(tiles_m * tiles_n * 2), dim3(256), NSTAGE * STAGE, s,
-                           a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n);
-    } else {
-        hipLaunchKernelGGL(gemm_prefill_kernel<false>, dim3(tiles_m * tiles_n), dim3(256), NSTAGE * STAGE, s,
-                           a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n);
     }
+    const dim3 grid((unsigned)(tiles_m * tiles_n * (split ? 2 : 1)));
+#define HEAL_PREFILL(SPLIT_, TWO_)                                                                    \
+    hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, TWO_>), grid, dim3(256), NSTAGE * STAGE, s, a, b, C, ldc, \
+                       (int)M, (int)N, (int)Kp, tiles_m, tiles_n)
+    if (split) {
+        if (b16) HEAL_PREFILL(true, true);
+        else HEAL_PREFILL(true, false);
+    } else {
+        if (b16) HEAL_PREFILL(false, true);
+        else HEAL_PREFILL(false, false);
+    }
+#undef HEAL_PREFILL
     return hipGetLastError();
 }
 

@@ -71,8 +71,9 @@ hipError_t launch_dequant(const int16_t* codes, int64_t rows, int64_t D, int64_t
                           const float* scales, int fmt, void* out, void* out_lo, int64_t ldo,
                           hipStream_t s);
 
-// C[M,N] from packed A (rows M) and packed B (rows N).
-hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, float* C, int64_t ldc, int64_t M,
+// C[M,N] from packed A (rows M) and packed B (rows N); b16: B was packed from
+// binary16 values (zero lo planes), so the A_hi.B_lo product is skipped.
+hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, bool b16, float* C, int64_t ldc, int64_t M,
                                int64_t N, int64_t K, hipStream_t s);
 
 // Decode path (M <= 64): fp32 W [N,K] streamed and split in registers.

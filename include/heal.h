@@ -124,8 +124,11 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  *          bit patterns), 2-byte aligned.  With HEAL_W_PACKED it is a
  *          heal_pack_w buffer for the same (N, K), 256-byte aligned.
  *   C      device fp32 [M, N], ldc >= N.  C must not overlap A or W.
- *   flags  one of HEAL_W_NK / HEAL_W_KN, optionally | HEAL_W_F16 or
- *          | HEAL_W_PACKED (not both: UNSUPPORTED), and/or | HEAL_A_PACKED
+ *   flags  one of HEAL_W_NK / HEAL_W_KN, optionally | HEAL_W_F16 and/or
+ *          | HEAL_W_PACKED (both: W is a buffer that heal_pack_w packed with
+ *          HEAL_W_F16, whose lo planes are zero, and the A_hi.B_lo product
+ *          is skipped; a buffer packed from fp32 values must not carry
+ *          HEAL_W_F16, or its lo planes are ignored), and/or | HEAL_A_PACKED
  *          (A then is heal_pack_w(A, lda, M, K, HEAL_W_NK)'s buffer: an
  *          activation split once can feed several GEMMs)
  *   workspace  device, >= heal_gemm_f32c_workspace(M, N, K, flags) bytes,

@@ -61,7 +61,7 @@ def _gemm(A=FAKE, lda=4096, W=FAKE, ldw=4096, C=FAKE, ldc=4096, M=8, N=4096, K=4
 def test_gemm_validation():
     assert _gemm(M=-1) == SHAPE
     assert _gemm(K=1 << 31) == SHAPE
-    assert _gemm(flags=heal.HEAL_W_F16 | heal.HEAL_W_PACKED) == UNSUP   # a packed weight is already split
+    assert _gemm(flags=heal.HEAL_W_F16 | heal.HEAL_W_PACKED, W=ctypes.c_void_p(0x10010)) == ALIGN  # packed: 256 B
     assert _gemm(flags=32) == UNSUP
     assert _gemm(M=0, A=None, W=None, C=None) == OK
     assert _gemm(N=0, A=None, W=None, C=None) == OK

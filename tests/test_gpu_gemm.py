@@ -224,9 +224,37 @@ def test_gemm_f16_weight_ragged_and_packed(M, N, K, layout):
     torch.cuda.synchronize()
     assert torch.equal(p16.buf, p32.buf)
     cp = heal.heal_gemm_f32c(Ad, p16).cpu().numpy()
+    if M > 64:   # both through the prefill kernel's two-product form
+        assert np.array_equal(cp, c16)
     C64 = oracle.gemm_f64(A, W32, layout)
     C32 = oracle.gemm_f32_naive(A, W32, layout)
     for C in (c16, cp):
         e_gpu = gemm_normwise_error(C, C64, A, W32, layout)
         e_naive = gemm_normwise_error(C32, C64, A, W32, layout)
         assert e_gpu <= gemm_tolerance(e_naive, K), (e_gpu, e_naive)
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 1024, 4096), (4096, 4096, 256)])
+def test_gemm_f16_weight_prefill_two_products(M, N, K):
+    """Prefill shapes (the k-split grid and the plain one): with fp16 weights the kernel
+    skips the A_hi.B_lo product; its result equals, bit for bit, the three-product
+    kernel's on the same values held in fp32 (whose B_lo is zero), packed or not,
+    and meets the tolerance on sampled rows."""
+    print(f"gemm f16 weight prefill M={M} N={N} K={K}", flush=True)
+    A, W = WL.decode_gemm(M, K, N, seed=5200 + M + N + K)
+    W16 = _f16_weight(W)
+    W32 = W16.astype(np.float32)
+    Ad = torch.from_numpy(A).to(DEV)
+    W16d, W32d = torch.from_numpy(W16).to(DEV), torch.from_numpy(W32).to(DEV)
+    c16 = heal.heal_gemm_f32c(Ad, W16d).cpu().numpy()
+    c32 = heal.heal_gemm_f32c(Ad, W32d).cpu().numpy()
+    cp = heal.heal_gemm_f32c(Ad, heal.heal_pack_w(W16d)).cpu().numpy()
+    assert np.array_equal(c16, c32)
+    assert np.array_equal(cp, c16)
+    rows = np.array([0, 1, M // 2, M - 1])
+    C64 = oracle.gemm_f64_rows(A, W32, rows)
+    C32 = oracle.gemm_f32_naive_rows(A, W32, rows)
+    e_gpu = gemm_normwise_error(c16[rows], C64, A, W32, rows=rows)
+    e_naive = gemm_normwise_error(C32, C64, A, W32, rows=rows)
+    print(f"  e_gpu={e_gpu:.3e} e_naive={e_naive:.3e}", flush=True)
+    assert e_gpu <= gemm_tolerance(e_naive, K)
