@@ -15,6 +15,9 @@ workload (inputs resident in HBM before timing starts):
            touch different weights and the 256 MB MALL cannot serve repeats)
   decode_w16  the same 16 GEMMs with the weights held as binary16 (2 bytes each;
            the paper's two-product form for 16-bit weights)
+  decode_kshift  the same 16 GEMMs with massive activation channels beyond
+           FP16's range (0.5% of channels x 2e5), rescaled per channel by powers
+           of two in the split (a_kshift) against a once-rescaled weight
   quant    INT16 quant of a Qwen3-8B-like layer's Q/K/V: 32 x 2048 tokens,
            32 + 8 + 8 heads of 128 (one [65536, 48, 128] launch)
   dequant  INT16 -> fp32 dequant of the same codes
@@ -106,6 +109,23 @@ def build_workload(rows_sel):
         W["decode_w16"] = calls16
         log(f"[bench] decode inputs ready ({time.time() - t0:.1f}s)")
 
+    if "decode_kshift" in rows_sel:
+        callsk = []
+        shifted = {}
+        for i, (K, N) in enumerate(WL.LLAMA3_8B_DECODE_KN):
+            A, Wt = WL.overflow_gemm(64, K, N, seed=2100 + i)
+            ks = torch.from_numpy(heal.heal_kshift_from_absmax(abs(A).max(axis=0))).to(dev)
+            Ws = heal.heal_scale_k(torch.from_numpy(Wt).to(dev), -ks)      # one-time weight rescaling
+            shifted[(K, N)] = (torch.from_numpy(A).to(dev), Ws, ks)
+        for M in WL.DECODE_M:
+            for (K, N) in WL.LLAMA3_8B_DECODE_KN:
+                Ad, Ws, ks = shifted[(K, N)]
+                ws = torch.empty(max(heal.heal_gemm_f32c_workspace(M, N, K, 0), 1), dtype=torch.uint8, device=dev)
+                C = torch.empty((M, N), dtype=torch.float32, device=dev)
+                callsk.append(dict(M=M, K=K, N=N, A=Ad[:M], W=Ws, ks=ks, C=C, ws=ws))
+        W["decode_kshift"] = callsk
+        log(f"[bench] rescaled decode inputs ready ({time.time() - t0:.1f}s)")
+
     if "quant" in rows_sel or "dequant" in rows_sel:
         tokens = 32 * 2048
         Q, K_, V = WL.qkv(tokens, 32, 8, 128, seed=4000)
@@ -179,6 +199,15 @@ def make_rows(W):
 
         d16bytes = sum(2 * c["K"] * c["N"] + 4 * (c["M"] * c["K"] + c["M"] * c["N"]) for c in calls16)
         rows.append(("decode_w16", run_decode16, d16bytes, "B"))
+    if "decode_kshift" in W:
+        callsk = W["decode_kshift"]
+
+        def run_decodek():
+            for c in callsk:
+                heal.heal_gemm_f32c(c["A"], c["W"], C=c["C"], workspace=c["ws"], a_kshift=c["ks"])
+
+        dkbytes = sum(4 * (c["K"] * c["N"] + c["M"] * c["K"] + c["M"] * c["N"]) + c["K"] for c in callsk)
+        rows.append(("decode_kshift", run_decodek, dkbytes, "B"))
     if "quant" in W:
         q = W["quant"]
         qbytes = q["n"] * (4 + 2) + q["rows"] * 4
@@ -223,7 +252,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--rows", default="split,prefill,prefill_w16,decode,decode_w16,quant,dequant,attn",
+    ap.add_argument("--rows", default="split,prefill,prefill_w16,decode,decode_w16,decode_kshift,quant,dequant,attn",
                     help="comma-separated subset of rows to run (profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -305,7 +334,8 @@ def main():
            "data": "synthetic (seeded; model-shaped, see heal_workloads.py)"}
     cfg = {"workload": "HEAL hot path step: split + prefill GEMM (M=2048; K,N = 4096,14336 and 14336,4096; "
                        "fp32 weights, and fp16 weights in the two-product form), "
-                       "16 decode GEMMs (M=1,8,32,64 x Llama-3-8B q/o, k/v, gate/up, down; fp32 and fp16 weights), "
+                       "16 decode GEMMs (M=1,8,32,64 x Llama-3-8B q/o, k/v, gate/up, down; fp32 and fp16 weights, "
+                       "and fp32 with per-channel rescaled massive activations), "
                        "INT16 quant + dequant "
                        "(32x2048 tokens, 32+8+8 heads x 128), INT16 decode attention (B=16, T=8192, 32/8 heads)",
            "rows": sorted(sel)}

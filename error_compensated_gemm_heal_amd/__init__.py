@@ -15,6 +15,7 @@ __all__ = [
     "HealError", "lib", "heal_status_str", "heal_version", "heal_split_f32", "heal_gemm_f32c",
     "heal_gemm_f32c_workspace", "heal_pack_w", "heal_pack_w_bytes", "heal_qkv_quant_i16",
     "heal_kv_dequant_i16", "heal_attn_decode_i16", "heal_attn_decode_workspace", "PackedOperand",
+    "heal_scale_k", "heal_kshift_from_absmax",
     "PackedWeight", "HEAL_W_NK", "HEAL_W_KN", "HEAL_W_PACKED", "HEAL_A_PACKED", "HEAL_W_F16",
     "HEAL_FLAG_F16_RANGE",
     "HEAL_DQ_F32", "HEAL_DQ_F16X2",
@@ -34,9 +35,11 @@ SIGNATURES = {
     "heal_status_str": ([_INT], ctypes.c_char_p),
     "heal_version": ([], _INT),
     "heal_split_f32": ([_P, _I64, _P, _P, _P, _P], _INT),
-    "heal_gemm_f32c": ([_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _U32, _P, _SZ, _P, _P], _INT),
+    "heal_gemm_f32c": ([_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _U32, _P, _P, _SZ, _P, _P], _INT),
     "heal_gemm_f32c_workspace": ([_I64, _I64, _I64, _U32], _SZ),
-    "heal_pack_w": ([_P, _I64, _I64, _I64, _U32, _P, _SZ, _P, _P], _INT),
+    "heal_pack_w": ([_P, _I64, _I64, _I64, _U32, _P, _P, _SZ, _P, _P], _INT),
+    "heal_scale_k": ([_P, _I64, _I64, _I64, _U32, _P, _P, _I64, _P], _INT),
+    "heal_kshift_from_absmax": ([_P, _I64, ctypes.c_float, _P], _INT),
     "heal_pack_w_bytes": ([_I64, _I64], _SZ),
     "heal_qkv_quant_i16": ([_P, _I64, _I64, _I64, _P, _I64, _P, _P], _INT),
     "heal_kv_dequant_i16": ([_P, _I64, _I64, _I64, _P, _INT, _P, _P, _I64, _P], _INT),
@@ -158,7 +161,20 @@ def _weight_dtype_flag(W: torch.Tensor) -> int:
     return 0
 
 
-def heal_pack_w(W: torch.Tensor, w_layout: str = "nk", dev_status=None, out=None) -> PackedOperand:
+def _kshift(kshift, K: int, name: str):
+    """A per-channel shift vector: a device int8 tensor of K entries, or None."""
+    if kshift is None:
+        return None
+    _dev(kshift, name, torch.int8)
+    if kshift.numel() != K or (K > 1 and kshift.stride(-1) != 1):
+        raise ValueError(f"{name} must be a contiguous int8 vector of K = {K} entries")
+    return kshift
+
+
+def heal_pack_w(W: torch.Tensor, w_layout: str = "nk", dev_status=None, out=None, kshift=None) -> PackedOperand:
+    """Split an operand once into the packed form.  kshift (int8 [K], optional):
+    element (r, k) is multiplied by 2^-kshift[k] first (an activation takes the
+    shifts given to heal_gemm_f32c as a_kshift, a weight their negation)."""
     _dev(W, "W")
     flags = (HEAL_W_KN if w_layout == "kn" else HEAL_W_NK) | _weight_dtype_flag(W)
     if w_layout == "kn":
@@ -173,7 +189,8 @@ def heal_pack_w(W: torch.Tensor, w_layout: str = "nk", dev_status=None, out=None
         buf = out.buf
         if buf.numel() < nbytes:
             raise ValueError("packed buffer too small")
-    _check("heal_pack_w", lib().heal_pack_w(_ptr(W), ldw, N, K, flags, _ptr(buf), nbytes,
+    ks = _kshift(kshift, K, "kshift")
+    _check("heal_pack_w", lib().heal_pack_w(_ptr(W), ldw, N, K, flags, _ptr(ks), _ptr(buf), nbytes,
                                             _ptr(dev_status), _stream()))
     return PackedOperand(buf, N, K, f16=bool(flags & HEAL_W_F16))
 
@@ -182,9 +199,11 @@ def heal_gemm_f32c_workspace(M: int, N: int, K: int, flags: int) -> int:
     return lib().heal_gemm_f32c_workspace(M, N, K, flags)
 
 
-def heal_gemm_f32c(A, W, w_layout: str = "nk", C=None, workspace=None, dev_status=None):
+def heal_gemm_f32c(A, W, w_layout: str = "nk", C=None, workspace=None, dev_status=None, a_kshift=None):
     """C = A . B with B = W^T ('nk', W [N,K]) or B = W ('kn', W [K,N]).
-    A and/or W may be PackedOperand buffers from heal_pack_w."""
+    A and/or W may be PackedOperand buffers from heal_pack_w.  a_kshift (int8
+    [K], optional): A's element (m, k) is multiplied by 2^-a_kshift[k] before
+    its split; W must hold reduction index k multiplied by 2^+a_kshift[k]."""
     aflags = 0
     if isinstance(A, PackedOperand):
         M, K, lda, aptr, adev, aflags = A.rows, A.K, 0, _ptr(A.buf), A.buf.device, HEAL_A_PACKED
@@ -217,10 +236,42 @@ def heal_gemm_f32c(A, W, w_layout: str = "nk", C=None, workspace=None, dev_statu
         workspace = _workspace(nbytes, adev)
     elif workspace.numel() < nbytes:
         raise ValueError("workspace too small")
-    _check("heal_gemm_f32c", lib().heal_gemm_f32c(aptr, lda, wptr, ldw, _ptr(C), ldc, M, N, K, flags,
+    ks = _kshift(a_kshift, K, "a_kshift")
+    _check("heal_gemm_f32c", lib().heal_gemm_f32c(aptr, lda, wptr, ldw, _ptr(C), ldc, M, N, K, flags, _ptr(ks),
                                                   _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                                   _ptr(dev_status), _stream()))
     return C
+
+
+def heal_scale_k(X: torch.Tensor, kshift: torch.Tensor, w_layout: str = "nk", out=None):
+    """out = X with element (r, k) multiplied by 2^-kshift[k] (fp32 or fp16, layout
+    'nk' = [rows, K] or 'kn' = [K, rows]); out may be X for an in-place update."""
+    _dev(X, "X")
+    flags = (HEAL_W_KN if w_layout == "kn" else HEAL_W_NK) | _weight_dtype_flag(X)
+    if w_layout == "kn":
+        K, rows = X.shape
+    else:
+        rows, K = X.shape
+    ks = _kshift(kshift, K, "kshift")
+    if ks is None:
+        raise ValueError("kshift is required")
+    out = torch.empty_like(X) if out is None else out
+    if out.shape != X.shape or out.dtype != X.dtype:
+        raise ValueError("out must match X in shape and dtype")
+    _check("heal_scale_k", lib().heal_scale_k(_ptr(X), _rowmajor_ld(X, "X"), rows, K, flags, _ptr(ks), _ptr(out),
+                                              _rowmajor_ld(out, "out"), _stream()))
+    return out
+
+
+def heal_kshift_from_absmax(absmax, limit: float = 32768.0):
+    """Host call: per-channel shifts (int8 numpy array) from calibration maxima
+    max|A[:, k]|: the smallest s >= 0 with absmax[k] * 2^-s < limit."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(absmax, dtype=np.float32).reshape(-1))
+    out = np.zeros(a.size, dtype=np.int8)
+    _check("heal_kshift_from_absmax", lib().heal_kshift_from_absmax(
+        a.ctypes.data_as(ctypes.c_void_p), a.size, float(limit), out.ctypes.data_as(ctypes.c_void_p)))
+    return out
 
 
 # ---- INT16 quant / dequant -------------------------------------------------------------

@@ -1,6 +1,7 @@
 // C ABI of libheal: argument validation (host only, before any HIP call),
 // workspace layout and kernel selection.  Entry points and their contracts
 // are documented in include/heal.h.
+#include <cmath>
 #include <cstdint>
 
 #include "heal_internal.h"
@@ -53,7 +54,7 @@ const char* heal_status_str(heal_status s) {
     return "HEAL: unknown status";
 }
 
-int heal_version(void) { return (1 << 16) | 0; }
+int heal_version(void) { return (1 << 16) | (1 << 8); }
 
 heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo,
                            uint32_t* dev_status, void* stream) {
@@ -71,7 +72,8 @@ size_t heal_pack_w_bytes(int64_t N, int64_t K) {
 }
 
 heal_status heal_pack_w(const void* W, int64_t ldw, int64_t N, int64_t K, uint32_t flags,
-                        void* packed, size_t packed_bytes, uint32_t* dev_status, void* stream) {
+                        const int8_t* kshift, void* packed, size_t packed_bytes, uint32_t* dev_status,
+                        void* stream) {
     if (N < 0 || K < 0 || N >= kMaxDim || K >= kMaxDim) return HEAL_ERR_SHAPE;
     if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_F16)) return HEAL_ERR_UNSUPPORTED;
     if (N == 0 || K == 0) return HEAL_OK;
@@ -81,7 +83,7 @@ heal_status heal_pack_w(const void* W, int64_t ldw, int64_t N, int64_t K, uint32
     if (ldw < (kn ? N : K)) return HEAL_ERR_STRIDE;
     if (misaligned(W, f16 ? 2 : 4) || misaligned(packed, 256) || misaligned(dev_status, 4)) return HEAL_ERR_ALIGN;
     if (packed_bytes < (size_t)pack_bytes(N, K)) return HEAL_ERR_WORKSPACE;
-    return hip_status(launch_pack(W, f16, ldw, N, K, kn ? 1 : 0, packed, dev_status,
+    return hip_status(launch_pack(W, f16, ldw, N, K, kn ? 1 : 0, kshift, packed, dev_status,
                                   static_cast<hipStream_t>(stream)));
 }
 
@@ -97,11 +99,12 @@ size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags)
 }
 
 heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t ldw, float* C,
-                           int64_t ldc, int64_t M, int64_t N, int64_t K, uint32_t flags,
+                           int64_t ldc, int64_t M, int64_t N, int64_t K, uint32_t flags, const int8_t* a_kshift,
                            void* workspace, size_t workspace_bytes, uint32_t* dev_status,
                            void* stream) {
     if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return HEAL_ERR_SHAPE;
     if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_PACKED | HEAL_A_PACKED | HEAL_W_F16)) return HEAL_ERR_UNSUPPORTED;
+    if ((flags & HEAL_A_PACKED) && a_kshift) return HEAL_ERR_UNSUPPORTED;   // a packed A carries its shifts
     if (M == 0 || N == 0) return HEAL_OK;
     if (!C) return HEAL_ERR_NULL;
     if (ldc < N) return HEAL_ERR_STRIDE;
@@ -131,13 +134,14 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
         if (ldw >= kMaxDecodeLdw || lda >= kMaxDecodeLda) return HEAL_ERR_UNSUPPORTED;
         const DecodePlan p = decode_plan(M, N, K);
         unsigned char* ws = static_cast<unsigned char*>(workspace);
-        return hip_status(launch_gemm_decode(A, lda, W, wf16, ldw, C, ldc, M, N, K, ws, p, dev_status, s));
+        return hip_status(
+            launch_gemm_decode(A, lda, a_kshift, W, wf16, ldw, C, ldc, M, N, K, ws, p, dev_status, s));
     }
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     const void* apk = A;
     const void* bpk = W;
     if (!a_packed) {
-        hipError_t e = launch_pack(A, false, lda, M, K, 0, ws, dev_status, s);
+        hipError_t e = launch_pack(A, false, lda, M, K, 0, a_kshift, ws, dev_status, s);
         if (e != hipSuccess) return HEAL_ERR_HIP;
         apk = ws;
         ws += round256(pack_bytes(M, K));
@@ -145,11 +149,48 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
     if (!packed) {
         void* wpk = ws;
         hipError_t e;
-        e = launch_pack(W, wf16, ldw, N, K, kn ? 1 : 0, wpk, dev_status, s);
+        e = launch_pack(W, wf16, ldw, N, K, kn ? 1 : 0, nullptr, wpk, dev_status, s);
         if (e != hipSuccess) return HEAL_ERR_HIP;
         bpk = wpk;
     }
     return hip_status(launch_gemm_prefill(apk, bpk, wf16, C, ldc, M, N, K, s));
+}
+
+heal_status heal_scale_k(const void* X, int64_t ldx, int64_t rows, int64_t K, uint32_t flags,
+                         const int8_t* kshift, void* out, int64_t ldo, void* stream) {
+    if (rows < 0 || K < 0 || rows >= kMaxDim || K >= kMaxDim) return HEAL_ERR_SHAPE;
+    if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_F16)) return HEAL_ERR_UNSUPPORTED;
+    if (rows == 0 || K == 0) return HEAL_OK;
+    if (!X || !kshift || !out) return HEAL_ERR_NULL;
+    const bool kn = flags & HEAL_W_KN;
+    const bool f16 = flags & HEAL_W_F16;
+    const int64_t row_len = kn ? rows : K;
+    if (ldx < row_len || ldo < row_len) return HEAL_ERR_STRIDE;
+    if (misaligned(X, f16 ? 2 : 4) || misaligned(out, f16 ? 2 : 4)) return HEAL_ERR_ALIGN;
+    return hip_status(launch_scale_k(X, f16, ldx, rows, K, kn ? 1 : 0, kshift, out, ldo,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+heal_status heal_kshift_from_absmax(const float* absmax, int64_t K, float limit, int8_t* kshift) {
+    if (K < 0 || K >= kMaxDim) return HEAL_ERR_SHAPE;
+    if (K == 0) return HEAL_OK;
+    if (!absmax || !kshift) return HEAL_ERR_NULL;
+    if (!(limit >= 1.0f && limit <= 65504.0f)) return HEAL_ERR_UNSUPPORTED;
+    // smallest s >= 0 with absmax * 2^-s < limit: scaling by a power of two is
+    // exact in double, so each comparison is exact.  Validate all first, so a
+    // rejected call writes nothing.
+    auto shift_of = [limit](double a) {
+        int sh = 0;
+        while (sh <= 127 && std::ldexp(a, -sh) >= (double)limit) ++sh;
+        return sh;
+    };
+    for (int64_t k = 0; k < K; ++k) {
+        const double a = absmax[k];
+        if (!(a >= 0.0 && a <= 3.4028234663852886e38)) return HEAL_ERR_UNSUPPORTED;   // negative, NaN, inf
+        if (shift_of(a) > 127) return HEAL_ERR_UNSUPPORTED;
+    }
+    for (int64_t k = 0; k < K; ++k) kshift[k] = (int8_t)shift_of(absmax[k]);
+    return HEAL_OK;
 }
 
 heal_status heal_qkv_quant_i16(const float* X, int64_t rows, int64_t D, int64_t ldx, int16_t* codes,

@@ -63,10 +63,12 @@ constexpr int block_bytes() { return 2 * STEPS * MT * 64 * 16; }
 // Block b (k in [128 b, 128 b + 128)), plane p (0 = hi, 1 = lo), step s,
 // tile t, lane l = 16 g + r holds, as 8 fp16, row 16 t + r at
 // k = 128 b + 32 s + {4g .. 4g+3, 16+4g .. 16+4g+3}.  Rows >= M and k >= K
-// are zero.  One thread per (b, s, t, l).
+// are zero.  kshift (nullable): element (m, k) is first multiplied by
+// 2^-kshift[k] (exact).  One thread per (b, s, t, l).
 template <int MT>
 __global__ __launch_bounds__(256) void asplit_kernel(const float* __restrict__ A, int64_t lda, int M,
-                                                     int K, int nblk, unsigned char* __restrict__ out,
+                                                     int K, int nblk, const int8_t* __restrict__ kshift,
+                                                     unsigned char* __restrict__ out,
                                                      uint32_t* __restrict__ status) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t total = (int64_t)nblk * STEPS * MT * 64;
@@ -83,6 +85,7 @@ __global__ __launch_bounds__(256) void asplit_kernel(const float* __restrict__ A
         for (int j = 0; j < 8; ++j) {
             const int64_t k = k0 + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
             x[j] = (m < M && k < K) ? A[(int64_t)m * lda + k] : 0.0f;
+            if (kshift && k < K) x[j] = __builtin_ldexpf(x[j], -(int)kshift[k]);
         }
         half8 h, lo;
 #pragma unroll
@@ -131,13 +134,17 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // step keeps two products, A_hi.W and A_lo.W (2^-10 applied at the end).
 // AVEC: A rows 16-byte aligned, activation units load as one 16-byte load.
 // MT == 1 stages A itself (A, lda); MT > 1 copies the pre-split blocks (Ablk).
-template <int MT, bool VEC, bool WF16, bool AVEC>
+// SHIFT (MT == 1): element (m, k) of A is multiplied by 2^-kshift[k] before
+// its split.
+template <int MT, bool VEC, bool WF16, bool AVEC, bool SHIFT>
 __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const float* __restrict__ A, int64_t lda,
                                                           const unsigned char* __restrict__ Ablk,
                                                           int a_total_bytes, const void* __restrict__ W,
                                                           int64_t ldw, float* __restrict__ out, int64_t ldo,
                                                           int64_t split_stride, int M, int N, int K,
-                                                          int kchunk, uint32_t* __restrict__ status) {
+                                                          int kchunk, const int8_t* __restrict__ kshift,
+                                                          uint32_t* __restrict__ status) {
+    static_assert(!SHIFT || MT == 1, "with MT > 1 the shift is applied by asplit_kernel");
     constexpr int BB = block_bytes<MT>();
     constexpr bool INK = MT == 1;                   // split the activation in the kernel
     constexpr int AU = 2 * MT;                      // 4-wide activation units per thread per block
@@ -163,9 +170,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const float* __res
     //      hi and lo halves go to the 16-byte operand slot (s, t, lane 16 g + r),
     //      bytes 8 half .. 8 half + 7, of the hi and lo planes.
     float4 areg[AU];
+    int sreg[AU][4];   // SHIFT: the units' 2^-kshift exponents (k >= K reads 0)
     // rows >= M fall outside the resource and read as zero; k past the
     // chunk end is zeroed when the block is stored
     const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(A, (uint32_t)((int64_t)M * lda * 4));
+    const __amdgpu_buffer_rsrc_t ksrc = make_rsrc(kshift, SHIFT ? (uint32_t)K : 0u);
     auto unit_k = [&](int b, int x) {
         return k_begin + KA * b + 32 * ((x >> 7) & 3) + 16 * ((x >> 6) & 1) + 4 * ((x >> 4) & 3);
     };
@@ -183,6 +192,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const float* __res
                                       __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(arsrc, off + 8, 0, 0)),
                                       __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(arsrc, off + 12, 0, 0)));
             }
+            if constexpr (SHIFT) {
+                const uint32_t k0 = (uint32_t)unit_k(b, x);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    sreg[i][j] = (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(ksrc, k0 + j, 0, 0);
+            }
         }
     };
     float amax = 0.0f;
@@ -193,8 +208,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const float* __res
             const int x = tid + 256 * i;
             const int r = x & 15, gg = (x >> 4) & 3, half = (x >> 6) & 1, st = (x >> 7) & 3, t = x >> 9;
             const int k = unit_k(b, x);
-            const float v[4] = {k < k_end ? areg[i].x : 0.0f, k + 1 < k_end ? areg[i].y : 0.0f,
-                                k + 2 < k_end ? areg[i].z : 0.0f, k + 3 < k_end ? areg[i].w : 0.0f};
+            float v[4] = {k < k_end ? areg[i].x : 0.0f, k + 1 < k_end ? areg[i].y : 0.0f,
+                          k + 2 < k_end ? areg[i].z : 0.0f, k + 3 < k_end ? areg[i].w : 0.0f};
+            if constexpr (SHIFT) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = __builtin_ldexpf(v[j], -sreg[i][j]);
+            }
             half4 h, l;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -417,9 +436,9 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
     return p;
 }
 
-hipError_t launch_gemm_decode(const float* A, int64_t lda, const void* W, bool wf16, int64_t ldw,
-                              float* C, int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace,
-                              const DecodePlan& plan, uint32_t* status, hipStream_t s) {
+hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift, const void* W, bool wf16,
+                              int64_t ldw, float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                              void* workspace, const DecodePlan& plan, uint32_t* status, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
     if (M > 64 || K == 0) return hipErrorInvalidValue;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -436,34 +455,39 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const void* W, bool w
     const bool vec = (reinterpret_cast<uintptr_t>(W) & walign) == 0 && (ldw & 3) == 0 && (K & 31) == 0;
     // activation units load as float4 when rows are 16-byte aligned
     const bool avec = (reinterpret_cast<uintptr_t>(A) & 15) == 0 && (lda & 3) == 0;
-#define HEAL_DEC_MAIN(MT_, VEC_, F16_, AV_)                                                             \
-    hipLaunchKernelGGL((gemm_decode_kernel<MT_, VEC_, F16_, AV_>), grid, dim3(64 * NW), 2 * block_bytes<MT_>(), \
-                       s, A, lda, ablk, (int)plan.a_bytes, W, ldw, out, ldo, stride, (int)M, (int)N, (int)K,  \
-                       (int)plan.kchunk, status)
-#define HEAL_DEC_AV(MT_, VEC_, F16_)                                                                    \
+#define HEAL_DEC_MAIN(MT_, VEC_, F16_, AV_, SH_)                                                        \
+    hipLaunchKernelGGL((gemm_decode_kernel<MT_, VEC_, F16_, AV_, SH_>), grid, dim3(64 * NW),             \
+                       2 * block_bytes<MT_>(), s, A, lda, ablk, (int)plan.a_bytes, W, ldw, out, ldo, stride, \
+                       (int)M, (int)N, (int)K, (int)plan.kchunk, kshift, status)
+#define HEAL_DEC_AV(MT_, VEC_, F16_, SH_)                                                               \
     do {                                                                                                \
-        if (avec) HEAL_DEC_MAIN(MT_, VEC_, F16_, true);                                                 \
-        else HEAL_DEC_MAIN(MT_, VEC_, F16_, false);                                                     \
+        if (avec) HEAL_DEC_MAIN(MT_, VEC_, F16_, true, SH_);                                            \
+        else HEAL_DEC_MAIN(MT_, VEC_, F16_, false, SH_);                                                \
     } while (0)
-#define HEAL_DEC(MT_)                                                                                   \
+#define HEAL_DEC(MT_, SH_)                                                                              \
     do {                                                                                                \
         if ((MT_) > 1) {                                                                                \
             const int64_t tot = (int64_t)nablk * STEPS * (MT_) * 64;                                    \
             hipLaunchKernelGGL((asplit_kernel<MT_>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, \
-                               A, lda, (int)M, (int)K, nablk, ablk, status);                            \
+                               A, lda, (int)M, (int)K, nablk, kshift, ablk, status);                    \
         }                                                                                               \
         if (wf16) {                                                                                     \
-            if (vec) HEAL_DEC_AV(MT_, true, true);                                                      \
-            else HEAL_DEC_AV(MT_, false, true);                                                         \
+            if (vec) HEAL_DEC_AV(MT_, true, true, SH_);                                                 \
+            else HEAL_DEC_AV(MT_, false, true, SH_);                                                    \
         } else {                                                                                        \
-            if (vec) HEAL_DEC_AV(MT_, true, false);                                                     \
-            else HEAL_DEC_AV(MT_, false, false);                                                        \
+            if (vec) HEAL_DEC_AV(MT_, true, false, SH_);                                                \
+            else HEAL_DEC_AV(MT_, false, false, SH_);                                                   \
         }                                                                                               \
     } while (0)
     const int mt = mtiles(M);
-    if (mt == 1) HEAL_DEC(1);
-    else if (mt == 2) HEAL_DEC(2);
-    else HEAL_DEC(4);
+    if (mt == 1) {
+        if (kshift) HEAL_DEC(1, true);
+        else HEAL_DEC(1, false);
+    } else if (mt == 2) {
+        HEAL_DEC(2, false);
+    } else {
+        HEAL_DEC(4, false);
+    }
 #undef HEAL_DEC
 #undef HEAL_DEC_AV
 #undef HEAL_DEC_MAIN

@@ -62,8 +62,13 @@ hipError_t launch_split(const float* X, int64_t n, uint16_t* hi, uint16_t* lo, u
 // Pack rows into the layout above.  src holds fp32 values, or binary16
 // values when f16 (their residual is zero).  kn == 0: src is [rows, K] with
 // ld; kn == 1: src is [K, rows] with ld (the packed operand is its transpose).
-hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int64_t K, int kn, void* packed,
-                       uint32_t* status, hipStream_t s);
+// kshift (nullable): element (r, k) is multiplied by 2^-kshift[k] first.
+hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int64_t K, int kn,
+                       const int8_t* kshift, void* packed, uint32_t* status, hipStream_t s);
+// out = src with element (r, k) multiplied by 2^-kshift[k], same element type
+// and layout (kn as above), ldo for out.
+hipError_t launch_scale_k(const void* src, bool f16, int64_t ld, int64_t rows, int64_t K, int kn,
+                          const int8_t* kshift, void* out, int64_t ldo, hipStream_t s);
 
 hipError_t launch_quant(const float* X, int64_t rows, int64_t D, int64_t ldx, int16_t* codes,
                         int64_t ldq, float* scales, hipStream_t s);
@@ -86,10 +91,11 @@ struct DecodePlan {
     int64_t p_bytes;   // workspace bytes of the split-K partials
 };
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K);
-// W is fp32, or binary16 values when wf16 (the two-product form).
-hipError_t launch_gemm_decode(const float* A, int64_t lda, const void* W, bool wf16, int64_t ldw,
-                              float* C, int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace,
-                              const DecodePlan& plan, uint32_t* status, hipStream_t s);
+// W is fp32, or binary16 values when wf16 (the two-product form).  kshift
+// (nullable): A's element (m, k) is multiplied by 2^-kshift[k] before its split.
+hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift, const void* W, bool wf16,
+                              int64_t ldw, float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                              void* workspace, const DecodePlan& plan, uint32_t* status, hipStream_t s);
 
 int64_t attn_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D);
 hipError_t launch_attn_decode(const int16_t* q, const float* qs, const int16_t* k, const float* ks,

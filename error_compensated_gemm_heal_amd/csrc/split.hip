@@ -9,6 +9,8 @@
 //    hi/lo-interleaved layout the prefill GEMM streams (one 128-byte line per
 //    row and 32-wide k block), so the GEMM needs no bounds checks.
 // Both are HBM-bound: 4 bytes read and 4 bytes written per element.
+#include <algorithm>
+
 #include "heal_internal.h"
 
 namespace heal {
@@ -63,13 +65,20 @@ hipError_t launch_split(const float* X, int64_t n, uint16_t* hi, uint16_t* lo, u
 __device__ __forceinline__ float src_value(float x) { return x; }
 __device__ __forceinline__ float src_value(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
+// x * 2^-kshift[k] (exact for normal results); kshift may be NULL.
+__device__ __forceinline__ float kscaled(float x, const int8_t* kshift, int64_t k) {
+    return kshift ? __builtin_ldexpf(x, -(int)kshift[k]) : x;
+}
+
 // Packed layout writer, source rows contiguous in k ([rows, K], ld).
 // One thread per (row, 4 consecutive k); the grid covers the padded extent
-// so the zero padding is written too.
+// so the zero padding is written too.  kshift (nullable): element (r, k) is
+// multiplied by 2^-kshift[k] before its split.
 template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void pack_rowmajor_kernel(const T* __restrict__ src, int64_t ld,
                                                             int64_t rows, int64_t K, int64_t Kp,
-                                                            int64_t rows_p, uint16_t* __restrict__ out,
+                                                            int64_t rows_p, const int8_t* __restrict__ kshift,
+                                                            uint16_t* __restrict__ out,
                                                             uint32_t* __restrict__ status) {
     const int64_t kq = Kp >> 2;  // 4-wide groups per padded row
     const int64_t total = rows_p * kq;
@@ -94,6 +103,9 @@ __global__ __launch_bounds__(256) void pack_rowmajor_kernel(const T* __restrict_
                 for (int j = 0; j < 4; ++j)
                     if (k + j < K) x[j] = src_value(p[j]);
             }
+            if (kshift)
+                for (int j = 0; j < 4; ++j)
+                    if (k + j < K) x[j] = kscaled(x[j], kshift, k + j);
         }
         uint16_t h[4], l[4];
         for (int j = 0; j < 4; ++j) {
@@ -117,7 +129,8 @@ __global__ __launch_bounds__(256) void pack_rowmajor_kernel(const T* __restrict_
 template <typename T>
 __global__ __launch_bounds__(256) void pack_colmajor_kernel(const T* __restrict__ src, int64_t ld,
                                                             int64_t rows, int64_t K, int64_t Kp,
-                                                            int64_t rows_p, uint16_t* __restrict__ out,
+                                                            int64_t rows_p, const int8_t* __restrict__ kshift,
+                                                            uint16_t* __restrict__ out,
                                                             uint32_t* __restrict__ status) {
     const int64_t kq = Kp >> 2;
     const int64_t total = rows_p * kq;
@@ -129,7 +142,7 @@ __global__ __launch_bounds__(256) void pack_colmajor_kernel(const T* __restrict_
         const int64_t k = kg << 2;
         uint16_t h[4], l[4];
         for (int j = 0; j < 4; ++j) {
-            float x = (r < rows && k + j < K) ? src_value(src[(k + j) * ld + r]) : 0.f;
+            float x = (r < rows && k + j < K) ? kscaled(src_value(src[(k + j) * ld + r]), kshift, k + j) : 0.f;
             _Float16 hh, ll;
             split_one(x, hh, ll);
             bad |= f16_out_of_range(x);
@@ -144,8 +157,8 @@ __global__ __launch_bounds__(256) void pack_colmajor_kernel(const T* __restrict_
     if (bad && status) atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
 }
 
-hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int64_t K, int kn, void* packed,
-                       uint32_t* status, hipStream_t s) {
+hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int64_t K, int kn,
+                       const int8_t* kshift, void* packed, uint32_t* status, hipStream_t s) {
     const int64_t Kp = pack_kp(K), rows_p = pack_rows(rows);
     const int64_t total = rows_p * (Kp >> 2);
     if (total == 0) return hipSuccess;
@@ -158,25 +171,64 @@ hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int6
         const uint16_t* p = static_cast<const uint16_t*>(src);
         if (kn)
             hipLaunchKernelGGL(pack_colmajor_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, s, p, ld,
-                               rows, K, Kp, rows_p, out, status);
+                               rows, K, Kp, rows_p, kshift, out, status);
         else if (vec)
             hipLaunchKernelGGL((pack_rowmajor_kernel<uint16_t, true>), dim3((unsigned)blocks), dim3(256), 0, s, p,
-                               ld, rows, K, Kp, rows_p, out, status);
+                               ld, rows, K, Kp, rows_p, kshift, out, status);
         else
             hipLaunchKernelGGL((pack_rowmajor_kernel<uint16_t, false>), dim3((unsigned)blocks), dim3(256), 0, s,
-                               p, ld, rows, K, Kp, rows_p, out, status);
+                               p, ld, rows, K, Kp, rows_p, kshift, out, status);
     } else {
         const float* p = static_cast<const float*>(src);
         if (kn)
             hipLaunchKernelGGL(pack_colmajor_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, p, ld, rows,
-                               K, Kp, rows_p, out, status);
+                               K, Kp, rows_p, kshift, out, status);
         else if (vec)
             hipLaunchKernelGGL((pack_rowmajor_kernel<float, true>), dim3((unsigned)blocks), dim3(256), 0, s, p, ld,
-                               rows, K, Kp, rows_p, out, status);
+                               rows, K, Kp, rows_p, kshift, out, status);
         else
             hipLaunchKernelGGL((pack_rowmajor_kernel<float, false>), dim3((unsigned)blocks), dim3(256), 0, s, p,
-                               ld, rows, K, Kp, rows_p, out, status);
+                               ld, rows, K, Kp, rows_p, kshift, out, status);
     }
+    return hipGetLastError();
+}
+
+// out = src with element (r, k) multiplied by 2^-kshift[k]: rows of K
+// ([rows, K], kn == 0) or K rows of `rows` ([K, rows], kn == 1).  Exact for
+// results in the format's normal range.
+template <typename T>
+__global__ __launch_bounds__(256) void scale_k_kernel(const T* __restrict__ src, int64_t ld, int64_t rows,
+                                                      int64_t K, int kn, const int8_t* __restrict__ kshift,
+                                                      T* __restrict__ out, int64_t ldo) {
+    const int64_t total = rows * K;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        // kn == 0: i runs along k within a row; kn == 1: along the row within a k
+        const int64_t outer = kn ? i / rows : i / K;
+        const int64_t inner = kn ? i - outer * rows : i - outer * K;
+        const int64_t k = kn ? outer : inner;
+        const int e = -(int)kshift[k];
+        if constexpr (sizeof(T) == 4) {
+            out[outer * ldo + inner] = __builtin_ldexpf(src[outer * ld + inner], e);
+        } else {
+            const float v = (float)__builtin_bit_cast(_Float16, src[outer * ld + inner]);
+            out[outer * ldo + inner] = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(v, e));
+        }
+    }
+}
+
+hipError_t launch_scale_k(const void* src, bool f16, int64_t ld, int64_t rows, int64_t K, int kn,
+                          const int8_t* kshift, void* out, int64_t ldo, hipStream_t s) {
+    const int64_t total = rows * K;
+    if (total == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 256 * 64);
+    if (f16)
+        hipLaunchKernelGGL(scale_k_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s,
+                           static_cast<const uint16_t*>(src), ld, rows, K, kn, kshift, static_cast<uint16_t*>(out),
+                           ldo);
+    else
+        hipLaunchKernelGGL(scale_k_kernel<float>, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(src),
+                           ld, rows, K, kn, kshift, static_cast<float*>(out), ldo);
     return hipGetLastError();
 }
 

@@ -47,6 +47,16 @@ def weights_nk(N: int, K: int, seed: int, std: float = 0.02) -> np.ndarray:
     return normal(rng(seed), (N, K), std)
 
 
+def overflow_gemm(M: int, K: int, N: int, seed: int):
+    """Linear layer whose activation has massive channels beyond FP16's range:
+    round(0.005 K) channels (the pages report 0.1-1% of fixed channels) x 2e5,
+    so |x| reaches ~1e6 > 65504; W ~ N(0, 0.02^2)."""
+    n_out = max(1, int(round(0.005 * K)))
+    A = activations(M, K, seed, n_outlier=n_out, outlier_gain=2.0e5)
+    W = weights_nk(N, K, seed + 500)
+    return A, W
+
+
 def smoke_gemm(seed: int = 1000):
     """Small case: A 16x256 ~ N(0,1) with 2 channels x100; W [256,256] ~ N(0, 0.02)."""
     A = activations(16, 256, seed, n_outlier=2, outlier_gain=100.0)

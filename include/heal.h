@@ -131,6 +131,17 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  *          HEAL_W_F16, or its lo planes are ignored), and/or | HEAL_A_PACKED
  *          (A then is heal_pack_w(A, lda, M, K, HEAL_W_NK)'s buffer: an
  *          activation split once can feed several GEMMs)
+ *   a_kshift  device int8 [K], nullable.  Per-channel power-of-two
+ *          rescaling of massive activations ([GEMM], the paragraph on FP16
+ *          overflow: values beyond FP16's range sit in a small fixed set of
+ *          channels, and rescaling those channels, e.g. on the weight side,
+ *          removes the overflow at no cost).  Element (m, k) of A is
+ *          multiplied by 2^-a_kshift[k] before its split, exactly; the caller
+ *          holds W with reduction index k multiplied by 2^+a_kshift[k]
+ *          (prepared once: heal_scale_k, or heal_pack_w with the negated
+ *          shifts), so C = A.B is unchanged.  Shifts come from
+ *          heal_kshift_from_absmax.  Not with HEAL_A_PACKED (UNSUPPORTED): a
+ *          packed activation takes its shifts in heal_pack_w.
  *   workspace  device, >= heal_gemm_f32c_workspace(M, N, K, flags) bytes,
  *          256-byte aligned (NULL allowed when that size is 0)
  *   dev_status  device, nullable; HEAL_FLAG_F16_RANGE as in heal_split_f32.
@@ -140,8 +151,8 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  * ------------------------------------------------------------------------ */
 heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t ldw,
                            float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                           uint32_t flags, void* workspace, size_t workspace_bytes,
-                           uint32_t* dev_status, void* stream);
+                           uint32_t flags, const int8_t* a_kshift, void* workspace,
+                           size_t workspace_bytes, uint32_t* dev_status, void* stream);
 
 /* Workspace bytes heal_gemm_f32c needs for this shape and flags. */
 size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags);
@@ -157,12 +168,44 @@ size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags)
  *   W      as in heal_gemm_f32c (flags HEAL_W_NK or HEAL_W_KN, optionally
  *          | HEAL_W_F16: binary16 input, its lo parts are zero), 4-byte
  *          aligned (2-byte with HEAL_W_F16)
+ *   kshift device int8 [K], nullable: element (r, k) is multiplied by
+ *          2^-kshift[k] before its split (exact; an activation takes the
+ *          shifts of heal_gemm_f32c's a_kshift, a weight their negation)
  *   packed device, >= heal_pack_w_bytes(N, K) bytes, 256-byte aligned
  * ------------------------------------------------------------------------ */
 heal_status heal_pack_w(const void* W, int64_t ldw, int64_t N, int64_t K, uint32_t flags,
-                        void* packed, size_t packed_bytes, uint32_t* dev_status, void* stream);
+                        const int8_t* kshift, void* packed, size_t packed_bytes,
+                        uint32_t* dev_status, void* stream);
 
 size_t heal_pack_w_bytes(int64_t N, int64_t K);
+
+/* ------------------------------------------------------------------------
+ * heal_scale_k -- per-channel power-of-two rescaling of an operand.  [GEMM]
+ *  out = X with element (r, k) multiplied by 2^-kshift[k]: the weight-side
+ *  half of heal_gemm_f32c's a_kshift (pass the negated shifts to scale a
+ *  weight up).  Exact while results stay in the format's normal range.
+ *   X, out device, rows x K in the layout of flags (HEAL_W_NK: [rows, K];
+ *          HEAL_W_KN: [K, rows]), fp32, or binary16 with HEAL_W_F16; 4-byte
+ *          (2-byte) aligned; ldx and ldo >= the row length.  out may be X
+ *          (same ld) for an in-place update.
+ *   kshift device int8 [K]
+ * ------------------------------------------------------------------------ */
+heal_status heal_scale_k(const void* X, int64_t ldx, int64_t rows, int64_t K, uint32_t flags,
+                         const int8_t* kshift, void* out, int64_t ldo, void* stream);
+
+/* ------------------------------------------------------------------------
+ * heal_kshift_from_absmax -- channel shifts from calibration maxima.  [GEMM]
+ *  Host call on host arrays: kshift[k] = the smallest s >= 0 with
+ *  absmax[k] * 2^-s < limit (exact), so channels inside the limit keep
+ *  s = 0 and only outlier channels are rescaled.  With limit <= 32768 the
+ *  scaled activations split with a finite fp16 high part.
+ *   absmax host fp32 [K]: max |A[:, k]| over calibration data (finite, >= 0)
+ *   limit  in [1, 65504]
+ *   kshift host int8 [K], written only when the call succeeds
+ * Errors: UNSUPPORTED for a limit out of range, an absmax that is negative,
+ * NaN or inf, or a shift above 127.
+ * ------------------------------------------------------------------------ */
+heal_status heal_kshift_from_absmax(const float* absmax, int64_t K, float limit, int8_t* kshift);
 
 /* ------------------------------------------------------------------------
  * heal_qkv_quant_i16 -- INT16 symmetric absmax quantization.   [INT16]

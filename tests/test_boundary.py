@@ -11,6 +11,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import error_compensated_gemm_heal_amd as heal
@@ -41,7 +42,7 @@ def test_header_symbols_exported_and_bound():
 def test_status_strings_and_version():
     for code in range(8):
         assert heal.heal_status_str(code).startswith("HEAL")
-    assert heal.heal_version() >> 16 == 1
+    assert heal.heal_version() >> 16 == 1 and (heal.heal_version() >> 8) & 0xff >= 1
 
 
 def test_split_validation():
@@ -54,8 +55,8 @@ def test_split_validation():
 
 
 def _gemm(A=FAKE, lda=4096, W=FAKE, ldw=4096, C=FAKE, ldc=4096, M=8, N=4096, K=4096, flags=0, ws=FAKE,
-          wsb=1 << 30, st=None):
-    return heal.lib().heal_gemm_f32c(A, lda, W, ldw, C, ldc, M, N, K, flags, ws, wsb, st, None)
+          wsb=1 << 30, st=None, ks=None):
+    return heal.lib().heal_gemm_f32c(A, lda, W, ldw, C, ldc, M, N, K, flags, ks, ws, wsb, st, None)
 
 
 def test_gemm_validation():
@@ -79,6 +80,7 @@ def test_gemm_validation():
     assert _gemm(flags=heal.HEAL_W_PACKED, W=ctypes.c_void_p(0x10010)) == ALIGN
     assert _gemm(flags=heal.HEAL_A_PACKED, A=ctypes.c_void_p(0x10010)) == ALIGN
     assert _gemm(flags=16) == UNSUP
+    assert _gemm(flags=heal.HEAL_A_PACKED, A=ctypes.c_void_p(0x10100), ks=FAKE) == UNSUP   # packed A: shift at pack time
     assert heal.heal_gemm_f32c_workspace(8, 4096, 4096, 0) > 0     # split-K partials
     assert _gemm(ws=None) == WS
     assert _gemm(wsb=16) == WS
@@ -105,16 +107,55 @@ def test_gemm_workspace_sizes():
 
 def test_pack_validation():
     L = heal.lib()
-    assert L.heal_pack_w(FAKE, 64, -1, 64, 0, FAKE, 1 << 30, None, None) == SHAPE
-    assert L.heal_pack_w(FAKE, 64, 64, 64, 4, FAKE, 1 << 30, None, None) == UNSUP
-    assert L.heal_pack_w(FAKE, 64, 0, 64, 0, None, 0, None, None) == OK
-    assert L.heal_pack_w(None, 64, 64, 64, 0, FAKE, 1 << 30, None, None) == NULL
-    assert L.heal_pack_w(FAKE, 32, 64, 64, 0, FAKE, 1 << 30, None, None) == STRIDE
-    assert L.heal_pack_w(FAKE, 64, 64, 64, 0, ctypes.c_void_p(0x10080), 1 << 30, None, None) == ALIGN
-    assert L.heal_pack_w(ctypes.c_void_p(0x10002), 64, 64, 64, 0, FAKE, 1 << 30, None, None) == ALIGN
-    assert L.heal_pack_w(ctypes.c_void_p(0x10001), 64, 64, 64, heal.HEAL_W_F16, FAKE, 1 << 30, None, None) == ALIGN
-    assert L.heal_pack_w(FAKE, 64, 64, 64, heal.HEAL_W_F16 | 16, FAKE, 1 << 30, None, None) == UNSUP
-    assert L.heal_pack_w(FAKE, 64, 64, 64, 0, FAKE, 100, None, None) == WS
+    assert L.heal_pack_w(FAKE, 64, -1, 64, 0, None, FAKE, 1 << 30, None, None) == SHAPE
+    assert L.heal_pack_w(FAKE, 64, 64, 64, 4, None, FAKE, 1 << 30, None, None) == UNSUP
+    assert L.heal_pack_w(FAKE, 64, 0, 64, 0, None, None, 0, None, None) == OK
+    assert L.heal_pack_w(None, 64, 64, 64, 0, None, FAKE, 1 << 30, None, None) == NULL
+    assert L.heal_pack_w(FAKE, 32, 64, 64, 0, None, FAKE, 1 << 30, None, None) == STRIDE
+    assert L.heal_pack_w(FAKE, 64, 64, 64, 0, None, ctypes.c_void_p(0x10080), 1 << 30, None, None) == ALIGN
+    assert L.heal_pack_w(ctypes.c_void_p(0x10002), 64, 64, 64, 0, None, FAKE, 1 << 30, None, None) == ALIGN
+    assert L.heal_pack_w(ctypes.c_void_p(0x10001), 64, 64, 64, heal.HEAL_W_F16, None, FAKE, 1 << 30, None, None) == ALIGN
+    assert L.heal_pack_w(FAKE, 64, 64, 64, heal.HEAL_W_F16 | 16, None, FAKE, 1 << 30, None, None) == UNSUP
+    assert L.heal_pack_w(FAKE, 64, 64, 64, 0, None, FAKE, 100, None, None) == WS
+
+
+def test_scale_k_validation():
+    L = heal.lib()
+    sk = L.heal_scale_k
+    assert sk(FAKE, 64, -1, 64, 0, FAKE, FAKE, 64, None) == SHAPE
+    assert sk(FAKE, 64, 64, 64, 2, FAKE, FAKE, 64, None) == UNSUP          # only HEAL_W_KN / HEAL_W_F16
+    assert sk(None, 64, 0, 64, 0, None, None, 64, None) == OK
+    assert sk(FAKE, 64, 64, 64, 0, None, FAKE, 64, None) == NULL          # the shifts are required
+    assert sk(FAKE, 63, 64, 64, 0, FAKE, FAKE, 64, None) == STRIDE
+    assert sk(FAKE, 64, 100, 64, heal.HEAL_W_KN, FAKE, FAKE, 100, None) == STRIDE   # [K, rows]: ld >= rows
+    assert sk(FAKE, 64, 64, 64, 0, FAKE, FAKE, 32, None) == STRIDE
+    assert sk(ctypes.c_void_p(0x10002), 64, 64, 64, 0, FAKE, FAKE, 64, None) == ALIGN
+    assert sk(FAKE, 64, 64, 64, heal.HEAL_W_F16, FAKE, ctypes.c_void_p(0x10001), 64, None) == ALIGN
+
+
+def test_kshift_from_absmax():
+    """Host arithmetic: the smallest s >= 0 with absmax * 2^-s < limit."""
+    f = heal.heal_kshift_from_absmax
+    a = np.array([0.0, 1.0, 32767.99, 32768.0, 65535.0, 65536.0, 1e6, 2.0 ** 40, 3e38], np.float32)
+    s = f(a, 32768.0)
+    assert s.dtype == np.int8
+    assert s.tolist() == [0, 0, 0, 1, 1, 2, 5, 26, 113]
+    for ai, si in zip(a.astype(np.float64), s.astype(int)):   # the definition, checked exactly
+        assert ai * 2.0 ** -si < 32768.0 and (si == 0 or ai * 2.0 ** -(si - 1) >= 32768.0)
+    assert f(np.array([1.0, 3.0], np.float32), 1.0).tolist() == [1, 2]
+    L = heal.lib()
+    out = np.full(3, 7, np.int8)
+    P = ctypes.c_void_p
+    for bad in (np.array([1.0, np.nan, 2.0], np.float32), np.array([1.0, np.inf, 2.0], np.float32),
+                np.array([1.0, -1.0, 2.0], np.float32)):
+        assert L.heal_kshift_from_absmax(bad.ctypes.data_as(P), 3, 32768.0, out.ctypes.data_as(P)) == UNSUP
+        assert out.tolist() == [7, 7, 7]      # nothing written on failure
+    good = np.ones(3, np.float32)
+    assert L.heal_kshift_from_absmax(good.ctypes.data_as(P), 3, 0.5, out.ctypes.data_as(P)) == UNSUP
+    assert L.heal_kshift_from_absmax(good.ctypes.data_as(P), 3, 70000.0, out.ctypes.data_as(P)) == UNSUP
+    assert L.heal_kshift_from_absmax(None, 3, 32768.0, out.ctypes.data_as(P)) == NULL
+    assert L.heal_kshift_from_absmax(None, 0, 32768.0, None) == OK
+    assert L.heal_kshift_from_absmax(good.ctypes.data_as(P), -1, 32768.0, out.ctypes.data_as(P)) == SHAPE
 
 
 def test_quant_dequant_validation():
