@@ -401,15 +401,26 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const float* __res
         }
 }
 
-// C[m, n] = sum over chunks s (in order) of P[s, m, n].
+// C[m, n] = sum over chunks s (in order) of P[s, m, n].  The partials of a
+// batch of chunks are loaded together (the clamped index keeps every load in
+// bounds) and then added in chunk order, so the chain of adds waits on one
+// round of loads per batch instead of one per chunk.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, int splits,
                                                             int64_t M, int64_t N, float* __restrict__ C,
                                                             int64_t ldc) {
+    constexpr int BATCH = 8;
     const int64_t total = M * N;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
-        float acc = P[i];
-        for (int s = 1; s < splits; ++s) acc += P[s * total + i];
+        float acc = 0.0f;
+        for (int s0 = 0; s0 < splits; s0 += BATCH) {
+            float v[BATCH];
+#pragma unroll
+            for (int j = 0; j < BATCH; ++j) v[j] = P[(int64_t)min(s0 + j, splits - 1) * total + i];
+#pragma unroll
+            for (int j = 0; j < BATCH; ++j)
+                if (s0 + j < splits) acc = (s0 + j == 0) ? v[j] : acc + v[j];
+        }
         const int64_t m = i / N, n = i - m * N;
         C[m * ldc + n] = acc;
     }
