@@ -9,6 +9,8 @@ workload (inputs resident in HBM before timing starts):
            weights split once beforehand (as deployed: weights are fixed)
   prefill_w16  the same GEMMs with the weights held as binary16 and packed
            once: the two-product form (2 of the 3 MFMA products)
+  prefill_1p  the same GEMMs in the one-product mode (plain FP16, no
+           compensation): the cost the compensation is measured against
   decode   16 compensated GEMMs of a Llama-3-8B-like layer: M = 1, 8, 32, 64
            x (K,N) in {(4096,4096), (4096,1024), (4096,14336), (14336,4096)},
            fp32 weights streamed from HBM (M-outer order, so consecutive calls
@@ -68,7 +70,7 @@ def build_workload(rows_sel):
     W = {}
     t0 = time.time()
 
-    if "split" in rows_sel or "prefill" in rows_sel or "prefill_w16" in rows_sel:
+    if any(r in rows_sel for r in ("split", "prefill", "prefill_w16", "prefill_1p")):
         pre = []
         for i, (K, N) in enumerate(WL.PREFILL_KN):
             A, Wt = WL.prefill_gemm(WL.PREFILL_M, K, N, seed=3000 + i)
@@ -181,6 +183,12 @@ def make_rows(W):
                     heal.heal_gemm_f32c(p["Ap"], p["Wp16"], C=p["C"])
 
             rows.append(("prefill_w16", run_prefill16, useful, "flop"))
+
+        def run_prefill1():
+            for p in pre:
+                heal.heal_gemm_f32c(p["Ap"], p["Wp"], C=p["C"], one_product=True)
+
+        rows.append(("prefill_1p", run_prefill1, useful, "flop"))
     if "decode" in W:
         calls = W["decode"]
 
@@ -252,7 +260,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--rows", default="split,prefill,prefill_w16,decode,decode_w16,decode_kshift,quant,dequant,attn",
+    ap.add_argument("--rows", default="split,prefill,prefill_w16,prefill_1p,decode,decode_w16,decode_kshift,quant,"
+                                      "dequant,attn",
                     help="comma-separated subset of rows to run (profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

@@ -16,7 +16,7 @@ __all__ = [
     "heal_gemm_f32c_workspace", "heal_pack_w", "heal_pack_w_bytes", "heal_qkv_quant_i16",
     "heal_kv_dequant_i16", "heal_attn_decode_i16", "heal_attn_decode_workspace", "PackedOperand",
     "heal_scale_k", "heal_kshift_from_absmax",
-    "PackedWeight", "HEAL_W_NK", "HEAL_W_KN", "HEAL_W_PACKED", "HEAL_A_PACKED", "HEAL_W_F16",
+    "PackedWeight", "HEAL_W_NK", "HEAL_W_KN", "HEAL_W_PACKED", "HEAL_A_PACKED", "HEAL_W_F16", "HEAL_ONE_PRODUCT",
     "HEAL_FLAG_F16_RANGE",
     "HEAL_DQ_F32", "HEAL_DQ_F16X2",
     "LIB_PATH",
@@ -25,7 +25,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libheal.so")
 
 HEAL_OK = 0
-HEAL_W_NK, HEAL_W_KN, HEAL_W_PACKED, HEAL_A_PACKED, HEAL_W_F16 = 0, 1, 2, 4, 8
+HEAL_W_NK, HEAL_W_KN, HEAL_W_PACKED, HEAL_A_PACKED, HEAL_W_F16, HEAL_ONE_PRODUCT = 0, 1, 2, 4, 8, 16
 HEAL_FLAG_F16_RANGE = 1
 HEAL_DQ_F32, HEAL_DQ_F16X2 = 0, 1
 
@@ -199,11 +199,13 @@ def heal_gemm_f32c_workspace(M: int, N: int, K: int, flags: int) -> int:
     return lib().heal_gemm_f32c_workspace(M, N, K, flags)
 
 
-def heal_gemm_f32c(A, W, w_layout: str = "nk", C=None, workspace=None, dev_status=None, a_kshift=None):
+def heal_gemm_f32c(A, W, w_layout: str = "nk", C=None, workspace=None, dev_status=None, a_kshift=None,
+                   one_product: bool = False):
     """C = A . B with B = W^T ('nk', W [N,K]) or B = W ('kn', W [K,N]).
     A and/or W may be PackedOperand buffers from heal_pack_w.  a_kshift (int8
     [K], optional): A's element (m, k) is multiplied by 2^-a_kshift[k] before
-    its split; W must hold reduction index k multiplied by 2^+a_kshift[k]."""
+    its split; W must hold reduction index k multiplied by 2^+a_kshift[k].
+    one_product: plain FP16, C = A_hi.B_hi (no compensation)."""
     aflags = 0
     if isinstance(A, PackedOperand):
         M, K, lda, aptr, adev, aflags = A.rows, A.K, 0, _ptr(A.buf), A.buf.device, HEAL_A_PACKED
@@ -227,7 +229,7 @@ def heal_gemm_f32c(A, W, w_layout: str = "nk", C=None, workspace=None, dev_statu
         if K2 != K:
             raise ValueError("inner dimensions differ")
         wptr, ldw = _ptr(W), _rowmajor_ld(W, "W")
-    flags |= aflags
+    flags |= aflags | (HEAL_ONE_PRODUCT if one_product else 0)
     if C is None:
         C = torch.empty((M, N), dtype=torch.float32, device=adev)
     ldc = _rowmajor_ld(C, "C") if M > 0 and N > 0 else N

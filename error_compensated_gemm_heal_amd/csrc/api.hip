@@ -103,7 +103,8 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
                            void* workspace, size_t workspace_bytes, uint32_t* dev_status,
                            void* stream) {
     if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return HEAL_ERR_SHAPE;
-    if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_PACKED | HEAL_A_PACKED | HEAL_W_F16)) return HEAL_ERR_UNSUPPORTED;
+    if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_PACKED | HEAL_A_PACKED | HEAL_W_F16 | HEAL_ONE_PRODUCT))
+        return HEAL_ERR_UNSUPPORTED;
     if ((flags & HEAL_A_PACKED) && a_kshift) return HEAL_ERR_UNSUPPORTED;   // a packed A carries its shifts
     if (M == 0 || N == 0) return HEAL_OK;
     if (!C) return HEAL_ERR_NULL;
@@ -119,6 +120,7 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
     const bool a_packed = flags & HEAL_A_PACKED;
     const bool kn = flags & HEAL_W_KN;
     const bool wf16 = flags & HEAL_W_F16;
+    const bool one = flags & HEAL_ONE_PRODUCT;
     if (!a_packed && lda < K) return HEAL_ERR_STRIDE;
     if (!packed && ldw < (kn ? N : K)) return HEAL_ERR_STRIDE;
     if (misaligned(A, a_packed ? 256 : 4) || misaligned(W, packed ? 256 : (wf16 ? 2 : 4)) || misaligned(C, 4) ||
@@ -135,7 +137,7 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
         const DecodePlan p = decode_plan(M, N, K);
         unsigned char* ws = static_cast<unsigned char*>(workspace);
         return hip_status(
-            launch_gemm_decode(A, lda, a_kshift, W, wf16, ldw, C, ldc, M, N, K, ws, p, dev_status, s));
+            launch_gemm_decode(A, lda, a_kshift, W, wf16, one, ldw, C, ldc, M, N, K, ws, p, dev_status, s));
     }
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     const void* apk = A;
@@ -153,7 +155,7 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
         if (e != hipSuccess) return HEAL_ERR_HIP;
         bpk = wpk;
     }
-    return hip_status(launch_gemm_prefill(apk, bpk, wf16, C, ldc, M, N, K, s));
+    return hip_status(launch_gemm_prefill(apk, bpk, one ? 1 : (wf16 ? 2 : 3), C, ldc, M, N, K, s));
 }
 
 heal_status heal_scale_k(const void* X, int64_t ldx, int64_t rows, int64_t K, uint32_t flags,

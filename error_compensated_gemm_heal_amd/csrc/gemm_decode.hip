@@ -135,8 +135,8 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // AVEC: A rows 16-byte aligned, activation units load as one 16-byte load.
 // MT == 1 stages A itself (A, lda); MT > 1 copies the pre-split blocks (Ablk).
 // SHIFT (MT == 1): element (m, k) of A is multiplied by 2^-kshift[k] before
-// its split.
-template <int MT, bool VEC, bool WF16, bool AVEC, bool SHIFT>
+// its split.  ONE: plain FP16, the A_hi.W_hi product alone.
+template <int MT, bool VEC, bool WF16, bool AVEC, bool SHIFT, bool ONE>
 __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const float* __restrict__ A, int64_t lda,
                                                           const unsigned char* __restrict__ Ablk,
                                                           int a_total_bytes, const void* __restrict__ W,
@@ -350,8 +350,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const float* __res
                     const half8 ah = *reinterpret_cast<const half8*>(abuf + off);
                     const half8 al = *reinterpret_cast<const half8*>(abuf + BB / 2 + off);
                     mfma16(ah, wh, acc_hh[t]);
-                    if constexpr (!WF16) mfma16(ah, wl, acc_c[t]);
-                    mfma16(al, wh, acc_c[t]);
+                    if constexpr (!WF16 && !ONE) mfma16(ah, wl, acc_c[t]);
+                    if constexpr (!ONE) mfma16(al, wh, acc_c[t]);
                 }
             }
         }
@@ -448,7 +448,7 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift, const void* W, bool wf16,
-                              int64_t ldw, float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                              bool one, int64_t ldw, float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                               void* workspace, const DecodePlan& plan, uint32_t* status, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
     if (M > 64 || K == 0) return hipErrorInvalidValue;
@@ -466,10 +466,15 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
     const bool vec = (reinterpret_cast<uintptr_t>(W) & walign) == 0 && (ldw & 3) == 0 && (K & 31) == 0;
     // activation units load as float4 when rows are 16-byte aligned
     const bool avec = (reinterpret_cast<uintptr_t>(A) & 15) == 0 && (lda & 3) == 0;
-#define HEAL_DEC_MAIN(MT_, VEC_, F16_, AV_, SH_)                                                        \
-    hipLaunchKernelGGL((gemm_decode_kernel<MT_, VEC_, F16_, AV_, SH_>), grid, dim3(64 * NW),             \
+#define HEAL_DEC_LAUNCH(MT_, VEC_, F16_, AV_, SH_, ONE_)                                                \
+    hipLaunchKernelGGL((gemm_decode_kernel<MT_, VEC_, F16_, AV_, SH_, ONE_>), grid, dim3(64 * NW),       \
                        2 * block_bytes<MT_>(), s, A, lda, ablk, (int)plan.a_bytes, W, ldw, out, ldo, stride, \
                        (int)M, (int)N, (int)K, (int)plan.kchunk, kshift, status)
+#define HEAL_DEC_MAIN(MT_, VEC_, F16_, AV_, SH_)                                                        \
+    do {                                                                                                \
+        if (one) HEAL_DEC_LAUNCH(MT_, VEC_, F16_, AV_, SH_, true);                                      \
+        else HEAL_DEC_LAUNCH(MT_, VEC_, F16_, AV_, SH_, false);                                         \
+    } while (0)
 #define HEAL_DEC_AV(MT_, VEC_, F16_, SH_)                                                               \
     do {                                                                                                \
         if (avec) HEAL_DEC_MAIN(MT_, VEC_, F16_, true, SH_);                                            \
@@ -502,6 +507,7 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
 #undef HEAL_DEC
 #undef HEAL_DEC_AV
 #undef HEAL_DEC_MAIN
+#undef HEAL_DEC_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
     const int64_t total = M * N;

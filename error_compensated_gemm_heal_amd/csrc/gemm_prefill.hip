@@ -33,7 +33,8 @@
 //    rows hit distinct banks with no padding;
 //  * with a 16-bit weight (binary16 values, packed with zero lo planes) the
 //    B_lo fragments are not read and the A_hi.B_lo product is skipped: the
-//    paper's own two-product form, 2/3 of the MFMAs;
+//    paper's own two-product form, 2/3 of the MFMAs; the one-product mode
+//    (plain FP16, no compensation) keeps A_hi.B_hi alone;
 //  * when the grid would fill at most half the chip, the k range is split in
 //    two and both halves add into a zeroed C with fp32 atomics; two addends
 //    commute exactly, so the result does not depend on their order;
@@ -69,8 +70,10 @@ __device__ __forceinline__ half8 scale_m10(const half8& x) {
     return x * (_Float16)0.0009765625f;
 }
 
-// TWO: B is a 16-bit weight (zero lo planes): two products instead of three.
-template <bool SPLIT, bool TWO>
+// NP: products per k step.  3: A_hi.B_hi + 2^-10 (A_hi.B_lo + A_lo.B_hi);
+// 2: B is a 16-bit weight (zero lo planes), A_hi.B + 2^-10 A_lo.B;
+// 1: plain FP16, A_hi.B_hi.
+template <bool SPLIT, int NP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned char* __restrict__ Bpk,
                          float* __restrict__ C, int64_t ldc, int M, int N, int Kp,
@@ -146,11 +149,12 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     do {                                                                                                 \
         _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                                 \
             ah_[i] = *reinterpret_cast<const half8*>(base + a_row + i * 32 * ROWB + slot_off[ks_][0]);   \
-            al_[i] = *reinterpret_cast<const half8*>(base + a_row + i * 32 * ROWB + slot_off[ks_][1]);   \
+            if constexpr (NP >= 2)                                                                       \
+                al_[i] = *reinterpret_cast<const half8*>(base + a_row + i * 32 * ROWB + slot_off[ks_][1]); \
         }                                                                                                \
         _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                                 \
             bh_[j] = *reinterpret_cast<const half8*>(base + b_row + j * 32 * ROWB + slot_off[ks_][0]);   \
-            if constexpr (!TWO)                                                                          \
+            if constexpr (NP == 3)                                                                       \
                 bl_[j] = *reinterpret_cast<const half8*>(base + b_row + j * 32 * ROWB + slot_off[ks_][1]); \
         }                                                                                                \
     } while (0)
@@ -161,14 +165,16 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
         _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                   \
             _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32(ah_[i], bh_[j], acc[i][j]);            \
         half8 as_[TM];                                                                                   \
-        if constexpr (!TWO) {                                                                            \
+        if constexpr (NP == 3) {                                                                         \
             _Pragma("unroll") for (int i = 0; i < TM; ++i) as_[i] = scale_m10(ah_[i]);                   \
             _Pragma("unroll") for (int i = 0; i < TM; ++i)                                               \
                 _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32(as_[i], bl_[j], acc[i][j]);        \
         }                                                                                                \
-        _Pragma("unroll") for (int i = 0; i < TM; ++i) as_[i] = scale_m10(al_[i]);                       \
-        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                   \
-            _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32(as_[i], bh_[j], acc[i][j]);            \
+        if constexpr (NP >= 2) {                                                                         \
+            _Pragma("unroll") for (int i = 0; i < TM; ++i) as_[i] = scale_m10(al_[i]);                   \
+            _Pragma("unroll") for (int i = 0; i < TM; ++i)                                               \
+                _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32(as_[i], bh_[j], acc[i][j]);        \
+        }                                                                                                \
     } while (0)
 
     // Pipeline, one barrier per k tile placed mid-tile:
@@ -199,7 +205,7 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
             HEAL_MFMAS(ah0, al0, bh0, bl0);
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, TWO ? 2 : 3, 0);   // MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x008, NP, 0);            // MFMAs
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // one LDS read
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -218,7 +224,7 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
             HEAL_MFMAS(ah1, al1, bh1, bl1);
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, TWO ? 2 : 3, 0);   // MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x008, NP, 0);            // MFMAs
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // one LDS read
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);             // one DMA load
             }
@@ -265,8 +271,9 @@ __global__ void zero_c_kernel(float* C, int64_t ldc, int64_t M, int64_t N) {
 
 }  // namespace
 
-hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, bool b16, float* C, int64_t ldc, int64_t M,
+hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, float* C, int64_t ldc, int64_t M,
                                int64_t N, int64_t K, hipStream_t s) {
+    if (nprod < 1 || nprod > 3) return hipErrorInvalidValue;
     if (M == 0 || N == 0) return hipSuccess;
     const int64_t Kp = pack_kp(K);
     if (Kp == 0) return hipErrorInvalidValue;  // K == 0 is handled by the caller
@@ -278,10 +285,12 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, bool b16, float
     const bool split = (int64_t)tiles_m * tiles_n <= 128 && Kp / BK >= 8;
     static bool attr_set = false;  // idempotent; racing first calls set the same value
     if (!attr_set) {
-        const void* fns[4] = {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, false>),
-                              reinterpret_cast<const void*>(&gemm_prefill_kernel<true, false>),
-                              reinterpret_cast<const void*>(&gemm_prefill_kernel<false, true>),
-                              reinterpret_cast<const void*>(&gemm_prefill_kernel<true, true>)};
+        const void* fns[6] = {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3>),
+                              reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 3>),
+                              reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2>),
+                              reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 2>),
+                              reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1>),
+                              reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1>)};
         for (const void* f : fns) {
             hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * STAGE);
             if (e != hipSuccess) return e;
@@ -295,16 +304,18 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, bool b16, float
         hipLaunchKernelGGL(zero_c_kernel, dim3(zb), dim3(256), 0, s, C, ldc, M, N);
     }
     const dim3 grid((unsigned)(tiles_m * tiles_n * (split ? 2 : 1)));
-#define HEAL_PREFILL(SPLIT_, TWO_)                                                                    \
-    hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, TWO_>), grid, dim3(256), NSTAGE * STAGE, s, a, b, C, ldc, \
+#define HEAL_PREFILL(SPLIT_, NP_)                                                                     \
+    hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, NP_>), grid, dim3(256), NSTAGE * STAGE, s, a, b, C, ldc, \
                        (int)M, (int)N, (int)Kp, tiles_m, tiles_n)
-    if (split) {
-        if (b16) HEAL_PREFILL(true, true);
-        else HEAL_PREFILL(true, false);
-    } else {
-        if (b16) HEAL_PREFILL(false, true);
-        else HEAL_PREFILL(false, false);
-    }
+#define HEAL_PREFILL_NP(SPLIT_)                                                                       \
+    do {                                                                                              \
+        if (nprod == 3) HEAL_PREFILL(SPLIT_, 3);                                                      \
+        else if (nprod == 2) HEAL_PREFILL(SPLIT_, 2);                                                 \
+        else HEAL_PREFILL(SPLIT_, 1);                                                                 \
+    } while (0)
+    if (split) HEAL_PREFILL_NP(true);
+    else HEAL_PREFILL_NP(false);
+#undef HEAL_PREFILL_NP
 #undef HEAL_PREFILL
     return hipGetLastError();
 }

@@ -76,9 +76,10 @@ hipError_t launch_dequant(const int16_t* codes, int64_t rows, int64_t D, int64_t
                           const float* scales, int fmt, void* out, void* out_lo, int64_t ldo,
                           hipStream_t s);
 
-// C[M,N] from packed A (rows M) and packed B (rows N); b16: B was packed from
-// binary16 values (zero lo planes), so the A_hi.B_lo product is skipped.
-hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, bool b16, float* C, int64_t ldc, int64_t M,
+// C[M,N] from packed A (rows M) and packed B (rows N) with nprod products
+// per k step: 3 (both fp32), 2 (B packed from binary16 values, zero lo
+// planes: A_hi.B_lo skipped), 1 (plain FP16: A_hi.B_hi alone).
+hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, float* C, int64_t ldc, int64_t M,
                                int64_t N, int64_t K, hipStream_t s);
 
 // Decode path (M <= 64): fp32 W [N,K] streamed and split in registers.
@@ -91,10 +92,11 @@ struct DecodePlan {
     int64_t p_bytes;   // workspace bytes of the split-K partials
 };
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K);
-// W is fp32, or binary16 values when wf16 (the two-product form).  kshift
-// (nullable): A's element (m, k) is multiplied by 2^-kshift[k] before its split.
+// W is fp32, or binary16 values when wf16 (the two-product form); one: plain
+// FP16 (A_hi.W_hi alone).  kshift (nullable): A's element (m, k) is
+// multiplied by 2^-kshift[k] before its split.
 hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift, const void* W, bool wf16,
-                              int64_t ldw, float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                              bool one, int64_t ldw, float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                               void* workspace, const DecodePlan& plan, uint32_t* status, hipStream_t s);
 
 int64_t attn_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D);

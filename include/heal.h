@@ -57,7 +57,8 @@ enum {
     HEAL_W_KN = 1u,     /* W is fp32 [K, N] (B = W)                                     */
     HEAL_W_PACKED = 2u, /* W is a buffer written by heal_pack_w (ldw and layout ignored) */
     HEAL_A_PACKED = 4u, /* A is a buffer written by heal_pack_w for A's M rows (lda ignored) */
-    HEAL_W_F16 = 8u     /* W holds binary16 values (2 bytes each), layout per HEAL_W_KN   */
+    HEAL_W_F16 = 8u,    /* W holds binary16 values (2 bytes each), layout per HEAL_W_KN   */
+    HEAL_ONE_PRODUCT = 16u /* plain FP16: C = A_hi.B_hi only (heal_gemm_f32c)             */
 };
 
 /* Bits of the optional device status word. */
@@ -110,7 +111,11 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  * exactly), B_lo is zero and two products remain,
  *   C = A_hi.B + 2^-10 A_lo.B,
  * the paper's own form (section 3, "Mitigating GEMM Truncation via FP16
- * Promotion and Algebraic Compensation"), reading 2 bytes per weight.  Accuracy: normwise error max_ij |C - C_exact| / (|a_i| |b_j|)
+ * Promotion and Algebraic Compensation"), reading 2 bytes per weight.
+ * HEAL_ONE_PRODUCT keeps the first product alone, C = A_hi.B_hi: plain FP16
+ * with fp32 accumulation, for layers run without compensation (the paper's
+ * HEAL++ upcasts only selected layers; the per-layer choice is the
+ * caller's).  Its error is that of FP16 operands, not the bar below.  Accuracy: normwise error max_ij |C - C_exact| / (|a_i| |b_j|)
  * within 2x that of a naive FP32 GEMM and below 1e-5.  The summation order
  * depends on (M, N, K) but not on the data.  For M <= 64 (NK layout, K <
  * 2^23, neither operand packed) it also does not depend on M, so
@@ -128,7 +133,8 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  *          | HEAL_W_PACKED (both: W is a buffer that heal_pack_w packed with
  *          HEAL_W_F16, whose lo planes are zero, and the A_hi.B_lo product
  *          is skipped; a buffer packed from fp32 values must not carry
- *          HEAL_W_F16, or its lo planes are ignored), and/or | HEAL_A_PACKED
+ *          HEAL_W_F16, or its lo planes are ignored), and/or | HEAL_A_PACKED,
+ *          and/or | HEAL_ONE_PRODUCT
  *          (A then is heal_pack_w(A, lda, M, K, HEAL_W_NK)'s buffer: an
  *          activation split once can feed several GEMMs)
  *   a_kshift  device int8 [K], nullable.  Per-channel power-of-two

@@ -152,6 +152,22 @@ def gemm_f32_naive_rows(A, W, rows, w_layout="nk"):
     return C
 
 
+def round_f16(x):
+    """Operands rounded to binary16 (the oracle's own conversion), held exactly in float32."""
+    return f16_bits_to_f64(f32_to_f16_bits(x)).astype(np.float32)
+
+
+def gemm_f16_plain_rows(A, W, rows, w_layout="nk"):
+    """Plain FP16 GEMM (one product): rows of fp16(A) . fp16(B) in binary64.
+    HEAL paper, section 3, "Mitigating GEMM Truncation via FP16 Promotion and
+    Algebraic Compensation": the single FP16 product that the compensation
+    extends.  Products of binary16 values are exact, so this is the exact
+    result of that product; a GPU run differs from it by its fp32 accumulation
+    only.  Returns (C64 rows, naive-fp32 rows of the same rounded operands)."""
+    Ah, Wh = round_f16(A), round_f16(W)
+    return gemm_f64_rows(Ah, Wh, rows, w_layout), gemm_f32_naive_rows(Ah, Wh, rows, w_layout)
+
+
 # --- INT16 quant / dequant ----------------------------------------------------
 
 def quant_i16(X):

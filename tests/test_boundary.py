@@ -64,6 +64,7 @@ def test_gemm_validation():
     assert _gemm(K=1 << 31) == SHAPE
     assert _gemm(flags=heal.HEAL_W_F16 | heal.HEAL_W_PACKED, W=ctypes.c_void_p(0x10010)) == ALIGN  # packed: 256 B
     assert _gemm(flags=32) == UNSUP
+    assert _gemm(flags=heal.HEAL_ONE_PRODUCT, C=None) == NULL          # a valid flag: validation goes on
     assert _gemm(M=0, A=None, W=None, C=None) == OK
     assert _gemm(N=0, A=None, W=None, C=None) == OK
     assert _gemm(C=None) == NULL
@@ -79,7 +80,6 @@ def test_gemm_validation():
     assert _gemm(flags=heal.HEAL_W_F16, W=ctypes.c_void_p(0x10001)) == ALIGN   # fp16 W: 2-byte aligned
     assert _gemm(flags=heal.HEAL_W_PACKED, W=ctypes.c_void_p(0x10010)) == ALIGN
     assert _gemm(flags=heal.HEAL_A_PACKED, A=ctypes.c_void_p(0x10010)) == ALIGN
-    assert _gemm(flags=16) == UNSUP
     assert _gemm(flags=heal.HEAL_A_PACKED, A=ctypes.c_void_p(0x10100), ks=FAKE) == UNSUP   # packed A: shift at pack time
     assert heal.heal_gemm_f32c_workspace(8, 4096, 4096, 0) > 0     # split-K partials
     assert _gemm(ws=None) == WS

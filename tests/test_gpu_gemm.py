@@ -258,3 +258,51 @@ def test_gemm_f16_weight_prefill_two_products(M, N, K):
     e_naive = gemm_normwise_error(C32, C64, A, W32, rows=rows)
     print(f"  e_gpu={e_gpu:.3e} e_naive={e_naive:.3e}", flush=True)
     assert e_gpu <= gemm_tolerance(e_naive, K)
+
+
+# ---- one-product mode (plain FP16, HEAL_ONE_PRODUCT) -----------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(1, 384, 1024), (17, 300, 700), (64, 130, 4096), (300, 260, 1000),
+                                   (2048, 1024, 512)])
+@pytest.mark.parametrize("layout", ["nk", "kn"])
+def test_gemm_one_product_against_plain_f16_oracle(M, N, K, layout):
+    """Decode and prefill grids: the one-product result against the oracle's exact
+    product of the fp16-rounded operands, to the fp32-accumulation bar on those
+    operands; and bit-equal to the three-product kernels when the operands are
+    binary16 (their correction products are exact zeros)."""
+    print(f"gemm one product M={M} N={N} K={K} {layout}", flush=True)
+    A, W = WL.decode_gemm(M, K, N, seed=5300 + M + N + K)
+    if layout == "kn":
+        W = np.ascontiguousarray(W.T)
+    Ad, Wd = torch.from_numpy(A).to(DEV), torch.from_numpy(W).to(DEV)
+    C = heal.heal_gemm_f32c(Ad, Wd, w_layout=layout, one_product=True).cpu().numpy()
+    rows = np.arange(M) if M <= 64 else np.sort(WL.rng(M + K).choice(M, size=24, replace=False))
+    C64, C32 = oracle.gemm_f16_plain_rows(A, W, rows, layout)
+    Ah, Wh = oracle.round_f16(A), oracle.round_f16(W)
+    e_gpu = gemm_normwise_error(C[rows], C64, Ah, Wh, layout, rows)
+    e_naive = gemm_normwise_error(C32, C64, Ah, Wh, layout, rows)
+    print(f"  e_gpu={e_gpu:.3e} e_naive={e_naive:.3e}", flush=True)
+    assert e_gpu <= gemm_tolerance(e_naive, K)
+    # binary16 operands: the compensation adds zeros, so one product gives the same bits
+    c1 = heal.heal_gemm_f32c(torch.from_numpy(Ah).to(DEV), torch.from_numpy(Wh).to(DEV), w_layout=layout,
+                             one_product=True).cpu().numpy()
+    c3 = heal.heal_gemm_f32c(torch.from_numpy(Ah).to(DEV), torch.from_numpy(Wh).to(DEV),
+                             w_layout=layout).cpu().numpy()
+    assert np.array_equal(c1, c3)
+
+
+def test_gemm_one_product_fp16_and_packed_weight():
+    """With an fp16 weight (packed or not) the one-product mode is the plain FP16 GEMM too."""
+    M, N, K = 200, 256, 768
+    A, W = WL.decode_gemm(M, K, N, seed=5400)
+    W16d = torch.from_numpy(W.astype(np.float16)).to(DEV)
+    Ad = torch.from_numpy(A).to(DEV)
+    c = heal.heal_gemm_f32c(Ad, W16d, one_product=True).cpu().numpy()
+    cp = heal.heal_gemm_f32c(Ad, heal.heal_pack_w(W16d), one_product=True).cpu().numpy()
+    assert np.array_equal(c, cp)
+    rows = np.arange(0, M, 9)
+    C64, C32 = oracle.gemm_f16_plain_rows(A, W.astype(np.float16).astype(np.float32), rows)
+    Ah, Wh = oracle.round_f16(A), W.astype(np.float16).astype(np.float32)
+    e_gpu = gemm_normwise_error(c[rows], C64, Ah, Wh, rows=rows)
+    e_naive = gemm_normwise_error(C32, C64, Ah, Wh, rows=rows)
+    assert e_gpu <= gemm_tolerance(e_naive, K)

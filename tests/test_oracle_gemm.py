@@ -115,3 +115,29 @@ def test_comp_model_exact_on_binary16_operands_and_bounded_otherwise():
     absum = np.abs(A).astype(np.float64) @ np.abs(W).astype(np.float64).T
     # each operand carries relative error <= 2^-22 (+ 2^-35 absolute): products <= ~2^-21
     assert np.all(err <= (2.0 ** -21 + 1e-12) * absum + 300 * 2.0 ** -35)
+
+
+def test_plain_f16_gemm_rounds_operands_then_multiplies_exactly():
+    """One-product (plain FP16) reference: on binary16 operands it is the binary64
+    product itself; on other operands it equals the binary64 product of the operands
+    rounded by numpy's float16 cast (an independent round-to-nearest-even
+    conversion), and it differs from the unrounded product by at most the operand
+    rounding (relative 2^-11 per operand)."""
+    g = np.random.Generator(np.random.PCG64(13))
+    A = (g.integers(-64, 65, size=(8, 96)) / 16.0).astype(np.float32)
+    W = (g.integers(-64, 65, size=(12, 96)) / 64.0).astype(np.float32)
+    rows = np.arange(8)
+    c64, c32 = oracle.gemm_f16_plain_rows(A, W, rows)
+    assert np.array_equal(c64, oracle.gemm_f64(A, W))
+    A = g.standard_normal((6, 200)).astype(np.float32)
+    W = (0.02 * g.standard_normal((10, 200))).astype(np.float32)
+    rows = np.arange(6)
+    c64, c32 = oracle.gemm_f16_plain_rows(A, W, rows)
+    ref = A.astype(np.float16).astype(np.float64) @ W.astype(np.float16).astype(np.float64).T
+    assert np.allclose(c64, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+    absum = np.abs(A).astype(np.float64) @ np.abs(W).astype(np.float64).T
+    assert np.all(np.abs(c64 - oracle.gemm_f64(A, W)) <= (2 * 2.0 ** -11 + 2.0 ** -22) * absum + 1e-9)
+    assert c32.dtype == np.float32 and np.all(np.abs(c32 - c64) <= 1e-4 * absum + 1e-9)
+    for layout in ("nk", "kn"):
+        Wl = W if layout == "nk" else np.ascontiguousarray(W.T)
+        assert np.array_equal(oracle.gemm_f16_plain_rows(A, Wl, rows, layout)[0], c64)
