@@ -40,7 +40,7 @@ SIGNATURES = {
     "heal_pack_w": ([_P, _I64, _I64, _I64, _U32, _P, _P, _SZ, _P, _P], _INT),
     "heal_scale_k": ([_P, _I64, _I64, _I64, _U32, _P, _P, _I64, _P], _INT),
     "heal_kshift_from_absmax": ([_P, _I64, ctypes.c_float, _P], _INT),
-    "heal_pack_w_bytes": ([_I64, _I64], _SZ),
+    "heal_pack_w_bytes": ([_I64, _I64, _U32], _SZ),
     "heal_qkv_quant_i16": ([_P, _I64, _I64, _I64, _P, _I64, _P, _P], _INT),
     "heal_kv_dequant_i16": ([_P, _I64, _I64, _I64, _P, _INT, _P, _P, _I64, _P], _INT),
     "heal_attn_decode_i16": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _SZ, _P], _INT),
@@ -148,8 +148,8 @@ class PackedOperand:
 PackedWeight = PackedOperand
 
 
-def heal_pack_w_bytes(N: int, K: int) -> int:
-    return lib().heal_pack_w_bytes(N, K)
+def heal_pack_w_bytes(N: int, K: int, flags: int = 0) -> int:
+    return lib().heal_pack_w_bytes(N, K, flags)
 
 
 def _weight_dtype_flag(W: torch.Tensor) -> int:
@@ -182,7 +182,7 @@ def heal_pack_w(W: torch.Tensor, w_layout: str = "nk", dev_status=None, out=None
     else:
         N, K = W.shape
     ldw = _rowmajor_ld(W, "W")
-    nbytes = heal_pack_w_bytes(N, K)
+    nbytes = heal_pack_w_bytes(N, K, flags)
     if out is None:
         buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=W.device)
     else:

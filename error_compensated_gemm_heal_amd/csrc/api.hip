@@ -66,9 +66,9 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
     return hip_status(launch_split(X, n, hi, lo, dev_status, static_cast<hipStream_t>(stream)));
 }
 
-size_t heal_pack_w_bytes(int64_t N, int64_t K) {
+size_t heal_pack_w_bytes(int64_t N, int64_t K, uint32_t flags) {
     if (N <= 0 || K <= 0 || N >= kMaxDim || K >= kMaxDim) return 0;
-    return (size_t)pack_bytes(N, K);
+    return (size_t)((flags & HEAL_W_F16) ? pack_bytes_hi(N, K) : pack_bytes(N, K));
 }
 
 heal_status heal_pack_w(const void* W, int64_t ldw, int64_t N, int64_t K, uint32_t flags,
@@ -82,7 +82,7 @@ heal_status heal_pack_w(const void* W, int64_t ldw, int64_t N, int64_t K, uint32
     const bool f16 = flags & HEAL_W_F16;
     if (ldw < (kn ? N : K)) return HEAL_ERR_STRIDE;
     if (misaligned(W, f16 ? 2 : 4) || misaligned(packed, 256) || misaligned(dev_status, 4)) return HEAL_ERR_ALIGN;
-    if (packed_bytes < (size_t)pack_bytes(N, K)) return HEAL_ERR_WORKSPACE;
+    if (packed_bytes < heal_pack_w_bytes(N, K, flags)) return HEAL_ERR_WORKSPACE;
     return hip_status(launch_pack(W, f16, ldw, N, K, kn ? 1 : 0, kshift, packed, dev_status,
                                   static_cast<hipStream_t>(stream)));
 }
@@ -94,7 +94,7 @@ size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags)
         return (size_t)(round256(p.a_bytes) + round256(p.p_bytes));
     }
     int64_t b = (flags & HEAL_A_PACKED) ? 0 : round256(pack_bytes(M, K));
-    if (!(flags & HEAL_W_PACKED)) b += round256(pack_bytes(N, K));
+    if (!(flags & HEAL_W_PACKED)) b += round256((flags & HEAL_W_F16) ? pack_bytes_hi(N, K) : pack_bytes(N, K));
     return (size_t)b;
 }
 
@@ -155,7 +155,7 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
         if (e != hipSuccess) return HEAL_ERR_HIP;
         bpk = wpk;
     }
-    return hip_status(launch_gemm_prefill(apk, bpk, one ? 1 : (wf16 ? 2 : 3), C, ldc, M, N, K, s));
+    return hip_status(launch_gemm_prefill(apk, bpk, one ? 1 : (wf16 ? 2 : 3), wf16, C, ldc, M, N, K, s));
 }
 
 heal_status heal_scale_k(const void* X, int64_t ldx, int64_t rows, int64_t K, uint32_t flags,

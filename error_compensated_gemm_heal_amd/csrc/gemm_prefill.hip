@@ -41,6 +41,8 @@
 //  * block -> tile order keeps the blocks that share a B tile on one XCD
 //    (blocks are dealt to the 8 XCDs round-robin), so B is read from HBM once
 //    and re-served from that XCD's L2.
+#include <utility>
+
 #include "heal_internal.h"
 
 namespace heal {
@@ -52,11 +54,16 @@ constexpr int WM = 128, WN = 128;           // wave tile
 constexpr int TM = WM / 32, TN = WN / 32;   // 32x32 MFMA tiles per wave
 constexpr int ROWB = 128;                   // LDS bytes per row: 32 hi + 32 lo fp16 (swizzled)
 constexpr int A_REGION = BM * ROWB;         // 32 KB
-constexpr int B_REGION = BN * ROWB;         // 32 KB
-constexpr int STAGE = A_REGION + B_REGION;  // 64 KB
 constexpr int NSTAGE = 2;
 constexpr int A_DMA = BM / 8 / 4;           // 1 KB (8-row) DMA blocks per wave per tile (A)
-constexpr int B_DMA = BN / 8 / 4;           // (B)
+// B in LDS: 128-byte rows (hi | lo), or 64-byte rows when B is in the hi-only
+// form of a 16-bit weight (then 16 rows per 1 KB DMA block)
+constexpr int b_rowb(bool bhi) { return bhi ? 64 : ROWB; }
+constexpr int stage_bytes(bool bhi) { return A_REGION + BN * b_rowb(bhi); }   // 64 KB or 48 KB
+
+// s_waitcnt immediate: at most n vector memory operations outstanding
+// (vmcnt in bits 3:0 and 15:14); expcnt and lgkmcnt not waited on.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -72,13 +79,17 @@ __device__ __forceinline__ half8 scale_m10(const half8& x) {
 
 // NP: products per k step.  3: A_hi.B_hi + 2^-10 (A_hi.B_lo + A_lo.B_hi);
 // 2: B is a 16-bit weight (zero lo planes), A_hi.B + 2^-10 A_lo.B;
-// 1: plain FP16, A_hi.B_hi.
-template <bool SPLIT, int NP>
+// 1: plain FP16, A_hi.B_hi.  BHI: B is in the hi-only packed form.
+template <bool SPLIT, int NP, bool BHI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned char* __restrict__ Bpk,
                          float* __restrict__ C, int64_t ldc, int M, int N, int Kp,
                          int tiles_m, int tiles_n) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    static_assert(!BHI || NP < 3, "a hi-only B has no lo planes");
+    constexpr int STAGE = stage_bytes(BHI);
+    constexpr int BROWB = b_rowb(BHI);
+    constexpr int B_DMA = BN * BROWB / 1024 / 4;   // 1 KB DMA blocks per wave per tile (B)
 
     // ---- XCD-aware tile order (tm fastest, then tn, then the k half) -------
     const int nblk = tiles_m * tiles_n * (SPLIT ? 2 : 1);
@@ -94,6 +105,7 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     const uint32_t rowbytes = (uint32_t)Kp * 4u;   // Kp hi + Kp lo fp16
+    const uint32_t browbytes = BHI ? (uint32_t)Kp * 2u : rowbytes;
     const int nkt_all = Kp / BK;
     const int kt_begin = SPLIT ? half_k * (nkt_all / 2) : 0;
     const int kt_end = SPLIT ? (half_k ? nkt_all : nkt_all / 2) : nkt_all;
@@ -106,8 +118,14 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     const int drow = lane >> 3;
     const int dsw = ((wave & 1) << 2) | (drow >> 1);
     const uint32_t dma_voff = (uint32_t)drow * rowbytes + (uint32_t)((lane & 7) ^ dsw) * 16u;
+    // hi-only B: lane L writes row L/4, slot L%4 of a 16-row block, holding
+    // chunk (L%4) ^ ((row / 4) % 4); 16 rows per block keep that lane-only
+    const int drow_b = BHI ? lane >> 2 : drow;
+    const uint32_t dma_voff_b =
+        BHI ? (uint32_t)drow_b * browbytes + (uint32_t)((lane & 3) ^ ((drow_b >> 2) & 3)) * 16u : dma_voff;
+    constexpr int B_ROWS_PER_DMA = 1024 / BROWB;
     const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(Apk + (int64_t)tm * BM * rowbytes, BM * rowbytes);
-    const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(Bpk + (int64_t)tn * BN * rowbytes, BN * rowbytes);
+    const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(Bpk + (int64_t)tn * BN * browbytes, BN * browbytes);
 
 #define HEAL_DMA_TILE(kt_, stage_)                                                                    \
     do {                                                                                              \
@@ -121,7 +139,9 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
         _Pragma("unroll") for (int i = 0; i < B_DMA; ++i) {                                           \
             const int b_ = wave + 4 * i;                                                              \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, (lds_ptr)(st_ + A_REGION + b_ * 1024), 16, \
-                                                     dma_voff, (uint32_t)(8 * b_) * rowbytes + koff_, 0, 0); \
+                                                     dma_voff_b,                                      \
+                                                     (uint32_t)(B_ROWS_PER_DMA * b_) * browbytes +    \
+                                                         (uint32_t)(kt_) * (BROWB == ROWB ? 128u : 64u), 0, 0); \
         }                                                                                             \
     } while (0)
 
@@ -129,12 +149,15 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     //      2 ks + l / 32 (hi) or 4 + 2 ks + l / 32 (lo), at its swizzled slot
     const int sw = (lane >> 1) & 7;
     const int a_row = (wm * WM + (lane & 31)) * ROWB;
-    const int b_row = A_REGION + (wn * WN + (lane & 31)) * ROWB;
+    const int b_row = A_REGION + (wn * WN + (lane & 31)) * BROWB;
     int slot_off[2][2];   // [ks][hi/lo]
+    int slot_off_b[2];    // B hi chunk: the A slots, or the hi-only swizzle (row / 4) % 4
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) slot_off[ks][p] = ((4 * p + 2 * ks + (lane >> 5)) ^ sw) * 16;
+        slot_off_b[ks] = BHI ? ((2 * ks + (lane >> 5)) ^ (((lane & 31) >> 2) & 3)) * 16 : slot_off[ks][0];
+    }
 
     floatx16 acc[TM][TN];
 #pragma unroll
@@ -153,7 +176,7 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
                 al_[i] = *reinterpret_cast<const half8*>(base + a_row + i * 32 * ROWB + slot_off[ks_][1]); \
         }                                                                                                \
         _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                                 \
-            bh_[j] = *reinterpret_cast<const half8*>(base + b_row + j * 32 * ROWB + slot_off[ks_][0]);   \
+            bh_[j] = *reinterpret_cast<const half8*>(base + b_row + j * 32 * BROWB + slot_off_b[ks_]);   \
             if constexpr (NP == 3)                                                                       \
                 bl_[j] = *reinterpret_cast<const half8*>(base + b_row + j * 32 * ROWB + slot_off[ks_][1]); \
         }                                                                                                \
@@ -186,7 +209,7 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     HEAL_DMA_TILE(kt_begin, 0);
     if (nkt > 1) {
         HEAL_DMA_TILE(kt_begin + 1, 1);
-        __builtin_amdgcn_s_waitcnt(0x4F70);          // vmcnt(16) (high bits [15:14]): tile 0 landed
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(A_DMA + B_DMA));   // tile 0 landed, tile 1 in flight
     } else {
         __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0)
     }
@@ -271,9 +294,10 @@ __global__ void zero_c_kernel(float* C, int64_t ldc, int64_t M, int64_t N) {
 
 }  // namespace
 
-hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, float* C, int64_t ldc, int64_t M,
-                               int64_t N, int64_t K, hipStream_t s) {
-    if (nprod < 1 || nprod > 3) return hipErrorInvalidValue;
+hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool b_hi, float* C, int64_t ldc,
+                               int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    // two products go with a 16-bit (hi-only) B, three with a hi/lo B
+    if (nprod < 1 || nprod > 3 || (nprod == 3 && b_hi) || (nprod == 2 && !b_hi)) return hipErrorInvalidValue;
     if (M == 0 || N == 0) return hipSuccess;
     const int64_t Kp = pack_kp(K);
     if (Kp == 0) return hipErrorInvalidValue;  // K == 0 is handled by the caller
@@ -285,14 +309,17 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, floa
     const bool split = (int64_t)tiles_m * tiles_n <= 128 && Kp / BK >= 8;
     static bool attr_set = false;  // idempotent; racing first calls set the same value
     if (!attr_set) {
-        const void* fns[6] = {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3>),
-                              reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 3>),
-                              reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2>),
-                              reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 2>),
-                              reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1>),
-                              reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1>)};
-        for (const void* f : fns) {
-            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * STAGE);
+        const std::pair<const void*, int> fns[8] = {
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3, false>), stage_bytes(false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 3, false>), stage_bytes(false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2, true>), stage_bytes(true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 2, true>), stage_bytes(true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, false>), stage_bytes(false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, false>), stage_bytes(false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true>), stage_bytes(true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true>), stage_bytes(true)}};
+        for (const auto& f : fns) {
+            hipError_t e = hipFuncSetAttribute(f.first, hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * f.second);
             if (e != hipSuccess) return e;
         }
         attr_set = true;
@@ -304,14 +331,15 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, floa
         hipLaunchKernelGGL(zero_c_kernel, dim3(zb), dim3(256), 0, s, C, ldc, M, N);
     }
     const dim3 grid((unsigned)(tiles_m * tiles_n * (split ? 2 : 1)));
-#define HEAL_PREFILL(SPLIT_, NP_)                                                                     \
-    hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, NP_>), grid, dim3(256), NSTAGE * STAGE, s, a, b, C, ldc, \
-                       (int)M, (int)N, (int)Kp, tiles_m, tiles_n)
+#define HEAL_PREFILL(SPLIT_, NP_, BHI_)                                                               \
+    hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, NP_, BHI_>), grid, dim3(256), NSTAGE * stage_bytes(BHI_), s, \
+                       a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n)
 #define HEAL_PREFILL_NP(SPLIT_)                                                                       \
     do {                                                                                              \
-        if (nprod == 3) HEAL_PREFILL(SPLIT_, 3);                                                      \
-        else if (nprod == 2) HEAL_PREFILL(SPLIT_, 2);                                                 \
-        else HEAL_PREFILL(SPLIT_, 1);                                                                 \
+        if (nprod == 3) HEAL_PREFILL(SPLIT_, 3, false);                                               \
+        else if (nprod == 2) HEAL_PREFILL(SPLIT_, 2, true);                                           \
+        else if (b_hi) HEAL_PREFILL(SPLIT_, 1, true);                                                 \
+        else HEAL_PREFILL(SPLIT_, 1, false);                                                          \
     } while (0)
     if (split) HEAL_PREFILL_NP(true);
     else HEAL_PREFILL_NP(false);

@@ -47,7 +47,9 @@ __device__ __forceinline__ bool f16_out_of_range4(const float4& v) {
 // Row r of a packed operand holds, for each 32-wide block kb of the reduction
 // dimension, 32 fp16 hi parts followed by 32 fp16 lo parts (128 bytes).  Rows
 // are padded to a multiple of kPackRows and k to a multiple of kPackK, with
-// zeros, so the GEMM main loop needs no bounds checks.
+// zeros, so the GEMM main loop needs no bounds checks.  A 16-bit weight (its
+// lo parts are zero) packs as the hi parts alone: row r holds its Kp fp16
+// values (64 bytes per 32-wide block), same padding.
 constexpr int kPackK = 32;
 constexpr int kPackRows = 256;
 
@@ -55,12 +57,14 @@ __host__ __device__ inline int64_t pack_kp(int64_t K) { return (K + kPackK - 1) 
 __host__ __device__ inline int64_t pack_rows(int64_t R) { return (R + kPackRows - 1) / kPackRows * kPackRows; }
 // bytes of one packed operand of R rows and reduction length K
 __host__ __device__ inline int64_t pack_bytes(int64_t R, int64_t K) { return pack_rows(R) * pack_kp(K) * 4; }
+// bytes of the hi-only packed form of a 16-bit operand
+__host__ __device__ inline int64_t pack_bytes_hi(int64_t R, int64_t K) { return pack_rows(R) * pack_kp(K) * 2; }
 
 // ---- launchers (return the launch status; never synchronize) -------------
 hipError_t launch_split(const float* X, int64_t n, uint16_t* hi, uint16_t* lo, uint32_t* status,
                         hipStream_t s);
-// Pack rows into the layout above.  src holds fp32 values, or binary16
-// values when f16 (their residual is zero).  kn == 0: src is [rows, K] with
+// Pack rows into the layout above.  src holds fp32 values (hi/lo form), or
+// binary16 values when f16 (hi-only form).  kn == 0: src is [rows, K] with
 // ld; kn == 1: src is [K, rows] with ld (the packed operand is its transpose).
 // kshift (nullable): element (r, k) is multiplied by 2^-kshift[k] first.
 hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int64_t K, int kn,
@@ -77,10 +81,10 @@ hipError_t launch_dequant(const int16_t* codes, int64_t rows, int64_t D, int64_t
                           hipStream_t s);
 
 // C[M,N] from packed A (rows M) and packed B (rows N) with nprod products
-// per k step: 3 (both fp32), 2 (B packed from binary16 values, zero lo
-// planes: A_hi.B_lo skipped), 1 (plain FP16: A_hi.B_hi alone).
-hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, float* C, int64_t ldc, int64_t M,
-                               int64_t N, int64_t K, hipStream_t s);
+// per k step: 3 (both fp32), 2 (B a 16-bit weight: A_hi.B_lo skipped), 1
+// (plain FP16: A_hi.B_hi alone).  b_hi: B is in the hi-only form.
+hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool b_hi, float* C, int64_t ldc,
+                               int64_t M, int64_t N, int64_t K, hipStream_t s);
 
 // Decode path (M <= 64): fp32 W [N,K] streamed and split in registers.
 // Workspace: the split activation planes (a_bytes), then, 256-byte aligned,

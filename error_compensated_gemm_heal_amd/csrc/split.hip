@@ -61,7 +61,8 @@ hipError_t launch_split(const float* X, int64_t n, uint16_t* hi, uint16_t* lo, u
 }
 
 // Source element T: float, or uint16_t holding binary16 values (whose split
-// is the value itself with a zero residual).
+// is the value itself with a zero residual).  A 16-bit source is written in
+// the hi-only form (its lo parts would all be zero).
 __device__ __forceinline__ float src_value(float x) { return x; }
 __device__ __forceinline__ float src_value(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
@@ -115,10 +116,15 @@ __global__ __launch_bounds__(256) void pack_rowmajor_kernel(const T* __restrict_
             h[j] = f16_bits(hh);
             l[j] = f16_bits(ll);
         }
-        uint16_t* o = out + r * (Kp * 2) + (k / kPackK) * (2 * kPackK) + (k % kPackK);
-        *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
-        *reinterpret_cast<uint2*>(o + kPackK) =
-            make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+        if constexpr (sizeof(T) == 2) {   // a 16-bit source: the hi-only form
+            uint16_t* o = out + r * Kp + k;
+            *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+        } else {
+            uint16_t* o = out + r * (Kp * 2) + (k / kPackK) * (2 * kPackK) + (k % kPackK);
+            *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+            *reinterpret_cast<uint2*>(o + kPackK) =
+                make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+        }
     }
     if (bad && status) atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
 }
@@ -149,10 +155,15 @@ __global__ __launch_bounds__(256) void pack_colmajor_kernel(const T* __restrict_
             h[j] = f16_bits(hh);
             l[j] = f16_bits(ll);
         }
-        uint16_t* o = out + r * (Kp * 2) + (k / kPackK) * (2 * kPackK) + (k % kPackK);
-        *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
-        *reinterpret_cast<uint2*>(o + kPackK) =
-            make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+        if constexpr (sizeof(T) == 2) {   // a 16-bit source: the hi-only form
+            uint16_t* o = out + r * Kp + k;
+            *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+        } else {
+            uint16_t* o = out + r * (Kp * 2) + (k / kPackK) * (2 * kPackK) + (k % kPackK);
+            *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+            *reinterpret_cast<uint2*>(o + kPackK) =
+                make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+        }
     }
     if (bad && status) atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
 }

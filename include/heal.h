@@ -169,21 +169,26 @@ size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags)
  *  and reused (HEAL_W_PACKED); an activation read by several GEMMs can be
  *  split once as well (HEAL_A_PACKED, with N := M rows of A and HEAL_W_NK).
  *  The packed form is internal and opaque: each row holds, for every 32-wide
- *  block of k, the 32 fp16 hi parts then the 32 fp16 lo parts.  Rows are
- *  padded to a multiple of 256 and k to a multiple of 32 with zeros.
+ *  block of k, the 32 fp16 hi parts then the 32 fp16 lo parts (with
+ *  HEAL_W_F16, the hi parts alone, half the bytes).  Rows are padded to a
+ *  multiple of 256 and k to a multiple of 32 with zeros.  An activation is
+ *  packed without HEAL_W_F16.
  *   W      as in heal_gemm_f32c (flags HEAL_W_NK or HEAL_W_KN, optionally
  *          | HEAL_W_F16: binary16 input, its lo parts are zero), 4-byte
  *          aligned (2-byte with HEAL_W_F16)
  *   kshift device int8 [K], nullable: element (r, k) is multiplied by
  *          2^-kshift[k] before its split (exact; an activation takes the
  *          shifts of heal_gemm_f32c's a_kshift, a weight their negation)
- *   packed device, >= heal_pack_w_bytes(N, K) bytes, 256-byte aligned
+ *   packed device, >= heal_pack_w_bytes(N, K, flags) bytes, 256-byte aligned
  * ------------------------------------------------------------------------ */
 heal_status heal_pack_w(const void* W, int64_t ldw, int64_t N, int64_t K, uint32_t flags,
                         const int8_t* kshift, void* packed, size_t packed_bytes,
                         uint32_t* dev_status, void* stream);
 
-size_t heal_pack_w_bytes(int64_t N, int64_t K);
+/* Bytes of heal_pack_w's buffer for these flags: 4 per element of the padded
+ * [N, K] (hi and lo), or 2 with HEAL_W_F16 (the hi parts alone: a 16-bit
+ * weight's lo parts are zero and are not stored). */
+size_t heal_pack_w_bytes(int64_t N, int64_t K, uint32_t flags);
 
 /* ------------------------------------------------------------------------
  * heal_scale_k -- per-channel power-of-two rescaling of an operand.  [GEMM]

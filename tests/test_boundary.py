@@ -103,6 +103,8 @@ def test_gemm_workspace_sizes():
     assert ws(8, 4096, 4096, heal.HEAL_A_PACKED) == 4096 * 4096 * 4   # packed A -> prefill path
     assert ws(65, 100, 33, 0) == 256 * 64 * 4 + 256 * 64 * 4
     assert heal.heal_pack_w_bytes(100, 33) == 256 * 64 * 4
+    assert heal.heal_pack_w_bytes(100, 33, heal.HEAL_W_F16) == 256 * 64 * 2      # hi parts only
+    assert ws(2048, 4096, 14336, heal.HEAL_W_F16) == 2048 * 14336 * 4 + 4096 * 14336 * 2
 
 
 def test_pack_validation():

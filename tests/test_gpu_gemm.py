@@ -222,7 +222,12 @@ def test_gemm_f16_weight_ragged_and_packed(M, N, K, layout):
     p16 = heal.heal_pack_w(W16d, layout)
     p32 = heal.heal_pack_w(W32d, layout)
     torch.cuda.synchronize()
-    assert torch.equal(p16.buf, p32.buf)
+    # the fp16 weight packs its hi parts alone: exactly the hi halves of the fp32 copy's packing
+    n16 = heal.heal_pack_w_bytes(N, K, heal.HEAL_W_F16)
+    assert n16 * 2 == heal.heal_pack_w_bytes(N, K)
+    hi32 = p32.buf[: 2 * n16].view(-1, 2, 64)[:, 0, :].reshape(-1)
+    assert torch.equal(p16.buf[:n16], hi32)
+    assert not torch.any(p32.buf[: 2 * n16].view(-1, 2, 64)[:, 1, :])
     cp = heal.heal_gemm_f32c(Ad, p16).cpu().numpy()
     if M > 64:   # both through the prefill kernel's two-product form
         assert np.array_equal(cp, c16)
