@@ -20,6 +20,9 @@ workload (inputs resident in HBM before timing starts):
   decode_kshift  the same 16 GEMMs with massive activation channels beyond
            FP16's range (0.5% of channels x 2e5), rescaled per channel by powers
            of two in the split (a_kshift) against a once-rescaled weight
+  qkv_proj the fused Q/K/V projection of a 2048-token prefill chunk (K = 4096,
+           32 + 8 + 8 heads of 128: N = 6144), compensated, stored as INT16
+           (Q codes, K/V codes written into a KV cache by slot)
   quant    INT16 quant of a Qwen3-8B-like layer's Q/K/V: 32 x 2048 tokens,
            32 + 8 + 8 heads of 128 (one [65536, 48, 128] launch)
   dequant  INT16 -> fp32 dequant of the same codes
@@ -128,6 +131,25 @@ def build_workload(rows_sel):
         W["decode_kshift"] = callsk
         log(f"[bench] rescaled decode inputs ready ({time.time() - t0:.1f}s)")
 
+    if "qkv_proj" in rows_sel:
+        M, K, Hq, Hkv, D = WL.PREFILL_M, 4096, 32, 8, 128
+        A, Wt = WL.prefill_gemm(M, K, (Hq + 2 * Hkv) * D, seed=3500)
+        Ad = torch.from_numpy(A).to(dev)
+        Wp = heal.heal_pack_w(torch.from_numpy(Wt).to(dev))
+        slots = torch.arange(M, dtype=torch.int64, device=dev)
+        kc = torch.empty((M, Hkv, D), dtype=torch.int16, device=dev)
+        vc = torch.empty_like(kc)
+        ks = torch.empty((M, Hkv), dtype=torch.float32, device=dev)
+        vs = torch.empty_like(ks)
+        qc = torch.empty((M, Hq, D), dtype=torch.int16, device=dev)
+        qs = torch.empty((M, Hq), dtype=torch.float32, device=dev)
+        ws = torch.empty(heal.heal_qkv_proj_quant_workspace(M, K, Hq, Hkv, D, heal.HEAL_W_PACKED), dtype=torch.uint8,
+                         device=dev)
+        W["qkv_proj"] = dict(A=Ad, Wp=Wp, slots=slots, kc=kc, vc=vc, ks=ks, vs=vs, qc=qc, qs=qs, ws=ws, M=M, K=K,
+                             Hq=Hq, Hkv=Hkv, D=D)
+        del A, Wt
+        log(f"[bench] qkv projection inputs ready ({time.time() - t0:.1f}s)")
+
     if "quant" in rows_sel or "dequant" in rows_sel:
         tokens = 32 * 2048
         Q, K_, V = WL.qkv(tokens, 32, 8, 128, seed=4000)
@@ -216,6 +238,14 @@ def make_rows(W):
 
         dkbytes = sum(4 * (c["K"] * c["N"] + c["M"] * c["K"] + c["M"] * c["N"]) + c["K"] for c in callsk)
         rows.append(("decode_kshift", run_decodek, dkbytes, "B"))
+    if "qkv_proj" in W:
+        p = W["qkv_proj"]
+
+        def run_qkv():
+            heal.heal_qkv_proj_quant_i16(p["A"], p["Wp"], p["Hq"], p["Hkv"], p["D"], p["slots"], p["kc"], p["ks"],
+                                         p["vc"], p["vs"], q_codes=p["qc"], q_scales=p["qs"], workspace=p["ws"])
+
+        rows.append(("qkv_proj", run_qkv, 2.0 * p["M"] * p["K"] * (p["Hq"] + 2 * p["Hkv"]) * p["D"], "flop"))
     if "quant" in W:
         q = W["quant"]
         qbytes = q["n"] * (4 + 2) + q["rows"] * 4
@@ -260,8 +290,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--rows", default="split,prefill,prefill_w16,prefill_1p,decode,decode_w16,decode_kshift,quant,"
-                                      "dequant,attn",
+    ap.add_argument("--rows", default="split,prefill,prefill_w16,prefill_1p,decode,decode_w16,decode_kshift,"
+                                      "qkv_proj,quant,dequant,attn",
                     help="comma-separated subset of rows to run (profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -345,6 +375,7 @@ def main():
                        "fp32 weights, and fp16 weights in the two-product form), "
                        "16 decode GEMMs (M=1,8,32,64 x Llama-3-8B q/o, k/v, gate/up, down; fp32 and fp16 weights, "
                        "and fp32 with per-channel rescaled massive activations), "
+                       "fused Q/K/V projection to INT16 (2048 tokens, K=4096, N=6144), "
                        "INT16 quant + dequant "
                        "(32x2048 tokens, 32+8+8 heads x 128), INT16 decode attention (B=16, T=8192, 32/8 heads)",
            "rows": sorted(sel)}

@@ -17,7 +17,7 @@ __all__ = [
     "heal_kv_dequant_i16", "heal_attn_decode_i16", "heal_attn_decode_workspace", "PackedOperand",
     "heal_scale_k", "heal_kshift_from_absmax",
     "PackedWeight", "HEAL_W_NK", "HEAL_W_KN", "HEAL_W_PACKED", "HEAL_A_PACKED", "HEAL_W_F16", "HEAL_ONE_PRODUCT",
-    "HEAL_FLAG_F16_RANGE",
+    "HEAL_FLAG_F16_RANGE", "HEAL_FLAG_SLOT_RANGE", "heal_qkv_proj_quant_i16", "heal_qkv_proj_quant_workspace",
     "HEAL_DQ_F32", "HEAL_DQ_F16X2",
     "LIB_PATH",
 ]
@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libheal.so"
 HEAL_OK = 0
 HEAL_W_NK, HEAL_W_KN, HEAL_W_PACKED, HEAL_A_PACKED, HEAL_W_F16, HEAL_ONE_PRODUCT = 0, 1, 2, 4, 8, 16
 HEAL_FLAG_F16_RANGE = 1
+HEAL_FLAG_SLOT_RANGE = 2
 HEAL_DQ_F32, HEAL_DQ_F16X2 = 0, 1
 
 # (name, argtypes, restype) of every exported entry point
@@ -45,6 +46,9 @@ SIGNATURES = {
     "heal_kv_dequant_i16": ([_P, _I64, _I64, _I64, _P, _INT, _P, _P, _I64, _P], _INT),
     "heal_attn_decode_i16": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _SZ, _P], _INT),
     "heal_attn_decode_workspace": ([_I64, _I64, _I64, _I64, _I64], _SZ),
+    "heal_qkv_proj_quant_i16": ([_P, _I64, _P, _I64, _I64, _I64, _I64, _I64, _I64, _U32, _P, _P, _P, _P, _I64,
+                                 _P, _P, _P, _P, _P, _SZ, _P, _P], _INT),
+    "heal_qkv_proj_quant_workspace": ([_I64, _I64, _I64, _I64, _I64, _U32], _SZ),
 }
 
 _LIB = None
@@ -277,6 +281,59 @@ def heal_kshift_from_absmax(absmax, limit: float = 32768.0):
 
 
 # ---- INT16 quant / dequant -------------------------------------------------------------
+
+def heal_qkv_proj_quant_workspace(M: int, K: int, Hq: int, Hkv: int, D: int, flags: int = 0) -> int:
+    return lib().heal_qkv_proj_quant_workspace(M, K, Hq, Hkv, D, flags)
+
+
+def heal_qkv_proj_quant_i16(A, W, Hq: int, Hkv: int, D: int, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                            k_scales: torch.Tensor, v_cache: torch.Tensor, v_scales: torch.Tensor, q_codes=None,
+                            q_scales=None, workspace=None, dev_status=None, a_kshift=None,
+                            one_product: bool = False):
+    """Fused Q/K/V projection stored as INT16: C = A . W^T (W [(Hq + 2 Hkv) D, K], or a
+    packed weight), Q rows -> (q_codes [M, Hq, D], q_scales [M, Hq]) returned, K/V rows
+    -> k/v_cache [num_slots, Hkv, D] and k/v_scales [num_slots, Hkv] at slot_mapping[m]."""
+    _dev(A, "A", torch.float32)
+    M, K = A.shape
+    N = (Hq + 2 * Hkv) * D
+    if isinstance(W, PackedOperand):
+        if W.K != K or W.rows != N:
+            raise ValueError("packed weight does not match (K, (Hq + 2 Hkv) D)")
+        flags, wptr, ldw = HEAL_W_PACKED | (HEAL_W_F16 if W.f16 else 0), _ptr(W.buf), 0
+    else:
+        _dev(W, "W")
+        if tuple(W.shape) != (N, K):
+            raise ValueError("W must be [(Hq + 2 Hkv) D, K]")
+        flags, wptr, ldw = _weight_dtype_flag(W), _ptr(W), _rowmajor_ld(W, "W")
+    flags |= HEAL_ONE_PRODUCT if one_product else 0
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    for t, name, dt in ((k_cache, "k_cache", torch.int16), (v_cache, "v_cache", torch.int16),
+                        (k_scales, "k_scales", torch.float32), (v_scales, "v_scales", torch.float32)):
+        _dev(t, name, dt)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    num_slots = k_cache.numel() // (Hkv * D)
+    if (k_cache.numel() != num_slots * Hkv * D or v_cache.numel() != k_cache.numel()
+            or k_scales.numel() != num_slots * Hkv or v_scales.numel() != k_scales.numel()):
+        raise ValueError("cache shapes must be [num_slots, Hkv, D] and scales [num_slots, Hkv]")
+    if slot_mapping.numel() != M or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int64 vector of M entries")
+    if q_codes is None:
+        q_codes = torch.empty((M, Hq, D), dtype=torch.int16, device=A.device)
+    if q_scales is None:
+        q_scales = torch.empty((M, Hq), dtype=torch.float32, device=A.device)
+    nbytes = heal_qkv_proj_quant_workspace(M, K, Hq, Hkv, D, flags)
+    if workspace is None:
+        workspace = _workspace(nbytes, A.device)
+    elif workspace.numel() < nbytes:
+        raise ValueError("workspace too small")
+    ks = _kshift(a_kshift, K, "a_kshift")
+    _check("heal_qkv_proj_quant_i16", lib().heal_qkv_proj_quant_i16(
+        _ptr(A), _rowmajor_ld(A, "A"), wptr, ldw, M, K, Hq, Hkv, D, flags, _ptr(ks), _ptr(q_codes), _ptr(q_scales),
+        _ptr(slot_mapping), num_slots, _ptr(k_cache), _ptr(k_scales), _ptr(v_cache), _ptr(v_scales),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _ptr(dev_status), _stream()))
+    return q_codes, q_scales
+
 
 def heal_qkv_quant_i16(X: torch.Tensor, codes=None, scales=None):
     """X [..., D] fp32 -> (codes int16 [..., D], scales fp32 [...]), one scale per row of D."""

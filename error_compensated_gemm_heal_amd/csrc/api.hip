@@ -207,6 +207,45 @@ heal_status heal_qkv_quant_i16(const float* X, int64_t rows, int64_t D, int64_t 
     return hip_status(launch_quant(X, rows, D, ldx, codes, ldq, scales, static_cast<hipStream_t>(stream)));
 }
 
+size_t heal_qkv_proj_quant_workspace(int64_t M, int64_t K, int64_t Hq, int64_t Hkv, int64_t D,
+                                     uint32_t flags) {
+    if (M <= 0 || K <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || M >= kMaxDim || K >= kMaxDim) return 0;
+    const int64_t N = (Hq + 2 * Hkv) * D;
+    if (N >= kMaxDim) return 0;
+    return (size_t)round256(M * N * 4) + heal_gemm_f32c_workspace(M, N, K, flags);
+}
+
+heal_status heal_qkv_proj_quant_i16(const float* A, int64_t lda, const void* W, int64_t ldw, int64_t M,
+                                    int64_t K, int64_t Hq, int64_t Hkv, int64_t D, uint32_t flags,
+                                    const int8_t* a_kshift, int16_t* q_codes, float* q_scales,
+                                    const int64_t* slot_mapping, int64_t num_slots, int16_t* k_cache,
+                                    float* k_scales, int16_t* v_cache, float* v_scales, void* workspace,
+                                    size_t workspace_bytes, uint32_t* dev_status, void* stream) {
+    if (M < 0 || K < 0 || Hq < 1 || Hkv < 1 || num_slots < 0 || M >= kMaxDim || K >= kMaxDim)
+        return HEAL_ERR_SHAPE;
+    if (D < 4 || D > 4096 || (D & 3) || (Hq + 2 * Hkv) * D >= kMaxDim) return HEAL_ERR_SHAPE;
+    if (flags & HEAL_W_KN) return HEAL_ERR_UNSUPPORTED;
+    if (M == 0) return HEAL_OK;
+    if (!q_codes || !q_scales || !slot_mapping || !k_cache || !k_scales || !v_cache || !v_scales)
+        return HEAL_ERR_NULL;
+    if (misaligned(q_codes, 8) || misaligned(k_cache, 8) || misaligned(v_cache, 8) || misaligned(q_scales, 4) ||
+        misaligned(k_scales, 4) || misaligned(v_scales, 4) || misaligned(slot_mapping, 8) ||
+        misaligned(dev_status, 4))
+        return HEAL_ERR_ALIGN;
+    const int64_t N = (Hq + 2 * Hkv) * D;
+    const size_t need = heal_qkv_proj_quant_workspace(M, K, Hq, Hkv, D, flags);
+    if (!workspace || workspace_bytes < need) return HEAL_ERR_WORKSPACE;
+    if (misaligned(workspace, 256)) return HEAL_ERR_ALIGN;
+    // the fp32 product lands in the workspace, the GEMM's own workspace after it
+    float* C = static_cast<float*>(workspace);
+    unsigned char* gws = static_cast<unsigned char*>(workspace) + round256(M * N * 4);
+    const heal_status st = heal_gemm_f32c(A, lda, W, ldw, C, N, M, N, K, flags, a_kshift, gws,
+                                          workspace_bytes - (size_t)round256(M * N * 4), dev_status, stream);
+    if (st != HEAL_OK) return st;
+    return hip_status(launch_quant_qkv(C, M, Hq, Hkv, D, q_codes, q_scales, slot_mapping, num_slots, k_cache,
+                                       k_scales, v_cache, v_scales, dev_status, static_cast<hipStream_t>(stream)));
+}
+
 heal_status heal_kv_dequant_i16(const int16_t* codes, int64_t rows, int64_t D, int64_t ldq,
                                 const float* scales, int fmt, void* out, void* out_lo, int64_t ldo,
                                 void* stream) {

@@ -76,6 +76,12 @@ hipError_t launch_scale_k(const void* src, bool f16, int64_t ld, int64_t rows, i
 
 hipError_t launch_quant(const float* X, int64_t rows, int64_t D, int64_t ldx, int16_t* codes,
                         int64_t ldq, float* scales, hipStream_t s);
+// Quantize the rows of a Q/K/V projection output C [M, (Hq + 2 Hkv) D]
+// (contiguous): Q heads to q_codes/q_scales, K and V heads to their cache
+// slots slot_mapping[m] (negative: skipped; >= num_slots: skipped and flagged).
+hipError_t launch_quant_qkv(const float* C, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, int16_t* q_codes,
+                            float* q_scales, const int64_t* slot_mapping, int64_t num_slots, int16_t* k_cache,
+                            float* k_scales, int16_t* v_cache, float* v_scales, uint32_t* status, hipStream_t s);
 hipError_t launch_dequant(const int16_t* codes, int64_t rows, int64_t D, int64_t ldq,
                           const float* scales, int fmt, void* out, void* out_lo, int64_t ldo,
                           hipStream_t s);

@@ -30,10 +30,61 @@ struct RowTiling {
     static constexpr int ROWS = U * RPW;                 // rows per wave per step
 };
 
-template <int LPR, int NCH>
+// Where a quantized row goes: at(r, codes, scale) sets the row's D codes and
+// its scale, or returns false for a row that is not written.
+struct PlainDst {   // codes [rows, ldq], scales [rows]
+    int16_t* codes;
+    int64_t ldq;
+    float* scales;
+    __device__ bool at(int64_t r, int16_t*& c, float*& s) const {
+        c = codes + r * ldq;
+        s = scales + r;
+        return true;
+    }
+};
+
+// Rows of a fused Q/K/V projection output [M, (Hq + 2 Hkv) D]: row r is
+// (token m, head h).  Q heads go to q_codes [M, Hq, D] and q_scales [M, Hq];
+// K and V heads go to cache slot slot_mapping[m] of k/v_cache
+// [num_slots, Hkv, D] and k/v_scales [num_slots, Hkv].  A negative slot is
+// skipped (a padding token); a slot >= num_slots is skipped and flagged.
+struct QkvDst {
+    int16_t* qc;
+    float* qs;
+    int16_t* kc;
+    float* ks;
+    int16_t* vc;
+    float* vs;
+    const int64_t* slots;
+    int64_t num_slots;
+    int hq, hkv, d;
+    uint32_t* status;
+    __device__ bool at(int64_t r, int16_t*& c, float*& s) const {
+        const int H = hq + 2 * hkv;
+        const int64_t m = r / H;
+        const int h = (int)(r - m * H);
+        if (h < hq) {
+            c = qc + (m * hq + h) * d;
+            s = qs + m * hq + h;
+            return true;
+        }
+        const int64_t slot = slots[m];
+        if (slot < 0) return false;
+        if (slot >= num_slots) {
+            if (status) atomicOr(status, (uint32_t)HEAL_FLAG_SLOT_RANGE);
+            return false;
+        }
+        const bool is_k = h < hq + hkv;
+        const int hk = is_k ? h - hq : h - hq - hkv;
+        c = (is_k ? kc : vc) + (slot * hkv + hk) * d;
+        s = (is_k ? ks : vs) + slot * hkv + hk;
+        return true;
+    }
+};
+
+template <int LPR, int NCH, class Dst>
 __global__ __launch_bounds__(256) void quant_kernel(const float* __restrict__ X, int64_t rows, int D,
-                                                    int64_t ldx, int16_t* __restrict__ codes,
-                                                    int64_t ldq, float* __restrict__ scales) {
+                                                    int64_t ldx, Dst dst) {
     using RT = RowTiling<LPR, NCH>;
     const int lane = threadIdx.x & 63;
     const int sub = lane / LPR;     // which row of a group
@@ -65,7 +116,10 @@ __global__ __launch_bounds__(256) void quant_kernel(const float* __restrict__ X,
 #pragma unroll
             for (int off = LPR / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
             if (r >= rows) continue;
-            if (gl == 0) scales[r] = (m == 0.0f) ? 0.0f : __fdiv_rn(m, 32767.0f);
+            int16_t* crow;
+            float* srow;
+            if (!dst.at(r, crow, srow)) continue;
+            if (gl == 0) *srow = (m == 0.0f) ? 0.0f : __fdiv_rn(m, 32767.0f);
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 const int j = gl + c * LPR;
@@ -79,7 +133,7 @@ __global__ __launch_bounds__(256) void quant_kernel(const float* __restrict__ X,
                         q.z = (short)__builtin_rintf(__fdiv_rn(__fmul_rn(32767.0f, x[u][c].z), m));
                         q.w = (short)__builtin_rintf(__fdiv_rn(__fmul_rn(32767.0f, x[u][c].w), m));
                     }
-                    *reinterpret_cast<short4*>(codes + r * ldq + 4 * j) = q;
+                    *reinterpret_cast<short4*>(crow + 4 * j) = q;
                 }
             }
         }
@@ -167,13 +221,13 @@ unsigned grid_for(int64_t rows, int rows_per_wave_step) {
 
 #define HEAL_QUANT_CASE(L, C)                                                                        \
     if (lpr == L && nch == C) {                                                                      \
-        hipLaunchKernelGGL((quant_kernel<L, C>), dim3(grid_for(rows, RowTiling<L, C>::ROWS)), dim3(256), 0, s, X, rows, \
-                           (int)D, ldx, codes, ldq, scales);                                         \
+        hipLaunchKernelGGL((quant_kernel<L, C, Dst>), dim3(grid_for(rows, RowTiling<L, C>::ROWS)), dim3(256), 0, s, X, \
+                           rows, (int)D, ldx, dst);                                                  \
         return hipGetLastError();                                                                    \
     }
 
-hipError_t launch_quant(const float* X, int64_t rows, int64_t D, int64_t ldx, int16_t* codes,
-                        int64_t ldq, float* scales, hipStream_t s) {
+template <class Dst>
+hipError_t launch_quant_to(const float* X, int64_t rows, int64_t D, int64_t ldx, const Dst& dst, hipStream_t s) {
     if (rows == 0) return hipSuccess;
     int lpr, nch;
     row_shape(D, lpr, nch);
@@ -183,6 +237,19 @@ hipError_t launch_quant(const float* X, int64_t rows, int64_t D, int64_t ldx, in
     return hipErrorInvalidValue;
 }
 #undef HEAL_QUANT_CASE
+
+hipError_t launch_quant(const float* X, int64_t rows, int64_t D, int64_t ldx, int16_t* codes,
+                        int64_t ldq, float* scales, hipStream_t s) {
+    return launch_quant_to(X, rows, D, ldx, PlainDst{codes, ldq, scales}, s);
+}
+
+hipError_t launch_quant_qkv(const float* C, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, int16_t* q_codes,
+                            float* q_scales, const int64_t* slot_mapping, int64_t num_slots, int16_t* k_cache,
+                            float* k_scales, int16_t* v_cache, float* v_scales, uint32_t* status, hipStream_t s) {
+    const QkvDst dst{q_codes, q_scales, k_cache, k_scales, v_cache, v_scales, slot_mapping, num_slots,
+                     (int)Hq, (int)Hkv, (int)D, status};
+    return launch_quant_to(C, M * (Hq + 2 * Hkv), D, D, dst, s);
+}
 
 #define HEAL_DQ_CASE(L, C)                                                                            \
     if (lpr == L && nch == C) {                                                                       \

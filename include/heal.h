@@ -63,7 +63,8 @@ enum {
 
 /* Bits of the optional device status word. */
 enum {
-    HEAL_FLAG_F16_RANGE = 1u  /* an operand had |x| >= 65520: its fp16 high part is inf */
+    HEAL_FLAG_F16_RANGE = 1u, /* an operand had |x| >= 65520: its fp16 high part is inf */
+    HEAL_FLAG_SLOT_RANGE = 2u /* a K/V cache slot was >= num_slots: that row was skipped */
 };
 
 /* Formats of heal_kv_dequant_i16. */
@@ -238,6 +239,39 @@ heal_status heal_kshift_from_absmax(const float* absmax, int64_t K, float limit,
  * ------------------------------------------------------------------------ */
 heal_status heal_qkv_quant_i16(const float* X, int64_t rows, int64_t D, int64_t ldx,
                                int16_t* codes, int64_t ldq, float* scales, void* stream);
+
+/* ------------------------------------------------------------------------
+ * heal_qkv_proj_quant_i16 -- Q/K/V projection with INT16 output.  [GEMM]+[INT16]
+ *  The fused Q/K/V linear layer, C = A . W^T with W [(Hq + 2 Hkv) D, K]
+ *  (Q heads, then K heads, then V heads, D rows each), computed as
+ *  heal_gemm_f32c does, then stored only as INT16 (the pages keep Q, K and
+ *  V in INT16; fp32 K/V would double the cache): each (token m, head h) row
+ *  of D values is quantized as heal_qkv_quant_i16 does, bit for bit.  Q
+ *  rows go to q_codes [M, Hq, D] / q_scales [M, Hq]; K and V rows go to the
+ *  cache slot slot_mapping[m] of k_cache / v_cache [num_slots, Hkv, D] and
+ *  k_scales / v_scales [num_slots, Hkv] (a paged cache of blocks of B
+ *  tokens is this layout with slot = block * B + offset).  A negative slot
+ *  writes no K/V row (a padding token); a slot >= num_slots writes none and
+ *  sets HEAL_FLAG_SLOT_RANGE in dev_status.  Slots of distinct tokens must
+ *  differ, or their rows race.
+ *   A, lda, W, ldw, flags, a_kshift  as in heal_gemm_f32c with N = (Hq + 2 Hkv) D
+ *          (HEAL_W_KN not supported)
+ *   q_codes, k_cache, v_cache  device int16, 8-byte aligned
+ *   q_scales, k_scales, v_scales  device fp32, 4-byte aligned
+ *   slot_mapping  device int64 [M], 8-byte aligned
+ *   workspace  device, >= heal_qkv_proj_quant_workspace(...) bytes, 256-byte
+ *          aligned (holds the fp32 product and the GEMM's own workspace)
+ * Limits: Hq, Hkv >= 1; D % 4 == 0, 4 <= D <= 4096; (Hq + 2 Hkv) D < 2^31.
+ * ------------------------------------------------------------------------ */
+heal_status heal_qkv_proj_quant_i16(const float* A, int64_t lda, const void* W, int64_t ldw, int64_t M,
+                                    int64_t K, int64_t Hq, int64_t Hkv, int64_t D, uint32_t flags,
+                                    const int8_t* a_kshift, int16_t* q_codes, float* q_scales,
+                                    const int64_t* slot_mapping, int64_t num_slots, int16_t* k_cache,
+                                    float* k_scales, int16_t* v_cache, float* v_scales, void* workspace,
+                                    size_t workspace_bytes, uint32_t* dev_status, void* stream);
+
+size_t heal_qkv_proj_quant_workspace(int64_t M, int64_t K, int64_t Hq, int64_t Hkv, int64_t D,
+                                     uint32_t flags);
 
 /* ------------------------------------------------------------------------
  * heal_kv_dequant_i16 -- INT16 dequantization.   [INT16]

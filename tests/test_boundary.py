@@ -181,6 +181,27 @@ def test_quant_dequant_validation():
     assert d(FAKE, 4, 128, 120, FAKE, heal.HEAL_DQ_F32, FAKE, None, 128, None) == STRIDE
 
 
+def _qkv(M=8, K=256, Hq=4, Hkv=2, D=128, flags=0, q=FAKE, sl=FAKE, kc=FAKE, ns=16, ws=FAKE, wsb=1 << 30):
+    return heal.lib().heal_qkv_proj_quant_i16(FAKE, K, FAKE, K, M, K, Hq, Hkv, D, flags, None, q, FAKE, sl, ns, kc,
+                                              FAKE, FAKE, FAKE, ws, wsb, None, None)
+
+
+def test_qkv_proj_validation():
+    assert _qkv(M=-1) == SHAPE
+    assert _qkv(Hkv=0) == SHAPE
+    assert _qkv(D=6) == SHAPE
+    assert _qkv(flags=heal.HEAL_W_KN) == UNSUP
+    assert _qkv(M=0, q=None, sl=None) == OK
+    assert _qkv(q=None) == NULL
+    assert _qkv(sl=None) == NULL
+    assert _qkv(kc=ctypes.c_void_p(0x10004)) == ALIGN
+    assert _qkv(sl=ctypes.c_void_p(0x10004)) == ALIGN
+    assert _qkv(ws=None) == WS
+    assert _qkv(wsb=16) == WS
+    n = heal.heal_qkv_proj_quant_workspace(8, 256, 4, 2, 128, 0)
+    assert n >= 8 * 1024 * 4 and n % 256 == 0
+
+
 def _attn(B=2, T=16, Hq=8, Hkv=2, D=128, ws=FAKE, wsb=1 << 30, q=FAKE):
     return heal.lib().heal_attn_decode_i16(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, T, Hq, Hkv, D, ws, wsb, None)
 
