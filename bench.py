@@ -26,6 +26,8 @@ workload (inputs resident in HBM before timing starts):
   quant    INT16 quant of a Qwen3-8B-like layer's Q/K/V: 32 x 2048 tokens,
            32 + 8 + 8 heads of 128 (one [65536, 48, 128] launch)
   dequant  INT16 -> fp32 dequant of the same codes
+  attn_prefill  causal self-attention of a 2048-token prompt over INT16 Q/K/V
+           (32 query / 8 KV heads, D = 128), dual-FP16 expansion on MFMA
   attn     decode attention over the INT16 KV cache: batch 16, context 8192,
            32 query / 8 KV heads, D = 128
 
@@ -165,6 +167,17 @@ def build_workload(rows_sel):
         W["quant"] = dict(X=X, codes=codes, scales=scales, deq=deq, n=X.numel(), rows=X.numel() // 128)
         log(f"[bench] quant inputs ready ({time.time() - t0:.1f}s)")
 
+    if "attn_prefill" in rows_sel:
+        B, T, Hq, Hkv, D = 1, 2048, 32, 8, 128
+        qf, kf, vf = WL.attention_prefill_fp32(B, T, Hq, Hkv, D, seed=5500)
+        q, qs = heal.heal_qkv_quant_i16(torch.from_numpy(qf).to(dev))
+        k, ks = heal.heal_qkv_quant_i16(torch.from_numpy(kf).to(dev))
+        v, vs = heal.heal_qkv_quant_i16(torch.from_numpy(vf).to(dev))
+        del qf, kf, vf
+        out = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
+        W["attn_prefill"] = dict(args=(q, qs, k, ks, v, vs), out=out, B=B, T=T, Hq=Hq, D=D)
+        log(f"[bench] prefill attention inputs ready ({time.time() - t0:.1f}s)")
+
     if "attn" in rows_sel:
         B, T, Hq, Hkv, D = 16, 8192, 32, 8, 128
         qf, kf, vf = WL.attention_fp32(B, T, Hq, Hkv, D, seed=5000)
@@ -252,11 +265,17 @@ def make_rows(W):
         rows.append(("quant", lambda: heal.heal_qkv_quant_i16(q["X"], q["codes"], q["scales"]), qbytes, "B"))
         rows.append(("dequant", lambda: heal.heal_kv_dequant_i16(q["codes"], q["scales"], "f32", out=q["deq"]),
                      qbytes, "B"))
+    if "attn_prefill" in W:
+        a = W["attn_prefill"]
+        # useful flops: two products of D multiply-adds per (query, visible key, head)
+        pairs = a["B"] * a["T"] * (a["T"] + 1) // 2
+        rows.append(("attn_prefill", lambda a=a: heal.heal_attn_prefill_i16(*a["args"], out=a["out"]),
+                     4.0 * a["D"] * a["Hq"] * pairs, "flop"))
     if "attn" in W:
         a = W["attn"]
         B, T, Hq, Hkv, D = a["B"], a["T"], a["Hq"], a["Hkv"], a["D"]
         abytes = 2 * B * T * Hkv * D * 2 + 2 * B * T * Hkv * 4 + B * Hq * D * 2 + B * Hq * 4 + B * Hq * D * 4
-        rows.append(("attn", lambda: heal.heal_attn_decode_i16(*a["args"], out=a["out"], workspace=a["ws"]),
+        rows.append(("attn", lambda a=a: heal.heal_attn_decode_i16(*a["args"], out=a["out"], workspace=a["ws"]),
                      abytes, "B"))
     return rows
 
@@ -291,7 +310,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--rows", default="split,prefill,prefill_w16,prefill_1p,decode,decode_w16,decode_kshift,"
-                                      "qkv_proj,quant,dequant,attn",
+                                      "qkv_proj,quant,dequant,attn_prefill,attn",
                     help="comma-separated subset of rows to run (profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -377,7 +396,8 @@ def main():
                        "and fp32 with per-channel rescaled massive activations), "
                        "fused Q/K/V projection to INT16 (2048 tokens, K=4096, N=6144), "
                        "INT16 quant + dequant "
-                       "(32x2048 tokens, 32+8+8 heads x 128), INT16 decode attention (B=16, T=8192, 32/8 heads)",
+                       "(32x2048 tokens, 32+8+8 heads x 128), INT16 prefill attention (T=2048, 32/8 heads), "
+                       "INT16 decode attention (B=16, T=8192, 32/8 heads)",
            "rows": sorted(sel)}
     res["config"] = cfg
     if "prefill" in per_row:

@@ -18,6 +18,7 @@ __all__ = [
     "heal_scale_k", "heal_kshift_from_absmax",
     "PackedWeight", "HEAL_W_NK", "HEAL_W_KN", "HEAL_W_PACKED", "HEAL_A_PACKED", "HEAL_W_F16", "HEAL_ONE_PRODUCT",
     "HEAL_FLAG_F16_RANGE", "HEAL_FLAG_SLOT_RANGE", "heal_qkv_proj_quant_i16", "heal_qkv_proj_quant_workspace",
+    "heal_attn_prefill_i16",
     "HEAL_DQ_F32", "HEAL_DQ_F16X2",
     "LIB_PATH",
 ]
@@ -49,6 +50,7 @@ SIGNATURES = {
     "heal_qkv_proj_quant_i16": ([_P, _I64, _P, _I64, _I64, _I64, _I64, _I64, _I64, _U32, _P, _P, _P, _P, _I64,
                                  _P, _P, _P, _P, _P, _SZ, _P, _P], _INT),
     "heal_qkv_proj_quant_workspace": ([_I64, _I64, _I64, _I64, _I64, _U32], _SZ),
+    "heal_attn_prefill_i16": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P], _INT),
 }
 
 _LIB = None
@@ -370,6 +372,26 @@ def heal_kv_dequant_i16(codes: torch.Tensor, scales=None, fmt: str = "f32", out=
 
 def heal_attn_decode_workspace(B, T, Hq, Hkv, D) -> int:
     return lib().heal_attn_decode_workspace(B, T, Hq, Hkv, D)
+
+
+def heal_attn_prefill_i16(q, q_scale, k, k_scale, v, v_scale, out=None):
+    """Causal self-attention of a prompt: q [B,T,Hq,D] int16 + [B,T,Hq]; k, v [B,T,Hkv,D]
+    int16 + [B,T,Hkv] -> out [B,T,Hq,D] fp32 (query t sees keys 0 .. t)."""
+    for name, t, dt in (("q", q, torch.int16), ("k", k, torch.int16), ("v", v, torch.int16),
+                        ("q_scale", q_scale, torch.float32), ("k_scale", k_scale, torch.float32),
+                        ("v_scale", v_scale, torch.float32)):
+        _dev(t, name, dt)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, T, Hkv, D) or tuple(v.shape) != (B, T, Hkv, D):
+        raise ValueError("k and v must be [B, T, Hkv, D] with q's B, T, D")
+    out = torch.empty((B, T, Hq, D), dtype=torch.float32, device=q.device) if out is None else out
+    _check("heal_attn_prefill_i16", lib().heal_attn_prefill_i16(
+        _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(v), _ptr(v_scale), _ptr(out), B, T, Hq, Hkv, D,
+        _stream()))
+    return out
 
 
 def heal_attn_decode_i16(q, q_scale, k, k_scale, v, v_scale, out=None, workspace=None):

@@ -292,4 +292,20 @@ heal_status heal_attn_decode_i16(const int16_t* q, const float* q_scale, const i
                                          workspace, static_cast<hipStream_t>(stream)));
 }
 
+heal_status heal_attn_prefill_i16(const int16_t* q, const float* q_scale, const int16_t* k,
+                                  const float* k_scale, const int16_t* v, const float* v_scale, float* out,
+                                  int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, void* stream) {
+    if (B < 0 || T < 0 || Hq < 0 || Hkv < 0 || D < 0 || B >= kMaxDim || T >= kMaxDim) return HEAL_ERR_SHAPE;
+    if (B == 0 || T == 0 || Hq == 0) return HEAL_OK;
+    if (Hkv == 0 || Hq % Hkv) return HEAL_ERR_SHAPE;
+    if (D != 128 || T > 262144 || B * Hq * ((T + 63) / 64) >= kMaxDim) return HEAL_ERR_UNSUPPORTED;
+    if (T * Hkv * D * 2 >= ((int64_t)1 << 32)) return HEAL_ERR_UNSUPPORTED;   // 32-bit offsets per batch
+    if (!q || !q_scale || !k || !k_scale || !v || !v_scale || !out) return HEAL_ERR_NULL;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 4) ||
+        misaligned(q_scale, 4) || misaligned(k_scale, 4) || misaligned(v_scale, 4))
+        return HEAL_ERR_ALIGN;
+    return hip_status(launch_attn_prefill(q, q_scale, k, k_scale, v, v_scale, out, B, T, Hq, Hkv, D,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

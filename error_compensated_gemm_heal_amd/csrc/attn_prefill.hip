@@ -1,0 +1,344 @@
+// Prefill (causal self-) attention over INT16 Q/K/V, with the INT16 ->
+// dual-FP16 unpack fused into the operand loads.
+//
+// HEAL paper, section 3, "Mitigating QKV Truncation Error via INT16
+// Quantization": Q, K and V are stored as INT16 codes with one scale per
+// token and head, and attention runs as 16-bit products of the codes' exact
+// FP16 parts with FP32 accumulation.  For a prompt of T tokens, query t
+// attends keys 0 .. t.
+//
+// Codes split as q = 64 qh + ql, qh = q >> 6 in [-512, 511], ql = q & 63;
+// 64 qh and ql are exact FP16 values, and every product of two such parts is
+// exact in FP32 (at most 2^30, 20 significant bits).
+//
+// One block of 4 waves owns 64 consecutive queries of one (batch, head);
+// wave w takes queries 16 w .. 16 w + 15 of them.  The block walks the key
+// blocks of 64 tokens that its queries can see (causal), K and V of the next
+// block copied into LDS by direct-to-LDS loads while the current one is used:
+//  * scores as S^T = K . Q^T on v_mfma_f32_16x16x32_f16: rows are keys,
+//    columns the wave's 16 queries.  A = {64 kh, kl}, B = {64 qh, ql}: the
+//    four products go into one accumulator, which then holds k . q;
+//  * online softmax in base 2 (log2 e folded into s_q s_k / sqrt(D)): per
+//    query the running maximum, the running sum, and the output rescaled by
+//    2^(m_old - m_new) when the maximum moves;
+//  * P . V: the S^T register layout is the A-operand layout of P (lane =
+//    query), so P needs no transpose.  A key's weight p_t s_v(t) 2^E (2^E a
+//    power of two per key block keeping the weights below 2) is split into
+//    fp16 hi + lo 2^-10; V comes from LDS through the transposing
+//    ds_read_b64_tr_b16 as {64 vh, vl}.  The block's hi and lo products go to
+//    two fresh accumulators (the lo part unscaled, so small weights keep their
+//    residual in fp16's normal range), merged into the output as
+//    out * 2^(m_old - m_new) + (hi + lo 2^-10) * 2^-E.
+#include "heal_internal.h"
+
+namespace heal {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int QW = 16;                // queries per wave
+constexpr int WPB = 4;                // waves per block
+constexpr int QB = QW * WPB;          // queries per block
+constexpr int KB = 64;                // keys per step (= QB: the diagonal is one block)
+constexpr int KTILE = KB * D * 2;     // LDS bytes of one K (or V) tile of codes
+constexpr int STAGE = 2 * KTILE;      // K then V
+constexpr float kLog2eInvSqrtD = 0.12751743074602467f;   // log2(e) / sqrt(128)
+
+typedef short short2v __attribute__((ext_vector_type(2)));
+typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(3))) short4v* lds_s4_ptr;
+
+__device__ __forceinline__ void mfma16(const half8& a, const half8& b, floatx4& c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 8 int16 codes (4 dwords) -> exact fp16 parts 64 (code >> 6) and (code & 63).
+// code >> 6 lies in [-512, 511]: adding the fp16 pattern 0x6600 gives the fp16
+// number 1536 + (code >> 6) in [1024, 2047], where fp16 spacing is 1, and
+// subtracting 1536 leaves it exactly; times 64 stays exact.  code & 63 or'ed
+// into 0x6400 is the fp16 number 1024 + (code & 63).
+__device__ __forceinline__ void unpack8x(const u32x4& raw, half8& hi64, half8& lo) {
+    u32x4 hw, lw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w = raw[i];
+        const short2v t = __builtin_bit_cast(short2v, w) >> (short2v)(short)6;
+        const ushort2v u = __builtin_bit_cast(ushort2v, t) + (ushort2v)(unsigned short)0x6600;
+        const half2v h = (__builtin_bit_cast(half2v, u) - (half2v)(_Float16)1536.0f) * (half2v)(_Float16)64.0f;
+        const half2v l =
+            __builtin_bit_cast(half2v, (w & 0x003F003Fu) | 0x64006400u) - (half2v)(_Float16)1024.0f;
+        hw[i] = __builtin_bit_cast(uint32_t, h);
+        lw[i] = __builtin_bit_cast(uint32_t, l);
+    }
+    hi64 = __builtin_bit_cast(half8, hw);
+    lo = __builtin_bit_cast(half8, lw);
+}
+
+// Reductions over the lanes that share lane % 16 (one query column).
+__device__ __forceinline__ float group_max(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t w = __builtin_bit_cast(uint32_t, x);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t w = __builtin_bit_cast(uint32_t, x);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// x of lane `src` (a lane-index permute; no LDS memory is touched)
+__device__ __forceinline__ float from_lane(float x, int src) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+}
+
+// LDS placement: token row r of a K tile holds its sixteen 16-byte chunks in
+// slots chunk ^ (r % 16), so 16 lanes reading one chunk of 16 rows hit 16
+// distinct slots; a V tile uses chunk ^ 2 (r % 8), which the transposing reads
+// need (as in the decode kernel).
+__device__ __forceinline__ int kswz(int r) { return r & 15; }
+__device__ __forceinline__ int vswz(int r) { return 2 * (r & 7); }
+
+__global__ __launch_bounds__(256) void attn_prefill_kernel(
+    const int16_t* __restrict__ q, const float* __restrict__ qs, const int16_t* __restrict__ k,
+    const float* __restrict__ ks, const int16_t* __restrict__ v, const float* __restrict__ vs,
+    float* __restrict__ out, int T, int Hq, int Hkv, int nqb) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // heavy (late) query blocks first: they see the most keys
+    const int qb = nqb - 1 - (int)(blockIdx.x % nqb);
+    const int h = (int)((blockIdx.x / nqb) % Hq);
+    const int b = (int)(blockIdx.x / ((unsigned)nqb * Hq));
+    const int G = Hq / Hkv;
+    const int gk = h / G;
+    const int c = lane & 15, grp = lane >> 4;
+    const int q0 = qb * QB + wid * QW;          // the wave's first query
+    const int qi = q0 + c;                      // this lane's query column
+    const int nkb = min(qb + 1, (T + KB - 1) / KB);   // key blocks up to the diagonal
+    const uint32_t row_bytes = (uint32_t)Hkv * D * 2;  // bytes between tokens in the cache
+
+    // ---- Q as the B operand: lane (c, grp) holds query qi, d = 32 s + 8 grp + j
+    half8 qh[4], ql[4];
+    {
+        const bool ok = qi < T;
+        const int16_t* qrow = q + (((int64_t)b * T + (ok ? qi : 0)) * Hq + h) * D;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * grp);
+            if (!ok) raw = (u32x4){0u, 0u, 0u, 0u};
+            unpack8x(raw, qh[s], ql[s]);
+        }
+    }
+    const float qscale = qi < T ? qs[((int64_t)b * T + qi) * Hq + h] * kLog2eInvSqrtD : 0.0f;
+
+    // ---- copies of key block kb into LDS stage kb & 1 (4 K and 4 V loads
+    //      per wave, 1 KB each: load i fills token rows 4 i .. 4 i + 3, lane L
+    //      row 4 i + L / 16, slot L % 16); tokens past T read as zero
+    auto copy_block = [&](int kb) {
+        const int t0 = kb * KB;
+        const int nt = __builtin_amdgcn_readfirstlane(min(KB, T - t0));
+        const int64_t tok0 = ((int64_t)b * T + t0) * Hkv + gk;
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + tok0 * D, (uint32_t)nt * row_bytes);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + tok0 * D, (uint32_t)nt * row_bytes);
+        unsigned char* st = lds + (kb & 1) * STAGE;
+        const int r_in = lane >> 4, slot = lane & 15;
+#pragma unroll
+        for (int j = 0; j < KB / 4 / WPB; ++j) {
+            const int i = wid + WPB * j;
+            const int row = 4 * i + r_in;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                krs, (lds_ptr)(st + 1024 * i), 16, (uint32_t)row * row_bytes + 16u * (uint32_t)(slot ^ kswz(row)),
+                0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                vrs, (lds_ptr)(st + KTILE + 1024 * i), 16,
+                (uint32_t)row * row_bytes + 16u * (uint32_t)(slot ^ vswz(row)), 0, 0, 0);
+        }
+    };
+    constexpr int COPIES = 2 * (KB / 4 / WPB);   // VMEM copies per wave per block
+
+    // ---- running softmax state of query column c (the same on its 4 lanes)
+    //      and the output: lane (c, grp) holds d = 16 dt + c of queries
+    //      q0 + 4 grp + e in acc[dt][e]
+    float m_run = -INFINITY, l_run = 0.0f;
+    floatx4 acc[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[dt] = (floatx4){0.f, 0.f, 0.f, 0.f};
+
+    copy_block(0);
+    for (int kb = 0; kb < nkb; ++kb) {
+        // scales of this block's keys where the score layout needs them:
+        // index 4 st + e is key 16 st + 4 grp + e (0 past T)
+        float ksv[16], vsv[16];
+        {
+            const int t0 = kb * KB;
+            const int nt = __builtin_amdgcn_readfirstlane(min(KB, T - t0));
+            const int64_t tok0 = ((int64_t)b * T + t0) * Hkv + gk;
+            const uint32_t srec = (uint32_t)(((nt - 1) * Hkv + 1) * 4);
+            const __amdgpu_buffer_rsrc_t ksrs = make_rsrc(ks + tok0, srec);
+            const __amdgpu_buffer_rsrc_t vsrs = make_rsrc(vs + tok0, srec);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t off = (uint32_t)((16 * (i >> 2) + 4 * grp + (i & 3)) * Hkv * 4);
+                ksv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ksrs, off, 0, 0));
+                vsv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vsrs, off, 0, 0));
+            }
+        }
+        // the next block's copy, then wait for this block's (issued earlier)
+        if (kb + 1 < nkb) {
+            copy_block(kb + 1);
+            __builtin_amdgcn_s_waitcnt((COPIES & 15) | ((COPIES >> 4) << 14) | 0x70 | 0xF00);
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        }
+        __syncthreads();
+        const unsigned char* kt = lds + (kb & 1) * STAGE;
+        const unsigned char* vt = kt + KTILE;
+
+        // ---- scores: sc[4 st + e] for key 16 st + 4 grp + e of the block
+        float sc[16];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            floatx4 s_acc = {0.f, 0.f, 0.f, 0.f};
+            const int row = 16 * st + c;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const u32x4 raw =
+                    *reinterpret_cast<const u32x4*>(kt + row * (D * 2) + 16 * ((4 * s + grp) ^ kswz(row)));
+                half8 kh, kl;
+                unpack8x(raw, kh, kl);
+                mfma16(kh, qh[s], s_acc);
+                mfma16(kh, ql[s], s_acc);
+                mfma16(kl, qh[s], s_acc);
+                mfma16(kl, ql[s], s_acc);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int key = kb * KB + 16 * st + 4 * grp + e;
+                const float mask = (key <= qi && key < T) ? 0.0f : -INFINITY;
+                sc[4 * st + e] = s_acc[e] * (qscale * ksv[4 * st + e]) + mask;
+            }
+        }
+        float mb = sc[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mb = fmaxf(mb, sc[i]);
+        mb = group_max(mb);
+        const float m_new = fmaxf(m_run, mb);
+        const bool live = m_new > -INFINITY;
+        const float alpha = (live && m_run > -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new) : (live ? 0.0f : 1.0f);
+        float p[16], psum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            p[i] = live ? __builtin_amdgcn_exp2f(sc[i] - m_new) : 0.0f;
+            psum += p[i];
+        }
+        l_run = l_run * alpha + group_sum(psum);
+        m_run = m_new;
+
+        // power of two keeping s_v(t) 2^E in [1, 2) over the block's keys (the
+        // whole wave holds all 64 of them)
+        float vmax = vsv[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) vmax = fmaxf(vmax, vsv[i]);
+        vmax = group_max(vmax);   // every lane group of 16 holds the same 16 keys' scales
+        int vexp = 0;
+        (void)frexpf(vmax, &vexp);
+        const float p2 = vmax > 0.0f ? ldexpf(1.0f, 1 - vexp) : 1.0f;
+        const float inv_p2 = vmax > 0.0f ? ldexpf(1.0f, vexp - 1) : 1.0f;
+
+        // ---- P as the A operand for key halves kh2 = 0, 1 (32 keys each):
+        //      slot i = key 32 kh2 + 16 (i / 4) + 4 grp + i % 4; hi and lo 2^-10
+        half8 pa_hi[2], pa_lo[2];
+#pragma unroll
+        for (int kh2 = 0; kh2 < 2; ++kh2)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float w = p[8 * kh2 + i] * vsv[8 * kh2 + i] * p2;
+                _Float16 hh, ll;
+                split_one(w, hh, ll);
+                pa_hi[kh2][i] = hh;
+                pa_lo[kh2][i] = ll;
+            }
+
+        // ---- P . V into a fresh accumulator; V by transposing LDS reads: in
+        //      each 16-lane group, lane 4 j + x supplies the address of 4 d at
+        //      16 dt + 4 x of token row 4 grp + j (+ 16 half + 32 kh2); lane i
+        //      receives d = 16 dt + i of those 4 tokens
+        floatx4 blk[8], blk_l[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            blk[dt] = (floatx4){0.f, 0.f, 0.f, 0.f};
+            blk_l[dt] = (floatx4){0.f, 0.f, 0.f, 0.f};
+        }
+        {
+            const int s16 = lane & 15;
+            const int rr = 4 * grp + (s16 >> 2);
+            const int lane_off = rr * (D * 2) + 16 * ((s16 & 3) >> 1) + 8 * (s16 & 1);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const int off = lane_off + 16 * ((2 * dt) ^ vswz(rr));
+#pragma unroll
+                for (int kh2 = 0; kh2 < 2; ++kh2) {
+                    const short4v lo4 =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(vt + off + (32 * kh2) * (D * 2)));
+                    const short4v hi4 =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(vt + off + (32 * kh2 + 16) * (D * 2)));
+                    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo4), hi2 = __builtin_bit_cast(u32x2, hi4);
+                    const u32x4 raw = {lo2.x, lo2.y, hi2.x, hi2.y};
+                    half8 vh, vl;
+                    unpack8x(raw, vh, vl);
+                    mfma16(pa_hi[kh2], vh, blk[dt]);
+                    mfma16(pa_hi[kh2], vl, blk[dt]);
+                    mfma16(pa_lo[kh2], vh, blk_l[dt]);
+                    mfma16(pa_lo[kh2], vl, blk_l[dt]);
+                }
+            }
+        }
+        // ---- out = out * alpha(query) + (hi + lo / 2^10) / 2^E; lane (c, grp)
+        //      holds the rows of queries 4 grp + e, whose alpha sits on lane 4 grp + e
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a_e = from_lane(alpha, 4 * grp + e);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+                acc[dt][e] = acc[dt][e] * a_e + (blk[dt][e] + blk_l[dt][e] * 0.0009765625f) * inv_p2;
+        }
+        __syncthreads();   // every wave is done with stage kb & 1 before it is refilled
+    }
+
+    // ---- normalize and store: rows q0 + 4 grp + e, d = 16 dt + c
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float l_e = from_lane(l_run, 4 * grp + e);
+        const int qrow = q0 + 4 * grp + e;
+        if (qrow < T) {
+            float* o = out + (((int64_t)b * T + qrow) * Hq + h) * D + c;
+            const float inv = 1.0f / l_e;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) o[16 * dt] = acc[dt][e] * inv;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_prefill(const int16_t* q, const float* qs, const int16_t* k, const float* ks,
+                               const int16_t* v, const float* vs, float* out, int64_t B, int64_t T, int64_t Hq,
+                               int64_t Hkv, int64_t Dd, hipStream_t s) {
+    if (Dd != D) return hipErrorInvalidValue;
+    const int nqb = (int)((T + QB - 1) / QB);
+    const unsigned blocks = (unsigned)(B * Hq * nqb);
+    hipLaunchKernelGGL(attn_prefill_kernel, dim3(blocks), dim3(256), 0, s, q, qs, k, ks, v, vs, out, (int)T,
+                       (int)Hq, (int)Hkv, nqb);
+    return hipGetLastError();
+}
+
+}  // namespace heal

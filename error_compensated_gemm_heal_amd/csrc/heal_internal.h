@@ -110,6 +110,11 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
                               void* workspace, const DecodePlan& plan, uint32_t* status, hipStream_t s);
 
 int64_t attn_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D);
+// Causal self-attention of a prompt: q [B, T, Hq, D], k/v [B, T, Hkv, D] INT16
+// codes with scales [B, T, H]; out fp32 [B, T, Hq, D].
+hipError_t launch_attn_prefill(const int16_t* q, const float* qs, const int16_t* k, const float* ks,
+                               const int16_t* v, const float* vs, float* out, int64_t B, int64_t T, int64_t Hq,
+                               int64_t Hkv, int64_t D, hipStream_t s);
 hipError_t launch_attn_decode(const int16_t* q, const float* qs, const int16_t* k, const float* ks,
                               const int16_t* v, const float* vs, float* out, int64_t B, int64_t T,
                               int64_t Hq, int64_t Hkv, int64_t D, void* workspace, hipStream_t s);

@@ -97,6 +97,16 @@ def qkv(tokens: int, Hq: int, Hkv: int, D: int, seed: int):
     return tuple(out)
 
 
+def attention_prefill_fp32(B: int, T: int, Hq: int, Hkv: int, D: int, seed: int):
+    """Prefill attention inputs before quantization: q [B,T,Hq,D], k and v
+    [B,T,Hkv,D], all ~ N(0,1)."""
+    g = rng(seed)
+    q = normal(g, (B, T, Hq, D))
+    k = normal(g, (B, T, Hkv, D))
+    v = normal(g, (B, T, Hkv, D))
+    return q, k, v
+
+
 def attention_fp32(B: int, T: int, Hq: int, Hkv: int, D: int, seed: int):
     """Decode attention inputs before quantization: q [B,Hq,D], k and v
     [B,T,Hkv,D], all ~ N(0,1)."""

@@ -320,6 +320,26 @@ heal_status heal_attn_decode_i16(const int16_t* q, const float* q_scale,
 
 size_t heal_attn_decode_workspace(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D);
 
+/* ------------------------------------------------------------------------
+ * heal_attn_prefill_i16 -- causal self-attention of a prompt over INT16
+ * Q/K/V with the dual-FP16 expansion.   [INT16]
+ *  For every batch b, query token t and head h (KV head h / (Hq / Hkv)):
+ *    o[b,t,h] = sum_{s <= t} softmax_s(s_q s_k (q . k_s) / sqrt(D)) s_v v_s
+ *  with q, k_s, v_s the INT16 codes and s_* their row scales; codes enter the
+ *  MFMA products as their exact fp16 parts (64 (c >> 6) and c & 63) with fp32
+ *  accumulation, the softmax weights split into fp16 hi + lo, as in
+ *  heal_attn_decode_i16.  Error bar as there.
+ *   q      device int16 [B, T, Hq, D], 16-byte aligned; q_scale fp32 [B, T, Hq]
+ *   k, v   device int16 [B, T, Hkv, D] (the decode cache layout), 16-byte
+ *          aligned; k_scale, v_scale fp32 [B, T, Hkv]
+ *   out    device fp32 [B, T, Hq, D], 4-byte aligned
+ * Limits: D = 128; Hq % Hkv == 0; T <= 262144; T Hkv D 2 < 2^32.  No
+ * workspace.
+ * ------------------------------------------------------------------------ */
+heal_status heal_attn_prefill_i16(const int16_t* q, const float* q_scale, const int16_t* k,
+                                  const float* k_scale, const int16_t* v, const float* v_scale, float* out,
+                                  int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -237,3 +237,29 @@ def attn_decode_f32_naive(q, qs, k, ks, v, vs):
     lib().oracle_attn_decode_f32_naive(_ptr(q), _ptr(qs), _ptr(k), _ptr(ks), _ptr(v), _ptr(vs),
                                        _ptr(out), B, T, Hq, Hkv, D)
     return out
+
+
+def _prefill_positions(q, qs, k, ks, v, vs, positions, fn):
+    """Causal prefill attention = decode attention of query t over keys 0 .. t:
+    q [B,T,Hq,D] + qs [B,T,Hq]; k, v [B,T,Hkv,D] + [B,T,Hkv] -> [B, len(positions), Hq, D]."""
+    q, k, v = _c(q, np.int16), _c(k, np.int16), _c(v, np.int16)
+    qs, ks, vs = _c(qs, np.float32), _c(ks, np.float32), _c(vs, np.float32)
+    outs = []
+    for t in positions:
+        outs.append(fn(q[:, t], qs[:, t], k[:, :t + 1], ks[:, :t + 1], v[:, :t + 1], vs[:, :t + 1]))
+    return np.stack(outs, axis=1)
+
+
+def attn_prefill_f64(q, qs, k, ks, v, vs, positions):
+    """Causal self-attention of a prompt at query positions `positions` (binary64):
+    HEAL paper, section 3, "Mitigating QKV Truncation Error via INT16 Quantization",
+    applied to every prefix; each position is the decode reference over keys 0 .. t."""
+    return _prefill_positions(q, qs, k, ks, v, vs, positions, attn_decode_f64)
+
+
+def attn_prefill_f32_naive(q, qs, k, ks, v, vs, positions):
+    return _prefill_positions(q, qs, k, ks, v, vs, positions, attn_decode_f32_naive)
+
+
+def attn_prefill_weight_norm(q, qs, k, ks, v, vs, positions):
+    return _prefill_positions(q, qs, k, ks, v, vs, positions, attn_decode_weight_norm)

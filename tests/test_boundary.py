@@ -206,6 +206,20 @@ def _attn(B=2, T=16, Hq=8, Hkv=2, D=128, ws=FAKE, wsb=1 << 30, q=FAKE):
     return heal.lib().heal_attn_decode_i16(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, T, Hq, Hkv, D, ws, wsb, None)
 
 
+def test_attention_prefill_validation():
+    f = heal.lib().heal_attn_prefill_i16
+    args = lambda q=FAKE, B=1, T=64, Hq=8, Hkv=2, D=128, o=FAKE: (q, FAKE, FAKE, FAKE, FAKE, FAKE, o, B, T, Hq, Hkv,
+                                                                   D, None)
+    assert f(*args(B=-1)) == SHAPE
+    assert f(*args(T=0, q=None)) == OK
+    assert f(*args(Hkv=3)) == SHAPE
+    assert f(*args(D=64)) == UNSUP
+    assert f(*args(T=262145)) == UNSUP
+    assert f(*args(q=None)) == NULL
+    assert f(*args(q=ctypes.c_void_p(0x10008))) == ALIGN
+    assert f(*args(o=ctypes.c_void_p(0x10002))) == ALIGN
+
+
 def test_attention_validation():
     assert _attn(B=-1) == SHAPE
     assert _attn(B=0, q=None) == OK

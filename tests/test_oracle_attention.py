@@ -84,3 +84,27 @@ def test_f64_and_naive_f32_against_high_precision(B, T, Hq, Hkv, D):
     assert np.all(np.abs(o32 - ref) <= 2e-5 * norm)
     # the normaliser really is sum_t P_t |v_t|: it bounds |o| and equals it for one-signed values
     assert np.all(np.abs(ref) <= norm * (1 + 1e-12))
+
+
+def test_prefill_reference_is_causal_and_matches_decode_at_each_prefix():
+    """Prefill reference (causal self-attention of every position): position 0 is
+    token 0's value row; changing keys or values after position t leaves position t
+    unchanged; the last position is the decode reference over all T tokens."""
+    import heal_workloads as WL
+    B, T, Hq, Hkv, D = 2, 9, 4, 2, 128
+    qf, kf, vf = WL.attention_prefill_fp32(B, T, Hq, Hkv, D, seed=11)
+    q, qs = oracle.quant_i16(qf)
+    k, ks = oracle.quant_i16(kf)
+    v, vs = oracle.quant_i16(vf)
+    pos = list(range(T))
+    o = oracle.attn_prefill_f64(q, qs, k, ks, v, vs, pos)
+    assert o.shape == (B, T, Hq, D)
+    v0 = v[:, 0].astype(np.float64) * vs[:, 0][..., None]          # [B, Hkv, D]
+    assert np.allclose(o[:, 0], np.repeat(v0, Hq // Hkv, axis=1), rtol=1e-15, atol=0)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 5:] = -k2[:, 5:]
+    v2[:, 5:] = 7
+    o2 = oracle.attn_prefill_f64(q, qs, k2, ks, v2, vs, pos)
+    assert np.array_equal(o2[:, :5], o[:, :5]) and not np.array_equal(o2[:, 5:], o[:, 5:])
+    last = oracle.attn_decode_f64(q[:, T - 1], qs[:, T - 1], k, ks, v, vs)
+    assert np.array_equal(o[:, T - 1], last)
