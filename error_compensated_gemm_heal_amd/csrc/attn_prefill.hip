@@ -8,16 +8,19 @@
 // attends keys 0 .. t.
 //
 // Codes split as q = 64 qh + ql, qh = q >> 6 in [-512, 511], ql = q & 63;
-// 64 qh and ql are exact FP16 values, and every product of two such parts is
-// exact in FP32 (at most 2^30, 20 significant bits).
+// qh, 64 qh and ql are exact FP16 values, and every product formed below is
+// exact in FP32 (at most 22 significant bits).
 //
 // One block of 4 waves owns 64 consecutive queries of one (batch, head);
 // wave w takes queries 16 w .. 16 w + 15 of them.  The block walks the key
 // blocks of 64 tokens that its queries can see (causal), K and V of the next
 // block copied into LDS by direct-to-LDS loads while the current one is used:
 //  * scores as S^T = K . Q^T on v_mfma_f32_16x16x32_f16: rows are keys,
-//    columns the wave's 16 queries.  A = {64 kh, kl}, B = {64 qh, ql}: the
-//    four products go into one accumulator, which then holds k . q;
+//    columns the wave's 16 queries.  A = {kh, kl + 1024}, B = {64 qh, ql}: the
+//    kh products go to one accumulator, the biased kl products to a second
+//    one that starts from -1024 sum_d (64 qh + ql) (an MFMA against a constant
+//    -1024 operand, once per wave), and k . q = 64 S_hi + S_lo.  The biased low
+//    half is one bit operation per two codes;
 //  * online softmax in base 2 (log2 e folded into s_q s_k / sqrt(D)): per
 //    query the running maximum, the running sum, and the output rescaled by
 //    2^(m_old - m_new) when the maximum moves;
@@ -25,9 +28,11 @@
 //    query), so P needs no transpose.  A key's weight p_t s_v(t) 2^E (2^E a
 //    power of two per key block keeping the weights below 2) is split into
 //    fp16 hi + lo 2^-10; V comes from LDS through the transposing
-//    ds_read_b64_tr_b16 as {64 vh, vl}.  The block's hi and lo products go to
-//    two fresh accumulators (the lo part unscaled, so small weights keep their
-//    residual in fp16's normal range), merged into the output as
+//    ds_read_b64_tr_b16 as {vh, vl + 1024}, and the 64 of 64 vh rides on the
+//    weights (64 P, exact).  The block's hi and lo weight products go to two
+//    fresh accumulators (the lo part unscaled, so small weights keep their
+//    residual in fp16's normal range), each started from -1024 times its
+//    weight sum to cancel the bias, and are merged into the output as
 //    out * 2^(m_old - m_new) + (hi + lo 2^-10) * 2^-E.
 #include "heal_internal.h"
 
@@ -56,26 +61,41 @@ __device__ __forceinline__ void mfma16(const half8& a, const half8& b, floatx4& 
     c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// 8 int16 codes (4 dwords) -> exact fp16 parts 64 (code >> 6) and (code & 63).
+// 8 int16 codes (4 dwords) -> exact fp16 parts (code >> 6) and (code & 63).
 // code >> 6 lies in [-512, 511]: adding the fp16 pattern 0x6600 gives the fp16
 // number 1536 + (code >> 6) in [1024, 2047], where fp16 spacing is 1, and
-// subtracting 1536 leaves it exactly; times 64 stays exact.  code & 63 or'ed
-// into 0x6400 is the fp16 number 1024 + (code & 63).
-__device__ __forceinline__ void unpack8x(const u32x4& raw, half8& hi64, half8& lo) {
+// subtracting 1536 leaves it exactly.  code & 63 or'ed into 0x6400 is the fp16
+// number 1024 + (code & 63).
+__device__ __forceinline__ void unpack8(const u32x4& raw, half8& hi, half8& lo) {
     u32x4 hw, lw;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t w = raw[i];
         const short2v t = __builtin_bit_cast(short2v, w) >> (short2v)(short)6;
         const ushort2v u = __builtin_bit_cast(ushort2v, t) + (ushort2v)(unsigned short)0x6600;
-        const half2v h = (__builtin_bit_cast(half2v, u) - (half2v)(_Float16)1536.0f) * (half2v)(_Float16)64.0f;
-        const half2v l =
-            __builtin_bit_cast(half2v, (w & 0x003F003Fu) | 0x64006400u) - (half2v)(_Float16)1024.0f;
-        hw[i] = __builtin_bit_cast(uint32_t, h);
-        lw[i] = __builtin_bit_cast(uint32_t, l);
+        hw[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, u) - (half2v)(_Float16)1536.0f);
+        lw[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, (w & 0x003F003Fu) | 0x64006400u) -
+                                                 (half2v)(_Float16)1024.0f);
     }
-    hi64 = __builtin_bit_cast(half8, hw);
+    hi = __builtin_bit_cast(half8, hw);
     lo = __builtin_bit_cast(half8, lw);
+}
+// The same high halves; the low halves left biased, as the fp16 numbers
+// 1024 + (code & 63), in one bit operation ((w & 0x003F003F) | 0x64006400).
+// A product chain over biased low halves starts from -1024 times the sum of
+// the other operand, which removes the bias; every product stays exact.
+__device__ __forceinline__ void unpack8_lobias(const u32x4& raw, half8& hi, half8& lob) {
+    u32x4 hw, lw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w = raw[i];
+        const short2v t = __builtin_bit_cast(short2v, w) >> (short2v)(short)6;
+        const ushort2v u = __builtin_bit_cast(ushort2v, t) + (ushort2v)(unsigned short)0x6600;
+        hw[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, u) - (half2v)(_Float16)1536.0f);
+        lw[i] = __builtin_amdgcn_bitop3_b32(w, 0x003F003Fu, 0x64006400u, 0xEA);   // (w & m) | b
+    }
+    hi = __builtin_bit_cast(half8, hw);
+    lob = __builtin_bit_cast(half8, lw);
 }
 
 // Reductions over the lanes that share lane % 16 (one query column).
@@ -135,7 +155,19 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
         for (int s = 0; s < 4; ++s) {
             u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * grp);
             if (!ok) raw = (u32x4){0u, 0u, 0u, 0u};
-            unpack8x(raw, qh[s], ql[s]);
+            half8 hi;
+            unpack8(raw, hi, ql[s]);
+            qh[s] = hi * (_Float16)64.0f;   // exact: |64 qh| <= 32768
+        }
+    }
+    // start of the biased kl chains: -1024 sum_d (64 qh + ql) of query column c
+    floatx4 qbias = {0.f, 0.f, 0.f, 0.f};
+    {
+        const half8 m1024 = (half8)(_Float16)-1024.0f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            mfma16(m1024, qh[s], qbias);
+            mfma16(m1024, ql[s], qbias);
         }
     }
     const float qscale = qi < T ? qs[((int64_t)b * T + qi) * Hq + h] * kLog2eInvSqrtD : 0.0f;
@@ -207,24 +239,24 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
         float sc[16];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            floatx4 s_acc = {0.f, 0.f, 0.f, 0.f};
+            floatx4 s_hi = {0.f, 0.f, 0.f, 0.f}, s_lo = qbias;
             const int row = 16 * st + c;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const u32x4 raw =
                     *reinterpret_cast<const u32x4*>(kt + row * (D * 2) + 16 * ((4 * s + grp) ^ kswz(row)));
-                half8 kh, kl;
-                unpack8x(raw, kh, kl);
-                mfma16(kh, qh[s], s_acc);
-                mfma16(kh, ql[s], s_acc);
-                mfma16(kl, qh[s], s_acc);
-                mfma16(kl, ql[s], s_acc);
+                half8 kh, klb;
+                unpack8_lobias(raw, kh, klb);
+                mfma16(kh, qh[s], s_hi);
+                mfma16(kh, ql[s], s_hi);
+                mfma16(klb, qh[s], s_lo);
+                mfma16(klb, ql[s], s_lo);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int key = kb * KB + 16 * st + 4 * grp + e;
                 const float mask = (key <= qi && key < T) ? 0.0f : -INFINITY;
-                sc[4 * st + e] = s_acc[e] * (qscale * ksv[4 * st + e]) + mask;
+                sc[4 * st + e] = (64.0f * s_hi[e] + s_lo[e]) * (qscale * ksv[4 * st + e]) + mask;
             }
         }
         float mb = sc[0];
@@ -256,9 +288,9 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
 
         // ---- P as the A operand for key halves kh2 = 0, 1 (32 keys each):
         //      slot i = key 32 kh2 + 16 (i / 4) + 4 grp + i % 4; hi and lo 2^-10
-        half8 pa_hi[2], pa_lo[2];
+        half8 pa_hi[2], pa_lo[2], pa_hi64[2], pa_lo64[2];
 #pragma unroll
-        for (int kh2 = 0; kh2 < 2; ++kh2)
+        for (int kh2 = 0; kh2 < 2; ++kh2) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float w = p[8 * kh2 + i] * vsv[8 * kh2 + i] * p2;
@@ -267,16 +299,29 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
                 pa_hi[kh2][i] = hh;
                 pa_lo[kh2][i] = ll;
             }
+            pa_hi64[kh2] = pa_hi[kh2] * (_Float16)64.0f;   // exact (|w| < 2)
+            pa_lo64[kh2] = pa_lo[kh2] * (_Float16)64.0f;
+        }
 
         // ---- P . V into a fresh accumulator; V by transposing LDS reads: in
         //      each 16-lane group, lane 4 j + x supplies the address of 4 d at
         //      16 dt + 4 x of token row 4 grp + j (+ 16 half + 32 kh2); lane i
         //      receives d = 16 dt + i of those 4 tokens
+        // the biased vl chains start from -1024 times the block's weight sums
+        floatx4 bias_h = {0.f, 0.f, 0.f, 0.f}, bias_l = {0.f, 0.f, 0.f, 0.f};
+        {
+            const half8 m1024 = (half8)(_Float16)-1024.0f;
+#pragma unroll
+            for (int kh2 = 0; kh2 < 2; ++kh2) {
+                mfma16(pa_hi[kh2], m1024, bias_h);
+                mfma16(pa_lo[kh2], m1024, bias_l);
+            }
+        }
         floatx4 blk[8], blk_l[8];
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-            blk[dt] = (floatx4){0.f, 0.f, 0.f, 0.f};
-            blk_l[dt] = (floatx4){0.f, 0.f, 0.f, 0.f};
+            blk[dt] = bias_h;
+            blk_l[dt] = bias_l;
         }
         {
             const int s16 = lane & 15;
@@ -293,12 +338,12 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
                         __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(vt + off + (32 * kh2 + 16) * (D * 2)));
                     const u32x2 lo2 = __builtin_bit_cast(u32x2, lo4), hi2 = __builtin_bit_cast(u32x2, hi4);
                     const u32x4 raw = {lo2.x, lo2.y, hi2.x, hi2.y};
-                    half8 vh, vl;
-                    unpack8x(raw, vh, vl);
-                    mfma16(pa_hi[kh2], vh, blk[dt]);
-                    mfma16(pa_hi[kh2], vl, blk[dt]);
-                    mfma16(pa_lo[kh2], vh, blk_l[dt]);
-                    mfma16(pa_lo[kh2], vl, blk_l[dt]);
+                    half8 vh, vlb;
+                    unpack8_lobias(raw, vh, vlb);
+                    mfma16(pa_hi64[kh2], vh, blk[dt]);
+                    mfma16(pa_hi[kh2], vlb, blk[dt]);
+                    mfma16(pa_lo64[kh2], vh, blk_l[dt]);
+                    mfma16(pa_lo[kh2], vlb, blk_l[dt]);
                 }
             }
         }
