@@ -21,7 +21,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
@@ -29,21 +28,49 @@ FLAGS = [
 ]
 
 
+# per-source additions: the prefill attention kernel keeps its MFMA accumulators
+# in ordinary VGPRs (no AGPR round trip before the softmax and rescale math)
+PER_SOURCE = {
+    "attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, *sources(), "-o", tmp]
+def _compile(src: str, obj: str, extra, verbose: bool):
+    cmd = [HIPCC, *FLAGS, *extra, *PER_SOURCE.get(os.path.basename(src), []), "-I", INCLUDE, "-I", CSRC, "-c",
+           src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libheal.so")
-    if verbose and r.stderr.strip():
-        sys.stderr.write(r.stderr)
+    return subprocess.run(cmd, capture_output=True, text=True)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile each source to an object (in parallel), then link the shared
+    library.  Every object carries its own gfx950 code object."""
+    import concurrent.futures
+    import tempfile
+    tmp = LIB + ".tmp"
+    with tempfile.TemporaryDirectory(prefix="heal_build_") as td:
+        srcs = sources()
+        objs = [os.path.join(td, os.path.basename(s) + ".o") for s in srcs]
+        with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+            results = list(ex.map(lambda so: _compile(so[0], so[1], extra, verbose), zip(srcs, objs)))
+        for src, r in zip(srcs, results):
+            if r.returncode != 0:
+                sys.stderr.write(r.stdout + r.stderr)
+                raise RuntimeError(f"hipcc failed compiling {os.path.basename(src)}")
+            if verbose and r.stderr.strip():
+                sys.stderr.write(r.stderr)
+        cmd = [HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError("hipcc failed linking libheal.so")
     os.replace(tmp, LIB)
     return LIB
 

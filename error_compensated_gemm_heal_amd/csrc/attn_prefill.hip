@@ -34,6 +34,8 @@
 //    residual in fp16's normal range), each started from -1024 times its
 //    weight sum to cancel the bias, and are merged into the output as
 //    out * 2^(m_old - m_new) + (hi + lo 2^-10) * 2^-E.
+#include <type_traits>
+
 #include "heal_internal.h"
 
 namespace heal {
@@ -130,14 +132,16 @@ __device__ __forceinline__ int vswz(int r) { return 2 * (r & 7); }
 __global__ __launch_bounds__(256) void attn_prefill_kernel(
     const int16_t* __restrict__ q, const float* __restrict__ qs, const int16_t* __restrict__ k,
     const float* __restrict__ ks, const int16_t* __restrict__ v, const float* __restrict__ vs,
-    float* __restrict__ out, int T, int Hq, int Hkv, int nqb) {
+    float* __restrict__ out, int T, int Hq, int Hkv, int nqb, int nbh) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // heavy (late) query blocks first: they see the most keys
-    const int qb = nqb - 1 - (int)(blockIdx.x % nqb);
-    const int h = (int)((blockIdx.x / nqb) % Hq);
-    const int b = (int)(blockIdx.x / ((unsigned)nqb * Hq));
+    // heavy (late) query blocks first over all (batch, head) pairs: they see
+    // the most keys, and the light ones fill the tail
+    const int bh = (int)(blockIdx.x % nbh);
+    const int qb = nqb - 1 - (int)(blockIdx.x / nbh);
+    const int h = bh % Hq;
+    const int b = bh / Hq;
     const int G = Hq / Hkv;
     const int gk = h / G;
     const int c = lane & 15, grp = lane >> 4;
@@ -205,8 +209,9 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[dt] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
-    copy_block(0);
-    for (int kb = 0; kb < nkb; ++kb) {
+    // one key block; only the last one (the diagonal, or the ragged end of the
+    // prompt) has keys a query of this block may not see
+    auto key_block = [&](int kb, auto masked) {
         // scales of this block's keys where the score layout needs them:
         // index 4 st + e is key 16 st + 4 grp + e (0 past T)
         float ksv[16], vsv[16];
@@ -254,9 +259,11 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int key = kb * KB + 16 * st + 4 * grp + e;
-                const float mask = (key <= qi && key < T) ? 0.0f : -INFINITY;
-                sc[4 * st + e] = (64.0f * s_hi[e] + s_lo[e]) * (qscale * ksv[4 * st + e]) + mask;
+                sc[4 * st + e] = (64.0f * s_hi[e] + s_lo[e]) * (qscale * ksv[4 * st + e]);
+                if constexpr (decltype(masked)::value) {
+                    const int key = kb * KB + 16 * st + 4 * grp + e;
+                    if (!(key <= qi && key < T)) sc[4 * st + e] = -INFINITY;
+                }
             }
         }
         float mb = sc[0];
@@ -264,12 +271,15 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
         for (int i = 1; i < 16; ++i) mb = fmaxf(mb, sc[i]);
         mb = group_max(mb);
         const float m_new = fmaxf(m_run, mb);
-        const bool live = m_new > -INFINITY;
-        const float alpha = (live && m_run > -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new) : (live ? 0.0f : 1.0f);
+        // m_new is finite: every key of an unmasked block is visible, and the
+        // first key of the last block is visible to every query of the block
+        // (and lies before T).  exp2(-inf) = 0 covers the first block's alpha
+        // and the masked scores.
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         float p[16], psum = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            p[i] = live ? __builtin_amdgcn_exp2f(sc[i] - m_new) : 0.0f;
+            p[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
             psum += p[i];
         }
         l_run = l_run * alpha + group_sum(psum);
@@ -287,42 +297,47 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
         const float inv_p2 = vmax > 0.0f ? ldexpf(1.0f, vexp - 1) : 1.0f;
 
         // ---- P as the A operand for key halves kh2 = 0, 1 (32 keys each):
-        //      slot i = key 32 kh2 + 16 (i / 4) + 4 grp + i % 4; hi and lo 2^-10
-        half8 pa_hi[2], pa_lo[2], pa_hi64[2], pa_lo64[2];
+        //      slot i = key 32 kh2 + 16 (i / 4) + 4 grp + i % 4.  w = hi + lo 2^-10
+        //      enters one accumulator as 2^8 hi + 2^-2 lo = 2^8 w (hi 2^8 < 2^9,
+        //      the lo part 2^-2 keeps its residual down to w ~ 2^-22 in normal
+        //      range); with V's parts v = 64 vh + vl, the operands are 2^14 hi and
+        //      2^4 lo against vh, 2^8 hi and 2^-2 lo against vl.  All scalings are
+        //      exact.
+        half8 pa_h8[2], pa_l2[2], pa_h14[2], pa_l4[2];
 #pragma unroll
         for (int kh2 = 0; kh2 < 2; ++kh2) {
+            half8 hh8, ll8;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float w = p[8 * kh2 + i] * vsv[8 * kh2 + i] * p2;
                 _Float16 hh, ll;
                 split_one(w, hh, ll);
-                pa_hi[kh2][i] = hh;
-                pa_lo[kh2][i] = ll;
+                hh8[i] = hh;
+                ll8[i] = ll;
             }
-            pa_hi64[kh2] = pa_hi[kh2] * (_Float16)64.0f;   // exact (|w| < 2)
-            pa_lo64[kh2] = pa_lo[kh2] * (_Float16)64.0f;
+            pa_h8[kh2] = hh8 * (_Float16)256.0f;
+            pa_h14[kh2] = hh8 * (_Float16)16384.0f;   // < 2^15
+            pa_l2[kh2] = ll8 * (_Float16)0.25f;
+            pa_l4[kh2] = ll8 * (_Float16)16.0f;
         }
 
         // ---- P . V into a fresh accumulator; V by transposing LDS reads: in
         //      each 16-lane group, lane 4 j + x supplies the address of 4 d at
         //      16 dt + 4 x of token row 4 grp + j (+ 16 half + 32 kh2); lane i
         //      receives d = 16 dt + i of those 4 tokens
-        // the biased vl chains start from -1024 times the block's weight sums
-        floatx4 bias_h = {0.f, 0.f, 0.f, 0.f}, bias_l = {0.f, 0.f, 0.f, 0.f};
+        // the biased vl products start from -1024 times the block's weight sums
+        floatx4 bias = {0.f, 0.f, 0.f, 0.f};
         {
             const half8 m1024 = (half8)(_Float16)-1024.0f;
 #pragma unroll
             for (int kh2 = 0; kh2 < 2; ++kh2) {
-                mfma16(pa_hi[kh2], m1024, bias_h);
-                mfma16(pa_lo[kh2], m1024, bias_l);
+                mfma16(pa_h8[kh2], m1024, bias);
+                mfma16(pa_l2[kh2], m1024, bias);
             }
         }
-        floatx4 blk[8], blk_l[8];
+        floatx4 blk[8];
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            blk[dt] = bias_h;
-            blk_l[dt] = bias_l;
-        }
+        for (int dt = 0; dt < 8; ++dt) blk[dt] = bias;
         {
             const int s16 = lane & 15;
             const int rr = 4 * grp + (s16 >> 2);
@@ -340,24 +355,27 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
                     const u32x4 raw = {lo2.x, lo2.y, hi2.x, hi2.y};
                     half8 vh, vlb;
                     unpack8_lobias(raw, vh, vlb);
-                    mfma16(pa_hi64[kh2], vh, blk[dt]);
-                    mfma16(pa_hi[kh2], vlb, blk[dt]);
-                    mfma16(pa_lo64[kh2], vh, blk_l[dt]);
-                    mfma16(pa_lo[kh2], vlb, blk_l[dt]);
+                    mfma16(pa_h14[kh2], vh, blk[dt]);
+                    mfma16(pa_h8[kh2], vlb, blk[dt]);
+                    mfma16(pa_l4[kh2], vh, blk[dt]);
+                    mfma16(pa_l2[kh2], vlb, blk[dt]);
                 }
             }
         }
-        // ---- out = out * alpha(query) + (hi + lo / 2^10) / 2^E; lane (c, grp)
-        //      holds the rows of queries 4 grp + e, whose alpha sits on lane 4 grp + e
+        // ---- out = out * alpha(query) + blk 2^-8 / 2^E; lane (c, grp) holds the
+        //      rows of queries 4 grp + e, whose alpha sits on lane 4 grp + e
+        const float bscale = inv_p2 * 0.00390625f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float a_e = from_lane(alpha, 4 * grp + e);
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-                acc[dt][e] = acc[dt][e] * a_e + (blk[dt][e] + blk_l[dt][e] * 0.0009765625f) * inv_p2;
+            for (int dt = 0; dt < 8; ++dt) acc[dt][e] = acc[dt][e] * a_e + blk[dt][e] * bscale;
         }
         __syncthreads();   // every wave is done with stage kb & 1 before it is refilled
-    }
+    };
+    copy_block(0);
+    for (int kb = 0; kb + 1 < nkb; ++kb) key_block(kb, std::false_type{});
+    key_block(nkb - 1, std::true_type{});
 
     // ---- normalize and store: rows q0 + 4 grp + e, d = 16 dt + c
 #pragma unroll
@@ -382,7 +400,7 @@ hipError_t launch_attn_prefill(const int16_t* q, const float* qs, const int16_t*
     const int nqb = (int)((T + QB - 1) / QB);
     const unsigned blocks = (unsigned)(B * Hq * nqb);
     hipLaunchKernelGGL(attn_prefill_kernel, dim3(blocks), dim3(256), 0, s, q, qs, k, ks, v, vs, out, (int)T,
-                       (int)Hq, (int)Hkv, nqb);
+                       (int)Hq, (int)Hkv, nqb, (int)(B * Hq));
     return hipGetLastError();
 }
 

@@ -67,6 +67,28 @@ def test_attn_prefill_peaked_scores():
     _check(B, T, Hq, Hkv, seed=0, inputs=(q, qs, k, ks, v, vs))
 
 
+def test_attn_prefill_flat_scores_give_prefix_means():
+    """Every key the same row: the weights of query t are uniform over keys
+    0 .. t, so its output is the mean of the dequantized values of its prefix."""
+    B, T, Hq, Hkv = 1, 150, 4, 1
+    q, qs, k, ks, v, vs = _inputs(B, T, Hq, Hkv, seed=21)
+    k = np.broadcast_to(k[:, :1], k.shape).copy()
+    ks = np.broadcast_to(ks[:, :1], ks.shape).copy()
+    o = _check(B, T, Hq, Hkv, seed=0, inputs=(q, qs, k, ks, v, vs))
+    vt = v.astype(np.float64) * vs.astype(np.float64)[..., None]           # [B, T, Hkv, D]
+    means = np.cumsum(vt, axis=1) / np.arange(1, T + 1)[None, :, None, None]
+    scale = np.cumsum(np.abs(vt), axis=1) / np.arange(1, T + 1)[None, :, None, None]
+    for h in range(Hq):
+        err = np.abs(o[:, :, h] - means[:, :, 0]) / scale[:, :, 0]
+        assert err.max() <= 1e-5, (h, err.max())
+
+
+def test_attn_prefill_full_size_sampled_positions():
+    """The measured shape (one 2048-token prompt, 32 query / 8 KV heads), sampled
+    query positions against the binary64 oracle."""
+    _check(1, 2048, 32, 8, seed=5500)
+
+
 def test_attn_prefill_pipeline_with_gpu_quantizer_and_last_position_equals_decode():
     """GPU quantizer -> prefill attention; its last position equals decode attention
     of the same query over the same cache within the tolerance of each."""
