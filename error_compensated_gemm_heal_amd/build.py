@@ -28,10 +28,12 @@ FLAGS = [
 ]
 
 
-# per-source additions: the prefill attention kernel keeps its MFMA accumulators
-# in ordinary VGPRs (no AGPR round trip before the softmax and rescale math)
+# per-source additions: the attention kernels keep their MFMA accumulators in
+# ordinary VGPRs (no AGPR round trip before the softmax and rescale math, and
+# fewer registers in all)
 PER_SOURCE = {
     "attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "attn_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
