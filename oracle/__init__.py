@@ -168,6 +168,61 @@ def gemm_f16_plain_rows(A, W, rows, w_layout="nk"):
     return gemm_f64_rows(Ah, Wh, rows, w_layout), gemm_f32_naive_rows(Ah, Wh, rows, w_layout)
 
 
+# --- BF16 three-way split (precision mode) ---------------------------------------
+#
+# A precision-mode variant of the same compensation (HEAL paper, section 3,
+# "Mitigating GEMM Truncation via FP16 Promotion and Algebraic Compensation":
+# an fp32 operand written as a sum of 16-bit parts, products accumulated in
+# fp32).  bfloat16 keeps fp32's exponent range with 8 significant bits, so three
+# parts are needed to hold an fp32 significand.
+
+def round_bf16(x):
+    """Values rounded to bfloat16 (8 significant bits, exponent range of
+    binary32, subnormal quantum 2^-133), to nearest with ties to even; returned
+    exactly as float64.  From the format's definition: the value is scaled by a
+    power of two so that its kept bits form the integer part, rounded by
+    numpy's rint (ties to even) and scaled back; results at or above 2^128 in
+    magnitude overflow to infinity."""
+    x = np.asarray(x, np.float64)
+    out = x.copy()
+    fin = np.isfinite(x) & (x != 0)
+    xf = x[fin]
+    _, e = np.frexp(xf)                    # |x| in [2^(e-1), 2^e)
+    q = np.maximum(e - 8, -133)            # quantum of 8 significant bits, or the subnormal one
+    y = np.ldexp(np.rint(np.ldexp(xf, -q)), q)
+    y = np.where(np.abs(y) >= 2.0 ** 128, np.copysign(np.inf, xf), y)
+    out[fin] = y
+    return out
+
+
+def split_bf16x3(x):
+    """x (float32) -> (b0, b1, b2) float64 with b0 = bf16(x), b1 = bf16(x - b0),
+    b2 = bf16(x - b0 - b1); the residuals are exact, and the parts sum to x
+    exactly while the last one stays a normal bf16 (|x| above about 2^-110)."""
+    x = np.asarray(x, np.float32).astype(np.float64)
+    b0 = round_bf16(x)
+    r1 = x - b0
+    b1 = round_bf16(r1)
+    b2 = round_bf16(r1 - b1)
+    return b0, b1, b2
+
+
+def gemm_bf16x3_model(A, W, w_layout="nk"):
+    """The six-product BF16 GEMM: sum over i + j <= 2 of A_i . B_j, in binary64
+    (products of bf16 parts are exact).  A GPU run differs from it by its fp32
+    accumulation only.  B = W^T ('nk') or W ('kn')."""
+    A = np.asarray(A, np.float32)
+    B = np.asarray(W, np.float32)
+    B = B.T if w_layout == "nk" else B
+    a = split_bf16x3(A)
+    b = split_bf16x3(B)
+    C = np.zeros((A.shape[0], B.shape[1]), np.float64)
+    for i in range(3):
+        for j in range(3 - i):
+            C += a[i] @ b[j]
+    return C
+
+
 # --- INT16 quant / dequant ----------------------------------------------------
 
 def quant_i16(X):
