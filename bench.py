@@ -11,6 +11,8 @@ workload (inputs resident in HBM before timing starts):
            once: the two-product form (2 of the 3 MFMA products)
   prefill_1p  the same GEMMs in the one-product mode (plain FP16, no
            compensation): the cost the compensation is measured against
+  prefill_bf16x3  the same GEMMs in the BF16 three-way precision mode (six
+           BF16 products; operands packed in that form beforehand)
   decode   16 compensated GEMMs of a Llama-3-8B-like layer: M = 1, 8, 32, 64
            x (K,N) in {(4096,4096), (4096,1024), (4096,14336), (14336,4096)},
            fp32 weights streamed from HBM (M-outer order, so consecutive calls
@@ -75,7 +77,7 @@ def build_workload(rows_sel):
     W = {}
     t0 = time.time()
 
-    if any(r in rows_sel for r in ("split", "prefill", "prefill_w16", "prefill_1p")):
+    if any(r in rows_sel for r in ("split", "prefill", "prefill_w16", "prefill_1p", "prefill_bf16x3")):
         pre = []
         for i, (K, N) in enumerate(WL.PREFILL_KN):
             A, Wt = WL.prefill_gemm(WL.PREFILL_M, K, N, seed=3000 + i)
@@ -85,8 +87,11 @@ def build_workload(rows_sel):
             # the same weight as binary16 (an FP16 checkpoint), packed once
             Wp16 = heal.heal_pack_w(Wd.half()) if "prefill_w16" in rows_sel else None
             Ap = heal.heal_pack_w(Ad)                                  # output buffer of the split row
+            x3 = "prefill_bf16x3" in rows_sel
+            Wp3 = heal.heal_pack_w(Wd, bf16x3=True) if x3 else None
+            Ap3 = heal.heal_pack_w(Ad, bf16x3=True) if x3 else None
             C = torch.empty((WL.PREFILL_M, N), dtype=torch.float32, device=dev)
-            pre.append(dict(M=WL.PREFILL_M, K=K, N=N, A=Ad, Ap=Ap, Wp=Wp, Wp16=Wp16, C=C))
+            pre.append(dict(M=WL.PREFILL_M, K=K, N=N, A=Ad, Ap=Ap, Wp=Wp, Wp16=Wp16, Ap3=Ap3, Wp3=Wp3, C=C))
             del A, Wt, Wd
         W["prefill"] = pre
         log(f"[bench] prefill inputs ready ({time.time() - t0:.1f}s)")
@@ -224,6 +229,12 @@ def make_rows(W):
                 heal.heal_gemm_f32c(p["Ap"], p["Wp"], C=p["C"], one_product=True)
 
         rows.append(("prefill_1p", run_prefill1, useful, "flop"))
+        if pre[0]["Wp3"] is not None:
+            def run_prefill3():
+                for p in pre:
+                    heal.heal_gemm_f32c(p["Ap3"], p["Wp3"], C=p["C"], bf16x3=True)
+
+            rows.append(("prefill_bf16x3", run_prefill3, useful, "flop"))
     if "decode" in W:
         calls = W["decode"]
 
@@ -309,7 +320,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--rows", default="split,prefill,prefill_w16,prefill_1p,decode,decode_w16,decode_kshift,"
+    ap.add_argument("--rows", default="split,prefill,prefill_w16,prefill_1p,prefill_bf16x3,decode,decode_w16,decode_kshift,"
                                       "qkv_proj,quant,dequant,attn_prefill,attn",
                     help="comma-separated subset of rows to run (profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -16,7 +16,7 @@ __all__ = [
     "heal_gemm_f32c_workspace", "heal_pack_w", "heal_pack_w_bytes", "heal_qkv_quant_i16",
     "heal_kv_dequant_i16", "heal_attn_decode_i16", "heal_attn_decode_workspace", "PackedOperand",
     "heal_scale_k", "heal_kshift_from_absmax",
-    "PackedWeight", "HEAL_W_NK", "HEAL_W_KN", "HEAL_W_PACKED", "HEAL_A_PACKED", "HEAL_W_F16", "HEAL_ONE_PRODUCT",
+    "PackedWeight", "HEAL_W_NK", "HEAL_W_KN", "HEAL_W_PACKED", "HEAL_A_PACKED", "HEAL_W_F16", "HEAL_ONE_PRODUCT", "HEAL_BF16X3",
     "HEAL_FLAG_F16_RANGE", "HEAL_FLAG_SLOT_RANGE", "heal_qkv_proj_quant_i16", "heal_qkv_proj_quant_workspace",
     "heal_attn_prefill_i16",
     "HEAL_DQ_F32", "HEAL_DQ_F16X2",
@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libheal.so"
 
 HEAL_OK = 0
 HEAL_W_NK, HEAL_W_KN, HEAL_W_PACKED, HEAL_A_PACKED, HEAL_W_F16, HEAL_ONE_PRODUCT = 0, 1, 2, 4, 8, 16
+HEAL_BF16X3 = 32
 HEAL_FLAG_F16_RANGE = 1
 HEAL_FLAG_SLOT_RANGE = 2
 HEAL_DQ_F32, HEAL_DQ_F16X2 = 0, 1
@@ -141,10 +142,11 @@ class PackedOperand:
     """An operand of `rows` x K split once into the GEMM's packed dual-FP16 form
     (opaque buffer): a weight (rows = N) or an activation (rows = M)."""
 
-    def __init__(self, buf: torch.Tensor, rows: int, K: int, f16: bool = False):
+    def __init__(self, buf: torch.Tensor, rows: int, K: int, f16: bool = False, bf16x3: bool = False):
         # f16: packed from binary16 weights (zero lo planes): GEMMs take the
-        # two-product form (HEAL_W_PACKED | HEAL_W_F16)
-        self.buf, self.rows, self.K, self.f16 = buf, rows, K, f16
+        # two-product form (HEAL_W_PACKED | HEAL_W_F16).  bf16x3: the BF16
+        # three-way form, for GEMMs in that mode only.
+        self.buf, self.rows, self.K, self.f16, self.bf16x3 = buf, rows, K, f16, bf16x3
 
     @property
     def N(self):
@@ -177,12 +179,14 @@ def _kshift(kshift, K: int, name: str):
     return kshift
 
 
-def heal_pack_w(W: torch.Tensor, w_layout: str = "nk", dev_status=None, out=None, kshift=None) -> PackedOperand:
+def heal_pack_w(W: torch.Tensor, w_layout: str = "nk", dev_status=None, out=None, kshift=None,
+                bf16x3: bool = False) -> PackedOperand:
     """Split an operand once into the packed form.  kshift (int8 [K], optional):
     element (r, k) is multiplied by 2^-kshift[k] first (an activation takes the
-    shifts given to heal_gemm_f32c as a_kshift, a weight their negation)."""
+    shifts given to heal_gemm_f32c as a_kshift, a weight their negation).
+    bf16x3: the BF16 three-way form (fp32 input, no kshift)."""
     _dev(W, "W")
-    flags = (HEAL_W_KN if w_layout == "kn" else HEAL_W_NK) | _weight_dtype_flag(W)
+    flags = (HEAL_W_KN if w_layout == "kn" else HEAL_W_NK) | _weight_dtype_flag(W) | (HEAL_BF16X3 if bf16x3 else 0)
     if w_layout == "kn":
         K, N = W.shape
     else:
@@ -198,7 +202,7 @@ def heal_pack_w(W: torch.Tensor, w_layout: str = "nk", dev_status=None, out=None
     ks = _kshift(kshift, K, "kshift")
     _check("heal_pack_w", lib().heal_pack_w(_ptr(W), ldw, N, K, flags, _ptr(ks), _ptr(buf), nbytes,
                                             _ptr(dev_status), _stream()))
-    return PackedOperand(buf, N, K, f16=bool(flags & HEAL_W_F16))
+    return PackedOperand(buf, N, K, f16=bool(flags & HEAL_W_F16), bf16x3=bool(bf16x3))
 
 
 def heal_gemm_f32c_workspace(M: int, N: int, K: int, flags: int) -> int:
@@ -206,12 +210,17 @@ def heal_gemm_f32c_workspace(M: int, N: int, K: int, flags: int) -> int:
 
 
 def heal_gemm_f32c(A, W, w_layout: str = "nk", C=None, workspace=None, dev_status=None, a_kshift=None,
-                   one_product: bool = False):
+                   one_product: bool = False, bf16x3: bool = False):
     """C = A . B with B = W^T ('nk', W [N,K]) or B = W ('kn', W [K,N]).
     A and/or W may be PackedOperand buffers from heal_pack_w.  a_kshift (int8
     [K], optional): A's element (m, k) is multiplied by 2^-a_kshift[k] before
     its split; W must hold reduction index k multiplied by 2^+a_kshift[k].
-    one_product: plain FP16, C = A_hi.B_hi (no compensation)."""
+    one_product: plain FP16, C = A_hi.B_hi (no compensation).  bf16x3: the
+    BF16 three-way split with six products (packed operands must be packed in
+    that form)."""
+    for X, name in ((A, "A"), (W, "W")):
+        if isinstance(X, PackedOperand) and X.bf16x3 != bool(bf16x3):
+            raise ValueError(f"packed {name} was packed {'with' if X.bf16x3 else 'without'} bf16x3")
     aflags = 0
     if isinstance(A, PackedOperand):
         M, K, lda, aptr, adev, aflags = A.rows, A.K, 0, _ptr(A.buf), A.buf.device, HEAL_A_PACKED
@@ -235,7 +244,7 @@ def heal_gemm_f32c(A, W, w_layout: str = "nk", C=None, workspace=None, dev_statu
         if K2 != K:
             raise ValueError("inner dimensions differ")
         wptr, ldw = _ptr(W), _rowmajor_ld(W, "W")
-    flags |= aflags | (HEAL_ONE_PRODUCT if one_product else 0)
+    flags |= aflags | (HEAL_ONE_PRODUCT if one_product else 0) | (HEAL_BF16X3 if bf16x3 else 0)
     if C is None:
         C = torch.empty((M, N), dtype=torch.float32, device=adev)
     ldc = _rowmajor_ld(C, "C") if M > 0 and N > 0 else N

@@ -21,8 +21,13 @@ heal_status hip_status(hipError_t e) { return e == hipSuccess ? HEAL_OK : HEAL_E
 // The decode kernel addresses its split activation (256 bytes per k) and
 // each 16-row slice of W with 32-bit byte offsets.
 bool use_decode(int64_t M, int64_t K, uint32_t flags) {
-    return M <= 64 && K < ((int64_t)1 << 23) && !(flags & (HEAL_W_PACKED | HEAL_A_PACKED)) &&
+    return M <= 64 && K < ((int64_t)1 << 23) && !(flags & (HEAL_W_PACKED | HEAL_A_PACKED | HEAL_BF16X3)) &&
            (flags & HEAL_W_KN) == 0;
+}
+// bytes of one packed operand in the form the flags select
+int64_t packed_bytes(int64_t R, int64_t K, uint32_t flags) {
+    if (flags & HEAL_BF16X3) return pack_bytes_x3(R, K);
+    return (flags & HEAL_W_F16) ? pack_bytes_hi(R, K) : pack_bytes(R, K);
 }
 constexpr int64_t kMaxDecodeLdw = (int64_t)1 << 26;
 constexpr int64_t kMaxDecodeLda = (int64_t)1 << 24;   // A (<= 64 rows) addressed with 32-bit byte offsets
@@ -54,7 +59,7 @@ const char* heal_status_str(heal_status s) {
     return "HEAL: unknown status";
 }
 
-int heal_version(void) { return (1 << 16) | (1 << 8); }
+int heal_version(void) { return (1 << 16) | (2 << 8); }
 
 heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo,
                            uint32_t* dev_status, void* stream) {
@@ -68,14 +73,16 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
 
 size_t heal_pack_w_bytes(int64_t N, int64_t K, uint32_t flags) {
     if (N <= 0 || K <= 0 || N >= kMaxDim || K >= kMaxDim) return 0;
-    return (size_t)((flags & HEAL_W_F16) ? pack_bytes_hi(N, K) : pack_bytes(N, K));
+    return (size_t)packed_bytes(N, K, flags);
 }
 
 heal_status heal_pack_w(const void* W, int64_t ldw, int64_t N, int64_t K, uint32_t flags,
                         const int8_t* kshift, void* packed, size_t packed_bytes, uint32_t* dev_status,
                         void* stream) {
     if (N < 0 || K < 0 || N >= kMaxDim || K >= kMaxDim) return HEAL_ERR_SHAPE;
-    if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_F16)) return HEAL_ERR_UNSUPPORTED;
+    if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_F16 | HEAL_BF16X3)) return HEAL_ERR_UNSUPPORTED;
+    const bool x3 = flags & HEAL_BF16X3;
+    if (x3 && ((flags & HEAL_W_F16) || kshift)) return HEAL_ERR_UNSUPPORTED;   // fp32 input, no shifts
     if (N == 0 || K == 0) return HEAL_OK;
     if (!W || !packed) return HEAL_ERR_NULL;
     const bool kn = flags & HEAL_W_KN;
@@ -83,6 +90,9 @@ heal_status heal_pack_w(const void* W, int64_t ldw, int64_t N, int64_t K, uint32
     if (ldw < (kn ? N : K)) return HEAL_ERR_STRIDE;
     if (misaligned(W, f16 ? 2 : 4) || misaligned(packed, 256) || misaligned(dev_status, 4)) return HEAL_ERR_ALIGN;
     if (packed_bytes < heal_pack_w_bytes(N, K, flags)) return HEAL_ERR_WORKSPACE;
+    if (x3)
+        return hip_status(launch_pack_bf16x3(static_cast<const float*>(W), ldw, N, K, kn ? 1 : 0, packed, dev_status,
+                                             static_cast<hipStream_t>(stream)));
     return hip_status(launch_pack(W, f16, ldw, N, K, kn ? 1 : 0, kshift, packed, dev_status,
                                   static_cast<hipStream_t>(stream)));
 }
@@ -93,8 +103,8 @@ size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags)
         const DecodePlan p = decode_plan(M, N, K);
         return (size_t)(round256(p.a_bytes) + round256(p.p_bytes));
     }
-    int64_t b = (flags & HEAL_A_PACKED) ? 0 : round256(pack_bytes(M, K));
-    if (!(flags & HEAL_W_PACKED)) b += round256((flags & HEAL_W_F16) ? pack_bytes_hi(N, K) : pack_bytes(N, K));
+    int64_t b = (flags & HEAL_A_PACKED) ? 0 : round256(packed_bytes(M, K, flags & HEAL_BF16X3));
+    if (!(flags & HEAL_W_PACKED)) b += round256(packed_bytes(N, K, flags));
     return (size_t)b;
 }
 
@@ -103,9 +113,12 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
                            void* workspace, size_t workspace_bytes, uint32_t* dev_status,
                            void* stream) {
     if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return HEAL_ERR_SHAPE;
-    if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_PACKED | HEAL_A_PACKED | HEAL_W_F16 | HEAL_ONE_PRODUCT))
+    if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_PACKED | HEAL_A_PACKED | HEAL_W_F16 | HEAL_ONE_PRODUCT | HEAL_BF16X3))
         return HEAL_ERR_UNSUPPORTED;
     if ((flags & HEAL_A_PACKED) && a_kshift) return HEAL_ERR_UNSUPPORTED;   // a packed A carries its shifts
+    // the BF16 three-way mode takes fp32 operands and needs no range shifts
+    if ((flags & HEAL_BF16X3) && ((flags & (HEAL_W_F16 | HEAL_ONE_PRODUCT)) || a_kshift))
+        return HEAL_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return HEAL_OK;
     if (!C) return HEAL_ERR_NULL;
     if (ldc < N) return HEAL_ERR_STRIDE;
@@ -142,6 +155,20 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     const void* apk = A;
     const void* bpk = W;
+    if (flags & HEAL_BF16X3) {
+        if (!a_packed) {
+            if (launch_pack_bf16x3(A, lda, M, K, 0, ws, dev_status, s) != hipSuccess) return HEAL_ERR_HIP;
+            apk = ws;
+            ws += round256(pack_bytes_x3(M, K));
+        }
+        if (!packed) {
+            if (launch_pack_bf16x3(static_cast<const float*>(W), ldw, N, K, kn ? 1 : 0, ws, dev_status, s) !=
+                hipSuccess)
+                return HEAL_ERR_HIP;
+            bpk = ws;
+        }
+        return hip_status(launch_gemm_prefill(apk, bpk, 6, true, C, ldc, M, N, K, s));
+    }
     if (!a_packed) {
         hipError_t e = launch_pack(A, false, lda, M, K, 0, a_kshift, ws, dev_status, s);
         if (e != hipSuccess) return HEAL_ERR_HIP;

@@ -40,7 +40,14 @@
 //    commute exactly, so the result does not depend on their order;
 //  * block -> tile order keeps the blocks that share a B tile on one XCD
 //    (blocks are dealt to the 8 XCDs round-robin), so B is read from HBM once
-//    and re-served from that XCD's L2.
+//    and re-served from that XCD's L2;
+//  * the BF16 three-way mode (X3) splits both operands as x = b0 + b1 + b2
+//    in BF16 (packed per 32-wide k block as [32 b0 | 32 b1 | 32 b2]) and
+//    keeps the six products b_i.c_j with i + j <= 2 on the BF16 MFMA, one
+//    fp32 accumulator.  It runs as a one-product GEMM over a virtual
+//    reduction six times as long: virtual k tile 6 kb + j stages A's plane
+//    (0,0,1,0,1,2)[j] and B's plane (0,1,0,2,1,0)[j] of block kb (64-byte
+//    LDS rows on both sides); the repeated planes are re-read from L2.
 #include <utility>
 
 #include "heal_internal.h"
@@ -53,13 +60,21 @@ constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int WM = 128, WN = 128;           // wave tile
 constexpr int TM = WM / 32, TN = WN / 32;   // 32x32 MFMA tiles per wave
 constexpr int ROWB = 128;                   // LDS bytes per row: 32 hi + 32 lo fp16 (swizzled)
-constexpr int A_REGION = BM * ROWB;         // 32 KB
 constexpr int NSTAGE = 2;
-constexpr int A_DMA = BM / 8 / 4;           // 1 KB (8-row) DMA blocks per wave per tile (A)
-// B in LDS: 128-byte rows (hi | lo), or 64-byte rows when B is in the hi-only
-// form of a 16-bit weight (then 16 rows per 1 KB DMA block)
-constexpr int b_rowb(bool bhi) { return bhi ? 64 : ROWB; }
-constexpr int stage_bytes(bool bhi) { return A_REGION + BN * b_rowb(bhi); }   // 64 KB or 48 KB
+// Operand rows in LDS: 128 bytes (hi | lo), or 64 bytes for a single 16-bit
+// plane (B in the hi-only form of a 16-bit weight; both operands in the BF16
+// three-way mode), then 16 rows per 1 KB DMA block
+constexpr int rowb(bool one_plane) { return one_plane ? 64 : ROWB; }
+constexpr int stage_bytes(bool ahi, bool bhi) { return BM * rowb(ahi) + BN * rowb(bhi); }   // 64, 48 or 32 KB
+
+// HBM byte offset of virtual k tile kt in a three-way BF16 packed row: block
+// kt / 6 (192 bytes), plane (planes >> 4 (kt % 6)) & 15 of it (64 bytes)
+constexpr uint32_t X3_PLANES_A = 0x210100u;   // j = 0..5 -> 0, 0, 1, 0, 1, 2
+constexpr uint32_t X3_PLANES_B = 0x012010u;   // j = 0..5 -> 0, 1, 0, 2, 1, 0
+__device__ __forceinline__ uint32_t x3_koff(int kt, uint32_t planes) {
+    const int kb = kt / 6, j = kt - 6 * kb;
+    return (uint32_t)kb * 192u + ((planes >> (4 * j)) & 0xFu) * 64u;
+}
 
 // s_waitcnt immediate: at most n vector memory operations outstanding
 // (vmcnt in bits 3:0 and 15:14); expcnt and lgkmcnt not waited on.
@@ -68,8 +83,16 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4)
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// 32x32x16 MFMA on fp16 operands, or on the same registers read as bf16
+template <bool BF16>
 __device__ __forceinline__ void mfma32(const half8& a, const half8& b, floatx16& c) {
-    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    if constexpr (BF16)
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                    0, 0, 0);
+    else
+        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // x * 2^-10 on 8 fp16 values (exact for normal results)
@@ -79,16 +102,22 @@ __device__ __forceinline__ half8 scale_m10(const half8& x) {
 
 // NP: products per k step.  3: A_hi.B_hi + 2^-10 (A_hi.B_lo + A_lo.B_hi);
 // 2: B is a 16-bit weight (zero lo planes), A_hi.B + 2^-10 A_lo.B;
-// 1: plain FP16, A_hi.B_hi.  BHI: B is in the hi-only packed form.
-template <bool SPLIT, int NP, bool BHI>
+// 1: plain FP16, A_hi.B_hi.  BHI: B is in the hi-only packed form.  X3: the
+// BF16 three-way mode (NP = 1 over the virtual reduction, single planes).
+template <bool SPLIT, int NP, bool BHI, bool X3>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned char* __restrict__ Bpk,
                          float* __restrict__ C, int64_t ldc, int M, int N, int Kp,
                          int tiles_m, int tiles_n) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     static_assert(!BHI || NP < 3, "a hi-only B has no lo planes");
-    constexpr int STAGE = stage_bytes(BHI);
-    constexpr int BROWB = b_rowb(BHI);
+    static_assert(!X3 || (NP == 1 && BHI), "the three-way mode is one product over single planes");
+    constexpr bool AHI = X3;
+    constexpr int STAGE = stage_bytes(AHI, BHI);
+    constexpr int AROWB = rowb(AHI);
+    constexpr int BROWB = rowb(BHI);
+    constexpr int A_REGION = BM * AROWB;
+    constexpr int A_DMA = BM * AROWB / 1024 / 4;   // 1 KB DMA blocks per wave per tile (A)
     constexpr int B_DMA = BN * BROWB / 1024 / 4;   // 1 KB DMA blocks per wave per tile (B)
 
     // ---- XCD-aware tile order (tm fastest, then tn, then the k half) -------
@@ -104,9 +133,10 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     // wave index as a scalar: DMA destinations and offsets must be wave-uniform
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
-    const uint32_t rowbytes = (uint32_t)Kp * 4u;   // Kp hi + Kp lo fp16
-    const uint32_t browbytes = BHI ? (uint32_t)Kp * 2u : rowbytes;
-    const int nkt_all = Kp / BK;
+    // HBM row bytes: Kp hi + Kp lo fp16; Kp fp16 (hi-only); 3 Kp bf16 (X3)
+    const uint32_t rowbytes = X3 ? (uint32_t)Kp * 6u : (uint32_t)Kp * 4u;
+    const uint32_t browbytes = X3 ? rowbytes : (BHI ? (uint32_t)Kp * 2u : rowbytes);
+    const int nkt_all = (X3 ? 6 : 1) * (Kp / BK);
     const int kt_begin = SPLIT ? half_k * (nkt_all / 2) : 0;
     const int kt_end = SPLIT ? (half_k ? nkt_all : nkt_all / 2) : nkt_all;
     const int nkt = kt_end - kt_begin;
@@ -120,9 +150,11 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     const uint32_t dma_voff = (uint32_t)drow * rowbytes + (uint32_t)((lane & 7) ^ dsw) * 16u;
     // hi-only B: lane L writes row L/4, slot L%4 of a 16-row block, holding
     // chunk (L%4) ^ ((row / 4) % 4); 16 rows per block keep that lane-only
-    const int drow_b = BHI ? lane >> 2 : drow;
-    const uint32_t dma_voff_b =
-        BHI ? (uint32_t)drow_b * browbytes + (uint32_t)((lane & 3) ^ ((drow_b >> 2) & 3)) * 16u : dma_voff;
+    const int drow_1 = lane >> 2;
+    const uint32_t slot_1 = (uint32_t)((lane & 3) ^ ((drow_1 >> 2) & 3)) * 16u;
+    const uint32_t dma_voff_b = BHI ? (uint32_t)drow_1 * browbytes + slot_1 : dma_voff;
+    const uint32_t dma_voff_a = AHI ? (uint32_t)drow_1 * rowbytes + slot_1 : dma_voff;
+    constexpr int A_ROWS_PER_DMA = 1024 / AROWB;
     constexpr int B_ROWS_PER_DMA = 1024 / BROWB;
     const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(Apk + (int64_t)tm * BM * rowbytes, BM * rowbytes);
     const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(Bpk + (int64_t)tn * BN * browbytes, BN * browbytes);
@@ -130,33 +162,39 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
 #define HEAL_DMA_TILE(kt_, stage_)                                                                    \
     do {                                                                                              \
         unsigned char* st_ = smem + (stage_) * STAGE;                                                 \
-        const uint32_t koff_ = (uint32_t)(kt_) * 128u;                                                \
+        const uint32_t koff_a_ = X3 ? x3_koff(kt_, X3_PLANES_A) : (uint32_t)(kt_) * 128u;             \
+        const uint32_t koff_b_ =                                                                      \
+            X3 ? x3_koff(kt_, X3_PLANES_B) : (uint32_t)(kt_) * (BROWB == ROWB ? 128u : 64u);           \
         _Pragma("unroll") for (int i = 0; i < A_DMA; ++i) {                                           \
             const int b_ = wave + 4 * i;                                                              \
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_ptr)(st_ + b_ * 1024), 16, dma_voff, \
-                                                     (uint32_t)(8 * b_) * rowbytes + koff_, 0, 0);   \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_ptr)(st_ + b_ * 1024), 16, dma_voff_a, \
+                                                     (uint32_t)(A_ROWS_PER_DMA * b_) * rowbytes + koff_a_, \
+                                                     0, 0);                                           \
         }                                                                                             \
         _Pragma("unroll") for (int i = 0; i < B_DMA; ++i) {                                           \
             const int b_ = wave + 4 * i;                                                              \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, (lds_ptr)(st_ + A_REGION + b_ * 1024), 16, \
                                                      dma_voff_b,                                      \
-                                                     (uint32_t)(B_ROWS_PER_DMA * b_) * browbytes +    \
-                                                         (uint32_t)(kt_) * (BROWB == ROWB ? 128u : 64u), 0, 0); \
+                                                     (uint32_t)(B_ROWS_PER_DMA * b_) * browbytes + koff_b_, \
+                                                     0, 0);                                           \
         }                                                                                             \
     } while (0)
 
     // ---- fragment reads: lane reads row (l % 32) of a 32-row tile, chunk
     //      2 ks + l / 32 (hi) or 4 + 2 ks + l / 32 (lo), at its swizzled slot
     const int sw = (lane >> 1) & 7;
-    const int a_row = (wm * WM + (lane & 31)) * ROWB;
+    const int a_row = (wm * WM + (lane & 31)) * AROWB;
     const int b_row = A_REGION + (wn * WN + (lane & 31)) * BROWB;
     int slot_off[2][2];   // [ks][hi/lo]
-    int slot_off_b[2];    // B hi chunk: the A slots, or the hi-only swizzle (row / 4) % 4
+    int slot_off_a[2];    // A hi chunk: the 128-byte-row slots, or the single-plane swizzle (row / 4) % 4
+    int slot_off_b[2];    // B hi chunk, likewise
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) slot_off[ks][p] = ((4 * p + 2 * ks + (lane >> 5)) ^ sw) * 16;
-        slot_off_b[ks] = BHI ? ((2 * ks + (lane >> 5)) ^ (((lane & 31) >> 2) & 3)) * 16 : slot_off[ks][0];
+        const int one_plane = ((2 * ks + (lane >> 5)) ^ (((lane & 31) >> 2) & 3)) * 16;
+        slot_off_a[ks] = AHI ? one_plane : slot_off[ks][0];
+        slot_off_b[ks] = BHI ? one_plane : slot_off[ks][0];
     }
 
     floatx16 acc[TM][TN];
@@ -171,7 +209,7 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
 #define HEAL_FRAGS(ah_, al_, bh_, bl_, ks_)                                                              \
     do {                                                                                                 \
         _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                                 \
-            ah_[i] = *reinterpret_cast<const half8*>(base + a_row + i * 32 * ROWB + slot_off[ks_][0]);   \
+            ah_[i] = *reinterpret_cast<const half8*>(base + a_row + i * 32 * AROWB + slot_off_a[ks_]);  \
             if constexpr (NP >= 2)                                                                       \
                 al_[i] = *reinterpret_cast<const half8*>(base + a_row + i * 32 * ROWB + slot_off[ks_][1]); \
         }                                                                                                \
@@ -186,17 +224,17 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
 #define HEAL_MFMAS(ah_, al_, bh_, bl_)                                                                   \
     do {                                                                                                 \
         _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                   \
-            _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32(ah_[i], bh_[j], acc[i][j]);            \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32<X3>(ah_[i], bh_[j], acc[i][j]);        \
         half8 as_[TM];                                                                                   \
         if constexpr (NP == 3) {                                                                         \
             _Pragma("unroll") for (int i = 0; i < TM; ++i) as_[i] = scale_m10(ah_[i]);                   \
             _Pragma("unroll") for (int i = 0; i < TM; ++i)                                               \
-                _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32(as_[i], bl_[j], acc[i][j]);        \
+                _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32<false>(as_[i], bl_[j], acc[i][j]);        \
         }                                                                                                \
         if constexpr (NP >= 2) {                                                                         \
             _Pragma("unroll") for (int i = 0; i < TM; ++i) as_[i] = scale_m10(al_[i]);                   \
             _Pragma("unroll") for (int i = 0; i < TM; ++i)                                               \
-                _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32(as_[i], bh_[j], acc[i][j]);        \
+                _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32<false>(as_[i], bh_[j], acc[i][j]);        \
         }                                                                                                \
     } while (0)
 
@@ -296,28 +334,32 @@ __global__ void zero_c_kernel(float* C, int64_t ldc, int64_t M, int64_t N) {
 
 hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool b_hi, float* C, int64_t ldc,
                                int64_t M, int64_t N, int64_t K, hipStream_t s) {
-    // two products go with a 16-bit (hi-only) B, three with a hi/lo B
-    if (nprod < 1 || nprod > 3 || (nprod == 3 && b_hi) || (nprod == 2 && !b_hi)) return hipErrorInvalidValue;
+    // two products go with a 16-bit (hi-only) B, three with a hi/lo B; 6 is
+    // the BF16 three-way mode (both operands in its packed form)
+    const bool x3 = nprod == 6;
+    if (!x3 && (nprod < 1 || nprod > 3 || (nprod == 3 && b_hi) || (nprod == 2 && !b_hi))) return hipErrorInvalidValue;
     if (M == 0 || N == 0) return hipSuccess;
     const int64_t Kp = pack_kp(K);
     if (Kp == 0) return hipErrorInvalidValue;  // K == 0 is handled by the caller
     // one operand block must be addressable by a 32-bit buffer offset
-    if ((int64_t)BM * Kp * 4 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    if ((int64_t)BM * Kp * (x3 ? 6 : 4) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
     // split the k range in two when the tiles fill at most half of the 256 CUs
     const bool split = (int64_t)tiles_m * tiles_n <= 128 && Kp / BK >= 8;
     static bool attr_set = false;  // idempotent; racing first calls set the same value
     if (!attr_set) {
-        const std::pair<const void*, int> fns[8] = {
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3, false>), stage_bytes(false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 3, false>), stage_bytes(false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2, true>), stage_bytes(true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 2, true>), stage_bytes(true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, false>), stage_bytes(false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, false>), stage_bytes(false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true>), stage_bytes(true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true>), stage_bytes(true)}};
+        const std::pair<const void*, int> fns[10] = {
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3, false, false>), stage_bytes(false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 3, false, false>), stage_bytes(false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2, true, false>), stage_bytes(false, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 2, true, false>), stage_bytes(false, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, false, false>), stage_bytes(false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, false, false>), stage_bytes(false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, false>), stage_bytes(false, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, false>), stage_bytes(false, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, true>), stage_bytes(true, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, true>), stage_bytes(true, true)}};
         for (const auto& f : fns) {
             hipError_t e = hipFuncSetAttribute(f.first, hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * f.second);
             if (e != hipSuccess) return e;
@@ -331,15 +373,16 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
         hipLaunchKernelGGL(zero_c_kernel, dim3(zb), dim3(256), 0, s, C, ldc, M, N);
     }
     const dim3 grid((unsigned)(tiles_m * tiles_n * (split ? 2 : 1)));
-#define HEAL_PREFILL(SPLIT_, NP_, BHI_)                                                               \
-    hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, NP_, BHI_>), grid, dim3(256), NSTAGE * stage_bytes(BHI_), s, \
-                       a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n)
+#define HEAL_PREFILL(SPLIT_, NP_, BHI_, X3_)                                                          \
+    hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, NP_, BHI_, X3_>), grid, dim3(256),                \
+                       NSTAGE * stage_bytes(X3_, BHI_), s, a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n)
 #define HEAL_PREFILL_NP(SPLIT_)                                                                       \
     do {                                                                                              \
-        if (nprod == 3) HEAL_PREFILL(SPLIT_, 3, false);                                               \
-        else if (nprod == 2) HEAL_PREFILL(SPLIT_, 2, true);                                           \
-        else if (b_hi) HEAL_PREFILL(SPLIT_, 1, true);                                                 \
-        else HEAL_PREFILL(SPLIT_, 1, false);                                                          \
+        if (x3) HEAL_PREFILL(SPLIT_, 1, true, true);                                                  \
+        else if (nprod == 3) HEAL_PREFILL(SPLIT_, 3, false, false);                                   \
+        else if (nprod == 2) HEAL_PREFILL(SPLIT_, 2, true, false);                                    \
+        else if (b_hi) HEAL_PREFILL(SPLIT_, 1, true, false);                                          \
+        else HEAL_PREFILL(SPLIT_, 1, false, false);                                                   \
     } while (0)
     if (split) HEAL_PREFILL_NP(true);
     else HEAL_PREFILL_NP(false);

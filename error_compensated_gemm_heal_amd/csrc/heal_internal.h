@@ -60,6 +60,10 @@ __host__ __device__ inline int64_t pack_bytes(int64_t R, int64_t K) { return pac
 // bytes of the hi-only packed form of a 16-bit operand
 __host__ __device__ inline int64_t pack_bytes_hi(int64_t R, int64_t K) { return pack_rows(R) * pack_kp(K) * 2; }
 
+// bytes of the BF16 three-way packed form: per row and 32-wide k block, the
+// 32 bf16 b0, then the 32 b1, then the 32 b2 (192 bytes), same padding
+__host__ __device__ inline int64_t pack_bytes_x3(int64_t R, int64_t K) { return pack_rows(R) * pack_kp(K) * 6; }
+
 // ---- launchers (return the launch status; never synchronize) -------------
 hipError_t launch_split(const float* X, int64_t n, uint16_t* hi, uint16_t* lo, uint32_t* status,
                         hipStream_t s);
@@ -69,6 +73,10 @@ hipError_t launch_split(const float* X, int64_t n, uint16_t* hi, uint16_t* lo, u
 // kshift (nullable): element (r, k) is multiplied by 2^-kshift[k] first.
 hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int64_t K, int kn,
                        const int8_t* kshift, void* packed, uint32_t* status, hipStream_t s);
+// BF16 three-way packing of fp32 rows (kn as for launch_pack); status gets
+// HEAL_FLAG_F16_RANGE where a value's bf16 high part is not finite.
+hipError_t launch_pack_bf16x3(const float* src, int64_t ld, int64_t rows, int64_t K, int kn, void* packed,
+                              uint32_t* status, hipStream_t s);
 // out = src with element (r, k) multiplied by 2^-kshift[k], same element type
 // and layout (kn as above), ldo for out.
 hipError_t launch_scale_k(const void* src, bool f16, int64_t ld, int64_t rows, int64_t K, int kn,
@@ -88,7 +96,8 @@ hipError_t launch_dequant(const int16_t* codes, int64_t rows, int64_t D, int64_t
 
 // C[M,N] from packed A (rows M) and packed B (rows N) with nprod products
 // per k step: 3 (both fp32), 2 (B a 16-bit weight: A_hi.B_lo skipped), 1
-// (plain FP16: A_hi.B_hi alone).  b_hi: B is in the hi-only form.
+// (plain FP16: A_hi.B_hi alone), or 6: the BF16 three-way mode (both
+// operands in that packed form; b_hi ignored).  b_hi: B is in the hi-only form.
 hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool b_hi, float* C, int64_t ldc,
                                int64_t M, int64_t N, int64_t K, hipStream_t s);
 

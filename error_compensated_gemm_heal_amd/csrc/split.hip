@@ -204,6 +204,82 @@ hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int6
     return hipGetLastError();
 }
 
+// ---- BF16 three-way split (a precision mode with fp32's exponent range) ----
+// x = b0 + b1 + b2 with b0 = bf16(x), b1 = bf16(x - b0), b2 = bf16(x - b0 - b1),
+// round to nearest even (the hardware conversion); both residuals are exact
+// in fp32, and the three 8-bit significands hold all 24 of x's bits while the
+// last part is a normal bf16 (|x| above about 2^-110).  A part is non-finite only if |x| rounds past bf16's largest value.
+__device__ __forceinline__ void split3_bf16(float x, uint16_t& b0, uint16_t& b1, uint16_t& b2) {
+    const __bf16 h0 = (__bf16)x;
+    const float r1 = x - (float)h0;
+    const __bf16 h1 = (__bf16)r1;
+    const __bf16 h2 = (__bf16)(r1 - (float)h1);
+    b0 = __builtin_bit_cast(uint16_t, h0);
+    b1 = __builtin_bit_cast(uint16_t, h1);
+    b2 = __builtin_bit_cast(uint16_t, h2);
+}
+
+// One item = 8 consecutive k of one row: reads 8 fp32 values (zero past the
+// operand), writes 16 bytes into each of the three planes of its 32-wide k
+// block.  kn == 0: src [rows, K] (k fastest across items); kn == 1: src
+// [K, rows] (r fastest, so neighbouring items read neighbouring addresses).
+template <int KN>
+__global__ __launch_bounds__(256) void pack_bf16x3_kernel(const float* __restrict__ src, int64_t ld, int64_t rows,
+                                                          int64_t K, int64_t Kp, int64_t rows_p,
+                                                          uint16_t* __restrict__ out,
+                                                          uint32_t* __restrict__ status) {
+    const int64_t k8n = Kp >> 3;
+    const int64_t total = rows_p * k8n;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    bool bad = false;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        int64_t r, c8;
+        if (KN) {
+            c8 = i / rows_p;
+            r = i - c8 * rows_p;
+        } else {
+            r = i / k8n;
+            c8 = i - r * k8n;
+        }
+        const int64_t k0 = c8 << 3;
+        uint32_t w0[4], w1[4], w2[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+            uint16_t a0, a1, a2, c0, c1, c2;
+            const int64_t ka = k0 + j, kb = k0 + j + 1;
+            const float xa = (r < rows && ka < K) ? (KN ? src[ka * ld + r] : src[r * ld + ka]) : 0.f;
+            const float xb = (r < rows && kb < K) ? (KN ? src[kb * ld + r] : src[r * ld + kb]) : 0.f;
+            split3_bf16(xa, a0, a1, a2);
+            split3_bf16(xb, c0, c1, c2);
+            bad |= ((a0 & 0x7F80u) == 0x7F80u) | ((c0 & 0x7F80u) == 0x7F80u);
+            w0[j >> 1] = a0 | ((uint32_t)c0 << 16);
+            w1[j >> 1] = a1 | ((uint32_t)c1 << 16);
+            w2[j >> 1] = a2 | ((uint32_t)c2 << 16);
+        }
+        uint16_t* o = out + r * (Kp * 3) + (k0 / kPackK) * (3 * kPackK) + (k0 % kPackK);
+        *reinterpret_cast<uint4*>(o) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+        *reinterpret_cast<uint4*>(o + kPackK) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+        *reinterpret_cast<uint4*>(o + 2 * kPackK) = make_uint4(w2[0], w2[1], w2[2], w2[3]);
+    }
+    if (bad && status) atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
+}
+
+hipError_t launch_pack_bf16x3(const float* src, int64_t ld, int64_t rows, int64_t K, int kn, void* packed,
+                              uint32_t* status, hipStream_t s) {
+    const int64_t Kp = pack_kp(K), rows_p = pack_rows(rows);
+    const int64_t total = rows_p * (Kp >> 3);
+    if (total == 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((total + 255) / 256, 256 * 64);
+    uint16_t* out = static_cast<uint16_t*>(packed);
+    if (kn)
+        hipLaunchKernelGGL(pack_bf16x3_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, src, ld, rows, K, Kp,
+                           rows_p, out, status);
+    else
+        hipLaunchKernelGGL(pack_bf16x3_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, src, ld, rows, K, Kp,
+                           rows_p, out, status);
+    return hipGetLastError();
+}
+
 // out = src with element (r, k) multiplied by 2^-kshift[k]: rows of K
 // ([rows, K], kn == 0) or K rows of `rows` ([K, rows], kn == 1).  Exact for
 // results in the format's normal range.

@@ -58,12 +58,14 @@ enum {
     HEAL_W_PACKED = 2u, /* W is a buffer written by heal_pack_w (ldw and layout ignored) */
     HEAL_A_PACKED = 4u, /* A is a buffer written by heal_pack_w for A's M rows (lda ignored) */
     HEAL_W_F16 = 8u,    /* W holds binary16 values (2 bytes each), layout per HEAL_W_KN   */
-    HEAL_ONE_PRODUCT = 16u /* plain FP16: C = A_hi.B_hi only (heal_gemm_f32c)             */
+    HEAL_ONE_PRODUCT = 16u, /* plain FP16: C = A_hi.B_hi only (heal_gemm_f32c)            */
+    HEAL_BF16X3 = 32u   /* BF16 three-way split, six products (heal_gemm_f32c, heal_pack_w) */
 };
 
 /* Bits of the optional device status word. */
 enum {
-    HEAL_FLAG_F16_RANGE = 1u, /* an operand had |x| >= 65520: its fp16 high part is inf */
+    HEAL_FLAG_F16_RANGE = 1u, /* an operand's 16-bit high part is inf: |x| >= 65520 (fp16),
+                                 or |x| beyond bf16's largest value (HEAL_BF16X3)        */
     HEAL_FLAG_SLOT_RANGE = 2u /* a K/V cache slot was >= num_slots: that row was skipped */
 };
 
@@ -116,7 +118,18 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  * HEAL_ONE_PRODUCT keeps the first product alone, C = A_hi.B_hi: plain FP16
  * with fp32 accumulation, for layers run without compensation (the paper's
  * HEAL++ upcasts only selected layers; the per-layer choice is the
- * caller's).  Its error is that of FP16 operands, not the bar below.  Accuracy: normwise error max_ij |C - C_exact| / (|a_i| |b_j|)
+ * caller's).  Its error is that of FP16 operands, not the bar below.
+ * HEAL_BF16X3 is a precision mode for operands FP16's range cannot hold
+ * without rescaling: each fp32 operand is split in BF16 (fp32's exponent
+ * range) as x = b0 + b1 + b2, b0 = bf16(x), b1 = bf16(x - b0),
+ * b2 = bf16(x - b0 - b1), round to nearest even (the sum is exact for
+ * |x| above about 2^-110, where the last part is still a normal bf16), and
+ *   C = sum over i + j <= 2 of A_i.B_j
+ * (six BF16 products, fp32 accumulation; the three dropped terms are below
+ * 2^-23 of |a||b|).  fp32 operands only: not with HEAL_W_F16,
+ * HEAL_ONE_PRODUCT or a_kshift (UNSUPPORTED); packed operands must come from
+ * heal_pack_w with HEAL_BF16X3.  Every M runs the prefill kernel.
+ * Accuracy: normwise error max_ij |C - C_exact| / (|a_i| |b_j|)
  * within 2x that of a naive FP32 GEMM and below 1e-5.  The summation order
  * depends on (M, N, K) but not on the data.  For M <= 64 (NK layout, K <
  * 2^23, neither operand packed) it also does not depend on M, so
@@ -135,7 +148,7 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  *          HEAL_W_F16, whose lo planes are zero, and the A_hi.B_lo product
  *          is skipped; a buffer packed from fp32 values must not carry
  *          HEAL_W_F16, or its lo planes are ignored), and/or | HEAL_A_PACKED,
- *          and/or | HEAL_ONE_PRODUCT
+ *          and/or | HEAL_ONE_PRODUCT, or | HEAL_BF16X3 (see above)
  *          (A then is heal_pack_w(A, lda, M, K, HEAL_W_NK)'s buffer: an
  *          activation split once can feed several GEMMs)
  *   a_kshift  device int8 [K], nullable.  Per-channel power-of-two
@@ -171,9 +184,11 @@ size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags)
  *  split once as well (HEAL_A_PACKED, with N := M rows of A and HEAL_W_NK).
  *  The packed form is internal and opaque: each row holds, for every 32-wide
  *  block of k, the 32 fp16 hi parts then the 32 fp16 lo parts (with
- *  HEAL_W_F16, the hi parts alone, half the bytes).  Rows are padded to a
- *  multiple of 256 and k to a multiple of 32 with zeros.  An activation is
- *  packed without HEAL_W_F16.
+ *  HEAL_W_F16, the hi parts alone, half the bytes; with HEAL_BF16X3, the 32
+ *  bf16 b0, then the 32 b1, then the 32 b2 of the three-way split).  Rows are
+ *  padded to a multiple of 256 and k to a multiple of 32 with zeros.  An
+ *  activation is packed without HEAL_W_F16 (with HEAL_BF16X3 when the GEMM
+ *  uses that mode).  HEAL_BF16X3 takes fp32 input and no kshift.
  *   W      as in heal_gemm_f32c (flags HEAL_W_NK or HEAL_W_KN, optionally
  *          | HEAL_W_F16: binary16 input, its lo parts are zero), 4-byte
  *          aligned (2-byte with HEAL_W_F16)
@@ -188,7 +203,7 @@ heal_status heal_pack_w(const void* W, int64_t ldw, int64_t N, int64_t K, uint32
 
 /* Bytes of heal_pack_w's buffer for these flags: 4 per element of the padded
  * [N, K] (hi and lo), or 2 with HEAL_W_F16 (the hi parts alone: a 16-bit
- * weight's lo parts are zero and are not stored). */
+ * weight's lo parts are zero and are not stored), or 6 with HEAL_BF16X3. */
 size_t heal_pack_w_bytes(int64_t N, int64_t K, uint32_t flags);
 
 /* ------------------------------------------------------------------------

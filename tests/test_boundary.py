@@ -63,7 +63,12 @@ def test_gemm_validation():
     assert _gemm(M=-1) == SHAPE
     assert _gemm(K=1 << 31) == SHAPE
     assert _gemm(flags=heal.HEAL_W_F16 | heal.HEAL_W_PACKED, W=ctypes.c_void_p(0x10010)) == ALIGN  # packed: 256 B
-    assert _gemm(flags=32) == UNSUP
+    assert _gemm(flags=64) == UNSUP
+    X3 = heal.HEAL_BF16X3
+    assert _gemm(flags=X3, C=None) == NULL                            # a valid flag: validation goes on
+    assert _gemm(flags=X3 | heal.HEAL_W_F16) == UNSUP                 # fp32 operands only
+    assert _gemm(flags=X3 | heal.HEAL_ONE_PRODUCT) == UNSUP
+    assert _gemm(flags=X3, ks=FAKE) == UNSUP                          # no range shifts in this mode
     assert _gemm(flags=heal.HEAL_ONE_PRODUCT, C=None) == NULL          # a valid flag: validation goes on
     assert _gemm(M=0, A=None, W=None, C=None) == OK
     assert _gemm(N=0, A=None, W=None, C=None) == OK
@@ -105,6 +110,12 @@ def test_gemm_workspace_sizes():
     assert heal.heal_pack_w_bytes(100, 33) == 256 * 64 * 4
     assert heal.heal_pack_w_bytes(100, 33, heal.HEAL_W_F16) == 256 * 64 * 2      # hi parts only
     assert ws(2048, 4096, 14336, heal.HEAL_W_F16) == 2048 * 14336 * 4 + 4096 * 14336 * 2
+    # BF16 three-way mode: 6 bytes per padded element, every M on the prefill path
+    X3 = heal.HEAL_BF16X3
+    assert heal.heal_pack_w_bytes(100, 33, X3) == 256 * 64 * 6
+    assert ws(1, 4096, 4096, X3) == 256 * 4096 * 6 + 4096 * 4096 * 6
+    assert ws(2048, 4096, 14336, X3 | heal.HEAL_W_PACKED) == 2048 * 14336 * 6
+    assert ws(2048, 4096, 14336, X3 | heal.HEAL_W_PACKED | heal.HEAL_A_PACKED) == 0
 
 
 def test_pack_validation():
@@ -119,6 +130,11 @@ def test_pack_validation():
     assert L.heal_pack_w(ctypes.c_void_p(0x10001), 64, 64, 64, heal.HEAL_W_F16, None, FAKE, 1 << 30, None, None) == ALIGN
     assert L.heal_pack_w(FAKE, 64, 64, 64, heal.HEAL_W_F16 | 16, None, FAKE, 1 << 30, None, None) == UNSUP
     assert L.heal_pack_w(FAKE, 64, 64, 64, 0, None, FAKE, 100, None, None) == WS
+    X3 = heal.HEAL_BF16X3
+    assert L.heal_pack_w(FAKE, 64, 64, 64, X3 | heal.HEAL_W_F16, None, FAKE, 1 << 30, None, None) == UNSUP
+    assert L.heal_pack_w(FAKE, 64, 64, 64, X3, FAKE, FAKE, 1 << 30, None, None) == UNSUP      # no kshift
+    assert L.heal_pack_w(FAKE, 64, 64, 64, X3, None, FAKE, 256 * 64 * 4, None, None) == WS  # needs 6 B/elem
+    assert L.heal_pack_w(None, 64, 64, 64, X3, None, FAKE, 1 << 30, None, None) == NULL
 
 
 def test_scale_k_validation():
