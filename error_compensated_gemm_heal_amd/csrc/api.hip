@@ -29,6 +29,14 @@ int64_t packed_bytes(int64_t R, int64_t K, uint32_t flags) {
     if (flags & HEAL_BF16X3) return pack_bytes_x3(R, K);
     return (flags & HEAL_W_F16) ? pack_bytes_hi(R, K) : pack_bytes(R, K);
 }
+// The Q/K/V projection quantizes in the prefill GEMM's epilogue for heads of
+// 128 outputs, the 3- and 2-product forms, and shapes the prefill kernel runs
+// without its k split; other cases store the fp32 product and quantize it in
+// a second pass (identical codes either way).
+bool qkv_fused(int64_t M, int64_t N, int64_t K, int64_t D, uint32_t flags) {
+    return D == 128 && K > 0 && !use_decode(M, K, flags) && !(flags & (HEAL_ONE_PRODUCT | HEAL_BF16X3)) &&
+           !prefill_ksplit(M, N, K);
+}
 constexpr int64_t kMaxDecodeLdw = (int64_t)1 << 26;
 constexpr int64_t kMaxDecodeLda = (int64_t)1 << 24;   // A (<= 64 rows) addressed with 32-bit byte offsets
 
@@ -108,10 +116,14 @@ size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags)
     return (size_t)b;
 }
 
-heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t ldw, float* C,
-                           int64_t ldc, int64_t M, int64_t N, int64_t K, uint32_t flags, const int8_t* a_kshift,
-                           void* workspace, size_t workspace_bytes, uint32_t* dev_status,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+// heal_gemm_f32c; with qkv set (the fused Q/K/V projection, qkv_fused true)
+// the prefill kernel quantizes its output instead of storing C.
+heal_status gemm_impl(const float* A, int64_t lda, const void* W, int64_t ldw, float* C, int64_t ldc, int64_t M,
+                      int64_t N, int64_t K, uint32_t flags, const int8_t* a_kshift, void* workspace,
+                      size_t workspace_bytes, uint32_t* dev_status, void* stream, const QkvDst* qkv) {
     if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return HEAL_ERR_SHAPE;
     if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_PACKED | HEAL_A_PACKED | HEAL_W_F16 | HEAL_ONE_PRODUCT | HEAL_BF16X3))
         return HEAL_ERR_UNSUPPORTED;
@@ -120,8 +132,8 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
     if ((flags & HEAL_BF16X3) && ((flags & (HEAL_W_F16 | HEAL_ONE_PRODUCT)) || a_kshift))
         return HEAL_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return HEAL_OK;
-    if (!C) return HEAL_ERR_NULL;
-    if (ldc < N) return HEAL_ERR_STRIDE;
+    if (!C && !qkv) return HEAL_ERR_NULL;
+    if (!qkv && ldc < N) return HEAL_ERR_STRIDE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (K == 0) {
         const int64_t blocks = std::min<int64_t>((M * N + 255) / 256, 4096);
@@ -167,7 +179,7 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
                 return HEAL_ERR_HIP;
             bpk = ws;
         }
-        return hip_status(launch_gemm_prefill(apk, bpk, 6, true, C, ldc, M, N, K, s));
+        return hip_status(launch_gemm_prefill(apk, bpk, 6, true, C, ldc, M, N, K, s, qkv));
     }
     if (!a_packed) {
         hipError_t e = launch_pack(A, false, lda, M, K, 0, a_kshift, ws, dev_status, s);
@@ -182,7 +194,18 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
         if (e != hipSuccess) return HEAL_ERR_HIP;
         bpk = wpk;
     }
-    return hip_status(launch_gemm_prefill(apk, bpk, one ? 1 : (wf16 ? 2 : 3), wf16, C, ldc, M, N, K, s));
+    return hip_status(launch_gemm_prefill(apk, bpk, one ? 1 : (wf16 ? 2 : 3), wf16, C, ldc, M, N, K, s, qkv));
+}
+}  // namespace
+
+extern "C" {
+
+heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t ldw, float* C,
+                           int64_t ldc, int64_t M, int64_t N, int64_t K, uint32_t flags, const int8_t* a_kshift,
+                           void* workspace, size_t workspace_bytes, uint32_t* dev_status,
+                           void* stream) {
+    return gemm_impl(A, lda, W, ldw, C, ldc, M, N, K, flags, a_kshift, workspace, workspace_bytes, dev_status,
+                     stream, nullptr);
 }
 
 heal_status heal_scale_k(const void* X, int64_t ldx, int64_t rows, int64_t K, uint32_t flags,
@@ -239,7 +262,8 @@ size_t heal_qkv_proj_quant_workspace(int64_t M, int64_t K, int64_t Hq, int64_t H
     if (M <= 0 || K <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || M >= kMaxDim || K >= kMaxDim) return 0;
     const int64_t N = (Hq + 2 * Hkv) * D;
     if (N >= kMaxDim) return 0;
-    return (size_t)round256(M * N * 4) + heal_gemm_f32c_workspace(M, N, K, flags);
+    const size_t gemm = heal_gemm_f32c_workspace(M, N, K, flags);
+    return qkv_fused(M, N, K, D, flags) ? gemm : (size_t)round256(M * N * 4) + gemm;
 }
 
 heal_status heal_qkv_proj_quant_i16(const float* A, int64_t lda, const void* W, int64_t ldw, int64_t M,
@@ -261,8 +285,14 @@ heal_status heal_qkv_proj_quant_i16(const float* A, int64_t lda, const void* W, 
         return HEAL_ERR_ALIGN;
     const int64_t N = (Hq + 2 * Hkv) * D;
     const size_t need = heal_qkv_proj_quant_workspace(M, K, Hq, Hkv, D, flags);
-    if (!workspace || workspace_bytes < need) return HEAL_ERR_WORKSPACE;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return HEAL_ERR_WORKSPACE;
     if (misaligned(workspace, 256)) return HEAL_ERR_ALIGN;
+    if (qkv_fused(M, N, K, D, flags)) {   // the INT16 epilogue of the GEMM itself
+        const QkvDst dst{q_codes, q_scales, k_cache, k_scales, v_cache, v_scales, slot_mapping, num_slots,
+                         (int)Hq, (int)Hkv, (int)D, dev_status};
+        return gemm_impl(A, lda, W, ldw, nullptr, N, M, N, K, flags, a_kshift, workspace, workspace_bytes, dev_status,
+                         stream, &dst);
+    }
     // the fp32 product lands in the workspace, the GEMM's own workspace after it
     float* C = static_cast<float*>(workspace);
     unsigned char* gws = static_cast<unsigned char*>(workspace) + round256(M * N * 4);

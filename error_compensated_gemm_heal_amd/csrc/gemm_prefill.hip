@@ -47,7 +47,13 @@
 //    fp32 accumulator.  It runs as a one-product GEMM over a virtual
 //    reduction six times as long: virtual k tile 6 kb + j stages A's plane
 //    (0,0,1,0,1,2)[j] and B's plane (0,1,0,2,1,0)[j] of block kb (64-byte
-//    LDS rows on both sides); the repeated planes are re-read from L2.
+//    LDS rows on both sides); the repeated planes are re-read from L2;
+//  * the Q/K/V projection epilogue (QKV) quantizes instead of storing: with
+//    heads of 128 outputs, a wave's 128 columns are one head, so each
+//    (token, head) row's maximum is a reduction over the wave's registers and
+//    the 32 lanes of its half, and the INT16 codes and scale are written
+//    straight to Q or to the K/V cache slot, with the standalone quantizer's
+//    arithmetic (identical codes, and no fp32 product in memory).
 #include <utility>
 
 #include "heal_internal.h"
@@ -66,6 +72,16 @@ constexpr int NSTAGE = 2;
 // three-way mode), then 16 rows per 1 KB DMA block
 constexpr int rowb(bool one_plane) { return one_plane ? 64 : ROWB; }
 constexpr int stage_bytes(bool ahi, bool bhi) { return BM * rowb(ahi) + BN * rowb(bhi); }   // 64, 48 or 32 KB
+
+// The INT16 epilogue's LDS: two wave tiles of 128 rows x 128 fp32 (row
+// stride padded to 132 floats against bank conflicts), then 256 token slots.
+constexpr int QKV_LD = 132;
+constexpr int QKV_TILE_FLOATS = 128 * QKV_LD;
+constexpr int QKV_SLOTS_OFF = 2 * QKV_TILE_FLOATS * 4;
+constexpr int QKV_LDS = QKV_SLOTS_OFF + 256 * 8;   // 137 KB
+constexpr int dyn_lds(bool ahi, bool bhi, bool qkv) {
+    return qkv && QKV_LDS > NSTAGE * stage_bytes(ahi, bhi) ? QKV_LDS : NSTAGE * stage_bytes(ahi, bhi);
+}
 
 // HBM byte offset of virtual k tile kt in a three-way BF16 packed row: block
 // kt / 6 (192 bytes), plane (planes >> 4 (kt % 6)) & 15 of it (64 bytes)
@@ -104,14 +120,16 @@ __device__ __forceinline__ half8 scale_m10(const half8& x) {
 // 2: B is a 16-bit weight (zero lo planes), A_hi.B + 2^-10 A_lo.B;
 // 1: plain FP16, A_hi.B_hi.  BHI: B is in the hi-only packed form.  X3: the
 // BF16 three-way mode (NP = 1 over the virtual reduction, single planes).
-template <bool SPLIT, int NP, bool BHI, bool X3>
+// QKV: the INT16 epilogue for heads of 128 outputs (not with SPLIT).
+template <bool SPLIT, int NP, bool BHI, bool X3, bool QKV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned char* __restrict__ Bpk,
                          float* __restrict__ C, int64_t ldc, int M, int N, int Kp,
-                         int tiles_m, int tiles_n) {
+                         int tiles_m, int tiles_n, QkvDst qkv) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     static_assert(!BHI || NP < 3, "a hi-only B has no lo planes");
     static_assert(!X3 || (NP == 1 && BHI), "the three-way mode is one product over single planes");
+    static_assert(!(QKV && SPLIT), "the INT16 epilogue needs whole sums");
     constexpr bool AHI = X3;
     constexpr int STAGE = stage_bytes(AHI, BHI);
     constexpr int AROWB = rowb(AHI);
@@ -301,6 +319,79 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     // ---- epilogue: bounds-checked store (or atomic add of one k half) -------
     const int row0 = tm * BM + wm * WM + (lane >> 5) * 4;
     const int col0 = tn * BN + wn * WN + (lane & 31);
+    if constexpr (QKV) {
+        // The output goes through LDS (the operand stages are free now): in
+        // pass p the two waves of wave column p write their 128 x 128 fp32
+        // tiles (one head each: heads are 128 outputs), then all four waves
+        // quantize those 256 (token, head) rows, one row per half wave (32
+        // lanes x 4 values), with the standalone quantizer's arithmetic.  The
+        // block's token slots are staged once.
+        __syncthreads();
+        float* tile = reinterpret_cast<float*>(smem);
+        int64_t* slot_lds = reinterpret_cast<int64_t*>(smem + QKV_SLOTS_OFF);
+        {
+            const int r = tm * BM + tid;
+            slot_lds[tid] = r < M ? qkv.slots[r] : -1;
+        }
+        bool bad_slot = false;
+#pragma unroll 1
+        for (int p = 0; p < 2; ++p) {
+            const int colp = tn * BN + p * WN;   // head colp / 128; block-uniform
+            if (colp >= N) break;                // N is a multiple of 128
+            if (wn == p) {
+                float* t = tile + wm * QKV_TILE_FLOATS;
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int rr = (lane >> 5) * 4 + i * 32 + (e >> 2) * 8 + (e & 3);
+                            t[rr * QKV_LD + j * 32 + (lane & 31)] = acc[i][j][e];
+                        }
+            }
+            __syncthreads();
+            const int hd = colp / 128;
+            const bool is_q = hd < qkv.hq;
+            const bool is_k = !is_q && hd < qkv.hq + qkv.hkv;
+            const int hk = is_q ? hd : (is_k ? hd - qkv.hq : hd - qkv.hq - qkv.hkv);
+            int16_t* const cbase = is_q ? qkv.qc : (is_k ? qkv.kc : qkv.vc);
+            float* const sbase = is_q ? qkv.qs : (is_k ? qkv.ks : qkv.vs);
+            const int hcount = is_q ? qkv.hq : qkv.hkv;
+            const int c4 = 4 * (lane & 31);
+#pragma unroll 8
+            for (int it = 0; it < 32; ++it) {
+                const int r = wave * 64 + it * 2 + (lane >> 5);   // 0..255: tile r / 128, row r % 128
+                const int rl = r;                                 // row in the block (tile 0: wm 0, tile 1: wm 1)
+                const float4 x = *reinterpret_cast<const float4*>(tile + (r >> 7) * QKV_TILE_FLOATS +
+                                                                  (r & 127) * QKV_LD + c4);
+                float m = fmaxf(fmaxf(__builtin_fabsf(x.x), __builtin_fabsf(x.y)),
+                                fmaxf(__builtin_fabsf(x.z), __builtin_fabsf(x.w)));
+#pragma unroll
+                for (int off = 16; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 32));
+                if (tm * BM + rl >= M) continue;
+                int64_t dst_row = tm * BM + rl;   // Q: the token row
+                if (!is_q) {
+                    dst_row = slot_lds[rl];
+                    if (dst_row < 0) continue;                                   // a padding token
+                    if (dst_row >= qkv.num_slots) { bad_slot = true; continue; }
+                }
+                const int64_t idx = dst_row * hcount + hk;
+                if ((lane & 31) == 0) sbase[idx] = (m == 0.0f) ? 0.0f : __fdiv_rn(m, 32767.0f);
+                // a zero row (m = 0, all x = 0) divides by 1 and gives zero codes
+                const float dm = (m == 0.0f) ? 1.0f : m;
+                short4 q;
+                q.x = (short)__builtin_rintf(__fdiv_rn(__fmul_rn(32767.0f, x.x), dm));
+                q.y = (short)__builtin_rintf(__fdiv_rn(__fmul_rn(32767.0f, x.y), dm));
+                q.z = (short)__builtin_rintf(__fdiv_rn(__fmul_rn(32767.0f, x.z), dm));
+                q.w = (short)__builtin_rintf(__fdiv_rn(__fmul_rn(32767.0f, x.w), dm));
+                *reinterpret_cast<short4*>(cbase + idx * 128 + c4) = q;
+            }
+            __syncthreads();   // the tiles are read before the next pass overwrites them
+        }
+        if (bad_slot && qkv.status) atomicOr(qkv.status, (uint32_t)HEAL_FLAG_SLOT_RANGE);
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -332,8 +423,13 @@ __global__ void zero_c_kernel(float* C, int64_t ldc, int64_t M, int64_t N) {
 
 }  // namespace
 
+bool prefill_ksplit(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    return tiles <= 128 && pack_kp(K) / BK >= 8;
+}
+
 hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool b_hi, float* C, int64_t ldc,
-                               int64_t M, int64_t N, int64_t K, hipStream_t s) {
+                               int64_t M, int64_t N, int64_t K, hipStream_t s, const QkvDst* qkv) {
     // two products go with a 16-bit (hi-only) B, three with a hi/lo B; 6 is
     // the BF16 three-way mode (both operands in its packed form)
     const bool x3 = nprod == 6;
@@ -346,22 +442,27 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
     // split the k range in two when the tiles fill at most half of the 256 CUs
-    const bool split = (int64_t)tiles_m * tiles_n <= 128 && Kp / BK >= 8;
+    const bool split = prefill_ksplit(M, N, K);
+    // the INT16 epilogue: heads of 128, whole sums, the 3- or 2-product form
+    if (qkv && (split || x3 || nprod == 1 || qkv->d != 128 || N % 128 != 0)) return hipErrorInvalidValue;
     static bool attr_set = false;  // idempotent; racing first calls set the same value
     if (!attr_set) {
-        const std::pair<const void*, int> fns[10] = {
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3, false, false>), stage_bytes(false, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 3, false, false>), stage_bytes(false, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2, true, false>), stage_bytes(false, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 2, true, false>), stage_bytes(false, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, false, false>), stage_bytes(false, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, false, false>), stage_bytes(false, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, false>), stage_bytes(false, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, false>), stage_bytes(false, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, true>), stage_bytes(true, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, true>), stage_bytes(true, true)}};
+        const std::pair<const void*, int> fns[12] = {
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3, false, false, false>), stage_bytes(false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 3, false, false, false>), stage_bytes(false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2, true, false, false>), stage_bytes(false, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 2, true, false, false>), stage_bytes(false, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, false, false, false>), stage_bytes(false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, false, false, false>), stage_bytes(false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, false, false>), stage_bytes(false, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, false, false>), stage_bytes(false, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, true, false>), stage_bytes(true, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, true, false>), stage_bytes(true, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3, false, false, true>), QKV_LDS},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2, true, false, true>), QKV_LDS}};
         for (const auto& f : fns) {
-            hipError_t e = hipFuncSetAttribute(f.first, hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * f.second);
+            const int bytes = f.second == QKV_LDS ? QKV_LDS : NSTAGE * f.second;
+            hipError_t e = hipFuncSetAttribute(f.first, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
             if (e != hipSuccess) return e;
         }
         attr_set = true;
@@ -373,9 +474,22 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
         hipLaunchKernelGGL(zero_c_kernel, dim3(zb), dim3(256), 0, s, C, ldc, M, N);
     }
     const dim3 grid((unsigned)(tiles_m * tiles_n * (split ? 2 : 1)));
+    const QkvDst none{};
 #define HEAL_PREFILL(SPLIT_, NP_, BHI_, X3_)                                                          \
-    hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, NP_, BHI_, X3_>), grid, dim3(256),                \
-                       NSTAGE * stage_bytes(X3_, BHI_), s, a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n)
+    hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, NP_, BHI_, X3_, false>), grid, dim3(256),         \
+                       NSTAGE * stage_bytes(X3_, BHI_), s, a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n, \
+                       none)
+    if (qkv) {
+        if (nprod == 3)
+            hipLaunchKernelGGL((gemm_prefill_kernel<false, 3, false, false, true>), grid, dim3(256),
+                               dyn_lds(false, false, true), s, a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m,
+                               tiles_n, *qkv);
+        else
+            hipLaunchKernelGGL((gemm_prefill_kernel<false, 2, true, false, true>), grid, dim3(256),
+                               dyn_lds(false, true, true), s, a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m,
+                               tiles_n, *qkv);
+        return hipGetLastError();
+    }
 #define HEAL_PREFILL_NP(SPLIT_)                                                                       \
     do {                                                                                              \
         if (x3) HEAL_PREFILL(SPLIT_, 1, true, true);                                                  \

@@ -64,6 +64,45 @@ __host__ __device__ inline int64_t pack_bytes_hi(int64_t R, int64_t K) { return 
 // 32 bf16 b0, then the 32 b1, then the 32 b2 (192 bytes), same padding
 __host__ __device__ inline int64_t pack_bytes_x3(int64_t R, int64_t K) { return pack_rows(R) * pack_kp(K) * 6; }
 
+// Rows of a fused Q/K/V projection output [M, (Hq + 2 Hkv) D]: row r is
+// (token m, head h).  Q heads go to q_codes [M, Hq, D] and q_scales [M, Hq];
+// K and V heads go to cache slot slot_mapping[m] of k/v_cache
+// [num_slots, Hkv, D] and k/v_scales [num_slots, Hkv].  A negative slot is
+// skipped (a padding token); a slot >= num_slots is skipped and flagged.
+struct QkvDst {
+    int16_t* qc;
+    float* qs;
+    int16_t* kc;
+    float* ks;
+    int16_t* vc;
+    float* vs;
+    const int64_t* slots;
+    int64_t num_slots;
+    int hq, hkv, d;
+    uint32_t* status;
+    __device__ bool at(int64_t r, int16_t*& c, float*& s) const {
+        const int H = hq + 2 * hkv;
+        const int64_t m = r / H;
+        const int h = (int)(r - m * H);
+        if (h < hq) {
+            c = qc + (m * hq + h) * d;
+            s = qs + m * hq + h;
+            return true;
+        }
+        const int64_t slot = slots[m];
+        if (slot < 0) return false;
+        if (slot >= num_slots) {
+            if (status) atomicOr(status, (uint32_t)HEAL_FLAG_SLOT_RANGE);
+            return false;
+        }
+        const bool is_k = h < hq + hkv;
+        const int hk = is_k ? h - hq : h - hq - hkv;
+        c = (is_k ? kc : vc) + (slot * hkv + hk) * d;
+        s = (is_k ? ks : vs) + slot * hkv + hk;
+        return true;
+    }
+};
+
 // ---- launchers (return the launch status; never synchronize) -------------
 hipError_t launch_split(const float* X, int64_t n, uint16_t* hi, uint16_t* lo, uint32_t* status,
                         hipStream_t s);
@@ -98,8 +137,13 @@ hipError_t launch_dequant(const int16_t* codes, int64_t rows, int64_t D, int64_t
 // per k step: 3 (both fp32), 2 (B a 16-bit weight: A_hi.B_lo skipped), 1
 // (plain FP16: A_hi.B_hi alone), or 6: the BF16 three-way mode (both
 // operands in that packed form; b_hi ignored).  b_hi: B is in the hi-only form.
+// qkv (nullable): instead of storing C, quantize each (token, head) row of
+// D = 128 outputs to INT16 in the epilogue and write it as dst.at() directs
+// (3- and 2-product forms, shapes without the k split: see prefill_ksplit).
 hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool b_hi, float* C, int64_t ldc,
-                               int64_t M, int64_t N, int64_t K, hipStream_t s);
+                               int64_t M, int64_t N, int64_t K, hipStream_t s, const QkvDst* qkv = nullptr);
+// Whether the prefill kernel splits the k range of this shape in two.
+bool prefill_ksplit(int64_t M, int64_t N, int64_t K);
 
 // Decode path (M <= 64): fp32 W [N,K] streamed and split in registers.
 // Workspace: the split activation planes (a_bytes), then, 256-byte aligned,

@@ -43,45 +43,6 @@ struct PlainDst {   // codes [rows, ldq], scales [rows]
     }
 };
 
-// Rows of a fused Q/K/V projection output [M, (Hq + 2 Hkv) D]: row r is
-// (token m, head h).  Q heads go to q_codes [M, Hq, D] and q_scales [M, Hq];
-// K and V heads go to cache slot slot_mapping[m] of k/v_cache
-// [num_slots, Hkv, D] and k/v_scales [num_slots, Hkv].  A negative slot is
-// skipped (a padding token); a slot >= num_slots is skipped and flagged.
-struct QkvDst {
-    int16_t* qc;
-    float* qs;
-    int16_t* kc;
-    float* ks;
-    int16_t* vc;
-    float* vs;
-    const int64_t* slots;
-    int64_t num_slots;
-    int hq, hkv, d;
-    uint32_t* status;
-    __device__ bool at(int64_t r, int16_t*& c, float*& s) const {
-        const int H = hq + 2 * hkv;
-        const int64_t m = r / H;
-        const int h = (int)(r - m * H);
-        if (h < hq) {
-            c = qc + (m * hq + h) * d;
-            s = qs + m * hq + h;
-            return true;
-        }
-        const int64_t slot = slots[m];
-        if (slot < 0) return false;
-        if (slot >= num_slots) {
-            if (status) atomicOr(status, (uint32_t)HEAL_FLAG_SLOT_RANGE);
-            return false;
-        }
-        const bool is_k = h < hq + hkv;
-        const int hk = is_k ? h - hq : h - hq - hkv;
-        c = (is_k ? kc : vc) + (slot * hkv + hk) * d;
-        s = (is_k ? ks : vs) + slot * hkv + hk;
-        return true;
-    }
-};
-
 template <int LPR, int NCH, class Dst>
 __global__ __launch_bounds__(256) void quant_kernel(const float* __restrict__ X, int64_t rows, int D,
                                                     int64_t ldx, Dst dst) {

@@ -275,7 +275,12 @@ heal_status heal_qkv_quant_i16(const float* X, int64_t rows, int64_t D, int64_t 
  *   q_scales, k_scales, v_scales  device fp32, 4-byte aligned
  *   slot_mapping  device int64 [M], 8-byte aligned
  *   workspace  device, >= heal_qkv_proj_quant_workspace(...) bytes, 256-byte
- *          aligned (holds the fp32 product and the GEMM's own workspace)
+ *          aligned.  With D = 128, fp32 or fp16 weights (not HEAL_ONE_PRODUCT
+ *          or HEAL_BF16X3) and a shape the prefill GEMM runs without its k
+ *          split (M > 64 with more than 128 output tiles of 256 x 256, or
+ *          K <= 224), the GEMM quantizes in its epilogue and the workspace
+ *          holds only its packed operands; otherwise it also holds the fp32
+ *          product, quantized by a second pass.  The codes are the same.
  * Limits: Hq, Hkv >= 1; D % 4 == 0, 4 <= D <= 4096; (Hq + 2 Hkv) D < 2^31.
  * ------------------------------------------------------------------------ */
 heal_status heal_qkv_proj_quant_i16(const float* A, int64_t lda, const void* W, int64_t ldw, int64_t M,

@@ -216,6 +216,15 @@ def test_qkv_proj_validation():
     assert _qkv(wsb=16) == WS
     n = heal.heal_qkv_proj_quant_workspace(8, 256, 4, 2, 128, 0)
     assert n >= 8 * 1024 * 4 and n % 256 == 0
+    # quantized in the GEMM epilogue (heads of 128, no k split): packed operands only
+    wsq, wsg = heal.heal_qkv_proj_quant_workspace, heal.heal_gemm_f32c_workspace
+    assert wsq(2048, 4096, 32, 8, 128, 0) == wsg(2048, 6144, 4096, 0)
+    assert wsq(300, 200, 4, 2, 128, 0) == wsg(300, 1024, 200, 0)
+    # two passes (the fp32 product lands in the workspace first): k split, D != 128, decode sizes
+    assert wsq(300, 512, 4, 2, 128, 0) == 300 * 1024 * 4 + wsg(300, 1024, 512, 0)
+    assert wsq(2048, 4096, 32, 8, 64, 0) == 2048 * 48 * 64 * 4 + wsg(2048, 48 * 64, 4096, 0)
+    assert wsq(2048, 4096, 32, 8, 128, heal.HEAL_ONE_PRODUCT) == \
+        2048 * 6144 * 4 + wsg(2048, 6144, 4096, heal.HEAL_ONE_PRODUCT)
 
 
 def _attn(B=2, T=16, Hq=8, Hkv=2, D=128, ws=FAKE, wsb=1 << 30, q=FAKE):

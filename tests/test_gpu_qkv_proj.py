@@ -90,6 +90,53 @@ def test_qkv_proj_codes_bit_exact_on_exact_operands(M, weight):
     _check_scatter(codes, scales, out, slots, Hq, Hkv)
 
 
+def _gemm_then_quant(A, W, Hq, Hkv, D, weight="fp32"):
+    """The GPU GEMM, then the standalone GPU quantizer over its fp32 product."""
+    M, H = A.shape[0], Hq + 2 * Hkv
+    Ad = torch.from_numpy(A).to(DEV)
+    Wd = torch.from_numpy(W.astype(np.float16) if weight != "fp32" else W).to(DEV)
+    if weight == "packed16":
+        Wd = heal.heal_pack_w(Wd)
+    C = heal.heal_gemm_f32c(Ad, Wd)
+    codes, scales = heal.heal_qkv_quant_i16(C.view(M, H, D))
+    return codes.cpu().numpy(), scales.cpu().numpy()
+
+
+@pytest.mark.parametrize("M,K,Hq,Hkv,weight", [(300, 200, 4, 2, "fp32"), (300, 200, 4, 2, "packed16"),
+                                                (1000, 100, 8, 2, "fp16"), (2048, 4096, 32, 8, "fp32"),
+                                                (2048, 4096, 32, 8, "packed16")])
+def test_qkv_proj_fused_epilogue_equals_gemm_then_quant(M, K, Hq, Hkv, weight):
+    """Shapes the prefill kernel runs without its k split quantize in the GEMM's
+    epilogue (the workspace then holds the packed operands only): codes and
+    scales equal, bit for bit, the GEMM's stored product quantized by the
+    standalone kernel, for random operands."""
+    D, H = 128, Hq + 2 * Hkv
+    print(f"qkv fused M={M} K={K} Hq={Hq} Hkv={Hkv} {weight}", flush=True)
+    flags = 0 if weight == "fp32" else (heal.HEAL_W_F16 | (heal.HEAL_W_PACKED if weight == "packed16" else 0))
+    assert heal.heal_qkv_proj_quant_workspace(M, K, Hq, Hkv, D, flags) == \
+        heal.heal_gemm_f32c_workspace(M, H * D, K, flags)
+    g = WL.rng(8400 + M + K)
+    A = WL.normal(g, (M, K))
+    W = WL.normal(g, (H * D, K), std=0.02)
+    num_slots = M + 37
+    slots = _slots(M, num_slots, seed=M + 1)
+    out = _run(A, W, Hq, Hkv, D, slots, num_slots, weight)
+    codes, scales = _gemm_then_quant(A, W, Hq, Hkv, D, weight)
+    _check_scatter(codes, scales, out, slots, Hq, Hkv)
+
+
+def test_qkv_proj_fused_epilogue_exact_operands():
+    """A fused shape on dyadic-grid operands: bit-equal to the oracle's INT16
+    quantization of the binary64 product."""
+    M, K, Hq, Hkv, D = 300, 200, 4, 2, 128
+    H = Hq + 2 * Hkv
+    A, W = _grid_operands(M, K, H * D, seed=8500)
+    slots = _slots(M, 2 * M, seed=3)
+    out = _run(A, W, Hq, Hkv, D, slots, 2 * M)
+    codes, scales = oracle.quant_i16(oracle.gemm_f64(A, W).astype(np.float32).reshape(M, H, D))
+    _check_scatter(codes, scales, out, slots, Hq, Hkv)
+
+
 @pytest.mark.parametrize("M", [8, 200])
 def test_qkv_proj_general_operands_within_bound(M):
     """Random operands: each dequantized value is within half a quantization step
