@@ -13,8 +13,10 @@
 //
 // One block of 4 waves owns 64 consecutive queries of one (batch, head);
 // wave w takes queries 16 w .. 16 w + 15 of them.  The block walks the key
-// blocks of 64 tokens that its queries can see (causal), K and V of the next
-// block copied into LDS by direct-to-LDS loads while the current one is used:
+// blocks of 64 tokens that its queries can see (causal).  Each thread loads a
+// sixteenth-row share of the next block's K and V codes into registers while
+// the current block is computed, and unpacks it into fp16 planes in LDS
+// (K and V hi exact, lo biased) once for all four waves:
 //  * scores as S^T = K . Q^T on v_mfma_f32_16x16x32_f16: rows are keys,
 //    columns the wave's 16 queries.  A = {kh, kl + 1024}, B = {64 qh, ql}: the
 //    kh products go to one accumulator, the biased kl products to a second
@@ -28,12 +30,11 @@
 //    query), so P needs no transpose.  A key's weight p_t s_v(t) 2^E (2^E a
 //    power of two per key block keeping the weights below 2) is split into
 //    fp16 hi + lo 2^-10; V comes from LDS through the transposing
-//    ds_read_b64_tr_b16 as {vh, vl + 1024}, and the 64 of 64 vh rides on the
-//    weights (64 P, exact).  The block's hi and lo weight products go to two
-//    fresh accumulators (the lo part unscaled, so small weights keep their
-//    residual in fp16's normal range), each started from -1024 times its
-//    weight sum to cancel the bias, and are merged into the output as
-//    out * 2^(m_old - m_new) + (hi + lo 2^-10) * 2^-E.
+//    ds_read_b64_tr_b16 on the V planes as {vh, vl + 1024}; the weight
+//    parts enter one fresh accumulator as 2^8 hi and 2^-2 lo (with the 64
+//    of 64 vh folded in for the vh products), started from -1024 times the
+//    weight sums to cancel the bias, and merged into the output as
+//    out * 2^(m_old - m_new) + block * 2^-8 * 2^-E.
 #include <type_traits>
 
 #include "heal_internal.h"
@@ -47,8 +48,8 @@ constexpr int QW = 16;                // queries per wave
 constexpr int WPB = 4;                // waves per block
 constexpr int QB = QW * WPB;          // queries per block
 constexpr int KB = 64;                // keys per step (= QB: the diagonal is one block)
-constexpr int KTILE = KB * D * 2;     // LDS bytes of one K (or V) tile of codes
-constexpr int STAGE = 2 * KTILE;      // K then V
+constexpr int PLANE = KB * D * 2;     // LDS bytes of one fp16 plane of a K or V tile
+constexpr int KH = 0, KL = PLANE, VH = 2 * PLANE, VL = 3 * PLANE;   // plane offsets (64 KB in all)
 constexpr float kLog2eInvSqrtD = 0.12751743074602467f;   // log2(e) / sqrt(128)
 
 typedef short short2v __attribute__((ext_vector_type(2)));
@@ -133,8 +134,9 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
     const int16_t* __restrict__ q, const float* __restrict__ qs, const int16_t* __restrict__ k,
     const float* __restrict__ ks, const int16_t* __restrict__ v, const float* __restrict__ vs,
     float* __restrict__ out, int T, int Hq, int Hkv, int nqb, int nbh) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[4 * PLANE];
     const int lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // heavy (late) query blocks first over all (batch, head) pairs: they see
     // the most keys, and the light ones fill the tail
@@ -176,30 +178,40 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
     }
     const float qscale = qi < T ? qs[((int64_t)b * T + qi) * Hq + h] * kLog2eInvSqrtD : 0.0f;
 
-    // ---- copies of key block kb into LDS stage kb & 1 (4 K and 4 V loads
-    //      per wave, 1 KB each: load i fills token rows 4 i .. 4 i + 3, lane L
-    //      row 4 i + L / 16, slot L % 16); tokens past T read as zero
-    auto copy_block = [&](int kb) {
+    // ---- this thread's share of a K (or V) tile: the 16-byte chunks
+    //      tid + 256 i, i.e. token row 16 i + tid / 16, chunk tid % 16, loaded
+    //      into registers (tokens past T read as zero) and unpacked into the
+    //      planes at the tile's swizzled slots
+    const int sh_row = tid >> 4, sh_chunk = tid & 15;
+    u32x4 rk[4], rv[4];
+    auto load_raw = [&](int kb) {
         const int t0 = kb * KB;
         const int nt = __builtin_amdgcn_readfirstlane(min(KB, T - t0));
         const int64_t tok0 = ((int64_t)b * T + t0) * Hkv + gk;
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + tok0 * D, (uint32_t)nt * row_bytes);
         const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + tok0 * D, (uint32_t)nt * row_bytes);
-        unsigned char* st = lds + (kb & 1) * STAGE;
-        const int r_in = lane >> 4, slot = lane & 15;
 #pragma unroll
-        for (int j = 0; j < KB / 4 / WPB; ++j) {
-            const int i = wid + WPB * j;
-            const int row = 4 * i + r_in;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                krs, (lds_ptr)(st + 1024 * i), 16, (uint32_t)row * row_bytes + 16u * (uint32_t)(slot ^ kswz(row)),
-                0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                vrs, (lds_ptr)(st + KTILE + 1024 * i), 16,
-                (uint32_t)row * row_bytes + 16u * (uint32_t)(slot ^ vswz(row)), 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t off = (uint32_t)(16 * i + sh_row) * row_bytes + 16u * (uint32_t)sh_chunk;
+            rk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+            rv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
         }
     };
-    constexpr int COPIES = 2 * (KB / 4 / WPB);   // VMEM copies per wave per block
+    auto write_planes = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * i + sh_row;
+            half8 hi, lo;
+            unpack8_lobias(rk[i], hi, lo);
+            const int ko = row * (D * 2) + 16 * (sh_chunk ^ kswz(row));
+            *reinterpret_cast<half8*>(lds + KH + ko) = hi;
+            *reinterpret_cast<half8*>(lds + KL + ko) = lo;
+            unpack8_lobias(rv[i], hi, lo);
+            const int vo = row * (D * 2) + 16 * (sh_chunk ^ vswz(row));
+            *reinterpret_cast<half8*>(lds + VH + vo) = hi;
+            *reinterpret_cast<half8*>(lds + VL + vo) = lo;
+        }
+    };
 
     // ---- running softmax state of query column c (the same on its 4 lanes)
     //      and the output: lane (c, grp) holds d = 16 dt + c of queries
@@ -212,6 +224,9 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
     // one key block; only the last one (the diagonal, or the ragged end of the
     // prompt) has keys a query of this block may not see
     auto key_block = [&](int kb, auto masked) {
+        __syncthreads();   // every wave is done with the previous block's planes; block kb's codes landed
+        write_planes();
+        __syncthreads();   // block kb's planes are complete
         // scales of this block's keys where the score layout needs them:
         // index 4 st + e is key 16 st + 4 grp + e (0 past T)
         float ksv[16], vsv[16];
@@ -229,16 +244,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
                 vsv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vsrs, off, 0, 0));
             }
         }
-        // the next block's copy, then wait for this block's (issued earlier)
-        if (kb + 1 < nkb) {
-            copy_block(kb + 1);
-            __builtin_amdgcn_s_waitcnt((COPIES & 15) | ((COPIES >> 4) << 14) | 0x70 | 0xF00);
-        } else {
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        }
-        __syncthreads();
-        const unsigned char* kt = lds + (kb & 1) * STAGE;
-        const unsigned char* vt = kt + KTILE;
+        // the next block's codes, in flight while this block is computed
+        if (kb + 1 < nkb) load_raw(kb + 1);
 
         // ---- scores: sc[4 st + e] for key 16 st + 4 grp + e of the block
         float sc[16];
@@ -248,10 +255,9 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
             const int row = 16 * st + c;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const u32x4 raw =
-                    *reinterpret_cast<const u32x4*>(kt + row * (D * 2) + 16 * ((4 * s + grp) ^ kswz(row)));
-                half8 kh, klb;
-                unpack8_lobias(raw, kh, klb);
+                const int ko = row * (D * 2) + 16 * ((4 * s + grp) ^ kswz(row));
+                const half8 kh = *reinterpret_cast<const half8*>(lds + KH + ko);
+                const half8 klb = *reinterpret_cast<const half8*>(lds + KL + ko);
                 mfma16(kh, qh[s], s_hi);
                 mfma16(kh, ql[s], s_hi);
                 mfma16(klb, qh[s], s_lo);
@@ -347,14 +353,13 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
                 const int off = lane_off + 16 * ((2 * dt) ^ vswz(rr));
 #pragma unroll
                 for (int kh2 = 0; kh2 < 2; ++kh2) {
-                    const short4v lo4 =
-                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(vt + off + (32 * kh2) * (D * 2)));
-                    const short4v hi4 =
-                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(vt + off + (32 * kh2 + 16) * (D * 2)));
-                    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo4), hi2 = __builtin_bit_cast(u32x2, hi4);
-                    const u32x4 raw = {lo2.x, lo2.y, hi2.x, hi2.y};
-                    half8 vh, vlb;
-                    unpack8_lobias(raw, vh, vlb);
+                    const int o0 = off + (32 * kh2) * (D * 2), o1 = off + (32 * kh2 + 16) * (D * 2);
+                    const u32x2 h0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(lds + VH + o0)));
+                    const u32x2 h1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(lds + VH + o1)));
+                    const u32x2 l0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(lds + VL + o0)));
+                    const u32x2 l1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(lds + VL + o1)));
+                    const half8 vh = __builtin_bit_cast(half8, (u32x4){h0.x, h0.y, h1.x, h1.y});
+                    const half8 vlb = __builtin_bit_cast(half8, (u32x4){l0.x, l0.y, l1.x, l1.y});
                     mfma16(pa_h14[kh2], vh, blk[dt]);
                     mfma16(pa_h8[kh2], vlb, blk[dt]);
                     mfma16(pa_l4[kh2], vh, blk[dt]);
@@ -371,9 +376,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) acc[dt][e] = acc[dt][e] * a_e + blk[dt][e] * bscale;
         }
-        __syncthreads();   // every wave is done with stage kb & 1 before it is refilled
     };
-    copy_block(0);
+    load_raw(0);
     for (int kb = 0; kb + 1 < nkb; ++kb) key_block(kb, std::false_type{});
     key_block(nkb - 1, std::true_type{});
 
