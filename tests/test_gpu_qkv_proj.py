@@ -103,7 +103,8 @@ def _gemm_then_quant(A, W, Hq, Hkv, D, weight="fp32"):
 
 
 @pytest.mark.parametrize("M,K,Hq,Hkv,weight", [(300, 200, 4, 2, "fp32"), (300, 200, 4, 2, "packed16"),
-                                                (1000, 100, 8, 2, "fp16"), (2048, 4096, 32, 8, "fp32"),
+                                                (1000, 100, 8, 2, "fp16"), (257, 96, 3, 1, "fp32"),
+                                                (2048, 4096, 32, 8, "fp32"),
                                                 (2048, 4096, 32, 8, "packed16")])
 def test_qkv_proj_fused_epilogue_equals_gemm_then_quant(M, K, Hq, Hkv, weight):
     """Shapes the prefill kernel runs without its k split quantize in the GEMM's
