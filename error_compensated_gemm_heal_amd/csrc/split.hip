@@ -3,12 +3,18 @@
 // HEAL paper, section 3, "Mitigating GEMM Truncation via FP16 Promotion and
 // Algebraic Compensation": the FP32 input is decomposed into an FP16 value
 // plus an FP16 residual shifted by 2^10, so that 16-bit matrix units can
-// evaluate the product.  Two kernels:
+// evaluate the product.  Kernels:
 //  * split_kernel: plain elementwise planes (hi[], lo[]), bit-exact.
 //  * pack kernels: the same split written straight into the padded,
 //    hi/lo-interleaved layout the prefill GEMM streams (one 128-byte line per
-//    row and 32-wide k block), so the GEMM needs no bounds checks.
-// Both are HBM-bound: 4 bytes read and 4 bytes written per element.
+//    row and 32-wide k block), so the GEMM needs no bounds checks; a binary16
+//    source packs its hi parts alone, and an optional per-channel power of two
+//    scales the source first.
+//  * pack_bf16x3_kernel: the BF16 three-way split of the precision mode, in
+//    the same padded layout with three 64-byte planes per k block.
+//  * scale_k_kernel: the per-channel power-of-two rescaling of an operand.
+// All are HBM-bound streaming maps (4 bytes read and 4 written per element
+// for the fp32 split).
 #include <algorithm>
 
 #include "heal_internal.h"
@@ -168,6 +174,50 @@ __global__ __launch_bounds__(256) void pack_colmajor_kernel(const T* __restrict_
     if (bad && status) atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
 }
 
+// The fp32 row-major pack without shifts, 8 elements per item: two 16-byte
+// loads, one 16-byte store into each of the hi and lo halves of the row's
+// 128-byte line for that k block.  Rows go to blockIdx.y (grid-stride), the
+// k groups of a row to x, so no item index is divided.
+__global__ __launch_bounds__(256) void pack_rowmajor8_kernel(const float* __restrict__ src, int64_t ld,
+                                                             int64_t rows, int64_t K, int64_t Kp, int64_t rows_p,
+                                                             uint16_t* __restrict__ out,
+                                                             uint32_t* __restrict__ status) {
+    const int c8n = (int)(Kp >> 3);
+    bool bad = false;
+    for (int64_t r = blockIdx.y; r < rows_p; r += gridDim.y) {
+        for (int c8 = blockIdx.x * 256 + threadIdx.x; c8 < c8n; c8 += gridDim.x * 256) {
+            const int64_t k = (int64_t)c8 << 3;
+            float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (r < rows) {
+                const float* p = src + r * ld + k;
+                if (k + 8 <= K) {
+                    const float4 a = *reinterpret_cast<const float4*>(p);
+                    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+                    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+                    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+                } else {
+                    for (int j = 0; j < 8; ++j)
+                        if (k + j < K) x[j] = p[j];
+                }
+            }
+            uint32_t h[4], l[4];
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+                _Float16 h0, l0, h1, l1;
+                split_one(x[j], h0, l0);
+                split_one(x[j + 1], h1, l1);
+                bad |= f16_out_of_range(x[j]) | f16_out_of_range(x[j + 1]);
+                h[j >> 1] = f16_bits(h0) | ((uint32_t)f16_bits(h1) << 16);
+                l[j >> 1] = f16_bits(l0) | ((uint32_t)f16_bits(l1) << 16);
+            }
+            uint16_t* o = out + r * (Kp * 2) + (k / kPackK) * (2 * kPackK) + (k % kPackK);
+            *reinterpret_cast<uint4*>(o) = make_uint4(h[0], h[1], h[2], h[3]);
+            *reinterpret_cast<uint4*>(o + kPackK) = make_uint4(l[0], l[1], l[2], l[3]);
+        }
+    }
+    if (bad && status) atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
+}
+
 hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int64_t K, int kn,
                        const int8_t* kshift, void* packed, uint32_t* status, hipStream_t s) {
     const int64_t Kp = pack_kp(K), rows_p = pack_rows(rows);
@@ -194,7 +244,13 @@ hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int6
         if (kn)
             hipLaunchKernelGGL(pack_colmajor_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, p, ld, rows,
                                K, Kp, rows_p, kshift, out, status);
-        else if (vec)
+        else if (vec && !kshift) {
+            const int64_t c8n = Kp >> 3;
+            const dim3 grid((unsigned)std::min<int64_t>((c8n + 255) / 256, 64),
+                            (unsigned)std::min<int64_t>(rows_p, 16384));
+            hipLaunchKernelGGL(pack_rowmajor8_kernel, grid, dim3(256), 0, s, p, ld, rows, K, Kp, rows_p, out,
+                               status);
+        } else if (vec)
             hipLaunchKernelGGL((pack_rowmajor_kernel<float, true>), dim3((unsigned)blocks), dim3(256), 0, s, p, ld,
                                rows, K, Kp, rows_p, kshift, out, status);
         else
