@@ -165,6 +165,10 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  *   workspace  device, >= heal_gemm_f32c_workspace(M, N, K, flags) bytes,
  *          256-byte aligned (NULL allowed when that size is 0)
  *   dev_status  device, nullable; HEAL_FLAG_F16_RANGE as in heal_split_f32.
+ * Layout note: in the M <= 64 case W streams from HBM row by row; rows whose
+ * byte stride is a multiple of 16 KB (K = 4096 fp32, ldw = K) all start in
+ * the same memory channel, and such a weight allocated with ldw = K + 64
+ * runs ~14% faster (measured at K = 4096, N = 14336).
  * Limits: M, N, K < 2^31.  K == 0 writes zeros.  In the M <= 64 case above,
  * ldw < 2^26 and lda < 2^24 (each 16-row slice of W, and A, are addressed
  * with 32-bit byte offsets), else HEAL_ERR_UNSUPPORTED.
