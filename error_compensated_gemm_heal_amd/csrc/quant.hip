@@ -9,7 +9,9 @@
 // row).  A row of D floats is owned by a group of LPR lanes of one wave
 // (LPR = D/4 rounded up to a power of two, at most 64).  Each lane holds
 // NCH float4 chunks in registers, so a row is read from HBM once; a wave
-// issues the loads of several row groups before processing any of them.  The row
+// issues the loads of several row groups before processing any of them, with
+// the non-temporal hint (each input byte is read once), and the grid holds up
+// to 80 blocks per compute unit before it strides.  The row
 // maximum is a butterfly over the group, which is exact and order-free.  The
 // per-element arithmetic follows the formula's own order with correctly
 // rounded fp32 operations: t = fl(32767 x), u = fl(t / M), q = rne(u).  That
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(256) void quant_kernel(const float* __restrict__ X,
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 const int j = gl + c * LPR;
-                x[u][c] = (r < rows && j < d4) ? *reinterpret_cast<const float4*>(X + r * ldx + 4 * j)
+                x[u][c] = (r < rows && j < d4) ? load_nt_f4(X + r * ldx + 4 * j)
                                                : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int16_t* __restrict_
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 const int j = gl + c * LPR;
-                qv[u][c] = (r < rows && j < d4) ? *reinterpret_cast<const short4*>(codes + r * ldq + 4 * j)
+                qv[u][c] = (r < rows && j < d4) ? __builtin_bit_cast(short4, load_nt_8b(codes + r * ldq + 4 * j))
                                                 : make_short4(0, 0, 0, 0);
             }
         }
@@ -174,7 +176,7 @@ void row_shape(int64_t D, int& lpr, int& nch) {
 unsigned grid_for(int64_t rows, int rows_per_wave_step) {
     const int64_t waves = (rows + rows_per_wave_step - 1) / rows_per_wave_step;
     int64_t blocks = (waves + 3) / 4;  // 4 waves per 256-thread block
-    const int64_t cap = 256 * 40;      // enough resident waves to cover HBM latency
+    const int64_t cap = 256 * 80;      // enough resident waves to cover HBM latency
     return (unsigned)std::max<int64_t>(1, std::min(blocks, cap));
 }
 
