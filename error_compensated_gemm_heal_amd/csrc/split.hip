@@ -206,7 +206,8 @@ __global__ __launch_bounds__(256) void pack_rowmajor8_kernel(const float* __rest
                 _Float16 h0, l0, h1, l1;
                 split_one(x[j], h0, l0);
                 split_one(x[j + 1], h1, l1);
-                bad |= f16_out_of_range(x[j]) | f16_out_of_range(x[j + 1]);
+                bad |= f16_out_of_range(x[j]);
+                bad |= f16_out_of_range(x[j + 1]);
                 h[j >> 1] = f16_bits(h0) | ((uint32_t)f16_bits(h1) << 16);
                 l[j >> 1] = f16_bits(l0) | ((uint32_t)f16_bits(l1) << 16);
             }
@@ -307,7 +308,8 @@ __global__ __launch_bounds__(256) void pack_bf16x3_kernel(const float* __restric
             const float xb = (r < rows && kb < K) ? (KN ? src[kb * ld + r] : src[r * ld + kb]) : 0.f;
             split3_bf16(xa, a0, a1, a2);
             split3_bf16(xb, c0, c1, c2);
-            bad |= ((a0 & 0x7F80u) == 0x7F80u) | ((c0 & 0x7F80u) == 0x7F80u);
+            bad |= (a0 & 0x7F80u) == 0x7F80u;
+            bad |= (c0 & 0x7F80u) == 0x7F80u;
             w0[j >> 1] = a0 | ((uint32_t)c0 << 16);
             w1[j >> 1] = a1 | ((uint32_t)c1 << 16);
             w2[j >> 1] = a2 | ((uint32_t)c2 << 16);
