@@ -300,23 +300,26 @@ def heal_qkv_proj_quant_workspace(M: int, K: int, Hq: int, Hkv: int, D: int, fla
 def heal_qkv_proj_quant_i16(A, W, Hq: int, Hkv: int, D: int, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
                             k_scales: torch.Tensor, v_cache: torch.Tensor, v_scales: torch.Tensor, q_codes=None,
                             q_scales=None, workspace=None, dev_status=None, a_kshift=None,
-                            one_product: bool = False):
+                            one_product: bool = False, bf16x3: bool = False):
     """Fused Q/K/V projection stored as INT16: C = A . W^T (W [(Hq + 2 Hkv) D, K], or a
     packed weight), Q rows -> (q_codes [M, Hq, D], q_scales [M, Hq]) returned, K/V rows
-    -> k/v_cache [num_slots, Hkv, D] and k/v_scales [num_slots, Hkv] at slot_mapping[m]."""
+    -> k/v_cache [num_slots, Hkv, D] and k/v_scales [num_slots, Hkv] at slot_mapping[m].
+    one_product / bf16x3: the GEMM's precision modes, as in heal_gemm_f32c."""
     _dev(A, "A", torch.float32)
     M, K = A.shape
     N = (Hq + 2 * Hkv) * D
     if isinstance(W, PackedOperand):
         if W.K != K or W.rows != N:
             raise ValueError("packed weight does not match (K, (Hq + 2 Hkv) D)")
+        if W.bf16x3 != bool(bf16x3):
+            raise ValueError(f"packed W was packed {'with' if W.bf16x3 else 'without'} bf16x3")
         flags, wptr, ldw = HEAL_W_PACKED | (HEAL_W_F16 if W.f16 else 0), _ptr(W.buf), 0
     else:
         _dev(W, "W")
         if tuple(W.shape) != (N, K):
             raise ValueError("W must be [(Hq + 2 Hkv) D, K]")
         flags, wptr, ldw = _weight_dtype_flag(W), _ptr(W), _rowmajor_ld(W, "W")
-    flags |= HEAL_ONE_PRODUCT if one_product else 0
+    flags |= (HEAL_ONE_PRODUCT if one_product else 0) | (HEAL_BF16X3 if bf16x3 else 0)
     _dev(slot_mapping, "slot_mapping", torch.int64)
     for t, name, dt in ((k_cache, "k_cache", torch.int16), (v_cache, "v_cache", torch.int16),
                         (k_scales, "k_scales", torch.float32), (v_scales, "v_scales", torch.float32)):

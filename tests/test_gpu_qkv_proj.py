@@ -126,6 +126,25 @@ def test_qkv_proj_fused_epilogue_equals_gemm_then_quant(M, K, Hq, Hkv, weight):
     _check_scatter(codes, scales, out, slots, Hq, Hkv)
 
 
+@pytest.mark.parametrize("mode", ["one_product", "bf16x3"])
+@pytest.mark.parametrize("M", [7, 300])
+def test_qkv_proj_precision_modes_exact_operands(mode, M):
+    """The GEMM's one-product and BF16 three-way modes through the projection (the
+    two-pass form): on dyadic-grid operands, which both modes hold exactly, the codes
+    equal the oracle's quantization of the binary64 product."""
+    K, Hq, Hkv, D = 384, 4, 2, 128
+    H = Hq + 2 * Hkv
+    A, W = _grid_operands(M, K, H * D, seed=8600 + M)
+    slots = _slots(M, M + 5, seed=M + 7)
+    kc, ks, vc, vs = _caches(M + 5, Hkv, D)
+    qc, qs = heal.heal_qkv_proj_quant_i16(torch.from_numpy(A).to(DEV), torch.from_numpy(W).to(DEV), Hq, Hkv, D,
+                                          torch.from_numpy(slots).to(DEV), kc, ks, vc, vs,
+                                          one_product=(mode == "one_product"), bf16x3=(mode == "bf16x3"))
+    out = [t.cpu().numpy() for t in (qc, qs, kc, ks, vc, vs)]
+    codes, scales = oracle.quant_i16(oracle.gemm_f64(A, W).astype(np.float32).reshape(M, H, D))
+    _check_scatter(codes, scales, out, slots, Hq, Hkv)
+
+
 def test_qkv_proj_fused_epilogue_exact_operands():
     """A fused shape on dyadic-grid operands: bit-equal to the oracle's INT16
     quantization of the binary64 product."""
