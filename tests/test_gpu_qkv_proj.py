@@ -191,6 +191,23 @@ def test_qkv_proj_slot_out_of_range_is_flagged_and_skipped():
     _check_scatter(codes, scales, out, slots_ok, Hq, Hkv)
 
 
+def test_qkv_proj_fused_epilogue_slot_out_of_range():
+    """The INT16 epilogue of the GEMM (a shape without k split) flags slots past
+    the cache and writes nothing for them, like the two-pass form."""
+    M, K, Hq, Hkv, D = 300, 160, 2, 1, 128
+    H = Hq + 2 * Hkv
+    assert heal.heal_qkv_proj_quant_workspace(M, K, Hq, Hkv, D, 0) == heal.heal_gemm_f32c_workspace(M, H * D, K, 0)
+    A, W = _grid_operands(M, K, H * D, seed=8700)
+    num_slots = 280
+    slots = np.arange(M, dtype=np.int64)          # tokens 280 .. 299 fall past the cache
+    slots[::7] = -1
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = _run(A, W, Hq, Hkv, D, slots, num_slots, status=st)
+    assert st.item() == heal.HEAL_FLAG_SLOT_RANGE
+    codes, scales = oracle.quant_i16(oracle.gemm_f64(A, W).astype(np.float32).reshape(M, H, D))
+    _check_scatter(codes, scales, out, np.where(slots >= num_slots, -1, slots), Hq, Hkv)
+
+
 def test_qkv_proj_into_cache_then_decode_attention():
     """Projection of B sequences of T tokens into a contiguous KV cache (slot =
     b T + t, i.e. [B, T, Hkv, D]), then decode attention of each sequence's last
