@@ -31,10 +31,11 @@
 //    power of two per key block keeping the weights below 2) is split into
 //    fp16 hi + lo 2^-10; V comes from LDS through the transposing
 //    ds_read_b64_tr_b16 on the V planes as {vh, vl + 1024}; the weight
-//    parts enter one fresh accumulator as 2^8 hi and 2^-2 lo (with the 64
-//    of 64 vh folded in for the vh products), started from -1024 times the
-//    weight sums to cancel the bias, and merged into the output as
-//    out * 2^(m_old - m_new) + block * 2^-8 * 2^-E.
+//    x = p s_v 2^(9 - E) splits into fp16 H + L, which enter one fresh
+//    accumulator (with the 64 of 64 vh folded in for the vh products),
+//    started from -1024 times the weight sums to cancel the bias; the output
+//    is held in units of the block factor 2^(E - 9) and merged as
+//    acc 2^(m_old - m_new) 2^(E_old - E) + block.
 #include <type_traits>
 
 #include "heal_internal.h"
@@ -217,6 +218,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
     //      and the output: lane (c, grp) holds d = 16 dt + c of queries
     //      q0 + 4 grp + e in acc[dt][e]
     float m_run = -INFINITY, l_run = 0.0f;
+    float beta_run = 1.0f;   // the output's current block factor (acc holds out / beta_run)
     floatx4 acc[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[dt] = (floatx4){0.f, 0.f, 0.f, 0.f};
@@ -299,32 +301,29 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
         vmax = group_max(vmax);   // every lane group of 16 holds the same 16 keys' scales
         int vexp = 0;
         (void)frexpf(vmax, &vexp);
-        const float p2 = vmax > 0.0f ? ldexpf(1.0f, 1 - vexp) : 1.0f;
-        const float inv_p2 = vmax > 0.0f ? ldexpf(1.0f, vexp - 1) : 1.0f;
+        // x = p s_v(t) 2^(9 - E) lies in [0, 512); its block factor 2^(E - 9)
+        const float p2 = vmax > 0.0f ? ldexpf(1.0f, 9 - vexp) : 1.0f;
+        const float beta = vmax > 0.0f ? ldexpf(1.0f, vexp - 9) : 1.0f;
 
         // ---- P as the A operand for key halves kh2 = 0, 1 (32 keys each):
-        //      slot i = key 32 kh2 + 16 (i / 4) + 4 grp + i % 4.  w = hi + lo 2^-10
-        //      enters one accumulator as 2^8 hi + 2^-2 lo = 2^8 w (hi 2^8 < 2^9,
-        //      the lo part 2^-2 keeps its residual down to w ~ 2^-22 in normal
-        //      range); with V's parts v = 64 vh + vl, the operands are 2^14 hi and
-        //      2^4 lo against vh, 2^8 hi and 2^-2 lo against vl.  All scalings are
-        //      exact.
-        half8 pa_h8[2], pa_l2[2], pa_h14[2], pa_l4[2];
+        //      slot i = key 32 kh2 + 16 (i / 4) + 4 grp + i % 4.  The weight
+        //      x splits as H = fp16(x), L = fp16(x - H) (x - H is exact in fp32;
+        //      H + L holds x to 2^-22, and L keeps it in normal range down to
+        //      x ~ 2^-3, to 2^-24 absolute below); with V's parts v = 64 vh + vl
+        //      the operands are 64 H and 64 L against vh (64 H < 2^15), H and L
+        //      against vl.  All scalings are exact.
+        half8 pa_h[2], pa_l[2], pa_h64[2], pa_l64[2];
 #pragma unroll
         for (int kh2 = 0; kh2 < 2; ++kh2) {
-            half8 hh8, ll8;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float w = p[8 * kh2 + i] * vsv[8 * kh2 + i] * p2;
-                _Float16 hh, ll;
-                split_one(w, hh, ll);
-                hh8[i] = hh;
-                ll8[i] = ll;
+                const float x = p[8 * kh2 + i] * vsv[8 * kh2 + i] * p2;
+                const _Float16 hh = (_Float16)x;
+                pa_h[kh2][i] = hh;
+                pa_l[kh2][i] = (_Float16)(x - (float)hh);
             }
-            pa_h8[kh2] = hh8 * (_Float16)256.0f;
-            pa_h14[kh2] = hh8 * (_Float16)16384.0f;   // < 2^15
-            pa_l2[kh2] = ll8 * (_Float16)0.25f;
-            pa_l4[kh2] = ll8 * (_Float16)16.0f;
+            pa_h64[kh2] = pa_h[kh2] * (_Float16)64.0f;
+            pa_l64[kh2] = pa_l[kh2] * (_Float16)64.0f;
         }
 
         // ---- P . V into a fresh accumulator; V by transposing LDS reads: in
@@ -337,8 +336,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
             const half8 m1024 = (half8)(_Float16)-1024.0f;
 #pragma unroll
             for (int kh2 = 0; kh2 < 2; ++kh2) {
-                mfma16(pa_h8[kh2], m1024, bias);
-                mfma16(pa_l2[kh2], m1024, bias);
+                mfma16(pa_h[kh2], m1024, bias);
+                mfma16(pa_l[kh2], m1024, bias);
             }
         }
         floatx4 blk[8];
@@ -360,21 +359,24 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
                     const u32x2 l1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(lds + VL + o1)));
                     const half8 vh = __builtin_bit_cast(half8, (u32x4){h0.x, h0.y, h1.x, h1.y});
                     const half8 vlb = __builtin_bit_cast(half8, (u32x4){l0.x, l0.y, l1.x, l1.y});
-                    mfma16(pa_h14[kh2], vh, blk[dt]);
-                    mfma16(pa_h8[kh2], vlb, blk[dt]);
-                    mfma16(pa_l4[kh2], vh, blk[dt]);
-                    mfma16(pa_l2[kh2], vlb, blk[dt]);
+                    mfma16(pa_h64[kh2], vh, blk[dt]);
+                    mfma16(pa_h[kh2], vlb, blk[dt]);
+                    mfma16(pa_l64[kh2], vh, blk[dt]);
+                    mfma16(pa_l[kh2], vlb, blk[dt]);
                 }
             }
         }
-        // ---- out = out * alpha(query) + blk 2^-8 / 2^E; lane (c, grp) holds the
-        //      rows of queries 4 grp + e, whose alpha sits on lane 4 grp + e
-        const float bscale = inv_p2 * 0.00390625f;
+        // ---- the output is kept in units of the current block factor:
+        //      out = acc beta, so acc <- acc alpha (beta_old / beta) + blk (the
+        //      ratio is a power of two, exact); lane (c, grp) holds the rows of
+        //      queries 4 grp + e, whose alpha sits on lane 4 grp + e
+        const float ratio = beta_run / beta;
+        beta_run = beta;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float a_e = from_lane(alpha, 4 * grp + e);
+            const float f_e = from_lane(alpha, 4 * grp + e) * ratio;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) acc[dt][e] = acc[dt][e] * a_e + blk[dt][e] * bscale;
+            for (int dt = 0; dt < 8; ++dt) acc[dt][e] = __builtin_fmaf(acc[dt][e], f_e, blk[dt][e]);
         }
     };
     load_raw(0);
@@ -390,7 +392,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
             float* o = out + (((int64_t)b * T + qrow) * Hq + h) * D + c;
             const float inv = 1.0f / l_e;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) o[16 * dt] = acc[dt][e] * inv;
+            for (int dt = 0; dt < 8; ++dt) o[16 * dt] = acc[dt][e] * beta_run * inv;
         }
     }
 }
