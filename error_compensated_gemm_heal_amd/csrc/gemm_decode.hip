@@ -39,10 +39,16 @@ namespace {
 constexpr int KA = 128;             // k block of activations per LDS buffer
 constexpr int STEPS = KA / 32;      // k32 steps per block
 constexpr int PF = 8;               // W prefetch distance in k32 steps (multiple of STEPS, <= 4 STEPS)
-constexpr int NW = 4;               // waves per workgroup
+constexpr int NW = 4;               // waves per workgroup (8 with four row tiles: see nw_for)
 constexpr int TARGET_WG = 512;      // workgroups aimed for (two per compute unit)
 constexpr int ROWS_PER_WAVE = 16;
-constexpr int DEC_ROWS = NW * ROWS_PER_WAVE;  // W rows (outputs) per workgroup
+constexpr int DEC_ROWS = NW * ROWS_PER_WAVE;  // W rows per 4-wave group: the unit of the split-K plan
+// Waves per workgroup (NWK): with four 16-row activation tiles (M > 32) the
+// activation block in LDS is as large as the weight block of 4 waves, so 8
+// waves share it (half the activation bytes per weight byte) when the grid
+// still has at least 192 workgroups (measured: 224 gain, 128 lose).  The split-K plan and each output's
+// summation order do not depend on it.
+constexpr int WIDE_MIN_WG = 192;
 
 
 // s_waitcnt immediate that waits until at most n vector memory operations
@@ -136,8 +142,8 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // MT == 1 stages A itself (A, lda); MT > 1 copies the pre-split blocks (Ablk).
 // SHIFT (MT == 1): element (m, k) of A is multiplied by 2^-kshift[k] before
 // its split.  ONE: plain FP16, the A_hi.W_hi product alone.
-template <int MT, bool VEC, bool WF16, bool AVEC, bool SHIFT, bool ONE>
-__global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const float* __restrict__ A, int64_t lda,
+template <int MT, bool VEC, bool WF16, bool AVEC, bool SHIFT, bool ONE, int NWK>
+__global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __restrict__ A, int64_t lda,
                                                           const unsigned char* __restrict__ Ablk,
                                                           int a_total_bytes, const void* __restrict__ W,
                                                           int64_t ldw, float* __restrict__ out, int64_t ldo,
@@ -148,13 +154,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const float* __res
     constexpr int BB = block_bytes<MT>();
     constexpr bool INK = MT == 1;                   // split the activation in the kernel
     constexpr int AU = 2 * MT;                      // 4-wide activation units per thread per block
-    constexpr int DMA_PER_WAVE = BB / 1024 / NW;    // 1 KB per wave-wide direct-to-LDS load
+    static_assert(NWK == NW || (NWK == 2 * NW && MT == 4), "8 waves only with four row tiles");
+    constexpr int DMA_PER_WAVE = BB / 1024 / NWK;   // 1 KB per wave-wide direct-to-LDS load
     extern __shared__ __attribute__((aligned(16))) unsigned char sa[];   // 2 x BB
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4;
-    const int n0 = blockIdx.x * DEC_ROWS + wave * ROWS_PER_WAVE;
+    const int n0 = blockIdx.x * (NWK * ROWS_PER_WAVE) + wave * ROWS_PER_WAVE;
     const int n = n0 + (lane & 15);
     const bool row_ok = n < N;
     const int split = blockIdx.y;
@@ -229,13 +236,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const float* __res
         }
     };
 
-    // pre-split activation blocks: wave w copies 1 KB pieces w, w + NW, ...
+    // pre-split activation blocks: wave w copies 1 KB pieces w, w + NWK, ...
     const int blk0 = k_begin / KA;
     const __amdgpu_buffer_rsrc_t pbrsrc = make_rsrc(Ablk, (uint32_t)a_total_bytes);
     auto dma_block = [&](int b) {
 #pragma unroll
         for (int i = 0; i < DMA_PER_WAVE; ++i) {
-            const int piece = wave + NW * i;
+            const int piece = wave + NWK * i;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(pbrsrc, (lds_ptr)(sa + (b & 1) * BB + piece * 1024), 16,
                                                      (uint32_t)(lane * 16),
                                                      (uint32_t)((blk0 + b) * BB + piece * 1024), 0, 0);
@@ -456,7 +463,11 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
     unsigned char* ablk = ws;
     float* part = reinterpret_cast<float*>(ws + (plan.a_bytes + 255) / 256 * 256);
     const int nablk = (int)((K + KA - 1) / KA);
-    const dim3 grid((unsigned)((N + DEC_ROWS - 1) / DEC_ROWS), (unsigned)plan.splits);
+    const int mt = mtiles(M);
+    const int64_t nblk2 = (N + 2 * DEC_ROWS - 1) / (2 * DEC_ROWS);
+    const bool wide = mt == 4 && nblk2 * plan.splits >= WIDE_MIN_WG;
+    const int wg_rows = (wide ? 2 * NW : NW) * ROWS_PER_WAVE;
+    const dim3 grid((unsigned)((N + wg_rows - 1) / wg_rows), (unsigned)plan.splits);
     float* out = plan.splits > 1 ? part : C;
     const int64_t ldo = plan.splits > 1 ? N : ldc;
     const int64_t stride = plan.splits > 1 ? M * N : 0;
@@ -466,10 +477,19 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
     const bool vec = (reinterpret_cast<uintptr_t>(W) & walign) == 0 && (ldw & 3) == 0 && (K & 31) == 0;
     // activation units load as float4 when rows are 16-byte aligned
     const bool avec = (reinterpret_cast<uintptr_t>(A) & 15) == 0 && (lda & 3) == 0;
-#define HEAL_DEC_LAUNCH(MT_, VEC_, F16_, AV_, SH_, ONE_)                                                \
-    hipLaunchKernelGGL((gemm_decode_kernel<MT_, VEC_, F16_, AV_, SH_, ONE_>), grid, dim3(64 * NW),       \
+#define HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW_)                                      \
+    hipLaunchKernelGGL((gemm_decode_kernel<MT_, VEC_, F16_, AV_, SH_, ONE_, NW_>), grid, dim3(64 * NW_), \
                        2 * block_bytes<MT_>(), s, A, lda, ablk, (int)plan.a_bytes, W, ldw, out, ldo, stride, \
                        (int)M, (int)N, (int)K, (int)plan.kchunk, kshift, status)
+#define HEAL_DEC_LAUNCH(MT_, VEC_, F16_, AV_, SH_, ONE_)                                                \
+    do {                                                                                                \
+        if constexpr (MT_ == 4) {                                                                       \
+            if (wide) HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, 2 * NW);                      \
+            else HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW);                               \
+        } else {                                                                                        \
+            HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW);                                    \
+        }                                                                                               \
+    } while (0)
 #define HEAL_DEC_MAIN(MT_, VEC_, F16_, AV_, SH_)                                                        \
     do {                                                                                                \
         if (one) HEAL_DEC_LAUNCH(MT_, VEC_, F16_, AV_, SH_, true);                                      \
@@ -495,7 +515,6 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
             else HEAL_DEC_AV(MT_, false, false, SH_);                                                   \
         }                                                                                               \
     } while (0)
-    const int mt = mtiles(M);
     if (mt == 1) {
         if (kshift) HEAL_DEC(1, true);
         else HEAL_DEC(1, false);
@@ -508,6 +527,7 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
 #undef HEAL_DEC_AV
 #undef HEAL_DEC_MAIN
 #undef HEAL_DEC_LAUNCH
+#undef HEAL_DEC_LAUNCH_NW
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
     const int64_t total = M * N;
