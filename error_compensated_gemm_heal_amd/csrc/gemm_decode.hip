@@ -43,12 +43,14 @@ constexpr int NW = 4;               // waves per workgroup (8 with four row tile
 constexpr int TARGET_WG = 512;      // workgroups aimed for (two per compute unit)
 constexpr int ROWS_PER_WAVE = 16;
 constexpr int DEC_ROWS = NW * ROWS_PER_WAVE;  // W rows per 4-wave group: the unit of the split-K plan
-// Waves per workgroup (NWK): with four 16-row activation tiles (M > 32) the
-// activation block in LDS is as large as the weight block of 4 waves, so 8
-// waves share it (half the activation bytes per weight byte) when the grid
-// still has at least 192 workgroups (measured: 224 gain, 128 lose).  The split-K plan and each output's
-// summation order do not depend on it.
-constexpr int WIDE_MIN_WG = 192;
+// Waves per workgroup (NWK): with the copied activation (M > 16) its block in
+// LDS is as large as the weight block of 4 waves (four row tiles) or half of
+// it (two), so 8 waves share it (half the activation bytes per weight byte)
+// when the grid keeps enough workgroups: measured, four tiles gain at 224 and
+// lose at 128; two tiles gain at 256 and lose at 224.  The split-K plan and
+// each output's summation order do not depend on it.
+constexpr int WIDE_MIN_WG4 = 192;
+constexpr int WIDE_MIN_WG2 = 256;
 
 
 // s_waitcnt immediate that waits until at most n vector memory operations
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
     constexpr int BB = block_bytes<MT>();
     constexpr bool INK = MT == 1;                   // split the activation in the kernel
     constexpr int AU = 2 * MT;                      // 4-wide activation units per thread per block
-    static_assert(NWK == NW || (NWK == 2 * NW && MT == 4), "8 waves only with four row tiles");
+    static_assert(NWK == NW || (NWK == 2 * NW && MT > 1), "8 waves only with the copied activation");
     constexpr int DMA_PER_WAVE = BB / 1024 / NWK;   // 1 KB per wave-wide direct-to-LDS load
     extern __shared__ __attribute__((aligned(16))) unsigned char sa[];   // 2 x BB
 
@@ -465,7 +467,7 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
     const int nablk = (int)((K + KA - 1) / KA);
     const int mt = mtiles(M);
     const int64_t nblk2 = (N + 2 * DEC_ROWS - 1) / (2 * DEC_ROWS);
-    const bool wide = mt == 4 && nblk2 * plan.splits >= WIDE_MIN_WG;
+    const bool wide = mt > 1 && nblk2 * plan.splits >= (mt == 4 ? WIDE_MIN_WG4 : WIDE_MIN_WG2);
     const int wg_rows = (wide ? 2 * NW : NW) * ROWS_PER_WAVE;
     const dim3 grid((unsigned)((N + wg_rows - 1) / wg_rows), (unsigned)plan.splits);
     float* out = plan.splits > 1 ? part : C;
@@ -483,7 +485,7 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
                        (int)M, (int)N, (int)K, (int)plan.kchunk, kshift, status)
 #define HEAL_DEC_LAUNCH(MT_, VEC_, F16_, AV_, SH_, ONE_)                                                \
     do {                                                                                                \
-        if constexpr (MT_ == 4) {                                                                       \
+        if constexpr (MT_ > 1) {                                                                        \
             if (wide) HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, 2 * NW);                      \
             else HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW);                               \
         } else {                                                                                        \
