@@ -181,8 +181,12 @@ heal_status gemm_impl(const float* A, int64_t lda, const void* W, int64_t ldw, f
         }
         return hip_status(launch_gemm_prefill(apk, bpk, 6, true, C, ldc, M, N, K, s, qkv));
     }
+    // one product: an activation packed here keeps its hi parts alone (half the
+    // GEMM's A staging); the workspace keeps the size of the hi/lo form
+    const bool a_hi = one && !a_packed && !a_kshift && !misaligned(A, 16) && (lda & 3) == 0;
     if (!a_packed) {
-        hipError_t e = launch_pack(A, false, lda, M, K, 0, a_kshift, ws, dev_status, s);
+        hipError_t e = a_hi ? launch_pack_hi_f32(A, lda, M, K, ws, dev_status, s)
+                            : launch_pack(A, false, lda, M, K, 0, a_kshift, ws, dev_status, s);
         if (e != hipSuccess) return HEAL_ERR_HIP;
         apk = ws;
         ws += round256(pack_bytes(M, K));
@@ -194,7 +198,7 @@ heal_status gemm_impl(const float* A, int64_t lda, const void* W, int64_t ldw, f
         if (e != hipSuccess) return HEAL_ERR_HIP;
         bpk = wpk;
     }
-    return hip_status(launch_gemm_prefill(apk, bpk, one ? 1 : (wf16 ? 2 : 3), wf16, C, ldc, M, N, K, s, qkv));
+    return hip_status(launch_gemm_prefill(apk, bpk, one ? 1 : (wf16 ? 2 : 3), wf16, C, ldc, M, N, K, s, qkv, a_hi));
 }
 }  // namespace
 

@@ -53,7 +53,9 @@
 //    (token, head) row's maximum is a reduction over the wave's registers and
 //    the 32 lanes of its half, and the INT16 codes and scale are written
 //    straight to Q or to the K/V cache slot, with the standalone quantizer's
-//    arithmetic (identical codes, and no fp32 product in memory).
+//    arithmetic (identical codes, and no fp32 product in memory);
+//  * in the one-product mode an activation packed per call keeps its hi
+//    parts alone (AH): 64-byte LDS rows for A, half its staging.
 #include <utility>
 
 #include "heal_internal.h"
@@ -120,8 +122,9 @@ __device__ __forceinline__ half8 scale_m10(const half8& x) {
 // 2: B is a 16-bit weight (zero lo planes), A_hi.B + 2^-10 A_lo.B;
 // 1: plain FP16, A_hi.B_hi.  BHI: B is in the hi-only packed form.  X3: the
 // BF16 three-way mode (NP = 1 over the virtual reduction, single planes).
-// QKV: the INT16 epilogue for heads of 128 outputs (not with SPLIT).
-template <bool SPLIT, int NP, bool BHI, bool X3, bool QKV>
+// QKV: the INT16 epilogue for heads of 128 outputs (not with SPLIT).  AH: A
+// is in the hi-only form (the one-product mode with an A packed per call).
+template <bool SPLIT, int NP, bool BHI, bool X3, bool QKV, bool AH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned char* __restrict__ Bpk,
                          float* __restrict__ C, int64_t ldc, int M, int N, int Kp,
@@ -130,7 +133,8 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     static_assert(!BHI || NP < 3, "a hi-only B has no lo planes");
     static_assert(!X3 || (NP == 1 && BHI), "the three-way mode is one product over single planes");
     static_assert(!(QKV && SPLIT), "the INT16 epilogue needs whole sums");
-    constexpr bool AHI = X3;
+    static_assert(!AH || (NP == 1 && !X3), "a hi-only A goes with the one-product mode");
+    constexpr bool AHI = X3 || AH;
     constexpr int STAGE = stage_bytes(AHI, BHI);
     constexpr int AROWB = rowb(AHI);
     constexpr int BROWB = rowb(BHI);
@@ -152,8 +156,8 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     // HBM row bytes: Kp hi + Kp lo fp16; Kp fp16 (hi-only); 3 Kp bf16 (X3)
-    const uint32_t rowbytes = X3 ? (uint32_t)Kp * 6u : (uint32_t)Kp * 4u;
-    const uint32_t browbytes = X3 ? rowbytes : (BHI ? (uint32_t)Kp * 2u : rowbytes);
+    const uint32_t rowbytes = X3 ? (uint32_t)Kp * 6u : (AH ? (uint32_t)Kp * 2u : (uint32_t)Kp * 4u);   // A
+    const uint32_t browbytes = X3 ? (uint32_t)Kp * 6u : (BHI ? (uint32_t)Kp * 2u : (uint32_t)Kp * 4u);
     const int nkt_all = (X3 ? 6 : 1) * (Kp / BK);
     const int kt_begin = SPLIT ? half_k * (nkt_all / 2) : 0;
     const int kt_end = SPLIT ? (half_k ? nkt_all : nkt_all / 2) : nkt_all;
@@ -165,13 +169,13 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     // sw depends on the lane and the wave only.
     const int drow = lane >> 3;
     const int dsw = ((wave & 1) << 2) | (drow >> 1);
-    const uint32_t dma_voff = (uint32_t)drow * rowbytes + (uint32_t)((lane & 7) ^ dsw) * 16u;
+    const uint32_t dma_slot = (uint32_t)((lane & 7) ^ dsw) * 16u;
     // hi-only B: lane L writes row L/4, slot L%4 of a 16-row block, holding
     // chunk (L%4) ^ ((row / 4) % 4); 16 rows per block keep that lane-only
     const int drow_1 = lane >> 2;
     const uint32_t slot_1 = (uint32_t)((lane & 3) ^ ((drow_1 >> 2) & 3)) * 16u;
-    const uint32_t dma_voff_b = BHI ? (uint32_t)drow_1 * browbytes + slot_1 : dma_voff;
-    const uint32_t dma_voff_a = AHI ? (uint32_t)drow_1 * rowbytes + slot_1 : dma_voff;
+    const uint32_t dma_voff_b = BHI ? (uint32_t)drow_1 * browbytes + slot_1 : (uint32_t)drow * browbytes + dma_slot;
+    const uint32_t dma_voff_a = AHI ? (uint32_t)drow_1 * rowbytes + slot_1 : (uint32_t)drow * rowbytes + dma_slot;
     constexpr int A_ROWS_PER_DMA = 1024 / AROWB;
     constexpr int B_ROWS_PER_DMA = 1024 / BROWB;
     const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(Apk + (int64_t)tm * BM * rowbytes, BM * rowbytes);
@@ -180,7 +184,7 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
 #define HEAL_DMA_TILE(kt_, stage_)                                                                    \
     do {                                                                                              \
         unsigned char* st_ = smem + (stage_) * STAGE;                                                 \
-        const uint32_t koff_a_ = X3 ? x3_koff(kt_, X3_PLANES_A) : (uint32_t)(kt_) * 128u;             \
+        const uint32_t koff_a_ = X3 ? x3_koff(kt_, X3_PLANES_A) : (uint32_t)(kt_) * (AH ? 64u : 128u); \
         const uint32_t koff_b_ =                                                                      \
             X3 ? x3_koff(kt_, X3_PLANES_B) : (uint32_t)(kt_) * (BROWB == ROWB ? 128u : 64u);           \
         _Pragma("unroll") for (int i = 0; i < A_DMA; ++i) {                                           \
@@ -429,7 +433,7 @@ bool prefill_ksplit(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool b_hi, float* C, int64_t ldc,
-                               int64_t M, int64_t N, int64_t K, hipStream_t s, const QkvDst* qkv) {
+                               int64_t M, int64_t N, int64_t K, hipStream_t s, const QkvDst* qkv, bool a_hi) {
     // two products go with a 16-bit (hi-only) B, three with a hi/lo B; 6 is
     // the BF16 three-way mode (both operands in its packed form)
     const bool x3 = nprod == 6;
@@ -445,21 +449,26 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
     const bool split = prefill_ksplit(M, N, K);
     // the INT16 epilogue: heads of 128, whole sums, the 3- or 2-product form
     if (qkv && (split || x3 || nprod == 1 || qkv->d != 128 || N % 128 != 0)) return hipErrorInvalidValue;
+    if (a_hi && (nprod != 1 || qkv)) return hipErrorInvalidValue;   // a hi-only A: the one-product mode
     static bool attr_set = false;  // idempotent; racing first calls set the same value
     if (!attr_set) {
-        const std::pair<const void*, int> fns[12] = {
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3, false, false, false>), stage_bytes(false, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 3, false, false, false>), stage_bytes(false, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2, true, false, false>), stage_bytes(false, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 2, true, false, false>), stage_bytes(false, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, false, false, false>), stage_bytes(false, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, false, false, false>), stage_bytes(false, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, false, false>), stage_bytes(false, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, false, false>), stage_bytes(false, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, true, false>), stage_bytes(true, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, true, false>), stage_bytes(true, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3, false, false, true>), QKV_LDS},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2, true, false, true>), QKV_LDS}};
+        const std::pair<const void*, int> fns[16] = {
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3, false, false, false, false>), stage_bytes(false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 3, false, false, false, false>), stage_bytes(false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2, true, false, false, false>), stage_bytes(false, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 2, true, false, false, false>), stage_bytes(false, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, false, false, false, false>), stage_bytes(false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, false, false, false, false>), stage_bytes(false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, false, false, false>), stage_bytes(false, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, false, false, false>), stage_bytes(false, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, true, false, false>), stage_bytes(true, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, true, false, false>), stage_bytes(true, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3, false, false, true, false>), QKV_LDS},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2, true, false, true, false>), QKV_LDS},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, false, false, false, true>), stage_bytes(true, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, false, false, false, true>), stage_bytes(true, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, false, false, true>), stage_bytes(true, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, false, false, true>), stage_bytes(true, true)}};
         for (const auto& f : fns) {
             const int bytes = f.second == QKV_LDS ? QKV_LDS : NSTAGE * f.second;
             hipError_t e = hipFuncSetAttribute(f.first, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
@@ -476,23 +485,29 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
     const dim3 grid((unsigned)(tiles_m * tiles_n * (split ? 2 : 1)));
     const QkvDst none{};
 #define HEAL_PREFILL(SPLIT_, NP_, BHI_, X3_)                                                          \
-    hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, NP_, BHI_, X3_, false>), grid, dim3(256),         \
+    hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, NP_, BHI_, X3_, false, false>), grid, dim3(256),  \
                        NSTAGE * stage_bytes(X3_, BHI_), s, a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n, \
+                       none)
+#define HEAL_PREFILL_AH(SPLIT_, BHI_)                                                                 \
+    hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, 1, BHI_, false, false, true>), grid, dim3(256),   \
+                       NSTAGE * stage_bytes(true, BHI_), s, a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n, \
                        none)
     if (qkv) {
         if (nprod == 3)
-            hipLaunchKernelGGL((gemm_prefill_kernel<false, 3, false, false, true>), grid, dim3(256),
+            hipLaunchKernelGGL((gemm_prefill_kernel<false, 3, false, false, true, false>), grid, dim3(256),
                                dyn_lds(false, false, true), s, a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m,
                                tiles_n, *qkv);
         else
-            hipLaunchKernelGGL((gemm_prefill_kernel<false, 2, true, false, true>), grid, dim3(256),
+            hipLaunchKernelGGL((gemm_prefill_kernel<false, 2, true, false, true, false>), grid, dim3(256),
                                dyn_lds(false, true, true), s, a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m,
                                tiles_n, *qkv);
         return hipGetLastError();
     }
 #define HEAL_PREFILL_NP(SPLIT_)                                                                       \
     do {                                                                                              \
-        if (x3) HEAL_PREFILL(SPLIT_, 1, true, true);                                                  \
+        if (a_hi && b_hi) HEAL_PREFILL_AH(SPLIT_, true);                                              \
+        else if (a_hi) HEAL_PREFILL_AH(SPLIT_, false);                                                \
+        else if (x3) HEAL_PREFILL(SPLIT_, 1, true, true);                                             \
         else if (nprod == 3) HEAL_PREFILL(SPLIT_, 3, false, false);                                   \
         else if (nprod == 2) HEAL_PREFILL(SPLIT_, 2, true, false);                                    \
         else if (b_hi) HEAL_PREFILL(SPLIT_, 1, true, false);                                          \
@@ -501,6 +516,7 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
     if (split) HEAL_PREFILL_NP(true);
     else HEAL_PREFILL_NP(false);
 #undef HEAL_PREFILL_NP
+#undef HEAL_PREFILL_AH
 #undef HEAL_PREFILL
     return hipGetLastError();
 }

@@ -123,6 +123,10 @@ hipError_t launch_split(const float* X, int64_t n, uint16_t* hi, uint16_t* lo, u
 // kshift (nullable): element (r, k) is multiplied by 2^-kshift[k] first.
 hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int64_t K, int kn,
                        const int8_t* kshift, void* packed, uint32_t* status, hipStream_t s);
+// The hi parts alone of fp32 rows [rows, K] (16-byte aligned rows, ld % 4 == 0),
+// in the hi-only packed layout, for the one-product mode.
+hipError_t launch_pack_hi_f32(const float* src, int64_t ld, int64_t rows, int64_t K, void* packed, uint32_t* status,
+                              hipStream_t s);
 // BF16 three-way packing of fp32 rows (kn as for launch_pack); status gets
 // HEAL_FLAG_F16_RANGE where a value's bf16 high part is not finite.
 hipError_t launch_pack_bf16x3(const float* src, int64_t ld, int64_t rows, int64_t K, int kn, void* packed,
@@ -147,12 +151,14 @@ hipError_t launch_dequant(const int16_t* codes, int64_t rows, int64_t D, int64_t
 // C[M,N] from packed A (rows M) and packed B (rows N) with nprod products
 // per k step: 3 (both fp32), 2 (B a 16-bit weight: A_hi.B_lo skipped), 1
 // (plain FP16: A_hi.B_hi alone), or 6: the BF16 three-way mode (both
-// operands in that packed form; b_hi ignored).  b_hi: B is in the hi-only form.
+// operands in that packed form; b_hi ignored).  b_hi: B is in the hi-only form;
+// a_hi (one product only): A is too.
 // qkv (nullable): instead of storing C, quantize each (token, head) row of
 // D = 128 outputs to INT16 in the epilogue and write it as dst.at() directs
 // (3- and 2-product forms, shapes without the k split: see prefill_ksplit).
 hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool b_hi, float* C, int64_t ldc,
-                               int64_t M, int64_t N, int64_t K, hipStream_t s, const QkvDst* qkv = nullptr);
+                               int64_t M, int64_t N, int64_t K, hipStream_t s, const QkvDst* qkv = nullptr,
+                               bool a_hi = false);
 // Whether the prefill kernel splits the k range of this shape in two.
 bool prefill_ksplit(int64_t M, int64_t N, int64_t K);
 

@@ -178,6 +178,7 @@ __global__ __launch_bounds__(256) void pack_colmajor_kernel(const T* __restrict_
 // loads, one 16-byte store into each of the hi and lo halves of the row's
 // 128-byte line for that k block.  Rows go to blockIdx.y (grid-stride), the
 // k groups of a row to x, so no item index is divided.
+template <bool HI_ONLY>
 __global__ __launch_bounds__(256) void pack_rowmajor8_kernel(const float* __restrict__ src, int64_t ld,
                                                              int64_t rows, int64_t K, int64_t Kp, int64_t rows_p,
                                                              uint16_t* __restrict__ out,
@@ -211,9 +212,13 @@ __global__ __launch_bounds__(256) void pack_rowmajor8_kernel(const float* __rest
                 h[j >> 1] = f16_bits(h0) | ((uint32_t)f16_bits(h1) << 16);
                 l[j >> 1] = f16_bits(l0) | ((uint32_t)f16_bits(l1) << 16);
             }
-            uint16_t* o = out + r * (Kp * 2) + (k / kPackK) * (2 * kPackK) + (k % kPackK);
-            *reinterpret_cast<uint4*>(o) = make_uint4(h[0], h[1], h[2], h[3]);
-            *reinterpret_cast<uint4*>(o + kPackK) = make_uint4(l[0], l[1], l[2], l[3]);
+            if constexpr (HI_ONLY) {   // the hi-only layout: Kp fp16 per row
+                *reinterpret_cast<uint4*>(out + r * Kp + k) = make_uint4(h[0], h[1], h[2], h[3]);
+            } else {
+                uint16_t* o = out + r * (Kp * 2) + (k / kPackK) * (2 * kPackK) + (k % kPackK);
+                *reinterpret_cast<uint4*>(o) = make_uint4(h[0], h[1], h[2], h[3]);
+                *reinterpret_cast<uint4*>(o + kPackK) = make_uint4(l[0], l[1], l[2], l[3]);
+            }
         }
     }
     if (bad && status) atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
@@ -249,7 +254,7 @@ hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int6
             const int64_t c8n = Kp >> 3;
             const dim3 grid((unsigned)std::min<int64_t>((c8n + 255) / 256, 64),
                             (unsigned)std::min<int64_t>(rows_p, 16384));
-            hipLaunchKernelGGL(pack_rowmajor8_kernel, grid, dim3(256), 0, s, p, ld, rows, K, Kp, rows_p, out,
+            hipLaunchKernelGGL(pack_rowmajor8_kernel<false>, grid, dim3(256), 0, s, p, ld, rows, K, Kp, rows_p, out,
                                status);
         } else if (vec)
             hipLaunchKernelGGL((pack_rowmajor_kernel<float, true>), dim3((unsigned)blocks), dim3(256), 0, s, p, ld,
@@ -258,6 +263,18 @@ hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int6
             hipLaunchKernelGGL((pack_rowmajor_kernel<float, false>), dim3((unsigned)blocks), dim3(256), 0, s, p,
                                ld, rows, K, Kp, rows_p, kshift, out, status);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_hi_f32(const float* src, int64_t ld, int64_t rows, int64_t K, void* packed, uint32_t* status,
+                              hipStream_t s) {
+    const int64_t Kp = pack_kp(K), rows_p = pack_rows(rows);
+    if (rows_p * Kp == 0) return hipSuccess;
+    if ((reinterpret_cast<uintptr_t>(src) & 15) != 0 || (ld & 3) != 0) return hipErrorInvalidValue;
+    const int64_t c8n = Kp >> 3;
+    const dim3 grid((unsigned)std::min<int64_t>((c8n + 255) / 256, 64), (unsigned)std::min<int64_t>(rows_p, 16384));
+    hipLaunchKernelGGL(pack_rowmajor8_kernel<true>, grid, dim3(256), 0, s, src, ld, rows, K, Kp, rows_p,
+                       static_cast<uint16_t*>(packed), status);
     return hipGetLastError();
 }
 
