@@ -450,8 +450,13 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
     // the INT16 epilogue: heads of 128, whole sums, the 3- or 2-product form
     if (qkv && (split || x3 || nprod == 1 || qkv->d != 128 || N % 128 != 0)) return hipErrorInvalidValue;
     if (a_hi && (nprod != 1 || qkv)) return hipErrorInvalidValue;   // a hi-only A: the one-product mode
-    static bool attr_set = false;  // idempotent; racing first calls set the same value
-    if (!attr_set) {
+    // once per device (the attribute is per device); idempotent, so racing
+    // first calls set the same value
+    constexpr int kMaxDevices = 64;
+    static bool attr_set[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (!attr_set[dev]) {
         const std::pair<const void*, int> fns[16] = {
             {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3, false, false, false, false>), stage_bytes(false, false)},
             {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 3, false, false, false, false>), stage_bytes(false, false)},
@@ -474,7 +479,7 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
             hipError_t e = hipFuncSetAttribute(f.first, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
             if (e != hipSuccess) return e;
         }
-        attr_set = true;
+        attr_set[dev] = true;
     }
     const unsigned char* a = static_cast<const unsigned char*>(Apk);
     const unsigned char* b = static_cast<const unsigned char*>(Bpk);
