@@ -11,12 +11,14 @@
 // qh, 64 qh and ql are exact FP16 values, and every product formed below is
 // exact in FP32 (at most 22 significant bits).
 //
-// One block of 4 waves owns 64 consecutive queries of one (batch, head);
+// One block of 8 waves owns 128 consecutive queries of one (batch, head);
 // wave w takes queries 16 w .. 16 w + 15 of them.  The block walks the key
-// blocks of 64 tokens that its queries can see (causal).  Each thread loads a
-// sixteenth-row share of the next block's K and V codes into registers while
-// the current block is computed, and unpacks it into fp16 planes in LDS
-// (K and V hi exact, lo biased) once for all four waves:
+// blocks of 64 tokens that its queries can see (causal); a wave computes the
+// ones its own queries see, so the first four waves skip the block's last
+// key block.  Each thread loads its share of the next block's K and V codes
+// into registers while the current block is computed, and unpacks it into
+// fp16 planes in LDS (K and V hi exact, lo biased) once for all eight waves;
+// two sets of planes alternate, so one barrier per key block suffices:
 //  * scores as S^T = K . Q^T on v_mfma_f32_16x16x32_f16: rows are keys,
 //    columns the wave's 16 queries.  A = {kh, kl + 1024}, B = {64 qh, ql}: the
 //    kh products go to one accumulator, the biased kl products to a second
@@ -46,11 +48,15 @@ namespace {
 
 constexpr int D = 128;
 constexpr int QW = 16;                // queries per wave
-constexpr int WPB = 4;                // waves per block
+constexpr int WPB = 8;                // waves per block
 constexpr int QB = QW * WPB;          // queries per block
-constexpr int KB = 64;                // keys per step (= QB: the diagonal is one block)
+constexpr int KB = 64;                // keys per step
 constexpr int PLANE = KB * D * 2;     // LDS bytes of one fp16 plane of a K or V tile
-constexpr int KH = 0, KL = PLANE, VH = 2 * PLANE, VL = 3 * PLANE;   // plane offsets (64 KB in all)
+constexpr int KH = 0, KL = PLANE, VH = 2 * PLANE, VL = 3 * PLANE;   // plane offsets in one set
+constexpr int BUF = 4 * PLANE;        // one set of the four planes (64 KB)
+constexpr int RPS = 64 * WPB / 16;    // token rows one pass of the block's threads covers
+constexpr int SHARE = KB / RPS;       // 16-byte chunks per thread per K (or V) tile
+static_assert(QB % KB == 0 && KB % QW == 0 && KB % RPS == 0, "tiling");
 constexpr float kLog2eInvSqrtD = 0.12751743074602467f;   // log2(e) / sqrt(128)
 
 typedef short short2v __attribute__((ext_vector_type(2)));
@@ -131,11 +137,13 @@ __device__ __forceinline__ float from_lane(float x, int src) {
 __device__ __forceinline__ int kswz(int r) { return r & 15; }
 __device__ __forceinline__ int vswz(int r) { return 2 * (r & 7); }
 
-__global__ __launch_bounds__(256) void attn_prefill_kernel(
+__global__ __launch_bounds__(64 * WPB) void attn_prefill_kernel(
     const int16_t* __restrict__ q, const float* __restrict__ qs, const int16_t* __restrict__ k,
     const float* __restrict__ ks, const int16_t* __restrict__ v, const float* __restrict__ vs,
     float* __restrict__ out, int T, int Hq, int Hkv, int nqb, int nbh) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[4 * PLANE];
+    // two sets of planes: the waves compute on one while the next key
+    // block is unpacked into the other
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * BUF];
     const int lane = threadIdx.x & 63;
     const int tid = threadIdx.x;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -150,7 +158,12 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
     const int c = lane & 15, grp = lane >> 4;
     const int q0 = qb * QB + wid * QW;          // the wave's first query
     const int qi = q0 + c;                      // this lane's query column
-    const int nkb = min(qb + 1, (T + KB - 1) / KB);   // key blocks up to the diagonal
+    const int nkb_t = (T + KB - 1) / KB;        // key blocks of the prompt
+    // key blocks the block walks (up to the diagonal of its last query), and
+    // those this wave computes: up to the one holding its own queries (no
+    // wave's 16 queries straddle two key blocks); none for a wave wholly past T
+    const int nkb = min((qb * QB + QB - 1) / KB + 1, nkb_t);
+    const int nkb_w = q0 < T ? min((q0 + QW - 1) / KB + 1, nkb_t) : 0;
     const uint32_t row_bytes = (uint32_t)Hkv * D * 2;  // bytes between tokens in the cache
 
     // ---- Q as the B operand: lane (c, grp) holds query qi, d = 32 s + 8 grp + j
@@ -180,37 +193,56 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
     const float qscale = qi < T ? qs[((int64_t)b * T + qi) * Hq + h] * kLog2eInvSqrtD : 0.0f;
 
     // ---- this thread's share of a K (or V) tile: the 16-byte chunks
-    //      tid + 256 i, i.e. token row 16 i + tid / 16, chunk tid % 16, loaded
-    //      into registers (tokens past T read as zero) and unpacked into the
-    //      planes at the tile's swizzled slots
+    //      tid + 64 WPB i, i.e. token row RPS i + tid / 16, chunk tid % 16,
+    //      loaded into registers and unpacked into the planes at the tile's
+    //      swizzled slots.  Tokens past T, and blocks past the last one the
+    //      block walks, read as zero (an empty buffer range: no memory is
+    //      touched), so the loads of a block ahead need no condition.
     const int sh_row = tid >> 4, sh_chunk = tid & 15;
-    u32x4 rk[4], rv[4];
+    u32x4 rk[SHARE], rv[SHARE];
     auto load_raw = [&](int kb) {
-        const int t0 = kb * KB;
-        const int nt = __builtin_amdgcn_readfirstlane(min(KB, T - t0));
+        const int t0 = min(kb, nkb - 1) * KB;
+        const int nt = kb < nkb ? __builtin_amdgcn_readfirstlane(min(KB, T - t0)) : 0;
         const int64_t tok0 = ((int64_t)b * T + t0) * Hkv + gk;
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + tok0 * D, (uint32_t)nt * row_bytes);
         const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + tok0 * D, (uint32_t)nt * row_bytes);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t off = (uint32_t)(16 * i + sh_row) * row_bytes + 16u * (uint32_t)sh_chunk;
+        for (int i = 0; i < SHARE; ++i) {
+            const uint32_t off = (uint32_t)(RPS * i + sh_row) * row_bytes + 16u * (uint32_t)sh_chunk;
             rk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
             rv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
         }
     };
-    auto write_planes = [&]() {
+    auto write_planes = [&](unsigned char* buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * i + sh_row;
+        for (int i = 0; i < SHARE; ++i) {
+            const int row = RPS * i + sh_row;
             half8 hi, lo;
             unpack8_lobias(rk[i], hi, lo);
             const int ko = row * (D * 2) + 16 * (sh_chunk ^ kswz(row));
-            *reinterpret_cast<half8*>(lds + KH + ko) = hi;
-            *reinterpret_cast<half8*>(lds + KL + ko) = lo;
+            *reinterpret_cast<half8*>(buf + KH + ko) = hi;
+            *reinterpret_cast<half8*>(buf + KL + ko) = lo;
             unpack8_lobias(rv[i], hi, lo);
             const int vo = row * (D * 2) + 16 * (sh_chunk ^ vswz(row));
-            *reinterpret_cast<half8*>(lds + VH + vo) = hi;
-            *reinterpret_cast<half8*>(lds + VL + vo) = lo;
+            *reinterpret_cast<half8*>(buf + VH + vo) = hi;
+            *reinterpret_cast<half8*>(buf + VL + vo) = lo;
+        }
+    };
+    // scales of a block's keys where the score layout needs them: index
+    // 4 st + e is key 16 st + 4 grp + e (0 past T, and past the last block)
+    float ksv[16], vsv[16];
+    auto load_scales = [&](int kb) {
+        const int t0 = min(kb, nkb - 1) * KB;
+        const int nt = kb < nkb ? __builtin_amdgcn_readfirstlane(min(KB, T - t0)) : 0;
+        const int64_t tok0 = ((int64_t)b * T + t0) * Hkv + gk;
+        const uint32_t srec = nt > 0 ? (uint32_t)(((nt - 1) * Hkv + 1) * 4) : 0u;
+        const __amdgpu_buffer_rsrc_t ksrs = make_rsrc(ks + tok0, srec);
+        const __amdgpu_buffer_rsrc_t vsrs = make_rsrc(vs + tok0, srec);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t off = (uint32_t)((16 * (i >> 2) + 4 * grp + (i & 3)) * Hkv * 4);
+            ksv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ksrs, off, 0, 0));
+            vsv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vsrs, off, 0, 0));
         }
     };
 
@@ -223,32 +255,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[dt] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
-    // one key block; only the last one (the diagonal, or the ragged end of the
-    // prompt) has keys a query of this block may not see
-    auto key_block = [&](int kb, auto masked) {
-        __syncthreads();   // every wave is done with the previous block's planes; block kb's codes landed
-        write_planes();
-        __syncthreads();   // block kb's planes are complete
-        // scales of this block's keys where the score layout needs them:
-        // index 4 st + e is key 16 st + 4 grp + e (0 past T)
-        float ksv[16], vsv[16];
-        {
-            const int t0 = kb * KB;
-            const int nt = __builtin_amdgcn_readfirstlane(min(KB, T - t0));
-            const int64_t tok0 = ((int64_t)b * T + t0) * Hkv + gk;
-            const uint32_t srec = (uint32_t)(((nt - 1) * Hkv + 1) * 4);
-            const __amdgpu_buffer_rsrc_t ksrs = make_rsrc(ks + tok0, srec);
-            const __amdgpu_buffer_rsrc_t vsrs = make_rsrc(vs + tok0, srec);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const uint32_t off = (uint32_t)((16 * (i >> 2) + 4 * grp + (i & 3)) * Hkv * 4);
-                ksv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ksrs, off, 0, 0));
-                vsv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vsrs, off, 0, 0));
-            }
-        }
-        // the next block's codes, in flight while this block is computed
-        if (kb + 1 < nkb) load_raw(kb + 1);
-
+    // one key block from the planes at buf; only the wave's last one (its
+    // diagonal, or the ragged end of the prompt) has keys a query of the wave
+    // may not see
+    auto key_block = [&](int kb, const unsigned char* buf, auto masked) {
         // ---- scores: sc[4 st + e] for key 16 st + 4 grp + e of the block
         float sc[16];
 #pragma unroll
@@ -258,8 +268,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int ko = row * (D * 2) + 16 * ((4 * s + grp) ^ kswz(row));
-                const half8 kh = *reinterpret_cast<const half8*>(lds + KH + ko);
-                const half8 klb = *reinterpret_cast<const half8*>(lds + KL + ko);
+                const half8 kh = *reinterpret_cast<const half8*>(buf + KH + ko);
+                const half8 klb = *reinterpret_cast<const half8*>(buf + KL + ko);
                 mfma16(kh, qh[s], s_hi);
                 mfma16(kh, ql[s], s_hi);
                 mfma16(klb, qh[s], s_lo);
@@ -280,9 +290,9 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
         mb = group_max(mb);
         const float m_new = fmaxf(m_run, mb);
         // m_new is finite: every key of an unmasked block is visible, and the
-        // first key of the last block is visible to every query of the block
-        // (and lies before T).  exp2(-inf) = 0 covers the first block's alpha
-        // and the masked scores.
+        // first key of the wave's last block is visible to every query of the
+        // wave (and lies before T).  exp2(-inf) = 0 covers the first block's
+        // alpha and the masked scores.
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         float p[16], psum = 0.0f;
 #pragma unroll
@@ -353,10 +363,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
 #pragma unroll
                 for (int kh2 = 0; kh2 < 2; ++kh2) {
                     const int o0 = off + (32 * kh2) * (D * 2), o1 = off + (32 * kh2 + 16) * (D * 2);
-                    const u32x2 h0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(lds + VH + o0)));
-                    const u32x2 h1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(lds + VH + o1)));
-                    const u32x2 l0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(lds + VL + o0)));
-                    const u32x2 l1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(lds + VL + o1)));
+                    const u32x2 h0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(buf + VH + o0)));
+                    const u32x2 h1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(buf + VH + o1)));
+                    const u32x2 l0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(buf + VL + o0)));
+                    const u32x2 l1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(buf + VL + o1)));
                     const half8 vh = __builtin_bit_cast(half8, (u32x4){h0.x, h0.y, h1.x, h1.y});
                     const half8 vlb = __builtin_bit_cast(half8, (u32x4){l0.x, l0.y, l1.x, l1.y});
                     mfma16(pa_h64[kh2], vh, blk[dt]);
@@ -379,20 +389,38 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
             for (int dt = 0; dt < 8; ++dt) acc[dt][e] = __builtin_fmaf(acc[dt][e], f_e, blk[dt][e]);
         }
     };
+
+    // block 0 unpacked into the first planes; block 1's codes and block 0's
+    // scales in flight
     load_raw(0);
-    for (int kb = 0; kb + 1 < nkb; ++kb) key_block(kb, std::false_type{});
-    key_block(nkb - 1, std::true_type{});
+    write_planes(lds);
+    load_scales(0);
+    load_raw(1);
+    for (int kb = 0; kb < nkb; ++kb) {
+        // block kb's planes are complete, and every wave is done with block
+        // kb - 1, whose planes block kb + 1 now takes
+        __syncthreads();
+        unsigned char* cur = lds + (kb & 1) * BUF;
+        unsigned char* nxt = lds + ((kb + 1) & 1) * BUF;
+        if (kb + 1 < nkb_w) key_block(kb, cur, std::false_type{});
+        else if (kb + 1 == nkb_w) key_block(kb, cur, std::true_type{});
+        if (kb + 1 < nkb) write_planes(nxt);
+        load_scales(kb + 1);
+        load_raw(kb + 2);
+    }
 
     // ---- normalize and store: rows q0 + 4 grp + e, d = 16 dt + c
+    if (nkb_w > 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float l_e = from_lane(l_run, 4 * grp + e);
-        const int qrow = q0 + 4 * grp + e;
-        if (qrow < T) {
-            float* o = out + (((int64_t)b * T + qrow) * Hq + h) * D + c;
-            const float inv = 1.0f / l_e;
+        for (int e = 0; e < 4; ++e) {
+            const float l_e = from_lane(l_run, 4 * grp + e);
+            const int qrow = q0 + 4 * grp + e;
+            if (qrow < T) {
+                float* o = out + (((int64_t)b * T + qrow) * Hq + h) * D + c;
+                const float inv = 1.0f / l_e;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) o[16 * dt] = acc[dt][e] * beta_run * inv;
+                for (int dt = 0; dt < 8; ++dt) o[16 * dt] = acc[dt][e] * beta_run * inv;
+            }
         }
     }
 }
@@ -405,7 +433,7 @@ hipError_t launch_attn_prefill(const int16_t* q, const float* qs, const int16_t*
     if (Dd != D) return hipErrorInvalidValue;
     const int nqb = (int)((T + QB - 1) / QB);
     const unsigned blocks = (unsigned)(B * Hq * nqb);
-    hipLaunchKernelGGL(attn_prefill_kernel, dim3(blocks), dim3(256), 0, s, q, qs, k, ks, v, vs, out, (int)T,
+    hipLaunchKernelGGL(attn_prefill_kernel, dim3(blocks), dim3(64 * WPB), 0, s, q, qs, k, ks, v, vs, out, (int)T,
                        (int)Hq, (int)Hkv, nqb, (int)(B * Hq));
     return hipGetLastError();
 }
