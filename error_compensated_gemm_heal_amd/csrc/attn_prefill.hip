@@ -250,7 +250,7 @@ __global__ __launch_bounds__(64 * WPB) void attn_prefill_kernel(
     //      and the output: lane (c, grp) holds d = 16 dt + c of queries
     //      q0 + 4 grp + e in acc[dt][e]
     float m_run = -INFINITY, l_run = 0.0f;
-    float beta_run = 1.0f;   // the output's current block factor (acc holds out / beta_run)
+    int ebeta_run = 0;       // the output's current block factor 2^ebeta_run (acc holds out / 2^ebeta_run)
     floatx4 acc[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[dt] = (floatx4){0.f, 0.f, 0.f, 0.f};
@@ -312,8 +312,8 @@ __global__ __launch_bounds__(64 * WPB) void attn_prefill_kernel(
         int vexp = 0;
         (void)frexpf(vmax, &vexp);
         // x = p s_v(t) 2^(9 - E) lies in [0, 512); its block factor 2^(E - 9)
-        const float p2 = vmax > 0.0f ? ldexpf(1.0f, 9 - vexp) : 1.0f;
-        const float beta = vmax > 0.0f ? ldexpf(1.0f, vexp - 9) : 1.0f;
+        const int ebeta = vmax > 0.0f ? vexp - 9 : 0;
+        const float p2 = ldexpf(1.0f, -ebeta);
 
         // ---- P as the A operand for key halves kh2 = 0, 1 (32 keys each):
         //      slot i = key 32 kh2 + 16 (i / 4) + 4 grp + i % 4.  The weight
@@ -380,8 +380,8 @@ __global__ __launch_bounds__(64 * WPB) void attn_prefill_kernel(
         //      out = acc beta, so acc <- acc alpha (beta_old / beta) + blk (the
         //      ratio is a power of two, exact); lane (c, grp) holds the rows of
         //      queries 4 grp + e, whose alpha sits on lane 4 grp + e
-        const float ratio = beta_run / beta;
-        beta_run = beta;
+        const float ratio = ldexpf(1.0f, ebeta_run - ebeta);
+        ebeta_run = ebeta;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float f_e = from_lane(alpha, 4 * grp + e) * ratio;
@@ -411,6 +411,7 @@ __global__ __launch_bounds__(64 * WPB) void attn_prefill_kernel(
 
     // ---- normalize and store: rows q0 + 4 grp + e, d = 16 dt + c
     if (nkb_w > 0) {
+        const float beta_run = ldexpf(1.0f, ebeta_run);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float l_e = from_lane(l_run, 4 * grp + e);
