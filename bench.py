@@ -292,27 +292,35 @@ def make_rows(W):
 
 
 def cpu_baseline(seconds):
-    """The oracle's FP64 GEMM, as it stands, on a row sample of the prefill shape."""
+    """The oracle's FP64 GEMM, as it stands, on a row sample of the two prefill shapes:
+    rows of the first shape, then of the second, until about `seconds` of CPU work."""
     import numpy as np
     import heal_workloads as WL
     import oracle
-    K, N = WL.PREFILL_KN[0]
-    A, Wt = WL.prefill_gemm(WL.PREFILL_M, K, N, seed=3000)
     nth = oracle.num_threads()
-    probe = np.arange(nth, dtype=np.int64)
-    t0 = time.perf_counter()
-    oracle.gemm_f64_rows(A, Wt, probe)
-    dt = time.perf_counter() - t0
-    # dt covers nth rows: scale the sample to about `seconds` of CPU work (whole multiples of nth)
-    nrows = int(max(nth, min(WL.PREFILL_M, round(seconds / max(dt, 1e-6)) * nth)))
-    rows = np.arange(nrows, dtype=np.int64)
-    t0 = time.perf_counter()
-    oracle.gemm_f64_rows(A, Wt, rows)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * nrows * N * K
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nth, "kind": "oracle",
-            "sample": f"FP64-accumulated GEMM (the oracle) on {nrows} of the 2048 rows of the "
-                      f"M=2048, K={K}, N={N} prefill shape; {dt:.1f} s"}
+    flops, total, parts = 0.0, 0.0, []
+    for K, N in WL.PREFILL_KN:
+        left = seconds - total
+        if left <= 0.5:
+            break
+        A, Wt = WL.prefill_gemm(WL.PREFILL_M, K, N, seed=3000)
+        probe = np.arange(nth, dtype=np.int64)
+        t0 = time.perf_counter()
+        oracle.gemm_f64_rows(A, Wt, probe)
+        dt = time.perf_counter() - t0
+        # dt covers nth rows: scale the sample to the time left (whole multiples of nth)
+        nrows = int(max(nth, min(WL.PREFILL_M, round(left / max(dt, 1e-6)) * nth)))
+        rows = np.arange(nrows, dtype=np.int64)
+        t0 = time.perf_counter()
+        oracle.gemm_f64_rows(A, Wt, rows)
+        dt = time.perf_counter() - t0
+        flops += 2.0 * nrows * N * K
+        total += dt
+        parts.append(f"{nrows} of the {WL.PREFILL_M} rows of K={K}, N={N}")
+        del A, Wt
+    return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": nth, "kind": "oracle",
+            "sample": "FP64-accumulated GEMM (the oracle) on the prefill shapes: " + "; ".join(parts) +
+                      f"; {total:.1f} s"}
 
 
 def main():
@@ -402,7 +410,8 @@ def main():
            "dtype": "fp32 in/out; fp16 hi/lo MFMA products, fp32 accumulate; int16 codes",
            "data": "synthetic (seeded; model-shaped, see heal_workloads.py)"}
     cfg = {"workload": "HEAL hot path step: split + prefill GEMM (M=2048; K,N = 4096,14336 and 14336,4096; "
-                       "fp32 weights, and fp16 weights in the two-product form), "
+                       "fp32 weights; also fp16 weights in the two-product form, the one-product mode and the "
+                       "BF16 three-way mode), "
                        "16 decode GEMMs (M=1,8,32,64 x Llama-3-8B q/o, k/v, gate/up, down; fp32 and fp16 weights, "
                        "and fp32 with per-channel rescaled massive activations), "
                        "fused Q/K/V projection to INT16 (2048 tokens, K=4096, N=6144), "
