@@ -279,8 +279,9 @@ __global__ __launch_bounds__(64 * WPB) void attn_prefill_kernel(
             for (int e = 0; e < 4; ++e) {
                 sc[4 * st + e] = (64.0f * s_hi[e] + s_lo[e]) * (qscale * ksv[4 * st + e]);
                 if constexpr (decltype(masked)::value) {
+                    // an added -inf rather than a branch (the score is finite)
                     const int key = kb * KB + 16 * st + 4 * grp + e;
-                    if (!(key <= qi && key < T)) sc[4 * st + e] = -INFINITY;
+                    sc[4 * st + e] += (key <= qi && key < T) ? 0.0f : -INFINITY;
                 }
             }
         }

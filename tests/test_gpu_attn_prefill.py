@@ -50,7 +50,8 @@ def _check(B, T, Hq, Hkv, seed, inputs=None):
 
 
 @pytest.mark.parametrize("B,T,Hq,Hkv", [(1, 1, 4, 1), (1, 5, 2, 2), (1, 64, 4, 2), (2, 100, 8, 2),
-                                        (1, 129, 4, 4), (1, 257, 6, 3), (2, 333, 16, 2), (1, 1000, 8, 1)])
+                                        (1, 129, 4, 4), (1, 192, 4, 2), (1, 257, 6, 3), (2, 333, 16, 2),
+                                        (1, 383, 8, 4), (1, 1000, 8, 1)])
 def test_attn_prefill_shapes(B, T, Hq, Hkv):
     o = _check(B, T, Hq, Hkv, seed=B * 1000 + T)
     if T >= 1:   # position 0 attends only itself: its output is token 0's value row
