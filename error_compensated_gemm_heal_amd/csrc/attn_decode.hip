@@ -37,6 +37,8 @@
 //  * the 4 waves merge their (m, l, o) in LDS, each block writes one partial
 //    for its range, and a second kernel merges the ranges of a head in
 //    range order.
+#include <algorithm>
+
 #include "heal_internal.h"
 
 namespace heal {
@@ -394,43 +396,72 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 
 // Merge the token ranges of one (b, h), in range order:
 //   out = sum_u w_u o_u / sum_u w_u l_u,   w_u = 2^(m_u - max_u m_u).
-// One pass: each thread (one d) reads (m_u, l_u, o_u[d]) for 16 ranges at a
-// time with independent loads and folds them into a running (M, L, O).
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part,
-                                                           float* __restrict__ out, int Hq, int Hkv,
-                                                           int G, int units) {
+// Up to four groups of D threads (one d each; one group per 8 ranges) take
+// consecutive shares of the ranges; each folds (m_u, l_u, o_u[d]) of its share
+// into a running (M, L, O), loading CB ranges at a time with independent
+// loads, and group 0 merges the groups in order.  The order depends on the
+// number of ranges only.
+constexpr int CNG = 4;   // most range groups per (b, h)
+constexpr int CB = 8;    // ranges per round of loads
+int combine_groups(int units) { return std::min(CNG, (units + CB - 1) / CB); }
+__global__ __launch_bounds__(CNG * D) void attn_combine_kernel(const float* __restrict__ part,
+                                                               float* __restrict__ out, int Hq, int Hkv,
+                                                               int G, int units) {
+    __shared__ float sm[CNG], sl[CNG], so[CNG][D];
     const int bh = blockIdx.x;
     const int b = bh / Hq, h = bh - b * Hq;
     const int gk = h / G, c = h - gk * G;
-    const int d = threadIdx.x;
+    const int d = threadIdx.x % D;
+    const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / D);
+    const int ng = blockDim.x / D;
+    const int per = (units + ng - 1) / ng;
+    const int ub = grp * per, ue = min(units, ub + per);
     const int64_t stride = 2 * G + G * D;
     const float* base = part + ((int64_t)b * Hkv + gk) * units * stride;
     float M = -INFINITY, L = 0.0f, O = 0.0f;
-    for (int u0 = 0; u0 < units; u0 += 16) {
-        float mu[16], lu[16], ou[16];
+    for (int u0 = ub; u0 < ue; u0 += CB) {
+        float mu[CB], lu[CB], ou[CB];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int u = min(u0 + i, units - 1);
+        for (int i = 0; i < CB; ++i) {
+            const int u = min(u0 + i, ue - 1);
             mu[i] = base[u * stride + c];
             lu[i] = base[u * stride + G + c];
             ou[i] = base[u * stride + 2 * G + c * D + d];
         }
         float mc = M;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            if (u0 + i < units) mc = fmaxf(mc, mu[i]);
+        for (int i = 0; i < CB; ++i)
+            if (u0 + i < ue) mc = fmaxf(mc, mu[i]);
         const float r = M > -INFINITY ? __builtin_amdgcn_exp2f(M - mc) : 0.0f;
         L *= r;
         O *= r;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float w = (u0 + i < units && mu[i] > -INFINITY) ? __builtin_amdgcn_exp2f(mu[i] - mc) : 0.0f;
+        for (int i = 0; i < CB; ++i) {
+            const float w = (u0 + i < ue && mu[i] > -INFINITY) ? __builtin_amdgcn_exp2f(mu[i] - mc) : 0.0f;
             L += w * lu[i];
             O += w * ou[i];
         }
         M = mc;
     }
-    out[(int64_t)bh * D + d] = O / L;
+    if (d == 0) {
+        sm[grp] = M;
+        sl[grp] = L;
+    }
+    so[grp][d] = O;
+    __syncthreads();
+    if (grp == 0) {
+        // every range holds at least one token with a finite score, so the
+        // maximum over the groups is finite; an empty group carries weight 0
+        float mx = sm[0];
+        for (int g = 1; g < ng; ++g) mx = fmaxf(mx, sm[g]);
+        float Lt = 0.0f, Ot = 0.0f;
+        for (int g = 0; g < ng; ++g) {
+            const float w = sm[g] > -INFINITY ? __builtin_amdgcn_exp2f(sm[g] - mx) : 0.0f;
+            Lt += w * sl[g];
+            Ot += w * so[g][d];
+        }
+        out[(int64_t)bh * D + d] = Ot / Lt;
+    }
 }
 
 }  // namespace
@@ -462,7 +493,7 @@ hipError_t launch_attn_decode(const int16_t* q, const float* qs, const int16_t* 
 #undef HEAL_ATT
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(B * Hq)), dim3(D), 0, s, part, out, (int)Hq,
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(B * Hq)), dim3(combine_groups(units) * D), 0, s, part, out, (int)Hq,
                        (int)Hkv, G, units);
     return hipGetLastError();
 }

@@ -51,7 +51,8 @@ def test_attn_single_token_is_value_row():
 
 
 @pytest.mark.parametrize("B,T,Hq,Hkv", [(1, 5, 4, 1), (2, 37, 8, 2), (1, 128, 4, 4), (2, 300, 6, 3),
-                                        (1, 129, 8, 1), (3, 1000, 16, 2), (1, 257, 7, 1), (2, 64, 2, 2)])
+                                        (1, 129, 8, 1), (3, 1000, 16, 2), (1, 257, 7, 1), (2, 64, 2, 2),
+                                        (1, 3000, 8, 2), (1, 20000, 8, 8)])
 def test_attn_ragged_shapes(B, T, Hq, Hkv):
     _check(B, T, Hq, Hkv, seed=B * 100 + T)
 
