@@ -11,6 +11,8 @@ using namespace heal;
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
+// a launch's thread count must fit the dispatch packet's 32-bit grid size
+bool fits_u32(__int128 threads) { return threads < ((__int128)1 << 32); }
 
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
@@ -327,6 +329,7 @@ heal_status heal_kv_dequant_i16(const int16_t* codes, int64_t rows, int64_t D, i
 
 size_t heal_attn_decode_workspace(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D) {
     if (B <= 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return 0;
+    if (B >= kMaxDim || T >= kMaxDim || Hq >= kMaxDim || Hkv >= kMaxDim) return 0;   // no valid call
     return (size_t)attn_workspace_bytes(B, T, Hq, Hkv, D);
 }
 
@@ -334,12 +337,17 @@ heal_status heal_attn_decode_i16(const int16_t* q, const float* q_scale, const i
                                  const float* k_scale, const int16_t* v, const float* v_scale,
                                  float* out, int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
                                  void* workspace, size_t workspace_bytes, void* stream) {
-    if (B < 0 || T < 0 || Hq < 0 || Hkv < 0 || D < 0 || B >= kMaxDim || T >= kMaxDim) return HEAL_ERR_SHAPE;
+    if (B < 0 || T < 0 || Hq < 0 || Hkv < 0 || D < 0 || B >= kMaxDim || T >= kMaxDim || Hq >= kMaxDim ||
+        Hkv >= kMaxDim)
+        return HEAL_ERR_SHAPE;
     if (B == 0 || Hq == 0) return HEAL_OK;
     if (Hkv == 0 || Hq % Hkv) return HEAL_ERR_SHAPE;
     if (T == 0) return HEAL_ERR_SHAPE;
     if (D != 128 || Hq / Hkv > 8 || T > 262144) return HEAL_ERR_UNSUPPORTED;
     if (T * Hkv * D * 2 >= ((int64_t)1 << 32)) return HEAL_ERR_UNSUPPORTED;   // 32-bit offsets per batch
+    // launch sizes in threads (32-bit): the range kernel and the merge
+    if (!fits_u32((__int128)B * Hkv * ((T + 255) / 256) * 256) || !fits_u32((__int128)B * Hq * 512))
+        return HEAL_ERR_UNSUPPORTED;
     if (!q || !q_scale || !k || !k_scale || !v || !v_scale || !out) return HEAL_ERR_NULL;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
         misaligned(q_scale, 4) || misaligned(k_scale, 4) || misaligned(v_scale, 4))
@@ -356,10 +364,13 @@ heal_status heal_attn_decode_i16(const int16_t* q, const float* q_scale, const i
 heal_status heal_attn_prefill_i16(const int16_t* q, const float* q_scale, const int16_t* k,
                                   const float* k_scale, const int16_t* v, const float* v_scale, float* out,
                                   int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, void* stream) {
-    if (B < 0 || T < 0 || Hq < 0 || Hkv < 0 || D < 0 || B >= kMaxDim || T >= kMaxDim) return HEAL_ERR_SHAPE;
+    if (B < 0 || T < 0 || Hq < 0 || Hkv < 0 || D < 0 || B >= kMaxDim || T >= kMaxDim || Hq >= kMaxDim ||
+        Hkv >= kMaxDim)
+        return HEAL_ERR_SHAPE;
     if (B == 0 || T == 0 || Hq == 0) return HEAL_OK;
     if (Hkv == 0 || Hq % Hkv) return HEAL_ERR_SHAPE;
-    if (D != 128 || T > 262144 || B * Hq * ((T + 63) / 64) >= kMaxDim) return HEAL_ERR_UNSUPPORTED;
+    if (D != 128 || T > 262144 || !fits_u32((__int128)B * Hq * ((T + 127) / 128) * 512))
+        return HEAL_ERR_UNSUPPORTED;   // launch size in threads (32-bit)
     if (T * Hkv * D * 2 >= ((int64_t)1 << 32)) return HEAL_ERR_UNSUPPORTED;   // 32-bit offsets per batch
     if (!q || !q_scale || !k || !k_scale || !v || !v_scale || !out) return HEAL_ERR_NULL;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 4) ||

@@ -333,7 +333,9 @@ heal_status heal_kv_dequant_i16(const int16_t* codes, int64_t rows, int64_t D, i
  *   bytes, 256-byte aligned.  All tensors dense, 16-byte aligned.
  * Limits: D == 128, Hq % Hkv == 0, Hq / Hkv <= 8, 1 <= T <= 262144 and
  * T * Hkv * D * 2 < 2^32 (one batch's K or V block is addressed with 32-bit
- * byte offsets) when B*Hq > 0; otherwise HEAL_ERR_UNSUPPORTED.
+ * byte offsets) when B*Hq > 0; the launches' thread counts
+ * B * Hkv * ceil(T / 256) * 256 and B * Hq * 512 below 2^32; otherwise
+ * HEAL_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------ */
 heal_status heal_attn_decode_i16(const int16_t* q, const float* q_scale,
                                  const int16_t* k, const float* k_scale,
@@ -357,8 +359,9 @@ size_t heal_attn_decode_workspace(int64_t B, int64_t T, int64_t Hq, int64_t Hkv,
  *   k, v   device int16 [B, T, Hkv, D] (the decode cache layout), 16-byte
  *          aligned; k_scale, v_scale fp32 [B, T, Hkv]
  *   out    device fp32 [B, T, Hq, D], 4-byte aligned
- * Limits: D = 128; Hq % Hkv == 0; T <= 262144; T Hkv D 2 < 2^32.  No
- * workspace.
+ * Limits: D = 128; Hq % Hkv == 0; T <= 262144; T Hkv D 2 < 2^32; the
+ * launch's thread count B Hq ceil(T / 128) 512 below 2^32 (else
+ * HEAL_ERR_UNSUPPORTED).  No workspace.
  * ------------------------------------------------------------------------ */
 heal_status heal_attn_prefill_i16(const int16_t* q, const float* q_scale, const int16_t* k,
                                   const float* k_scale, const int16_t* v, const float* v_scale, float* out,

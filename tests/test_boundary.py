@@ -243,6 +243,10 @@ def test_attention_prefill_validation():
     assert f(*args(q=None)) == NULL
     assert f(*args(q=ctypes.c_void_p(0x10008))) == ALIGN
     assert f(*args(o=ctypes.c_void_p(0x10002))) == ALIGN
+    assert f(*args(Hq=1 << 40, Hkv=1 << 40)) == SHAPE
+    # 2^14 batches x 64 heads x 2048 query blocks x 512 threads: past the 32-bit grid size
+    assert f(*args(B=1 << 14, T=262144, Hq=64, Hkv=1)) == UNSUP
+    assert f(*args(B=1 << 14, T=64, Hq=64, Hkv=1, q=None)) == NULL   # the same heads at T = 64 fit
 
 
 def test_attention_validation():
@@ -254,6 +258,11 @@ def test_attention_validation():
     assert _attn(Hq=18, Hkv=1) == UNSUP
     assert _attn(T=262145) == UNSUP
     assert _attn(T=131072, Hq=128, Hkv=128) == UNSUP   # K block of one batch past 4 GiB
+    assert _attn(Hq=1 << 40, Hkv=1 << 40) == SHAPE
+    # launch sizes past the 32-bit grid size: the range kernel, then the merge
+    assert _attn(B=1 << 20, T=8192, Hq=8, Hkv=8) == UNSUP
+    assert _attn(B=1 << 24, T=1, Hq=1, Hkv=1) == UNSUP
+    assert _attn(B=1 << 12, T=8192, Hq=8, Hkv=8, q=None) == NULL   # within both
     assert _attn(q=None) == NULL
     assert _attn(q=ctypes.c_void_p(0x10008)) == ALIGN
     assert _attn(ws=None) == WS
