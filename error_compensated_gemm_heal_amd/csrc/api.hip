@@ -143,6 +143,12 @@ heal_status gemm_impl(const float* A, int64_t lda, const void* W, int64_t ldw, f
         return hip_status(hipGetLastError());
     }
     if (!A || !W) return HEAL_ERR_NULL;
+    // launch sizes in threads (32-bit): the prefill grid (256 x 256 tiles,
+    // at most two k halves) and the decode grid (one 64-row group per 256
+    // threads, about 512 workgroups in all when the rows are few)
+    if (!fits_u32((__int128)((M + 255) / 256) * ((N + 255) / 256) * 2 * 256) ||
+        !fits_u32((__int128)((N + 63) / 64) * 256 + 512 * 512))
+        return HEAL_ERR_UNSUPPORTED;
     const bool packed = flags & HEAL_W_PACKED;
     const bool a_packed = flags & HEAL_A_PACKED;
     const bool kn = flags & HEAL_W_KN;

@@ -171,7 +171,10 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  * runs ~14% faster (measured at K = 4096, N = 14336).
  * Limits: M, N, K < 2^31.  K == 0 writes zeros.  In the M <= 64 case above,
  * ldw < 2^26 and lda < 2^24 (each 16-row slice of W, and A, are addressed
- * with 32-bit byte offsets), else HEAL_ERR_UNSUPPORTED.
+ * with 32-bit byte offsets), else HEAL_ERR_UNSUPPORTED.  The launches'
+ * thread counts must fit 32 bits: ceil(M/256) ceil(N/256) 512 and
+ * ceil(N/64) 256 + 2^18 below 2^32 (M N below about 2^39, N below about
+ * 2^30), else HEAL_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------ */
 heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t ldw,
                            float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,

@@ -62,6 +62,9 @@ def _gemm(A=FAKE, lda=4096, W=FAKE, ldw=4096, C=FAKE, ldc=4096, M=8, N=4096, K=4
 def test_gemm_validation():
     assert _gemm(M=-1) == SHAPE
     assert _gemm(K=1 << 31) == SHAPE
+    # launches past the 32-bit grid size (in threads): prefill tiles, then decode row groups
+    assert _gemm(M=1 << 20, N=1 << 20, K=64, lda=64, ldw=64, ldc=1 << 20) == UNSUP
+    assert _gemm(M=1, N=1 << 30, K=64, lda=64, ldw=64, ldc=1 << 30) == UNSUP
     assert _gemm(flags=heal.HEAL_W_F16 | heal.HEAL_W_PACKED, W=ctypes.c_void_p(0x10010)) == ALIGN  # packed: 256 B
     assert _gemm(flags=64) == UNSUP
     X3 = heal.HEAL_BF16X3
