@@ -90,6 +90,12 @@ def test_attn_prefill_full_size_sampled_positions():
     _check(1, 2048, 32, 8, seed=5500)
 
 
+def test_attn_prefill_long_prompt_sampled_positions():
+    """An 8191-token prompt (64 query blocks, the last one ragged; 128 key
+    blocks for the last queries), sampled positions against the binary64 oracle."""
+    _check(1, 8191, 8, 2, seed=5501)
+
+
 def test_attn_prefill_pipeline_with_gpu_quantizer_and_last_position_equals_decode():
     """GPU quantizer -> prefill attention; its last position equals decode attention
     of the same query over the same cache within the tolerance of each."""
