@@ -33,6 +33,8 @@ def lib():
             "oracle_gemm_f64": [_p, _c_i64, _p, _c_i64, ctypes.c_int, _p, _c_i64, _c_i64, _c_i64, _c_i64],
             "oracle_gemm_f32_naive": [_p, _c_i64, _p, _c_i64, ctypes.c_int, _p, _c_i64, _c_i64, _c_i64, _c_i64],
             "oracle_gemm_comp_model": [_p, _c_i64, _p, _c_i64, ctypes.c_int, _p, _c_i64, _c_i64, _c_i64, _c_i64],
+            "oracle_row_exponent": [_p, _c_i64, _c_i64, _c_i64, _p],
+            "oracle_split_rownorm": [_p, _c_i64, _c_i64, _c_i64, _p, _p, _p],
             "oracle_gemm_f64_rows": [_p, _c_i64, _p, _c_i64, ctypes.c_int, _p, _c_i64, _p, _c_i64, _c_i64, _c_i64],
             "oracle_gemm_f32_naive_rows": [_p, _c_i64, _p, _c_i64, ctypes.c_int, _p, _c_i64, _p, _c_i64, _c_i64, _c_i64],
             "oracle_quant_i16": [_p, _c_i64, _c_i64, _c_i64, _p, _c_i64, _p],
@@ -90,6 +92,51 @@ def split_f16(x):
     lo = np.empty(x.shape, np.uint16)
     lib().oracle_split_f16(_ptr(x), x.size, _ptr(hi), _ptr(lo))
     return hi, lo
+
+
+# --- row normalization ------------------------------------------------------------
+
+def row_exponent(X):
+    """X float32 [rows, K] -> int32 [rows]: e with 2^14 <= max_k |x_k| 2^e < 2^15
+    (0 for a zero row).  HEAL paper, section 3, "Mitigating GEMM Truncation via
+    FP16 Promotion and Algebraic Compensation" (FP16's narrow range, handled by
+    targeted power-of-two rescaling)."""
+    X = _c(X, np.float32)
+    rows, K = X.shape
+    e = np.empty(rows, np.int32)
+    lib().oracle_row_exponent(_ptr(X), rows, K, K, _ptr(e))
+    return e
+
+
+def split_rownorm(X):
+    """X float32 [rows, K] -> (hi, res) binary16 bit patterns of x' = x 2^e_r and
+    e int32 [rows]: hi = fp16(x'), res = fp16(x' - hi)."""
+    X = _c(X, np.float32)
+    rows, K = X.shape
+    hi = np.empty((rows, K), np.uint16)
+    res = np.empty((rows, K), np.uint16)
+    e = np.empty(rows, np.int32)
+    lib().oracle_split_rownorm(_ptr(X), rows, K, K, _ptr(hi), _ptr(res), _ptr(e))
+    return hi, res, e
+
+
+def gemm_rownorm_model(A, W, w_layout="nk", norm_w=True):
+    """Representation model of the compensated GEMM on row-normalized operands
+    (diagnostic): (A'_hi.B'_hi + A'_hi.B'_res + A'_res.B'_hi) 2^-(e_a + e_b) in
+    binary64, the three 16-bit products of the paper's expansion.  norm_w =
+    False leaves B unnormalized (e_b = 0), as for a weight held in binary16."""
+    A = _c(A, np.float32)
+    Wn = _c(W, np.float32) if w_layout == "nk" else np.ascontiguousarray(np.asarray(W, np.float32).T)
+    ah, ar, ea = split_rownorm(A)
+    if norm_w:
+        bh, br, eb = split_rownorm(Wn)
+    else:
+        bh, br = split_f16(Wn)
+        br = np.zeros_like(br)
+        eb = np.zeros(Wn.shape[0], np.int32)
+    f = f16_bits_to_f64
+    C = f(ah) @ f(bh).T + f(ah) @ f(br).T + f(ar) @ f(bh).T
+    return np.ldexp(C, -(ea[:, None] + eb[None, :]).astype(np.int64))
 
 
 # --- GEMM -----------------------------------------------------------------------

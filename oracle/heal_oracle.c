@@ -240,6 +240,67 @@ ORACLE_API void oracle_gemm_comp_model(const float* A, int64_t lda, const float*
 }
 
 /* ------------------------------------------------------------------------ */
+/* Row normalization by a power of two, and the split of a normalized row.  */
+/* [HEAL §3, "Mitigating GEMM Truncation via FP16 Promotion and Algebraic   */
+/*  Compensation"]: FP16's narrow dynamic range is the method's weak point  */
+/*  (values beyond it overflow, values below it lose bits), and the pages   */
+/*  answer it by targeted rescaling.  Reading taken: every operand row is   */
+/*  multiplied by the power of two 2^e that brings its largest magnitude    */
+/*  into [2^14, 2^15) -- the top binade that cannot round past 65504 --     */
+/*  before its split, and the product is multiplied back by 2^-(e_a + e_b). */
+/*  Powers of two are exact in binary floating point, so the product is    */
+/*  unchanged; the split then sees every significant element of the row in  */
+/*  FP16's normal range, whatever the row's own scale.                      */
+/* ------------------------------------------------------------------------ */
+
+/* e = 14 - floor(log2(max_k |x_k|)), so that 2^14 <= max * 2^e < 2^15;
+ * e = 0 for a row of zeros.  frexp gives max = f * 2^p with f in [0.5, 1),
+ * i.e. floor(log2(max)) = p - 1, exactly, subnormal binary32 included.
+ * Pinned by the defining inequality on rows spanning binary32's range.    */
+static int32_t row_exponent(const float* x, int64_t K)
+{
+    double m = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double a = fabs((double)x[k]);
+        if (a > m) m = a;
+    }
+    if (m == 0.0) return 0;
+    int p;
+    (void)frexp(m, &p);
+    return 14 - (p - 1);
+}
+
+ORACLE_API void oracle_row_exponent(const float* X, int64_t rows, int64_t K, int64_t ldx, int32_t* e)
+{
+    for (int64_t r = 0; r < rows; ++r) e[r] = row_exponent(X + r * ldx, K);
+}
+
+/* Split of a normalized row: x' = x * 2^e (binary32, rounded once: exact
+ * unless it falls below binary32's subnormal quantum), hi = rne16(x'),
+ * res = rne16(x' - hi) with x' - hi exact in binary32.  This is the dual-FP16
+ * pair of the pages with the residual kept at its own scale: res equals
+ * lo / 2^10 of oracle_split_f16(x') whenever that is a normal binary16, which
+ * on a normalized row holds for every element above 2^-17 of the row's
+ * largest.  Pinned against numpy's binary16 conversion and against
+ * oracle_split_f16.                                                        */
+ORACLE_API void oracle_split_rownorm(const float* X, int64_t rows, int64_t K, int64_t ldx,
+                                     uint16_t* hi, uint16_t* res, int32_t* e)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* x = X + r * ldx;
+        int32_t er = row_exponent(x, K);
+        e[r] = er;
+        for (int64_t k = 0; k < K; ++k) {
+            float xs = (float)ldexp((double)x[k], er);
+            uint16_t h = f32_to_f16_bits(xs);
+            float rr = xs - (float)f16_bits_to_f64(h);
+            hi[r * K + k] = h;
+            res[r * K + k] = f32_to_f16_bits(rr);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* INT16 quantizer.                                                         */
 /* [HEAL §3, "Mitigating QKV Truncation Error via INT16 Quantization"]:     */
 /*  Q_INT16(X) = Round((2^15 - 1) X / max|X|), step Delta = M / (2^15 - 1). */
