@@ -110,8 +110,7 @@ heal_status heal_pack_w(const void* W, int64_t ldw, int64_t N, int64_t K, uint32
 size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags) {
     if (M <= 0 || N <= 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return 0;
     if (use_decode(M, K, flags)) {
-        const DecodePlan p = decode_plan(M, N, K);
-        return (size_t)(round256(p.a_bytes) + round256(p.p_bytes));
+        return (size_t)decode_plan(M, N, K).bytes();
     }
     int64_t b = (flags & HEAL_A_PACKED) ? 0 : round256(packed_bytes(M, K, flags & HEAL_BF16X3));
     if (!(flags & HEAL_W_PACKED)) b += round256(packed_bytes(N, K, flags));
@@ -271,10 +270,12 @@ heal_status heal_qkv_quant_i16(const float* X, int64_t rows, int64_t D, int64_t 
 
 size_t heal_qkv_proj_quant_workspace(int64_t M, int64_t K, int64_t Hq, int64_t Hkv, int64_t D,
                                      uint32_t flags) {
-    if (M <= 0 || K <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || M >= kMaxDim || K >= kMaxDim) return 0;
+    if (M <= 0 || K < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || M >= kMaxDim || K >= kMaxDim) return 0;
     const int64_t N = (Hq + 2 * Hkv) * D;
     if (N >= kMaxDim) return 0;
-    const size_t gemm = heal_gemm_f32c_workspace(M, N, K, flags);
+    const size_t gemm = heal_gemm_f32c_workspace(M, N, K, flags);   // 0 when K == 0
+    // unless the GEMM quantizes in its epilogue, the fp32 product is staged
+    // here (K == 0 included: a zero product, quantized to zero codes)
     return qkv_fused(M, N, K, D, flags) ? gemm : (size_t)round256(M * N * 4) + gemm;
 }
 
@@ -305,11 +306,14 @@ heal_status heal_qkv_proj_quant_i16(const float* A, int64_t lda, const void* W, 
         return gemm_impl(A, lda, W, ldw, nullptr, N, M, N, K, flags, a_kshift, workspace, workspace_bytes, dev_status,
                          stream, &dst);
     }
-    // the fp32 product lands in the workspace, the GEMM's own workspace after it
+    // the fp32 product lands in the workspace, the GEMM's own workspace after
+    // it (need >= round256(M N 4) was checked above, so the rest is >= 0)
     float* C = static_cast<float*>(workspace);
-    unsigned char* gws = static_cast<unsigned char*>(workspace) + round256(M * N * 4);
+    const size_t cbytes = (size_t)round256(M * N * 4);
+    if (need < cbytes || workspace_bytes < cbytes) return HEAL_ERR_WORKSPACE;
+    unsigned char* gws = static_cast<unsigned char*>(workspace) + cbytes;
     const heal_status st = heal_gemm_f32c(A, lda, W, ldw, C, N, M, N, K, flags, a_kshift, gws,
-                                          workspace_bytes - (size_t)round256(M * N * 4), dev_status, stream);
+                                          workspace_bytes - cbytes, dev_status, stream);
     if (st != HEAL_OK) return st;
     return hip_status(launch_quant_qkv(C, M, Hq, Hkv, D, q_codes, q_scales, slot_mapping, num_slots, k_cache,
                                        k_scales, v_cache, v_scales, dev_status, static_cast<hipStream_t>(stream)));

@@ -6,15 +6,20 @@
 // but shaped for a skinny activation, where the weight is the traffic:
 //  * W is read once from HBM as fp32 [N, K] (4 bytes per element, the same
 //    bytes as its two fp16 parts) and split into hi/lo in registers;
+//  * FP16's narrow range (the same paragraph: handled by targeted
+//    rescaling): a small first kernel (decode_prep_kernel, one workgroup per
+//    activation row) finds each row's largest magnitude and the power of two
+//    2^e that puts it in [2^14, 2^15); rows are split as x 2^e and each
+//    output is multiplied back by 2^-e in fp32, so the result does not
+//    depend on the activation's absolute scale (W is split as it is);
 //  * the activation (<= 64 rows) is staged in 128-wide k blocks in a
 //    double-buffered LDS tile, in MFMA operand order, so every operand read
 //    is one conflict-free 16-byte LDS access.  Up to 16 rows, each
 //    workgroup loads the next block into registers while the current one
-//    is in use and splits it into hi/lo itself (no extra pass or launch);
-//    above 16 rows, where that split would be repeated by every workgroup,
-//    a small kernel splits the activation once per call into operand-ordered
-//    planes (asplit_kernel) and workgroups copy blocks of them into LDS with
-//    direct-to-LDS loads;
+//    is in use and normalizes and splits it itself; above 16 rows, where that
+//    split would be repeated by every workgroup, the first kernel also writes
+//    the split rows as operand-ordered planes and workgroups copy blocks of
+//    them into LDS with direct-to-LDS loads;
 //  * v_mfma_f32_16x16x32_f16 with the activation as the 16-row operand and W
 //    as the 16-column operand (16 W rows per wave), so output columns are
 //    consecutive lanes;
@@ -67,50 +72,54 @@ __device__ __forceinline__ void mfma16(const half8& a, const half8& b, floatx4& 
 template <int MT>
 constexpr int block_bytes() { return 2 * STEPS * MT * 64 * 16; }
 
-// ---- activation split into operand order --------------------------------
-// Block b (k in [128 b, 128 b + 128)), plane p (0 = hi, 1 = lo), step s,
-// tile t, lane l = 16 g + r holds, as 8 fp16, row 16 t + r at
-// k = 128 b + 32 s + {4g .. 4g+3, 16+4g .. 16+4g+3}.  Rows >= M and k >= K
-// are zero.  kshift (nullable): element (m, k) is first multiplied by
-// 2^-kshift[k] (exact).  One thread per (b, s, t, l).
+// ---- the first kernel: row exponents and (MT > 1) operand-ordered planes ----
+// Workgroup m (one per row of the MT 16-row tiles) takes row m of A: its
+// largest magnitude (after the optional 2^-kshift[k]) gives the row exponent
+// e_m (aexp[m]; rows >= M get 0).  With MT > 1 it then writes the row's
+// split, x 2^(e_m - kshift[k]) as hi = fp16, lo = fp16((x - hi) 2^10), in
+// operand order: block b (k in [128 b, 128 b + 128)), plane p (0 = hi,
+// 1 = lo), step s, tile t, lane l = 16 g + r holds, as 8 fp16, row 16 t + r
+// at k = 128 b + 32 s + {4g .. 4g+3, 16+4g .. 16+4g+3}.  Rows >= M and
+// k >= K are zero.
 template <int MT>
-__global__ __launch_bounds__(256) void asplit_kernel(const float* __restrict__ A, int64_t lda, int M,
-                                                     int K, int nblk, const int8_t* __restrict__ kshift,
-                                                     unsigned char* __restrict__ out,
-                                                     uint32_t* __restrict__ status) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t total = (int64_t)nblk * STEPS * MT * 64;
-    bool bad = false;
-    if (idx < total) {
-        const int l = (int)(idx & 63);
-        const int t = (int)((idx >> 6) % MT);
-        const int s = (int)((idx / (64 * MT)) % STEPS);
-        const int64_t b = idx / (64 * MT * STEPS);
-        const int m = 16 * t + (l & 15), g = l >> 4;
-        const int64_t k0 = b * KA + 32 * s;
-        float x[8];
+__global__ __launch_bounds__(256) void decode_prep_kernel(const float* __restrict__ A, int64_t lda, int M, int K,
+                                                          int nblk, const int8_t* __restrict__ kshift,
+                                                          int* __restrict__ aexp, unsigned char* __restrict__ out) {
+    __shared__ float red[4];
+    const int m = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float* a = A + (int64_t)m * lda;
+    auto shift = [&](int k) { return kshift ? -(int)kshift[k] : 0; };
+    float mx = 0.0f;
+    for (int k = tid; k < K && m < M; k += 256) mx = fmaxf(mx, __builtin_fabsf(__builtin_ldexpf(a[k], shift(k))));
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t k = k0 + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
-            x[j] = (m < M && k < K) ? A[(int64_t)m * lda + k] : 0.0f;
-            if (kshift && k < K) x[j] = __builtin_ldexpf(x[j], -(int)kshift[k]);
-        }
-        half8 h, lo;
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const int e = row_norm_exp(mx);
+    if (tid == 0) aexp[m] = e;
+    if constexpr (MT > 1) {
+        const int t = m >> 4, r = m & 15;
+        for (int item = tid; item < nblk * STEPS * 4; item += 256) {   // (b, s, g)
+            const int g = item & 3, st = (item >> 2) % STEPS, b = item / (4 * STEPS);
+            const int k0 = b * KA + 32 * st;
+            half8 h, lo;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            _Float16 hh, ll;
-            split_one(x[j], hh, ll);
-            bad |= f16_out_of_range(x[j]);
-            h[j] = hh;
-            lo[j] = ll;
+            for (int j = 0; j < 8; ++j) {
+                const int k = k0 + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
+                _Float16 hh, ll;
+                // one scaling by 2^(e - kshift[k]), as the in-kernel split does
+                split_one((m < M && k < K) ? __builtin_ldexpf(a[k], e + shift(k)) : 0.0f, hh, ll);
+                h[j] = hh;
+                lo[j] = ll;
+            }
+            unsigned char* blk = out + (int64_t)b * block_bytes<MT>();
+            const int off = ((st * MT + t) * 64 + 16 * g + r) * 16;
+            *reinterpret_cast<half8*>(blk + off) = h;
+            *reinterpret_cast<half8*>(blk + block_bytes<MT>() / 2 + off) = lo;
         }
-        unsigned char* blk = out + b * block_bytes<MT>();
-        const int64_t off = ((int64_t)(s * MT + t) * 64 + l) * 16;
-        *reinterpret_cast<half8*>(blk + off) = h;
-        *reinterpret_cast<half8*>(blk + block_bytes<MT>() / 2 + off) = lo;
     }
-    if (status && __builtin_amdgcn_ballot_w64(bad) && (threadIdx.x & 63) == 0)
-        atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
 }
 
 __device__ __forceinline__ void split8(const float4& a, const float4& b, half8& h, half8& l) {
@@ -146,13 +155,14 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // its split.  ONE: plain FP16, the A_hi.W_hi product alone.
 template <int MT, bool VEC, bool WF16, bool AVEC, bool SHIFT, bool ONE, int NWK>
 __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __restrict__ A, int64_t lda,
+                                                          const int* __restrict__ aexp,
                                                           const unsigned char* __restrict__ Ablk,
                                                           int a_total_bytes, const void* __restrict__ W,
                                                           int64_t ldw, float* __restrict__ out, int64_t ldo,
                                                           int64_t split_stride, int M, int N, int K,
                                                           int kchunk, const int8_t* __restrict__ kshift,
                                                           uint32_t* __restrict__ status) {
-    static_assert(!SHIFT || MT == 1, "with MT > 1 the shift is applied by asplit_kernel");
+    static_assert(!SHIFT || MT == 1, "with MT > 1 the shift is applied by decode_prep_kernel");
     constexpr int BB = block_bytes<MT>();
     constexpr bool INK = MT == 1;                   // split the activation in the kernel
     constexpr int AU = 2 * MT;                      // 4-wide activation units per thread per block
@@ -209,7 +219,8 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
             }
         }
     };
-    float amax = 0.0f;
+    // MT == 1: the thread's units all lie in row tid % 16; its exponent
+    const int erow = INK ? aexp[tid & 15] : 0;
     auto store_a = [&](int b) {
         unsigned char* base = sa + (b & 1) * BB;
 #pragma unroll
@@ -219,10 +230,8 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
             const int k = unit_k(b, x);
             float v[4] = {k < k_end ? areg[i].x : 0.0f, k + 1 < k_end ? areg[i].y : 0.0f,
                           k + 2 < k_end ? areg[i].z : 0.0f, k + 3 < k_end ? areg[i].w : 0.0f};
-            if constexpr (SHIFT) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = __builtin_ldexpf(v[j], -sreg[i][j]);
-            }
+            for (int j = 0; j < 4; ++j) v[j] = __builtin_ldexpf(v[j], SHIFT ? erow - sreg[i][j] : erow);
             half4 h, l;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -230,7 +239,6 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
                 split_one(v[j], hh, ll);
                 h[j] = hh;
                 l[j] = ll;
-                amax = fmaxf(amax, __builtin_fabsf(v[j]));
             }
             const int off = ((st * MT + t) * 64 + 16 * gg + r) * 16 + 8 * half;
             *reinterpret_cast<half4*>(base + off) = h;
@@ -395,19 +403,24 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
         b += PFW / STEPS;
     } while (b < nblocks);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // drain the clamped tail loads
-    if (status && __builtin_amdgcn_ballot_w64(fmaxf(wmax, amax) >= 65520.0f) && lane == 0)
+    // the normalized activation cannot overflow fp16; W is split as it is
+    if (status && __builtin_amdgcn_ballot_w64(wmax >= 65520.0f) && lane == 0)
         atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
 
-    // ---- epilogue: lane holds column n, rows t*16 + 4g + e ------------------
+    // ---- epilogue: lane holds column n, rows t*16 + 4g + e; each output is
+    //      (acc_hh + 2^-10 acc_c) 2^-e_m --------------------------------------
     if (!row_ok) return;
     float* o = out + split * split_stride;
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+    for (int t = 0; t < MT; ++t) {
+        const int4 er = *reinterpret_cast<const int4*>(aexp + t * 16 + 4 * g);
+        const int ev[4] = {er.x, er.y, er.z, er.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int m = t * 16 + 4 * g + e;
-            if (m < M) o[(int64_t)m * ldo + n] = acc_hh[t][e] + acc_c[t][e] * 0.0009765625f;
+            if (m < M) o[(int64_t)m * ldo + n] = __builtin_ldexpf(acc_hh[t][e] + acc_c[t][e] * 0.0009765625f, -ev[e]);
         }
+    }
 }
 
 // C[m, n] = sum over chunks s (in order) of P[s, m, n].  The partials of a
@@ -439,6 +452,10 @@ int mtiles(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
 }  // namespace
 
+// workspace: row exponents (256 bytes), activation planes, split-K partials
+constexpr int64_t kExpBytes = 256;
+int64_t DecodePlan::bytes() const { return kExpBytes + (a_bytes + 255) / 256 * 256 + (p_bytes + 255) / 256 * 256; }
+
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
     DecodePlan p{};
     const int64_t nblk = (N + DEC_ROWS - 1) / DEC_ROWS;
@@ -462,8 +479,9 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
     if (M == 0 || N == 0) return hipSuccess;
     if (M > 64 || K == 0) return hipErrorInvalidValue;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    unsigned char* ablk = ws;
-    float* part = reinterpret_cast<float*>(ws + (plan.a_bytes + 255) / 256 * 256);
+    int* aexp = reinterpret_cast<int*>(ws);
+    unsigned char* ablk = ws + kExpBytes;
+    float* part = reinterpret_cast<float*>(ablk + (plan.a_bytes + 255) / 256 * 256);
     const int nablk = (int)((K + KA - 1) / KA);
     const int mt = mtiles(M);
     const int64_t nblk2 = (N + 2 * DEC_ROWS - 1) / (2 * DEC_ROWS);
@@ -481,7 +499,7 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
     const bool avec = (reinterpret_cast<uintptr_t>(A) & 15) == 0 && (lda & 3) == 0;
 #define HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW_)                                      \
     hipLaunchKernelGGL((gemm_decode_kernel<MT_, VEC_, F16_, AV_, SH_, ONE_, NW_>), grid, dim3(64 * NW_), \
-                       2 * block_bytes<MT_>(), s, A, lda, ablk, (int)plan.a_bytes, W, ldw, out, ldo, stride, \
+                       2 * block_bytes<MT_>(), s, A, lda, aexp, ablk, (int)plan.a_bytes, W, ldw, out, ldo, stride, \
                        (int)M, (int)N, (int)K, (int)plan.kchunk, kshift, status)
 #define HEAL_DEC_LAUNCH(MT_, VEC_, F16_, AV_, SH_, ONE_)                                                \
     do {                                                                                                \
@@ -504,11 +522,8 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
     } while (0)
 #define HEAL_DEC(MT_, SH_)                                                                              \
     do {                                                                                                \
-        if ((MT_) > 1) {                                                                                \
-            const int64_t tot = (int64_t)nablk * STEPS * (MT_) * 64;                                    \
-            hipLaunchKernelGGL((asplit_kernel<MT_>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, \
-                               A, lda, (int)M, (int)K, nablk, kshift, ablk, status);                    \
-        }                                                                                               \
+        hipLaunchKernelGGL((decode_prep_kernel<MT_>), dim3(16 * (MT_)), dim3(256), 0, s, A, lda, (int)M,   \
+                           (int)K, nablk, kshift, aexp, ablk);                                          \
         if (wf16) {                                                                                     \
             if (vec) HEAL_DEC_AV(MT_, true, true, SH_);                                                 \
             else HEAL_DEC_AV(MT_, false, true, SH_);                                                    \

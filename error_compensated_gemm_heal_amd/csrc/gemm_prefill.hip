@@ -10,12 +10,17 @@
 //
 // Kernel structure (MFMA-bound; 3 x 2MNK flops on the 16-bit pipe):
 //  * operands arrive packed by the split kernels: per row, each 32-wide k
-//    block is one 128-byte line [32 hi | 32 lo] fp16, zero-padded to whole
+//    block is one 128-byte line [32 hi | 32 res] fp16, zero-padded to whole
 //    tiles, so the main loop has no bounds checks;
-//  * the 2^-10 of the correction terms is folded into the activation
-//    fragments in registers (A_hi 2^-10 and A_lo 2^-10, exact power-of-two
-//    fp16 scaling), so all three products accumulate into one fp32
-//    accumulator per output and the epilogue is a plain store;
+//  * FP16's narrow range (the same paragraph: handled by targeted
+//    rescaling) is met by normalizing every operand row by a power of two:
+//    its largest magnitude lies in [2^14, 2^15), and its residual is stored
+//    at its own scale, res = fp16(x' - hi), which equals the paper's
+//    lo 2^-10 for every element above 2^-17 of its row's largest.  So all
+//    three products accumulate into one fp32 accumulator per output with no
+//    scaling in the main loop, and the epilogue multiplies each output by
+//    2^-(e_a[m] + e_b[n]) (exact, barring fp32 underflow): the result does
+//    not depend on the operands' absolute scale;
 //  * block tile 256 x 256 x 32, 4 waves in a 2 x 2 grid of 128 x 128 wave
 //    tiles, each 4 x 4 tiles of v_mfma_f32_32x32x16_f16 (256 accumulator
 //    registers per wave); a wave issues 96 MFMAs per k tile for 32 16-byte
@@ -113,13 +118,8 @@ __device__ __forceinline__ void mfma32(const half8& a, const half8& b, floatx16&
         c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// x * 2^-10 on 8 fp16 values (exact for normal results)
-__device__ __forceinline__ half8 scale_m10(const half8& x) {
-    return x * (_Float16)0.0009765625f;
-}
-
-// NP: products per k step.  3: A_hi.B_hi + 2^-10 (A_hi.B_lo + A_lo.B_hi);
-// 2: B is a 16-bit weight (zero lo planes), A_hi.B + 2^-10 A_lo.B;
+// NP: products per k step.  3: A_hi.B_hi + A_hi.B_res + A_res.B_hi;
+// 2: B is a 16-bit weight (no residual), A_hi.B + A_res.B;
 // 1: plain FP16, A_hi.B_hi.  BHI: B is in the hi-only packed form.  X3: the
 // BF16 three-way mode (NP = 1 over the virtual reduction, single planes).
 // QKV: the INT16 epilogue for heads of 128 outputs (not with SPLIT).  AH: A
@@ -127,6 +127,7 @@ __device__ __forceinline__ half8 scale_m10(const half8& x) {
 template <bool SPLIT, int NP, bool BHI, bool X3, bool QKV, bool AH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned char* __restrict__ Bpk,
+                         const int* __restrict__ ea, const int* __restrict__ eb,
                          float* __restrict__ C, int64_t ldc, int M, int N, int Kp,
                          int tiles_m, int tiles_n, QkvDst qkv) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -241,22 +242,20 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
                 bl_[j] = *reinterpret_cast<const half8*>(base + b_row + j * 32 * ROWB + slot_off[ks_][1]); \
         }                                                                                                \
     } while (0)
-    // the three products of one k16 step; each product sweeps all 16 output
-    // tiles before the next, so an accumulator is re-read 16 MFMAs later
+    // the products of one k16 step (residuals at their own scale: no
+    // scaling); each product sweeps all 16 output tiles before the next, so
+    // an accumulator is re-read 16 MFMAs later
 #define HEAL_MFMAS(ah_, al_, bh_, bl_)                                                                   \
     do {                                                                                                 \
         _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                   \
             _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32<X3>(ah_[i], bh_[j], acc[i][j]);        \
-        half8 as_[TM];                                                                                   \
         if constexpr (NP == 3) {                                                                         \
-            _Pragma("unroll") for (int i = 0; i < TM; ++i) as_[i] = scale_m10(ah_[i]);                   \
             _Pragma("unroll") for (int i = 0; i < TM; ++i)                                               \
-                _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32<false>(as_[i], bl_[j], acc[i][j]);        \
+                _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32<false>(ah_[i], bl_[j], acc[i][j]); \
         }                                                                                                \
         if constexpr (NP >= 2) {                                                                         \
-            _Pragma("unroll") for (int i = 0; i < TM; ++i) as_[i] = scale_m10(al_[i]);                   \
             _Pragma("unroll") for (int i = 0; i < TM; ++i)                                               \
-                _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32<false>(as_[i], bh_[j], acc[i][j]);        \
+                _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32<false>(al_[i], bh_[j], acc[i][j]); \
         }                                                                                                \
     } while (0)
 
@@ -323,6 +322,28 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     // ---- epilogue: bounds-checked store (or atomic add of one k half) -------
     const int row0 = tm * BM + wm * WM + (lane >> 5) * 4;
     const int col0 = tn * BN + wn * WN + (lane & 31);
+    // undo the row normalization: output (row, col) times 2^-(ea[row] + eb[col]),
+    // exact barring fp32 underflow.  The exponent arrays cover the padded rows.
+    if constexpr (!X3) {
+        int ebc[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) ebc[j] = eb[col0 + j * 32];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            int4 er[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) er[q] = *reinterpret_cast<const int4*>(ea + row0 + i * 32 + q * 8);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[i][j][4 * q + 0] = __builtin_ldexpf(acc[i][j][4 * q + 0], -(er[q].x + ebc[j]));
+                    acc[i][j][4 * q + 1] = __builtin_ldexpf(acc[i][j][4 * q + 1], -(er[q].y + ebc[j]));
+                    acc[i][j][4 * q + 2] = __builtin_ldexpf(acc[i][j][4 * q + 2], -(er[q].z + ebc[j]));
+                    acc[i][j][4 * q + 3] = __builtin_ldexpf(acc[i][j][4 * q + 3], -(er[q].w + ebc[j]));
+                }
+        }
+    }
     if constexpr (QKV) {
         // The output goes through LDS (the operand stages are free now): in
         // pass p the two waves of wave column p write their 128 x 128 fp32
@@ -483,6 +504,11 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
     }
     const unsigned char* a = static_cast<const unsigned char*>(Apk);
     const unsigned char* b = static_cast<const unsigned char*>(Bpk);
+    // the row exponents follow each packed operand's rows (none in the BF16 mode)
+    const int* ea = x3 ? nullptr
+                       : reinterpret_cast<const int*>(a + (a_hi ? pack_data_bytes_hi(M, K) : pack_data_bytes(M, K)));
+    const int* eb = x3 ? nullptr
+                       : reinterpret_cast<const int*>(b + (b_hi ? pack_data_bytes_hi(N, K) : pack_data_bytes(N, K)));
     if (split) {
         const unsigned zb = (unsigned)std::min<int64_t>((M * N + 255) / 256, 4096);
         hipLaunchKernelGGL(zero_c_kernel, dim3(zb), dim3(256), 0, s, C, ldc, M, N);
@@ -491,20 +517,20 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
     const QkvDst none{};
 #define HEAL_PREFILL(SPLIT_, NP_, BHI_, X3_)                                                          \
     hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, NP_, BHI_, X3_, false, false>), grid, dim3(256),  \
-                       NSTAGE * stage_bytes(X3_, BHI_), s, a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n, \
+                       NSTAGE * stage_bytes(X3_, BHI_), s, a, b, ea, eb, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n, \
                        none)
 #define HEAL_PREFILL_AH(SPLIT_, BHI_)                                                                 \
     hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, 1, BHI_, false, false, true>), grid, dim3(256),   \
-                       NSTAGE * stage_bytes(true, BHI_), s, a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n, \
+                       NSTAGE * stage_bytes(true, BHI_), s, a, b, ea, eb, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n, \
                        none)
     if (qkv) {
         if (nprod == 3)
             hipLaunchKernelGGL((gemm_prefill_kernel<false, 3, false, false, true, false>), grid, dim3(256),
-                               dyn_lds(false, false, true), s, a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m,
+                               dyn_lds(false, false, true), s, a, b, ea, eb, C, ldc, (int)M, (int)N, (int)Kp, tiles_m,
                                tiles_n, *qkv);
         else
             hipLaunchKernelGGL((gemm_prefill_kernel<false, 2, true, false, true, false>), grid, dim3(256),
-                               dyn_lds(false, true, true), s, a, b, C, ldc, (int)M, (int)N, (int)Kp, tiles_m,
+                               dyn_lds(false, true, true), s, a, b, ea, eb, C, ldc, (int)M, (int)N, (int)Kp, tiles_m,
                                tiles_n, *qkv);
         return hipGetLastError();
     }

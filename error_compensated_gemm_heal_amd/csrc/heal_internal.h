@@ -47,6 +47,23 @@ __device__ __forceinline__ void split_one(float x, _Float16& hi, _Float16& lo) {
 
 __device__ __forceinline__ uint16_t f16_bits(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
 
+// Row normalization (the packed GEMM operands and the decode activation):
+// each row is multiplied by 2^e with e = 14 - floor(log2(max |x|)), so its
+// largest magnitude lies in [2^14, 2^15), the top binade that cannot round
+// past 65504; e = 0 for a zero row.  The product is multiplied back by
+// 2^-(e_a + e_b) in fp32.  frexp's exponent p gives max = f 2^p, f in [0.5, 1).
+__device__ __forceinline__ int row_norm_exp(float amax) {
+    return amax > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(amax) : 0;
+}
+// Split of a normalized element with its residual at its own scale:
+// hi = fp16(x), res = fp16(x - hi) (x - hi exact in fp32).  On a normalized
+// row res equals the paper's lo / 2^10 for every element above 2^-17 of the
+// row's largest, so the three products accumulate with no scaling.
+__device__ __forceinline__ void split_res(float x, _Float16& hi, _Float16& res) {
+    hi = (_Float16)x;
+    res = (_Float16)(x - (float)hi);
+}
+
 // An operand magnitude at or above 65520 rounds to an infinite fp16 high part.
 __device__ __forceinline__ bool f16_out_of_range(float x) { return __builtin_fabsf(x) >= 65520.0f; }
 __device__ __forceinline__ bool f16_out_of_range4(const float4& v) {
@@ -55,24 +72,32 @@ __device__ __forceinline__ bool f16_out_of_range4(const float4& v) {
 }
 
 // ---- packed dual-FP16 operand layout used by the prefill GEMM --------------
-// Row r of a packed operand holds, for each 32-wide block kb of the reduction
-// dimension, 32 fp16 hi parts followed by 32 fp16 lo parts (128 bytes).  Rows
-// are padded to a multiple of kPackRows and k to a multiple of kPackK, with
-// zeros, so the GEMM main loop needs no bounds checks.  A 16-bit weight (its
-// lo parts are zero) packs as the hi parts alone: row r holds its Kp fp16
-// values (64 bytes per 32-wide block), same padding.
+// Row r of a packed operand is normalized (row_norm_exp) and holds, for each
+// 32-wide block kb of the reduction dimension, 32 fp16 hi parts followed by
+// 32 fp16 residuals (split_res; 128 bytes).  Rows are padded to a multiple of
+// kPackRows and k to a multiple of kPackK, with zeros, so the GEMM main loop
+// needs no bounds checks.  After the rows come the row exponents, int32
+// [pack_rows(R)] (0 for padding rows).  A 16-bit weight (its residuals are
+// zero) packs as the hi parts alone, not normalized: row r holds its Kp fp16
+// values (64 bytes per 32-wide block), same padding, exponents 0.  An fp32
+// activation packed for the one-product mode keeps its normalized hi parts
+// alone in the same form.
 constexpr int kPackK = 32;
 constexpr int kPackRows = 256;
 
 __host__ __device__ inline int64_t pack_kp(int64_t K) { return (K + kPackK - 1) / kPackK * kPackK; }
 __host__ __device__ inline int64_t pack_rows(int64_t R) { return (R + kPackRows - 1) / kPackRows * kPackRows; }
-// bytes of one packed operand of R rows and reduction length K
-__host__ __device__ inline int64_t pack_bytes(int64_t R, int64_t K) { return pack_rows(R) * pack_kp(K) * 4; }
-// bytes of the hi-only packed form of a 16-bit operand
-__host__ __device__ inline int64_t pack_bytes_hi(int64_t R, int64_t K) { return pack_rows(R) * pack_kp(K) * 2; }
+// bytes of the rows of a packed operand (hi/res form), where its exponents start
+__host__ __device__ inline int64_t pack_data_bytes(int64_t R, int64_t K) { return pack_rows(R) * pack_kp(K) * 4; }
+__host__ __device__ inline int64_t pack_data_bytes_hi(int64_t R, int64_t K) { return pack_rows(R) * pack_kp(K) * 2; }
+// bytes of one packed operand of R rows and reduction length K: rows, then exponents
+__host__ __device__ inline int64_t pack_bytes(int64_t R, int64_t K) { return pack_data_bytes(R, K) + pack_rows(R) * 4; }
+// bytes of the hi-only packed form
+__host__ __device__ inline int64_t pack_bytes_hi(int64_t R, int64_t K) { return pack_data_bytes_hi(R, K) + pack_rows(R) * 4; }
 
 // bytes of the BF16 three-way packed form: per row and 32-wide k block, the
-// 32 bf16 b0, then the 32 b1, then the 32 b2 (192 bytes), same padding
+// 32 bf16 b0, then the 32 b1, then the 32 b2 (192 bytes), same padding; not
+// normalized (bf16 has fp32's exponent range) and no exponents
 __host__ __device__ inline int64_t pack_bytes_x3(int64_t R, int64_t K) { return pack_rows(R) * pack_kp(K) * 6; }
 
 // Rows of a fused Q/K/V projection output [M, (Hq + 2 Hkv) D]: row r is
@@ -117,14 +142,15 @@ struct QkvDst {
 // ---- launchers (return the launch status; never synchronize) -------------
 hipError_t launch_split(const float* X, int64_t n, uint16_t* hi, uint16_t* lo, uint32_t* status,
                         hipStream_t s);
-// Pack rows into the layout above.  src holds fp32 values (hi/lo form), or
-// binary16 values when f16 (hi-only form).  kn == 0: src is [rows, K] with
-// ld; kn == 1: src is [K, rows] with ld (the packed operand is its transpose).
-// kshift (nullable): element (r, k) is multiplied by 2^-kshift[k] first.
+// Pack rows into the layout above.  src holds fp32 values (normalized rows,
+// hi/res form), or binary16 values when f16 (hi-only form, exponents 0).
+// kn == 0: src is [rows, K] with ld; kn == 1: src is [K, rows] with ld (the
+// packed operand is its transpose).  kshift (nullable): element (r, k) is
+// multiplied by 2^-kshift[k] first (before the row's maximum is taken).
 hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int64_t K, int kn,
                        const int8_t* kshift, void* packed, uint32_t* status, hipStream_t s);
-// The hi parts alone of fp32 rows [rows, K] (16-byte aligned rows, ld % 4 == 0),
-// in the hi-only packed layout, for the one-product mode.
+// The normalized hi parts alone of fp32 rows [rows, K], in the hi-only packed
+// layout with their exponents, for the one-product mode.
 hipError_t launch_pack_hi_f32(const float* src, int64_t ld, int64_t rows, int64_t K, void* packed, uint32_t* status,
                               hipStream_t s);
 // BF16 three-way packing of fp32 rows (kn as for launch_pack); status gets
@@ -156,20 +182,25 @@ hipError_t launch_dequant(const int16_t* codes, int64_t rows, int64_t D, int64_t
 // qkv (nullable): instead of storing C, quantize each (token, head) row of
 // D = 128 outputs to INT16 in the epilogue and write it as dst.at() directs
 // (3- and 2-product forms, shapes without the k split: see prefill_ksplit).
+// The packed operands carry their row exponents (except in the BF16 mode):
+// C = acc 2^-(e_a[m] + e_b[n]).
 hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool b_hi, float* C, int64_t ldc,
                                int64_t M, int64_t N, int64_t K, hipStream_t s, const QkvDst* qkv = nullptr,
                                bool a_hi = false);
 // Whether the prefill kernel splits the k range of this shape in two.
 bool prefill_ksplit(int64_t M, int64_t N, int64_t K);
 
-// Decode path (M <= 64): fp32 W [N,K] streamed and split in registers.
-// Workspace: the split activation planes (a_bytes), then, 256-byte aligned,
-// the split-K partials (p_bytes).
+// Decode path (M <= 64): fp32 W [N,K] streamed and split in registers, the
+// activation rows normalized by a first small kernel (their exponents, and for
+// M > 16 their split planes).  Workspace, each part 256-byte aligned: the row
+// exponents (256 bytes), the split activation planes (a_bytes), the split-K
+// partials (p_bytes).
 struct DecodePlan {
     int splits;        // number of K chunks (fixed by N and K only)
     int64_t kchunk;    // reduction length of one chunk (multiple of 256)
     int64_t a_bytes;   // workspace bytes of the split activation planes
     int64_t p_bytes;   // workspace bytes of the split-K partials
+    int64_t bytes() const;
 };
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K);
 // W is fp32, or binary16 values when wf16 (the two-product form); one: plain

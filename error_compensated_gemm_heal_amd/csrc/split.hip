@@ -3,13 +3,17 @@
 // HEAL paper, section 3, "Mitigating GEMM Truncation via FP16 Promotion and
 // Algebraic Compensation": the FP32 input is decomposed into an FP16 value
 // plus an FP16 residual shifted by 2^10, so that 16-bit matrix units can
-// evaluate the product.  Kernels:
+// evaluate the product; FP16's narrow dynamic range is handled by targeted
+// power-of-two rescaling.  Kernels:
 //  * split_kernel: plain elementwise planes (hi[], lo[]), bit-exact.
-//  * pack kernels: the same split written straight into the padded,
-//    hi/lo-interleaved layout the prefill GEMM streams (one 128-byte line per
-//    row and 32-wide k block), so the GEMM needs no bounds checks; a binary16
-//    source packs its hi parts alone, and an optional per-channel power of two
-//    scales the source first.
+//  * pack kernels: the operand rows of the prefill GEMM, each normalized by
+//    the power of two that puts its largest magnitude in [2^14, 2^15), split
+//    as hi = fp16(x'), res = fp16(x' - hi) and written straight into the
+//    padded, hi/res-interleaved layout the GEMM streams (one 128-byte line per
+//    row and 32-wide k block), with the row exponents after the rows, so the
+//    GEMM needs no bounds checks and no scaling in its main loop; a binary16
+//    source packs its hi parts alone (not normalized), and an optional
+//    per-channel power of two scales the source first.
 //  * pack_bf16x3_kernel: the BF16 three-way split of the precision mode, in
 //    the same padded layout with three 64-byte planes per k block.
 //  * scale_k_kernel: the per-channel power-of-two rescaling of an operand.
@@ -85,7 +89,7 @@ template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void pack_rowmajor_kernel(const T* __restrict__ src, int64_t ld,
                                                             int64_t rows, int64_t K, int64_t Kp,
                                                             int64_t rows_p, const int8_t* __restrict__ kshift,
-                                                            uint16_t* __restrict__ out,
+                                                            uint16_t* __restrict__ out, int* __restrict__ exps,
                                                             uint32_t* __restrict__ status) {
     const int64_t kq = Kp >> 2;  // 4-wide groups per padded row
     const int64_t total = rows_p * kq;
@@ -115,9 +119,15 @@ __global__ __launch_bounds__(256) void pack_rowmajor_kernel(const T* __restrict_
                     if (k + j < K) x[j] = kscaled(x[j], kshift, k + j);
         }
         uint16_t h[4], l[4];
+        if constexpr (sizeof(T) == 4) {   // the row's normalization (exponents from rowexp_*_kernel)
+            const int e = exps[r];
+            for (int j = 0; j < 4; ++j) x[j] = __builtin_ldexpf(x[j], e);
+        } else if (k == 0) {
+            exps[r] = 0;                  // a 16-bit source is not normalized
+        }
         for (int j = 0; j < 4; ++j) {
             _Float16 hh, ll;
-            split_one(x[j], hh, ll);
+            split_res(x[j], hh, ll);
             bad |= f16_out_of_range(x[j]);
             h[j] = f16_bits(hh);
             l[j] = f16_bits(ll);
@@ -142,7 +152,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void pack_colmajor_kernel(const T* __restrict__ src, int64_t ld,
                                                             int64_t rows, int64_t K, int64_t Kp,
                                                             int64_t rows_p, const int8_t* __restrict__ kshift,
-                                                            uint16_t* __restrict__ out,
+                                                            uint16_t* __restrict__ out, int* __restrict__ exps,
                                                             uint32_t* __restrict__ status) {
     const int64_t kq = Kp >> 2;
     const int64_t total = rows_p * kq;
@@ -152,11 +162,15 @@ __global__ __launch_bounds__(256) void pack_colmajor_kernel(const T* __restrict_
         const int64_t kg = i / rows_p;
         const int64_t r = i - kg * rows_p;
         const int64_t k = kg << 2;
+        int e = 0;
+        if constexpr (sizeof(T) == 4) e = exps[r];   // the row's normalization
+        else if (k == 0) exps[r] = 0;                 // a 16-bit source is not normalized
         uint16_t h[4], l[4];
         for (int j = 0; j < 4; ++j) {
             float x = (r < rows && k + j < K) ? kscaled(src_value(src[(k + j) * ld + r]), kshift, k + j) : 0.f;
+            if constexpr (sizeof(T) == 4) x = __builtin_ldexpf(x, e);
             _Float16 hh, ll;
-            split_one(x, hh, ll);
+            split_res(x, hh, ll);
             bad |= f16_out_of_range(x);
             h[j] = f16_bits(hh);
             l[j] = f16_bits(ll);
@@ -174,43 +188,88 @@ __global__ __launch_bounds__(256) void pack_colmajor_kernel(const T* __restrict_
     if (bad && status) atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
 }
 
-// The fp32 row-major pack without shifts, 8 elements per item: two 16-byte
-// loads, one 16-byte store into each of the hi and lo halves of the row's
-// 128-byte line for that k block.  Rows go to blockIdx.y (grid-stride), the
-// k groups of a row to x, so no item index is divided.
-template <bool HI_ONLY>
-__global__ __launch_bounds__(256) void pack_rowmajor8_kernel(const float* __restrict__ src, int64_t ld,
+__device__ __forceinline__ float wave_max(float m) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    return m;
+}
+
+// Largest magnitude of the workgroup's values (256 threads); red holds 4
+// floats of LDS and is free again when this returns.
+__device__ __forceinline__ float block_max(float m, float* red) {
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    return m;
+}
+
+// The fp32 row-major pack: one workgroup per packed row (grid-stride over the
+// padded rows).  The row is loaded once into registers, MAXI items of 8
+// consecutive k per thread (Kp <= 2048 MAXI), its largest magnitude reduced
+// across the workgroup, and the normalized values split and stored: 16 bytes
+// into each of the hi and res halves of the row's 128-byte line for that k
+// block (or one 16-byte store of hi parts in the hi-only form).  VEC: rows
+// 16-byte aligned.  SHIFT: element (r, k) is multiplied by 2^-kshift[k]
+// first.  Padding rows and k write zeros and exponent 0.
+template <bool HI_ONLY, bool VEC, bool SHIFT, int MAXI>
+__global__ __launch_bounds__(256) void pack_rows_norm_kernel(const float* __restrict__ src, int64_t ld,
                                                              int64_t rows, int64_t K, int64_t Kp, int64_t rows_p,
-                                                             uint16_t* __restrict__ out,
+                                                             const int8_t* __restrict__ kshift,
+                                                             uint16_t* __restrict__ out, int* __restrict__ exps,
                                                              uint32_t* __restrict__ status) {
+    __shared__ float red[4];
     const int c8n = (int)(Kp >> 3);
+    const int tid = threadIdx.x;
     bool bad = false;
-    for (int64_t r = blockIdx.y; r < rows_p; r += gridDim.y) {
-        for (int c8 = blockIdx.x * 256 + threadIdx.x; c8 < c8n; c8 += gridDim.x * 256) {
+    for (int64_t r = blockIdx.x; r < rows_p; r += gridDim.x) {
+        float x[MAXI][8];
+        float m = 0.0f;
+#pragma unroll
+        for (int j = 0; j < MAXI; ++j) {
+            const int c8 = tid + 256 * j;
             const int64_t k = (int64_t)c8 << 3;
-            float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            if (r < rows) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[j][i] = 0.0f;
+            if (r < rows && c8 < c8n) {
                 const float* p = src + r * ld + k;
-                if (k + 8 <= K) {
+                if (VEC && k + 8 <= K) {
                     const float4 a = *reinterpret_cast<const float4*>(p);
                     const float4 b = *reinterpret_cast<const float4*>(p + 4);
-                    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-                    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+                    x[j][0] = a.x; x[j][1] = a.y; x[j][2] = a.z; x[j][3] = a.w;
+                    x[j][4] = b.x; x[j][5] = b.y; x[j][6] = b.z; x[j][7] = b.w;
                 } else {
-                    for (int j = 0; j < 8; ++j)
-                        if (k + j < K) x[j] = p[j];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (k + i < K) x[j][i] = p[i];
+                }
+                if constexpr (SHIFT) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (k + i < K) x[j][i] = __builtin_ldexpf(x[j][i], -(int)kshift[k + i]);
                 }
             }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(x[j][i]));
+        }
+        m = block_max(m, red);
+        bad |= !(m <= 3.40282347e38f);   // an infinite (or NaN) element
+        const int e = row_norm_exp(m);
+        if (tid == 0) exps[r] = e;
+#pragma unroll
+        for (int j = 0; j < MAXI; ++j) {
+            const int c8 = tid + 256 * j;
+            if (c8 >= c8n) break;
+            const int64_t k = (int64_t)c8 << 3;
             uint32_t h[4], l[4];
 #pragma unroll
-            for (int j = 0; j < 8; j += 2) {
+            for (int i = 0; i < 8; i += 2) {
                 _Float16 h0, l0, h1, l1;
-                split_one(x[j], h0, l0);
-                split_one(x[j + 1], h1, l1);
-                bad |= f16_out_of_range(x[j]);
-                bad |= f16_out_of_range(x[j + 1]);
-                h[j >> 1] = f16_bits(h0) | ((uint32_t)f16_bits(h1) << 16);
-                l[j >> 1] = f16_bits(l0) | ((uint32_t)f16_bits(l1) << 16);
+                split_res(__builtin_ldexpf(x[j][i], e), h0, l0);
+                split_res(__builtin_ldexpf(x[j][i + 1], e), h1, l1);
+                h[i >> 1] = f16_bits(h0) | ((uint32_t)f16_bits(h1) << 16);
+                l[i >> 1] = f16_bits(l0) | ((uint32_t)f16_bits(l1) << 16);
             }
             if constexpr (HI_ONLY) {   // the hi-only layout: Kp fp16 per row
                 *reinterpret_cast<uint4*>(out + r * Kp + k) = make_uint4(h[0], h[1], h[2], h[3]);
@@ -221,8 +280,52 @@ __global__ __launch_bounds__(256) void pack_rowmajor8_kernel(const float* __rest
             }
         }
     }
-    if (bad && status) atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
+    if (bad && status && tid == 0) atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
 }
+
+// Row exponents for the general pack path.  [rows, K] source (kn == 0): one
+// workgroup per row, threads along k.  [K, rows] source (kn == 1): one thread
+// per packed row, walking k down its column (neighbouring threads read
+// neighbouring addresses).  Padding rows get 0.
+__global__ __launch_bounds__(256) void rowexp_nk_kernel(const float* __restrict__ src, int64_t ld, int64_t rows,
+                                                        int64_t K, int64_t rows_p, const int8_t* __restrict__ kshift,
+                                                        int* __restrict__ exps) {
+    __shared__ float red[4];
+    for (int64_t r = blockIdx.x; r < rows_p; r += gridDim.x) {
+        float m = 0.0f;
+        if (r < rows)
+            for (int64_t k = threadIdx.x; k < K; k += 256) m = fmaxf(m, __builtin_fabsf(kscaled(src[r * ld + k], kshift, k)));
+        m = block_max(m, red);
+        if (threadIdx.x == 0) exps[r] = row_norm_exp(m);
+    }
+}
+
+__global__ __launch_bounds__(256) void rowexp_kn_kernel(const float* __restrict__ src, int64_t ld, int64_t rows,
+                                                        int64_t K, int64_t rows_p, const int8_t* __restrict__ kshift,
+                                                        int* __restrict__ exps) {
+    for (int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x; r < rows_p; r += (int64_t)gridDim.x * 256) {
+        float m = 0.0f;
+        if (r < rows)
+            for (int64_t k = 0; k < K; ++k) m = fmaxf(m, __builtin_fabsf(kscaled(src[k * ld + r], kshift, k)));
+        exps[r] = row_norm_exp(m);
+    }
+}
+
+namespace {
+// the fused row pack, items of 8 k per thread: MAXI 2 (Kp <= 4096) or 8 (<= 16384)
+template <bool HI_ONLY, bool VEC, bool SHIFT>
+void launch_rows_norm(const float* p, int64_t ld, int64_t rows, int64_t K, int64_t Kp, int64_t rows_p,
+                      const int8_t* kshift, uint16_t* out, int* exps, uint32_t* status, hipStream_t s) {
+    const dim3 grid((unsigned)std::min<int64_t>(rows_p, 65536));
+    if (Kp <= 4096)
+        hipLaunchKernelGGL((pack_rows_norm_kernel<HI_ONLY, VEC, SHIFT, 2>), grid, dim3(256), 0, s, p, ld, rows, K, Kp,
+                           rows_p, kshift, out, exps, status);
+    else
+        hipLaunchKernelGGL((pack_rows_norm_kernel<HI_ONLY, VEC, SHIFT, 8>), grid, dim3(256), 0, s, p, ld, rows, K, Kp,
+                           rows_p, kshift, out, exps, status);
+}
+constexpr int64_t kRowsNormMaxKp = 16384;
+}  // namespace
 
 hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int64_t K, int kn,
                        const int8_t* kshift, void* packed, uint32_t* status, hipStream_t s) {
@@ -232,37 +335,47 @@ hipError_t launch_pack(const void* src, bool f16, int64_t ld, int64_t rows, int6
     int64_t blocks = (total + 255) / 256;
     if (blocks > 256 * 64) blocks = 256 * 64;
     uint16_t* out = static_cast<uint16_t*>(packed);
+    int* exps = reinterpret_cast<int*>(static_cast<unsigned char*>(packed) +
+                                       (f16 ? pack_data_bytes_hi(rows, K) : pack_data_bytes(rows, K)));
     const uintptr_t align = f16 ? 7 : 15;   // 4 elements per vector load
     const bool vec = (reinterpret_cast<uintptr_t>(src) & align) == 0 && (ld & 3) == 0;
     if (f16) {
         const uint16_t* p = static_cast<const uint16_t*>(src);
         if (kn)
             hipLaunchKernelGGL(pack_colmajor_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, s, p, ld,
-                               rows, K, Kp, rows_p, kshift, out, status);
+                               rows, K, Kp, rows_p, kshift, out, exps, status);
         else if (vec)
             hipLaunchKernelGGL((pack_rowmajor_kernel<uint16_t, true>), dim3((unsigned)blocks), dim3(256), 0, s, p,
-                               ld, rows, K, Kp, rows_p, kshift, out, status);
+                               ld, rows, K, Kp, rows_p, kshift, out, exps, status);
         else
             hipLaunchKernelGGL((pack_rowmajor_kernel<uint16_t, false>), dim3((unsigned)blocks), dim3(256), 0, s,
-                               p, ld, rows, K, Kp, rows_p, kshift, out, status);
-    } else {
-        const float* p = static_cast<const float*>(src);
-        if (kn)
-            hipLaunchKernelGGL(pack_colmajor_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, p, ld, rows,
-                               K, Kp, rows_p, kshift, out, status);
-        else if (vec && !kshift) {
-            const int64_t c8n = Kp >> 3;
-            const dim3 grid((unsigned)std::min<int64_t>((c8n + 255) / 256, 64),
-                            (unsigned)std::min<int64_t>(rows_p, 16384));
-            hipLaunchKernelGGL(pack_rowmajor8_kernel<false>, grid, dim3(256), 0, s, p, ld, rows, K, Kp, rows_p, out,
-                               status);
-        } else if (vec)
-            hipLaunchKernelGGL((pack_rowmajor_kernel<float, true>), dim3((unsigned)blocks), dim3(256), 0, s, p, ld,
-                               rows, K, Kp, rows_p, kshift, out, status);
-        else
-            hipLaunchKernelGGL((pack_rowmajor_kernel<float, false>), dim3((unsigned)blocks), dim3(256), 0, s, p,
-                               ld, rows, K, Kp, rows_p, kshift, out, status);
+                               p, ld, rows, K, Kp, rows_p, kshift, out, exps, status);
+        return hipGetLastError();
     }
+    const float* p = static_cast<const float*>(src);
+    if (!kn && Kp <= kRowsNormMaxKp) {   // one pass: the row in registers
+        if (vec && kshift) launch_rows_norm<false, true, true>(p, ld, rows, K, Kp, rows_p, kshift, out, exps, status, s);
+        else if (vec) launch_rows_norm<false, true, false>(p, ld, rows, K, Kp, rows_p, kshift, out, exps, status, s);
+        else if (kshift) launch_rows_norm<false, false, true>(p, ld, rows, K, Kp, rows_p, kshift, out, exps, status, s);
+        else launch_rows_norm<false, false, false>(p, ld, rows, K, Kp, rows_p, kshift, out, exps, status, s);
+        return hipGetLastError();
+    }
+    // general path: the row exponents first, then the split
+    if (kn)
+        hipLaunchKernelGGL(rowexp_kn_kernel, dim3((unsigned)std::min<int64_t>((rows_p + 255) / 256, 4096)), dim3(256),
+                           0, s, p, ld, rows, K, rows_p, kshift, exps);
+    else
+        hipLaunchKernelGGL(rowexp_nk_kernel, dim3((unsigned)std::min<int64_t>(rows_p, 65536)), dim3(256), 0, s, p, ld,
+                           rows, K, rows_p, kshift, exps);
+    if (kn)
+        hipLaunchKernelGGL(pack_colmajor_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, p, ld, rows, K, Kp,
+                           rows_p, kshift, out, exps, status);
+    else if (vec)
+        hipLaunchKernelGGL((pack_rowmajor_kernel<float, true>), dim3((unsigned)blocks), dim3(256), 0, s, p, ld, rows,
+                           K, Kp, rows_p, kshift, out, exps, status);
+    else
+        hipLaunchKernelGGL((pack_rowmajor_kernel<float, false>), dim3((unsigned)blocks), dim3(256), 0, s, p, ld,
+                           rows, K, Kp, rows_p, kshift, out, exps, status);
     return hipGetLastError();
 }
 
@@ -270,11 +383,11 @@ hipError_t launch_pack_hi_f32(const float* src, int64_t ld, int64_t rows, int64_
                               hipStream_t s) {
     const int64_t Kp = pack_kp(K), rows_p = pack_rows(rows);
     if (rows_p * Kp == 0) return hipSuccess;
-    if ((reinterpret_cast<uintptr_t>(src) & 15) != 0 || (ld & 3) != 0) return hipErrorInvalidValue;
-    const int64_t c8n = Kp >> 3;
-    const dim3 grid((unsigned)std::min<int64_t>((c8n + 255) / 256, 64), (unsigned)std::min<int64_t>(rows_p, 16384));
-    hipLaunchKernelGGL(pack_rowmajor8_kernel<true>, grid, dim3(256), 0, s, src, ld, rows, K, Kp, rows_p,
-                       static_cast<uint16_t*>(packed), status);
+    if ((reinterpret_cast<uintptr_t>(src) & 15) != 0 || (ld & 3) != 0 || Kp > kRowsNormMaxKp)
+        return hipErrorInvalidValue;
+    int* exps = reinterpret_cast<int*>(static_cast<unsigned char*>(packed) + pack_data_bytes_hi(rows, K));
+    launch_rows_norm<true, true, false>(src, ld, rows, K, Kp, rows_p, nullptr, static_cast<uint16_t*>(packed), exps,
+                                        status, s);
     return hipGetLastError();
 }
 

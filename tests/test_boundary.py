@@ -104,15 +104,17 @@ def test_gemm_workspace_sizes():
         b = ws(M, 4096, 4096, 0)
         assert b % 256 == 0
     assert ws(64, 4096, 4096, 0) >= 64 * 4096 * 4
-    # prefill path: packed A (rows padded to 256, k to 32, 4 bytes per element) + packed W
-    assert ws(2048, 4096, 14336, 0) == 2048 * 14336 * 4 + 4096 * 14336 * 4
-    assert ws(2048, 4096, 14336, heal.HEAL_W_PACKED) == 2048 * 14336 * 4
+    # prefill path: packed A (rows padded to 256, k to 32, 4 bytes per element,
+    # then one int32 row exponent per padded row) + packed W
+    pk = lambda R, Kp, b: R * Kp * b + R * 4
+    assert ws(2048, 4096, 14336, 0) == pk(2048, 14336, 4) + pk(4096, 14336, 4)
+    assert ws(2048, 4096, 14336, heal.HEAL_W_PACKED) == pk(2048, 14336, 4)
     assert ws(2048, 4096, 14336, heal.HEAL_W_PACKED | heal.HEAL_A_PACKED) == 0
-    assert ws(8, 4096, 4096, heal.HEAL_A_PACKED) == 4096 * 4096 * 4   # packed A -> prefill path
-    assert ws(65, 100, 33, 0) == 256 * 64 * 4 + 256 * 64 * 4
-    assert heal.heal_pack_w_bytes(100, 33) == 256 * 64 * 4
-    assert heal.heal_pack_w_bytes(100, 33, heal.HEAL_W_F16) == 256 * 64 * 2      # hi parts only
-    assert ws(2048, 4096, 14336, heal.HEAL_W_F16) == 2048 * 14336 * 4 + 4096 * 14336 * 2
+    assert ws(8, 4096, 4096, heal.HEAL_A_PACKED) == pk(4096, 4096, 4)   # packed A -> prefill path
+    assert ws(65, 100, 33, 0) == pk(256, 64, 4) + pk(256, 64, 4)
+    assert heal.heal_pack_w_bytes(100, 33) == pk(256, 64, 4)
+    assert heal.heal_pack_w_bytes(100, 33, heal.HEAL_W_F16) == pk(256, 64, 2)      # hi parts only
+    assert ws(2048, 4096, 14336, heal.HEAL_W_F16) == pk(2048, 14336, 4) + pk(4096, 14336, 2)
     # BF16 three-way mode: 6 bytes per padded element, every M on the prefill path
     X3 = heal.HEAL_BF16X3
     assert heal.heal_pack_w_bytes(100, 33, X3) == 256 * 64 * 6
@@ -228,6 +230,11 @@ def test_qkv_proj_validation():
     assert wsq(2048, 4096, 32, 8, 64, 0) == 2048 * 48 * 64 * 4 + wsg(2048, 48 * 64, 4096, 0)
     assert wsq(2048, 4096, 32, 8, 128, heal.HEAL_ONE_PRODUCT) == \
         2048 * 6144 * 4 + wsg(2048, 6144, 4096, heal.HEAL_ONE_PRODUCT)
+    # K == 0: a zero product, staged and quantized to zero codes; the workspace
+    # holds it, so a missing or short one is rejected before any launch
+    assert wsq(8, 0, 4, 2, 128, 0) == 8 * 1024 * 4
+    assert _qkv(K=0, ws=None) == WS
+    assert _qkv(K=0, wsb=8 * 1024 * 4 - 256) == WS
 
 
 def _attn(B=2, T=16, Hq=8, Hkv=2, D=128, ws=FAKE, wsb=1 << 30, q=FAKE):

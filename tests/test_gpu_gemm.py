@@ -127,10 +127,29 @@ def test_gemm_k_zero_and_empty():
     assert out.shape == (0, 4)
 
 
-def test_gemm_range_flag():
-    A = np.ones((4, 64), np.float32)
+@pytest.mark.parametrize("M", [4, 40, 100])
+def test_gemm_activation_past_fp16_range_is_normalized(M):
+    """An activation beyond 65504 is brought into FP16's range with its row (decode
+    in-kernel split, split planes, prefill): no flag, and the tolerance holds."""
+    g = WL.rng(60 + M)
+    A = WL.normal(g, (M, 64))
     A[2, 5] = 70000.0
+    A[M - 1, 7] = -3.0e9
+    W = WL.normal(g, (8, 64), std=0.02)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    C = heal.heal_gemm_f32c(torch.from_numpy(A).to(DEV), torch.from_numpy(W).to(DEV), dev_status=st).cpu().numpy()
+    assert st.item() == 0
+    e = gemm_normwise_error(C, oracle.gemm_f64(A, W), A, W)
+    e32 = gemm_normwise_error(oracle.gemm_f32_naive(A, W), oracle.gemm_f64(A, W), A, W)
+    assert e <= gemm_tolerance(e32, 64)
+
+
+def test_gemm_range_flag_on_streamed_weight():
+    """The decode path splits an fp32 weight as it streams it, unnormalized: an
+    element at or past 65520 has an infinite fp16 high part and sets the flag."""
+    A = np.ones((4, 64), np.float32)
     W = np.ones((8, 64), np.float32)
+    W[3, 9] = 70000.0
     st = torch.zeros(1, dtype=torch.int32, device=DEV)
     heal.heal_gemm_f32c(torch.from_numpy(A).to(DEV), torch.from_numpy(W).to(DEV), dev_status=st)
     assert st.item() == heal.HEAL_FLAG_F16_RANGE
@@ -151,7 +170,7 @@ def test_gemm_decode_shapes_and_batch_invariance(K, N):
         outs[M] = heal.heal_gemm_f32c(Ad[:M], Wd).cpu().numpy()
     for M in Ms:
         assert np.array_equal(outs[M], outs[64][:M]), M
-    rows = np.array([0, 1, 7, 31, 63])
+    rows = np.arange(64)            # every row of the M = 64 call against the oracle
     C64 = oracle.gemm_f64_rows(A, W, rows)
     C32 = oracle.gemm_f32_naive_rows(A, W, rows)
     e_gpu = gemm_normwise_error(outs[64][rows], C64, A, W, rows=rows)
@@ -163,10 +182,48 @@ def test_gemm_decode_shapes_and_batch_invariance(K, N):
 @pytest.mark.parametrize("K,N", WL.PREFILL_KN)
 def test_gemm_prefill_full_size_sampled_rows(K, N):
     """Prefill shape M = 2048 with massive-activation channels, packed weight as
-    the benchmark times it; 24 sampled rows against the oracle."""
+    the benchmark times it; 256 sampled rows (all N columns) against the oracle."""
     A, W = WL.prefill_gemm(WL.PREFILL_M, K, N, seed=3000 + K)
-    rows = np.sort(WL.rng(K).choice(WL.PREFILL_M, size=24, replace=False))
+    rows = np.sort(WL.rng(K).choice(WL.PREFILL_M, size=256, replace=False))
     _check(A, W, "nk", packed=True, rows=rows, label="prefill")
+
+
+# ---- the packed operand layout -------------------------------------------------------------
+
+def unpack(buf, R, K, hi_only=False):
+    """Read a heal_pack_w buffer (test code): rows padded to 256, k to 32; per row
+    and 32-wide k block 32 hi then 32 residual fp16 (hi parts alone in the
+    hi-only form); then one int32 exponent per padded row.  Returns (hi, res, e)
+    for the R real rows, k padded."""
+    Rp, Kp = -(-R // 256) * 256, -(-K // 32) * 32
+    planes = 1 if hi_only else 2
+    data = np.frombuffer(buf[: Rp * Kp * 2 * planes].tobytes(), np.uint16).reshape(Rp, Kp // 32, planes, 32)
+    e = np.frombuffer(buf[Rp * Kp * 2 * planes: Rp * Kp * 2 * planes + Rp * 4].tobytes(), np.int32)
+    hi = data[:, :, 0, :].reshape(Rp, Kp)
+    res = data[:, :, 1, :].reshape(Rp, Kp) if not hi_only else np.zeros_like(hi)
+    assert not hi[R:].any() and not res[R:].any() and not e[R:].any()      # zero padding rows
+    assert not hi[:, K:].any() and not res[:, K:].any()                    # zero padding k
+    return hi[:R], res[:R], e[:R]
+
+
+@pytest.mark.parametrize("layout", ["nk", "kn"])
+@pytest.mark.parametrize("R,K,sigma", [(1, 7, 1.0), (300, 1000, 1e-6), (100, 4096, 3e4), (257, 14336, 1.0),
+                                       (64, 20000, 1e-3)])
+def test_pack_bit_exact_against_oracle(R, K, sigma, layout):
+    """heal_pack_w on fp32 values: hi parts, residuals and row exponents equal the
+    oracle's split of the normalized rows, bit for bit (the fused one-pass kernel
+    for K <= 16384 in the NK layout, the two-pass form otherwise)."""
+    print(f"pack R={R} K={K} sigma={sigma:g} {layout}", flush=True)
+    g = WL.rng(R + K)
+    X = (WL.normal(g, (R, K)) * np.float32(sigma))
+    X[:, g.choice(K, size=min(K, 3), replace=False)] *= np.float32(40.0)
+    X[R // 2] = 0.0                                   # a zero row: exponent 0
+    src = X if layout == "nk" else np.ascontiguousarray(X.T)
+    p = heal.heal_pack_w(torch.from_numpy(src).to(DEV), layout)
+    h, r, e = unpack(p.buf.cpu().numpy(), R, K)
+    oh, orr, oe = oracle.split_rownorm(X)
+    assert np.array_equal(e, oe)
+    assert np.array_equal(h[:, :K], oh) and np.array_equal(r[:, :K], orr)
 
 
 # ---- 16-bit weights (HEAL_W_F16): the two-product form -------------------------------------
@@ -222,12 +279,14 @@ def test_gemm_f16_weight_ragged_and_packed(M, N, K, layout):
     p16 = heal.heal_pack_w(W16d, layout)
     p32 = heal.heal_pack_w(W32d, layout)
     torch.cuda.synchronize()
-    # the fp16 weight packs its hi parts alone: exactly the hi halves of the fp32 copy's packing
-    n16 = heal.heal_pack_w_bytes(N, K, heal.HEAL_W_F16)
-    assert n16 * 2 == heal.heal_pack_w_bytes(N, K)
-    hi32 = p32.buf[: 2 * n16].view(-1, 2, 64)[:, 0, :].reshape(-1)
-    assert torch.equal(p16.buf[:n16], hi32)
-    assert not torch.any(p32.buf[: 2 * n16].view(-1, 2, 64)[:, 1, :])
+    # the fp16 weight packs its binary16 values alone, not normalized (exponents 0);
+    # the fp32 copy packs normalized rows whose residuals are all zero
+    Wnk = W32 if layout == "nk" else np.ascontiguousarray(W32.T)
+    h16, r16, e16 = unpack(p16.buf.cpu().numpy(), N, K, hi_only=True)
+    assert np.array_equal(h16[:, :K], Wnk.astype(np.float16).view(np.uint16)) and not e16.any()
+    h32, r32, e32 = unpack(p32.buf.cpu().numpy(), N, K)
+    oh, orr, oe = oracle.split_rownorm(Wnk)
+    assert np.array_equal(h32[:, :K], oh) and np.array_equal(e32, oe) and not r32.any()
     cp = heal.heal_gemm_f32c(Ad, p16).cpu().numpy()
     if M > 64:   # both through the prefill kernel's two-product form
         assert np.array_equal(cp, c16)

@@ -35,8 +35,10 @@ def _pow2(ks):
 @pytest.mark.parametrize("M", [1, 8, 16, 17, 64, 300])
 def test_kshift_gemm_within_tolerance_and_no_overflow(M):
     """Decode (in-kernel split, split pass) and prefill paths: with the shifts the
-    range flag stays clear and the result meets the tolerance; without them the
-    flag is raised."""
+    range flag stays clear and the result meets the tolerance.  Without them the
+    row normalization alone brings the rows into FP16's range: no flag either,
+    and the tolerance holds too (the shifts keep more bits of the ordinary
+    channels of those rows)."""
     K, N = 1024, 384
     print(f"kshift gemm M={M} K={K} N={N}", flush=True)
     A, W, ks = _case(M, K, N, seed=7000 + M)
@@ -48,15 +50,16 @@ def test_kshift_gemm_within_tolerance_and_no_overflow(M):
     assert st.item() == 0
     assert np.all(np.isfinite(C))
     st0 = torch.zeros(1, dtype=torch.int32, device=DEV)
-    heal.heal_gemm_f32c(Ad, torch.from_numpy(W).to(DEV), dev_status=st0)
-    assert st0.item() == heal.HEAL_FLAG_F16_RANGE
+    C0 = heal.heal_gemm_f32c(Ad, torch.from_numpy(W).to(DEV), dev_status=st0).cpu().numpy()
+    assert st0.item() == 0
     rows = np.arange(M) if M <= 64 else np.sort(WL.rng(M).choice(M, size=24, replace=False))
     C64 = oracle.gemm_f64_rows(A, W, rows)
     C32 = oracle.gemm_f32_naive_rows(A, W, rows)
-    e_gpu = gemm_normwise_error(C[rows], C64, A, W, rows=rows)
     e_naive = gemm_normwise_error(C32, C64, A, W, rows=rows)
-    print(f"  e_gpu={e_gpu:.3e} e_naive={e_naive:.3e}", flush=True)
-    assert e_gpu <= gemm_tolerance(e_naive, K)
+    for label, Cx in (("shifted", C), ("unshifted", C0)):
+        e_gpu = gemm_normwise_error(Cx[rows], C64, A, W, rows=rows)
+        print(f"  {label}: e_gpu={e_gpu:.3e} e_naive={e_naive:.3e}", flush=True)
+        assert e_gpu <= gemm_tolerance(e_naive, K)
 
 
 @pytest.mark.parametrize("M", [1, 16, 17, 64, 200])
