@@ -1,12 +1,28 @@
 // C ABI of libheal: argument validation (host only, before any HIP call),
 // workspace layout and kernel selection.  Entry points and their contracts
 // are documented in include/heal.h.
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdint>
 
 #include "heal_internal.h"
 
 using namespace heal;
+
+namespace heal {
+// Call epochs for the decode GEMM's split-K counters: unique within the
+// process; the start is taken from the clock so that a workspace that held
+// another process's counters is not mistaken for this one's.
+uint64_t next_epoch() {
+    static std::atomic<uint64_t> next{
+        ((uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() & 0xFFFFFFFFull) << 12 | 1u};
+    for (;;) {
+        const uint64_t e = next.fetch_add(1, std::memory_order_relaxed) & 0xFFFFFFFFFFFFull;
+        if (e != 0) return e;
+    }
+}
+}  // namespace heal
 
 namespace {
 
@@ -168,8 +184,8 @@ heal_status gemm_impl(const float* A, int64_t lda, const void* W, int64_t ldw, f
         if (ldw >= kMaxDecodeLdw || lda >= kMaxDecodeLda) return HEAL_ERR_UNSUPPORTED;
         const DecodePlan p = decode_plan(M, N, K);
         unsigned char* ws = static_cast<unsigned char*>(workspace);
-        return hip_status(
-            launch_gemm_decode(A, lda, a_kshift, W, wf16, one, ldw, C, ldc, M, N, K, ws, p, dev_status, s));
+        return hip_status(launch_gemm_decode(A, lda, a_kshift, W, wf16, one, ldw, C, ldc, M, N, K, ws, p,
+                                             next_epoch(), dev_status, s));
     }
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     const void* apk = A;

@@ -7,19 +7,24 @@
 //  * W is read once from HBM as fp32 [N, K] (4 bytes per element, the same
 //    bytes as its two fp16 parts) and split into hi/lo in registers;
 //  * FP16's narrow range (the same paragraph: handled by targeted
-//    rescaling): a small first kernel (decode_prep_kernel, one workgroup per
-//    activation row) finds each row's largest magnitude and the power of two
-//    2^e that puts it in [2^14, 2^15); rows are split as x 2^e and each
-//    output is multiplied back by 2^-e in fp32, so the result does not
-//    depend on the activation's absolute scale (W is split as it is);
+//    rescaling): every 128-wide k block of every activation row is
+//    multiplied by the power of two 2^e that puts its largest magnitude in
+//    [2^14, 2^15) before its split; the block's products accumulate in fresh
+//    fp32 accumulators, which are folded into the running sums as
+//    (acc_hh + 2^-10 acc_c) 2^-e once per block.  The result thus does not
+//    depend on the activation's absolute scale (W is split as it is), and no
+//    pass over the activation is needed before the split;
 //  * the activation (<= 64 rows) is staged in 128-wide k blocks in a
 //    double-buffered LDS tile, in MFMA operand order, so every operand read
-//    is one conflict-free 16-byte LDS access.  Up to 16 rows, each
-//    workgroup loads the next block into registers while the current one
-//    is in use and normalizes and splits it itself; above 16 rows, where that
-//    split would be repeated by every workgroup, the first kernel also writes
-//    the split rows as operand-ordered planes and workgroups copy blocks of
-//    them into LDS with direct-to-LDS loads;
+//    is one conflict-free 16-byte LDS access; the block's 16 MT exponents
+//    travel with it.  Up to 16 rows, each workgroup loads the next block into
+//    registers while the current one is in use (one wave per four rows, so
+//    a row's block maximum is a reduction inside one wave) and normalizes
+//    and splits it itself: one launch in all.  Above 16 rows, where that work
+//    would be repeated by every workgroup, a first small kernel
+//    (decode_prep_kernel, one workgroup per row) writes the blocks the same
+//    way into operand-ordered planes once, and workgroups copy them into LDS
+//    with direct-to-LDS loads;
 //  * v_mfma_f32_16x16x32_f16 with the activation as the 16-row operand and W
 //    as the 16-column operand (16 W rows per wave), so output columns are
 //    consecutive lanes;
@@ -29,10 +34,17 @@
 //  * W for the next 8 k steps is always in flight: every step issues exactly
 //    two W loads (the last steps re-read a clamped step), so the number of
 //    loads outstanding at each block boundary is a constant;
-//  * split-K: the k range is cut into chunks chosen from (N, K) only, and
-//    chunk partials are summed in chunk order by a second kernel.  The
-//    summation order of an output therefore does not depend on M: a
-//    decode-sized product does not change with the batch it is computed in.
+//  * split-K: the k range is cut into chunks chosen from (N, K) only.  Each
+//    workgroup writes its chunk's partial outputs with write-through stores,
+//    waits for them to complete, sets its (row block, chunk) flag to the
+//    call's epoch the same way, and reads its row block's flags; a workgroup
+//    that finds them all set sums the chunk partials in chunk order (its own
+//    from registers, the others with loads that bypass the non-coherent L2)
+//    and writes C.  Flags from earlier calls hold other epochs, so the
+//    workspace needs no zeroing pass; no atomic read-modify-write, no second
+//    launch, no L2 write-back, and the summation order of an output does not
+//    depend on M or on arrival order: a decode-sized product does not change
+//    with the batch it is computed in.
 #include <type_traits>
 
 #include "heal_internal.h"
@@ -72,54 +84,69 @@ __device__ __forceinline__ void mfma16(const half8& a, const half8& b, floatx4& 
 template <int MT>
 constexpr int block_bytes() { return 2 * STEPS * MT * 64 * 16; }
 
-// ---- the first kernel: row exponents and (MT > 1) operand-ordered planes ----
-// Workgroup m (one per row of the MT 16-row tiles) takes row m of A: its
-// largest magnitude (after the optional 2^-kshift[k]) gives the row exponent
-// e_m (aexp[m]; rows >= M get 0).  With MT > 1 it then writes the row's
-// split, x 2^(e_m - kshift[k]) as hi = fp16, lo = fp16((x - hi) 2^10), in
-// operand order: block b (k in [128 b, 128 b + 128)), plane p (0 = hi,
-// 1 = lo), step s, tile t, lane l = 16 g + r holds, as 8 fp16, row 16 t + r
-// at k = 128 b + 32 s + {4g .. 4g+3, 16+4g .. 16+4g+3}.  Rows >= M and
-// k >= K are zero.
+// Bytes of one activation block image: the two planes, then the exponents
+// of its 16 MT rows (int32, padded to 256 bytes).
 template <int MT>
-__global__ __launch_bounds__(256) void decode_prep_kernel(const float* __restrict__ A, int64_t lda, int M, int K,
-                                                          int nblk, const int8_t* __restrict__ kshift,
-                                                          int* __restrict__ aexp, unsigned char* __restrict__ out) {
-    __shared__ float red[4];
+constexpr int img_bytes() { return block_bytes<MT>() + 256; }
+
+// ---- the first kernel (MT > 1): operand-ordered blocks with their exponents
+// Workgroup (m, y) takes 16 blocks of row m of A (k in [2048 y, 2048 y +
+// 2048)), one float4 of 4 consecutive k per lane: the 32 lanes of a half
+// wave hold one 128-wide block, so the block's largest magnitude (after the
+// optional 2^-kshift[k]) is a reduction inside the half wave.  It gives the
+// block's exponent e; the lane writes its 4 values, x 2^(e - kshift[k]), split
+// as hi = fp16, lo = fp16((x - hi) 2^10), into block b's image: plane p
+// (0 = hi, 1 = lo), step s, tile t, lane 16 g + r holds, as 8 fp16, row
+// 16 t + r at k = 128 b + 32 s + {4g .. 4g+3, 16+4g .. 16+4g+3}; then e at
+// byte block_bytes + 4 m.  Rows >= M and k >= K are zero (exponent 0).  One
+// load per thread: the kernel costs about one memory latency.
+constexpr int PREP_T = 512;
+template <int MT, bool AVEC>
+__global__ __launch_bounds__(PREP_T) void decode_prep_kernel(const float* __restrict__ A, int64_t lda, int M, int K,
+                                                             int nblk, const int8_t* __restrict__ kshift,
+                                                             unsigned char* __restrict__ out) {
+    constexpr int BB = block_bytes<MT>();
     const int m = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int q = blockIdx.y * PREP_T + threadIdx.x;   // float4 slot: k = 4 q .. 4 q + 3
+    const int t = m >> 4, r = m & 15;
     const float* a = A + (int64_t)m * lda;
-    auto shift = [&](int k) { return kshift ? -(int)kshift[k] : 0; };
-    float mx = 0.0f;
-    for (int k = tid; k < K && m < M; k += 256) mx = fmaxf(mx, __builtin_fabsf(__builtin_ldexpf(a[k], shift(k))));
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    if ((tid & 63) == 0) red[tid >> 6] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const int e = row_norm_exp(mx);
-    if (tid == 0) aexp[m] = e;
-    if constexpr (MT > 1) {
-        const int t = m >> 4, r = m & 15;
-        for (int item = tid; item < nblk * STEPS * 4; item += 256) {   // (b, s, g)
-            const int g = item & 3, st = (item >> 2) % STEPS, b = item / (4 * STEPS);
-            const int k0 = b * KA + 32 * st;
-            half8 h, lo;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int k = k0 + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
-                _Float16 hh, ll;
-                // one scaling by 2^(e - kshift[k]), as the in-kernel split does
-                split_one((m < M && k < K) ? __builtin_ldexpf(a[k], e + shift(k)) : 0.0f, hh, ll);
-                h[j] = hh;
-                lo[j] = ll;
-            }
-            unsigned char* blk = out + (int64_t)b * block_bytes<MT>();
-            const int off = ((st * MT + t) * 64 + 16 * g + r) * 16;
-            *reinterpret_cast<half8*>(blk + off) = h;
-            *reinterpret_cast<half8*>(blk + block_bytes<MT>() / 2 + off) = lo;
+    auto val = [&](int k) {
+        return (m < M && k < K) ? __builtin_ldexpf(a[k], kshift ? -(int)kshift[k] : 0) : 0.0f;
+    };
+    const int k = 4 * q;
+    float4 v;
+    if (AVEC && m < M && k + 3 < K) {
+        v = *reinterpret_cast<const float4*>(a + k);
+        if (kshift) {
+            v.x = __builtin_ldexpf(v.x, -(int)kshift[k]);
+            v.y = __builtin_ldexpf(v.y, -(int)kshift[k + 1]);
+            v.z = __builtin_ldexpf(v.z, -(int)kshift[k + 2]);
+            v.w = __builtin_ldexpf(v.w, -(int)kshift[k + 3]);
         }
+    } else {
+        v = make_float4(val(k), val(k + 1), val(k + 2), val(k + 3));
     }
+    float mx = fmaxf(fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)), fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w)));
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
+    if (q >= nblk * 32) return;   // past the last block (whole half waves)
+    const int e = row_norm_exp(mx);
+    const int b = q >> 5, j = q & 31;   // j = 8 s + 4 h + g: k = 128 b + 32 s + 16 h + 4 g
+    const int st = j >> 3, h = (j >> 2) & 1, g = j & 3;
+    const float x[4] = {v.x, v.y, v.z, v.w};
+    half4 hi, lo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        _Float16 hh, ll;
+        split_one(__builtin_ldexpf(x[i], e), hh, ll);
+        hi[i] = hh;
+        lo[i] = ll;
+    }
+    unsigned char* blk = out + (int64_t)b * img_bytes<MT>();
+    const int off = ((st * MT + t) * 64 + 16 * g + r) * 16 + 8 * h;
+    *reinterpret_cast<half4*>(blk + off) = hi;
+    *reinterpret_cast<half4*>(blk + BB / 2 + off) = lo;
+    if (j == 0) *reinterpret_cast<int*>(blk + BB + 4 * m) = e;
 }
 
 __device__ __forceinline__ void split8(const float4& a, const float4& b, half8& h, half8& l) {
@@ -148,27 +175,28 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // lanes load element by element with bounds checks, and block boundaries
 // wait for every load.
 // WF16: W holds binary16 values, exact in fp16: its residual is zero, so each
-// step keeps two products, A_hi.W and A_lo.W (2^-10 applied at the end).
+// step keeps two products, A_hi.W and A_lo.W (2^-10 applied in the fold).
 // AVEC: A rows 16-byte aligned, activation units load as one 16-byte load.
-// MT == 1 stages A itself (A, lda); MT > 1 copies the pre-split blocks (Ablk).
+// MT == 1 stages A itself (A, lda); MT > 1 copies the block images (Ablk).
 // SHIFT (MT == 1): element (m, k) of A is multiplied by 2^-kshift[k] before
-// its split.  ONE: plain FP16, the A_hi.W_hi product alone.
+// its block maximum and split.  ONE: plain FP16, the A_hi.W_hi product alone.
 template <int MT, bool VEC, bool WF16, bool AVEC, bool SHIFT, bool ONE, int NWK>
 __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __restrict__ A, int64_t lda,
-                                                          const int* __restrict__ aexp,
                                                           const unsigned char* __restrict__ Ablk,
-                                                          int a_total_bytes, const void* __restrict__ W,
-                                                          int64_t ldw, float* __restrict__ out, int64_t ldo,
-                                                          int64_t split_stride, int M, int N, int K,
-                                                          int kchunk, const int8_t* __restrict__ kshift,
+                                                          uint32_t a_total_bytes, const void* __restrict__ W,
+                                                          int64_t ldw, float* __restrict__ C, int64_t ldc,
+                                                          float* __restrict__ part,
+                                                          unsigned long long* __restrict__ flag_base, uint64_t epoch,
+                                                          int M, int N, int K, int kchunk,
+                                                          const int8_t* __restrict__ kshift,
                                                           uint32_t* __restrict__ status) {
     static_assert(!SHIFT || MT == 1, "with MT > 1 the shift is applied by decode_prep_kernel");
     constexpr int BB = block_bytes<MT>();
+    constexpr int SB = img_bytes<MT>();             // LDS bytes per block buffer: planes + exponents
     constexpr bool INK = MT == 1;                   // split the activation in the kernel
-    constexpr int AU = 2 * MT;                      // 4-wide activation units per thread per block
     static_assert(NWK == NW || (NWK == 2 * NW && MT > 1), "8 waves only with the copied activation");
     constexpr int DMA_PER_WAVE = BB / 1024 / NWK;   // 1 KB per wave-wide direct-to-LDS load
-    extern __shared__ __attribute__((aligned(16))) unsigned char sa[];   // 2 x BB
+    extern __shared__ __attribute__((aligned(16))) unsigned char sa[];   // 2 x SB
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -182,27 +210,26 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
     const int nsteps = (k_end - k_begin + 31) / 32;
     const int nblocks = (nsteps + STEPS - 1) / STEPS;
 
-    // ---- activation blocks.  Unit x = tid + 256 i (i < AU) of a block is 4
-    //      consecutive k of one row: r = x % 16, g = (x / 16) % 4, half =
-    //      (x / 64) % 2, step s = (x / 128) % 4, tile t = x / 512; it holds
-    //      row 16 t + r at k = 128 b + 32 s + 16 half + 4 g .. + 3, and its
-    //      hi and lo halves go to the 16-byte operand slot (s, t, lane 16 g + r),
-    //      bytes 8 half .. 8 half + 7, of the hi and lo planes.
-    float4 areg[AU];
-    int sreg[AU][4];   // SHIFT: the units' 2^-kshift exponents (k >= K reads 0)
+    // ---- MT == 1: activation blocks split in the kernel.  Wave w owns rows
+    //      4w .. 4w+3; lane l's unit i (i < 2) is 4 consecutive k of row
+    //      r = 4w + l % 4 at k = 128 b + 32 s + 16 half + 4 gg with gg =
+    //      (l / 4) % 4, half = (l / 16) % 2, s = (l / 32) % 2 + 2 i.  Its hi
+    //      and lo halves go to the 16-byte operand slot (s, lane 16 gg + r),
+    //      bytes 8 half .. 8 half + 7, of the hi and lo planes; the row's block
+    //      exponent to byte BB + 4 r.
+    float4 areg[2];
+    int sreg[2][4];   // SHIFT: the units' 2^-kshift exponents (k >= K reads 0)
     // rows >= M fall outside the resource and read as zero; k past the
     // chunk end is zeroed when the block is stored
     const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(A, (uint32_t)((int64_t)M * lda * 4));
     const __amdgpu_buffer_rsrc_t ksrc = make_rsrc(kshift, SHIFT ? (uint32_t)K : 0u);
-    auto unit_k = [&](int b, int x) {
-        return k_begin + KA * b + 32 * ((x >> 7) & 3) + 16 * ((x >> 6) & 1) + 4 * ((x >> 4) & 3);
-    };
+    const int ur = 4 * wave + (lane & 3);
+    const int ugg = (lane >> 2) & 3, uhalf = (lane >> 4) & 1, ust = (lane >> 5) & 1;
+    auto unit_k = [&](int b, int i) { return k_begin + KA * b + 32 * (ust + 2 * i) + 16 * uhalf + 4 * ugg; };
     auto load_a = [&](int b) {
 #pragma unroll
-        for (int i = 0; i < AU; ++i) {
-            const int x = tid + 256 * i;
-            const int m = 16 * (x >> 9) + (x & 15);
-            const uint32_t off = (uint32_t)(((int64_t)m * lda + unit_k(b, x)) * 4);
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t off = (uint32_t)(((int64_t)ur * lda + unit_k(b, i)) * 4);
             if constexpr (AVEC) {
                 areg[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, off, 0, 0));
             } else {
@@ -212,51 +239,64 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
                                       __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(arsrc, off + 12, 0, 0)));
             }
             if constexpr (SHIFT) {
-                const uint32_t k0 = (uint32_t)unit_k(b, x);
+                const uint32_t k0 = (uint32_t)unit_k(b, i);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     sreg[i][j] = (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(ksrc, k0 + j, 0, 0);
             }
         }
     };
-    // MT == 1: the thread's units all lie in row tid % 16; its exponent
-    const int erow = INK ? aexp[tid & 15] : 0;
     auto store_a = [&](int b) {
-        unsigned char* base = sa + (b & 1) * BB;
+        unsigned char* base = sa + (b & 1) * SB;
+        float v[2][4];
+        float mx = 0.0f;
 #pragma unroll
-        for (int i = 0; i < AU; ++i) {
-            const int x = tid + 256 * i;
-            const int r = x & 15, gg = (x >> 4) & 3, half = (x >> 6) & 1, st = (x >> 7) & 3, t = x >> 9;
-            const int k = unit_k(b, x);
-            float v[4] = {k < k_end ? areg[i].x : 0.0f, k + 1 < k_end ? areg[i].y : 0.0f,
-                          k + 2 < k_end ? areg[i].z : 0.0f, k + 3 < k_end ? areg[i].w : 0.0f};
+        for (int i = 0; i < 2; ++i) {
+            const int k = unit_k(b, i);
+            const float x[4] = {areg[i].x, areg[i].y, areg[i].z, areg[i].w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = __builtin_ldexpf(v[j], SHIFT ? erow - sreg[i][j] : erow);
+            for (int j = 0; j < 4; ++j) {
+                v[i][j] = k + j < k_end ? (SHIFT ? __builtin_ldexpf(x[j], -sreg[i][j]) : x[j]) : 0.0f;
+                mx = fmaxf(mx, __builtin_fabsf(v[i][j]));
+            }
+        }
+        // the row's maximum over the block: the 16 lanes with the same l % 4
+#pragma unroll
+        for (int off = 4; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        const int e = row_norm_exp(mx);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
             half4 h, l;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 _Float16 hh, ll;
-                split_one(v[j], hh, ll);
+                split_one(__builtin_ldexpf(v[i][j], e), hh, ll);
                 h[j] = hh;
                 l[j] = ll;
             }
-            const int off = ((st * MT + t) * 64 + 16 * gg + r) * 16 + 8 * half;
+            const int off = ((ust + 2 * i) * 64 + 16 * ugg + ur) * 16 + 8 * uhalf;
             *reinterpret_cast<half4*>(base + off) = h;
             *reinterpret_cast<half4*>(base + BB / 2 + off) = l;
         }
+        if ((lane >> 2) == 0) *reinterpret_cast<int*>(base + BB + 4 * ur) = e;
     };
 
-    // pre-split activation blocks: wave w copies 1 KB pieces w, w + NWK, ...
+    // block images (MT > 1): wave w copies 1 KB pieces w, w + NWK, ... of the
+    // planes; wave 0 also the 256 bytes of exponents (4 bytes per lane)
     const int blk0 = k_begin / KA;
-    const __amdgpu_buffer_rsrc_t pbrsrc = make_rsrc(Ablk, (uint32_t)a_total_bytes);
+    const __amdgpu_buffer_rsrc_t pbrsrc = make_rsrc(Ablk, a_total_bytes);
     auto dma_block = [&](int b) {
 #pragma unroll
         for (int i = 0; i < DMA_PER_WAVE; ++i) {
             const int piece = wave + NWK * i;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(pbrsrc, (lds_ptr)(sa + (b & 1) * BB + piece * 1024), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(pbrsrc, (lds_ptr)(sa + (b & 1) * SB + piece * 1024), 16,
                                                      (uint32_t)(lane * 16),
-                                                     (uint32_t)((blk0 + b) * BB + piece * 1024), 0, 0);
+                                                     (uint32_t)(blk0 + b) * (uint32_t)SB + piece * 1024u, 0, 0);
         }
+        if (wave == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(pbrsrc, (lds_ptr)(sa + (b & 1) * SB + BB), 4,
+                                                     (uint32_t)(lane * 4), (uint32_t)(blk0 + b) * (uint32_t)SB + BB,
+                                                     0, 0);
     };
 
     // W: lane reads row n, k = k_begin + 32 step + {4g.., 16+4g..}
@@ -306,11 +346,13 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
         }
     };
 
+    // running sums (fp32) and one block's accumulators
+    float tot[MT][4];
     floatx4 acc_hh[MT], acc_c[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { acc_hh[t][e] = 0.f; acc_c[t][e] = 0.f; }
+        for (int e = 0; e < 4; ++e) tot[t][e] = 0.f;
 
     // prologue: W for steps 0 .. PFW-1 and activation block 0 in flight
     // together; block 0 lands in LDS buffer 0 (split here, or copied, in
@@ -345,7 +387,11 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
             else dma_block(b + 1);
         }
         __builtin_amdgcn_sched_barrier(0);
-        const unsigned char* abuf = sa + (b & 1) * BB;
+        const unsigned char* abuf = sa + (b & 1) * SB;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { acc_hh[t][e] = 0.f; acc_c[t][e] = 0.f; }
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) {
             const int step = b * STEPS + s;
@@ -371,6 +417,16 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
                     if constexpr (!ONE) mfma16(al, wh, acc_c[t]);
                 }
             }
+        }
+        // fold the block: rows t*16 + 4g + e of this lane, scaled by their
+        // block exponents 2^-e
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            const int4 er = *reinterpret_cast<const int4*>(abuf + BB + 4 * (t * 16 + 4 * g));
+            const int ev[4] = {er.x, er.y, er.z, er.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                tot[t][e] += __builtin_ldexpf(acc_hh[t][e] + acc_c[t][e] * 0.0009765625f, -ev[e]);
         }
         if (more) {
             // the other buffer was last read in block b - 1, before the
@@ -407,54 +463,101 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
     if (status && __builtin_amdgcn_ballot_w64(wmax >= 65520.0f) && lane == 0)
         atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
 
-    // ---- epilogue: lane holds column n, rows t*16 + 4g + e; each output is
-    //      (acc_hh + 2^-10 acc_c) 2^-e_m --------------------------------------
-    if (!row_ok) return;
-    float* o = out + split * split_stride;
+    // ---- epilogue: lane holds column n, rows t*16 + 4g + e ------------------
+    const int nsplit = gridDim.y;
+    if (nsplit == 1) {
+        if (!row_ok) return;
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        const int4 er = *reinterpret_cast<const int4*>(aexp + t * 16 + 4 * g);
-        const int ev[4] = {er.x, er.y, er.z, er.w};
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = t * 16 + 4 * g + e;
+                if (m < M) C[(int64_t)m * ldc + n] = tot[t][e];
+            }
+        return;
+    }
+    // split-K: this chunk's partials P[split][m][n], stored through to memory
+    // (write-through: no dirty L2 line to write back), completed before the
+    // workgroup counts itself in on its row block's counter
+    const int64_t pstride = (int64_t)M * N;
+    if (row_ok) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = t * 16 + 4 * g + e;
+                if (m < M)
+                    __hip_atomic_store(part + split * pstride + (int64_t)m * N + n, tot[t][e], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // then the workgroup's flag for (row block, chunk) := this call's epoch,
+    // also written through and completed; then it reads the flags of all
+    // chunks of its row block.  The workgroup whose flag completes last sees
+    // every flag set, so at least one workgroup sums; any other that sees
+    // them all too writes the same values.  A flag from an earlier call (or
+    // whatever the workspace held) differs from this call's epoch.
+    __shared__ int missing;
+    unsigned long long* flags = flag_base + (int64_t)blockIdx.x * nsplit;
+    if (tid == 0) missing = 0;
+    __syncthreads();
+    if (tid == 0) {
+        __hip_atomic_store(flags + split, (unsigned long long)epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    __syncthreads();
+    bool miss = false;
+    for (int j = tid; j < nsplit; j += 64 * NWK)
+        miss |= __hip_atomic_load(flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (unsigned long long)epoch;
+    if (__builtin_amdgcn_ballot_w64(miss) && lane == 0) missing = 1;
+    __syncthreads();
+    if (missing || !row_ok) return;
+    // a workgroup that saw every chunk done: C = sum over chunks in chunk order
+    // (the other chunks' partials read past the L2, its own from registers);
+    // the loads of NB chunks for all the lane's outputs are in flight together
+    constexpr int NB = 16 / MT;
+    float acc[MT][4];
+    for (int s0 = 0; s0 < nsplit; s0 += NB) {
+        float pv[NB][MT][4];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int sj = min(s0 + j, nsplit - 1);
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = min(t * 16 + 4 * g + e, M - 1);
+                    pv[j][t][e] = sj == split ? tot[t][e]
+                                              : __hip_atomic_load(part + sj * pstride + (int64_t)m * N + n,
+                                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            if (s0 + j < nsplit)
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[t][e] = (s0 + j == 0) ? pv[j][t][e] : acc[t][e] + pv[j][t][e];
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int m = t * 16 + 4 * g + e;
-            if (m < M) o[(int64_t)m * ldo + n] = __builtin_ldexpf(acc_hh[t][e] + acc_c[t][e] * 0.0009765625f, -ev[e]);
+            if (m < M) C[(int64_t)m * ldc + n] = acc[t][e];
         }
-    }
-}
-
-// C[m, n] = sum over chunks s (in order) of P[s, m, n].  The partials of a
-// batch of chunks are loaded together (the clamped index keeps every load in
-// bounds) and then added in chunk order, so the chain of adds waits on one
-// round of loads per batch instead of one per chunk.
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, int splits,
-                                                            int64_t M, int64_t N, float* __restrict__ C,
-                                                            int64_t ldc) {
-    constexpr int BATCH = 8;
-    const int64_t total = M * N;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        float acc = 0.0f;
-        for (int s0 = 0; s0 < splits; s0 += BATCH) {
-            float v[BATCH];
-#pragma unroll
-            for (int j = 0; j < BATCH; ++j) v[j] = P[(int64_t)min(s0 + j, splits - 1) * total + i];
-#pragma unroll
-            for (int j = 0; j < BATCH; ++j)
-                if (s0 + j < splits) acc = (s0 + j == 0) ? v[j] : acc + v[j];
-        }
-        const int64_t m = i / N, n = i - m * N;
-        C[m * ldc + n] = acc;
-    }
 }
 
 int mtiles(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
 }  // namespace
 
-// workspace: row exponents (256 bytes), activation planes, split-K partials
-constexpr int64_t kExpBytes = 256;
-int64_t DecodePlan::bytes() const { return kExpBytes + (a_bytes + 255) / 256 * 256 + (p_bytes + 255) / 256 * 256; }
+// workspace: split-K flags, activation block images, split-K partials
+int64_t DecodePlan::bytes() const {
+    return (c_bytes + 255) / 256 * 256 + (a_bytes + 255) / 256 * 256 + (p_bytes + 255) / 256 * 256;
+}
 
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
     DecodePlan p{};
@@ -468,19 +571,22 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
     p.splits = (int)std::max<int64_t>(1, (K + p.kchunk - 1) / p.kchunk);
     const int64_t ablocks = (K + KA - 1) / KA;
     const int mt = mtiles(M);
-    p.a_bytes = mt == 1 ? 0 : ablocks * (mt == 2 ? block_bytes<2>() : block_bytes<4>());
+    p.a_bytes = mt == 1 ? 0 : ablocks * (mt == 2 ? img_bytes<2>() : img_bytes<4>());
     p.p_bytes = p.splits > 1 ? (p.splits * M * N * 4 + 255) / 256 * 256 : 0;
+    p.ncount = p.splits > 1 ? (N + DEC_ROWS - 1) / DEC_ROWS * p.splits : 0;   // (row block, chunk) flags
+    p.c_bytes = p.ncount * 8;
     return p;
 }
 
 hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift, const void* W, bool wf16,
                               bool one, int64_t ldw, float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                              void* workspace, const DecodePlan& plan, uint32_t* status, hipStream_t s) {
+                              void* workspace, const DecodePlan& plan, uint64_t epoch, uint32_t* status,
+                              hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
     if (M > 64 || K == 0) return hipErrorInvalidValue;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    int* aexp = reinterpret_cast<int*>(ws);
-    unsigned char* ablk = ws + kExpBytes;
+    unsigned long long* flags = reinterpret_cast<unsigned long long*>(ws);
+    unsigned char* ablk = ws + (plan.c_bytes + 255) / 256 * 256;
     float* part = reinterpret_cast<float*>(ablk + (plan.a_bytes + 255) / 256 * 256);
     const int nablk = (int)((K + KA - 1) / KA);
     const int mt = mtiles(M);
@@ -488,9 +594,6 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
     const bool wide = mt > 1 && nblk2 * plan.splits >= (mt == 4 ? WIDE_MIN_WG4 : WIDE_MIN_WG2);
     const int wg_rows = (wide ? 2 * NW : NW) * ROWS_PER_WAVE;
     const dim3 grid((unsigned)((N + wg_rows - 1) / wg_rows), (unsigned)plan.splits);
-    float* out = plan.splits > 1 ? part : C;
-    const int64_t ldo = plan.splits > 1 ? N : ldc;
-    const int64_t stride = plan.splits > 1 ? M * N : 0;
     // W loads of 8 elements per step need rows aligned to the load width
     // (16 bytes fp32, 8 bytes fp16) and whole k32 steps
     const uintptr_t walign = wf16 ? 7 : 15;
@@ -499,7 +602,8 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
     const bool avec = (reinterpret_cast<uintptr_t>(A) & 15) == 0 && (lda & 3) == 0;
 #define HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW_)                                      \
     hipLaunchKernelGGL((gemm_decode_kernel<MT_, VEC_, F16_, AV_, SH_, ONE_, NW_>), grid, dim3(64 * NW_), \
-                       2 * block_bytes<MT_>(), s, A, lda, aexp, ablk, (int)plan.a_bytes, W, ldw, out, ldo, stride, \
+                       2 * img_bytes<MT_>(), s, A, lda, ablk, (uint32_t)plan.a_bytes, W, ldw, C, ldc, part,            \
+                       flags, epoch,                                                                          \
                        (int)M, (int)N, (int)K, (int)plan.kchunk, kshift, status)
 #define HEAL_DEC_LAUNCH(MT_, VEC_, F16_, AV_, SH_, ONE_)                                                \
     do {                                                                                                \
@@ -522,8 +626,15 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
     } while (0)
 #define HEAL_DEC(MT_, SH_)                                                                              \
     do {                                                                                                \
-        hipLaunchKernelGGL((decode_prep_kernel<MT_>), dim3(16 * (MT_)), dim3(256), 0, s, A, lda, (int)M,   \
-                           (int)K, nablk, kshift, aexp, ablk);                                          \
+        if constexpr ((MT_) > 1) {                                                                      \
+            const dim3 pgrid(16 * (MT_), (unsigned)((nablk * 32 + PREP_T - 1) / PREP_T));                \
+            if (avec)                                                                                   \
+                hipLaunchKernelGGL((decode_prep_kernel<MT_, true>), pgrid, dim3(PREP_T), 0, s, A, lda, (int)M, \
+                                   (int)K, nablk, kshift, ablk);                                        \
+            else                                                                                        \
+                hipLaunchKernelGGL((decode_prep_kernel<MT_, false>), pgrid, dim3(PREP_T), 0, s, A, lda, (int)M, \
+                                   (int)K, nablk, kshift, ablk);                                        \
+        }                                                                                               \
         if (wf16) {                                                                                     \
             if (vec) HEAL_DEC_AV(MT_, true, true, SH_);                                                 \
             else HEAL_DEC_AV(MT_, false, true, SH_);                                                    \
@@ -545,12 +656,6 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
 #undef HEAL_DEC_MAIN
 #undef HEAL_DEC_LAUNCH
 #undef HEAL_DEC_LAUNCH_NW
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || plan.splits == 1) return e;
-    const int64_t total = M * N;
-    const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 256 * 16);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, part, plan.splits, M, N, C,
-                       ldc);
     return hipGetLastError();
 }
 

@@ -191,13 +191,16 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
 bool prefill_ksplit(int64_t M, int64_t N, int64_t K);
 
 // Decode path (M <= 64): fp32 W [N,K] streamed and split in registers, the
-// activation rows normalized by a first small kernel (their exponents, and for
-// M > 16 their split planes).  Workspace, each part 256-byte aligned: the row
-// exponents (256 bytes), the split activation planes (a_bytes), the split-K
-// partials (p_bytes).
+// activation normalized per row and 128-wide k block (in the GEMM kernel up
+// to 16 rows, else by a first small kernel that writes the split blocks).
+// Workspace, each part 256-byte aligned: the split-K flags (c_bytes), the
+// split activation block images (a_bytes, M > 16), the split-K partials
+// (p_bytes).
 struct DecodePlan {
     int splits;        // number of K chunks (fixed by N and K only)
     int64_t kchunk;    // reduction length of one chunk (multiple of 256)
+    int64_t ncount;    // split-K flags (per 64-row block of W and chunk), 0 without split-K
+    int64_t c_bytes;   // workspace bytes of the flags
     int64_t a_bytes;   // workspace bytes of the split activation planes
     int64_t p_bytes;   // workspace bytes of the split-K partials
     int64_t bytes() const;
@@ -206,9 +209,14 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K);
 // W is fp32, or binary16 values when wf16 (the two-product form); one: plain
 // FP16 (A_hi.W_hi alone).  kshift (nullable): A's element (m, k) is
 // multiplied by 2^-kshift[k] before its split.
+// epoch: a number no earlier call in the process used (the split-K counters
+// tell this call's arrivals from stale contents by it).
 hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift, const void* W, bool wf16,
                               bool one, int64_t ldw, float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                              void* workspace, const DecodePlan& plan, uint32_t* status, hipStream_t s);
+                              void* workspace, const DecodePlan& plan, uint64_t epoch, uint32_t* status,
+                              hipStream_t s);
+// A fresh call epoch (48 bits, never 0; thread-safe).
+uint64_t next_epoch();
 
 int64_t attn_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D);
 // Causal self-attention of a prompt: q [B, T, Hq, D], k/v [B, T, Hkv, D] INT16
