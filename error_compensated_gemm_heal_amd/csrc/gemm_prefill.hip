@@ -86,9 +86,12 @@ constexpr int QKV_LD = 132;
 constexpr int QKV_TILE_FLOATS = 128 * QKV_LD;
 constexpr int QKV_SLOTS_OFF = 2 * QKV_TILE_FLOATS * 4;
 constexpr int QKV_LDS = QKV_SLOTS_OFF + 256 * 8;   // 137 KB
-constexpr int dyn_lds(bool ahi, bool bhi, bool qkv) {
+constexpr int lds_base(bool ahi, bool bhi, bool qkv) {
     return qkv && QKV_LDS > NSTAGE * stage_bytes(ahi, bhi) ? QKV_LDS : NSTAGE * stage_bytes(ahi, bhi);
 }
+// After the stages (or the INT16 epilogue's tiles): the tile's 256 A and 256
+// B row exponents (none in the BF16 mode)
+constexpr int dyn_lds(bool ahi, bool bhi, bool qkv, bool x3) { return lds_base(ahi, bhi, qkv) + (x3 ? 0 : 2048); }
 
 // HBM byte offset of virtual k tile kt in a three-way BF16 packed row: block
 // kt / 6 (192 bytes), plane (planes >> 4 (kt % 6)) & 15 of it (64 bytes)
@@ -142,6 +145,7 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     constexpr int A_REGION = BM * AROWB;
     constexpr int A_DMA = BM * AROWB / 1024 / 4;   // 1 KB DMA blocks per wave per tile (A)
     constexpr int B_DMA = BN * BROWB / 1024 / 4;   // 1 KB DMA blocks per wave per tile (B)
+    int* const exp_lds = reinterpret_cast<int*>(smem + lds_base(AHI, BHI, QKV));
 
     // ---- XCD-aware tile order (tm fastest, then tn, then the k half) -------
     const int nblk = tiles_m * tiles_n * (SPLIT ? 2 : 1);
@@ -153,6 +157,12 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
+    // the tile's row exponents, loaded first and parked in LDS for the epilogue
+    int ea_v = 0, eb_v = 0;
+    if constexpr (!X3) {
+        ea_v = ea[tm * BM + tid];
+        eb_v = eb[tn * BN + tid];
+    }
     // wave index as a scalar: DMA destinations and offsets must be wave-uniform
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
@@ -272,6 +282,10 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     } else {
         __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0)
     }
+    if constexpr (!X3) {
+        exp_lds[tid] = ea_v;
+        exp_lds[256 + tid] = eb_v;
+    }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     {
@@ -323,16 +337,18 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     const int row0 = tm * BM + wm * WM + (lane >> 5) * 4;
     const int col0 = tn * BN + wn * WN + (lane & 31);
     // undo the row normalization: output (row, col) times 2^-(ea[row] + eb[col]),
-    // exact barring fp32 underflow.  The exponent arrays cover the padded rows.
+    // exact barring fp32 underflow; the exponents come from LDS
     if constexpr (!X3) {
+        __syncthreads();   // the exponents' LDS writes are visible (also when the loop had one tile)
+        const int rl = wm * WM + (lane >> 5) * 4, cl = wn * WN + (lane & 31);
         int ebc[TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) ebc[j] = eb[col0 + j * 32];
+        for (int j = 0; j < TN; ++j) ebc[j] = exp_lds[256 + cl + j * 32];
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             int4 er[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) er[q] = *reinterpret_cast<const int4*>(ea + row0 + i * 32 + q * 8);
+            for (int q = 0; q < 4; ++q) er[q] = *reinterpret_cast<const int4*>(exp_lds + rl + i * 32 + q * 8);
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -479,24 +495,24 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
     if (!attr_set[dev]) {
         const std::pair<const void*, int> fns[16] = {
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3, false, false, false, false>), stage_bytes(false, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 3, false, false, false, false>), stage_bytes(false, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2, true, false, false, false>), stage_bytes(false, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 2, true, false, false, false>), stage_bytes(false, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, false, false, false, false>), stage_bytes(false, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, false, false, false, false>), stage_bytes(false, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, false, false, false>), stage_bytes(false, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, false, false, false>), stage_bytes(false, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, true, false, false>), stage_bytes(true, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, true, false, false>), stage_bytes(true, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3, false, false, true, false>), QKV_LDS},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2, true, false, true, false>), QKV_LDS},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, false, false, false, true>), stage_bytes(true, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, false, false, false, true>), stage_bytes(true, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, false, false, true>), stage_bytes(true, true)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, false, false, true>), stage_bytes(true, true)}};
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3, false, false, false, false>), dyn_lds(false, false, false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 3, false, false, false, false>), dyn_lds(false, false, false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2, true, false, false, false>), dyn_lds(false, true, false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 2, true, false, false, false>), dyn_lds(false, true, false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, false, false, false, false>), dyn_lds(false, false, false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, false, false, false, false>), dyn_lds(false, false, false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, false, false, false>), dyn_lds(false, true, false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, false, false, false>), dyn_lds(false, true, false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, true, false, false>), dyn_lds(true, true, false, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, true, false, false>), dyn_lds(true, true, false, true)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3, false, false, true, false>), dyn_lds(false, false, true, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2, true, false, true, false>), dyn_lds(false, true, true, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, false, false, false, true>), dyn_lds(true, false, false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, false, false, false, true>), dyn_lds(true, false, false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, false, false, true>), dyn_lds(true, true, false, false)},
+            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, false, false, true>), dyn_lds(true, true, false, false)}};
         for (const auto& f : fns) {
-            const int bytes = f.second == QKV_LDS ? QKV_LDS : NSTAGE * f.second;
+            const int bytes = f.second;
             hipError_t e = hipFuncSetAttribute(f.first, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
             if (e != hipSuccess) return e;
         }
@@ -517,20 +533,20 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
     const QkvDst none{};
 #define HEAL_PREFILL(SPLIT_, NP_, BHI_, X3_)                                                          \
     hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, NP_, BHI_, X3_, false, false>), grid, dim3(256),  \
-                       NSTAGE * stage_bytes(X3_, BHI_), s, a, b, ea, eb, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n, \
+                       dyn_lds(X3_, BHI_, false, X3_), s, a, b, ea, eb, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n, \
                        none)
 #define HEAL_PREFILL_AH(SPLIT_, BHI_)                                                                 \
     hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, 1, BHI_, false, false, true>), grid, dim3(256),   \
-                       NSTAGE * stage_bytes(true, BHI_), s, a, b, ea, eb, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n, \
+                       dyn_lds(true, BHI_, false, false), s, a, b, ea, eb, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n, \
                        none)
     if (qkv) {
         if (nprod == 3)
             hipLaunchKernelGGL((gemm_prefill_kernel<false, 3, false, false, true, false>), grid, dim3(256),
-                               dyn_lds(false, false, true), s, a, b, ea, eb, C, ldc, (int)M, (int)N, (int)Kp, tiles_m,
+                               dyn_lds(false, false, true, false), s, a, b, ea, eb, C, ldc, (int)M, (int)N, (int)Kp, tiles_m,
                                tiles_n, *qkv);
         else
             hipLaunchKernelGGL((gemm_prefill_kernel<false, 2, true, false, true, false>), grid, dim3(256),
-                               dyn_lds(false, true, true), s, a, b, ea, eb, C, ldc, (int)M, (int)N, (int)Kp, tiles_m,
+                               dyn_lds(false, true, true, false), s, a, b, ea, eb, C, ldc, (int)M, (int)N, (int)Kp, tiles_m,
                                tiles_n, *qkv);
         return hipGetLastError();
     }
