@@ -13,7 +13,7 @@ import torch
 
 __all__ = [
     "HealError", "lib", "heal_status_str", "heal_version", "heal_split_f32", "heal_gemm_f32c",
-    "heal_gemm_f32c_workspace", "heal_pack_w", "heal_pack_w_bytes", "heal_qkv_quant_i16",
+    "heal_gemm_f32c_workspace", "heal_gemm_f32c_noalloc", "heal_pack_w", "heal_pack_w_bytes", "heal_qkv_quant_i16",
     "heal_kv_dequant_i16", "heal_attn_decode_i16", "heal_attn_decode_workspace", "PackedOperand",
     "heal_scale_k", "heal_kshift_from_absmax",
     "PackedWeight", "HEAL_W_NK", "HEAL_W_KN", "HEAL_W_PACKED", "HEAL_A_PACKED", "HEAL_W_F16", "HEAL_ONE_PRODUCT", "HEAL_BF16X3",
@@ -40,6 +40,7 @@ SIGNATURES = {
     "heal_split_f32": ([_P, _I64, _P, _P, _P, _P], _INT),
     "heal_gemm_f32c": ([_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _U32, _P, _P, _SZ, _P, _P], _INT),
     "heal_gemm_f32c_workspace": ([_I64, _I64, _I64, _U32], _SZ),
+    "heal_gemm_f32c_noalloc": ([_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _U32, _P, _P, _P], _INT),
     "heal_pack_w": ([_P, _I64, _I64, _I64, _U32, _P, _P, _SZ, _P, _P], _INT),
     "heal_scale_k": ([_P, _I64, _I64, _I64, _U32, _P, _P, _I64, _P], _INT),
     "heal_kshift_from_absmax": ([_P, _I64, ctypes.c_float, _P], _INT),
@@ -257,6 +258,27 @@ def heal_gemm_f32c(A, W, w_layout: str = "nk", C=None, workspace=None, dev_statu
     _check("heal_gemm_f32c", lib().heal_gemm_f32c(aptr, lda, wptr, ldw, _ptr(C), ldc, M, N, K, flags, _ptr(ks),
                                                   _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                                   _ptr(dev_status), _stream()))
+    return C
+
+
+def heal_gemm_f32c_noalloc(A: torch.Tensor, W: torch.Tensor, C: torch.Tensor, dev_status=None, a_kshift=None):
+    """C = A . W^T on the decode path with the library's own scratch memory:
+    no allocation anywhere in the call (C is the caller's).  A fp32 [M, K]
+    with M <= 64, W fp32 or float16 [N, K]."""
+    _dev(A, "A", torch.float32)
+    _dev(W, "W")
+    _dev(C, "C", torch.float32)
+    M, K = A.shape
+    N, K2 = W.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError("shapes of A, W and C do not match")
+    flags = HEAL_W_NK | _weight_dtype_flag(W)
+    ks = _kshift(a_kshift, K, "a_kshift")
+    ldc = _rowmajor_ld(C, "C") if M > 0 and N > 0 else N
+    _check("heal_gemm_f32c_noalloc",
+           lib().heal_gemm_f32c_noalloc(_ptr(A), _rowmajor_ld(A, "A") if M > 0 else K, _ptr(W),
+                                        _rowmajor_ld(W, "W") if N > 0 else K, _ptr(C), ldc, M, N, K, flags,
+                                        _ptr(ks), _ptr(dev_status), _stream()))
     return C
 
 

@@ -11,7 +11,16 @@
 using namespace heal;
 
 namespace heal {
-// Call epochs for the decode GEMM's split-K counters: unique within the
+// Path choice for heal_gemm_f32c.  The decode kernel streams an fp32 [N,K]
+// weight directly; every other case packs the operands for the prefill kernel.
+// The decode kernel addresses its split activation (256 bytes per k) and
+// each 16-row slice of W with 32-bit byte offsets.
+bool decode_path(int64_t M, int64_t K, uint32_t flags) {
+    return M <= 64 && K < ((int64_t)1 << 23) && !(flags & (HEAL_W_PACKED | HEAL_A_PACKED | HEAL_BF16X3)) &&
+           (flags & HEAL_W_KN) == 0;
+}
+
+// Call epochs for the decode GEMM's split-K flags: unique within the
 // process; the start is taken from the clock so that a workspace that held
 // another process's counters is not mistaken for this one's.
 uint64_t next_epoch() {
@@ -34,14 +43,7 @@ bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t
 int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 heal_status hip_status(hipError_t e) { return e == hipSuccess ? HEAL_OK : HEAL_ERR_HIP; }
 
-// Path choice for heal_gemm_f32c.  The decode kernel streams an fp32 [N,K]
-// weight directly; every other case packs the operands for the prefill kernel.
-// The decode kernel addresses its split activation (256 bytes per k) and
-// each 16-row slice of W with 32-bit byte offsets.
-bool use_decode(int64_t M, int64_t K, uint32_t flags) {
-    return M <= 64 && K < ((int64_t)1 << 23) && !(flags & (HEAL_W_PACKED | HEAL_A_PACKED | HEAL_BF16X3)) &&
-           (flags & HEAL_W_KN) == 0;
-}
+bool use_decode(int64_t M, int64_t K, uint32_t flags) { return decode_path(M, K, flags); }
 // bytes of one packed operand in the form the flags select
 int64_t packed_bytes(int64_t R, int64_t K, uint32_t flags) {
     if (flags & HEAL_BF16X3) return pack_bytes_x3(R, K);

@@ -217,6 +217,8 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
                               hipStream_t s);
 // A fresh call epoch (48 bits, never 0; thread-safe).
 uint64_t next_epoch();
+// Whether heal_gemm_f32c runs this shape and these flags on the decode kernel.
+bool decode_path(int64_t M, int64_t K, uint32_t flags);
 
 int64_t attn_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D);
 // Causal self-attention of a prompt: q [B, T, Hq, D], k/v [B, T, Hkv, D] INT16

@@ -16,7 +16,9 @@
  * Conventions shared by every call
  *  - Pointers named as device pointers are device memory owned by the caller.
  *    The library never allocates, frees or synchronizes.  Scratch memory is
- *    the caller's `workspace`, sized by the matching *_workspace call.
+ *    the caller's `workspace`, sized by the matching *_workspace call, except
+ *    for heal_gemm_f32c_noalloc, whose scratch is a fixed device array of the
+ *    library (one per GPU, 16 MiB).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Each call enqueues its kernels on that stream and returns at once.
  *  - Matrices are row-major.  Leading dimensions (ld*) count elements.
@@ -183,6 +185,27 @@ heal_status heal_gemm_f32c(const float* A, int64_t lda, const void* W, int64_t l
 
 /* Workspace bytes heal_gemm_f32c needs for this shape and flags. */
 size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags);
+
+/* ------------------------------------------------------------------------
+ * heal_gemm_f32c_noalloc -- heal_gemm_f32c without a workspace argument, for
+ * callers that cannot allocate: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.
+ *  Same arguments, results and kernels as heal_gemm_f32c (bit for bit), on
+ *  the decode path only: M <= 64, W fp32 or binary16 (HEAL_W_F16) in the
+ *  [N, K] layout, not packed, not HEAL_BF16X3, K < 2^23 (else
+ *  HEAL_ERR_UNSUPPORTED).  Its scratch memory is a 16 MiB array of device
+ *  memory that the library owns, one per GPU, held until the process ends;
+ *  shapes whose heal_gemm_f32c_workspace exceeds 16 MiB get
+ *  HEAL_ERR_WORKSPACE (the Llama-3-8B-like decode layers need at most
+ *  12.1 MB at M = 64).  No call allocates or frees memory.  The array keeps
+ *  the last call's contents; nothing in it needs clearing.  Calls that
+ *  overlap on one GPU (other streams or threads) share the array and race:
+ *  serialize them.
+ * ------------------------------------------------------------------------ */
+heal_status heal_gemm_f32c_noalloc(const float* A, int64_t lda, const void* W, int64_t ldw,
+                                   float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                   uint32_t flags, const int8_t* a_kshift, uint32_t* dev_status,
+                                   void* stream);
 
 /* ------------------------------------------------------------------------
  * heal_pack_w -- split an operand once into the GEMM's packed dual-FP16 form.

@@ -96,6 +96,24 @@ def test_gemm_validation():
     assert _gemm(st=ctypes.c_void_p(0x10002)) == ALIGN
 
 
+def test_gemm_noalloc_validation():
+    """heal_gemm_f32c_noalloc: decode path only, and shapes whose scratch would
+    pass the library's 16 MiB array are rejected; both before any HIP call."""
+    f = heal.lib().heal_gemm_f32c_noalloc
+    args = lambda M=8, N=64, K=256, flags=0: (FAKE, K, FAKE, K, FAKE, N, M, N, K, flags, None, None, None)
+    assert f(*args(M=-1)) == SHAPE
+    assert f(*args(M=65)) == UNSUP                       # the prefill path allocates its packed operands
+    assert f(*args(flags=heal.HEAL_W_PACKED)) == UNSUP
+    assert f(*args(flags=heal.HEAL_W_KN)) == UNSUP
+    assert f(*args(flags=heal.HEAL_BF16X3)) == UNSUP
+    assert heal.heal_gemm_f32c_workspace(64, 256, 1 << 20, 0) > 16 << 20
+    assert f(*args(M=64, N=256, K=1 << 20)) == WS       # split blocks past 16 MiB
+    assert heal.heal_gemm_f32c_workspace(64, 4096, 14336, 0) <= 16 << 20   # the Llama-3-8B-like layers fit
+    assert heal.heal_gemm_f32c_workspace(64, 14336, 4096, 0) <= 16 << 20
+    assert heal.heal_gemm_f32c_workspace(64, 1024, 4096, 0) <= 16 << 20
+    assert f(*args(M=0)) == OK
+
+
 def test_gemm_workspace_sizes():
     ws = heal.heal_gemm_f32c_workspace
     assert ws(0, 64, 64, 0) == 0 and ws(8, 64, -1, 0) == 0

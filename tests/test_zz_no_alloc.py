@@ -1,0 +1,51 @@
+"""heal_gemm_f32c_noalloc: the decode-path GEMM with the library's own scratch
+memory, called through the C ABI, against heal_gemm_f32c with a workspace.
+
+The kernels are the same, so the outputs must be equal bit for bit: two calls
+in a row, the second on a smaller input (the scratch keeps the first call's
+contents), for fp32 and binary16 weights and a shape with split planes.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import error_compensated_gemm_heal_amd as heal
+import heal_workloads as WL
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _noalloc(A, W, f16=False):
+    M, K = A.shape
+    N = W.shape[0]
+    C = torch.full((M, N), float("nan"), device=DEV)
+    flags = heal.HEAL_W_F16 if f16 else 0
+    st = heal.lib().heal_gemm_f32c_noalloc(ctypes.c_void_p(A.data_ptr()), K, ctypes.c_void_p(W.data_ptr()), K,
+                                           ctypes.c_void_p(C.data_ptr()), N, M, N, K, flags, None, None,
+                                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, heal.heal_status_str(st)
+    return C
+
+
+@pytest.mark.parametrize("f16", [False, True])
+def test_noalloc_equals_workspace_entry_point_two_calls(f16):
+    for (M, K, N, seed) in [(64, 14336, 4096, 11), (40, 4096, 1024, 12), (5, 1000, 300, 13)]:
+        print(f"noalloc M={M} K={K} N={N} f16={f16}", flush=True)
+        A, W = WL.decode_gemm(M, K, N, seed=seed)
+        Ad = torch.from_numpy(A).to(DEV)
+        Wd = torch.from_numpy(W.astype(np.float16) if f16 else W).to(DEV)
+        ref = heal.heal_gemm_f32c(Ad, Wd).cpu().numpy()
+        got = _noalloc(Ad, Wd, f16).cpu().numpy()
+        torch.cuda.synchronize()
+        assert np.array_equal(ref, got)
+
+
+def test_noalloc_binding_and_limits():
+    A, W = WL.decode_gemm(8, 512, 256, seed=14)
+    Ad, Wd = torch.from_numpy(A).to(DEV), torch.from_numpy(W).to(DEV)
+    C = torch.empty((8, 256), device=DEV)
+    heal.heal_gemm_f32c_noalloc(Ad, Wd, C)
+    assert np.array_equal(C.cpu().numpy(), heal.heal_gemm_f32c(Ad, Wd).cpu().numpy())
