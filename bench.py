@@ -291,36 +291,142 @@ def make_rows(W):
     return rows
 
 
-def cpu_baseline(seconds):
-    """The oracle's FP64 GEMM, as it stands, on a row sample of the two prefill shapes:
-    rows of the first shape, then of the second, until about `seconds` of CPU work."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _gemm_rows_rate(fn, seconds, nth):
+    """Rows of the two prefill shapes through an oracle GEMM (row-parallel), until
+    about `seconds` of CPU work: (flops per second, sample text)."""
     import numpy as np
     import heal_workloads as WL
-    import oracle
-    nth = oracle.num_threads()
     flops, total, parts = 0.0, 0.0, []
     for K, N in WL.PREFILL_KN:
         left = seconds - total
-        if left <= 0.5:
+        if left <= 0.25 * seconds / len(WL.PREFILL_KN):
             break
         A, Wt = WL.prefill_gemm(WL.PREFILL_M, K, N, seed=3000)
         probe = np.arange(nth, dtype=np.int64)
         t0 = time.perf_counter()
-        oracle.gemm_f64_rows(A, Wt, probe)
+        fn(A, Wt, probe)
         dt = time.perf_counter() - t0
-        # dt covers nth rows: scale the sample to the time left (whole multiples of nth)
-        nrows = int(max(nth, min(WL.PREFILL_M, round(left / max(dt, 1e-6)) * nth)))
+        # dt covers nth rows: scale the sample to its share of the time left (whole multiples of nth)
+        share = left if K == WL.PREFILL_KN[-1][0] else left / 2
+        nrows = int(max(nth, min(WL.PREFILL_M, round(share / max(dt, 1e-6)) * nth)))
         rows = np.arange(nrows, dtype=np.int64)
         t0 = time.perf_counter()
-        oracle.gemm_f64_rows(A, Wt, rows)
+        fn(A, Wt, rows)
         dt = time.perf_counter() - t0
         flops += 2.0 * nrows * N * K
         total += dt
-        parts.append(f"{nrows} of the {WL.PREFILL_M} rows of K={K}, N={N}")
+        parts.append(f"{nrows} of {WL.PREFILL_M} rows of K={K}, N={N}")
         del A, Wt
-    return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": nth, "kind": "oracle",
-            "sample": "FP64-accumulated GEMM (the oracle) on the prefill shapes: " + "; ".join(parts) +
-                      f"; {total:.1f} s"}
+    return flops / total, "; ".join(parts) + f" ({total:.1f} s)"
+
+
+def _quant_rate(seconds):
+    """The oracle's INT16 quant and dequant on a token slice of the Q/K/V layer
+    (48 heads of 128 per token): (quant B/s, dequant B/s, sample text); bytes
+    counted as the GPU rows count them (4 in + 2 out per element + 4 per row)."""
+    import heal_workloads as WL
+    import oracle
+    tokens = 4096
+    Q, K_, V = WL.qkv(tokens, 32, 8, 128, seed=4000)
+    import numpy as np
+    X = np.concatenate([Q, K_, V], axis=1)
+    del Q, K_, V
+    n, rows = X.size, X.size // 128
+    nbytes = n * 6 + rows * 4
+    out = []
+    for fn in (lambda: oracle.quant_i16(X), None):
+        if fn is None:
+            codes, scales = oracle.quant_i16(X)
+            fn = (lambda c=codes, s_=scales: oracle.dequant_f32(c, s_))
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= seconds / 2:
+                break
+        out.append(nbytes * reps / dt)
+    return out[0], out[1], f"{tokens} tokens x 48 heads x 128 ({n / 1e6:.1f} M elements)"
+
+
+def cpu_baseline(seconds):
+    """The oracle, as it stands, on bounded samples of the benchmark's workloads, on
+    all host threads and on one: `value` is its FP64-accumulated GEMM on row samples
+    of the two prefill shapes (the metric's first half, the GPU `value`'s unit);
+    `parts` adds the naive FP32 GEMM and the INT16 quant and dequant (the metric's
+    second half, GB/s), and the one-thread rates."""
+    import oracle
+    nth = oracle.num_threads()
+    share = seconds / 6
+    parts = {}
+    f64, s64 = _gemm_rows_rate(oracle.gemm_f64_rows, 2 * share, nth)
+    f32, s32 = _gemm_rows_rate(oracle.gemm_f32_naive_rows, share, nth)
+    q, dq, sq = _quant_rate(share)
+    parts["gemm_f64_TFLOPs"] = f64 / 1e12
+    parts["gemm_f32_naive_TFLOPs"] = f32 / 1e12
+    parts["quant_GBps"] = q / 1e9
+    parts["dequant_GBps"] = dq / 1e9
+    oracle.set_num_threads(1)
+    try:
+        f64_1, s64_1 = _gemm_rows_rate(oracle.gemm_f64_rows, share, 1)
+        q1, dq1, _ = _quant_rate(share)
+    finally:
+        oracle.set_num_threads(nth)
+    parts["gemm_f64_TFLOPs_1thread"] = f64_1 / 1e12
+    parts["quant_GBps_1thread"] = q1 / 1e9
+    parts["dequant_GBps_1thread"] = dq1 / 1e9
+    return {"value": f64 / 1e12, "unit": "TFLOP/s", "cores": nth, "kind": "oracle",
+            "cpu_model": _cpu_model(), "parts": parts,
+            "sample": f"the oracle on {nth} threads and on 1: FP64 GEMM on {s64}; naive FP32 GEMM on {s32}; "
+                      f"quant/dequant of {sq}; one thread: FP64 GEMM on {s64_1}"}
+
+
+def calibrate(torch, heal):
+    """Measured ceilings: the register-only 16-bit MFMA rate in the prefill GEMM's
+    launch shape (one workgroup of 4 waves per CU), the HBM read rate of a
+    streaming kernel (2 GiB, best of five grid sizes), and a device copy (1 GiB
+    each way), all timed with HIP events on the current stream (best of 5 after
+    a warm-up)."""
+    def best(fn, reps=5):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts)
+    out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda:0")
+    iters = 20000
+    _, mflop = heal.heal_calib_mfma_f16(iters, 256, out)
+    t_mfma = best(lambda: heal.heal_calib_mfma_f16(iters, 256, out))
+    buf = torch.ones(1 << 29, dtype=torch.float32, device="cuda:0")      # 2 GiB
+    out = torch.empty(16384 * 256, dtype=torch.float32, device="cuda:0")
+    reads = {wg: best(lambda wg=wg: heal.heal_calib_read(buf, wg, out)) for wg in (1024, 2048, 4096, 8192, 16384)}
+    wg_read = min(reads, key=reads.get)
+    t_read = reads[wg_read]
+    src = buf[: 1 << 28]
+    dst = torch.empty_like(src)
+    t_copy = best(lambda: dst.copy_(src))
+    res = {"mfma_f16_TFLOPs": mflop / t_mfma / 1e12, "hbm_read_GBps": buf.numel() * 4 / t_read / 1e9,
+           "copy_GBps": 2 * src.numel() * 4 / t_copy / 1e9,
+           "note": "register-only v_mfma_f32_32x32x16_f16 loop, 256 workgroups x 4 waves x 16 accumulators; "
+                   f"2 GiB streaming read (8 non-temporal 16-byte loads in flight per thread; the best grid, "
+                   f"{wg_read} workgroups of 256); 1 GiB device copy (read + write bytes)"}
+    del buf, dst
+    return res
 
 
 def main():
@@ -332,9 +438,11 @@ def main():
                                       "qkv_proj,quant,dequant,attn_prefill,attn",
                     help="comma-separated subset of rows to run (profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=24.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a device copy of this many MiB (counter calibration) and exit")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only measure the MFMA and HBM ceilings (calibration kernels) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -359,6 +467,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 3}))
+        return
+
+    if args.calibrate:
+        print(json.dumps(calibrate(torch, heal)))
         return
 
     sel = set(args.rows.split(","))
@@ -446,6 +558,15 @@ def main():
         res["value"] = None
     if "quant" in per_row:
         res["quant_GBps"] = per_row["quant"]["GBps"]
+    # measured ceilings, after the timed steps: the fractions beside the spec ones
+    cal = calibrate(torch, heal)
+    res["calibration"] = cal
+    if "roofline" in res:
+        res["roofline"]["peak_measured"] = cal["mfma_f16_TFLOPs"]
+        res["roofline"]["frac_measured"] = res["roofline"]["achieved"] / cal["mfma_f16_TFLOPs"]
+    for name, r in per_row.items():
+        if "GBps" in r:
+            r["hbm_frac_measured"] = r["GBps"] / cal["hbm_read_GBps"]
     res["rows"] = per_row
 
     if not args.no_cpu_baseline:

@@ -18,7 +18,7 @@ __all__ = [
     "heal_scale_k", "heal_kshift_from_absmax",
     "PackedWeight", "HEAL_W_NK", "HEAL_W_KN", "HEAL_W_PACKED", "HEAL_A_PACKED", "HEAL_W_F16", "HEAL_ONE_PRODUCT", "HEAL_BF16X3",
     "HEAL_FLAG_F16_RANGE", "HEAL_FLAG_SLOT_RANGE", "heal_qkv_proj_quant_i16", "heal_qkv_proj_quant_workspace",
-    "heal_attn_prefill_i16",
+    "heal_attn_prefill_i16", "heal_calib_mfma_f16", "heal_calib_read",
     "HEAL_DQ_F32", "HEAL_DQ_F16X2",
     "LIB_PATH",
 ]
@@ -53,6 +53,8 @@ SIGNATURES = {
                                  _P, _P, _P, _P, _P, _SZ, _P, _P], _INT),
     "heal_qkv_proj_quant_workspace": ([_I64, _I64, _I64, _I64, _I64, _U32], _SZ),
     "heal_attn_prefill_i16": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P], _INT),
+    "heal_calib_mfma_f16": ([_I64, _I64, _P, _P], _INT),
+    "heal_calib_read": ([_P, _I64, _I64, _P, _P], _INT),
 }
 
 _LIB = None
@@ -280,6 +282,25 @@ def heal_gemm_f32c_noalloc(A: torch.Tensor, W: torch.Tensor, C: torch.Tensor, de
                                         _rowmajor_ld(W, "W") if N > 0 else K, _ptr(C), ldc, M, N, K, flags,
                                         _ptr(ks), _ptr(dev_status), _stream()))
     return C
+
+
+def heal_calib_mfma_f16(iters: int, workgroups: int = 256, out=None):
+    """Register-only 16-bit MFMA loop (roofline calibration); returns out and
+    the flops it performs."""
+    if out is None:
+        out = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda")
+    _check("heal_calib_mfma_f16", lib().heal_calib_mfma_f16(iters, workgroups, _ptr(out), _stream()))
+    return out, workgroups * 4 * iters * 16 * 32768
+
+
+def heal_calib_read(buf: torch.Tensor, workgroups: int = 2048, out=None):
+    """Streaming read of a device buffer (roofline calibration)."""
+    _dev(buf, "buf")
+    if out is None:
+        out = torch.empty(workgroups * 256, dtype=torch.float32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check("heal_calib_read", lib().heal_calib_read(_ptr(buf), nbytes, workgroups, _ptr(out), _stream()))
+    return out
 
 
 def heal_scale_k(X: torch.Tensor, kshift: torch.Tensor, w_layout: str = "nk", out=None):

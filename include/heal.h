@@ -393,6 +393,23 @@ heal_status heal_attn_prefill_i16(const int16_t* q, const float* q_scale, const 
                                   const float* k_scale, const int16_t* v, const float* v_scale, float* out,
                                   int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Roofline calibration (measurement only; not part of the method).  The
+ * denominators of the library's roofline figures, measured on the device.
+ *
+ * heal_calib_mfma_f16 -- `workgroups` workgroups of 4 waves (one per compute
+ *  unit as the prefill GEMM runs), each wave issuing `iters` rounds of 16
+ *  independent v_mfma_f32_32x32x16_f16 on registers (no LDS, no memory):
+ *  workgroups * 4 * iters * 16 * 32768 flops.  out: device fp32
+ *  [workgroups * 256], 4-byte aligned (a checksum that keeps the work).
+ * heal_calib_read -- a streaming read of `bytes` bytes at buf (16-byte
+ *  aligned, bytes % 16 == 0) by `workgroups` workgroups of 256 threads.
+ *  out: device fp32 [workgroups * 256], 4-byte aligned.
+ * Limits: workgroups <= 2^20.
+ * ------------------------------------------------------------------------ */
+heal_status heal_calib_mfma_f16(int64_t iters, int64_t workgroups, float* out, void* stream);
+heal_status heal_calib_read(const void* buf, int64_t bytes, int64_t workgroups, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -50,6 +50,8 @@ def lib():
             fn.restype = None
         L.oracle_abi_version.restype = ctypes.c_int
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_num_threads.restype = None
         _LIB = L
     return _LIB
 
@@ -57,6 +59,11 @@ def lib():
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Set the OpenMP threads of the oracle's parallel loops (for CPU timings)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def _ptr(a: np.ndarray):

@@ -523,3 +523,6 @@ ORACLE_API int oracle_abi_version(void) { return 1; }
 
 /* Threads the OpenMP loops above run on (for reporting CPU timings). */
 ORACLE_API int oracle_num_threads(void) { return omp_get_max_threads(); }
+
+/* Set the OpenMP thread count of the loops above (CPU timings on 1 core). */
+ORACLE_API void oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }

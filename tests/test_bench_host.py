@@ -22,9 +22,13 @@ def test_bench_refuses_more_than_one_gpu(gpus):
 def test_bench_cpu_baseline_reports_the_oracle_sample():
     sys.path.insert(0, ROOT)
     import bench
-    res = bench.cpu_baseline(0.6)
+    res = bench.cpu_baseline(1.2)
     json.dumps(res)
-    assert set(res) == {"value", "unit", "cores", "kind", "sample"}
+    assert {"value", "unit", "cores", "kind", "sample"} <= set(res)
     assert res["kind"] == "oracle" and res["unit"] == "TFLOP/s"
-    assert res["value"] > 0 and res["cores"] >= 1
+    assert res["value"] > 0 and res["cores"] >= 1 and res["cpu_model"]
     assert "K=4096, N=14336" in res["sample"]
+    # both halves of the metric, on all threads and on one
+    for key in ("gemm_f64_TFLOPs", "gemm_f32_naive_TFLOPs", "quant_GBps", "dequant_GBps",
+                "gemm_f64_TFLOPs_1thread", "quant_GBps_1thread", "dequant_GBps_1thread"):
+        assert res["parts"][key] > 0, key

@@ -153,3 +153,14 @@ def test_quant_dequant_qwen_layer_sampled_full_size():
     # property over every row: the absmax element of each row carries code +-32767
     amax = torch.max(torch.abs(codes.reshape(-1, 128).to(torch.int32)), dim=1).values
     assert bool(torch.all(amax == 32767) | torch.all(scales.reshape(-1) == 0))
+
+
+def test_calibration_kernels_run():
+    """The roofline calibration kernels (measurement only) run and return finite values."""
+    out, flops = heal.heal_calib_mfma_f16(10, 8)
+    assert flops == 8 * 4 * 10 * 16 * 32768
+    assert torch.isfinite(out[: 8 * 256]).all().item()
+    buf = torch.arange(1 << 20, dtype=torch.float32, device="cuda:0")
+    r = heal.heal_calib_read(buf, 64)
+    torch.cuda.synchronize()
+    assert torch.isfinite(r).all().item()
