@@ -313,18 +313,65 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
         }
         {   // phase 2 (branch-free so the loads interleave with the MFMAs): near
             // the end the tile indices clamp to the last tile, whose re-fetch
-            // writes bytes identical to the ones already in LDS
-            HEAL_DMA_TILE(kt_begin + min(t + 2, nkt - 1), t & 1);
+            // writes bytes identical to the ones already in LDS.  Issued in 16
+            // slots, each NP MFMAs, its share of the copies and of the next
+            // fragment reads, in this order (the scheduler may not move work
+            // across slots)
+            const int kt2 = kt_begin + min(t + 2, nkt - 1);
+            unsigned char* const st2 = smem + (t & 1) * STAGE;
+            const uint32_t koff_a2 = X3 ? x3_koff(kt2, X3_PLANES_A) : (uint32_t)kt2 * (AH ? 64u : 128u);
+            const uint32_t koff_b2 = X3 ? x3_koff(kt2, X3_PLANES_B) : (uint32_t)kt2 * (BROWB == ROWB ? 128u : 64u);
             const unsigned char* base = smem + (min(t + 1, nkt - 1) & 1) * STAGE;
-            HEAL_FRAGS(ah0, al0, bh0, bl0, 0);
-            HEAL_MFMAS(ah1, al1, bh1, bl1);
+            constexpr int NM = 16 * NP, ND = A_DMA + B_DMA;
+            constexpr int NR = TM + (NP >= 2 ? TM : 0) + TN + (NP == 3 ? TN : 0);
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, NP, 0);            // MFMAs
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // one LDS read
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);             // one DMA load
+#pragma unroll
+                for (int m = q * NM / 16; m < (q + 1) * NM / 16; ++m) {   // m = 16 p + 4 i + j
+                    const int p = m >> 4, i = (m >> 2) & 3, j = m & 3;
+                    if (p == 0) mfma32<X3>(ah1[i], bh1[j], acc[i][j]);
+                    else if (NP == 3 && p == 1) mfma32<false>(ah1[i], bl1[j], acc[i][j]);
+                    else mfma32<false>(al1[i], bh1[j], acc[i][j]);
+                }
+#pragma unroll
+                for (int d = q * ND / 16; d < (q + 1) * ND / 16; ++d) {
+                    if (d < A_DMA) {
+                        const int b_ = wave + 4 * d;
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_ptr)(st2 + b_ * 1024), 16, dma_voff_a,
+                                                                 (uint32_t)(A_ROWS_PER_DMA * b_) * rowbytes + koff_a2, 0, 0);
+                    } else {
+                        const int b_ = wave + 4 * (d - A_DMA);
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, (lds_ptr)(st2 + A_REGION + b_ * 1024), 16,
+                                                                 dma_voff_b,
+                                                                 (uint32_t)(B_ROWS_PER_DMA * b_) * browbytes + koff_b2,
+                                                                 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int r0 = q * NR / 16; r0 < (q + 1) * NR / 16; ++r0) {
+                    int r = r0;
+                    if (r < TM) {
+                        ah0[r] = *reinterpret_cast<const half8*>(base + a_row + r * 32 * AROWB + slot_off_a[0]);
+                        continue;
+                    }
+                    r -= TM;
+                    if constexpr (NP >= 2) {
+                        if (r < TM) {
+                            al0[r] = *reinterpret_cast<const half8*>(base + a_row + r * 32 * ROWB + slot_off[0][1]);
+                            continue;
+                        }
+                        r -= TM;
+                    }
+                    if (r < TN) {
+                        bh0[r] = *reinterpret_cast<const half8*>(base + b_row + r * 32 * BROWB + slot_off_b[0]);
+                        continue;
+                    }
+                    r -= TN;
+                    if constexpr (NP == 3)
+                        bl0[r] = *reinterpret_cast<const half8*>(base + b_row + r * 32 * ROWB + slot_off[0][1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
     }
     // no LDS write of this block may land after it ends
