@@ -252,23 +252,35 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
                 bl_[j] = *reinterpret_cast<const half8*>(base + b_row + j * 32 * ROWB + slot_off[ks_][1]); \
         }                                                                                                \
     } while (0)
-    // the products of one k16 step (residuals at their own scale: no
-    // scaling); each product sweeps all 16 output tiles before the next, so
-    // an accumulator is re-read 16 MFMAs later
-#define HEAL_MFMAS(ah_, al_, bh_, bl_)                                                                   \
-    do {                                                                                                 \
-        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                   \
-            _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32<X3>(ah_[i], bh_[j], acc[i][j]);        \
-        if constexpr (NP == 3) {                                                                         \
-            _Pragma("unroll") for (int i = 0; i < TM; ++i)                                               \
-                _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32<false>(ah_[i], bl_[j], acc[i][j]); \
-        }                                                                                                \
+    // The k16 step's work is issued in 16 slots separated by scheduling
+    // barriers (the scheduler does not keep an interleave of MFMAs, copies and
+    // LDS reads by itself once nothing but loads feeds the MFMAs): slot q runs
+    // NP MFMAs of the product-major sequence m = 16 p + 4 i + j (each product
+    // sweeps the 16 output tiles, so an accumulator is re-read 16 MFMAs later)
+    // and its share of the next fragment reads (and, in the second half of a
+    // tile, of the next tile's copies).
+    constexpr int NM_ = 16 * NP;
+    constexpr int NR_ = TM + (NP >= 2 ? TM : 0) + TN + (NP == 3 ? TN : 0);
+#define HEAL_SLOT_MFMAS(q_, ah_, al_, bh_, bl_)                                                           \
+    _Pragma("unroll") for (int m = (q_) * NM_ / 16; m < ((q_) + 1) * NM_ / 16; ++m) {                    \
+        const int p = m >> 4, i = (m >> 2) & 3, j = m & 3;                                               \
+        if (p == 0) mfma32<X3>(ah_[i], bh_[j], acc[i][j]);                                              \
+        else if (NP == 3 && p == 1) mfma32<false>(ah_[i], bl_[j], acc[i][j]);                           \
+        else mfma32<false>(al_[i], bh_[j], acc[i][j]);                                                  \
+    }
+#define HEAL_SLOT_READS(q_, base_, ks_, ah_, al_, bh_, bl_)                                               \
+    _Pragma("unroll") for (int r0 = (q_) * NR_ / 16; r0 < ((q_) + 1) * NR_ / 16; ++r0) {                 \
+        int r = r0;                                                                                      \
+        if (r < TM) { ah_[r] = *reinterpret_cast<const half8*>(base_ + a_row + r * 32 * AROWB + slot_off_a[ks_]); continue; } \
+        r -= TM;                                                                                         \
         if constexpr (NP >= 2) {                                                                         \
-            _Pragma("unroll") for (int i = 0; i < TM; ++i)                                               \
-                _Pragma("unroll") for (int j = 0; j < TN; ++j) mfma32<false>(al_[i], bh_[j], acc[i][j]); \
+            if (r < TM) { al_[r] = *reinterpret_cast<const half8*>(base_ + a_row + r * 32 * ROWB + slot_off[ks_][1]); continue; } \
+            r -= TM;                                                                                     \
         }                                                                                                \
-    } while (0)
-
+        if (r < TN) { bh_[r] = *reinterpret_cast<const half8*>(base_ + b_row + r * 32 * BROWB + slot_off_b[ks_]); continue; } \
+        r -= TN;                                                                                         \
+        if constexpr (NP == 3) bl_[r] = *reinterpret_cast<const half8*>(base_ + b_row + r * 32 * ROWB + slot_off[ks_][1]); \
+    }
     // Pipeline, one barrier per k tile placed mid-tile:
     //   phase 1 of tile t: MFMAs of k16 step 0 while step 1's fragments load;
     //   sync: this wave's reads of stage t done, tile t+1's DMA landed, barrier;
@@ -297,14 +309,12 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     for (int t = 0; t < nkt; ++t) {
         {   // phase 1
             const unsigned char* base = smem + (t & 1) * STAGE;
-            HEAL_FRAGS(ah1, al1, bh1, bl1, 1);
-            HEAL_MFMAS(ah0, al0, bh0, bl0);
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, NP, 0);            // MFMAs
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // one LDS read
+                HEAL_SLOT_MFMAS(q, ah0, al0, bh0, bl0)
+                HEAL_SLOT_READS(q, base, 1, ah1, al1, bh1, bl1)
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
         if (t + 1 < nkt) {   // sync (uniform across the block)
             __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
@@ -313,26 +323,17 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
         }
         {   // phase 2 (branch-free so the loads interleave with the MFMAs): near
             // the end the tile indices clamp to the last tile, whose re-fetch
-            // writes bytes identical to the ones already in LDS.  Issued in 16
-            // slots, each NP MFMAs, its share of the copies and of the next
-            // fragment reads, in this order (the scheduler may not move work
-            // across slots)
+            // writes bytes identical to the ones already in LDS.  Slots: MFMAs,
+            // copies, next fragment reads
             const int kt2 = kt_begin + min(t + 2, nkt - 1);
             unsigned char* const st2 = smem + (t & 1) * STAGE;
             const uint32_t koff_a2 = X3 ? x3_koff(kt2, X3_PLANES_A) : (uint32_t)kt2 * (AH ? 64u : 128u);
             const uint32_t koff_b2 = X3 ? x3_koff(kt2, X3_PLANES_B) : (uint32_t)kt2 * (BROWB == ROWB ? 128u : 64u);
             const unsigned char* base = smem + (min(t + 1, nkt - 1) & 1) * STAGE;
-            constexpr int NM = 16 * NP, ND = A_DMA + B_DMA;
-            constexpr int NR = TM + (NP >= 2 ? TM : 0) + TN + (NP == 3 ? TN : 0);
+            constexpr int ND = A_DMA + B_DMA;
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-#pragma unroll
-                for (int m = q * NM / 16; m < (q + 1) * NM / 16; ++m) {   // m = 16 p + 4 i + j
-                    const int p = m >> 4, i = (m >> 2) & 3, j = m & 3;
-                    if (p == 0) mfma32<X3>(ah1[i], bh1[j], acc[i][j]);
-                    else if (NP == 3 && p == 1) mfma32<false>(ah1[i], bl1[j], acc[i][j]);
-                    else mfma32<false>(al1[i], bh1[j], acc[i][j]);
-                }
+                HEAL_SLOT_MFMAS(q, ah1, al1, bh1, bl1)
 #pragma unroll
                 for (int d = q * ND / 16; d < (q + 1) * ND / 16; ++d) {
                     if (d < A_DMA) {
@@ -347,29 +348,7 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
                                                                  0, 0);
                     }
                 }
-#pragma unroll
-                for (int r0 = q * NR / 16; r0 < (q + 1) * NR / 16; ++r0) {
-                    int r = r0;
-                    if (r < TM) {
-                        ah0[r] = *reinterpret_cast<const half8*>(base + a_row + r * 32 * AROWB + slot_off_a[0]);
-                        continue;
-                    }
-                    r -= TM;
-                    if constexpr (NP >= 2) {
-                        if (r < TM) {
-                            al0[r] = *reinterpret_cast<const half8*>(base + a_row + r * 32 * ROWB + slot_off[0][1]);
-                            continue;
-                        }
-                        r -= TM;
-                    }
-                    if (r < TN) {
-                        bh0[r] = *reinterpret_cast<const half8*>(base + b_row + r * 32 * BROWB + slot_off_b[0]);
-                        continue;
-                    }
-                    r -= TN;
-                    if constexpr (NP == 3)
-                        bl0[r] = *reinterpret_cast<const half8*>(base + b_row + r * 32 * ROWB + slot_off[0][1]);
-                }
+                HEAL_SLOT_READS(q, base, 0, ah0, al0, bh0, bl0)
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -377,7 +356,8 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     // no LDS write of this block may land after it ends
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 #undef HEAL_FRAGS
-#undef HEAL_MFMAS
+#undef HEAL_SLOT_MFMAS
+#undef HEAL_SLOT_READS
 #undef HEAL_DMA_TILE
 
     // ---- epilogue: bounds-checked store (or atomic add of one k half) -------
