@@ -263,24 +263,30 @@ def heal_gemm_f32c(A, W, w_layout: str = "nk", C=None, workspace=None, dev_statu
     return C
 
 
-def heal_gemm_f32c_noalloc(A: torch.Tensor, W: torch.Tensor, C: torch.Tensor, dev_status=None, a_kshift=None):
+def heal_gemm_f32c_noalloc(A: torch.Tensor, W, C: torch.Tensor, dev_status=None, a_kshift=None):
     """C = A . W^T on the decode path with the library's own scratch memory:
     no allocation anywhere in the call (C is the caller's).  A fp32 [M, K]
-    with M <= 64, W fp32 or float16 [N, K]."""
+    with M <= 64, W fp32 or float16 [N, K], or a PackedOperand of it."""
     _dev(A, "A", torch.float32)
-    _dev(W, "W")
     _dev(C, "C", torch.float32)
     M, K = A.shape
-    N, K2 = W.shape
+    if isinstance(W, PackedOperand):
+        if W.bf16x3:
+            raise ValueError("a weight packed with bf16x3 takes the prefill path")
+        N, K2, wptr, ldw = W.rows, W.K, _ptr(W.buf), 0
+        flags = HEAL_W_PACKED | (HEAL_W_F16 if W.f16 else 0)
+    else:
+        _dev(W, "W")
+        N, K2 = W.shape
+        wptr, ldw = _ptr(W), _rowmajor_ld(W, "W") if N > 0 else K
+        flags = HEAL_W_NK | _weight_dtype_flag(W)
     if K2 != K or tuple(C.shape) != (M, N):
         raise ValueError("shapes of A, W and C do not match")
-    flags = HEAL_W_NK | _weight_dtype_flag(W)
     ks = _kshift(a_kshift, K, "a_kshift")
     ldc = _rowmajor_ld(C, "C") if M > 0 and N > 0 else N
     _check("heal_gemm_f32c_noalloc",
-           lib().heal_gemm_f32c_noalloc(_ptr(A), _rowmajor_ld(A, "A") if M > 0 else K, _ptr(W),
-                                        _rowmajor_ld(W, "W") if N > 0 else K, _ptr(C), ldc, M, N, K, flags,
-                                        _ptr(ks), _ptr(dev_status), _stream()))
+           lib().heal_gemm_f32c_noalloc(_ptr(A), _rowmajor_ld(A, "A") if M > 0 else K, wptr, ldw, _ptr(C), ldc,
+                                        M, N, K, flags, _ptr(ks), _ptr(dev_status), _stream()))
     return C
 
 

@@ -16,8 +16,9 @@ namespace heal {
 // The decode kernel addresses its split activation (256 bytes per k) and
 // each 16-row slice of W with 32-bit byte offsets.
 bool decode_path(int64_t M, int64_t K, uint32_t flags) {
-    return M <= 64 && K < ((int64_t)1 << 23) && !(flags & (HEAL_W_PACKED | HEAL_A_PACKED | HEAL_BF16X3)) &&
-           (flags & HEAL_W_KN) == 0;
+    // a packed weight has no layout flag: its rows are [N, K]
+    return M <= 64 && K < ((int64_t)1 << 23) && !(flags & (HEAL_A_PACKED | HEAL_BF16X3)) &&
+           ((flags & HEAL_W_PACKED) || (flags & HEAL_W_KN) == 0);
 }
 
 // Call epochs for the decode GEMM's split-K flags: unique within the
@@ -183,10 +184,10 @@ heal_status gemm_impl(const float* A, int64_t lda, const void* W, int64_t ldw, f
     }
 
     if (use_decode(M, K, flags)) {
-        if (ldw >= kMaxDecodeLdw || lda >= kMaxDecodeLda) return HEAL_ERR_UNSUPPORTED;
+        if ((!packed && ldw >= kMaxDecodeLdw) || lda >= kMaxDecodeLda) return HEAL_ERR_UNSUPPORTED;
         const DecodePlan p = decode_plan(M, N, K);
         unsigned char* ws = static_cast<unsigned char*>(workspace);
-        return hip_status(launch_gemm_decode(A, lda, a_kshift, W, wf16, one, ldw, C, ldc, M, N, K, ws, p,
+        return hip_status(launch_gemm_decode(A, lda, a_kshift, W, wf16, packed, one, ldw, C, ldc, M, N, K, ws, p,
                                              next_epoch(), dev_status, s));
     }
     unsigned char* ws = static_cast<unsigned char*>(workspace);

@@ -97,11 +97,11 @@ constexpr int img_bytes() { return block_bytes<MT>() + 256; }
 // block's exponent e; the lane writes its 4 values, x 2^(e - kshift[k]), split
 // as hi = fp16, lo = fp16((x - hi) 2^10), into block b's image: plane p
 // (0 = hi, 1 = lo), step s, tile t, lane 16 g + r holds, as 8 fp16, row
-// 16 t + r at k = 128 b + 32 s + {4g .. 4g+3, 16+4g .. 16+4g+3}; then e at
-// byte block_bytes + 4 m.  Rows >= M and k >= K are zero (exponent 0).  One
+// 16 t + r at k = 128 b + 32 s + {4g .. 4g+3, 16+4g .. 16+4g+3} (K8, for a
+// packed W: k = 128 b + 32 s + 8g .. 8g+7); then e at byte block_bytes + 4 m.  Rows >= M and k >= K are zero (exponent 0).  One
 // load per thread: the kernel costs about one memory latency.
 constexpr int PREP_T = 512;
-template <int MT, bool AVEC>
+template <int MT, bool AVEC, bool K8>
 __global__ __launch_bounds__(PREP_T) void decode_prep_kernel(const float* __restrict__ A, int64_t lda, int M, int K,
                                                              int nblk, const int8_t* __restrict__ kshift,
                                                              unsigned char* __restrict__ out) {
@@ -131,8 +131,10 @@ __global__ __launch_bounds__(PREP_T) void decode_prep_kernel(const float* __rest
     for (int off = 16; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
     if (q >= nblk * 32) return;   // past the last block (whole half waves)
     const int e = row_norm_exp(mx);
-    const int b = q >> 5, j = q & 31;   // j = 8 s + 4 h + g: k = 128 b + 32 s + 16 h + 4 g
-    const int st = j >> 3, h = (j >> 2) & 1, g = j & 3;
+    // j = 8 s + 4 h + g: k = 128 b + 32 s + 16 h + 4 g; K8 (packed W):
+    // j = 8 s + 2 g + h: k = 128 b + 32 s + 8 g + 4 h
+    const int b = q >> 5, j = q & 31;
+    const int st = j >> 3, h = K8 ? (j & 1) : ((j >> 2) & 1), g = K8 ? ((j >> 1) & 3) : (j & 3);
     const float x[4] = {v.x, v.y, v.z, v.w};
     half4 hi, lo;
 #pragma unroll
@@ -170,27 +172,36 @@ __device__ __forceinline__ float absmax8(float m, const float4& a, const float4&
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// VEC: W rows aligned to the load width and K % 32 == 0, so every step is two
-// buffer loads per lane (16 bytes each for fp32 W, 8 for fp16 W).  Otherwise
-// lanes load element by element with bounds checks, and block boundaries
-// wait for every load.
+// WM: how W arrives.  1: fp32 (or binary16) rows aligned to the load width
+// and K % 32 == 0, so every step is two buffer loads per lane (16 bytes each
+// for fp32 W, 8 for fp16 W).  0: the same rows, loaded element by element with
+// bounds checks (block boundaries wait for every load).  2: packed by
+// heal_pack_w (normalized rows of [32 hi | 32 res] fp16 per 32-wide k block,
+// or hi parts alone for a binary16 weight, rows padded): no split in the
+// kernel; lane group g takes k = 8g .. 8g+7 of each step (16 contiguous bytes
+// of hi, 16 of res), A's operand order follows, and each output is multiplied
+// by 2^-e_w[n], the row exponent of W.  The residual is at its own scale, so
+// A_hi.W_res joins A_hi.W_hi in one accumulator.
 // WF16: W holds binary16 values, exact in fp16: its residual is zero, so each
 // step keeps two products, A_hi.W and A_lo.W (2^-10 applied in the fold).
 // AVEC: A rows 16-byte aligned, activation units load as one 16-byte load.
 // MT == 1 stages A itself (A, lda); MT > 1 copies the block images (Ablk).
 // SHIFT (MT == 1): element (m, k) of A is multiplied by 2^-kshift[k] before
 // its block maximum and split.  ONE: plain FP16, the A_hi.W_hi product alone.
-template <int MT, bool VEC, bool WF16, bool AVEC, bool SHIFT, bool ONE, int NWK>
+template <int MT, int WM, bool WF16, bool AVEC, bool SHIFT, bool ONE, int NWK>
 __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __restrict__ A, int64_t lda,
                                                           const unsigned char* __restrict__ Ablk,
                                                           uint32_t a_total_bytes, const void* __restrict__ W,
-                                                          int64_t ldw, float* __restrict__ C, int64_t ldc,
+                                                          int64_t wrow_bytes, const int* __restrict__ wexp,
+                                                          float* __restrict__ C, int64_t ldc,
                                                           float* __restrict__ part,
                                                           unsigned long long* __restrict__ flag_base, uint64_t epoch,
                                                           int M, int N, int K, int kchunk,
                                                           const int8_t* __restrict__ kshift,
                                                           uint32_t* __restrict__ status) {
     static_assert(!SHIFT || MT == 1, "with MT > 1 the shift is applied by decode_prep_kernel");
+    constexpr bool VEC = WM >= 1;
+    constexpr bool PKW = WM == 2;                   // W packed: k = 8g .. 8g+7 per lane group
     constexpr int BB = block_bytes<MT>();
     constexpr int SB = img_bytes<MT>();             // LDS bytes per block buffer: planes + exponents
     constexpr bool INK = MT == 1;                   // split the activation in the kernel
@@ -225,7 +236,9 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
     const __amdgpu_buffer_rsrc_t ksrc = make_rsrc(kshift, SHIFT ? (uint32_t)K : 0u);
     const int ur = 4 * wave + (lane & 3);
     const int ugg = (lane >> 2) & 3, uhalf = (lane >> 4) & 1, ust = (lane >> 5) & 1;
-    auto unit_k = [&](int b, int i) { return k_begin + KA * b + 32 * (ust + 2 * i) + 16 * uhalf + 4 * ugg; };
+    auto unit_k = [&](int b, int i) {
+        return k_begin + KA * b + 32 * (ust + 2 * i) + (PKW ? 8 * ugg + 4 * uhalf : 16 * uhalf + 4 * ugg);
+    };
     auto load_a = [&](int b) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -299,19 +312,32 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
                                                      0, 0);
     };
 
-    // W: lane reads row n, k = k_begin + 32 step + {4g.., 16+4g..}
-    // (scalars made explicit: the buffer resource must live in SGPRs)
-    constexpr int ESZ = WF16 ? 2 : 4;          // bytes per W element
+    // W: lane reads row n, k = k_begin + 32 step + {4g.., 16+4g..} (packed:
+    // 8g .. 8g+7) (scalars made explicit: the buffer resource must live in SGPRs)
+    constexpr int ESZ = WF16 ? 2 : 4;          // bytes per W element (unpacked)
+    constexpr int KBB = WF16 ? 64 : 128;       // packed bytes per row and 32-wide k block
     constexpr int PFW = PF;                    // W steps in flight
-    using WReg = std::conditional_t<WF16, u32x4, u32x8>;   // one step's 8 W values
+    constexpr int LPS = PKW && WF16 ? 1 : 2;   // buffer loads per W step (VEC)
+    using WReg = std::conditional_t<WF16, u32x4, u32x8>;   // one step's 8 W values (packed: hi, then res)
+    const int64_t ldw = wrow_bytes / ESZ;      // unpacked: elements per row
     const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(ROWS_PER_WAVE, N - n0)));
     const int wrow0 = __builtin_amdgcn_readfirstlane(min(n0, N - 1));
     const unsigned char* Wb = static_cast<const unsigned char*>(W);
     const __amdgpu_buffer_rsrc_t wrsrc =
-        make_rsrc(Wb + (int64_t)wrow0 * ldw * ESZ, (uint32_t)((int64_t)nrows * ldw * ESZ));
-    const uint32_t wlane = (uint32_t)((lane & 15) * ldw * ESZ + (int64_t)(k_begin + 4 * g) * ESZ);
+        make_rsrc(Wb + (int64_t)wrow0 * wrow_bytes, (uint32_t)((int64_t)nrows * wrow_bytes));
+    const uint32_t wlane = PKW ? (uint32_t)((lane & 15) * wrow_bytes + (int64_t)(k_begin / 32) * KBB + 16 * g)
+                               : (uint32_t)((lane & 15) * wrow_bytes + (int64_t)(k_begin + 4 * g) * ESZ);
     auto load_w = [&](int step, WReg& w) {
-        if (VEC) {
+        if constexpr (PKW) {
+            const uint32_t off = wlane + (uint32_t)(step * KBB);
+            const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off, 0, 0);
+            if constexpr (WF16) {
+                w = h;
+            } else {
+                const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off + 64, 0, 0);
+                w = WReg{h[0], h[1], h[2], h[3], r[0], r[1], r[2], r[3]};
+            }
+        } else if (VEC) {
             const uint32_t off = wlane + (uint32_t)(step * 32 * ESZ);
             if constexpr (WF16) {
                 const auto a = __builtin_amdgcn_raw_buffer_load_b64(wrsrc, off, 0, 0);
@@ -370,7 +396,7 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
 #pragma unroll
         for (int s = 0; s < PFW; ++s) load_w(min(s, nsteps - 1), wr[s]);
         __builtin_amdgcn_sched_barrier(0);
-        if (VEC) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PFW));   // block 0 landed; W still in flight
+        if (VEC) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS * PFW));   // block 0 landed; W still in flight
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
     __builtin_amdgcn_s_barrier();
@@ -399,6 +425,9 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
             half8 wh, wl;
             if constexpr (WF16) {
                 wh = __builtin_bit_cast(half8, w);
+            } else if constexpr (PKW) {
+                wh = __builtin_bit_cast(half8, (u32x4){w[0], w[1], w[2], w[3]});
+                wl = __builtin_bit_cast(half8, (u32x4){w[4], w[5], w[6], w[7]});
             } else {
                 const floatx8 wf = __builtin_bit_cast(floatx8, w);
                 const float4 ra = {wf[0], wf[1], wf[2], wf[3]}, rb = {wf[4], wf[5], wf[6], wf[7]};
@@ -413,7 +442,7 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
                     const half8 ah = *reinterpret_cast<const half8*>(abuf + off);
                     const half8 al = *reinterpret_cast<const half8*>(abuf + BB / 2 + off);
                     mfma16(ah, wh, acc_hh[t]);
-                    if constexpr (!WF16 && !ONE) mfma16(ah, wl, acc_c[t]);
+                    if constexpr (!WF16 && !ONE) mfma16(ah, wl, PKW ? acc_hh[t] : acc_c[t]);   // packed: res unshifted
                     if constexpr (!ONE) mfma16(al, wh, acc_c[t]);
                 }
             }
@@ -436,8 +465,8 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
                 store_a(b + 1);
                 __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
             } else {
-                // the copy was issued before this block's 2 STEPS W loads
-                if (VEC) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * STEPS));
+                // the copy was issued before this block's LPS * STEPS W loads
+                if (VEC) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS * STEPS));
                 else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             }
             __builtin_amdgcn_s_barrier();
@@ -464,6 +493,13 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
         atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
 
     // ---- epilogue: lane holds column n, rows t*16 + 4g + e ------------------
+    if constexpr (PKW) {   // W's row exponent (padding rows hold 0)
+        const int ew = row_ok ? wexp[n] : 0;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tot[t][e] = __builtin_ldexpf(tot[t][e], -ew);
+    }
     const int nsplit = gridDim.y;
     if (nsplit == 1) {
         if (!row_ok) return;
@@ -579,8 +615,8 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift, const void* W, bool wf16,
-                              bool one, int64_t ldw, float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                              void* workspace, const DecodePlan& plan, uint64_t epoch, uint32_t* status,
+                              bool packed, bool one, int64_t ldw, float* C, int64_t ldc, int64_t M, int64_t N,
+                              int64_t K, void* workspace, const DecodePlan& plan, uint64_t epoch, uint32_t* status,
                               hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
     if (M > 64 || K == 0) return hipErrorInvalidValue;
@@ -598,11 +634,16 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
     // (16 bytes fp32, 8 bytes fp16) and whole k32 steps
     const uintptr_t walign = wf16 ? 7 : 15;
     const bool vec = (reinterpret_cast<uintptr_t>(W) & walign) == 0 && (ldw & 3) == 0 && (K & 31) == 0;
+    // packed W: padded rows, the row exponents after them
+    const int64_t wrow_bytes = packed ? (wf16 ? pack_row_bytes_hi(K) : pack_row_bytes(K)) : ldw * (wf16 ? 2 : 4);
+    const int* wexp = packed ? reinterpret_cast<const int*>(static_cast<const unsigned char*>(W) +
+                                                            (wf16 ? pack_data_bytes_hi(N, K) : pack_data_bytes(N, K)))
+                             : nullptr;
     // activation units load as float4 when rows are 16-byte aligned
     const bool avec = (reinterpret_cast<uintptr_t>(A) & 15) == 0 && (lda & 3) == 0;
 #define HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW_)                                      \
     hipLaunchKernelGGL((gemm_decode_kernel<MT_, VEC_, F16_, AV_, SH_, ONE_, NW_>), grid, dim3(64 * NW_), \
-                       2 * img_bytes<MT_>(), s, A, lda, ablk, (uint32_t)plan.a_bytes, W, ldw, C, ldc, part,            \
+                       2 * img_bytes<MT_>(), s, A, lda, ablk, (uint32_t)plan.a_bytes, W, wrow_bytes, wexp, C, ldc, part, \
                        flags, epoch,                                                                          \
                        (int)M, (int)N, (int)K, (int)plan.kchunk, kshift, status)
 #define HEAL_DEC_LAUNCH(MT_, VEC_, F16_, AV_, SH_, ONE_)                                                \
@@ -628,19 +669,27 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
     do {                                                                                                \
         if constexpr ((MT_) > 1) {                                                                      \
             const dim3 pgrid(16 * (MT_), (unsigned)((nablk * 32 + PREP_T - 1) / PREP_T));                \
-            if (avec)                                                                                   \
-                hipLaunchKernelGGL((decode_prep_kernel<MT_, true>), pgrid, dim3(PREP_T), 0, s, A, lda, (int)M, \
-                                   (int)K, nablk, kshift, ablk);                                        \
+            if (avec && packed)                                                                         \
+                hipLaunchKernelGGL((decode_prep_kernel<MT_, true, true>), pgrid, dim3(PREP_T), 0, s, A, lda, \
+                                   (int)M, (int)K, nablk, kshift, ablk);                                \
+            else if (avec)                                                                              \
+                hipLaunchKernelGGL((decode_prep_kernel<MT_, true, false>), pgrid, dim3(PREP_T), 0, s, A, lda, \
+                                   (int)M, (int)K, nablk, kshift, ablk);                                \
+            else if (packed)                                                                            \
+                hipLaunchKernelGGL((decode_prep_kernel<MT_, false, true>), pgrid, dim3(PREP_T), 0, s, A, lda, \
+                                   (int)M, (int)K, nablk, kshift, ablk);                                \
             else                                                                                        \
-                hipLaunchKernelGGL((decode_prep_kernel<MT_, false>), pgrid, dim3(PREP_T), 0, s, A, lda, (int)M, \
-                                   (int)K, nablk, kshift, ablk);                                        \
+                hipLaunchKernelGGL((decode_prep_kernel<MT_, false, false>), pgrid, dim3(PREP_T), 0, s, A, lda, \
+                                   (int)M, (int)K, nablk, kshift, ablk);                                \
         }                                                                                               \
         if (wf16) {                                                                                     \
-            if (vec) HEAL_DEC_AV(MT_, true, true, SH_);                                                 \
-            else HEAL_DEC_AV(MT_, false, true, SH_);                                                    \
+            if (packed) HEAL_DEC_AV(MT_, 2, true, SH_);                                                 \
+            else if (vec) HEAL_DEC_AV(MT_, 1, true, SH_);                                               \
+            else HEAL_DEC_AV(MT_, 0, true, SH_);                                                        \
         } else {                                                                                        \
-            if (vec) HEAL_DEC_AV(MT_, true, false, SH_);                                                \
-            else HEAL_DEC_AV(MT_, false, false, SH_);                                                   \
+            if (packed) HEAL_DEC_AV(MT_, 2, false, SH_);                                                \
+            else if (vec) HEAL_DEC_AV(MT_, 1, false, SH_);                                              \
+            else HEAL_DEC_AV(MT_, 0, false, SH_);                                                       \
         }                                                                                               \
     } while (0)
     if (mt == 1) {

@@ -167,8 +167,9 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     // HBM row bytes: Kp hi + Kp lo fp16; Kp fp16 (hi-only); 3 Kp bf16 (X3)
-    const uint32_t rowbytes = X3 ? (uint32_t)Kp * 6u : (AH ? (uint32_t)Kp * 2u : (uint32_t)Kp * 4u);   // A
-    const uint32_t browbytes = X3 ? (uint32_t)Kp * 6u : (BHI ? (uint32_t)Kp * 2u : (uint32_t)Kp * 4u);
+    // packed row strides: 3 Kp bf16 (X3, no pad), or the padded hi-only / hi-res rows
+    const uint32_t rowbytes = X3 ? (uint32_t)Kp * 6u : (uint32_t)(AH ? pack_row_bytes_hi(Kp) : pack_row_bytes(Kp));
+    const uint32_t browbytes = X3 ? (uint32_t)Kp * 6u : (uint32_t)(BHI ? pack_row_bytes_hi(Kp) : pack_row_bytes(Kp));
     const int nkt_all = (X3 ? 6 : 1) * (Kp / BK);
     const int kt_begin = SPLIT ? half_k * (nkt_all / 2) : 0;
     const int kt_end = SPLIT ? (half_k ? nkt_all : nkt_all / 2) : nkt_all;
@@ -506,7 +507,7 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
     const int64_t Kp = pack_kp(K);
     if (Kp == 0) return hipErrorInvalidValue;  // K == 0 is handled by the caller
     // one operand block must be addressable by a 32-bit buffer offset
-    if ((int64_t)BM * Kp * (x3 ? 6 : 4) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    if ((int64_t)BM * (x3 ? Kp * 6 : pack_row_bytes(K)) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
     // split the k range in two when the tiles fill at most half of the 256 CUs

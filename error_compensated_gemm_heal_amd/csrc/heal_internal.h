@@ -74,9 +74,9 @@ __device__ __forceinline__ bool f16_out_of_range4(const float4& v) {
 // ---- packed dual-FP16 operand layout used by the prefill GEMM --------------
 // Row r of a packed operand is normalized (row_norm_exp) and holds, for each
 // 32-wide block kb of the reduction dimension, 32 fp16 hi parts followed by
-// 32 fp16 residuals (split_res; 128 bytes).  Rows are padded to a multiple of
-// kPackRows and k to a multiple of kPackK, with zeros, so the GEMM main loop
-// needs no bounds checks.  After the rows come the row exponents, int32
+// 32 fp16 residuals (split_res; 128 bytes), rows pack_row_bytes apart.  Rows
+// are padded to a multiple of kPackRows and k to a multiple of kPackK, with
+// zeros, so the GEMM main loop needs no bounds checks.  After the rows come the row exponents, int32
 // [pack_rows(R)] (0 for padding rows).  A 16-bit weight (its residuals are
 // zero) packs as the hi parts alone, not normalized: row r holds its Kp fp16
 // values (64 bytes per 32-wide block), same padding, exponents 0.  An fp32
@@ -85,11 +85,19 @@ __device__ __forceinline__ bool f16_out_of_range4(const float4& v) {
 constexpr int kPackK = 32;
 constexpr int kPackRows = 256;
 
+// Each packed row is followed by 256 unused bytes: rows whose stride is a
+// multiple of 16 KB (K = 4096) would otherwise start in the same memory
+// channel, and a kernel reading 16 rows at one k would queue on it.
+constexpr int kPackRowPad = 256;
+
 __host__ __device__ inline int64_t pack_kp(int64_t K) { return (K + kPackK - 1) / kPackK * kPackK; }
 __host__ __device__ inline int64_t pack_rows(int64_t R) { return (R + kPackRows - 1) / kPackRows * kPackRows; }
+// byte stride of the rows of a packed operand: hi/res form, hi-only form
+__host__ __device__ inline int64_t pack_row_bytes(int64_t K) { return pack_kp(K) * 4 + kPackRowPad; }
+__host__ __device__ inline int64_t pack_row_bytes_hi(int64_t K) { return pack_kp(K) * 2 + kPackRowPad; }
 // bytes of the rows of a packed operand (hi/res form), where its exponents start
-__host__ __device__ inline int64_t pack_data_bytes(int64_t R, int64_t K) { return pack_rows(R) * pack_kp(K) * 4; }
-__host__ __device__ inline int64_t pack_data_bytes_hi(int64_t R, int64_t K) { return pack_rows(R) * pack_kp(K) * 2; }
+__host__ __device__ inline int64_t pack_data_bytes(int64_t R, int64_t K) { return pack_rows(R) * pack_row_bytes(K); }
+__host__ __device__ inline int64_t pack_data_bytes_hi(int64_t R, int64_t K) { return pack_rows(R) * pack_row_bytes_hi(K); }
 // bytes of one packed operand of R rows and reduction length K: rows, then exponents
 __host__ __device__ inline int64_t pack_bytes(int64_t R, int64_t K) { return pack_data_bytes(R, K) + pack_rows(R) * 4; }
 // bytes of the hi-only packed form
@@ -211,9 +219,11 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K);
 // multiplied by 2^-kshift[k] before its split.
 // epoch: a number no earlier call in the process used (the split-K counters
 // tell this call's arrivals from stale contents by it).
+// packed: W is a heal_pack_w buffer for (N, K) (hi-only when wf16); ldw is
+// then ignored.
 hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift, const void* W, bool wf16,
-                              bool one, int64_t ldw, float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                              void* workspace, const DecodePlan& plan, uint64_t epoch, uint32_t* status,
+                              bool packed, bool one, int64_t ldw, float* C, int64_t ldc, int64_t M, int64_t N,
+                              int64_t K, void* workspace, const DecodePlan& plan, uint64_t epoch, uint32_t* status,
                               hipStream_t s);
 // A fresh call epoch (48 bits, never 0; thread-safe).
 uint64_t next_epoch();

@@ -51,7 +51,7 @@ extern "C" heal_status heal_gemm_f32c_noalloc(const float* A, int64_t lda, const
                                               const int8_t* a_kshift, uint32_t* dev_status, void* stream) {
     if (M < 0 || N < 0 || K < 0 || M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31))
         return HEAL_ERR_SHAPE;
-    if (!heal::decode_path(M, K, flags)) return HEAL_ERR_UNSUPPORTED;   // M <= 64, fp32/fp16 [N, K] W, not packed
+    if (!heal::decode_path(M, K, flags)) return HEAL_ERR_UNSUPPORTED;   // M <= 64, [N, K] or packed W, A unpacked
     if (heal_gemm_f32c_workspace(M, N, K, flags) > kScratchBytes) return HEAL_ERR_WORKSPACE;
     if (M == 0 || N == 0) return HEAL_OK;
     void* ws = nullptr;

@@ -133,10 +133,10 @@ __global__ __launch_bounds__(256) void pack_rowmajor_kernel(const T* __restrict_
             l[j] = f16_bits(ll);
         }
         if constexpr (sizeof(T) == 2) {   // a 16-bit source: the hi-only form
-            uint16_t* o = out + r * Kp + k;
+            uint16_t* o = out + r * (pack_row_bytes_hi(K) / 2) + k;
             *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
         } else {
-            uint16_t* o = out + r * (Kp * 2) + (k / kPackK) * (2 * kPackK) + (k % kPackK);
+            uint16_t* o = out + r * (pack_row_bytes(K) / 2) + (k / kPackK) * (2 * kPackK) + (k % kPackK);
             *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
             *reinterpret_cast<uint2*>(o + kPackK) =
                 make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
@@ -176,10 +176,10 @@ __global__ __launch_bounds__(256) void pack_colmajor_kernel(const T* __restrict_
             l[j] = f16_bits(ll);
         }
         if constexpr (sizeof(T) == 2) {   // a 16-bit source: the hi-only form
-            uint16_t* o = out + r * Kp + k;
+            uint16_t* o = out + r * (pack_row_bytes_hi(K) / 2) + k;
             *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
         } else {
-            uint16_t* o = out + r * (Kp * 2) + (k / kPackK) * (2 * kPackK) + (k % kPackK);
+            uint16_t* o = out + r * (pack_row_bytes(K) / 2) + (k / kPackK) * (2 * kPackK) + (k % kPackK);
             *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
             *reinterpret_cast<uint2*>(o + kPackK) =
                 make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
@@ -272,9 +272,9 @@ __global__ __launch_bounds__(256) void pack_rows_norm_kernel(const float* __rest
                 l[i >> 1] = f16_bits(l0) | ((uint32_t)f16_bits(l1) << 16);
             }
             if constexpr (HI_ONLY) {   // the hi-only layout: Kp fp16 per row
-                *reinterpret_cast<uint4*>(out + r * Kp + k) = make_uint4(h[0], h[1], h[2], h[3]);
+                *reinterpret_cast<uint4*>(out + r * (pack_row_bytes_hi(K) / 2) + k) = make_uint4(h[0], h[1], h[2], h[3]);
             } else {
-                uint16_t* o = out + r * (Kp * 2) + (k / kPackK) * (2 * kPackK) + (k % kPackK);
+                uint16_t* o = out + r * (pack_row_bytes(K) / 2) + (k / kPackK) * (2 * kPackK) + (k % kPackK);
                 *reinterpret_cast<uint4*>(o) = make_uint4(h[0], h[1], h[2], h[3]);
                 *reinterpret_cast<uint4*>(o + kPackK) = make_uint4(l[0], l[1], l[2], l[3]);
             }

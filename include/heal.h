@@ -192,8 +192,8 @@ size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags)
  * loops, harnesses that forbid hipMalloc.
  *  Same arguments, results and kernels as heal_gemm_f32c (bit for bit), on
  *  the decode path only: M <= 64, W fp32 or binary16 (HEAL_W_F16) in the
- *  [N, K] layout, not packed, not HEAL_BF16X3, K < 2^23 (else
- *  HEAL_ERR_UNSUPPORTED).  Its scratch memory is a 16 MiB array of device
+ *  [N, K] layout or packed by heal_pack_w (HEAL_W_PACKED), A not packed,
+ *  not HEAL_BF16X3, K < 2^23 (else HEAL_ERR_UNSUPPORTED).  Its scratch memory is a 16 MiB array of device
  *  memory that the library owns, one per GPU, held until the process ends;
  *  shapes whose heal_gemm_f32c_workspace exceeds 16 MiB get
  *  HEAL_ERR_WORKSPACE (the Llama-3-8B-like decode layers need at most

@@ -103,7 +103,7 @@ def test_gemm_noalloc_validation():
     args = lambda M=8, N=64, K=256, flags=0: (FAKE, K, FAKE, K, FAKE, N, M, N, K, flags, None, None, None)
     assert f(*args(M=-1)) == SHAPE
     assert f(*args(M=65)) == UNSUP                       # the prefill path allocates its packed operands
-    assert f(*args(flags=heal.HEAL_W_PACKED)) == UNSUP
+    assert f(*args(flags=heal.HEAL_A_PACKED)) == UNSUP
     assert f(*args(flags=heal.HEAL_W_KN)) == UNSUP
     assert f(*args(flags=heal.HEAL_BF16X3)) == UNSUP
     assert heal.heal_gemm_f32c_workspace(64, 256, 1 << 20, 0) > 16 << 20
@@ -122,13 +122,17 @@ def test_gemm_workspace_sizes():
         b = ws(M, 4096, 4096, 0)
         assert b % 256 == 0
     assert ws(64, 4096, 4096, 0) >= 64 * 4096 * 4
-    # prefill path: packed A (rows padded to 256, k to 32, 4 bytes per element,
-    # then one int32 row exponent per padded row) + packed W
-    pk = lambda R, Kp, b: R * Kp * b + R * 4
+    # prefill path: packed A (rows padded to 256, k to 32, 4 bytes per element
+    # and 256 bytes more per row, then one int32 row exponent per padded row)
+    # + packed W
+    pk = lambda R, Kp, b: R * (Kp * b + 256) + R * 4
     assert ws(2048, 4096, 14336, 0) == pk(2048, 14336, 4) + pk(4096, 14336, 4)
     assert ws(2048, 4096, 14336, heal.HEAL_W_PACKED) == pk(2048, 14336, 4)
     assert ws(2048, 4096, 14336, heal.HEAL_W_PACKED | heal.HEAL_A_PACKED) == 0
     assert ws(8, 4096, 4096, heal.HEAL_A_PACKED) == pk(4096, 4096, 4)   # packed A -> prefill path
+    for M in (1, 8, 64):      # a packed weight keeps the decode path and its workspace
+        assert ws(M, 4096, 4096, heal.HEAL_W_PACKED) == ws(M, 4096, 4096, 0)
+        assert ws(M, 4096, 4096, heal.HEAL_W_PACKED | heal.HEAL_W_F16) == ws(M, 4096, 4096, 0)
     assert ws(65, 100, 33, 0) == pk(256, 64, 4) + pk(256, 64, 4)
     assert heal.heal_pack_w_bytes(100, 33) == pk(256, 64, 4)
     assert heal.heal_pack_w_bytes(100, 33, heal.HEAL_W_F16) == pk(256, 64, 2)      # hi parts only

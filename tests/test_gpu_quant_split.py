@@ -126,12 +126,13 @@ def test_dequant_all_codes():
     assert np.array_equal(_u16(hi), hr) and np.array_equal(_u16(lo), lr)
 
 
-def test_quant_dequant_qwen_layer_sampled_full_size():
+def test_quant_dequant_qwen_layer_full_size_every_row():
     """Full Qwen3-8B-like layer: 32 x 2048 tokens, 32 + 8 + 8 heads of 128.
 
     The whole tensor is quantized and dequantized on the GPU exactly as the
-    benchmark does (one [tokens, 48, 128] launch each); 20000 sampled rows are
-    compared bit-for-bit with the oracle."""
+    benchmark does (one [tokens, 48, 128] launch each), and every one of its
+    3.1 M rows is compared bit for bit with the oracle's quantizer and
+    dequantizer (402.65 M codes, scales and fp32 values)."""
     print("quant full size: generating", flush=True)
     tokens = 32 * 2048
     Q, K, V = WL.qkv(tokens, 32, 8, 128, seed=4000)
@@ -141,18 +142,14 @@ def test_quant_dequant_qwen_layer_sampled_full_size():
     codes, scales = heal.heal_qkv_quant_i16(Xd)
     deq = heal.heal_kv_dequant_i16(codes, scales, "f32")
     torch.cuda.synchronize()
+    del Xd
+    print("quant full size: oracle", flush=True)
+    cr, sr = oracle.quant_i16(X)
+    del X
     print("quant full size: comparing", flush=True)
-    rows = WL.rng(1).choice(tokens * 48, size=20000, replace=False)
-    Xr = X.reshape(-1, 128)[rows]
-    cr, sr = oracle.quant_i16(Xr)
-    ridx = torch.from_numpy(rows).to(DEV)
-    assert np.array_equal(codes.reshape(-1, 128)[ridx].cpu().numpy(), cr)
-    assert np.array_equal(scales.reshape(-1)[ridx].cpu().numpy().view(np.uint32), sr.view(np.uint32))
-    assert np.array_equal(deq.reshape(-1, 128)[ridx].cpu().numpy().view(np.uint32),
-                          oracle.dequant_f32(cr, sr).view(np.uint32))
-    # property over every row: the absmax element of each row carries code +-32767
-    amax = torch.max(torch.abs(codes.reshape(-1, 128).to(torch.int32)), dim=1).values
-    assert bool(torch.all(amax == 32767) | torch.all(scales.reshape(-1) == 0))
+    assert np.array_equal(codes.cpu().numpy(), cr)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(deq.cpu().numpy().view(np.uint32), oracle.dequant_f32(cr, sr).view(np.uint32))
 
 
 def test_calibration_kernels_run():

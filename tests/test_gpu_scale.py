@@ -9,9 +9,9 @@ back, so:
     magnitude (sigma from 1e-20 to 1e6 here, and rows of mixed scales);
   * scaling a row of A by 2^j scales that row of C by 2^j, bit for bit.
 Paths: decode with the in-kernel split (M <= 16) and with split planes
-(M > 16), fp32 and binary16 weights; prefill with and without its k split,
-packed weight, packed activation, binary16 weight; the Q/K/V projection with
-INT16 output, fused and two-pass.
+(M > 16), fp32 and binary16 weights, streamed or packed; prefill with and
+without its k split, packed weight, packed activation, binary16 weight; the
+Q/K/V projection with INT16 output, fused and two-pass.
 """
 import numpy as np
 import pytest
@@ -32,7 +32,9 @@ SCALES = [1.0, 1e-2, 1e-3, 1e-4, 1e-5, 1e-8, 1e-20, 1e6]
 PATHS = [("decode_ink", 8, 1024, 384, "fp32"), ("decode_planes", 40, 1024, 384, "fp32"),
          ("decode_w16", 16, 1024, 256, "fp16"), ("prefill_ksplit", 300, 1024, 512, "fp32"),
          ("prefill", 2048, 256, 4608, "fp32"), ("prefill_packed", 300, 768, 640, "packed"),
-         ("prefill_w16", 300, 768, 640, "fp16"), ("prefill_packed_a", 260, 512, 384, "packed_a")]
+         ("prefill_w16", 300, 768, 640, "fp16"), ("prefill_packed_a", 260, 512, 384, "packed_a"),
+         ("decode_packed", 8, 1024, 384, "packed"), ("decode_packed_planes", 40, 1000, 384, "packed"),
+         ("decode_packed_w16", 16, 1024, 256, "packed16")]
 
 
 def _operands(M, K, N, sigma, seed):
@@ -44,11 +46,11 @@ def _operands(M, K, N, sigma, seed):
 
 def _gpu(A, W, form):
     Ad = torch.from_numpy(A).to(DEV)
-    if form == "fp16":
+    if form in ("fp16", "packed16"):
         Wd = torch.from_numpy(W.astype(np.float16)).to(DEV)
     else:
         Wd = torch.from_numpy(W).to(DEV)
-    if form in ("packed", "packed_a"):
+    if form in ("packed", "packed_a", "packed16"):
         Wd = heal.heal_pack_w(Wd)
     if form == "packed_a":
         Ad = heal.heal_pack_w(Ad)
@@ -78,7 +80,7 @@ def test_gemm_tolerance_at_every_activation_scale(label, M, K, N, form):
     for i, sigma in enumerate(SCALES):
         print(f"scale {label} M={M} K={K} N={N} sigma={sigma:g}", flush=True)
         A, W = _operands(M, K, N, sigma, seed=9000 + 17 * i + M)
-        Wref = W.astype(np.float16).astype(np.float32) if form == "fp16" else W
+        Wref = W.astype(np.float16).astype(np.float32) if form in ("fp16", "packed16") else W
         C = _gpu(A, W, form)
         _check(C, A, Wref, _rows(M), f"sigma={sigma:g}")
 
@@ -108,7 +110,7 @@ def test_gemm_mixed_scales(label, M, K, N, form):
     wide = g.random(M) < 0.5
     cols = g.random(K) < 0.5
     A[np.ix_(wide, cols)] *= np.float32(1e-6)
-    Wref = W.astype(np.float16).astype(np.float32) if form == "fp16" else W
+    Wref = W.astype(np.float16).astype(np.float32) if form in ("fp16", "packed16") else W
     C = _gpu(A, W, form)
     _check(C, A, Wref, _rows(M), "mixed")
 

@@ -3,7 +3,7 @@ memory, called through the C ABI, against heal_gemm_f32c with a workspace.
 
 The kernels are the same, so the outputs must be equal bit for bit: two calls
 in a row, the second on a smaller input (the scratch keeps the first call's
-contents), for fp32 and binary16 weights and a shape with split planes.
+contents), for fp32, binary16 and packed weights and a shape with split planes.
 """
 import ctypes
 
@@ -20,23 +20,28 @@ DEV = "cuda:0"
 
 def _noalloc(A, W, f16=False):
     M, K = A.shape
-    N = W.shape[0]
+    if isinstance(W, heal.PackedOperand):
+        N, wbuf, ldw, flags = W.rows, W.buf, 0, heal.HEAL_W_PACKED | (heal.HEAL_W_F16 if W.f16 else 0)
+    else:
+        N, wbuf, ldw, flags = W.shape[0], W, K, heal.HEAL_W_F16 if f16 else 0
     C = torch.full((M, N), float("nan"), device=DEV)
-    flags = heal.HEAL_W_F16 if f16 else 0
-    st = heal.lib().heal_gemm_f32c_noalloc(ctypes.c_void_p(A.data_ptr()), K, ctypes.c_void_p(W.data_ptr()), K,
+    st = heal.lib().heal_gemm_f32c_noalloc(ctypes.c_void_p(A.data_ptr()), K, ctypes.c_void_p(wbuf.data_ptr()), ldw,
                                            ctypes.c_void_p(C.data_ptr()), N, M, N, K, flags, None, None,
                                            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     assert st == 0, heal.heal_status_str(st)
     return C
 
 
-@pytest.mark.parametrize("f16", [False, True])
-def test_noalloc_equals_workspace_entry_point_two_calls(f16):
+@pytest.mark.parametrize("form", ["fp32", "fp16", "packed"])
+def test_noalloc_equals_workspace_entry_point_two_calls(form):
+    f16 = form == "fp16"
     for (M, K, N, seed) in [(64, 14336, 4096, 11), (40, 4096, 1024, 12), (5, 1000, 300, 13)]:
-        print(f"noalloc M={M} K={K} N={N} f16={f16}", flush=True)
+        print(f"noalloc M={M} K={K} N={N} {form}", flush=True)
         A, W = WL.decode_gemm(M, K, N, seed=seed)
         Ad = torch.from_numpy(A).to(DEV)
         Wd = torch.from_numpy(W.astype(np.float16) if f16 else W).to(DEV)
+        if form == "packed":
+            Wd = heal.heal_pack_w(Wd)
         ref = heal.heal_gemm_f32c(Ad, Wd).cpu().numpy()
         got = _noalloc(Ad, Wd, f16).cpu().numpy()
         torch.cuda.synchronize()
