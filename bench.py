@@ -19,6 +19,9 @@ workload (inputs resident in HBM before timing starts):
            touch different weights and the 256 MB MALL cannot serve repeats)
   decode_w16  the same 16 GEMMs with the weights held as binary16 (2 bytes each;
            the paper's two-product form for 16-bit weights)
+  decode_packed  the same 16 GEMMs with the fp32 weights split once beforehand
+           (heal_pack_w: row-normalized fp16 hi and residual, 4 bytes each)
+  decode_w16_packed  the binary16 weights packed once (2 bytes each)
   decode_kshift  the same 16 GEMMs with massive activation channels beyond
            FP16's range (0.5% of channels x 2e5), rescaled per channel by powers
            of two in the split (a_kshift) against a once-rescaled weight
@@ -96,7 +99,7 @@ def build_workload(rows_sel):
         W["prefill"] = pre
         log(f"[bench] prefill inputs ready ({time.time() - t0:.1f}s)")
 
-    if "decode" in rows_sel or "decode_w16" in rows_sel:
+    if rows_sel & {"decode", "decode_w16", "decode_packed", "decode_w16_packed"}:
         weights = {}
         acts = {}
         for i, (K, N) in enumerate(WL.LLAMA3_8B_DECODE_KN):
@@ -119,6 +122,13 @@ def build_workload(rows_sel):
         for c in calls:
             calls16.append(dict(c, W=w16[(c["K"], c["N"])]))
         W["decode_w16"] = calls16
+        if "decode_packed" in rows_sel:
+            wp = {kn: heal.heal_pack_w(w) for kn, w in weights.items()}
+            W["decode_packed"] = [dict(c, W=wp[(c["K"], c["N"])]) for c in calls]
+        if "decode_w16_packed" in rows_sel:
+            wp16 = {kn: heal.heal_pack_w(w) for kn, w in w16.items()}
+            W["decode_w16_packed"] = [dict(c, W=wp16[(c["K"], c["N"])]) for c in calls]
+        torch.cuda.synchronize()
         log(f"[bench] decode inputs ready ({time.time() - t0:.1f}s)")
 
     if "decode_kshift" in rows_sel:
@@ -253,6 +263,17 @@ def make_rows(W):
 
         d16bytes = sum(2 * c["K"] * c["N"] + 4 * (c["M"] * c["K"] + c["M"] * c["N"]) for c in calls16)
         rows.append(("decode_w16", run_decode16, d16bytes, "B"))
+    for name, esz in (("decode_packed", 4), ("decode_w16_packed", 2)):
+        if name in W:
+            pcalls = W[name]
+
+            def run_packed(pcalls=pcalls):
+                for c in pcalls:
+                    heal.heal_gemm_f32c(c["A"], c["W"], C=c["C"], workspace=c["ws"])
+
+            # algorithmic bytes: the weight's elements at esz bytes, A and C in fp32
+            pbytes = sum(esz * c["K"] * c["N"] + 4 * (c["M"] * c["K"] + c["M"] * c["N"]) for c in pcalls)
+            rows.append((name, run_packed, pbytes, "B"))
     if "decode_kshift" in W:
         callsk = W["decode_kshift"]
 
@@ -434,7 +455,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--rows", default="split,prefill,prefill_w16,prefill_1p,prefill_bf16x3,decode,decode_w16,decode_kshift,"
+    ap.add_argument("--rows", default="split,prefill,prefill_w16,prefill_1p,prefill_bf16x3,decode,decode_w16,"
+                                      "decode_packed,decode_w16_packed,decode_kshift,"
                                       "qkv_proj,quant,dequant,attn_prefill,attn",
                     help="comma-separated subset of rows to run (profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -527,7 +549,7 @@ def main():
                        "fp32 weights; also fp16 weights in the two-product form, the one-product mode and the "
                        "BF16 three-way mode), "
                        "16 decode GEMMs (M=1,8,32,64 x Llama-3-8B q/o, k/v, gate/up, down; fp32 and fp16 weights, "
-                       "and fp32 with per-channel rescaled massive activations), "
+                       "streamed or packed once, and fp32 with per-channel rescaled massive activations), "
                        "fused Q/K/V projection to INT16 (2048 tokens, K=4096, N=6144), "
                        "INT16 quant + dequant "
                        "(32x2048 tokens, 32+8+8 heads x 128), INT16 prefill attention (T=2048, 32/8 heads), "

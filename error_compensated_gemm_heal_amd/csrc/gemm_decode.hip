@@ -5,7 +5,9 @@
 //     C = A_hi.B_hi + 2^-10 (A_hi.B_lo + A_lo.B_hi),  fp32 accumulation,
 // but shaped for a skinny activation, where the weight is the traffic:
 //  * W is read once from HBM as fp32 [N, K] (4 bytes per element, the same
-//    bytes as its two fp16 parts) and split into hi/lo in registers;
+//    bytes as its two fp16 parts) and split into hi/lo in registers, or as a
+//    weight packed once by heal_pack_w (row-normalized hi and residual
+//    parts, rows padded off power-of-two strides), which needs no split;
 //  * FP16's narrow range (the same paragraph: handled by targeted
 //    rescaling): every 128-wide k block of every activation row is
 //    multiplied by the power of two 2^e that puts its largest magnitude in
@@ -18,22 +20,26 @@
 //    double-buffered LDS tile, in MFMA operand order, so every operand read
 //    is one conflict-free 16-byte LDS access; the block's 16 MT exponents
 //    travel with it.  Up to 16 rows, each workgroup loads the next block into
-//    registers while the current one is in use (one wave per four rows, so
-//    a row's block maximum is a reduction inside one wave) and normalizes
-//    and splits it itself: one launch in all.  Above 16 rows, where that work
-//    would be repeated by every workgroup, a first small kernel
-//    (decode_prep_kernel, one workgroup per row) writes the blocks the same
-//    way into operand-ordered planes once, and workgroups copy them into LDS
-//    with direct-to-LDS loads;
+//    registers while the current one is in use (each wave takes groups of
+//    four rows, so a row's block maximum is a reduction inside one wave) and
+//    normalizes and splits it itself: one launch in all.  Above 16 rows the
+//    same holds where that work stays light; otherwise, where it would be
+//    repeated by every workgroup, a first small kernel (decode_prep_kernel,
+//    one workgroup per row) writes the blocks the same way into
+//    operand-ordered planes once, and workgroups copy them into LDS with
+//    direct-to-LDS loads;
 //  * v_mfma_f32_16x16x32_f16 with the activation as the 16-row operand and W
 //    as the 16-column operand (16 W rows per wave), so output columns are
 //    consecutive lanes;
 //  * inside each 32-wide k step, lane group g (lanes 16g..16g+15) carries
 //    k = 4g..4g+3 and 16+4g..16+4g+3: any k order is valid as long as both
 //    operands use it, and this one makes each W load a 64-byte run per row;
-//  * W for the next 8 k steps is always in flight: every step issues exactly
-//    two W loads (the last steps re-read a clamped step), so the number of
-//    loads outstanding at each block boundary is a constant;
+//  * W for the next 8 k steps is always in flight: every step issues a
+//    fixed number of W loads (the last steps re-read a clamped step), so the
+//    number of loads outstanding at each block boundary is a constant;
+//  * with fewer than 8 k chunks, each 128-row group of W visits its chunk's
+//    k blocks in a rotated order, so that rows with a power-of-two stride do
+//    not all hit the same HBM channels at once;
 //  * split-K: the k range is cut into chunks chosen from (N, K) only.  Each
 //    workgroup writes its chunk's partial outputs with write-through stores,
 //    waits for them to complete, sets its (row block, chunk) flag to the
@@ -188,7 +194,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // MT == 1 stages A itself (A, lda); MT > 1 copies the block images (Ablk).
 // SHIFT (MT == 1): element (m, k) of A is multiplied by 2^-kshift[k] before
 // its block maximum and split.  ONE: plain FP16, the A_hi.W_hi product alone.
-template <int MT, int WM, bool WF16, bool AVEC, bool SHIFT, bool ONE, int NWK>
+template <int MT, int WM, bool WF16, bool AVEC, bool SHIFT, bool ONE, int NWK, bool INKT>
 __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __restrict__ A, int64_t lda,
                                                           const unsigned char* __restrict__ Ablk,
                                                           uint32_t a_total_bytes, const void* __restrict__ W,
@@ -199,13 +205,13 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
                                                           int M, int N, int K, int kchunk,
                                                           const int8_t* __restrict__ kshift,
                                                           uint32_t* __restrict__ status) {
-    static_assert(!SHIFT || MT == 1, "with MT > 1 the shift is applied by decode_prep_kernel");
+    constexpr bool INK = MT == 1 || INKT;           // split the activation in the kernel
+    static_assert(!SHIFT || INK, "with copied blocks the shift is applied by decode_prep_kernel");
     constexpr bool VEC = WM >= 1;
     constexpr bool PKW = WM == 2;                   // W packed: k = 8g .. 8g+7 per lane group
     constexpr int BB = block_bytes<MT>();
     constexpr int SB = img_bytes<MT>();             // LDS bytes per block buffer: planes + exponents
-    constexpr bool INK = MT == 1;                   // split the activation in the kernel
-    static_assert(NWK == NW || (NWK == 2 * NW && MT > 1), "8 waves only with the copied activation");
+    static_assert(NWK == NW || (NWK == 2 * NW && MT > 1), "8 waves only with several row tiles");
     constexpr int DMA_PER_WAVE = BB / 1024 / NWK;   // 1 KB per wave-wide direct-to-LDS load
     extern __shared__ __attribute__((aligned(16))) unsigned char sa[];   // 2 x SB
 
@@ -220,78 +226,108 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
     const int k_end = min(k_begin + kchunk, K);
     const int nsteps = (k_end - k_begin + 31) / 32;
     const int nblocks = (nsteps + STEPS - 1) / STEPS;
+    // With few chunks (under 8), the chunk's k blocks are visited in a
+    // rotated order, rot = (128-row group of W) mod nblocks: workgroups that
+    // run together then read at different k offsets, which spreads rows with
+    // a power-of-two stride (K = 4096 fp32 rows are 16 KiB apart) over the
+    // HBM channels.  With 8 chunks or more their start offsets already spread
+    // the reads, and rotation measured slower (K = 4096, N = 4096: 24.0 ->
+    // 26.1 us at M = 1; K = 4096, N = 14336 with 2 chunks: 55.7 -> 52.0 us).
+    // The order depends on the output rows and (N, K) only, not on M or the
+    // workgroup shape.
+    const int rot = gridDim.y < 8 ? (int)((unsigned)(blockIdx.x * NWK / 8) % (unsigned)nblocks) : 0;
+    auto pblock = [&](int b) { return b + rot >= nblocks ? b + rot - nblocks : b + rot; };
+    // the step to load for logical step L (clamped: the ring's last loads
+    // re-read a valid step)
+    auto pstep = [&](int L) {
+        L = min(L, nblocks * STEPS - 1);
+        return min(pblock(L / STEPS) * STEPS + L % STEPS, nsteps - 1);
+    };
 
-    // ---- MT == 1: activation blocks split in the kernel.  Wave w owns rows
-    //      4w .. 4w+3; lane l's unit i (i < 2) is 4 consecutive k of row
-    //      r = 4w + l % 4 at k = 128 b + 32 s + 16 half + 4 gg with gg =
-    //      (l / 4) % 4, half = (l / 16) % 2, s = (l / 32) % 2 + 2 i.  Its hi
-    //      and lo halves go to the 16-byte operand slot (s, lane 16 gg + r),
-    //      bytes 8 half .. 8 half + 7, of the hi and lo planes; the row's block
-    //      exponent to byte BB + 4 r.
-    float4 areg[2];
-    int sreg[2][4];   // SHIFT: the units' 2^-kshift exponents (k >= K reads 0)
+    // ---- INK: activation blocks split in the kernel.  Wave w owns rows
+    //      4 (w RND + j) .. +3 for j < RND (the 16 MT rows shared by the NWK
+    //      waves); lane l's unit (j, i) (i < 2) is 4 consecutive k of row
+    //      m = 4 (w RND + j) + l % 4 at k = 128 b + 32 s + 16 half + 4 gg with
+    //      gg = (l / 4) % 4, half = (l / 16) % 2, s = (l / 32) % 2 + 2 i (for
+    //      a packed W: 8 gg + 4 half).  Its hi and lo halves go to the 16-byte
+    //      operand slot (s, tile m / 16, lane 16 gg + m % 16), bytes 8 half ..
+    //      8 half + 7, of the hi and lo planes; the row's block exponent to
+    //      byte BB + 4 m.
+    constexpr int RND = INK ? 16 * MT / (4 * NWK) : 1;
+    static_assert(!INK || RND * 4 * NWK == 16 * MT, "whole groups of 4 rows per wave");
+    float4 areg[RND][2];
+    int sreg[RND][2][4];   // SHIFT: the units' 2^-kshift exponents (k >= K reads 0)
     // rows >= M fall outside the resource and read as zero; k past the
     // chunk end is zeroed when the block is stored
     const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(A, (uint32_t)((int64_t)M * lda * 4));
     const __amdgpu_buffer_rsrc_t ksrc = make_rsrc(kshift, SHIFT ? (uint32_t)K : 0u);
-    const int ur = 4 * wave + (lane & 3);
+    auto urow = [&](int j) { return 4 * (wave * RND + j) + (lane & 3); };
     const int ugg = (lane >> 2) & 3, uhalf = (lane >> 4) & 1, ust = (lane >> 5) & 1;
-    auto unit_k = [&](int b, int i) {
-        return k_begin + KA * b + 32 * (ust + 2 * i) + (PKW ? 8 * ugg + 4 * uhalf : 16 * uhalf + 4 * ugg);
+    auto unit_k = [&](int pb, int i) {   // pb: the block's place in the chunk
+        return k_begin + KA * pb + 32 * (ust + 2 * i) + (PKW ? 8 * ugg + 4 * uhalf : 16 * uhalf + 4 * ugg);
     };
     auto load_a = [&](int b) {
+        const int pb = pblock(b);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint32_t off = (uint32_t)(((int64_t)ur * lda + unit_k(b, i)) * 4);
-            if constexpr (AVEC) {
-                areg[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, off, 0, 0));
-            } else {
-                areg[i] = make_float4(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(arsrc, off, 0, 0)),
-                                      __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(arsrc, off + 4, 0, 0)),
-                                      __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(arsrc, off + 8, 0, 0)),
-                                      __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(arsrc, off + 12, 0, 0)));
-            }
-            if constexpr (SHIFT) {
-                const uint32_t k0 = (uint32_t)unit_k(b, i);
+        for (int j = 0; j < RND; ++j)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    sreg[i][j] = (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(ksrc, k0 + j, 0, 0);
+            for (int i = 0; i < 2; ++i) {
+                const uint32_t off = (uint32_t)(((int64_t)urow(j) * lda + unit_k(pb, i)) * 4);
+                if constexpr (AVEC) {
+                    areg[j][i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, off, 0, 0));
+                } else {
+                    areg[j][i] = make_float4(
+                        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(arsrc, off, 0, 0)),
+                        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(arsrc, off + 4, 0, 0)),
+                        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(arsrc, off + 8, 0, 0)),
+                        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(arsrc, off + 12, 0, 0)));
+                }
+                if constexpr (SHIFT) {
+                    const uint32_t k0 = (uint32_t)unit_k(pb, i);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        sreg[j][i][q] = (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(ksrc, k0 + q, 0, 0);
+                }
             }
-        }
     };
     auto store_a = [&](int b) {
         unsigned char* base = sa + (b & 1) * SB;
-        float v[2][4];
-        float mx = 0.0f;
+        const int pb = pblock(b);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int k = unit_k(b, i);
-            const float x[4] = {areg[i].x, areg[i].y, areg[i].z, areg[i].w};
+        for (int j = 0; j < RND; ++j) {
+            float v[2][4];
+            float mx = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[i][j] = k + j < k_end ? (SHIFT ? __builtin_ldexpf(x[j], -sreg[i][j]) : x[j]) : 0.0f;
-                mx = fmaxf(mx, __builtin_fabsf(v[i][j]));
+            for (int i = 0; i < 2; ++i) {
+                const int k = unit_k(pb, i);
+                const float x[4] = {areg[j][i].x, areg[j][i].y, areg[j][i].z, areg[j][i].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    v[i][q] = k + q < k_end ? (SHIFT ? __builtin_ldexpf(x[q], -sreg[j][i][q]) : x[q]) : 0.0f;
+                    mx = fmaxf(mx, __builtin_fabsf(v[i][q]));
+                }
             }
-        }
-        // the row's maximum over the block: the 16 lanes with the same l % 4
+            // the row's maximum over the block: the 16 lanes with the same l % 4
 #pragma unroll
-        for (int off = 4; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-        const int e = row_norm_exp(mx);
+            for (int off = 4; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            const int e = row_norm_exp(mx);
+            const int m = urow(j), t = m >> 4, r = m & 15;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            half4 h, l;
+            for (int i = 0; i < 2; ++i) {
+                half4 h, l;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                _Float16 hh, ll;
-                split_one(__builtin_ldexpf(v[i][j], e), hh, ll);
-                h[j] = hh;
-                l[j] = ll;
+                for (int q = 0; q < 4; ++q) {
+                    _Float16 hh, ll;
+                    split_one(__builtin_ldexpf(v[i][q], e), hh, ll);
+                    h[q] = hh;
+                    l[q] = ll;
+                }
+                const int off = (((ust + 2 * i) * MT + t) * 64 + 16 * ugg + r) * 16 + 8 * uhalf;
+                *reinterpret_cast<half4*>(base + off) = h;
+                *reinterpret_cast<half4*>(base + BB / 2 + off) = l;
             }
-            const int off = ((ust + 2 * i) * 64 + 16 * ugg + ur) * 16 + 8 * uhalf;
-            *reinterpret_cast<half4*>(base + off) = h;
-            *reinterpret_cast<half4*>(base + BB / 2 + off) = l;
+            if ((lane >> 2) == 0) *reinterpret_cast<int*>(base + BB + 4 * m) = e;
         }
-        if ((lane >> 2) == 0) *reinterpret_cast<int*>(base + BB + 4 * ur) = e;
     };
 
     // block images (MT > 1): wave w copies 1 KB pieces w, w + NWK, ... of the
@@ -304,11 +340,11 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
             const int piece = wave + NWK * i;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(pbrsrc, (lds_ptr)(sa + (b & 1) * SB + piece * 1024), 16,
                                                      (uint32_t)(lane * 16),
-                                                     (uint32_t)(blk0 + b) * (uint32_t)SB + piece * 1024u, 0, 0);
+                                                     (uint32_t)(blk0 + pblock(b)) * (uint32_t)SB + piece * 1024u, 0, 0);
         }
         if (wave == 0)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(pbrsrc, (lds_ptr)(sa + (b & 1) * SB + BB), 4,
-                                                     (uint32_t)(lane * 4), (uint32_t)(blk0 + b) * (uint32_t)SB + BB,
+                                                     (uint32_t)(lane * 4), (uint32_t)(blk0 + pblock(b)) * (uint32_t)SB + BB,
                                                      0, 0);
     };
 
@@ -386,7 +422,7 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
     WReg wr[PFW];
     if constexpr (INK) {
 #pragma unroll
-        for (int s = 0; s < PFW; ++s) load_w(min(s, nsteps - 1), wr[s]);
+        for (int s = 0; s < PFW; ++s) load_w(pstep(s), wr[s]);
         load_a(0);
         __builtin_amdgcn_sched_barrier(0);
         store_a(0);
@@ -394,7 +430,7 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
     } else {
         dma_block(0);
 #pragma unroll
-        for (int s = 0; s < PFW; ++s) load_w(min(s, nsteps - 1), wr[s]);
+        for (int s = 0; s < PFW; ++s) load_w(pstep(s), wr[s]);
         __builtin_amdgcn_sched_barrier(0);
         if (VEC) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS * PFW));   // block 0 landed; W still in flight
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -414,6 +450,7 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
         }
         __builtin_amdgcn_sched_barrier(0);
         const unsigned char* abuf = sa + (b & 1) * SB;
+        const int pb = pblock(b);
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -434,8 +471,8 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
                 split8(ra, rb, wh, wl);
                 wmax = absmax8(wmax, ra, rb);
             }
-            load_w(min(step + PFW, nsteps - 1), w);
-            if (step < nsteps) {
+            load_w(pstep(step + PFW), w);
+            if (pb * STEPS + s < nsteps) {
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {
                     const int off = ((s * MT + t) * 64 + lane) * 16;
@@ -641,18 +678,37 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
                              : nullptr;
     // activation units load as float4 when rows are 16-byte aligned
     const bool avec = (reinterpret_cast<uintptr_t>(A) & 15) == 0 && (lda & 3) == 0;
-#define HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW_)                                      \
-    hipLaunchKernelGGL((gemm_decode_kernel<MT_, VEC_, F16_, AV_, SH_, ONE_, NW_>), grid, dim3(64 * NW_), \
+    // With several row tiles the workgroups split their activation blocks
+    // themselves (no block images, no first kernel) when that work is light:
+    // one group of 4 rows per wave, or two over short chunks (at most 4
+    // blocks).  Measured (K, N, M = 32 / 64): it gains 1.4 - 4.1 us on those
+    // shapes, and loses 1.3 - 22 us with 2 groups over 14 - 16 blocks or 4
+    // groups per wave.  Both forms store the same split blocks: the results
+    // are identical.
+    const int rnd = 16 * mt / (4 * (wide ? 2 * NW : NW));
+    const bool ink = mt > 1 && !kshift && avec && (rnd == 1 || (rnd == 2 && plan.kchunk / KA <= 4));
+#define HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW_, INK_)                                \
+    hipLaunchKernelGGL((gemm_decode_kernel<MT_, VEC_, F16_, AV_, SH_, ONE_, NW_, INK_>), grid, dim3(64 * NW_), \
                        2 * img_bytes<MT_>(), s, A, lda, ablk, (uint32_t)plan.a_bytes, W, wrow_bytes, wexp, C, ldc, part, \
                        flags, epoch,                                                                          \
                        (int)M, (int)N, (int)K, (int)plan.kchunk, kshift, status)
+#define HEAL_DEC_LAUNCH_INK(MT_, VEC_, F16_, AV_, SH_, ONE_, NW_)                                      \
+    do {                                                                                                \
+        if constexpr (AV_ && !SH_) {                                                                    \
+            if (ink) {                                                                                  \
+                HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW_, true);                         \
+                break;                                                                                  \
+            }                                                                                           \
+        }                                                                                               \
+        HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW_, false);                                \
+    } while (0)
 #define HEAL_DEC_LAUNCH(MT_, VEC_, F16_, AV_, SH_, ONE_)                                                \
     do {                                                                                                \
         if constexpr (MT_ > 1) {                                                                        \
-            if (wide) HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, 2 * NW);                      \
-            else HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW);                               \
+            if (wide) HEAL_DEC_LAUNCH_INK(MT_, VEC_, F16_, AV_, SH_, ONE_, 2 * NW);                     \
+            else HEAL_DEC_LAUNCH_INK(MT_, VEC_, F16_, AV_, SH_, ONE_, NW);                              \
         } else {                                                                                        \
-            HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW);                                    \
+            HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW, false);                             \
         }                                                                                               \
     } while (0)
 #define HEAL_DEC_MAIN(MT_, VEC_, F16_, AV_, SH_)                                                        \
@@ -668,6 +724,7 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
 #define HEAL_DEC(MT_, SH_)                                                                              \
     do {                                                                                                \
         if constexpr ((MT_) > 1) {                                                                      \
+          if (!ink) {                                                                                   \
             const dim3 pgrid(16 * (MT_), (unsigned)((nablk * 32 + PREP_T - 1) / PREP_T));                \
             if (avec && packed)                                                                         \
                 hipLaunchKernelGGL((decode_prep_kernel<MT_, true, true>), pgrid, dim3(PREP_T), 0, s, A, lda, \
@@ -681,6 +738,7 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
             else                                                                                        \
                 hipLaunchKernelGGL((decode_prep_kernel<MT_, false, false>), pgrid, dim3(PREP_T), 0, s, A, lda, \
                                    (int)M, (int)K, nablk, kshift, ablk);                                \
+          }                                                                                             \
         }                                                                                               \
         if (wf16) {                                                                                     \
             if (packed) HEAL_DEC_AV(MT_, 2, true, SH_);                                                 \
@@ -704,6 +762,7 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
 #undef HEAL_DEC_AV
 #undef HEAL_DEC_MAIN
 #undef HEAL_DEC_LAUNCH
+#undef HEAL_DEC_LAUNCH_INK
 #undef HEAL_DEC_LAUNCH_NW
     return hipGetLastError();
 }
