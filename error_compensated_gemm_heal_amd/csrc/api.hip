@@ -88,7 +88,7 @@ const char* heal_status_str(heal_status s) {
     return "HEAL: unknown status";
 }
 
-int heal_version(void) { return (1 << 16) | (2 << 8); }
+int heal_version(void) { return (1 << 16) | (3 << 8); }
 
 heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo,
                            uint32_t* dev_status, void* stream) {

@@ -66,8 +66,9 @@ enum {
 
 /* Bits of the optional device status word. */
 enum {
-    HEAL_FLAG_F16_RANGE = 1u, /* an operand's 16-bit high part is inf: |x| >= 65520 (fp16),
-                                 or |x| beyond bf16's largest value (HEAL_BF16X3)        */
+    HEAL_FLAG_F16_RANGE = 1u, /* a value split as it is (not normalized) has an infinite
+                                 16-bit high part: |x| >= 65520 (fp16), or |x| beyond
+                                 bf16's largest value (HEAL_BF16X3)                     */
     HEAL_FLAG_SLOT_RANGE = 2u /* a K/V cache slot was >= num_slots: that row was skipped */
 };
 
@@ -108,10 +109,17 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  *
  * Both fp32 operands are split as in heal_split_f32.  The product expands to
  *   C = A_hi.B_hi + 2^-10 (A_hi.B_lo + A_lo.B_hi)
- * with the three 16-bit products on fp16 MFMA and fp32 accumulation (the
- * 2^-10 applied exactly, as a power of two, to the correction terms).  The
+ * with the three 16-bit products on fp16 MFMA and fp32 accumulation.  The
  * output stays fp32, so no downcast happens at the kernel boundary.  The
- * lo.lo term (2^-20) is dropped.  With HEAL_W_F16 the weight is already
+ * lo.lo term (2^-20) is dropped.  FP16's narrow range (the same paragraph:
+ * handled by targeted rescaling) is met by exact powers of two: before its
+ * split, each row of a packed operand, and each 128-wide k block of each
+ * activation row on the M <= 64 path, is multiplied by the 2^e that puts its
+ * largest magnitude in [2^14, 2^15), and the product is multiplied back by
+ * 2^-e in fp32.  The result does not depend on the activation's scale:
+ * scaling a row of A by a power of two scales that row of C by the same
+ * power, bit for bit, and the accuracy below holds for activations of any
+ * magnitude in fp32's normal range.  With HEAL_W_F16 the weight is already
  * 16-bit (exact in fp16, e.g. an FP16 checkpoint or a BF16 one converted
  * exactly), B_lo is zero and two products remain,
  *   C = A_hi.B + 2^-10 A_lo.B,
@@ -133,8 +141,8 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  * heal_pack_w with HEAL_BF16X3.  Every M runs the prefill kernel.
  * Accuracy: normwise error max_ij |C - C_exact| / (|a_i| |b_j|)
  * within 2x that of a naive FP32 GEMM and below 1e-5.  The summation order
- * depends on (M, N, K) but not on the data.  For M <= 64 (NK layout, K <
- * 2^23, neither operand packed) it also does not depend on M, so
+ * depends on (M, N, K) but not on the data.  For M <= 64 (NK layout or a
+ * packed W, A not packed, K < 2^23) it also does not depend on M, so
  * decode-sized results do not change with batch size.
  *
  *   A      device fp32, lda >= K, 4-byte aligned (rows that are 16-byte
@@ -166,11 +174,16 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  *          packed activation takes its shifts in heal_pack_w.
  *   workspace  device, >= heal_gemm_f32c_workspace(M, N, K, flags) bytes,
  *          256-byte aligned (NULL allowed when that size is 0)
- *   dev_status  device, nullable; HEAL_FLAG_F16_RANGE as in heal_split_f32.
+ *   dev_status  device, nullable.  HEAL_FLAG_F16_RANGE is set on the M <= 64
+ *          path when an fp32 W (streamed and split as it is, not
+ *          normalized) holds an element with |w| >= 65520: pack such a
+ *          weight (heal_pack_w normalizes its rows).  The normalized
+ *          operands never set it.
  * Layout note: in the M <= 64 case W streams from HBM row by row; rows whose
- * byte stride is a multiple of 16 KB (K = 4096 fp32, ldw = K) all start in
- * the same memory channel, and such a weight allocated with ldw = K + 64
- * runs ~14% faster (measured at K = 4096, N = 14336).
+ * byte stride is a multiple of 16 KB (K = 4096 fp32, ldw = K) start in the
+ * same memory channels.  The kernel visits k in a rotated order per group
+ * of rows where that helps, and a packed W pads its rows, which is faster
+ * still (K = 4096, N = 14336 at M = 1: 52.0 us streamed, 47.7 us packed).
  * Limits: M, N, K < 2^31.  K == 0 writes zeros.  In the M <= 64 case above,
  * ldw < 2^26 and lda < 2^24 (each 16-row slice of W, and A, are addressed
  * with 32-bit byte offsets), else HEAL_ERR_UNSUPPORTED.  The launches'
@@ -212,16 +225,25 @@ heal_status heal_gemm_f32c_noalloc(const float* A, int64_t lda, const void* W, i
  *  [GEMM]  Weights are fixed across calls, so their split can be done once
  *  and reused (HEAL_W_PACKED); an activation read by several GEMMs can be
  *  split once as well (HEAL_A_PACKED, with N := M rows of A and HEAL_W_NK).
- *  The packed form is internal and opaque: each row holds, for every 32-wide
- *  block of k, the 32 fp16 hi parts then the 32 fp16 lo parts (with
- *  HEAL_W_F16, the hi parts alone, half the bytes; with HEAL_BF16X3, the 32
- *  bf16 b0, then the 32 b1, then the 32 b2 of the three-way split).  Rows are
- *  padded to a multiple of 256 and k to a multiple of 32 with zeros.  An
- *  activation is packed without HEAL_W_F16 (with HEAL_BF16X3 when the GEMM
- *  uses that mode).  HEAL_BF16X3 takes fp32 input and no kshift.
+ *  The packed form is internal and opaque: each fp32 row r is multiplied by
+ *  the power of two 2^e[r] that puts its largest magnitude in [2^14, 2^15)
+ *  (e[r] = 0 for a zero row), then holds, for every 32-wide block of k, the
+ *  32 fp16 hi parts then the 32 fp16 residuals fp16(x' - hi), each at its
+ *  own scale (the residual equals heal_split_f32's lo / 2^10 wherever that
+ *  is a normal fp16).  With HEAL_W_F16 a row holds its binary16 values
+ *  alone, not normalized (e = 0), half the bytes; with HEAL_BF16X3, the 32
+ *  bf16 b0, then the 32 b1, then the 32 b2 of the three-way split, not
+ *  normalized.  Rows are padded to a multiple of 256 and k to a multiple of
+ *  32 with zeros; in the fp16 forms each row is followed by 256 unused bytes
+ *  (so rows are never a power-of-two number of bytes apart), and the int32
+ *  exponents of the padded rows follow the rows.  An activation is packed
+ *  without HEAL_W_F16 (with HEAL_BF16X3 when the GEMM uses that mode).
+ *  HEAL_BF16X3 takes fp32 input and no kshift.
  *   W      as in heal_gemm_f32c (flags HEAL_W_NK or HEAL_W_KN, optionally
  *          | HEAL_W_F16: binary16 input, its lo parts are zero), 4-byte
- *          aligned (2-byte with HEAL_W_F16)
+ *          aligned (2-byte with HEAL_W_F16).  Normalized rows cannot
+ *          overflow fp16; dev_status is set only by HEAL_BF16X3 (a value
+ *          beyond bf16's largest).
  *   kshift device int8 [K], nullable: element (r, k) is multiplied by
  *          2^-kshift[k] before its split (exact; an activation takes the
  *          shifts of heal_gemm_f32c's a_kshift, a weight their negation)
@@ -231,9 +253,10 @@ heal_status heal_pack_w(const void* W, int64_t ldw, int64_t N, int64_t K, uint32
                         const int8_t* kshift, void* packed, size_t packed_bytes,
                         uint32_t* dev_status, void* stream);
 
-/* Bytes of heal_pack_w's buffer for these flags: 4 per element of the padded
- * [N, K] (hi and lo), or 2 with HEAL_W_F16 (the hi parts alone: a 16-bit
- * weight's lo parts are zero and are not stored), or 6 with HEAL_BF16X3. */
+/* Bytes of heal_pack_w's buffer for these flags: per padded row, 4 bytes per
+ * element of the padded K (hi and residual), or 2 with HEAL_W_F16 (the hi
+ * parts alone: a 16-bit weight's residuals are zero and are not stored), plus
+ * 256, plus 4 for the row's exponent; or 6 per element with HEAL_BF16X3. */
 size_t heal_pack_w_bytes(int64_t N, int64_t K, uint32_t flags);
 
 /* ------------------------------------------------------------------------
