@@ -191,9 +191,11 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // WF16: W holds binary16 values, exact in fp16: its residual is zero, so each
 // step keeps two products, A_hi.W and A_lo.W (2^-10 applied in the fold).
 // AVEC: A rows 16-byte aligned, activation units load as one 16-byte load.
-// MT == 1 stages A itself (A, lda); MT > 1 copies the block images (Ablk).
-// SHIFT (MT == 1): element (m, k) of A is multiplied by 2^-kshift[k] before
-// its block maximum and split.  ONE: plain FP16, the A_hi.W_hi product alone.
+// MT == 1, or INKT: the workgroup stages and splits A itself (A, lda);
+// otherwise it copies the block images decode_prep_kernel wrote (Ablk).
+// SHIFT (splitting A itself): element (m, k) of A is multiplied by
+// 2^-kshift[k] before its block maximum and split.  ONE: plain FP16, the
+// A_hi.W_hi product alone.  NWK: waves per workgroup.
 template <int MT, int WM, bool WF16, bool AVEC, bool SHIFT, bool ONE, int NWK, bool INKT>
 __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __restrict__ A, int64_t lda,
                                                           const unsigned char* __restrict__ Ablk,

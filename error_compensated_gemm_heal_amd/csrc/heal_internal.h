@@ -198,12 +198,12 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
 // Whether the prefill kernel splits the k range of this shape in two.
 bool prefill_ksplit(int64_t M, int64_t N, int64_t K);
 
-// Decode path (M <= 64): fp32 W [N,K] streamed and split in registers, the
-// activation normalized per row and 128-wide k block (in the GEMM kernel up
-// to 16 rows, else by a first small kernel that writes the split blocks).
-// Workspace, each part 256-byte aligned: the split-K flags (c_bytes), the
-// split activation block images (a_bytes, M > 16), the split-K partials
-// (p_bytes).
+// Decode path (M <= 64): W [N,K] streamed (fp32 split in registers, or
+// binary16) or packed once, the activation normalized per row and 128-wide k
+// block (in the GEMM kernel up to 16 rows and where that work stays light,
+// else by a first small kernel that writes the split blocks).  Workspace,
+// each part 256-byte aligned: the split-K flags (c_bytes), the split
+// activation block images (a_bytes, M > 16), the split-K partials (p_bytes).
 struct DecodePlan {
     int splits;        // number of K chunks (fixed by N and K only)
     int64_t kchunk;    // reduction length of one chunk (multiple of 256)

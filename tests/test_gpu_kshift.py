@@ -91,6 +91,31 @@ def test_kshift_packed_activation_and_weight():
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("M", [1, 8, 17, 40, 64])
+def test_kshift_decode_packed_weight(M):
+    """Decode kernel on a weight packed once with the negated shifts: the shifted
+    call equals, bit for bit, the call on the host-prescaled activation with the
+    same packed weight (in-kernel split and split-pass forms), and meets the
+    tolerance against the binary64 product of the unscaled operands."""
+    K, N = 1000, 320
+    print(f"kshift decode packed M={M}", flush=True)
+    A, W, ks = _case(M, K, N, seed=7500 + M)
+    ksd = torch.from_numpy(ks).to(DEV)
+    Wp = heal.heal_pack_w(torch.from_numpy(W).to(DEV), kshift=-ksd)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    c1 = heal.heal_gemm_f32c(torch.from_numpy(A).to(DEV), Wp, a_kshift=ksd, dev_status=st).cpu().numpy()
+    assert st.item() == 0
+    As = (A.astype(np.float64) / _pow2(ks)[None, :]).astype(np.float32)
+    c2 = heal.heal_gemm_f32c(torch.from_numpy(As).to(DEV), Wp).cpu().numpy()
+    assert np.array_equal(c1, c2)
+    rows = np.arange(M)
+    C64 = oracle.gemm_f64_rows(A, W, rows)
+    C32 = oracle.gemm_f32_naive_rows(A, W, rows)
+    e_gpu = gemm_normwise_error(c1, C64, A, W, rows=rows)
+    e_naive = gemm_normwise_error(C32, C64, A, W, rows=rows)
+    assert e_gpu <= gemm_tolerance(e_naive, K)
+
+
 @pytest.mark.parametrize("dtype", [np.float32, np.float16])
 @pytest.mark.parametrize("layout", ["nk", "kn"])
 def test_scale_k_exact(dtype, layout):
