@@ -143,7 +143,8 @@ namespace {
 // the prefill kernel quantizes its output instead of storing C.
 heal_status gemm_impl(const float* A, int64_t lda, const void* W, int64_t ldw, float* C, int64_t ldc, int64_t M,
                       int64_t N, int64_t K, uint32_t flags, const int8_t* a_kshift, void* workspace,
-                      size_t workspace_bytes, uint32_t* dev_status, void* stream, const QkvDst* qkv) {
+                      size_t workspace_bytes, uint32_t* dev_status, void* stream, const QkvDst* qkv,
+                      unsigned long long* counters = nullptr) {
     if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return HEAL_ERR_SHAPE;
     if (flags & ~(uint32_t)(HEAL_W_KN | HEAL_W_PACKED | HEAL_A_PACKED | HEAL_W_F16 | HEAL_ONE_PRODUCT | HEAL_BF16X3))
         return HEAL_ERR_UNSUPPORTED;
@@ -186,9 +187,16 @@ heal_status gemm_impl(const float* A, int64_t lda, const void* W, int64_t ldw, f
     if (use_decode(M, K, flags)) {
         if ((!packed && ldw >= kMaxDecodeLdw) || lda >= kMaxDecodeLda) return HEAL_ERR_UNSUPPORTED;
         const DecodePlan p = decode_plan(M, N, K);
+        // the epoch of a captured call would be replayed with the graph, and
+        // a replay would take the previous one's flags for its own
+        if (p.splits > 1 && !counters) {
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            if (hipStreamIsCapturing(s, &cs) != hipSuccess) return HEAL_ERR_HIP;
+            if (cs != hipStreamCaptureStatusNone) return HEAL_ERR_UNSUPPORTED;
+        }
         unsigned char* ws = static_cast<unsigned char*>(workspace);
         return hip_status(launch_gemm_decode(A, lda, a_kshift, W, wf16, packed, one, ldw, C, ldc, M, N, K, ws, p,
-                                             next_epoch(), dev_status, s));
+                                             next_epoch(), counters, dev_status, s));
     }
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     const void* apk = A;
@@ -227,6 +235,14 @@ heal_status gemm_impl(const float* A, int64_t lda, const void* W, int64_t ldw, f
     return hip_status(launch_gemm_prefill(apk, bpk, one ? 1 : (wf16 ? 2 : 3), wf16, C, ldc, M, N, K, s, qkv, a_hi));
 }
 }  // namespace
+
+heal_status heal::gemm_f32c_counters(const float* A, int64_t lda, const void* W, int64_t ldw, float* C,
+                                     int64_t ldc, int64_t M, int64_t N, int64_t K, uint32_t flags,
+                                     const int8_t* a_kshift, void* workspace, size_t workspace_bytes,
+                                     unsigned long long* counters, uint32_t* dev_status, void* stream) {
+    return gemm_impl(A, lda, W, ldw, C, ldc, M, N, K, flags, a_kshift, workspace, workspace_bytes, dev_status,
+                     stream, nullptr, counters);
+}
 
 extern "C" {
 

@@ -567,25 +567,44 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
             }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    // then the workgroup's flag for (row block, chunk) := this call's epoch,
-    // also written through and completed; then it reads the flags of all
-    // chunks of its row block.  The workgroup whose flag completes last sees
-    // every flag set, so at least one workgroup sums; any other that sees
-    // them all too writes the same values.  A flag from an earlier call (or
-    // whatever the workspace held) differs from this call's epoch.
     __shared__ int missing;
-    unsigned long long* flags = flag_base + (int64_t)blockIdx.x * nsplit;
     if (tid == 0) missing = 0;
     __syncthreads();
-    if (tid == 0) {
-        __hip_atomic_store(flags + split, (unsigned long long)epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    if (epoch == 0) {
+        // counter form (a zeroed array of one counter per row block, which
+        // every call leaves zeroed: the same arguments can be replayed, as
+        // from a captured graph): the workgroup counts itself in once its
+        // partials are stored; the one that counts last sums and puts the
+        // counter back to zero
+        if (tid == 0) {
+            unsigned long long* cnt = flag_base + blockIdx.x;
+            const unsigned long long old =
+                __hip_atomic_fetch_add(cnt, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (old + 1 == (unsigned long long)nsplit)
+                __hip_atomic_store(cnt, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                missing = 1;
+        }
+    } else {
+        // epoch form: the workgroup's flag for (row block, chunk) := this
+        // call's epoch, also written through and completed; then it reads the
+        // flags of all chunks of its row block.  The workgroup whose flag
+        // completes last sees every flag set, so at least one workgroup sums;
+        // any other that sees them all too writes the same values.  A flag
+        // from an earlier call (or whatever the workspace held) differs from
+        // this call's epoch.
+        unsigned long long* flags = flag_base + (int64_t)blockIdx.x * nsplit;
+        if (tid == 0) {
+            __hip_atomic_store(flags + split, (unsigned long long)epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+        __syncthreads();
+        bool miss = false;
+        for (int j = tid; j < nsplit; j += 64 * NWK)
+            miss |= __hip_atomic_load(flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
+                    (unsigned long long)epoch;
+        if (__builtin_amdgcn_ballot_w64(miss) && lane == 0) missing = 1;
     }
-    __syncthreads();
-    bool miss = false;
-    for (int j = tid; j < nsplit; j += 64 * NWK)
-        miss |= __hip_atomic_load(flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (unsigned long long)epoch;
-    if (__builtin_amdgcn_ballot_w64(miss) && lane == 0) missing = 1;
     __syncthreads();
     if (missing || !row_ok) return;
     // a workgroup that saw every chunk done: C = sum over chunks in chunk order
@@ -655,12 +674,15 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift, const void* W, bool wf16,
                               bool packed, bool one, int64_t ldw, float* C, int64_t ldc, int64_t M, int64_t N,
-                              int64_t K, void* workspace, const DecodePlan& plan, uint64_t epoch, uint32_t* status,
-                              hipStream_t s) {
+                              int64_t K, void* workspace, const DecodePlan& plan, uint64_t epoch,
+                              unsigned long long* counters, uint32_t* status, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
-    if (M > 64 || K == 0) return hipErrorInvalidValue;
+    if (M > 64 || K == 0 || (!counters && epoch == 0)) return hipErrorInvalidValue;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    unsigned long long* flags = reinterpret_cast<unsigned long long*>(ws);
+    // split-K completion: the epoch flags at the start of the workspace, or
+    // the caller's zeroed counters (epoch 0 selects them in the kernel)
+    unsigned long long* flags = counters ? counters : reinterpret_cast<unsigned long long*>(ws);
+    if (counters) epoch = 0;
     unsigned char* ablk = ws + (plan.c_bytes + 255) / 256 * 256;
     float* part = reinterpret_cast<float*>(ablk + (plan.a_bytes + 255) / 256 * 256);
     const int nablk = (int)((K + KA - 1) / KA);

@@ -220,15 +220,25 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K);
 // epoch: a number no earlier call in the process used (the split-K counters
 // tell this call's arrivals from stale contents by it).
 // packed: W is a heal_pack_w buffer for (N, K) (hi-only when wf16); ldw is
-// then ignored.
+// then ignored.  Split-K completion: with counters == nullptr, flags in the
+// workspace compared against `epoch` (a value no earlier call on this
+// workspace used, never 0); otherwise `counters`, one 8-byte counter per
+// workgroup row group (ceil(N / 64) suffice), zero on entry and left zero
+// (the form a replayed graph needs).
 hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift, const void* W, bool wf16,
                               bool packed, bool one, int64_t ldw, float* C, int64_t ldc, int64_t M, int64_t N,
-                              int64_t K, void* workspace, const DecodePlan& plan, uint64_t epoch, uint32_t* status,
-                              hipStream_t s);
+                              int64_t K, void* workspace, const DecodePlan& plan, uint64_t epoch,
+                              unsigned long long* counters, uint32_t* status, hipStream_t s);
 // A fresh call epoch (48 bits, never 0; thread-safe).
 uint64_t next_epoch();
 // Whether heal_gemm_f32c runs this shape and these flags on the decode kernel.
 bool decode_path(int64_t M, int64_t K, uint32_t flags);
+// heal_gemm_f32c on the decode path with the split-K counters of
+// launch_gemm_decode (zero on entry, left zero) instead of epoch flags.
+heal_status gemm_f32c_counters(const float* A, int64_t lda, const void* W, int64_t ldw, float* C, int64_t ldc,
+                               int64_t M, int64_t N, int64_t K, uint32_t flags, const int8_t* a_kshift,
+                               void* workspace, size_t workspace_bytes, unsigned long long* counters,
+                               uint32_t* dev_status, void* stream);
 
 int64_t attn_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D);
 // Causal self-attention of a prompt: q [B, T, Hq, D], k/v [B, T, Hkv, D] INT16

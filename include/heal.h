@@ -184,6 +184,12 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  * same memory channels.  The kernel visits k in a rotated order per group
  * of rows where that helps, and a packed W pads its rows, which is faster
  * still (K = 4096, N = 14336 at M = 1: 52.0 us streamed, 47.7 us packed).
+ * Graph capture: on the M <= 64 path with a k split (chosen from N and K),
+ * the call marks its split-K flags in the workspace with a per-call value
+ * taken on the host, which a captured graph would replay; under stream
+ * capture such a call returns HEAL_ERR_UNSUPPORTED before any launch.
+ * heal_gemm_f32c_noalloc captures and replays correctly.  Other shapes
+ * capture normally.
  * Limits: M, N, K < 2^31.  K == 0 writes zeros.  In the M <= 64 case above,
  * ldw < 2^26 and lda < 2^24 (each 16-row slice of W, and A, are addressed
  * with 32-bit byte offsets), else HEAL_ERR_UNSUPPORTED.  The launches'
@@ -206,14 +212,17 @@ size_t heal_gemm_f32c_workspace(int64_t M, int64_t N, int64_t K, uint32_t flags)
  *  Same arguments, results and kernels as heal_gemm_f32c (bit for bit), on
  *  the decode path only: M <= 64, W fp32 or binary16 (HEAL_W_F16) in the
  *  [N, K] layout or packed by heal_pack_w (HEAL_W_PACKED), A not packed,
- *  not HEAL_BF16X3, K < 2^23 (else HEAL_ERR_UNSUPPORTED).  Its scratch memory is a 16 MiB array of device
- *  memory that the library owns, one per GPU, held until the process ends;
- *  shapes whose heal_gemm_f32c_workspace exceeds 16 MiB get
- *  HEAL_ERR_WORKSPACE (the Llama-3-8B-like decode layers need at most
- *  12.1 MB at M = 64).  No call allocates or frees memory.  The array keeps
- *  the last call's contents; nothing in it needs clearing.  Calls that
- *  overlap on one GPU (other streams or threads) share the array and race:
- *  serialize them.
+ *  not HEAL_BF16X3, K < 2^23, N <= 2^19 (else HEAL_ERR_UNSUPPORTED).  Its
+ *  scratch memory is a 16 MiB array of device memory that the library owns,
+ *  one per GPU, held until the process ends: 64 KiB of split-K counters,
+ *  then the workspace; shapes whose heal_gemm_f32c_workspace exceeds
+ *  16 MiB - 64 KiB get HEAL_ERR_WORKSPACE (the Llama-3-8B-like decode
+ *  layers need at most 12.1 MB at M = 64).  No call allocates or frees
+ *  memory.  The counters start at zero and every call leaves them zero, so
+ *  the call can be captured into a HIP graph and replayed (it records
+ *  kernel launches only); nothing in the array needs clearing.  Calls that
+ *  overlap on one GPU (other streams or threads, or replays on several
+ *  streams) share the array and race: serialize them.
  * ------------------------------------------------------------------------ */
 heal_status heal_gemm_f32c_noalloc(const float* A, int64_t lda, const void* W, int64_t ldw,
                                    float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,

@@ -106,6 +106,7 @@ def test_gemm_noalloc_validation():
     assert f(*args(flags=heal.HEAL_A_PACKED)) == UNSUP
     assert f(*args(flags=heal.HEAL_W_KN)) == UNSUP
     assert f(*args(flags=heal.HEAL_BF16X3)) == UNSUP
+    assert f(*args(N=(1 << 19) + 64)) == UNSUP           # one split-K counter per 64 rows of W, 8192 at most
     assert heal.heal_gemm_f32c_workspace(64, 256, 1 << 20, 0) > 16 << 20
     assert f(*args(M=64, N=256, K=1 << 20)) == WS       # split blocks past 16 MiB
     assert heal.heal_gemm_f32c_workspace(64, 4096, 14336, 0) <= 16 << 20   # the Llama-3-8B-like layers fit

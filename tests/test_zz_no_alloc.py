@@ -54,3 +54,34 @@ def test_noalloc_binding_and_limits():
     C = torch.empty((8, 256), device=DEV)
     heal.heal_gemm_f32c_noalloc(Ad, Wd, C)
     assert np.array_equal(C.cpu().numpy(), heal.heal_gemm_f32c(Ad, Wd).cpu().numpy())
+
+
+@pytest.mark.parametrize("M,K,N,form", [(8, 4096, 1024, "fp32"), (40, 4096, 4096, "fp32"),
+                                        (64, 14336, 4096, "packed"), (1, 4096, 14336, "fp16")])
+def test_noalloc_graph_replays(M, K, N, form):
+    """Captured once in a HIP graph and replayed with new activations (copied into
+    the captured input between replays): every replay equals the workspace entry
+    point's eager result, bit for bit.  The split-K counters are left zero by each
+    call, so each replay starts from the state the capture saw."""
+    print(f"noalloc graph M={M} K={K} N={N} {form}", flush=True)
+    A0, W = WL.decode_gemm(M, K, N, seed=20 + M)
+    Wd = torch.from_numpy(W.astype(np.float16) if form == "fp16" else W).to(DEV)
+    if form == "packed":
+        Wd = heal.heal_pack_w(Wd)
+    Ad = torch.from_numpy(A0).to(DEV)
+    C = torch.full((M, N), float("nan"), device=DEV)
+    heal.heal_gemm_f32c_noalloc(Ad, Wd, C)          # eager first call: the scratch array's address
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        heal.heal_gemm_f32c_noalloc(Ad, Wd, C)
+    for r in range(3):
+        Ar, _ = WL.decode_gemm(M, K, N, seed=30 + 7 * r + M)
+        Ad.copy_(torch.from_numpy(Ar).to(DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = C.cpu().numpy()
+        ref = heal.heal_gemm_f32c(Ad, Wd).cpu().numpy()
+        torch.cuda.synchronize()
+        assert np.array_equal(got, ref), r
