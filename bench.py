@@ -4,6 +4,8 @@
 One step is one pass over every step of the path, each on its synthetic
 workload (inputs resident in HBM before timing starts):
 
+  smoke    the small configuration: a 16 x 256 x 256 compensated GEMM and the INT16
+           quant of 16 x 256 values, two calls (launch-bound: reported as time per call)
   split    activation split of the two prefill GEMMs (fp32 -> packed fp16 hi/lo)
   prefill  compensated GEMM, M=2048 tokens, (K,N) = (4096,14336) and (14336,4096),
            weights split once beforehand (as deployed: weights are fixed)
@@ -193,6 +195,15 @@ def build_workload(rows_sel):
         W["attn_prefill"] = dict(args=(q, qs, k, ks, v, vs), out=out, B=B, T=T, Hq=Hq, D=D)
         log(f"[bench] prefill attention inputs ready ({time.time() - t0:.1f}s)")
 
+    if "smoke" in rows_sel:
+        A, Wt = WL.smoke_gemm()
+        X = WL.smoke_quant()
+        W["smoke"] = dict(A=torch.from_numpy(A).to(dev), W=torch.from_numpy(Wt).to(dev),
+                          C=torch.empty((A.shape[0], Wt.shape[0]), dtype=torch.float32, device=dev),
+                          X=torch.from_numpy(X).to(dev),
+                          codes=torch.empty(X.shape, dtype=torch.int16, device=dev),
+                          scales=torch.empty(X.shape[:-1], dtype=torch.float32, device=dev))
+
     if "attn" in rows_sel:
         B, T, Hq, Hkv, D = 16, 8192, 32, 8, 128
         qf, kf, vf = WL.attention_fp32(B, T, Hq, Hkv, D, seed=5000)
@@ -303,6 +314,14 @@ def make_rows(W):
         pairs = a["B"] * a["T"] * (a["T"] + 1) // 2
         rows.append(("attn_prefill", lambda a=a: heal.heal_attn_prefill_i16(*a["args"], out=a["out"]),
                      4.0 * a["D"] * a["Hq"] * pairs, "flop"))
+    if "smoke" in W:
+        sm = W["smoke"]
+
+        def run_smoke():
+            heal.heal_gemm_f32c(sm["A"], sm["W"], C=sm["C"])
+            heal.heal_qkv_quant_i16(sm["X"], sm["codes"], sm["scales"])
+
+        rows.append(("smoke", run_smoke, 2, "call"))   # two calls: latency only
     if "attn" in W:
         a = W["attn"]
         B, T, Hq, Hkv, D = a["B"], a["T"], a["Hq"], a["Hkv"], a["D"]
@@ -380,23 +399,47 @@ def _quant_rate(seconds):
     return out[0], out[1], f"{tokens} tokens x 48 heads x 128 ({n / 1e6:.1f} M elements)"
 
 
+def _attn_rate(seconds):
+    """The oracle's binary64 decode attention on a batch slice of the decode-attention
+    workload (T = 8192, 32 / 8 heads of 128): (B/s, sample text), bytes counted as the
+    GPU row counts them (codes and scales of K and V, q in, o out)."""
+    import heal_workloads as WL
+    import oracle
+    B, T, Hq, Hkv, D = 2, 8192, 32, 8, 128
+    qf, kf, vf = WL.attention_fp32(B, T, Hq, Hkv, D, seed=5000)
+    ins = oracle.quant_i16(qf) + oracle.quant_i16(kf) + oracle.quant_i16(vf)
+    del qf, kf, vf
+    nbytes = 2 * B * T * Hkv * D * 2 + 2 * B * T * Hkv * 4 + B * Hq * D * 2 + B * Hq * 4 + B * Hq * D * 4
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.attn_decode_f64(*ins)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    return nbytes * reps / dt, f"{B} of 16 sequences of T={T}, {Hq}/{Hkv} heads ({reps} passes, {dt:.1f} s)"
+
+
 def cpu_baseline(seconds):
     """The oracle, as it stands, on bounded samples of the benchmark's workloads, on
     all host threads and on one: `value` is its FP64-accumulated GEMM on row samples
     of the two prefill shapes (the metric's first half, the GPU `value`'s unit);
-    `parts` adds the naive FP32 GEMM and the INT16 quant and dequant (the metric's
-    second half, GB/s), and the one-thread rates."""
+    `parts` adds the naive FP32 GEMM, the INT16 quant and dequant (the metric's
+    second half, GB/s), the binary64 decode attention (GB/s of the cache it
+    reads), and the one-thread rates."""
     import oracle
     nth = oracle.num_threads()
-    share = seconds / 6
+    share = seconds / 7
     parts = {}
     f64, s64 = _gemm_rows_rate(oracle.gemm_f64_rows, 2 * share, nth)
     f32, s32 = _gemm_rows_rate(oracle.gemm_f32_naive_rows, share, nth)
     q, dq, sq = _quant_rate(share)
+    at, sat = _attn_rate(share)
     parts["gemm_f64_TFLOPs"] = f64 / 1e12
     parts["gemm_f32_naive_TFLOPs"] = f32 / 1e12
     parts["quant_GBps"] = q / 1e9
     parts["dequant_GBps"] = dq / 1e9
+    parts["attn_decode_f64_GBps"] = at / 1e9
     oracle.set_num_threads(1)
     try:
         f64_1, s64_1 = _gemm_rows_rate(oracle.gemm_f64_rows, share, 1)
@@ -409,7 +452,7 @@ def cpu_baseline(seconds):
     return {"value": f64 / 1e12, "unit": "TFLOP/s", "cores": nth, "kind": "oracle",
             "cpu_model": _cpu_model(), "parts": parts,
             "sample": f"the oracle on {nth} threads and on 1: FP64 GEMM on {s64}; naive FP32 GEMM on {s32}; "
-                      f"quant/dequant of {sq}; one thread: FP64 GEMM on {s64_1}"}
+                      f"quant/dequant of {sq}; decode attention on {sat}; one thread: FP64 GEMM on {s64_1}"}
 
 
 def calibrate(torch, heal):
@@ -455,7 +498,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--rows", default="split,prefill,prefill_w16,prefill_1p,prefill_bf16x3,decode,decode_w16,"
+    ap.add_argument("--rows", default="smoke,split,prefill,prefill_w16,prefill_1p,prefill_bf16x3,decode,decode_w16,"
                                       "decode_packed,decode_w16_packed,decode_kshift,"
                                       "qkv_proj,quant,dequant,attn_prefill,attn",
                     help="comma-separated subset of rows to run (profiling)")
@@ -538,6 +581,8 @@ def main():
         rate = work / (ms * 1e-3)
         if unit == "flop":
             per_row[name] = {"ms": ms, "ms_median": med, "TFLOPs": rate / 1e12}
+        elif unit == "call":
+            per_row[name] = {"ms": ms, "ms_median": med, "us_per_call": ms * 1e3 / work}
         else:
             per_row[name] = {"ms": ms, "ms_median": med, "GBps": rate / 1e9, "hbm_frac": rate / 1e9 / PEAK_HBM_GBPS}
 
