@@ -361,9 +361,7 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
 #undef HEAL_SLOT_READS
 #undef HEAL_DMA_TILE
 
-    // ---- epilogue: bounds-checked store (or atomic add of one k half) -------
-    const int row0 = tm * BM + wm * WM + (lane >> 5) * 4;
-    const int col0 = tn * BN + wn * WN + (lane & 31);
+    // ---- epilogue: store (or atomic add of one k half) ----------------------
     // undo the row normalization: output (row, col) times 2^-(ea[row] + eb[col]),
     // exact barring fp32 underflow; the exponents come from LDS
     if constexpr (!X3) {
@@ -461,6 +459,33 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
         if (bad_slot && qkv.status) atomicOr(qkv.status, (uint32_t)HEAL_FLAG_SLOT_RANGE);
         return;
     }
+    const int ln = __lane_id();   // recomputed (mbcnt): no lane value is held over the main loop
+    if ((tm + 1) * BM <= M && (tn + 1) * BN <= N && ldc < ((int64_t)1 << 26)) {
+        // a whole tile (block-uniform): no bounds checks.  Each store is a
+        // wave-uniform row address (the wave tile's corner plus r ldc, scalar
+        // arithmetic), the lane's 32-bit byte offset (its row in the group of
+        // four, its column) and the 32-column tile as an immediate offset.
+        char* const wbase = reinterpret_cast<char*>(C + (int64_t)(tm * BM + wm * WM) * ldc + (tn * BN + wn * WN));
+        const uint32_t loff = (uint32_t)(((ln >> 5) * 4 * (int)ldc + (ln & 31)) * 4);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                char* const rb = wbase + (int64_t)(i * 32 + (e >> 2) * 8 + (e & 3)) * ldc * 4;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    float* const dst = reinterpret_cast<float*>(rb + loff + j * 128);
+                    if (SPLIT)
+                        unsafeAtomicAdd(dst, acc[i][j][e]);
+                    else
+                        *dst = acc[i][j][e];
+                }
+            }
+        return;
+    }
+    // a partial tile: every element checked
+    const int row0 = tm * BM + wm * WM + (ln >> 5) * 4;
+    const int col0 = tn * BN + wn * WN + (ln & 31);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
