@@ -434,8 +434,7 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
                                                                   (r & 127) * QKV_LD + c4);
                 float m = fmaxf(fmaxf(__builtin_fabsf(x.x), __builtin_fabsf(x.y)),
                                 fmaxf(__builtin_fabsf(x.z), __builtin_fabsf(x.w)));
-#pragma unroll
-                for (int off = 16; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 32));
+                m = max_half(m);
                 if (tm * BM + rl >= M) continue;
                 int64_t dst_row = tm * BM + rl;   // Q: the token row
                 if (!is_q) {

@@ -71,6 +71,39 @@ __device__ __forceinline__ bool f16_out_of_range4(const float4& v) {
                  fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w))) >= 65520.0f;
 }
 
+// Lane reductions with no LDS-pipe instruction (all lanes active).  DPP
+// row_ror:N hands lane i of each 16-lane row the value of lane (i - N) mod 16
+// of the same row; v_permlane16_swap of x with itself exchanges rows 0 <-> 1
+// and 2 <-> 3, v_permlane32_swap the two halves, so one of the two results
+// holds the partner lane's value.  The swap results are copied into scalars
+// before they are reinterpreted: this compiler's __builtin_bit_cast of a
+// vector element reads element 0.
+template <int N>
+__device__ __forceinline__ float max_row_ror(float x) {
+    return fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + N,
+                                                                          0xF, 0xF, false)));
+}
+__device__ __forceinline__ float max_swap16(float x) {   // with lane ^ 16
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const uint32_t a0 = a[0], a1 = a[1];
+    return fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+}
+__device__ __forceinline__ float max_swap32(float x) {   // with lane ^ 32
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const uint32_t a0 = a[0], a1 = a[1];
+    return fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+}
+// over the 16 lanes of the wave that share lane % 4
+__device__ __forceinline__ float max16_mod4(float x) {
+    return max_swap32(max_swap16(max_row_ror<8>(max_row_ror<4>(x))));
+}
+// over the 32 lanes of each half wave
+__device__ __forceinline__ float max_half(float x) {
+    return max_swap16(max_row_ror<8>(max_row_ror<4>(max_row_ror<2>(max_row_ror<1>(x)))));
+}
+
 // ---- packed dual-FP16 operand layout used by the prefill GEMM --------------
 // Row r of a packed operand is normalized (row_norm_exp) and holds, for each
 // 32-wide block kb of the reduction dimension, 32 fp16 hi parts followed by
