@@ -363,10 +363,12 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
 
     // ---- epilogue: store (or atomic add of one k half) ----------------------
     // undo the row normalization: output (row, col) times 2^-(ea[row] + eb[col]),
-    // exact barring fp32 underflow; the exponents come from LDS
-    if constexpr (!X3) {
+    // exact barring fp32 underflow; the exponents come from LDS.  (The INT16
+    // epilogue scales each value as it stages it.)
+    const int ln = __lane_id();   // recomputed (mbcnt): no lane value is held over the main loop
+    if constexpr (!X3 && !QKV) {
         __syncthreads();   // the exponents' LDS writes are visible (also when the loop had one tile)
-        const int rl = wm * WM + (lane >> 5) * 4, cl = wn * WN + (lane & 31);
+        const int rl = wm * WM + (ln >> 5) * 4, cl = wn * WN + (ln & 31);
         int ebc[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) ebc[j] = exp_lds[256 + cl + j * 32];
@@ -393,7 +395,13 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
         // quantize those 256 (token, head) rows, one row per half wave (32
         // lanes x 4 values), with the standalone quantizer's arithmetic.  The
         // block's token slots are staged once.
-        __syncthreads();
+        __syncthreads();   // also makes the exponents' LDS writes visible
+        const int rl = wm * WM + (ln >> 5) * 4, cl = wn * WN + (ln & 31);
+        int ebc[TN] = {};
+        if constexpr (!X3) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) ebc[j] = exp_lds[256 + cl + j * 32];
+        }
         float* tile = reinterpret_cast<float*>(smem);
         int64_t* slot_lds = reinterpret_cast<int64_t*>(smem + QKV_SLOTS_OFF);
         {
@@ -408,14 +416,27 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
             if (wn == p) {
                 float* t = tile + wm * QKV_TILE_FLOATS;
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
+                for (int i = 0; i < TM; ++i) {
+                    int er[16] = {};
+                    if constexpr (!X3) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int4 v = *reinterpret_cast<const int4*>(exp_lds + rl + i * 32 + q * 8);
+                            er[4 * q + 0] = v.x;
+                            er[4 * q + 1] = v.y;
+                            er[4 * q + 2] = v.z;
+                            er[4 * q + 3] = v.w;
+                        }
+                    }
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
 #pragma unroll
                         for (int e = 0; e < 16; ++e) {
-                            const int rr = (lane >> 5) * 4 + i * 32 + (e >> 2) * 8 + (e & 3);
-                            t[rr * QKV_LD + j * 32 + (lane & 31)] = acc[i][j][e];
+                            const int rr = (ln >> 5) * 4 + i * 32 + (e >> 2) * 8 + (e & 3);
+                            t[rr * QKV_LD + j * 32 + (ln & 31)] =
+                                X3 ? acc[i][j][e] : __builtin_ldexpf(acc[i][j][e], -(er[e] + ebc[j]));
                         }
+                }
             }
             __syncthreads();
             const int hd = colp / 128;
@@ -425,10 +446,10 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
             int16_t* const cbase = is_q ? qkv.qc : (is_k ? qkv.kc : qkv.vc);
             float* const sbase = is_q ? qkv.qs : (is_k ? qkv.ks : qkv.vs);
             const int hcount = is_q ? qkv.hq : qkv.hkv;
-            const int c4 = 4 * (lane & 31);
+            const int c4 = 4 * (ln & 31);
 #pragma unroll 8
             for (int it = 0; it < 32; ++it) {
-                const int r = wave * 64 + it * 2 + (lane >> 5);   // 0..255: tile r / 128, row r % 128
+                const int r = wave * 64 + it * 2 + (ln >> 5);   // 0..255: tile r / 128, row r % 128
                 const int rl = r;                                 // row in the block (tile 0: wm 0, tile 1: wm 1)
                 const float4 x = *reinterpret_cast<const float4*>(tile + (r >> 7) * QKV_TILE_FLOATS +
                                                                   (r & 127) * QKV_LD + c4);
@@ -443,7 +464,7 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
                     if (dst_row >= qkv.num_slots) { bad_slot = true; continue; }
                 }
                 const int64_t idx = dst_row * hcount + hk;
-                if ((lane & 31) == 0) sbase[idx] = (m == 0.0f) ? 0.0f : __fdiv_rn(m, 32767.0f);
+                if ((ln & 31) == 0) sbase[idx] = (m == 0.0f) ? 0.0f : __fdiv_rn(m, 32767.0f);
                 // a zero row (m = 0, all x = 0) divides by 1 and gives zero codes
                 const float dm = (m == 0.0f) ? 1.0f : m;
                 short4 q;
@@ -458,7 +479,6 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
         if (bad_slot && qkv.status) atomicOr(qkv.status, (uint32_t)HEAL_FLAG_SLOT_RANGE);
         return;
     }
-    const int ln = __lane_id();   // recomputed (mbcnt): no lane value is held over the main loop
     if ((tm + 1) * BM <= M && (tn + 1) * BN <= N && ldc < ((int64_t)1 << 26)) {
         // a whole tile (block-uniform): no bounds checks.  Each store is a
         // wave-uniform row address (the wave tile's corner plus r ldc, scalar
