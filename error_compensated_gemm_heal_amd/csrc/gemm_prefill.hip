@@ -123,16 +123,19 @@ __device__ __forceinline__ void mfma32(const half8& a, const half8& b, floatx16&
 
 // NP: products per k step.  3: A_hi.B_hi + A_hi.B_res + A_res.B_hi;
 // 2: B is a 16-bit weight (no residual), A_hi.B + A_res.B;
-// 1: plain FP16, A_hi.B_hi.  BHI: B is in the hi-only packed form.  X3: the
-// BF16 three-way mode (NP = 1 over the virtual reduction, single planes).
-// QKV: the INT16 epilogue for heads of 128 outputs (not with SPLIT).  AH: A
-// is in the hi-only form (the one-product mode with an A packed per call).
+// 1: plain FP16, A_hi.B_hi.  BHI / AH: B / A is staged as its hi parts alone
+// (64-byte LDS rows): a 16-bit weight, and both operands in the one-product
+// mode.  The packed source rows hold a_kstep / b_kstep bytes per 32-wide k
+// block (128: hi and residual; 64: hi-only packing), so the one-product mode
+// copies just the hi half of hi/residual rows.  X3: the BF16 three-way mode
+// (NP = 1 over the virtual reduction, single planes).  QKV: the INT16
+// epilogue for heads of 128 outputs (not with SPLIT).
 template <bool SPLIT, int NP, bool BHI, bool X3, bool QKV, bool AH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned char* __restrict__ Bpk,
                          const int* __restrict__ ea, const int* __restrict__ eb,
                          float* __restrict__ C, int64_t ldc, int M, int N, int Kp,
-                         int tiles_m, int tiles_n, QkvDst qkv) {
+                         int tiles_m, int tiles_n, uint32_t a_kstep, uint32_t b_kstep, QkvDst qkv) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     static_assert(!BHI || NP < 3, "a hi-only B has no lo planes");
     static_assert(!X3 || (NP == 1 && BHI), "the three-way mode is one product over single planes");
@@ -168,8 +171,8 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
     const int wm = wave & 1, wn = wave >> 1;
     // HBM row bytes: Kp hi + Kp lo fp16; Kp fp16 (hi-only); 3 Kp bf16 (X3)
     // packed row strides: 3 Kp bf16 (X3, no pad), or the padded hi-only / hi-res rows
-    const uint32_t rowbytes = X3 ? (uint32_t)Kp * 6u : (uint32_t)(AH ? pack_row_bytes_hi(Kp) : pack_row_bytes(Kp));
-    const uint32_t browbytes = X3 ? (uint32_t)Kp * 6u : (uint32_t)(BHI ? pack_row_bytes_hi(Kp) : pack_row_bytes(Kp));
+    const uint32_t rowbytes = X3 ? (uint32_t)Kp * 6u : (uint32_t)(Kp / 32) * a_kstep + (uint32_t)kPackRowPad;
+    const uint32_t browbytes = X3 ? (uint32_t)Kp * 6u : (uint32_t)(Kp / 32) * b_kstep + (uint32_t)kPackRowPad;
     const int nkt_all = (X3 ? 6 : 1) * (Kp / BK);
     const int kt_begin = SPLIT ? half_k * (nkt_all / 2) : 0;
     const int kt_end = SPLIT ? (half_k ? nkt_all : nkt_all / 2) : nkt_all;
@@ -196,9 +199,8 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
 #define HEAL_DMA_TILE(kt_, stage_)                                                                    \
     do {                                                                                              \
         unsigned char* st_ = smem + (stage_) * STAGE;                                                 \
-        const uint32_t koff_a_ = X3 ? x3_koff(kt_, X3_PLANES_A) : (uint32_t)(kt_) * (AH ? 64u : 128u); \
-        const uint32_t koff_b_ =                                                                      \
-            X3 ? x3_koff(kt_, X3_PLANES_B) : (uint32_t)(kt_) * (BROWB == ROWB ? 128u : 64u);           \
+        const uint32_t koff_a_ = X3 ? x3_koff(kt_, X3_PLANES_A) : (uint32_t)(kt_) * a_kstep;          \
+        const uint32_t koff_b_ = X3 ? x3_koff(kt_, X3_PLANES_B) : (uint32_t)(kt_) * b_kstep;          \
         _Pragma("unroll") for (int i = 0; i < A_DMA; ++i) {                                           \
             const int b_ = wave + 4 * i;                                                              \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_ptr)(st_ + b_ * 1024), 16, dma_voff_a, \
@@ -328,8 +330,8 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
             // copies, next fragment reads
             const int kt2 = kt_begin + min(t + 2, nkt - 1);
             unsigned char* const st2 = smem + (t & 1) * STAGE;
-            const uint32_t koff_a2 = X3 ? x3_koff(kt2, X3_PLANES_A) : (uint32_t)kt2 * (AH ? 64u : 128u);
-            const uint32_t koff_b2 = X3 ? x3_koff(kt2, X3_PLANES_B) : (uint32_t)kt2 * (BROWB == ROWB ? 128u : 64u);
+            const uint32_t koff_a2 = X3 ? x3_koff(kt2, X3_PLANES_A) : (uint32_t)kt2 * a_kstep;
+            const uint32_t koff_b2 = X3 ? x3_koff(kt2, X3_PLANES_B) : (uint32_t)kt2 * b_kstep;
             const unsigned char* base = smem + (min(t + 1, nkt - 1) & 1) * STAGE;
             constexpr int ND = A_DMA + B_DMA;
 #pragma unroll
@@ -562,21 +564,15 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
     if (!attr_set[dev]) {
-        const std::pair<const void*, int> fns[16] = {
+        const std::pair<const void*, int> fns[10] = {
             {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3, false, false, false, false>), dyn_lds(false, false, false, false)},
             {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 3, false, false, false, false>), dyn_lds(false, false, false, false)},
             {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2, true, false, false, false>), dyn_lds(false, true, false, false)},
             {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 2, true, false, false, false>), dyn_lds(false, true, false, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, false, false, false, false>), dyn_lds(false, false, false, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, false, false, false, false>), dyn_lds(false, false, false, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, false, false, false>), dyn_lds(false, true, false, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, false, false, false>), dyn_lds(false, true, false, false)},
             {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, true, false, false>), dyn_lds(true, true, false, true)},
             {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, true, false, false>), dyn_lds(true, true, false, true)},
             {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 3, false, false, true, false>), dyn_lds(false, false, true, false)},
             {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 2, true, false, true, false>), dyn_lds(false, true, true, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, false, false, false, true>), dyn_lds(true, false, false, false)},
-            {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, false, false, false, true>), dyn_lds(true, false, false, false)},
             {reinterpret_cast<const void*>(&gemm_prefill_kernel<false, 1, true, false, false, true>), dyn_lds(true, true, false, false)},
             {reinterpret_cast<const void*>(&gemm_prefill_kernel<true, 1, true, false, false, true>), dyn_lds(true, true, false, false)}};
         for (const auto& f : fns) {
@@ -599,39 +595,39 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
     }
     const dim3 grid((unsigned)(tiles_m * tiles_n * (split ? 2 : 1)));
     const QkvDst none{};
+    // bytes per 32-wide k block in the packed source rows
+    const uint32_t a_kstep = a_hi ? 64u : 128u, b_kstep = b_hi ? 64u : 128u;
 #define HEAL_PREFILL(SPLIT_, NP_, BHI_, X3_)                                                          \
     hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, NP_, BHI_, X3_, false, false>), grid, dim3(256),  \
                        dyn_lds(X3_, BHI_, false, X3_), s, a, b, ea, eb, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n, \
-                       none)
-#define HEAL_PREFILL_AH(SPLIT_, BHI_)                                                                 \
-    hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, 1, BHI_, false, false, true>), grid, dim3(256),   \
-                       dyn_lds(true, BHI_, false, false), s, a, b, ea, eb, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n, \
-                       none)
+                       a_kstep, b_kstep, none)
+#define HEAL_PREFILL_1P(SPLIT_)                                                                       \
+    hipLaunchKernelGGL((gemm_prefill_kernel<SPLIT_, 1, true, false, false, true>), grid, dim3(256),    \
+                       dyn_lds(true, true, false, false), s, a, b, ea, eb, C, ldc, (int)M, (int)N, (int)Kp, tiles_m, tiles_n, \
+                       a_kstep, b_kstep, none)
     if (qkv) {
         if (nprod == 3)
             hipLaunchKernelGGL((gemm_prefill_kernel<false, 3, false, false, true, false>), grid, dim3(256),
                                dyn_lds(false, false, true, false), s, a, b, ea, eb, C, ldc, (int)M, (int)N, (int)Kp, tiles_m,
-                               tiles_n, *qkv);
+                               tiles_n, a_kstep, b_kstep, *qkv);
         else
             hipLaunchKernelGGL((gemm_prefill_kernel<false, 2, true, false, true, false>), grid, dim3(256),
                                dyn_lds(false, true, true, false), s, a, b, ea, eb, C, ldc, (int)M, (int)N, (int)Kp, tiles_m,
-                               tiles_n, *qkv);
+                               tiles_n, a_kstep, b_kstep, *qkv);
         return hipGetLastError();
     }
+    // the one-product mode stages the hi parts alone, from either packing
 #define HEAL_PREFILL_NP(SPLIT_)                                                                       \
     do {                                                                                              \
-        if (a_hi && b_hi) HEAL_PREFILL_AH(SPLIT_, true);                                              \
-        else if (a_hi) HEAL_PREFILL_AH(SPLIT_, false);                                                \
-        else if (x3) HEAL_PREFILL(SPLIT_, 1, true, true);                                             \
+        if (x3) HEAL_PREFILL(SPLIT_, 1, true, true);                                                  \
         else if (nprod == 3) HEAL_PREFILL(SPLIT_, 3, false, false);                                   \
         else if (nprod == 2) HEAL_PREFILL(SPLIT_, 2, true, false);                                    \
-        else if (b_hi) HEAL_PREFILL(SPLIT_, 1, true, false);                                          \
-        else HEAL_PREFILL(SPLIT_, 1, false, false);                                                   \
+        else HEAL_PREFILL_1P(SPLIT_);                                                                 \
     } while (0)
     if (split) HEAL_PREFILL_NP(true);
     else HEAL_PREFILL_NP(false);
 #undef HEAL_PREFILL_NP
-#undef HEAL_PREFILL_AH
+#undef HEAL_PREFILL_1P
 #undef HEAL_PREFILL
     return hipGetLastError();
 }
