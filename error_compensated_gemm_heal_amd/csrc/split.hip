@@ -188,11 +188,7 @@ __global__ __launch_bounds__(256) void pack_colmajor_kernel(const T* __restrict_
     if (bad && status) atomicOr(status, (uint32_t)HEAL_FLAG_F16_RANGE);
 }
 
-__device__ __forceinline__ float wave_max(float m) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    return m;
-}
+__device__ __forceinline__ float wave_max(float m) { return max_swap32(max_half(m)); }
 
 // Largest magnitude of the workgroup's values (256 threads); red holds 4
 // floats of LDS and is free again when this returns.
