@@ -231,12 +231,15 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
     // rotated order, rot = (128-row group of W) mod nblocks: workgroups that
     // run together then read at different k offsets, which spreads rows with
     // a power-of-two stride (K = 4096 fp32 rows are 16 KiB apart) over the
-    // HBM channels.  With 8 chunks or more their start offsets already spread
-    // the reads, and rotation measured slower (K = 4096, N = 4096: 24.0 ->
-    // 26.1 us at M = 1; K = 4096, N = 14336 with 2 chunks: 55.7 -> 52.0 us).
-    // The order depends on the output rows and (N, K) only, not on M or the
-    // workgroup shape.
-    const int rot = gridDim.y < 8 ? (int)((unsigned)(blockIdx.x * NWK / 8) % (unsigned)nblocks) : 0;
+    // HBM channels.  With 8 chunks or more their start offsets spread the
+    // reads, and rotation measured slower (K = 4096, N = 4096: 24.0 -> 26.1 us
+    // at M = 1; K = 4096, N = 14336 with 2 chunks: 55.7 -> 52.0 us), except
+    // for rows a multiple of 32 KiB apart read in chunks of 8 blocks or more
+    // (K = 8192, N = 4096: 50.2 -> 35.9 us; K = 16384: 67.7 -> 54.8 us).  The
+    // order depends on the output rows, (N, K) and W's row stride only, not
+    // on M or the workgroup shape.
+    const bool rotate = gridDim.y < 8 || (wrow_bytes % 32768 == 0 && kchunk >= 8 * KA);
+    const int rot = rotate ? (int)((unsigned)(blockIdx.x * NWK / 8) % (unsigned)nblocks) : 0;
     auto pblock = [&](int b) { return b + rot >= nblocks ? b + rot - nblocks : b + rot; };
     // the step to load for logical step L (clamped: the ring's last loads
     // re-read a valid step)

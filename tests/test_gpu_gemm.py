@@ -185,6 +185,25 @@ def test_gemm_decode_shapes_and_batch_invariance(K, N, packed):
     assert e_gpu <= gemm_tolerance(e_naive, K)
 
 
+@pytest.mark.parametrize("K,N", [(8192, 4096), (16384, 4096)])
+def test_gemm_decode_aligned_long_rows(K, N):
+    """Weight rows a multiple of 32 KiB apart, read in 8 chunks of 8 or more k
+    blocks each: the rotated k order is on.  Tolerance on every row of the
+    M = 64 call, and each row identical for every M."""
+    print(f"decode aligned rows K={K} N={N}", flush=True)
+    A, W = WL.decode_gemm(64, K, N, seed=2100 + K)
+    Ad, Wd = torch.from_numpy(A).to(DEV), torch.from_numpy(W).to(DEV)
+    outs = {M: heal.heal_gemm_f32c(Ad[:M], Wd).cpu().numpy() for M in (1, 8, 17, 64)}
+    for M in outs:
+        assert np.array_equal(outs[M], outs[64][:M]), M
+    rows = np.arange(64)
+    C64 = oracle.gemm_f64_rows(A, W, rows)
+    e_gpu = gemm_normwise_error(outs[64], C64, A, W, rows=rows)
+    e_naive = gemm_normwise_error(oracle.gemm_f32_naive_rows(A, W, rows), C64, A, W, rows=rows)
+    print(f"decode aligned rows K={K}: e_gpu={e_gpu:.3e} e_naive={e_naive:.3e}", flush=True)
+    assert e_gpu <= gemm_tolerance(e_naive, K)
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 384, 1024), (8, 300, 1000), (40, 260, 700), (64, 512, 4096),
                                    (300, 384, 1024)])
 @pytest.mark.parametrize("f16", [False, True])
