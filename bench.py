@@ -493,6 +493,62 @@ def calibrate(torch, heal):
     return res
 
 
+def vendor_gemms(torch, reps=20):
+    """The vendor's GEMM (torch.matmul, i.e. hipBLASLt/rocBLAS) on the same shapes,
+    as context beside the calibration: plain fp16 and bf16 (one 16-bit product,
+    no compensation: the library's own 16-bit rate on these shapes) and plain
+    FP32 (the FP32 pipeline the pages compare HEAL with; TF32-style reduced
+    precision switched off) on the two prefill shapes; FP32 and fp16 on the 16
+    decode calls in bench order.  C = A.W^T with W in nn.Linear's [N, K]
+    layout, random normal operands; each timed with HIP events on the current
+    stream after the same untimed cache flush as the rows (mean of `reps`).
+    Nothing here is part of the HEAL path or of `value`."""
+    import heal_workloads as WL
+    torch.backends.cuda.matmul.allow_tf32 = False
+    torch.backends.cuda.matmul.allow_fp16_reduced_precision_reduction = False
+    torch.backends.cuda.matmul.allow_bf16_reduced_precision_reduction = False
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    flush = torch.ones(512 << 18, dtype=torch.float32, device=dev)
+    flush_out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        tot = 0.0
+        for _ in range(reps):
+            torch.amax(flush, dim=0, out=flush_out)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            tot += e0.elapsed_time(e1) * 1e-3
+        return tot / reps
+
+    out = {}
+    flop = sum(2.0 * WL.PREFILL_M * K * N for K, N in WL.PREFILL_KN)
+    for name, dt in (("fp16", torch.float16), ("bf16", torch.bfloat16), ("fp32", torch.float32)):
+        ops = [(torch.randn(WL.PREFILL_M, K, device=dev, generator=gen).to(dt),
+                torch.randn(N, K, device=dev, generator=gen).to(dt)) for K, N in WL.PREFILL_KN]
+        t = timed(lambda ops=ops: [torch.matmul(a, w.t()) for a, w in ops])
+        out[f"prefill_{name}"] = {"ms": t * 1e3, "TFLOPs": flop / t / 1e12}
+        del ops
+    for name, dt, esz in (("fp32", torch.float32, 4), ("fp16", torch.float16, 2)):
+        ws = {(K, N): torch.randn(N, K, device=dev, generator=gen).to(dt) for K, N in WL.LLAMA3_8B_DECODE_KN}
+        calls = [(torch.randn(M, K, device=dev, generator=gen).to(dt), ws[(K, N)])
+                 for M in WL.DECODE_M for K, N in WL.LLAMA3_8B_DECODE_KN]
+        nbytes = sum(esz * (w.numel() + a.numel() + a.shape[0] * w.shape[0]) for a, w in calls)
+        t = timed(lambda calls=calls: [torch.matmul(a, w.t()) for a, w in calls])
+        out[f"decode_{name}"] = {"ms": t * 1e3, "GBps": nbytes / t / 1e9}
+        del ws, calls
+    del flush
+    out["note"] = ("torch.matmul (vendor BLAS), not HEAL: prefill = both M=2048 shapes, useful TFLOP/s; "
+                   "decode = the 16 calls, GB/s of weights + activations + outputs in that dtype")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -503,6 +559,7 @@ def main():
                                       "qkv_proj,quant,dequant,attn_prefill,attn",
                     help="comma-separated subset of rows to run (profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-vendor", action="store_true", help="skip the vendor-GEMM context timings")
     ap.add_argument("--cpu-seconds", type=float, default=24.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a device copy of this many MiB (counter calibration) and exit")
@@ -635,6 +692,8 @@ def main():
         if "GBps" in r:
             r["hbm_frac_measured"] = r["GBps"] / cal["hbm_read_GBps"]
     res["rows"] = per_row
+    if not args.no_vendor:
+        res["vendor_gemm"] = vendor_gemms(torch)
 
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")

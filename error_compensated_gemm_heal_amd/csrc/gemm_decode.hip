@@ -32,8 +32,13 @@
 //    as the 16-column operand (16 W rows per wave), so output columns are
 //    consecutive lanes;
 //  * inside each 32-wide k step, lane group g (lanes 16g..16g+15) carries
-//    k = 4g..4g+3 and 16+4g..16+4g+3: any k order is valid as long as both
-//    operands use it, and this one makes each W load a 64-byte run per row;
+//    k = 8g..8g+7 (k = 4g..4g+3 and 16+4g..16+4g+3 where W is loaded element
+//    by element): any k order is valid as long as both operands use it, and
+//    this one keeps each lane's W values contiguous (one 16-byte load of
+//    binary16 W or of each packed part, two of fp32).  The MFMA's sum over
+//    its 32 k positions is not invariant under permuting them, so every
+//    vector-loaded W (fp32, binary16, packed) uses the same order: a binary16
+//    weight gives the bits of its fp32 copy;
 //  * W for the next 8 k steps is always in flight: every step issues a
 //    fixed number of W loads (the last steps re-read a clamped step), so the
 //    number of loads outstanding at each block boundary is a constant;
@@ -104,7 +109,7 @@ constexpr int img_bytes() { return block_bytes<MT>() + 256; }
 // as hi = fp16, lo = fp16((x - hi) 2^10), into block b's image: plane p
 // (0 = hi, 1 = lo), step s, tile t, lane 16 g + r holds, as 8 fp16, row
 // 16 t + r at k = 128 b + 32 s + {4g .. 4g+3, 16+4g .. 16+4g+3} (K8, for a
-// packed W: k = 128 b + 32 s + 8g .. 8g+7); then e at byte block_bytes + 4 m.  Rows >= M and k >= K are zero (exponent 0).  One
+// vector-loaded W: k = 128 b + 32 s + 8g .. 8g+7); then e at byte block_bytes + 4 m.  Rows >= M and k >= K are zero (exponent 0).  One
 // load per thread: the kernel costs about one memory latency.
 constexpr int PREP_T = 512;
 template <int MT, bool AVEC, bool K8>
@@ -136,7 +141,7 @@ __global__ __launch_bounds__(PREP_T) void decode_prep_kernel(const float* __rest
     mx = max_half(mx);
     if (q >= nblk * 32) return;   // past the last block (whole half waves)
     const int e = row_norm_exp(mx);
-    // j = 8 s + 4 h + g: k = 128 b + 32 s + 16 h + 4 g; K8 (packed W):
+    // j = 8 s + 4 h + g: k = 128 b + 32 s + 16 h + 4 g; K8:
     // j = 8 s + 2 g + h: k = 128 b + 32 s + 8 g + 4 h
     const int b = q >> 5, j = q & 31;
     const int st = j >> 3, h = K8 ? (j & 1) : ((j >> 2) & 1), g = K8 ? ((j >> 1) & 3) : (j & 3);
@@ -177,9 +182,9 @@ __device__ __forceinline__ float absmax8(float m, const float4& a, const float4&
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// WM: how W arrives.  1: fp32 (or binary16) rows aligned to the load width
-// and K % 32 == 0, so every step is two buffer loads per lane (16 bytes each
-// for fp32 W, 8 for fp16 W).  0: the same rows, loaded element by element with
+// WM: how W arrives.  1: fp32 (or binary16) rows 16-byte aligned and
+// K % 32 == 0, so every step is two 16-byte buffer loads per lane for fp32
+// W, one for binary16 W (lane group g takes k = 8g .. 8g+7).  0: the same rows, loaded element by element with
 // bounds checks (block boundaries wait for every load).  2: packed by
 // heal_pack_w (normalized rows of [32 hi | 32 res] fp16 per 32-wide k block,
 // or hi parts alone for a binary16 weight, rows padded): no split in the
@@ -210,6 +215,8 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
     static_assert(!SHIFT || INK, "with copied blocks the shift is applied by decode_prep_kernel");
     constexpr bool VEC = WM >= 1;
     constexpr bool PKW = WM == 2;                   // W packed: k = 8g .. 8g+7 per lane group
+    // k = 8g .. 8g+7 per lane group for every vector-loaded W
+    constexpr bool K8 = WM >= 1;
     constexpr int BB = block_bytes<MT>();
     constexpr int SB = img_bytes<MT>();             // LDS bytes per block buffer: planes + exponents
     static_assert(NWK == NW || (NWK == 2 * NW && MT > 1), "8 waves only with several row tiles");
@@ -268,7 +275,7 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
     auto urow = [&](int j) { return 4 * (wave * RND + j) + (lane & 3); };
     const int ugg = (lane >> 2) & 3, uhalf = (lane >> 4) & 1, ust = (lane >> 5) & 1;
     auto unit_k = [&](int pb, int i) {   // pb: the block's place in the chunk
-        return k_begin + KA * pb + 32 * (ust + 2 * i) + (PKW ? 8 * ugg + 4 * uhalf : 16 * uhalf + 4 * ugg);
+        return k_begin + KA * pb + 32 * (ust + 2 * i) + (K8 ? 8 * ugg + 4 * uhalf : 16 * uhalf + 4 * ugg);
     };
     auto load_a = [&](int b) {
         const int pb = pblock(b);
@@ -351,12 +358,12 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
                                                      0, 0);
     };
 
-    // W: lane reads row n, k = k_begin + 32 step + {4g.., 16+4g..} (packed:
-    // 8g .. 8g+7) (scalars made explicit: the buffer resource must live in SGPRs)
+    // W: lane reads row n, k = k_begin + 32 step + 8g .. 8g+7 (element loads:
+    // {4g.., 16+4g..}) (scalars made explicit: the buffer resource must live in SGPRs)
     constexpr int ESZ = WF16 ? 2 : 4;          // bytes per W element (unpacked)
     constexpr int KBB = WF16 ? 64 : 128;       // packed bytes per row and 32-wide k block
     constexpr int PFW = PF;                    // W steps in flight
-    constexpr int LPS = PKW && WF16 ? 1 : 2;   // buffer loads per W step (VEC)
+    constexpr int LPS = K8 && WF16 ? 1 : 2;    // buffer loads per W step (VEC)
     using WReg = std::conditional_t<WF16, u32x4, u32x8>;   // one step's 8 W values (packed: hi, then res)
     const int64_t ldw = wrow_bytes / ESZ;      // unpacked: elements per row
     const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(ROWS_PER_WAVE, N - n0)));
@@ -365,7 +372,7 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
     const __amdgpu_buffer_rsrc_t wrsrc =
         make_rsrc(Wb + (int64_t)wrow0 * wrow_bytes, (uint32_t)((int64_t)nrows * wrow_bytes));
     const uint32_t wlane = PKW ? (uint32_t)((lane & 15) * wrow_bytes + (int64_t)(k_begin / 32) * KBB + 16 * g)
-                               : (uint32_t)((lane & 15) * wrow_bytes + (int64_t)(k_begin + 4 * g) * ESZ);
+                               : (uint32_t)((lane & 15) * wrow_bytes + (int64_t)(k_begin + (K8 ? 8 : 4) * g) * ESZ);
     auto load_w = [&](int step, WReg& w) {
         if constexpr (PKW) {
             const uint32_t off = wlane + (uint32_t)(step * KBB);
@@ -379,12 +386,10 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
         } else if (VEC) {
             const uint32_t off = wlane + (uint32_t)(step * 32 * ESZ);
             if constexpr (WF16) {
-                const auto a = __builtin_amdgcn_raw_buffer_load_b64(wrsrc, off, 0, 0);
-                const auto b = __builtin_amdgcn_raw_buffer_load_b64(wrsrc, off + 16 * ESZ, 0, 0);
-                w = WReg{a[0], a[1], b[0], b[1]};
+                w = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off, 0, 0);
             } else {
                 const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off, 0, 0);
-                const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off + 16 * ESZ, 0, 0);
+                const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off + 4 * ESZ, 0, 0);
                 w = WReg{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
             }
         } else {
@@ -692,10 +697,12 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
     const bool wide = mt > 1 && nblk2 * plan.splits >= (mt == 4 ? WIDE_MIN_WG4 : WIDE_MIN_WG2);
     const int wg_rows = (wide ? 2 * NW : NW) * ROWS_PER_WAVE;
     const dim3 grid((unsigned)((N + wg_rows - 1) / wg_rows), (unsigned)plan.splits);
-    // W loads of 8 elements per step need rows aligned to the load width
-    // (16 bytes fp32, 8 bytes fp16) and whole k32 steps
-    const uintptr_t walign = wf16 ? 7 : 15;
-    const bool vec = (reinterpret_cast<uintptr_t>(W) & walign) == 0 && (ldw & 3) == 0 && (K & 31) == 0;
+    // W loads of 8 elements per step (two 16-byte loads of fp32, one of
+    // binary16) need 16-byte aligned rows and whole k32 steps
+    const bool vec = (reinterpret_cast<uintptr_t>(W) & 15) == 0 && (ldw & (wf16 ? 7 : 3)) == 0 && (K & 31) == 0;
+    // the activation's k order within a step: 8 consecutive k per lane group
+    // for every vector-loaded W
+    const bool k8 = packed || vec;
     // packed W: padded rows, the row exponents after them
     const int64_t wrow_bytes = packed ? (wf16 ? pack_row_bytes_hi(K) : pack_row_bytes(K)) : ldw * (wf16 ? 2 : 4);
     const int* wexp = packed ? reinterpret_cast<const int*>(static_cast<const unsigned char*>(W) +
@@ -751,13 +758,13 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
         if constexpr ((MT_) > 1) {                                                                      \
           if (!ink) {                                                                                   \
             const dim3 pgrid(16 * (MT_), (unsigned)((nablk * 32 + PREP_T - 1) / PREP_T));                \
-            if (avec && packed)                                                                         \
+            if (avec && k8)                                                                             \
                 hipLaunchKernelGGL((decode_prep_kernel<MT_, true, true>), pgrid, dim3(PREP_T), 0, s, A, lda, \
                                    (int)M, (int)K, nablk, kshift, ablk);                                \
             else if (avec)                                                                              \
                 hipLaunchKernelGGL((decode_prep_kernel<MT_, true, false>), pgrid, dim3(PREP_T), 0, s, A, lda, \
                                    (int)M, (int)K, nablk, kshift, ablk);                                \
-            else if (packed)                                                                            \
+            else if (k8)                                                                                \
                 hipLaunchKernelGGL((decode_prep_kernel<MT_, false, true>), pgrid, dim3(PREP_T), 0, s, A, lda, \
                                    (int)M, (int)K, nablk, kshift, ablk);                                \
             else                                                                                        \
