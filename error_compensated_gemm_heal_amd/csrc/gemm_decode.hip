@@ -200,7 +200,13 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // SHIFT (splitting A itself): element (m, k) of A is multiplied by
 // 2^-kshift[k] before its block maximum and split.  ONE: plain FP16, the
 // A_hi.W_hi product alone.  NWK: waves per workgroup.
-template <int MT, int WM, bool WF16, bool AVEC, bool SHIFT, bool ONE, int NWK, bool INKT>
+// KW (one row tile, a k split of 2 .. 8 chunks): the workgroup is one
+// 16-row slice of W and its waves are the slice's chunks (wave w takes chunk
+// w, blockDim.x / 64 of them), each with its own LDS buffers and no barrier
+// in the main loop; the chunk sums meet in LDS and are added in chunk order,
+// as the cross-workgroup completion adds them: the same bits, with no
+// memory round trips after the main loop.
+template <int MT, int WM, bool WF16, bool AVEC, bool SHIFT, bool ONE, int NWK, bool INKT, bool KW = false>
 __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __restrict__ A, int64_t lda,
                                                           const unsigned char* __restrict__ Ablk,
                                                           uint32_t a_total_bytes, const void* __restrict__ W,
@@ -219,17 +225,19 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
     constexpr bool K8 = WM >= 1;
     constexpr int BB = block_bytes<MT>();
     constexpr int SB = img_bytes<MT>();             // LDS bytes per block buffer: planes + exponents
-    static_assert(NWK == NW || (NWK == 2 * NW && MT > 1), "8 waves only with several row tiles");
+    static_assert(NWK == NW || (NWK == 2 * NW && (MT > 1 || KW)), "8 waves only with several row tiles");
+    static_assert(!KW || (MT == 1 && !SHIFT), "chunks as waves with one row tile, no channel shifts");
     constexpr int DMA_PER_WAVE = BB / 1024 / NWK;   // 1 KB per wave-wide direct-to-LDS load
     extern __shared__ __attribute__((aligned(16))) unsigned char sa[];   // 2 x SB
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4;
-    const int n0 = blockIdx.x * (NWK * ROWS_PER_WAVE) + wave * ROWS_PER_WAVE;
+    const int n0 = KW ? blockIdx.x * ROWS_PER_WAVE : blockIdx.x * (NWK * ROWS_PER_WAVE) + wave * ROWS_PER_WAVE;
     const int n = n0 + (lane & 15);
     const bool row_ok = n < N;
-    const int split = blockIdx.y;
+    const int split = KW ? wave : blockIdx.y;
+    const int nchunks = KW ? (int)(blockDim.x >> 6) : (int)gridDim.y;   // the plan's k chunks
     const int k_begin = split * kchunk;
     const int k_end = min(k_begin + kchunk, K);
     const int nsteps = (k_end - k_begin + 31) / 32;
@@ -245,8 +253,9 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
     // (K = 8192, N = 4096: 50.2 -> 35.9 us; K = 16384: 67.7 -> 54.8 us).  The
     // order depends on the output rows, (N, K) and W's row stride only, not
     // on M or the workgroup shape.
-    const bool rotate = gridDim.y < 8 || (wrow_bytes % 32768 == 0 && kchunk >= 8 * KA);
-    const int rot = rotate ? (int)((unsigned)(blockIdx.x * NWK / 8) % (unsigned)nblocks) : 0;
+    const bool rotate = nchunks < 8 || (wrow_bytes % 32768 == 0 && kchunk >= 8 * KA);
+    const int rgroup = KW ? blockIdx.x / 8 : blockIdx.x * NWK / 8;   // 128-row group of W
+    const int rot = rotate ? (int)((unsigned)rgroup % (unsigned)nblocks) : 0;
     auto pblock = [&](int b) { return b + rot >= nblocks ? b + rot - nblocks : b + rot; };
     // the step to load for logical step L (clamped: the ring's last loads
     // re-read a valid step)
@@ -264,27 +273,40 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
     //      operand slot (s, tile m / 16, lane 16 gg + m % 16), bytes 8 half ..
     //      8 half + 7, of the hi and lo planes; the row's block exponent to
     //      byte BB + 4 m.
-    constexpr int RND = INK ? 16 * MT / (4 * NWK) : 1;
-    static_assert(!INK || RND * 4 * NWK == 16 * MT, "whole groups of 4 rows per wave");
+    // (KW: each wave stages all 16 rows of its own chunk's blocks)
+    constexpr int RND = INK ? (KW ? 4 : 16 * MT / (4 * NWK)) : 1;
+    static_assert(!INK || KW || RND * 4 * NWK == 16 * MT, "whole groups of 4 rows per wave");
+    const int wbase = KW ? wave * 2 * SB : 0;   // the wave's own LDS buffers (KW)
     float4 areg[RND][2];
-    int sreg[RND][2][4];   // SHIFT: the units' 2^-kshift exponents (k >= K reads 0)
+    int sreg[2][4];        // SHIFT: the units' 2^-kshift exponents (k >= K reads 0)
     // rows >= M fall outside the resource and read as zero; k past the
     // chunk end is zeroed when the block is stored
     const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(A, (uint32_t)((int64_t)M * lda * 4));
     const __amdgpu_buffer_rsrc_t ksrc = make_rsrc(kshift, SHIFT ? (uint32_t)K : 0u);
-    auto urow = [&](int j) { return 4 * (wave * RND + j) + (lane & 3); };
+    auto urow = [&](int j) { return 4 * ((KW ? 0 : wave * RND) + j) + (lane & 3); };
     const int ugg = (lane >> 2) & 3, uhalf = (lane >> 4) & 1, ust = (lane >> 5) & 1;
     auto unit_k = [&](int pb, int i) {   // pb: the block's place in the chunk
         return k_begin + KA * pb + 32 * (ust + 2 * i) + (K8 ? 8 * ugg + 4 * uhalf : 16 * uhalf + 4 * ugg);
     };
     auto load_a = [&](int b) {
         const int pb = pblock(b);
+        if constexpr (SHIFT) {   // the same k for every row group
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint32_t k0 = (uint32_t)unit_k(pb, i);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    sreg[i][q] = (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(ksrc, k0 + q, 0, 0);
+            }
+        }
 #pragma unroll
         for (int j = 0; j < RND; ++j)
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const uint32_t off = (uint32_t)(((int64_t)urow(j) * lda + unit_k(pb, i)) * 4);
-                if constexpr (AVEC) {
+                if (KW && 4 * j >= M) {   // a group of rows past M: zeros, no loads
+                    areg[j][i] = make_float4(0.f, 0.f, 0.f, 0.f);
+                } else if constexpr (AVEC) {
                     areg[j][i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, off, 0, 0));
                 } else {
                     areg[j][i] = make_float4(
@@ -293,16 +315,10 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
                         __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(arsrc, off + 8, 0, 0)),
                         __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(arsrc, off + 12, 0, 0)));
                 }
-                if constexpr (SHIFT) {
-                    const uint32_t k0 = (uint32_t)unit_k(pb, i);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        sreg[j][i][q] = (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(ksrc, k0 + q, 0, 0);
-                }
             }
     };
     auto store_a = [&](int b) {
-        unsigned char* base = sa + (b & 1) * SB;
+        unsigned char* base = sa + wbase + (b & 1) * SB;
         const int pb = pblock(b);
 #pragma unroll
         for (int j = 0; j < RND; ++j) {
@@ -314,7 +330,7 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
                 const float x[4] = {areg[j][i].x, areg[j][i].y, areg[j][i].z, areg[j][i].w};
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    v[i][q] = k + q < k_end ? (SHIFT ? __builtin_ldexpf(x[q], -sreg[j][i][q]) : x[q]) : 0.0f;
+                    v[i][q] = k + q < k_end ? (SHIFT ? __builtin_ldexpf(x[q], -sreg[i][q]) : x[q]) : 0.0f;
                     mx = fmaxf(mx, __builtin_fabsf(v[i][q]));
                 }
             }
@@ -425,13 +441,16 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
         for (int e = 0; e < 4; ++e) tot[t][e] = 0.f;
 
     // prologue: W for steps 0 .. PFW-1 and activation block 0 in flight
-    // together; block 0 lands in LDS buffer 0 (split here, or copied, in
-    // which case the copy is issued first so its wait leaves W in flight)
+    // together; block 0 lands in LDS buffer 0 (split here, or copied); its
+    // loads are issued first, so that waiting for them leaves W in flight
+    // (issuing the activation loads last cost 0.7-1.1 us per call on the
+    // in-kernel split path)
     WReg wr[PFW];
     if constexpr (INK) {
+        load_a(0);   // first, so that waiting for it leaves W in flight
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < PFW; ++s) load_w(pstep(s), wr[s]);
-        load_a(0);
         __builtin_amdgcn_sched_barrier(0);
         store_a(0);
         __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
@@ -443,7 +462,7 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
         if (VEC) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS * PFW));   // block 0 landed; W still in flight
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
-    __builtin_amdgcn_s_barrier();
+    if constexpr (!KW) __builtin_amdgcn_s_barrier();   // KW: the wave's own buffers, LDS in program order
     __builtin_amdgcn_sched_barrier(0);
     float wmax = 0.0f;
 
@@ -457,7 +476,7 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
             else dma_block(b + 1);
         }
         __builtin_amdgcn_sched_barrier(0);
-        const unsigned char* abuf = sa + (b & 1) * SB;
+        const unsigned char* abuf = sa + wbase + (b & 1) * SB;
         const int pb = pblock(b);
 #pragma unroll
         for (int t = 0; t < MT; ++t)
@@ -514,7 +533,7 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
                 if (VEC) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS * STEPS));
                 else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             }
-            __builtin_amdgcn_s_barrier();
+            if constexpr (!KW) __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -544,6 +563,29 @@ __global__ __launch_bounds__(64 * NWK) void gemm_decode_kernel(const float* __re
         for (int t = 0; t < MT; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) tot[t][e] = __builtin_ldexpf(tot[t][e], -ew);
+    }
+    if constexpr (KW) {
+        // each wave's chunk sums into its own (no longer read) LDS buffer;
+        // after the one barrier every wave reaches, wave 0 adds them in
+        // chunk order and writes C
+        float* mine = reinterpret_cast<float*>(sa + wbase);
+        *reinterpret_cast<float4*>(mine + 4 * lane) = make_float4(tot[0][0], tot[0][1], tot[0][2], tot[0][3]);
+        __syncthreads();
+        if (wave != 0 || !row_ok) return;
+        float acc[4] = {tot[0][0], tot[0][1], tot[0][2], tot[0][3]};
+        for (int c = 1; c < nchunks; ++c) {
+            const float4 p = *reinterpret_cast<const float4*>(sa + c * 2 * SB + 16 * lane);
+            acc[0] += p.x;
+            acc[1] += p.y;
+            acc[2] += p.z;
+            acc[3] += p.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = 4 * g + e;
+            if (m < M) C[(int64_t)m * ldc + n] = acc[e];
+        }
+        return;
     }
     const int nsplit = gridDim.y;
     if (nsplit == 1) {
@@ -718,6 +760,20 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
     // groups per wave.  Both forms store the same split blocks: the results
     // are identical.
     const int rnd = 16 * mt / (4 * (wide ? 2 * NW : NW));
+    // One row tile, 2 .. 8 chunks of at most 4 blocks, and at least 256
+    // slices of 16 rows (one workgroup per slice fills the chip): the chunks
+    // are the waves of one workgroup (KW), with no completion through memory.
+    // Measured per call (back to back, cold Infinity Cache): K = N = 4096
+    // (8 chunks of 4 blocks) 21.7 -> 19.5 us at M = 1, 22.4 -> 20.8 us at
+    // M = 8; with longer chunks the chunk-per-wave grid streams slower than
+    // it saves (K = 14336, N = 4096, 8 chunks of 14 blocks: 47.8 -> 47.9 us
+    // at M = 1, 49.2 -> 53.2 us at M = 8; K = 4096, N = 14336, 2 chunks of
+    // 16 blocks: 51.7 -> 52.6 and 52.5 -> 57.0 us), so it stays off there.
+    const int64_t nslices = (N + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
+    // (Not with a_kshift: that form's per-wave staging of all 16 rows did not
+    // fit in registers.)
+    const bool kw = mt == 1 && !kshift && plan.splits >= 2 && plan.splits <= 2 * NW && plan.kchunk <= 4 * KA &&
+                    nslices >= 256;
     const bool ink = mt > 1 && !kshift && avec && (rnd == 1 || (rnd == 2 && plan.kchunk / KA <= 4));
 #define HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW_, INK_)                                \
     hipLaunchKernelGGL((gemm_decode_kernel<MT_, VEC_, F16_, AV_, SH_, ONE_, NW_, INK_>), grid, dim3(64 * NW_), \
@@ -734,12 +790,23 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
         }                                                                                               \
         HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW_, false);                                \
     } while (0)
+#define HEAL_DEC_LAUNCH_KW(VEC_, F16_, AV_, SH_, ONE_)                                                 \
+    hipLaunchKernelGGL((gemm_decode_kernel<1, VEC_, F16_, AV_, SH_, ONE_, 2 * NW, false, true>),          \
+                       dim3((unsigned)nslices), dim3(64 * plan.splits), plan.splits * 2 * img_bytes<1>(), s, A, \
+                       lda, ablk, (uint32_t)plan.a_bytes, W, wrow_bytes, wexp, C, ldc, part, flags, epoch,    \
+                       (int)M, (int)N, (int)K, (int)plan.kchunk, kshift, status)
 #define HEAL_DEC_LAUNCH(MT_, VEC_, F16_, AV_, SH_, ONE_)                                                \
     do {                                                                                                \
         if constexpr (MT_ > 1) {                                                                        \
             if (wide) HEAL_DEC_LAUNCH_INK(MT_, VEC_, F16_, AV_, SH_, ONE_, 2 * NW);                     \
             else HEAL_DEC_LAUNCH_INK(MT_, VEC_, F16_, AV_, SH_, ONE_, NW);                              \
         } else {                                                                                        \
+            if constexpr (!SH_) {                                                                       \
+                if (kw) {                                                                               \
+                    HEAL_DEC_LAUNCH_KW(VEC_, F16_, AV_, false, ONE_);                                   \
+                    break;                                                                              \
+                }                                                                                       \
+            }                                                                                           \
             HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW, false);                             \
         }                                                                                               \
     } while (0)
@@ -795,6 +862,7 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
 #undef HEAL_DEC_MAIN
 #undef HEAL_DEC_LAUNCH
 #undef HEAL_DEC_LAUNCH_INK
+#undef HEAL_DEC_LAUNCH_KW
 #undef HEAL_DEC_LAUNCH_NW
     return hipGetLastError();
 }

@@ -185,6 +185,47 @@ def test_gemm_decode_shapes_and_batch_invariance(K, N, packed):
     assert e_gpu <= gemm_tolerance(e_naive, K)
 
 
+@pytest.mark.parametrize("K,N", [(2048, 4100), (2000, 4100), (4096, 4096)])
+@pytest.mark.parametrize("wkind", ["fp32", "f16", "packed", "kshift"])
+def test_gemm_decode_chunks_as_waves(K, N, wkind):
+    """M <= 16 with short k chunks (at most 4 blocks of 128) over at least 256 slices
+    of 16 rows: the chunks are the waves of one workgroup and meet in LDS.  Every M
+    gives the rows of the M = 17 call (chunks completed through memory) bit for bit,
+    the allocation-free entry point gives the same bits, and the M = 16 result meets
+    the tolerance on every row (ragged N; K = 2000 loads W element by element)."""
+    print(f"decode chunks as waves K={K} N={N} {wkind}", flush=True)
+    A, W = WL.decode_gemm(17, K, N, seed=2200 + K + N)
+    ks = None
+    if wkind == "kshift":     # two channels past FP16's range, rescaled per channel
+        A[:, 3] *= 3.0e5
+        A[:, K - 1] *= -7.0e5
+        ks = np.zeros(K, np.int8)
+        ks[3], ks[K - 1] = 6, 6
+        W = W * np.exp2(ks.astype(np.float32))[None, :]
+    if wkind == "f16":
+        W = W.astype(np.float16)
+    Ad, Wd = torch.from_numpy(A).to(DEV), torch.from_numpy(W).to(DEV)
+    Wop = heal.heal_pack_w(Wd) if wkind == "packed" else Wd
+    ksd = None if ks is None else torch.from_numpy(ks).to(DEV)
+    outs = {M: heal.heal_gemm_f32c(Ad[:M], Wop, a_kshift=ksd).cpu().numpy() for M in (1, 3, 8, 16, 17)}
+    for M in outs:
+        assert np.array_equal(outs[M], outs[17][:M]), M
+    C = torch.empty(16, N, dtype=torch.float32, device=DEV)
+    heal.heal_gemm_f32c_noalloc(Ad[:16], Wop, C, a_kshift=ksd)
+    assert np.array_equal(C.cpu().numpy(), outs[16])
+    W64 = W.astype(np.float32)
+    A16 = A[:16]
+    if ks is not None:        # the product the rescaled operands stand for
+        A16 = (A16.astype(np.float64) * np.exp2(-ks.astype(np.float64))[None, :]).astype(np.float32)
+    rows = np.arange(16)
+    C64 = oracle.gemm_f64_rows(A16, W64, rows)
+    C32 = oracle.gemm_f32_naive_rows(A16, W64, rows)
+    e_gpu = gemm_normwise_error(outs[16], C64, A16, W64, rows=rows)
+    e_naive = gemm_normwise_error(C32, C64, A16, W64, rows=rows)
+    print(f"  e_gpu={e_gpu:.3e} e_naive={e_naive:.3e}", flush=True)
+    assert e_gpu <= gemm_tolerance(e_naive, K)
+
+
 @pytest.mark.parametrize("K,N", [(8192, 4096), (16384, 4096)])
 def test_gemm_decode_aligned_long_rows(K, N):
     """Weight rows a multiple of 32 KiB apart, read in 8 chunks of 8 or more k
