@@ -523,12 +523,17 @@ void gemm_prefill_kernel(const unsigned char* __restrict__ Apk, const unsigned c
         }
 }
 
+// C := 0 before the k halves add into it: rows by blockIdx.y (grid-stride),
+// 16-byte stores where C's rows are 16-byte aligned
 __global__ void zero_c_kernel(float* C, int64_t ldc, int64_t M, int64_t N) {
-    const int64_t total = M * N;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t m = i / N;
-        C[m * ldc + (i - m * N)] = 0.0f;
+    const bool vec = ((reinterpret_cast<uintptr_t>(C) | (uintptr_t)(ldc * 4)) & 15) == 0;
+    const int64_t n4 = vec ? N / 4 : 0;
+    const int64_t step = (int64_t)gridDim.x * blockDim.x;
+    const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+        float* row = C + m * ldc;
+        for (int64_t i = t0; i < n4; i += step) reinterpret_cast<float4*>(row)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int64_t i = 4 * n4 + t0; i < N; i += step) row[i] = 0.0f;
     }
 }
 
@@ -590,8 +595,8 @@ hipError_t launch_gemm_prefill(const void* Apk, const void* Bpk, int nprod, bool
     const int* eb = x3 ? nullptr
                        : reinterpret_cast<const int*>(b + (b_hi ? pack_data_bytes_hi(N, K) : pack_data_bytes(N, K)));
     if (split) {
-        const unsigned zb = (unsigned)std::min<int64_t>((M * N + 255) / 256, 4096);
-        hipLaunchKernelGGL(zero_c_kernel, dim3(zb), dim3(256), 0, s, C, ldc, M, N);
+        const dim3 zg((unsigned)std::min<int64_t>((N + 1023) / 1024, 64), (unsigned)std::min<int64_t>(M, 1024));
+        hipLaunchKernelGGL(zero_c_kernel, zg, dim3(256), 0, s, C, ldc, M, N);
     }
     const dim3 grid((unsigned)(tiles_m * tiles_n * (split ? 2 : 1)));
     const QkvDst none{};
