@@ -17,7 +17,7 @@
 // ones its own queries see, so the first four waves skip the block's last
 // key block.  Each thread loads its share of the next block's K and V codes
 // into registers while the current block is computed, and unpacks it into
-// fp16 planes in LDS (K and V hi exact, lo biased) once for all eight waves;
+// fp16 planes in LDS (K hi and 64 V hi exact, lo biased) once for all eight waves;
 // two sets of planes alternate, so one barrier per key block suffices:
 //  * scores as S^T = K . Q^T on v_mfma_f32_16x16x32_f16: rows are keys,
 //    columns the wave's 16 queries.  A = {kh, kl + 1024}, B = {64 qh, ql}: the
@@ -34,7 +34,7 @@
 //    fp16 hi + lo 2^-10; V comes from LDS through the transposing
 //    ds_read_b64_tr_b16 on the V planes as {vh, vl + 1024}; the weight
 //    x = p s_v 2^(9 - E) splits into fp16 H + L, which enter one fresh
-//    accumulator (with the 64 of 64 vh folded in for the vh products),
+//    accumulator against the planes {64 vh, vl + 1024},
 //    started from -1024 times the weight sums to cancel the bias; the output
 //    is held in units of the block factor 2^(E - 9) and merged as
 //    acc 2^(m_old - m_new) 2^(E_old - E) + block.
@@ -144,6 +144,10 @@ __global__ __launch_bounds__(64 * WPB) void attn_prefill_kernel(
     // two sets of planes: the waves compute on one while the next key
     // block is unpacked into the other
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * BUF];
+    // per set: the key block's K and V scales and its block factor's
+    // exponent E - 9, written once by wave 0
+    __shared__ __attribute__((aligned(16))) float sks[2][KB], svs[2][KB];
+    __shared__ int sbeta[2];
     const int lane = threadIdx.x & 63;
     const int tid = threadIdx.x;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -224,26 +228,38 @@ __global__ __launch_bounds__(64 * WPB) void attn_prefill_kernel(
             *reinterpret_cast<half8*>(buf + KL + ko) = lo;
             unpack8_lobias(rv[i], hi, lo);
             const int vo = row * (D * 2) + 16 * (sh_chunk ^ vswz(row));
-            *reinterpret_cast<half8*>(buf + VH + vo) = hi;
+            *reinterpret_cast<half8*>(buf + VH + vo) = hi * (_Float16)64.0f;   // exact: |64 vh| <= 32768
             *reinterpret_cast<half8*>(buf + VL + vo) = lo;
         }
     };
-    // scales of a block's keys where the score layout needs them: index
-    // 4 st + e is key 16 st + 4 grp + e (0 past T, and past the last block)
-    float ksv[16], vsv[16];
+    // scales of a block's keys: lane t of wave 0 loads key t's K and V scales
+    // (0 past T, and past the last block) and, once the block's planes are
+    // written, puts them in the block's set with E - 9, E the exponent of
+    // the largest V scale of the block's 64 keys (so s_v(t) 2^(9 - E) lies
+    // in [0, 512)); every wave then reads them from LDS instead of loading
+    // and reducing them itself
+    float ks_r = 0.0f, vs_r = 0.0f;
     auto load_scales = [&](int kb) {
+        if (wid != 0) return;
         const int t0 = min(kb, nkb - 1) * KB;
         const int nt = kb < nkb ? __builtin_amdgcn_readfirstlane(min(KB, T - t0)) : 0;
         const int64_t tok0 = ((int64_t)b * T + t0) * Hkv + gk;
         const uint32_t srec = nt > 0 ? (uint32_t)(((nt - 1) * Hkv + 1) * 4) : 0u;
         const __amdgpu_buffer_rsrc_t ksrs = make_rsrc(ks + tok0, srec);
         const __amdgpu_buffer_rsrc_t vsrs = make_rsrc(vs + tok0, srec);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t off = (uint32_t)((16 * (i >> 2) + 4 * grp + (i & 3)) * Hkv * 4);
-            ksv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ksrs, off, 0, 0));
-            vsv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vsrs, off, 0, 0));
-        }
+        const uint32_t off = (uint32_t)(lane * Hkv * 4);
+        ks_r = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ksrs, off, 0, 0));
+        vs_r = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vsrs, off, 0, 0));
+    };
+    auto write_scales = [&](int set) {
+        if (wid != 0) return;
+        const float vmax = max_swap32(max_half(vs_r));
+        int vexp = 0;
+        (void)frexpf(vmax, &vexp);
+        const int ebeta = vmax > 0.0f ? vexp - 9 : 0;
+        sks[set][lane] = ks_r;
+        svs[set][lane] = vs_r;
+        if (lane == 0) sbeta[set] = ebeta;
     };
 
     // ---- running softmax state of query column c (the same on its 4 lanes)
@@ -258,7 +274,19 @@ __global__ __launch_bounds__(64 * WPB) void attn_prefill_kernel(
     // one key block from the planes at buf; only the wave's last one (its
     // diagonal, or the ragged end of the prompt) has keys a query of the wave
     // may not see
-    auto key_block = [&](int kb, const unsigned char* buf, auto masked) {
+    auto key_block = [&](int kb, const unsigned char* buf, int set, auto masked) {
+        // the block's scales where the score layout needs them: index 4 st + e
+        // is key 16 st + 4 grp + e
+        float ksv[16], vsv[16];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const float4 k4 = *reinterpret_cast<const float4*>(&sks[set][16 * st + 4 * grp]);
+            const float4 v4 = *reinterpret_cast<const float4*>(&svs[set][16 * st + 4 * grp]);
+            ksv[4 * st] = k4.x; ksv[4 * st + 1] = k4.y; ksv[4 * st + 2] = k4.z; ksv[4 * st + 3] = k4.w;
+            vsv[4 * st] = v4.x; vsv[4 * st + 1] = v4.y; vsv[4 * st + 2] = v4.z; vsv[4 * st + 3] = v4.w;
+        }
+        const int ebeta = sbeta[set];
+        const float p2 = ldexpf(1.0f, -ebeta);
         // ---- scores: sc[4 st + e] for key 16 st + 4 grp + e of the block
         float sc[16];
 #pragma unroll
@@ -304,26 +332,16 @@ __global__ __launch_bounds__(64 * WPB) void attn_prefill_kernel(
         l_run = l_run * alpha + group_sum(psum);
         m_run = m_new;
 
-        // power of two keeping s_v(t) 2^E in [1, 2) over the block's keys (the
-        // whole wave holds all 64 of them)
-        float vmax = vsv[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) vmax = fmaxf(vmax, vsv[i]);
-        vmax = group_max(vmax);   // every lane group of 16 holds the same 16 keys' scales
-        int vexp = 0;
-        (void)frexpf(vmax, &vexp);
         // x = p s_v(t) 2^(9 - E) lies in [0, 512); its block factor 2^(E - 9)
-        const int ebeta = vmax > 0.0f ? vexp - 9 : 0;
-        const float p2 = ldexpf(1.0f, -ebeta);
 
         // ---- P as the A operand for key halves kh2 = 0, 1 (32 keys each):
         //      slot i = key 32 kh2 + 16 (i / 4) + 4 grp + i % 4.  The weight
         //      x splits as H = fp16(x), L = fp16(x - H) (x - H is exact in fp32;
         //      H + L holds x to 2^-22, and L keeps it in normal range down to
         //      x ~ 2^-3, to 2^-24 absolute below); with V's parts v = 64 vh + vl
-        //      the operands are 64 H and 64 L against vh (64 H < 2^15), H and L
-        //      against vl.  All scalings are exact.
-        half8 pa_h[2], pa_l[2], pa_h64[2], pa_l64[2];
+        //      the operands are H and L against the plane of 64 vh (|64 vh| <=
+        //      2^15, exact), and against vl.  Every product is exact.
+        half8 pa_h[2], pa_l[2];
 #pragma unroll
         for (int kh2 = 0; kh2 < 2; ++kh2) {
 #pragma unroll
@@ -333,8 +351,6 @@ __global__ __launch_bounds__(64 * WPB) void attn_prefill_kernel(
                 pa_h[kh2][i] = hh;
                 pa_l[kh2][i] = (_Float16)(x - (float)hh);
             }
-            pa_h64[kh2] = pa_h[kh2] * (_Float16)64.0f;
-            pa_l64[kh2] = pa_l[kh2] * (_Float16)64.0f;
         }
 
         // ---- P . V into a fresh accumulator; V by transposing LDS reads: in
@@ -368,11 +384,11 @@ __global__ __launch_bounds__(64 * WPB) void attn_prefill_kernel(
                     const u32x2 h1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(buf + VH + o1)));
                     const u32x2 l0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(buf + VL + o0)));
                     const u32x2 l1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(buf + VL + o1)));
-                    const half8 vh = __builtin_bit_cast(half8, (u32x4){h0.x, h0.y, h1.x, h1.y});
+                    const half8 vh64 = __builtin_bit_cast(half8, (u32x4){h0.x, h0.y, h1.x, h1.y});
                     const half8 vlb = __builtin_bit_cast(half8, (u32x4){l0.x, l0.y, l1.x, l1.y});
-                    mfma16(pa_h64[kh2], vh, blk[dt]);
+                    mfma16(pa_h[kh2], vh64, blk[dt]);
                     mfma16(pa_h[kh2], vlb, blk[dt]);
-                    mfma16(pa_l64[kh2], vh, blk[dt]);
+                    mfma16(pa_l[kh2], vh64, blk[dt]);
                     mfma16(pa_l[kh2], vlb, blk[dt]);
                 }
             }
@@ -394,20 +410,25 @@ __global__ __launch_bounds__(64 * WPB) void attn_prefill_kernel(
     // block 0 unpacked into the first planes; block 1's codes and block 0's
     // scales in flight
     load_raw(0);
-    write_planes(lds);
     load_scales(0);
+    write_planes(lds);
+    write_scales(0);
     load_raw(1);
+    load_scales(1);
     for (int kb = 0; kb < nkb; ++kb) {
-        // block kb's planes are complete, and every wave is done with block
-        // kb - 1, whose planes block kb + 1 now takes
+        // block kb's planes and scales are complete, and every wave is done
+        // with block kb - 1, whose set block kb + 1 now takes
         __syncthreads();
         unsigned char* cur = lds + (kb & 1) * BUF;
         unsigned char* nxt = lds + ((kb + 1) & 1) * BUF;
-        if (kb + 1 < nkb_w) key_block(kb, cur, std::false_type{});
-        else if (kb + 1 == nkb_w) key_block(kb, cur, std::true_type{});
-        if (kb + 1 < nkb) write_planes(nxt);
-        load_scales(kb + 1);
+        if (kb + 1 < nkb_w) key_block(kb, cur, kb & 1, std::false_type{});
+        else if (kb + 1 == nkb_w) key_block(kb, cur, kb & 1, std::true_type{});
+        if (kb + 1 < nkb) {
+            write_planes(nxt);
+            write_scales((kb + 1) & 1);
+        }
         load_raw(kb + 2);
+        load_scales(kb + 2);
     }
 
     // ---- normalize and store: rows q0 + 4 grp + e, d = 16 dt + c
