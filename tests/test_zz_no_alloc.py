@@ -57,7 +57,8 @@ def test_noalloc_binding_and_limits():
 
 
 @pytest.mark.parametrize("M,K,N,form", [(8, 4096, 1024, "fp32"), (40, 4096, 4096, "fp32"),
-                                        (64, 14336, 4096, "packed"), (1, 4096, 14336, "fp16")])
+                                        (64, 14336, 4096, "packed"), (1, 4096, 14336, "fp16"),
+                                        (8, 4096, 4096, "fp32")])   # the last: k chunks as waves
 def test_noalloc_graph_replays(M, K, N, form):
     """Captured once in a HIP graph and replayed with new activations (copied into
     the captured input between replays): every replay equals the workspace entry
