@@ -45,7 +45,9 @@ Output: one JSON line.  `value` is the metric's first half, FP32-accurate GEMM
 TFLOP/s on the prefill workload (useful flops 2MNK over the time of split +
 GEMM); `quant_GBps` is its second half.  `roofline` is the prefill GEMM kernel
 against the 16-bit MFMA peak (3 fp16 products per useful multiply-add).
-`cpu_baseline` is the CPU oracle timed on host cores on a bounded sample.
+`cpu_baseline` is the CPU oracle timed on host cores on a bounded sample;
+`calibration` holds the measured MFMA and HBM ceilings; `vendor_gemm` times the
+vendor's GEMM (torch.matmul) on the same shapes as context (never part of `value`).
 """
 import argparse
 import hashlib
