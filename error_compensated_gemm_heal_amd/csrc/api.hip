@@ -188,8 +188,9 @@ heal_status gemm_impl(const float* A, int64_t lda, const void* W, int64_t ldw, f
         if ((!packed && ldw >= kMaxDecodeLdw) || lda >= kMaxDecodeLda) return HEAL_ERR_UNSUPPORTED;
         const DecodePlan p = decode_plan(M, N, K);
         // the epoch of a captured call would be replayed with the graph, and
-        // a replay would take the previous one's flags for its own
-        if (p.splits > 1 && !counters) {
+        // a replay would take the previous one's flags for its own (chunks
+        // that meet in LDS use no flags)
+        if (p.splits > 1 && !counters && !decode_chunks_as_waves(M, N, p, a_kshift != nullptr)) {
             hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
             if (hipStreamIsCapturing(s, &cs) != hipSuccess) return HEAL_ERR_HIP;
             if (cs != hipStreamCaptureStatusNone) return HEAL_ERR_UNSUPPORTED;

@@ -701,6 +701,11 @@ int64_t DecodePlan::bytes() const {
     return (c_bytes + 255) / 256 * 256 + (a_bytes + 255) / 256 * 256 + (p_bytes + 255) / 256 * 256;
 }
 
+bool decode_chunks_as_waves(int64_t M, int64_t N, const DecodePlan& p, bool kshift) {
+    const int64_t nslices = (N + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
+    return mtiles(M) == 1 && !kshift && p.splits >= 2 && p.splits <= 2 * NW && p.kchunk <= 4 * KA && nslices >= 256;
+}
+
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
     DecodePlan p{};
     const int64_t nblk = (N + DEC_ROWS - 1) / DEC_ROWS;
@@ -769,11 +774,10 @@ hipError_t launch_gemm_decode(const float* A, int64_t lda, const int8_t* kshift,
     // it saves (K = 14336, N = 4096, 8 chunks of 14 blocks: 47.8 -> 47.9 us
     // at M = 1, 49.2 -> 53.2 us at M = 8; K = 4096, N = 14336, 2 chunks of
     // 16 blocks: 51.7 -> 52.6 and 52.5 -> 57.0 us), so it stays off there.
-    const int64_t nslices = (N + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
     // (Not with a_kshift: that form's per-wave staging of all 16 rows did not
     // fit in registers.)
-    const bool kw = mt == 1 && !kshift && plan.splits >= 2 && plan.splits <= 2 * NW && plan.kchunk <= 4 * KA &&
-                    nslices >= 256;
+    const int64_t nslices = (N + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
+    const bool kw = decode_chunks_as_waves(M, N, plan, kshift != nullptr);
     const bool ink = mt > 1 && !kshift && avec && (rnd == 1 || (rnd == 2 && plan.kchunk / KA <= 4));
 #define HEAL_DEC_LAUNCH_NW(MT_, VEC_, F16_, AV_, SH_, ONE_, NW_, INK_)                                \
     hipLaunchKernelGGL((gemm_decode_kernel<MT_, VEC_, F16_, AV_, SH_, ONE_, NW_, INK_>), grid, dim3(64 * NW_), \

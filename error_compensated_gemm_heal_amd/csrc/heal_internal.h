@@ -247,6 +247,10 @@ struct DecodePlan {
     int64_t bytes() const;
 };
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K);
+// Whether the plan's k chunks are the waves of one workgroup and meet in LDS
+// (one row tile, 2 .. 8 chunks of at most 4 blocks, at least 256 slices of 16
+// rows, no a_kshift): no split-K completion through memory, so no epoch.
+bool decode_chunks_as_waves(int64_t M, int64_t N, const DecodePlan& p, bool kshift);
 // W is fp32, or binary16 values when wf16 (the two-product form); one: plain
 // FP16 (A_hi.W_hi alone).  kshift (nullable): A's element (m, k) is
 // multiplied by 2^-kshift[k] before its split.

@@ -184,12 +184,14 @@ heal_status heal_split_f32(const float* X, int64_t n, uint16_t* hi, uint16_t* lo
  * same memory channels.  The kernel visits k in a rotated order per group
  * of rows where that helps, and a packed W pads its rows, which is faster
  * still (K = 4096, N = 14336 at M = 1: 52.0 us streamed, 47.7 us packed).
- * Graph capture: on the M <= 64 path with a k split (chosen from N and K),
- * the call marks its split-K flags in the workspace with a per-call value
- * taken on the host, which a captured graph would replay; under stream
- * capture such a call returns HEAL_ERR_UNSUPPORTED before any launch.
- * heal_gemm_f32c_noalloc captures and replays correctly.  Other shapes
- * capture normally.
+ * Graph capture: on the M <= 64 path with a k split (chosen from N and K)
+ * completed through memory, the call marks its split-K flags in the
+ * workspace with a per-call value taken on the host, which a captured graph
+ * would replay; under stream capture such a call returns
+ * HEAL_ERR_UNSUPPORTED before any launch.  heal_gemm_f32c_noalloc captures
+ * and replays correctly.  Other shapes capture normally, among them the
+ * k splits whose chunks meet in LDS (M <= 16, N >= 4081, no a_kshift, and
+ * 2 to 8 chunks of at most 512 k, e.g. K = N = 4096).
  * Limits: M, N, K < 2^31.  K == 0 writes zeros.  In the M <= 64 case above,
  * ldw < 2^26 and lda < 2^24 (each 16-row slice of W, and A, are addressed
  * with 32-bit byte offsets), else HEAL_ERR_UNSUPPORTED.  The launches'

@@ -43,10 +43,11 @@ def test_capture_refused_with_split_k():
     assert st == 5, heal.heal_status_str(st)        # HEAL_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("M,K,N", [(4, 256, 192), (300, 512, 384)])
+@pytest.mark.parametrize("M,K,N", [(4, 256, 192), (300, 512, 384), (8, 4096, 4096), (1, 2048, 4100)])
 def test_capture_and_replay_without_split_k(M, K, N):
-    """A decode shape with one k chunk, and a prefill shape: replays with new
-    activations equal the eager calls, bit for bit."""
+    """A decode shape with one k chunk, a prefill shape, and decode shapes whose k
+    chunks are the waves of one workgroup (no flags in the workspace): replays
+    with new activations equal the eager calls, bit for bit."""
     print(f"graph M={M} K={K} N={N}", flush=True)
     A0, W = WL.decode_gemm(M, K, N, seed=42 + M)
     Wd = torch.from_numpy(W).to(DEV)
